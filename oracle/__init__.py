@@ -1,0 +1,20 @@
+"""CPU oracle for ring / zigzag / striped / Ulysses-hybrid sequence-parallel attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports this package:
+only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may use it.  It shares no code with the HIP library.
+
+Modules
+  index_ref      integer token-order formulas (which positions each virtual
+                 rank holds; Ulysses seq<->head relayout) in plain Python ints
+  attention_ref  the definition: naive full-matrix masked softmax attention
+                 in float64 over the unpermuted sequence, with the visibility
+                 predicate on global positions
+  ring_ref       the ring-decomposed float64 reference: per (rank, step)
+                 block attention with its partial output and log-sum-exp, and
+                 the associative max/logsumexp merge of partials
+
+Every function is pinned by ``tests/test_oracle_*.py`` against brute force,
+a library routine, closed forms, or values and invariants the pages state.
+"""
+from . import index_ref, attention_ref, ring_ref  # noqa: F401

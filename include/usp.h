@@ -1,0 +1,257 @@
+/*
+ * usp.h -- C ABI of libusp: one GPU's share of ring / zigzag / striped /
+ * Ulysses-hybrid sequence-parallel attention, as HIP kernels for gfx950.
+ *
+ * Sources for what each call computes (cited by page title and section):
+ *   [YC]  YunChang (USP) README: "2. Usage" (extract the local shard with the
+ *         ring layout, then run LongContextAttention with a ring_impl_type of
+ *         basic / zigzag / stripe; ulysses x ring degrees), "Why not apply
+ *         Ulysses and Ring Attention Individually?" (Ulysses all-to-all splits
+ *         heads; its degree cannot exceed the head count).
+ *   [SWA] ring sliding-window attention README: argument list (q/k/v shapes,
+ *         window_size, cu_seqlens global over all ranks, softmax_scale default
+ *         1/sqrt(head_dim), cp_group None = single-GPU mode), varlen example,
+ *         streaming-LLM (attention sink) section.
+ *   [LCA] Long Context Attention notes: "Ring Attention" (N hosts on a ring
+ *         pass KV pieces; block order is free), "Solution" (striped
+ *         permutation), "Zig-Zag Attention" (fold the mask), "Tree Attention"
+ *         (max / logsumexp are associative), "Motivation" (keep the LSE).
+ *
+ * Conventions shared by every call
+ *   - All tensors are dense, row-major, contiguous, in device memory owned by
+ *     the caller.  bf16 is IEEE bfloat16; f32 is IEEE binary32.
+ *   - q is [B,S,Hq,D]; k and v are [B,S,Hkv,D] (varlen: B = 1, [T,H,D]).
+ *     Hq must be a multiple of Hkv; query head h reads kv head h / (Hq/Hkv).
+ *   - LSE is the natural-log log-sum-exp of the scaled scores over the
+ *     visible keys, f32, laid out [B,Hq,S]; a row with no visible key has
+ *     LSE = -inf and output 0.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
+ *     enqueued; nothing synchronises except where a call says so.
+ *   - Every argument is validated on the host before anything is enqueued.
+ *     On a non-OK status nothing was enqueued and outputs are untouched;
+ *     usp_last_error() returns a message for the calling thread.
+ *     USP_ERR_HIP reports a HIP runtime failure (launch or memory call).
+ *   - Results are deterministic: no atomics in any reduction.
+ */
+#ifndef USP_H_
+#define USP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  USP_OK = 0,
+  USP_ERR_INVALID_ARG = 1,   /* bad pointer, shape, divisibility, range    */
+  USP_ERR_UNSUPPORTED = 2,   /* valid request this library does not serve  */
+  USP_ERR_WORKSPACE = 3,     /* workspace missing or too small             */
+  USP_ERR_HIP = 4            /* HIP runtime error                          */
+} usp_status;
+
+/* Ring layouts of the sequence over N virtual ranks, L = S/N rows each.
+ *   BASIC  : rank r holds positions [r*L, (r+1)*L)                    [LCA "Ring Attention"]
+ *   ZIGZAG : 2N chunks of c = S/(2N); rank r holds chunk r then chunk 2N-1-r
+ *                                                                    [LCA "Zig-Zag Attention"]
+ *   STRIPE : blocks of b tokens; block beta goes to rank beta mod N, so
+ *            local row t of rank r is position ((t/b)*N + r)*b + t%b [LCA "Solution"] */
+typedef enum { USP_RING_BASIC = 0, USP_RING_ZIGZAG = 1, USP_RING_STRIPE = 2 } usp_ring_impl;
+
+/* Mask of one block-attention call.  POSITIONAL derives visibility from the
+ * global positions of the rows (qmap/kmap) and causal / window / n_sink /
+ * cu_seqlens.  The explicit classes use local indices t (query) and u (key):
+ *   FULL: every key;  CAUSAL: u <= t;  CAUSAL_STRICT: u < t (the striped
+ *   round that drops the first query and the last key, [LCA "Solution"]);
+ *   EMPTY: no key (the call writes O = 0, LSE = -inf, or with accumulate=1
+ *   changes nothing). */
+typedef enum {
+  USP_MASK_EMPTY = 0,
+  USP_MASK_FULL = 1,
+  USP_MASK_CAUSAL = 2,
+  USP_MASK_CAUSAL_STRICT = 3,
+  USP_MASK_POSITIONAL = 4
+} usp_mask_class;
+
+typedef enum { USP_DT_BF16 = 0, USP_DT_F32 = 1 } usp_dtype;
+
+/* Which global positions the rows of one virtual rank hold. */
+typedef struct usp_posmap {
+  int32_t impl;          /* usp_ring_impl                        */
+  int32_t ring_degree;   /* N >= 1                               */
+  int32_t rank;          /* 0 <= rank < N                        */
+  int32_t stripe_block;  /* b >= 1 (STRIPE only)                 */
+  int64_t S_global;      /* total sequence length S              */
+} usp_posmap;
+
+/* Message for the last non-OK status of the calling thread ("" if none). */
+const char* usp_last_error(void);
+
+/* Library version string. */
+const char* usp_version(void);
+
+/* ------------------------------------------------------------------ permute
+ * Token reorder along the sequence axis of a tensor viewed as
+ * [outer, S, inner] (inner elements of dtype dt per row), [YC "2. Usage":
+ * the extract function reorders inputs for the load-balanced ring].
+ *   rank == -1, inverse == 0: out[o, r*L + t, :] = in[o, pos_r(t), :]
+ *        (natural order -> rank-major order, all ranks);
+ *   rank == -1, inverse == 1: the inverse (rank-major -> natural);
+ *   rank >= 0 : global USP rank g = rank = r*ud + u (ring rank r, Ulysses
+ *        rank u) holding the u-th contiguous piece of L/ud rows of ring rank
+ *        r's shard; inverse == 0 extracts it: out is [outer, L/ud, inner];
+ *        inverse == 1 scatters such a shard back into the natural-order out
+ *        (only that shard's rows are written).
+ * Out-of-place only (in and out must not overlap).  S must be divisible by N
+ * (BASIC), 2N (ZIGZAG) or N*b (STRIPE), and L by ulysses_degree.  Bit-exact
+ * copy; HBM-bound. */
+usp_status usp_permute(const void* in, void* out, int64_t outer, int64_t S, int64_t inner,
+                       usp_dtype dt, usp_ring_impl impl, int ring_degree, int ulysses_degree,
+                       int stripe_block, int rank, int inverse, void* stream);
+
+/* ------------------------------------------------------- Ulysses relayout
+ * The local pack / unpack around the Ulysses all-to-all for Ulysses rank u
+ * of ud, with the all-to-all itself replaced by reading every peer's piece
+ * from this device [YC "Why not apply Ulysses and Ring Attention
+ * Individually?": Ulysses trades sequence for heads].  Hg = H/ud.
+ *   direction 0 (seq -> head): shards[u'] is [B, Ls, H, D] for u' < ud;
+ *       local is [B, ud*Ls, Hg, D];
+ *       local[b, u'*Ls + s, h', :] = shards[u'][b, s, u*Hg + h', :].
+ *   direction 1 (head -> seq): the inverse; writes only head group u of
+ *       each shards[u'] and nothing else.
+ * `shards` is a host array of ud device pointers; 1 <= ud <= 8, ud divides
+ * H.  Bit-exact copy. */
+usp_status usp_ulysses_relayout(void* const* shards, void* local, int64_t B, int64_t S_shard,
+                                int64_t H, int64_t D, usp_dtype dt, int ulysses_degree,
+                                int ulysses_rank, int direction, void* stream);
+
+/* ------------------------------------------------------ block attention
+ * One ring step: softmax attention of q [B,Lq,Hq,D] (bf16) against k, v
+ * [B,Lk,Hkv,D] (bf16) under `mask`, emitting the partial output and LSE
+ * [LCA "Ring Attention", "Motivation"].  For every visible (query t, key u):
+ * s = softmax_scale * <q_t, k_u> (bf16 products, f32 accumulation); the
+ * partial is O_t = sum_u exp(s - m) v_u / sum_u exp(s - m), LSE_t = m +
+ * ln sum_u exp(s - m).  softmax_scale <= 0 selects 1/sqrt(D) [SWA args].
+ *
+ * POSITIONAL masks: qmap/kmap give the global positions of the q and k rows
+ * (same impl, N, b and S; Lq and Lk equal S/N).  A key is visible when it is
+ * in the query's sequence (cu_seqlens, global over all ranks [SWA varlen];
+ * B must then be 1), and, if causal or window > 0, p_k <= p_q, and, if
+ * window > 0, p_q - p_k < window [SWA window_size: the number of keys each
+ * query attends to, itself included] or the key is one of the first n_sink
+ * tokens of that sequence [SWA streaming-LLM attention sink].
+ * Explicit classes require causal = window = n_sink = 0 and no cu_seqlens.
+ *
+ * out is [B,Lq,Hq,D] in out_dt, lse is [B,Hq,Lq] f32.  accumulate = 0
+ * overwrites them with this call's partial; accumulate = 1 (out_dt must be
+ * F32) merges this partial into the running (out, lse) with the associative
+ * rescale of usp_lse_merge.  D must be 64 or 128.  cu_seqlens_host (nseq+1
+ * int32, host) plans the tiles; cu_seqlens_dev (same values, device) is read
+ * by the kernel.  The first call with a new shape/mask builds and uploads a
+ * tile plan (one synchronous copy); later calls reuse it. */
+usp_status usp_block_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                              int64_t B, int64_t Lq, int64_t Lk, int64_t Hq, int64_t Hkv, int64_t D,
+                              float softmax_scale, usp_mask_class mask,
+                              const usp_posmap* qmap, const usp_posmap* kmap,
+                              int causal, int window, int n_sink,
+                              const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int nseq,
+                              usp_dtype out_dt, int accumulate, void* stream);
+
+/* ---------------------------------------------------------------- merge
+ * In-place associative combine of a partial into a running result, rows
+ * [row_begin, row_end) of the sequence axis [LCA "Tree Attention": max and
+ * logsumexp are associative]:
+ *   M = max(L_a, L_b); L = M + ln(e^(L_a - M) + e^(L_b - M));
+ *   O = e^(L_a - L) O_a + e^(L_b - L) O_b;   (L_b = -inf leaves (O_a, L_a)).
+ * out_acc/out_part are f32 [B,L,H,D]; lse_acc/lse_part f32 [B,H,L]. */
+usp_status usp_lse_merge(float* out_acc, float* lse_acc, const float* out_part, const float* lse_part,
+                         int64_t B, int64_t L, int64_t H, int64_t D, int64_t row_begin,
+                         int64_t row_end, void* stream);
+
+/* ------------------------------------------------------- virtual ring
+ * All ring_degree steps of ring attention on one device [LCA "Ring
+ * Attention"; SWA single-GPU mode]: host i holds query piece i and at step s
+ * the KV piece of j = (i - s) mod N; each step runs block attention with the
+ * mask its positions imply and merges its partial into the running result.
+ * The KV "send" is a pointer offset; every step is enqueued in order on one
+ * stream.  With ulysses_degree ud > 1 the Ulysses seq -> head relayout of
+ * q, k, v runs first for Ulysses rank `ulysses_rank` [YC "2. Usage"].
+ *
+ * Inputs q [B,S,Hq,D], k/v [B,S,Hkv,D] bf16 hold the whole sequence, in
+ * natural order (input_order 0; permuted on the device first) or already
+ * rank-major (input_order 1).  Varlen (cu_seqlens set) requires BASIC and
+ * B = 1.
+ * Outputs:
+ *   rank == -1: every rank; out [B,S,Hq,D] (out_dtype) and lse [B,Hq,S] in
+ *     the input's order (ud must be 1: the head split does not change the
+ *     result of all ranks together);
+ *   rank >= 0 : ring rank `rank`'s share for Ulysses rank `ulysses_rank`:
+ *     out [B,L,Hq/ud,D] and lse [B,Hq/ud,L] in that rank's local row order.
+ * merge_mode 0 merges in the attention kernel's epilogue; 1 writes each
+ * step's partial to the workspace and runs usp_lse_merge. */
+typedef struct usp_ring_args {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;
+  int64_t B, S, Hq, Hkv, D;
+  float softmax_scale;               /* <= 0: 1/sqrt(D)                   */
+  int32_t causal, window, n_sink;
+  const int32_t* cu_seqlens_dev;     /* NULL unless varlen                 */
+  const int32_t* cu_seqlens_host;
+  int32_t nseq;
+  int32_t impl;                      /* usp_ring_impl                      */
+  int32_t ring_degree, ulysses_degree, stripe_block;
+  int32_t rank, ulysses_rank;
+  int32_t input_order;               /* 0 natural, 1 rank-major            */
+  int32_t out_dtype;                 /* usp_dtype                          */
+  int32_t merge_mode;                /* 0 fused epilogue, 1 separate merge */
+} usp_ring_args;
+
+/* Bytes of device workspace usp_ring_fwd needs for these arguments. */
+size_t usp_ring_fwd_workspace_size(const usp_ring_args* a);
+
+/* Runs the virtual ring.  workspace: device memory of at least
+ * usp_ring_fwd_workspace_size(a) bytes (may be NULL when that is 0), owned
+ * by the caller, 256-byte aligned. */
+usp_status usp_ring_fwd(const usp_ring_args* a, void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------ tile scheduler
+ * Host-only inspection of the tile plan usp_block_attn_fwd would run (no
+ * device work).  Items are 8 int32 each: {q_row0, t0, q_rows, q_rank, k_row0,
+ * k_rank, run_begin, run_end}; runs are 4 int32 each: {k_begin, k_end, full,
+ * 0}: keys [k_begin, k_end) of the item's KV rows, `full` = 1 when every key
+ * of the run is visible to every query row of the item (no per-element
+ * mask; length a multiple of *tile_n).  Keys outside every run are visible
+ * to no row of the item.  Items come ordered by decreasing work.
+ * Pass NULL buffers to query the counts only. */
+usp_status usp_plan_block(int64_t Lq, int64_t Lk, int64_t D, usp_mask_class mask,
+                          const usp_posmap* qmap, const usp_posmap* kmap,
+                          int causal, int window, int n_sink,
+                          const int32_t* cu_seqlens_host, int nseq, int accumulate,
+                          int32_t* items, int64_t items_cap, int32_t* runs, int64_t runs_cap,
+                          int64_t* n_items, int64_t* n_runs, int32_t* tile_m, int32_t* tile_n);
+
+/* ---------------------------------------------------- kernel timing
+ * Instrumentation for benchmarks.  While enabled, every kernel launch of the
+ * library is bracketed by two hipEvents recorded on its stream; read sums
+ * the elapsed times of the recorded launches of one kernel class (waiting on
+ * their events).  Off by default; enabling adds two event records per
+ * launch.  Not thread-safe with respect to concurrent reset. */
+typedef enum {
+  USP_KERNEL_ATTN = 0,      /* block attention (usp_block_attn_fwd and ring steps) */
+  USP_KERNEL_PERMUTE = 1,   /* token permutation, output reorder / conversion      */
+  USP_KERNEL_RELAYOUT = 2,  /* Ulysses relayout                                     */
+  USP_KERNEL_MERGE = 3      /* separate LSE merge                                   */
+} usp_kernel_class;
+
+usp_status usp_timing_enable(int enable);
+usp_status usp_timing_reset(void);
+usp_status usp_timing_read(int kernel_class, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* USP_H_ */

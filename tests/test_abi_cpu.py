@@ -1,0 +1,274 @@
+"""CPU tests of the C ABI: exported symbols, host-side validation and the
+tile planner (usp_plan_block), which is host code and is checked here
+bit-exactly against the oracle's visibility predicate.
+
+No test here launches device work: every call either fails validation on the
+host before anything is enqueued, or is the host-only planner.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import ulysses_sequence_attention_zigzag_amd as usp
+from oracle import index_ref as ix
+from oracle.attention_ref import visibility
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "usp.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(usp.LIB_PATH), reason="libusp.so not built")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(usp_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_header_function():
+    names = header_functions()
+    assert "usp_ring_fwd" in names and "usp_block_attn_fwd" in names
+    lib = ctypes.CDLL(usp.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(usp.EXPORTS) == names
+
+
+def test_version_and_empty_error():
+    assert usp.lib().usp_version().decode().startswith("usp-")
+
+
+FAKE = ctypes.c_void_p(0x10000)
+FAKE2 = ctypes.c_void_p(0x7f0000000000)
+
+
+def _status(fn, *args):
+    st = fn(*args)
+    return st, usp.lib().usp_last_error().decode()
+
+
+def test_permute_validation():
+    L = usp.lib()
+    st, msg = _status(L.usp_permute, None, FAKE, 1, 16, 8, 0, 1, 4, 1, 1, -1, 0, None)
+    assert st == 1 and "null" in msg
+    st, msg = _status(L.usp_permute, FAKE, FAKE2, 1, 12, 8, 0, 1, 4, 1, 1, -1, 0, None)
+    assert st == 1 and "zigzag" in msg
+    st, msg = _status(L.usp_permute, FAKE, FAKE2, 1, 12, 8, 0, 2, 4, 1, 2, -1, 0, None)
+    assert st == 1 and "stripe" in msg
+    st, msg = _status(L.usp_permute, FAKE, FAKE2, 1, 16, 8, 0, 7, 4, 1, 1, -1, 0, None)
+    assert st == 1 and "impl" in msg
+    st, msg = _status(L.usp_permute, FAKE, FAKE2, 1, 16, 8, 0, 0, 4, 3, 1, -1, 0, None)
+    assert st == 1 and "ulysses" in msg
+    st, msg = _status(L.usp_permute, FAKE, FAKE2, 1, 16, 8, 0, 0, 4, 1, 1, 4, 0, None)
+    assert st == 1 and "rank" in msg
+    st, msg = _status(L.usp_permute, FAKE, ctypes.c_void_p(0x10000 + 64), 1, 16, 8, 0, 0, 4, 1, 1, -1, 0, None)
+    assert st == 1 and "overlap" in msg
+
+
+def test_relayout_validation():
+    L = usp.lib()
+    arr9 = (ctypes.c_void_p * 9)(*[0x10000 * (i + 1) for i in range(9)])
+    st, msg = _status(L.usp_ulysses_relayout, ctypes.cast(arr9, ctypes.c_void_p), FAKE2, 1, 4, 9, 8, 0, 9, 0, 0, None)
+    assert st == 2 and "ulysses_degree" in msg
+    arr = (ctypes.c_void_p * 2)(0x10000, 0x20000)
+    st, msg = _status(L.usp_ulysses_relayout, ctypes.cast(arr, ctypes.c_void_p), FAKE2, 1, 4, 5, 8, 0, 2, 0, 0, None)
+    assert st == 1 and "divide" in msg
+    st, msg = _status(L.usp_ulysses_relayout, ctypes.cast(arr, ctypes.c_void_p), FAKE2, 1, 4, 4, 8, 0, 2, 2, 0, None)
+    assert st == 1 and "ulysses_rank" in msg
+    st, msg = _status(L.usp_ulysses_relayout, ctypes.cast(arr, ctypes.c_void_p), FAKE2, 1, 4, 4, 8, 0, 2, 0, 3, None)
+    assert st == 1 and "direction" in msg
+
+
+def _attn(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE2, lse=FAKE2, B=1, Lq=64, Lk=64, Hq=4, Hkv=2, D=128, scale=0.0,
+             mask=usp.MASK["causal"], qmap=None, kmap=None, causal=0, window=0, n_sink=0, cud=None, cuh=None,
+             nseq=0, dt=1, acc=0)
+    a.update(kw)
+    L = usp.lib()
+    return _status(L.usp_block_attn_fwd, a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Lq"], a["Lk"],
+                   a["Hq"], a["Hkv"], a["D"], a["scale"], a["mask"], a["qmap"], a["kmap"], a["causal"],
+                   a["window"], a["n_sink"], a["cud"], a["cuh"], a["nseq"], a["dt"], a["acc"], None)
+
+
+def test_block_attn_validation():
+    assert _attn(q=None)[0] == 1
+    st, msg = _attn(D=96)
+    assert st == 2 and "head_dim" in msg
+    st, msg = _attn(Hq=3, Hkv=2)
+    assert st == 1 and "multiple" in msg
+    st, msg = _attn(dt=0, acc=1)
+    assert st == 1 and "accumulate" in msg
+    st, msg = _attn(causal=1)
+    assert st == 1 and "explicit" in msg
+    st, msg = _attn(mask=usp.MASK["positional"])
+    assert st == 1 and "qmap" in msg
+    qm = usp.posmap("zigzag", 4, 0, 512)
+    km = usp.posmap("stripe", 4, 1, 512)
+    st, msg = _attn(mask=usp.MASK["positional"], qmap=ctypes.byref(qm), kmap=ctypes.byref(km), Lq=128, Lk=128)
+    assert st == 1 and "same layout" in msg
+    km = usp.posmap("zigzag", 4, 1, 512)
+    st, msg = _attn(mask=usp.MASK["positional"], qmap=ctypes.byref(qm), kmap=ctypes.byref(km), Lq=64, Lk=128)
+    assert st == 1 and "Lq == Lk" in msg
+    cu = torch.tensor([0, 100, 512], dtype=torch.int32)
+    st, msg = _attn(mask=usp.MASK["positional"], qmap=ctypes.byref(qm), kmap=ctypes.byref(km), Lq=128, Lk=128,
+                    cud=FAKE, cuh=ctypes.c_void_p(cu.data_ptr()), nseq=2, causal=1)
+    assert st == 2 and "basic" in msg
+    qb = usp.posmap("basic", 4, 0, 512)
+    kb = usp.posmap("basic", 4, 1, 512)
+    bad = torch.tensor([0, 300, 200], dtype=torch.int32)
+    st, msg = _attn(mask=usp.MASK["positional"], qmap=ctypes.byref(qb), kmap=ctypes.byref(kb), Lq=128, Lk=128,
+                    cud=FAKE, cuh=ctypes.c_void_p(bad.data_ptr()), nseq=2)
+    assert st == 1 and "cu_seqlens" in msg
+    st, msg = _attn(window=-1, mask=usp.MASK["positional"], qmap=ctypes.byref(qb), kmap=ctypes.byref(kb), Lq=128, Lk=128)
+    assert st == 1 and "window" in msg
+
+
+def test_merge_validation():
+    L = usp.lib()
+    st, msg = _status(L.usp_lse_merge, FAKE, FAKE, FAKE, FAKE, 1, 10, 2, 128, 5, 11, None)
+    assert st == 1 and "row range" in msg
+    st, msg = _status(L.usp_lse_merge, FAKE, FAKE, FAKE, FAKE, 1, 10, 2, 6, 0, 10, None)
+    assert st == 2
+
+
+def _ring_args(**kw):
+    a = usp.RingArgs()
+    a.q = a.k = a.v = 0x10000
+    a.out = a.lse = 0x7f0000000000
+    a.B, a.S, a.Hq, a.Hkv, a.D = 1, 1024, 8, 2, 128
+    a.impl, a.ring_degree, a.ulysses_degree, a.stripe_block = 1, 4, 1, 1
+    a.rank, a.ulysses_rank = -1, 0
+    a.causal = 1
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+def test_ring_validation_and_workspace():
+    L = usp.lib()
+    cases = [
+        (dict(S=1020), 1, "zigzag"),
+        (dict(D=80), 2, "head_dim"),
+        (dict(ulysses_degree=2), 1, "all-ranks"),
+        (dict(ulysses_degree=4, rank=0), 1, "divide"),
+        (dict(rank=4), 1, "rank"),
+        (dict(merge_mode=3), 1, "merge_mode"),
+        (dict(q=None), 1, "null"),
+    ]
+    for kw, code, word in cases:
+        a = _ring_args(**kw)
+        assert L.usp_ring_fwd_workspace_size(ctypes.byref(a)) == 0
+        st, msg = _status(L.usp_ring_fwd, ctypes.byref(a), None, 0, None)
+        assert st == code and word in msg, (kw, st, msg)
+    # workspace: natural-order zigzag input needs permuted copies of q, k, v plus
+    # an f32 accumulator in permuted order
+    a = _ring_args()
+    need = L.usp_ring_fwd_workspace_size(ctypes.byref(a))
+    qkv = 1024 * (8 + 2 + 2) * 128 * 2
+    acc = 1024 * 8 * 128 * 4 + 8 * 1024 * 4
+    assert need >= qkv + acc
+    st, msg = _status(L.usp_ring_fwd, ctypes.byref(a), None, 0, None)
+    assert st == 3 and "workspace" in msg
+    st, msg = _status(L.usp_ring_fwd, ctypes.byref(a), ctypes.c_void_p(0x10010), need, None)
+    assert st == 3 and "aligned" in msg
+    # pre-permuted f32 output of basic layout accumulates in place: no workspace
+    a = _ring_args(impl=0, input_order=1, out_dtype=1)
+    assert L.usp_ring_fwd_workspace_size(ctypes.byref(a)) == 0
+    # varlen only with the basic layout
+    cu = torch.tensor([0, 500, 1024], dtype=torch.int32)
+    a = _ring_args(cu_seqlens_dev=0x10000, cu_seqlens_host=cu.data_ptr(), nseq=2)
+    st, msg = _status(L.usp_ring_fwd, ctypes.byref(a), None, 0, None)
+    assert st == 2 and "basic" in msg
+
+
+# ---------------------------------------------------------------- planner
+def _check_plan(Lq, Lk, qpos, kpos, vis, accumulate, items, runs, tn):
+    """vis: bool [Lq, Lk] oracle visibility on local indices."""
+    covered = torch.zeros(Lq, dtype=torch.int32)
+    costs = []
+    for it in items.tolist():
+        q_row0, t0, rows, qrank, k_row0, krank, rb, re_ = it
+        assert q_row0 == t0 and 0 < rows <= 128
+        covered[t0:t0 + rows] += 1
+        keys = torch.zeros(Lk, dtype=torch.int32)
+        cost = 0
+        for r in runs[rb:re_].tolist():
+            kb, ke, full, _ = r
+            assert 0 <= kb < ke <= Lk
+            keys[kb:ke] += 1
+            cost += ke - kb
+            if full:
+                assert (ke - kb) % tn == 0
+                assert vis[t0:t0 + rows, kb:ke].all(), (it, r)
+        assert (keys <= 1).all(), "a key appears in two runs"
+        # every visible key of every row lies inside a run
+        outside = vis[t0:t0 + rows][:, keys == 0]
+        assert not outside.any(), it
+        costs.append((1 + cost) * rows)
+    assert costs == sorted(costs, reverse=True)
+    if accumulate:
+        assert (covered <= 1).all()
+        # rows without any item see no key
+        assert not vis[covered == 0].any()
+    else:
+        assert (covered == 1).all()
+
+
+CASES = [
+    # impl, S, N, b, causal, window, n_sink, cu
+    ("zigzag", 1024, 4, 1, True, 0, 0, None),
+    ("zigzag", 2 * 4 * 200, 4, 1, True, 0, 0, None),      # chunk 200: ragged tiles
+    ("stripe", 2048, 8, 1, True, 0, 0, None),
+    ("stripe", 1536, 4, 3, True, 0, 0, None),
+    ("basic", 8192, 8, 1, False, 1000, 0, None),
+    ("basic", 8192, 4, 1, False, 1000, 4, [0, 512, 4000, 8192]),
+    ("basic", 4096, 4, 1, True, 0, 0, [0, 1, 700, 701, 2900, 4096]),
+    ("basic", 4096, 4, 1, False, 0, 0, [0, 1500, 4096]),
+    ("basic", 3000, 3, 1, False, 130, 7, [0, 100, 1234, 3000]),
+    ("zigzag", 1200, 3, 1, False, 0, 0, None),
+    ("zigzag", 3072, 4, 1, False, 300, 2, None),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_planner_against_oracle_visibility(case, accumulate):
+    impl, S, N, b, causal, window, n_sink, cu = case
+    L = S // N
+    for i in range(N):
+        for j in {0, i, (i + 1) % N, N - 1}:
+            qpos = torch.tensor(ix.rank_positions(impl, S, N, i, b))
+            kpos = torch.tensor(ix.rank_positions(impl, S, N, j, b))
+            vis = visibility(qpos, kpos, causal=causal, window=window, n_sink=n_sink, cu_seqlens=cu)
+            items, runs, tm, tn = usp.plan_block(
+                L, L, 128, mask="positional", qmap=usp.posmap(impl, N, i, S, b), kmap=usp.posmap(impl, N, j, S, b),
+                causal=causal, window=window, n_sink=n_sink, cu_seqlens=cu, accumulate=accumulate)
+            assert tm == 128 and tn == 64
+            _check_plan(L, L, qpos, kpos, vis, accumulate, items, runs, tn)
+
+
+@pytest.mark.parametrize("mask", ["full", "causal", "causal_strict", "empty"])
+@pytest.mark.parametrize("Lq,Lk", [(256, 256), (300, 300), (200, 77), (64, 1000)])
+def test_planner_explicit_classes(mask, Lq, Lk):
+    t = torch.arange(Lq)[:, None]
+    u = torch.arange(Lk)[None, :]
+    vis = {"full": torch.ones(Lq, Lk, dtype=torch.bool), "causal": u <= t, "causal_strict": u < t,
+           "empty": torch.zeros(Lq, Lk, dtype=torch.bool)}[mask]
+    for acc in (False, True):
+        items, runs, tm, tn = usp.plan_block(Lq, Lk, 64, mask=mask, accumulate=acc)
+        _check_plan(Lq, Lk, None, None, vis, acc, items, runs, tn)
+
+
+def test_planner_full_tiles_dominate_large_causal():
+    # the bulk of a long causal zigzag block is planned as full tiles (no per-element mask)
+    S, N = 16384, 4
+    items, runs, tm, tn = usp.plan_block(S // N, S // N, 128, qmap=usp.posmap("zigzag", N, 1, S),
+                                         kmap=usp.posmap("zigzag", N, 1, S), causal=True)
+    r = runs.tolist()
+    full = sum(x[1] - x[0] for x in r if x[2])
+    part = sum(x[1] - x[0] for x in r if not x[2])
+    # 32 q-tiles of 128 rows: full keys sum to 128*(0+...+31), one partial diagonal run each
+    assert part == 32 * 128 and full == 128 * 31 * 32 // 2

@@ -1,0 +1,315 @@
+"""Python binding of libusp: ring / zigzag / striped / Ulysses-hybrid attention on gfx950.
+
+Argument marshalling only: every step runs in the HIP kernels of libusp.so,
+which must be built (``python -m ulysses_sequence_attention_zigzag_amd.build``).
+Calls raise ``UspError`` on any non-OK status and ``RuntimeError`` when the
+library is missing -- there is no fallback path.  torch supplies device
+memory and the current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libusp.so")
+
+IMPL = {"basic": 0, "zigzag": 1, "stripe": 2}
+MASK = {"empty": 0, "full": 1, "causal": 2, "causal_strict": 3, "positional": 4}
+DT = {torch.bfloat16: 0, torch.float32: 1}
+STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "HIP"}
+
+
+class UspError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"usp error {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class PosMap(ctypes.Structure):
+    _fields_ = [("impl", ctypes.c_int32), ("ring_degree", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("stripe_block", ctypes.c_int32), ("S_global", ctypes.c_int64)]
+
+
+class RingArgs(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+                ("B", ctypes.c_int64), ("S", ctypes.c_int64), ("Hq", ctypes.c_int64),
+                ("Hkv", ctypes.c_int64), ("D", ctypes.c_int64),
+                ("softmax_scale", ctypes.c_float),
+                ("causal", ctypes.c_int32), ("window", ctypes.c_int32), ("n_sink", ctypes.c_int32),
+                ("cu_seqlens_dev", ctypes.c_void_p), ("cu_seqlens_host", ctypes.c_void_p),
+                ("nseq", ctypes.c_int32), ("impl", ctypes.c_int32), ("ring_degree", ctypes.c_int32),
+                ("ulysses_degree", ctypes.c_int32), ("stripe_block", ctypes.c_int32),
+                ("rank", ctypes.c_int32), ("ulysses_rank", ctypes.c_int32),
+                ("input_order", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("merge_mode", ctypes.c_int32)]
+
+
+_lib = None
+
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int
+_P = ctypes.c_void_p
+_SIGS = {
+    "usp_last_error": ([], ctypes.c_char_p),
+    "usp_version": ([], ctypes.c_char_p),
+    "usp_permute": ([_P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P], _I32),
+    "usp_ulysses_relayout": ([_P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P], _I32),
+    "usp_block_attn_fwd": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, ctypes.c_float, _I32,
+                            ctypes.POINTER(PosMap), ctypes.POINTER(PosMap), _I32, _I32, _I32, _P, _P, _I32,
+                            _I32, _I32, _P], _I32),
+    "usp_lse_merge": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P], _I32),
+    "usp_ring_fwd_workspace_size": ([ctypes.POINTER(RingArgs)], ctypes.c_size_t),
+    "usp_ring_fwd": ([ctypes.POINTER(RingArgs), _P, ctypes.c_size_t, _P], _I32),
+    "usp_plan_block": ([_I64, _I64, _I64, _I32, ctypes.POINTER(PosMap), ctypes.POINTER(PosMap), _I32, _I32,
+                        _I32, _P, _I32, _I32, _P, _I64, _P, _I64, ctypes.POINTER(_I64),
+                        ctypes.POINTER(_I64), ctypes.POINTER(ctypes.c_int32),
+                        ctypes.POINTER(ctypes.c_int32)], _I32),
+    "usp_timing_enable": ([_I32], _I32),
+    "usp_timing_reset": ([], _I32),
+    "usp_timing_read": ([_I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64)], _I32),
+}
+EXPORTS = tuple(_SIGS)
+
+
+def lib():
+    """The loaded libusp.so (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run python -m ulysses_sequence_attention_zigzag_amd.build")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = handle
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise UspError(status, lib().usp_last_error().decode())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t: torch.Tensor, dtype=None, name="tensor"):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def posmap(impl: str, ring_degree: int, rank: int, S_global: int, stripe_block: int = 1) -> PosMap:
+    return PosMap(IMPL[impl], ring_degree, rank, stripe_block, S_global)
+
+
+# ---------------------------------------------------------------- permute
+def permute(x: torch.Tensor, impl: str, ring_degree: int, *, ulysses_degree: int = 1, stripe_block: int = 1,
+            rank: int = -1, inverse: bool = False, dim: int = 1, S_global: Optional[int] = None,
+            out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Token reorder along ``dim`` (see usp_permute).  rank >= 0 extracts
+    (or, with inverse, scatters back) global USP rank ``rank``'s shard."""
+    dim = dim % x.dim()
+    outer = 1
+    for s in x.shape[:dim]:
+        outer *= s
+    inner = 1
+    for s in x.shape[dim + 1:]:
+        inner *= s
+    if rank >= 0 and inverse:
+        S = S_global
+        if S is None:
+            raise ValueError("inverse extract needs S_global")
+    else:
+        S = x.shape[dim]
+    if out is None:
+        shape = list(x.shape)
+        if rank >= 0:
+            shape[dim] = S if inverse else S // ring_degree // ulysses_degree
+        out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    _check(lib().usp_permute(_dev(x, name="in"), _dev(out, x.dtype, "out"), outer, S, inner, DT[x.dtype],
+                             IMPL[impl], ring_degree, ulysses_degree, stripe_block, rank, int(inverse),
+                             _stream(stream)))
+    return out
+
+
+def ulysses_relayout(shards: Sequence[torch.Tensor], local: torch.Tensor, ulysses_rank: int, direction: int,
+                     stream=None) -> None:
+    """seq -> head (direction 0: shards -> local) or head -> seq (1)."""
+    ud = len(shards)
+    B, Ls, H, D = shards[0].shape
+    arr = (ctypes.c_void_p * ud)(*[_dev(s, local.dtype, "shard").value for s in shards])
+    _check(lib().usp_ulysses_relayout(ctypes.cast(arr, ctypes.c_void_p), _dev(local, name="local"), B, Ls, H, D,
+                                      DT[local.dtype], ud, ulysses_rank, direction, _stream(stream)))
+
+
+# ---------------------------------------------------------------- attention
+def _cu(cu_seqlens, device):
+    if cu_seqlens is None:
+        return None, None, 0, None
+    host = torch.tensor(list(cu_seqlens) if not torch.is_tensor(cu_seqlens) else cu_seqlens.tolist(),
+                        dtype=torch.int32)
+    dev = host.to(device)
+    return dev, host, host.numel() - 1, (dev, host)
+
+
+def block_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, mask: str = "positional",
+                   qmap: Optional[PosMap] = None, kmap: Optional[PosMap] = None, causal: bool = False,
+                   window: int = 0, n_sink: int = 0, cu_seqlens=None, softmax_scale: float = 0.0,
+                   out_dtype=torch.float32, accumulate: bool = False, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """One ring step (usp_block_attn_fwd).  q [B,Lq,Hq,D], k/v [B,Lk,Hkv,D] bf16."""
+    B, Lq, Hq, D = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    if out is None:
+        out = torch.empty((B, Lq, Hq, D), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    cu_dev, cu_host, nseq, keep = _cu(cu_seqlens, q.device)
+    _check(lib().usp_block_attn_fwd(
+        _dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"),
+        _dev(out, out_dtype, "out"), _dev(lse, torch.float32, "lse"), B, Lq, Lk, Hq, Hkv, D,
+        float(softmax_scale), MASK[mask], ctypes.byref(qmap) if qmap else None,
+        ctypes.byref(kmap) if kmap else None, int(causal), int(window), int(n_sink),
+        ctypes.c_void_p(cu_dev.data_ptr()) if cu_dev is not None else None,
+        ctypes.c_void_p(cu_host.data_ptr()) if cu_host is not None else None, nseq,
+        DT[out.dtype], int(accumulate), _stream(stream)))
+    if keep is not None:
+        torch.cuda.current_stream().synchronize()  # cu_seqlens copies must outlive the launch
+    return out, lse
+
+
+def lse_merge(out_acc: torch.Tensor, lse_acc: torch.Tensor, out_part: torch.Tensor, lse_part: torch.Tensor,
+              row_begin: int = 0, row_end: Optional[int] = None, stream=None) -> None:
+    """In-place merge of (out_part, lse_part) into (out_acc, lse_acc)."""
+    B, L, H, D = out_acc.shape
+    row_end = L if row_end is None else row_end
+    _check(lib().usp_lse_merge(_dev(out_acc, torch.float32, "out_acc"), _dev(lse_acc, torch.float32, "lse_acc"),
+                               _dev(out_part, torch.float32, "out_part"), _dev(lse_part, torch.float32, "lse_part"),
+                               B, L, H, D, row_begin, row_end, _stream(stream)))
+
+
+class RingCall:
+    """A prepared usp_ring_fwd call: arguments, outputs and workspace are
+    allocated once; ``run()`` only enqueues the kernels."""
+
+    def __init__(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, impl: str, ring_degree: int,
+                 ulysses_degree: int = 1, stripe_block: int = 1, causal: bool = False, window: int = 0,
+                 n_sink: int = 0, cu_seqlens=None, softmax_scale: float = 0.0, rank: int = -1,
+                 ulysses_rank: int = 0, input_order: str = "natural", out_dtype=torch.float32,
+                 merge_mode: int = 0):
+        varlen = cu_seqlens is not None
+        if varlen:
+            S, Hq, D = q.shape
+            B = 1
+            Hkv = k.shape[1]
+        else:
+            B, S, Hq, D = q.shape
+            Hkv = k.shape[2]
+        N, ud = ring_degree, ulysses_degree
+        L = S // N
+        Hl = Hq // ud
+        if rank < 0:
+            out_shape = (S, Hq, D) if varlen else (B, S, Hq, D)
+            lse_shape = (Hq, S) if varlen else (B, Hq, S)
+        else:
+            out_shape = (L, Hl, D) if varlen else (B, L, Hl, D)
+            lse_shape = (Hl, L) if varlen else (B, Hl, L)
+        self.q, self.k, self.v = q, k, v
+        self.out = torch.empty(out_shape, dtype=out_dtype, device=q.device)
+        self.lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
+        cu_dev, cu_host, nseq, _ = _cu(cu_seqlens, q.device)
+        self._cu = (cu_dev, cu_host)
+        a = RingArgs()
+        a.q, a.k, a.v = (_dev(q, torch.bfloat16, "q").value, _dev(k, torch.bfloat16, "k").value,
+                         _dev(v, torch.bfloat16, "v").value)
+        a.out, a.lse = self.out.data_ptr(), self.lse.data_ptr()
+        a.B, a.S, a.Hq, a.Hkv, a.D = B, S, Hq, Hkv, D
+        a.softmax_scale = float(softmax_scale)
+        a.causal, a.window, a.n_sink = int(causal), int(window), int(n_sink)
+        a.cu_seqlens_dev = cu_dev.data_ptr() if cu_dev is not None else None
+        a.cu_seqlens_host = cu_host.data_ptr() if cu_host is not None else None
+        a.nseq = nseq
+        a.impl, a.ring_degree, a.ulysses_degree, a.stripe_block = IMPL[impl], N, ud, stripe_block
+        a.rank, a.ulysses_rank = rank, ulysses_rank
+        a.input_order = {"natural": 0, "permuted": 1}[input_order]
+        a.out_dtype = DT[out_dtype]
+        a.merge_mode = merge_mode
+        self.args = a
+        nbytes = lib().usp_ring_fwd_workspace_size(ctypes.byref(a))
+        if nbytes == 0:
+            # either nothing is needed or the arguments are invalid: let the call report which
+            self.workspace = None
+        else:
+            self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+        self.ws_bytes = nbytes
+
+    def run(self, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+        ws = ctypes.c_void_p(self.workspace.data_ptr()) if self.workspace is not None else None
+        _check(lib().usp_ring_fwd(ctypes.byref(self.args), ws, self.ws_bytes, _stream(stream)))
+        return self.out, self.lse
+
+
+def ring_fwd(q, k, v, **kw) -> Tuple[torch.Tensor, torch.Tensor]:
+    """All ring steps on one device (usp_ring_fwd); see RingCall for arguments."""
+    call = RingCall(q, k, v, **kw)
+    out = call.run()
+    torch.cuda.current_stream().synchronize()  # the workspace is released on return
+    return out
+
+
+# ---------------------------------------------------------------- timing
+KERNEL_CLASSES = {"attn": 0, "permute": 1, "relayout": 2, "merge": 3}
+
+
+def timing_enable(on: bool = True) -> None:
+    _check(lib().usp_timing_enable(int(on)))
+
+
+def timing_reset() -> None:
+    _check(lib().usp_timing_reset())
+
+
+def timing_read(kernel_class: str) -> Tuple[float, int]:
+    """(total milliseconds, launches) recorded for one kernel class."""
+    ms = ctypes.c_double(0.0)
+    n = _I64(0)
+    _check(lib().usp_timing_read(KERNEL_CLASSES[kernel_class], ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
+
+
+# ---------------------------------------------------------------- planner
+def plan_block(Lq: int, Lk: int, D: int = 128, *, mask: str = "positional", qmap: Optional[PosMap] = None,
+               kmap: Optional[PosMap] = None, causal: bool = False, window: int = 0, n_sink: int = 0,
+               cu_seqlens=None, accumulate: bool = False):
+    """Host-only tile plan (usp_plan_block): (items [n,8] int32, runs [m,4] int32, tile_m, tile_n)."""
+    L = lib()
+    cu_host = None if cu_seqlens is None else torch.tensor(list(cu_seqlens), dtype=torch.int32)
+    nseq = 0 if cu_host is None else cu_host.numel() - 1
+    cu_p = ctypes.c_void_p(cu_host.data_ptr()) if cu_host is not None else None
+    ni, nr = _I64(0), _I64(0)
+    tm, tn = ctypes.c_int32(0), ctypes.c_int32(0)
+    qm = ctypes.byref(qmap) if qmap else None
+    km = ctypes.byref(kmap) if kmap else None
+    _check(L.usp_plan_block(Lq, Lk, D, MASK[mask], qm, km, int(causal), int(window), int(n_sink), cu_p, nseq,
+                            int(accumulate), None, 0, None, 0, ctypes.byref(ni), ctypes.byref(nr),
+                            ctypes.byref(tm), ctypes.byref(tn)))
+    items = torch.zeros((max(1, ni.value), 8), dtype=torch.int32)
+    runs = torch.zeros((max(1, nr.value), 4), dtype=torch.int32)
+    _check(L.usp_plan_block(Lq, Lk, D, MASK[mask], qm, km, int(causal), int(window), int(n_sink), cu_p, nseq,
+                            int(accumulate), ctypes.c_void_p(items.data_ptr()), ni.value,
+                            ctypes.c_void_p(runs.data_ptr()), nr.value, ctypes.byref(ni), ctypes.byref(nr),
+                            ctypes.byref(tm), ctypes.byref(tn)))
+    return items[:ni.value], runs[:nr.value], tm.value, tn.value

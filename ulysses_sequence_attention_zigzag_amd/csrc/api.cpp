@@ -1,0 +1,680 @@
+// C ABI of libusp: argument validation, tile-plan cache, and the virtual
+// ring driver.  Every entry point validates everything on the host before
+// enqueueing anything; see include/usp.h for the contract of each call.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "usp_internal.h"
+
+namespace usp {
+
+namespace {
+thread_local std::string g_err;
+}
+
+void set_error(const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+}
+
+namespace {
+
+#define USP_CHECK(cond, code, ...) \
+  do {                             \
+    if (!(cond)) {                 \
+      set_error(__VA_ARGS__);      \
+      return (code);               \
+    }                              \
+  } while (0)
+
+constexpr int64_t kMaxI32 = 0x7fffffff;
+
+// ------------------------------------------------------------ plan cache
+std::mutex g_plan_mu;
+std::unordered_map<std::string, DevicePlan> g_plans;
+
+// Returns the device copy of the plan cached under `key`; builds it with
+// `build` and uploads it on a miss (one synchronous copy).
+template <typename F>
+usp_status device_plan(const std::string& key_in, F&& build, DevicePlan* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    set_error("hipGetDevice failed");
+    return USP_ERR_HIP;
+  }
+  const std::string key = std::to_string(dev) + "|" + key_in;
+  std::lock_guard<std::mutex> lock(g_plan_mu);
+  auto f = g_plans.find(key);
+  if (f != g_plans.end()) {
+    *out = f->second;
+    return USP_OK;
+  }
+  Plan plan;
+  build(plan);
+  finalize_plan(plan);
+  USP_CHECK(plan.items.size() <= (size_t)kMaxI32 && plan.runs.size() <= (size_t)kMaxI32,
+            USP_ERR_UNSUPPORTED, "tile plan too large");
+  DevicePlan dp;
+  dp.n_items = (int32_t)plan.items.size();
+  dp.n_runs = (int32_t)plan.runs.size();
+  const size_t ib = std::max<size_t>(1, plan.items.size()) * sizeof(WorkItem);
+  const size_t rb = std::max<size_t>(1, plan.runs.size()) * sizeof(Run);
+  if (hipMalloc(reinterpret_cast<void**>(&dp.items), ib) != hipSuccess ||
+      hipMalloc(reinterpret_cast<void**>(&dp.runs), rb) != hipSuccess) {
+    if (dp.items) (void)hipFree(dp.items);
+    set_error("hipMalloc of tile plan failed");
+    return USP_ERR_HIP;
+  }
+  hipError_t e = hipSuccess;
+  if (!plan.items.empty())
+    e = hipMemcpy(dp.items, plan.items.data(), plan.items.size() * sizeof(WorkItem), hipMemcpyHostToDevice);
+  if (e == hipSuccess && !plan.runs.empty())
+    e = hipMemcpy(dp.runs, plan.runs.data(), plan.runs.size() * sizeof(Run), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(dp.items);
+    (void)hipFree(dp.runs);
+    set_error("upload of tile plan failed: %s", hipGetErrorString(e));
+    return USP_ERR_HIP;
+  }
+  g_plans.emplace(key, dp);
+  *out = dp;
+  return USP_OK;
+}
+
+std::string cu_key(const int32_t* cu, int nseq) {
+  std::string s;
+  if (!cu) return "-";
+  for (int i = 0; i <= nseq; ++i) s += std::to_string(cu[i]) + ",";
+  return s;
+}
+
+// ------------------------------------------------------------ validation
+usp_status check_layout(int impl, int64_t S, int N, int b) {
+  USP_CHECK(impl >= USP_RING_BASIC && impl <= USP_RING_STRIPE, USP_ERR_INVALID_ARG,
+            "impl must be 0 (basic), 1 (zigzag) or 2 (stripe), got %d", impl);
+  USP_CHECK(N >= 1, USP_ERR_INVALID_ARG, "ring_degree must be >= 1, got %d", N);
+  USP_CHECK(S >= 1 && S <= (int64_t)1 << 30, USP_ERR_INVALID_ARG,
+            "sequence length %lld out of range [1, 2^30]", (long long)S);
+  if (impl == USP_RING_BASIC)
+    USP_CHECK(S % N == 0, USP_ERR_INVALID_ARG, "basic layout needs S %% N == 0 (S=%lld, N=%d)", (long long)S, N);
+  if (impl == USP_RING_ZIGZAG)
+    USP_CHECK(S % (2 * N) == 0, USP_ERR_INVALID_ARG, "zigzag layout needs S %% 2N == 0 (S=%lld, N=%d)", (long long)S, N);
+  if (impl == USP_RING_STRIPE) {
+    USP_CHECK(b >= 1, USP_ERR_INVALID_ARG, "stripe_block must be >= 1, got %d", b);
+    USP_CHECK(S % ((int64_t)N * b) == 0, USP_ERR_INVALID_ARG,
+              "stripe layout needs S %% (N*b) == 0 (S=%lld, N=%d, b=%d)", (long long)S, N, b);
+  }
+  return USP_OK;
+}
+
+usp_status check_cu(const int32_t* cu_host, int nseq, int64_t total) {
+  USP_CHECK(nseq >= 1, USP_ERR_INVALID_ARG, "nseq must be >= 1 with cu_seqlens");
+  USP_CHECK(cu_host[0] == 0, USP_ERR_INVALID_ARG, "cu_seqlens[0] must be 0");
+  for (int i = 0; i < nseq; ++i)
+    USP_CHECK(cu_host[i + 1] >= cu_host[i], USP_ERR_INVALID_ARG, "cu_seqlens must be non-decreasing");
+  USP_CHECK(cu_host[nseq] == total, USP_ERR_INVALID_ARG,
+            "cu_seqlens[nseq] (%d) must equal the total length (%lld)", cu_host[nseq], (long long)total);
+  return USP_OK;
+}
+
+PosMap make_map(const usp_posmap& m) {
+  PosMap p;
+  p.kind = m.impl;
+  p.N = m.ring_degree;
+  p.rank = m.rank;
+  p.b = m.impl == USP_RING_STRIPE ? m.stripe_block : 1;
+  p.L = (int32_t)(m.S_global / m.ring_degree);
+  p.offset = 0;
+  return p;
+}
+
+PosMap affine_map(int32_t L, int32_t offset) {
+  PosMap p;
+  p.kind = MAP_AFFINE;
+  p.N = 1;
+  p.rank = 0;
+  p.b = 1;
+  p.L = L;
+  p.offset = offset;
+  return p;
+}
+
+struct BlockMaskSetup {
+  PosMap qmap, kmap;
+  MaskSpec ms;
+  bool empty = false;
+};
+
+usp_status setup_block_mask(int64_t Lq, int64_t Lk, usp_mask_class mask, const usp_posmap* qmap,
+                            const usp_posmap* kmap, int causal, int window, int n_sink,
+                            const int32_t* cu_host, int nseq, int64_t B, BlockMaskSetup* out) {
+  BlockMaskSetup s;
+  s.ms.causal = causal ? 1 : 0;
+  s.ms.window = window;
+  s.ms.n_sink = n_sink;
+  s.ms.nseq = 0;
+  USP_CHECK(window >= 0, USP_ERR_INVALID_ARG, "window must be >= 0, got %d", window);
+  USP_CHECK(n_sink >= 0, USP_ERR_INVALID_ARG, "n_sink must be >= 0, got %d", n_sink);
+  switch (mask) {
+    case USP_MASK_EMPTY:
+    case USP_MASK_FULL:
+    case USP_MASK_CAUSAL:
+    case USP_MASK_CAUSAL_STRICT:
+      USP_CHECK(!causal && window == 0 && n_sink == 0 && !cu_host, USP_ERR_INVALID_ARG,
+                "explicit mask classes take no causal/window/n_sink/cu_seqlens");
+      s.qmap = affine_map((int32_t)Lq, 0);
+      s.kmap = affine_map((int32_t)Lk, mask == USP_MASK_CAUSAL_STRICT ? 1 : 0);
+      s.ms.causal = (mask == USP_MASK_CAUSAL || mask == USP_MASK_CAUSAL_STRICT) ? 1 : 0;
+      s.ms.S = (int32_t)(std::max(Lq, Lk) + 1);
+      s.empty = mask == USP_MASK_EMPTY;
+      break;
+    case USP_MASK_POSITIONAL: {
+      USP_CHECK(qmap && kmap, USP_ERR_INVALID_ARG, "POSITIONAL mask needs qmap and kmap");
+      usp_status st = check_layout(qmap->impl, qmap->S_global, qmap->ring_degree, qmap->stripe_block);
+      if (st != USP_OK) return st;
+      USP_CHECK(qmap->impl == kmap->impl && qmap->ring_degree == kmap->ring_degree &&
+                    qmap->S_global == kmap->S_global &&
+                    (qmap->impl != USP_RING_STRIPE || qmap->stripe_block == kmap->stripe_block),
+                USP_ERR_INVALID_ARG, "qmap and kmap must describe the same layout");
+      USP_CHECK(qmap->rank >= 0 && qmap->rank < qmap->ring_degree && kmap->rank >= 0 &&
+                    kmap->rank < kmap->ring_degree,
+                USP_ERR_INVALID_ARG, "posmap rank out of range");
+      const int64_t L = qmap->S_global / qmap->ring_degree;
+      USP_CHECK(Lq == L && Lk == L, USP_ERR_INVALID_ARG,
+                "POSITIONAL mask needs Lq == Lk == S/N (%lld), got %lld, %lld", (long long)L,
+                (long long)Lq, (long long)Lk);
+      s.qmap = make_map(*qmap);
+      s.kmap = make_map(*kmap);
+      s.ms.S = (int32_t)qmap->S_global;
+      if (cu_host) {
+        USP_CHECK(B == 1, USP_ERR_INVALID_ARG, "varlen (cu_seqlens) needs B == 1");
+        USP_CHECK(qmap->impl == USP_RING_BASIC, USP_ERR_UNSUPPORTED,
+                  "varlen is supported with the basic layout only");
+        st = check_cu(cu_host, nseq, qmap->S_global);
+        if (st != USP_OK) return st;
+        s.ms.nseq = nseq;
+      }
+      break;
+    }
+    default:
+      USP_CHECK(false, USP_ERR_INVALID_ARG, "unknown mask class %d", (int)mask);
+  }
+  *out = s;
+  return USP_OK;
+}
+
+std::string map_key(const PosMap& m) {
+  char buf[96];
+  snprintf(buf, sizeof(buf), "%d.%d.%d.%d.%d.%d", m.kind, m.N, m.rank, m.b, m.L, m.offset);
+  return buf;
+}
+
+std::string mask_key(const MaskSpec& ms) {
+  char buf[96];
+  snprintf(buf, sizeof(buf), "c%d.w%d.s%d.n%d.S%d", ms.causal, ms.window, ms.n_sink, ms.nseq, ms.S);
+  return buf;
+}
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+}  // namespace usp
+
+using namespace usp;
+
+extern "C" {
+
+const char* usp_last_error(void) { return g_err.c_str(); }
+
+const char* usp_version(void) { return "usp-gfx950 0.1"; }
+
+usp_status usp_permute(const void* in, void* out, int64_t outer, int64_t S, int64_t inner,
+                       usp_dtype dt, usp_ring_impl impl, int ring_degree, int ulysses_degree,
+                       int stripe_block, int rank, int inverse, void* stream) {
+  USP_CHECK(in && out, USP_ERR_INVALID_ARG, "null tensor pointer");
+  USP_CHECK(outer >= 0 && inner >= 1, USP_ERR_INVALID_ARG, "bad outer/inner sizes");
+  USP_CHECK(dt == USP_DT_BF16 || dt == USP_DT_F32, USP_ERR_INVALID_ARG, "bad dtype %d", (int)dt);
+  usp_status st = check_layout(impl, S, ring_degree, stripe_block);
+  if (st != USP_OK) return st;
+  USP_CHECK(ulysses_degree >= 1, USP_ERR_INVALID_ARG, "ulysses_degree must be >= 1");
+  const int64_t L = S / ring_degree;
+  USP_CHECK(L % ulysses_degree == 0, USP_ERR_INVALID_ARG,
+            "rows per ring rank (%lld) not divisible by ulysses_degree %d", (long long)L, ulysses_degree);
+  USP_CHECK(rank >= -1 && rank < ring_degree * ulysses_degree, USP_ERR_INVALID_ARG,
+            "rank %d out of range [-1, %d)", rank, ring_degree * ulysses_degree);
+  USP_CHECK(outer * S <= kMaxI32 * 4, USP_ERR_UNSUPPORTED, "tensor too large");
+  const int64_t eb = dt == USP_DT_BF16 ? 2 : 4;
+  const char* ib = static_cast<const char*>(in);
+  const char* ob = static_cast<const char*>(out);
+  const int64_t Sout = rank < 0 ? S : (inverse ? S : L / ulysses_degree);
+  const int64_t Sin = rank < 0 ? S : (inverse ? L / ulysses_degree : S);
+  const int64_t in_bytes = outer * Sin * inner * eb, out_bytes = outer * Sout * inner * eb;
+  USP_CHECK(ib + in_bytes <= ob || ob + out_bytes <= ib, USP_ERR_INVALID_ARG,
+            "permute is out-of-place: in and out overlap");
+  GatherSpec gs;
+  gs.impl = impl;
+  gs.N = ring_degree;
+  gs.ud = ulysses_degree;
+  gs.b = impl == USP_RING_STRIPE ? stripe_block : 1;
+  gs.g = rank < 0 ? 0 : rank;
+  gs.L = (int32_t)L;
+  gs.S = (int32_t)S;
+  gs.kind = rank < 0 ? (inverse ? G_UNPERMUTE : G_PERMUTE) : (inverse ? G_INSERT : G_EXTRACT);
+  return launch_permute(in, out, outer, Sin, Sout, inner * eb, gs, as_stream(stream));
+}
+
+usp_status usp_ulysses_relayout(void* const* shards, void* local, int64_t B, int64_t S_shard,
+                                int64_t H, int64_t D, usp_dtype dt, int ulysses_degree,
+                                int ulysses_rank, int direction, void* stream) {
+  USP_CHECK(shards && local, USP_ERR_INVALID_ARG, "null pointer");
+  USP_CHECK(ulysses_degree >= 1 && ulysses_degree <= 8, USP_ERR_UNSUPPORTED,
+            "ulysses_degree must be in [1, 8], got %d", ulysses_degree);
+  for (int i = 0; i < ulysses_degree; ++i) USP_CHECK(shards[i], USP_ERR_INVALID_ARG, "null shard pointer %d", i);
+  USP_CHECK(B >= 0 && S_shard >= 0 && H >= 1 && D >= 1, USP_ERR_INVALID_ARG, "bad sizes");
+  USP_CHECK(H % ulysses_degree == 0, USP_ERR_INVALID_ARG,
+            "ulysses_degree %d must divide the head count %lld", ulysses_degree, (long long)H);
+  USP_CHECK(ulysses_rank >= 0 && ulysses_rank < ulysses_degree, USP_ERR_INVALID_ARG, "ulysses_rank out of range");
+  USP_CHECK(direction == 0 || direction == 1, USP_ERR_INVALID_ARG, "direction must be 0 or 1");
+  USP_CHECK(dt == USP_DT_BF16 || dt == USP_DT_F32, USP_ERR_INVALID_ARG, "bad dtype");
+  USP_CHECK(B * S_shard * ulysses_degree <= kMaxI32, USP_ERR_UNSUPPORTED, "tensor too large");
+  const int64_t eb = dt == USP_DT_BF16 ? 2 : 4;
+  return launch_relayout(shards, local, B, S_shard, H, D, eb, ulysses_degree, ulysses_rank, direction,
+                         as_stream(stream));
+}
+
+usp_status usp_lse_merge(float* out_acc, float* lse_acc, const float* out_part, const float* lse_part,
+                         int64_t B, int64_t L, int64_t H, int64_t D, int64_t row_begin,
+                         int64_t row_end, void* stream) {
+  USP_CHECK(out_acc && lse_acc && out_part && lse_part, USP_ERR_INVALID_ARG, "null pointer");
+  USP_CHECK(B >= 0 && L >= 0 && H >= 1, USP_ERR_INVALID_ARG, "bad sizes");
+  USP_CHECK(D >= 4 && D % 4 == 0 && 256 % (D / 4) == 0, USP_ERR_UNSUPPORTED,
+            "merge supports D with D/4 dividing 256 (got %lld)", (long long)D);
+  USP_CHECK(0 <= row_begin && row_begin <= row_end && row_end <= L, USP_ERR_INVALID_ARG,
+            "row range [%lld, %lld) outside [0, %lld)", (long long)row_begin, (long long)row_end, (long long)L);
+  USP_CHECK(B * L * H <= kMaxI32, USP_ERR_UNSUPPORTED, "tensor too large");
+  return launch_lse_merge(out_acc, lse_acc, out_part, lse_part, B, L, H, D, row_begin, row_end,
+                          as_stream(stream));
+}
+
+usp_status usp_plan_block(int64_t Lq, int64_t Lk, int64_t D, usp_mask_class mask,
+                          const usp_posmap* qmap, const usp_posmap* kmap, int causal, int window,
+                          int n_sink, const int32_t* cu_seqlens_host, int nseq, int accumulate,
+                          int32_t* items, int64_t items_cap, int32_t* runs, int64_t runs_cap,
+                          int64_t* n_items, int64_t* n_runs, int32_t* tile_m, int32_t* tile_n) {
+  USP_CHECK(n_items && n_runs, USP_ERR_INVALID_ARG, "null count pointer");
+  USP_CHECK(Lq >= 0 && Lk >= 0 && Lq <= kMaxI32 / 2 && Lk <= kMaxI32 / 2, USP_ERR_INVALID_ARG, "bad Lq/Lk");
+  USP_CHECK(D == 64 || D == 128, USP_ERR_UNSUPPORTED, "head_dim must be 64 or 128, got %lld", (long long)D);
+  BlockMaskSetup su;
+  usp_status st = setup_block_mask(Lq, Lk, mask, qmap, kmap, causal, window, n_sink, cu_seqlens_host,
+                                   nseq, 1, &su);
+  if (st != USP_OK) return st;
+  Plan plan;
+  if (!su.empty) {
+    BlockSpec blk{su.qmap, su.kmap, (int32_t)Lq, (int32_t)Lk, 0, 0};
+    plan_block(blk, su.ms, cu_seqlens_host, accumulate, plan);
+  } else if (!accumulate) {
+    // EMPTY without accumulate: items with no runs write O = 0, LSE = -inf
+    for (int32_t t0 = 0; t0 < Lq; t0 += kTileM)
+      plan.items.push_back({t0, t0, std::min<int32_t>(kTileM, (int32_t)Lq - t0), 0, 0, 0, 0, 0});
+  }
+  finalize_plan(plan);
+  *n_items = (int64_t)plan.items.size();
+  *n_runs = (int64_t)plan.runs.size();
+  if (tile_m) *tile_m = kTileM;
+  if (tile_n) *tile_n = kTileN;
+  if (items) {
+    USP_CHECK(items_cap >= *n_items, USP_ERR_INVALID_ARG, "items buffer too small");
+    std::memcpy(items, plan.items.data(), plan.items.size() * sizeof(WorkItem));
+  }
+  if (runs) {
+    USP_CHECK(runs_cap >= *n_runs, USP_ERR_INVALID_ARG, "runs buffer too small");
+    std::memcpy(runs, plan.runs.data(), plan.runs.size() * sizeof(Run));
+  }
+  return USP_OK;
+}
+
+usp_status usp_block_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                              int64_t B, int64_t Lq, int64_t Lk, int64_t Hq, int64_t Hkv, int64_t D,
+                              float softmax_scale, usp_mask_class mask, const usp_posmap* qmap,
+                              const usp_posmap* kmap, int causal, int window, int n_sink,
+                              const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int nseq,
+                              usp_dtype out_dt, int accumulate, void* stream) {
+  USP_CHECK(q && k && v && out && lse, USP_ERR_INVALID_ARG, "null tensor pointer");
+  USP_CHECK(B >= 1 && Lq >= 0 && Lk >= 0 && Hq >= 1 && Hkv >= 1, USP_ERR_INVALID_ARG, "bad sizes");
+  USP_CHECK(D == 64 || D == 128, USP_ERR_UNSUPPORTED, "head_dim must be 64 or 128, got %lld", (long long)D);
+  USP_CHECK(Hq % Hkv == 0, USP_ERR_INVALID_ARG, "Hq (%lld) must be a multiple of Hkv (%lld)", (long long)Hq, (long long)Hkv);
+  USP_CHECK(out_dt == USP_DT_BF16 || out_dt == USP_DT_F32, USP_ERR_INVALID_ARG, "bad out dtype");
+  USP_CHECK(!accumulate || out_dt == USP_DT_F32, USP_ERR_INVALID_ARG, "accumulate needs an f32 output");
+  USP_CHECK((cu_seqlens_host == nullptr) == (cu_seqlens_dev == nullptr), USP_ERR_INVALID_ARG,
+            "cu_seqlens must be given on both host and device, or neither");
+  USP_CHECK(B * Lq <= kMaxI32 && B * Lk <= kMaxI32 && Lq * Hq <= kMaxI32 * 8, USP_ERR_UNSUPPORTED, "tensor too large");
+  USP_CHECK(std::isfinite(softmax_scale), USP_ERR_INVALID_ARG, "softmax_scale must be finite");
+  BlockMaskSetup su;
+  usp_status st = setup_block_mask(Lq, Lk, mask, qmap, kmap, causal, window, n_sink, cu_seqlens_host,
+                                   nseq, B, &su);
+  if (st != USP_OK) return st;
+  if (Lq == 0) return USP_OK;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)D);
+
+  std::string key = "blk|" + std::to_string(Lq) + "|" + std::to_string(Lk) + "|" + map_key(su.qmap) + "|" +
+                    map_key(su.kmap) + "|" + mask_key(su.ms) + "|" + cu_key(su.ms.nseq ? cu_seqlens_host : nullptr, nseq) +
+                    "|a" + std::to_string(accumulate) + "|e" + std::to_string(su.empty);
+  DevicePlan dp;
+  st = device_plan(key, [&](Plan& plan) {
+    if (!su.empty) {
+      BlockSpec blk{su.qmap, su.kmap, (int32_t)Lq, (int32_t)Lk, 0, 0};
+      plan_block(blk, su.ms, cu_seqlens_host, accumulate, plan);
+    } else if (!accumulate) {
+      for (int32_t t0 = 0; t0 < Lq; t0 += kTileM)
+        plan.items.push_back({t0, t0, std::min<int32_t>(kTileM, (int32_t)Lq - t0), 0, 0, 0, 0, 0});
+    }
+  }, &dp);
+  if (st != USP_OK) return st;
+
+  AttnParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.out = out;
+  p.lse = lse;
+  p.items = dp.items;
+  p.runs = dp.runs;
+  p.cu_seqlens = su.ms.nseq ? cu_seqlens_dev : nullptr;
+  p.q_batch_stride = Lq * Hq * D;
+  p.o_batch_stride = Lq * Hq * D;
+  p.kv_batch_stride = Lk * Hkv * D;
+  p.Lq_buf = (int32_t)Lq;
+  p.n_items = dp.n_items;
+  p.B = (int32_t)B;
+  p.Hq = (int32_t)Hq;
+  p.Hkv = (int32_t)Hkv;
+  p.out_f32 = out_dt == USP_DT_F32;
+  p.accumulate = accumulate ? 1 : 0;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.qmap = su.qmap;
+  p.kmap = su.kmap;
+  p.mask = su.ms;
+  return launch_attn_fwd(p, (int)D, as_stream(stream));
+}
+
+// ------------------------------------------------------------ virtual ring
+namespace {
+
+struct RingLayout {
+  bool one;          // one rank's share
+  bool need_perm;    // natural-order input with a non-basic layout
+  int64_t L, Ls;     // rows per ring rank, per Ulysses piece
+  int64_t Hq_l, Hkv_l;
+  int64_t q_rows;    // rows of the q buffer the kernel reads (per batch)
+  // workspace offsets (bytes), SIZE_MAX if unused
+  size_t off_qp, off_kp, off_vp, off_ql, off_kl, off_vl, off_oacc, off_lacc, off_opart, off_lpart;
+  size_t total;
+  bool out_is_acc;   // accumulate straight into out / lse
+};
+
+usp_status check_ring_args(const usp_ring_args* a) {
+  USP_CHECK(a, USP_ERR_INVALID_ARG, "null args");
+  USP_CHECK(a->q && a->k && a->v && a->out && a->lse, USP_ERR_INVALID_ARG, "null tensor pointer");
+  USP_CHECK(a->B >= 1 && a->Hq >= 1 && a->Hkv >= 1, USP_ERR_INVALID_ARG, "bad sizes");
+  USP_CHECK(a->D == 64 || a->D == 128, USP_ERR_UNSUPPORTED, "head_dim must be 64 or 128, got %lld", (long long)a->D);
+  USP_CHECK(a->Hq % a->Hkv == 0, USP_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
+  usp_status st = check_layout(a->impl, a->S, a->ring_degree, a->stripe_block);
+  if (st != USP_OK) return st;
+  USP_CHECK(a->ulysses_degree >= 1 && a->ulysses_degree <= 8, USP_ERR_UNSUPPORTED, "ulysses_degree must be in [1, 8]");
+  USP_CHECK(a->Hq % a->ulysses_degree == 0 && a->Hkv % a->ulysses_degree == 0, USP_ERR_INVALID_ARG,
+            "ulysses_degree %d must divide Hq (%lld) and Hkv (%lld)", a->ulysses_degree, (long long)a->Hq,
+            (long long)a->Hkv);
+  const int64_t L = a->S / a->ring_degree;
+  USP_CHECK(L % a->ulysses_degree == 0, USP_ERR_INVALID_ARG, "rows per ring rank not divisible by ulysses_degree");
+  USP_CHECK(a->rank >= -1 && a->rank < a->ring_degree, USP_ERR_INVALID_ARG, "rank %d out of range", a->rank);
+  USP_CHECK(a->ulysses_rank >= 0 && a->ulysses_rank < a->ulysses_degree, USP_ERR_INVALID_ARG, "ulysses_rank out of range");
+  USP_CHECK(a->rank >= 0 || a->ulysses_degree == 1, USP_ERR_INVALID_ARG, "all-ranks mode (rank -1) needs ulysses_degree 1");
+  USP_CHECK(a->window >= 0 && a->n_sink >= 0, USP_ERR_INVALID_ARG, "window and n_sink must be >= 0");
+  USP_CHECK(a->input_order == 0 || a->input_order == 1, USP_ERR_INVALID_ARG, "input_order must be 0 or 1");
+  USP_CHECK(a->out_dtype == USP_DT_BF16 || a->out_dtype == USP_DT_F32, USP_ERR_INVALID_ARG, "bad out dtype");
+  USP_CHECK(a->merge_mode == 0 || a->merge_mode == 1, USP_ERR_INVALID_ARG, "merge_mode must be 0 or 1");
+  USP_CHECK(std::isfinite(a->softmax_scale), USP_ERR_INVALID_ARG, "softmax_scale must be finite");
+  USP_CHECK((a->cu_seqlens_host == nullptr) == (a->cu_seqlens_dev == nullptr), USP_ERR_INVALID_ARG,
+            "cu_seqlens must be given on both host and device, or neither");
+  if (a->cu_seqlens_host) {
+    USP_CHECK(a->impl == USP_RING_BASIC, USP_ERR_UNSUPPORTED, "varlen is supported with the basic layout only");
+    USP_CHECK(a->B == 1, USP_ERR_INVALID_ARG, "varlen needs B == 1");
+    st = check_cu(a->cu_seqlens_host, a->nseq, a->S);
+    if (st != USP_OK) return st;
+  }
+  USP_CHECK(a->B * a->S <= kMaxI32, USP_ERR_UNSUPPORTED, "B*S too large");
+  return USP_OK;
+}
+
+RingLayout ring_layout(const usp_ring_args* a) {
+  RingLayout r;
+  const size_t NONE = SIZE_MAX;
+  r.one = a->rank >= 0;
+  r.need_perm = a->input_order == 0 && a->impl != USP_RING_BASIC;
+  r.L = a->S / a->ring_degree;
+  const int ud = a->ulysses_degree;
+  r.Ls = r.L / ud;
+  r.Hq_l = a->Hq / ud;
+  r.Hkv_l = a->Hkv / ud;
+  r.q_rows = r.one ? r.L : a->S;
+  r.off_qp = r.off_kp = r.off_vp = r.off_ql = r.off_kl = r.off_vl = NONE;
+  r.off_oacc = r.off_lacc = r.off_opart = r.off_lpart = NONE;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  const size_t D = (size_t)a->D, B = (size_t)a->B, S = (size_t)a->S;
+  if (r.need_perm) {
+    r.off_qp = take(B * (size_t)r.q_rows * a->Hq * D * 2);
+    r.off_kp = take(B * S * a->Hkv * D * 2);
+    r.off_vp = take(B * S * a->Hkv * D * 2);
+  }
+  if (ud > 1) {
+    r.off_ql = take(B * (size_t)r.L * r.Hq_l * D * 2);
+    r.off_kl = take(B * S * r.Hkv_l * D * 2);
+    r.off_vl = take(B * S * r.Hkv_l * D * 2);
+  }
+  // accumulate directly into out/lse when they are f32 and already in the
+  // order the kernel computes in
+  r.out_is_acc = a->out_dtype == USP_DT_F32 && (r.one || !r.need_perm);
+  if (!r.out_is_acc) {
+    r.off_oacc = take(B * (size_t)r.q_rows * r.Hq_l * D * 4);
+    r.off_lacc = take(B * (size_t)r.Hq_l * r.q_rows * 4);
+  }
+  if (a->merge_mode == 1) {
+    r.off_opart = take(B * (size_t)r.q_rows * r.Hq_l * D * 4);
+    r.off_lpart = take(B * (size_t)r.Hq_l * r.q_rows * 4);
+  }
+  r.total = off;
+  return r;
+}
+
+}  // namespace
+
+size_t usp_ring_fwd_workspace_size(const usp_ring_args* a) {
+  if (check_ring_args(a) != USP_OK) return 0;
+  return ring_layout(a).total;
+}
+
+usp_status usp_ring_fwd(const usp_ring_args* a, void* workspace, size_t ws_bytes, void* stream_) {
+  usp_status st = check_ring_args(a);
+  if (st != USP_OK) return st;
+  const RingLayout R = ring_layout(a);
+  USP_CHECK(R.total == 0 || (workspace && ws_bytes >= R.total), USP_ERR_WORKSPACE,
+            "workspace of %zu bytes needed, %zu given", R.total, workspace ? ws_bytes : (size_t)0);
+  USP_CHECK(((uintptr_t)workspace & 255) == 0, USP_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  hipStream_t stream = as_stream(stream_);
+  char* ws = static_cast<char*>(workspace);
+  const int N = a->ring_degree, ud = a->ulysses_degree, u = a->ulysses_rank;
+  const int64_t B = a->B, S = a->S, D = a->D, L = R.L;
+  const int b = a->impl == USP_RING_STRIPE ? a->stripe_block : 1;
+
+  // 1. token order: rank-major q (or ring rank r's rows), k, v
+  const uint16_t* qsrc = static_cast<const uint16_t*>(a->q);
+  const uint16_t* ksrc = static_cast<const uint16_t*>(a->k);
+  const uint16_t* vsrc = static_cast<const uint16_t*>(a->v);
+  int64_t q_batch_rows = S;   // rows between batches in the q buffer
+  int64_t q_row_off = 0;      // first row of the rank's q rows
+  if (R.need_perm) {
+    uint16_t* qp = reinterpret_cast<uint16_t*>(ws + R.off_qp);
+    uint16_t* kp = reinterpret_cast<uint16_t*>(ws + R.off_kp);
+    uint16_t* vp = reinterpret_cast<uint16_t*>(ws + R.off_vp);
+    st = usp_permute(a->k, kp, B, S, a->Hkv * D, USP_DT_BF16, (usp_ring_impl)a->impl, N, 1, b, -1, 0, stream);
+    if (st == USP_OK)
+      st = usp_permute(a->v, vp, B, S, a->Hkv * D, USP_DT_BF16, (usp_ring_impl)a->impl, N, 1, b, -1, 0, stream);
+    if (st == USP_OK)
+      st = usp_permute(a->q, qp, B, S, a->Hq * D, USP_DT_BF16, (usp_ring_impl)a->impl, N, 1, b,
+                       R.one ? a->rank : -1, 0, stream);
+    if (st != USP_OK) return st;
+    qsrc = qp;
+    ksrc = kp;
+    vsrc = vp;
+    q_batch_rows = R.q_rows;
+  } else if (R.one) {
+    q_row_off = (int64_t)a->rank * L;
+  }
+
+  // 2. Ulysses seq -> head relayout for Ulysses rank u
+  int64_t Hq_l = a->Hq, Hkv_l = a->Hkv;
+  if (ud > 1) {
+    uint16_t* ql = reinterpret_cast<uint16_t*>(ws + R.off_ql);
+    uint16_t* kl = reinterpret_cast<uint16_t*>(ws + R.off_kl);
+    uint16_t* vl = reinterpret_cast<uint16_t*>(ws + R.off_vl);
+    void* sh[8];
+    for (int up = 0; up < ud; ++up)
+      sh[up] = const_cast<uint16_t*>(qsrc) + (q_row_off + up * R.Ls) * a->Hq * D;
+    st = launch_relayout_strided(sh, ql, B, R.Ls, a->Hq, D, 2, ud, u, 0, q_batch_rows, L, stream);
+    if (st != USP_OK) return st;
+    for (int j = 0; j < N; ++j) {
+      for (int up = 0; up < ud; ++up)
+        sh[up] = const_cast<uint16_t*>(ksrc) + ((int64_t)j * L + up * R.Ls) * a->Hkv * D;
+      st = launch_relayout_strided(sh, kl + (int64_t)j * L * R.Hkv_l * D, B, R.Ls, a->Hkv, D, 2, ud, u, 0, S, S, stream);
+      if (st != USP_OK) return st;
+      for (int up = 0; up < ud; ++up)
+        sh[up] = const_cast<uint16_t*>(vsrc) + ((int64_t)j * L + up * R.Ls) * a->Hkv * D;
+      st = launch_relayout_strided(sh, vl + (int64_t)j * L * R.Hkv_l * D, B, R.Ls, a->Hkv, D, 2, ud, u, 0, S, S, stream);
+      if (st != USP_OK) return st;
+    }
+    qsrc = ql;
+    ksrc = kl;
+    vsrc = vl;
+    q_batch_rows = L;
+    q_row_off = 0;
+    Hq_l = R.Hq_l;
+    Hkv_l = R.Hkv_l;
+  }
+
+  // 3. ring steps
+  float* oacc = R.out_is_acc ? static_cast<float*>(a->out) : reinterpret_cast<float*>(ws + R.off_oacc);
+  float* lacc = R.out_is_acc ? a->lse : reinterpret_cast<float*>(ws + R.off_lacc);
+  float* opart = a->merge_mode ? reinterpret_cast<float*>(ws + R.off_opart) : nullptr;
+  float* lpart = a->merge_mode ? reinterpret_cast<float*>(ws + R.off_lpart) : nullptr;
+  const float scale = a->softmax_scale > 0.f ? a->softmax_scale : 1.0f / std::sqrt((float)D);
+
+  MaskSpec ms;
+  ms.causal = a->causal ? 1 : 0;
+  ms.window = a->window;
+  ms.n_sink = a->n_sink;
+  ms.nseq = a->cu_seqlens_host ? a->nseq : 0;
+  ms.S = (int32_t)S;
+  usp_posmap pm{a->impl, N, 0, b, S};
+  const PosMap base_map = make_map(pm);
+
+  for (int s = 0; s < N; ++s) {
+    const int acc_flag = (s > 0 && a->merge_mode == 0) ? 1 : 0;
+    const std::string key = "ring|" + map_key(base_map) + "|" + mask_key(ms) + "|" +
+                            cu_key(ms.nseq ? a->cu_seqlens_host : nullptr, a->nseq) + "|r" +
+                            std::to_string(a->rank) + "|s" + std::to_string(s) + "|a" + std::to_string(acc_flag);
+    DevicePlan dp;
+    st = device_plan(key, [&](Plan& plan) {
+      const int i0 = R.one ? a->rank : 0, i1 = R.one ? a->rank + 1 : N;
+      for (int i = i0; i < i1; ++i) {
+        const int j = ((i - s) % N + N) % N;
+        BlockSpec blk;
+        blk.qmap = base_map;
+        blk.qmap.rank = i;
+        blk.kmap = base_map;
+        blk.kmap.rank = j;
+        blk.Lq = (int32_t)L;
+        blk.Lk = (int32_t)L;
+        blk.q_row_base = R.one ? 0 : (int32_t)(i * L);
+        blk.k_row_base = (int32_t)(j * L);
+        plan_block(blk, ms, a->cu_seqlens_host, acc_flag, plan);
+      }
+    }, &dp);
+    if (st != USP_OK) return st;
+
+    AttnParams p{};
+    p.q = qsrc + q_row_off * Hq_l * D;
+    p.k = ksrc;
+    p.v = vsrc;
+    const bool to_part = a->merge_mode == 1 && s > 0;
+    p.out = to_part ? static_cast<void*>(opart) : static_cast<void*>(oacc);
+    p.lse = to_part ? lpart : lacc;
+    p.items = dp.items;
+    p.runs = dp.runs;
+    p.cu_seqlens = ms.nseq ? a->cu_seqlens_dev : nullptr;
+    p.q_batch_stride = q_batch_rows * Hq_l * D;
+    p.o_batch_stride = R.q_rows * Hq_l * D;
+    p.kv_batch_stride = S * Hkv_l * D;
+    p.Lq_buf = (int32_t)R.q_rows;
+    p.n_items = dp.n_items;
+    p.B = (int32_t)B;
+    p.Hq = (int32_t)Hq_l;
+    p.Hkv = (int32_t)Hkv_l;
+    p.out_f32 = 1;
+    p.accumulate = acc_flag;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    p.qmap = base_map;
+    p.kmap = base_map;
+    p.mask = ms;
+    st = launch_attn_fwd(p, (int)D, stream);
+    if (st != USP_OK) return st;
+    if (to_part) {
+      st = launch_lse_merge(oacc, lacc, opart, lpart, B, R.q_rows, Hq_l, D, 0, R.q_rows, stream);
+      if (st != USP_OK) return st;
+    }
+  }
+
+  // 4. finalize: dtype and order of the outputs
+  if (!R.out_is_acc) {
+    GatherSpec gs{};
+    gs.impl = R.need_perm && !R.one ? a->impl : USP_RING_BASIC;
+    gs.N = R.need_perm && !R.one ? N : 1;
+    gs.ud = 1;
+    gs.b = R.need_perm && !R.one ? b : 1;
+    gs.g = 0;
+    gs.L = (int32_t)(R.need_perm && !R.one ? L : R.q_rows);
+    gs.S = (int32_t)R.q_rows;
+    gs.kind = G_UNPERMUTE;
+    if (a->out_dtype == USP_DT_F32) {
+      st = launch_permute(oacc, a->out, B, R.q_rows, R.q_rows, Hq_l * D * 4, gs, stream);
+    } else {
+      st = launch_permute_f32_to_bf16(oacc, static_cast<uint16_t*>(a->out), B, R.q_rows, R.q_rows,
+                                      Hq_l * D, gs, stream);
+    }
+    if (st != USP_OK) return st;
+    st = launch_permute(lacc, a->lse, B * Hq_l, R.q_rows, R.q_rows, 4, gs, stream);
+    if (st != USP_OK) return st;
+  }
+  return USP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,207 @@
+// Internal definitions shared by the host planner, the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/usp.h"
+
+namespace usp {
+
+// Internal position-map kind: the three ring layouts plus an affine map
+// (p = t + offset) used for the explicit mask classes.
+enum MapKind : int32_t { MAP_BASIC = 0, MAP_ZIGZAG = 1, MAP_STRIPE = 2, MAP_AFFINE = 3 };
+
+// Global position of local row t of one virtual rank.
+//   basic : rank*L + t
+//   zigzag: chunk `rank` then chunk 2N-1-rank, c = L/2 rows each
+//   stripe: ((t/b)*N + rank)*b + t%b
+//   affine: t + offset
+struct PosMap {
+  int32_t kind;
+  int32_t N;
+  int32_t rank;
+  int32_t b;
+  int32_t L;       // rows per rank
+  int32_t offset;  // affine only
+};
+
+__host__ __device__ inline int32_t position(const PosMap& m, int32_t t) {
+  switch (m.kind) {
+    case MAP_BASIC:
+      return m.rank * m.L + t;
+    case MAP_ZIGZAG: {
+      const int32_t c = m.L >> 1;
+      return t < c ? m.rank * c + t : (2 * m.N - 1 - m.rank) * c + (t - c);
+    }
+    case MAP_STRIPE:
+      return ((t / m.b) * m.N + m.rank) * m.b + t % m.b;
+    default:
+      return t + m.offset;
+  }
+}
+
+// Monotone pieces of a rank's local rows: positions increase with t inside
+// each piece.  Zigzag has two (its two chunks); the others one.
+inline int monotone_segments(const PosMap& m, int32_t seg_lo[2], int32_t seg_hi[2]) {
+  if (m.kind == MAP_ZIGZAG) {
+    seg_lo[0] = 0;
+    seg_hi[0] = m.L / 2;
+    seg_lo[1] = m.L / 2;
+    seg_hi[1] = m.L;
+    return 2;
+  }
+  seg_lo[0] = 0;
+  seg_hi[0] = m.L;
+  return 1;
+}
+
+// Mask parameters on global positions (shared by planner and kernel).
+struct MaskSpec {
+  int32_t causal;   // causal (implied when window > 0)
+  int32_t window;   // <= 0: none
+  int32_t n_sink;
+  int32_t nseq;     // 0: not varlen (one sequence [0, S))
+  int32_t S;        // total positions (non-varlen sequence end)
+};
+
+// One work item: BM query rows of one rank against one rank's KV rows.
+struct WorkItem {
+  int32_t q_row0;     // first query row in the q buffer
+  int32_t t0;         // local row index of q_row0 within its rank
+  int32_t q_rows;     // valid rows (<= BM)
+  int32_t q_rank;
+  int32_t k_row0;     // row of local key 0 of the KV rank in the k/v buffers
+  int32_t k_rank;
+  int32_t run_begin;  // runs [run_begin, run_end)
+  int32_t run_end;
+};
+static_assert(sizeof(WorkItem) == 32, "WorkItem layout");
+
+struct Run {
+  int32_t k_begin;    // local key rows [k_begin, k_end)
+  int32_t k_end;
+  int32_t full;       // 1: every key visible to every row of the item
+  int32_t pad;
+};
+static_assert(sizeof(Run) == 16, "Run layout");
+
+// Tile shape of the attention kernel.
+constexpr int kTileM = 128;   // query rows per workgroup (4 waves x 32)
+constexpr int kTileN = 64;    // keys per iteration
+
+// Host-side plan for one launch (all ranks of one step, or one block call).
+struct Plan {
+  std::vector<WorkItem> items;
+  std::vector<Run> runs;
+};
+
+// One (q rank, kv rank) block to plan.
+struct BlockSpec {
+  PosMap qmap;
+  PosMap kmap;
+  int32_t Lq;        // rows of the q rank
+  int32_t Lk;        // rows of the kv rank
+  int32_t q_row_base;
+  int32_t k_row_base;
+};
+
+// Appends the items / runs of one block (not yet sorted).
+void plan_block(const BlockSpec& blk, const MaskSpec& ms, const int32_t* cu_host, int accumulate,
+                Plan& plan);
+// Orders items by decreasing work (stable).
+void finalize_plan(Plan& plan);
+
+// Device-resident plan, cached by key.
+struct DevicePlan {
+  WorkItem* items = nullptr;
+  Run* runs = nullptr;
+  int32_t n_items = 0;
+  int32_t n_runs = 0;
+};
+
+// Attention kernel parameters (passed by value).
+struct AttnParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  void* out;
+  float* lse;
+  const WorkItem* items;
+  const Run* runs;
+  const int32_t* cu_seqlens;
+  int64_t q_batch_stride;   // elements between batch rows of q
+  int64_t o_batch_stride;   // elements between batch rows of out
+  int64_t kv_batch_stride;  // elements between batch rows of k / v
+  int32_t Lq_buf;           // rows per batch of q / out / lse
+  int32_t n_items;
+  int32_t B;
+  int32_t Hq;
+  int32_t Hkv;
+  int32_t out_f32;
+  int32_t accumulate;
+  float scale_log2;         // softmax_scale * log2(e)
+  PosMap qmap;              // rank field overridden per item
+  PosMap kmap;
+  MaskSpec mask;
+};
+
+// Launchers (return USP_ERR_HIP on launch failure).
+usp_status launch_attn_fwd(const AttnParams& p, int D, hipStream_t stream);
+
+// Generic row gather: out row i (of n_out rows per outer slice) copies
+// row src(i) of `in`; see permute.hip for the index kinds.
+struct GatherSpec {
+  int32_t kind;           // GatherKind
+  int32_t impl;
+  int32_t N;
+  int32_t ud;
+  int32_t b;
+  int32_t g;              // extract: global rank
+  int32_t L;              // rows per ring rank
+  int32_t S;              // rows of the natural tensor
+};
+enum GatherKind : int32_t { G_PERMUTE = 0, G_UNPERMUTE = 1, G_EXTRACT = 2, G_INSERT = 3 };
+usp_status launch_permute(const void* in, void* out, int64_t outer, int64_t S_in, int64_t S_out,
+                          int64_t row_bytes, const GatherSpec& gs, hipStream_t stream);
+// Same as launch_permute with fp32 -> bf16 conversion (row_elems fp32 in, bf16 out).
+usp_status launch_permute_f32_to_bf16(const float* in, uint16_t* out, int64_t outer, int64_t S_in,
+                                      int64_t S_out, int64_t row_elems, const GatherSpec& gs,
+                                      hipStream_t stream);
+usp_status launch_relayout(void* const* shards, void* local, int64_t B, int64_t Ls, int64_t H,
+                           int64_t D, int64_t elem_bytes, int ud, int u, int direction,
+                           hipStream_t stream);
+// Same with explicit batch strides (in rows) of the shards and the local tensor.
+usp_status launch_relayout_strided(void* const* shards, void* local, int64_t B, int64_t Ls,
+                                   int64_t H, int64_t D, int64_t elem_bytes, int ud, int u,
+                                   int direction, int64_t shard_batch_rows,
+                                   int64_t local_batch_rows, hipStream_t stream);
+usp_status launch_lse_merge(float* out_acc, float* lse_acc, const float* out_part,
+                            const float* lse_part, int64_t B, int64_t L, int64_t H, int64_t D,
+                            int64_t row_begin, int64_t row_end, hipStream_t stream);
+
+void set_error(const char* fmt, ...);
+
+// Kernel classes of the timing facility (usp_timing_*).
+enum KernelClass : int { K_ATTN = 0, K_PERMUTE = 1, K_RELAYOUT = 2, K_MERGE = 3 };
+
+// Brackets one launch with hipEvents on `stream` while timing is enabled.
+class TimingScope {
+ public:
+  TimingScope(int cls, hipStream_t stream);
+  ~TimingScope();
+  TimingScope(const TimingScope&) = delete;
+  TimingScope& operator=(const TimingScope&) = delete;
+
+ private:
+  int cls_;
+  hipStream_t stream_;
+  void* start_ = nullptr;
+  void* stop_ = nullptr;
+  bool active_ = false;
+};
+
+}  // namespace usp

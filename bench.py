@@ -1,0 +1,256 @@
+"""Benchmark: one GPU's share of USP / ring attention on MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one usp_ring_fwd call over the whole hot path of the workload:
+token permutation of q/k/v (natural -> ring layout), Ulysses seq->head
+relayout, every ring step's block attention with the LSE merge, and the
+output finalisation.  Inputs are seeded bf16 N(0,1), resident in HBM before
+the timed region.  Prints one JSON line.
+
+value  = mask-adjusted attention TFLOP/s of the whole step
+         (4 * D * Hq_local * B * visible pairs / step time);
+roofline = the block-attention kernel alone: the same FLOPs over the summed
+         duration of its launches, measured with HIP events on the launch
+         stream, against the dense bf16 MFMA peak;
+cpu_baseline = the float64 oracle on a bounded sample of the same
+         workload's output rows, on this host's cores, in the same unit.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0       # HBM3E
+
+
+def visible_pairs_per_head(w, rank_rows=None) -> int:
+    """Visible (query, key) pairs per (batch row, head) of the workload's
+    output rows: closed forms of the causal / window / sink / varlen masks."""
+    N, S = w.ring_degree, w.S
+    L = S // N
+
+    def window_count(n):  # pairs of one sequence of length n
+        W, ns = w.window, w.n_sink
+        if W <= 0:
+            return n * (n + 1) // 2 if (w.causal) else n * n
+        tot = 0
+        full = min(n, W)
+        tot += full * (full + 1) // 2
+        if n > W:
+            tot += (n - W) * W
+            # sinks outside the window: p - W + 1 capped at ns, for p >= W
+            for p in range(W, n):
+                tot += min(ns, p - W + 1)
+        return tot
+
+    if w.rank < 0:
+        if w.cu_seqlens is not None:
+            cu = w.cu_seqlens
+            return sum(window_count(cu[i + 1] - cu[i]) for i in range(len(cu) - 1))
+        return window_count(S)
+    # one rank's share under a causal mask (the two one-rank workloads)
+    assert w.causal and w.window == 0 and w.cu_seqlens is None
+    if w.impl == "zigzag":
+        c = S // (2 * N)
+        return 2 * N * c * c + c
+    if w.impl == "stripe" and w.stripe_block == 1:
+        return N * L * (L - 1) // 2 + (w.rank + 1) * L
+    raise ValueError("no closed form for this workload")
+
+
+def step_bytes(w):
+    """Algorithmic HBM bytes (read + write) of the copy kernels in one step."""
+    N, ud, S, B, D = w.ring_degree, w.ulysses_degree, w.S, w.B, w.D
+    L = S // N
+    perm = 0
+    if w.impl != "basic":
+        perm += 2 * 2 * B * S * w.Hkv * D * 2                      # k and v, full permute
+        q_rows = L if w.rank >= 0 else S                          # q: rank extract or full
+        perm += 2 * B * q_rows * w.Hq * D * 2
+    relay = 0
+    if ud > 1:
+        relay += 2 * B * L * (w.Hq // ud) * D * 2                  # q
+        relay += 2 * 2 * B * S * (w.Hkv // ud) * D * 2             # k and v
+    return perm, relay
+
+
+def cpu_baseline(w, q, k, v, budget_s: float):
+    """Times the float64 oracle on a seeded sample of the workload's output rows."""
+    import torch
+    from oracle import index_ref as ix
+    from oracle.attention_ref import attention_ref
+
+    threads = torch.get_num_threads()
+    if w.rank >= 0:
+        pos = ix.rank_positions(w.impl, w.S, w.ring_degree, w.rank, w.stripe_block)
+        Hl = w.Hq // w.ulysses_degree
+        heads = list(range(w.ulysses_rank * Hl, (w.ulysses_rank + 1) * Hl))
+    else:
+        pos = list(range(w.S))
+        heads = list(range(w.Hq))
+    g = torch.Generator().manual_seed(4242)
+    order = torch.randperm(len(pos), generator=g).tolist()
+    kw = dict(softmax_scale=w.scale, causal=w.causal, window=w.window, n_sink=w.n_sink,
+              cu_seqlens=w.cu_seqlens, heads=heads)
+
+    def keys_seen(p):
+        if w.window > 0:
+            s = 0
+            if w.cu_seqlens is not None:
+                s = max(c for c in w.cu_seqlens[:-1] if c <= p)
+            off = p - s
+            return min(w.window, off + 1) + max(0, min(w.n_sink, off - w.window + 1))
+        if w.causal:
+            return p + 1
+        return w.S
+
+    done, flops, t_used, n = 0, 0.0, 0.0, 4
+    while t_used < budget_s and done < len(order):
+        rows = [pos[i] for i in order[done:done + n]]
+        t0 = time.perf_counter()
+        attention_ref(q, k, v, rows=rows, **kw)
+        dt = time.perf_counter() - t0
+        t_used += dt
+        done += len(rows)
+        bmul = 1 if w.cu_seqlens is not None else w.B
+        flops += sum(4.0 * w.D * len(heads) * bmul * keys_seen(p) for p in rows)
+        # grow the batch so the remaining budget is used in a few calls
+        per_row = dt / max(1, len(rows))
+        n = max(1, min(4096, int(0.3 * max(0.0, budget_s - t_used) / max(per_row, 1e-6))))
+    return {
+        "value": flops / t_used / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} of {len(pos)} output rows x {len(heads)} heads"
+                  f"{' x ' + str(w.B) + ' batch rows' if w.B > 1 and w.cu_seqlens is None else ''}, "
+                  f"float64 torch CPU, {t_used:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="usp_zigzag_gqa")
+    ap.add_argument("--merge-mode", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs one GPU's share only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU ring and Ulysses all-to-all are not part of this library)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import seeded_inputs as si
+    import ulysses_sequence_attention_zigzag_amd as usp
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    w = si.WORKLOADS[args.workload]
+    t0 = time.perf_counter()
+    q, k, v = w.make_inputs()
+    t_gen = time.perf_counter() - t0
+    print(f"# inputs generated in {t_gen:.1f}s", file=sys.stderr, flush=True)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    call = usp.RingCall(qd, kd, vd, impl=w.impl, ring_degree=w.ring_degree, ulysses_degree=w.ulysses_degree,
+                        stripe_block=w.stripe_block, causal=w.causal, window=w.window, n_sink=w.n_sink,
+                        cu_seqlens=w.cu_seqlens, softmax_scale=w.softmax_scale or 0.0, rank=w.rank,
+                        ulysses_rank=w.ulysses_rank, merge_mode=args.merge_mode)
+    for _ in range(args.warmup):
+        call.run()
+    torch.cuda.synchronize()
+    print("# warmup done", file=sys.stderr, flush=True)
+
+    usp.timing_reset()
+    usp.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call.run()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    usp.timing_enable(False)
+    ms_step = elapsed * 1e3 / args.steps
+    kt = {c: usp.timing_read(c) for c in ("attn", "permute", "relayout", "merge")}
+    usp.timing_reset()
+
+    Hl = w.Hq // w.ulysses_degree
+    bmul = 1 if w.cu_seqlens is not None else w.B
+    pairs = visible_pairs_per_head(w)
+    flops = 4.0 * w.D * Hl * bmul * pairs
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    attn_ms, attn_n = kt["attn"]
+    attn_ms_step = attn_ms / args.steps
+    attn_tflops = flops / (attn_ms_step * 1e-3) / 1e12 if attn_ms > 0 else None
+    perm_bytes, relay_bytes = step_bytes(w)
+    perm_ms = kt["permute"][0] / args.steps
+    relay_ms = kt["relayout"][0] / args.steps
+
+    def gbs(b, ms):
+        return round(b / (ms * 1e-3) / 1e9, 1) if ms > 0 and b > 0 else None
+
+    rec = {
+        "metric": "masked-attention TFLOPS (mask-adjusted, % of dense bf16 MFMA peak); permute/merge GB/s",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "B": w.B, "S_global": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+            "ring_impl": w.impl, "ring_degree": w.ring_degree, "ulysses_degree": w.ulysses_degree,
+            "rank": w.rank, "ulysses_rank": w.ulysses_rank, "causal": w.causal, "window": w.window,
+            "n_sink": w.n_sink, "cu_seqlens": w.cu_seqlens, "merge_mode": args.merge_mode,
+            "mask_adjusted_tflop_per_step": round(flops / 1e12, 4),
+        },
+        "pct_peak_end_to_end": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 2) if attn_tflops else None,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4) if attn_tflops else None,
+            "traffic": None,
+            "kernel": "attn_fwd_kernel<%d>" % w.D,
+            "launches_per_step": attn_n // max(1, args.steps),
+            "kernel_ms_per_step": round(attn_ms_step, 4),
+        },
+        "copy_kernels": {
+            "permute": {"bytes": perm_bytes, "ms": round(perm_ms, 4), "GB/s": gbs(perm_bytes, perm_ms),
+                        "pct_hbm": round(100 * perm_bytes / (perm_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 1)
+                        if perm_ms > 0 and perm_bytes > 0 else None},
+            "relayout": {"bytes": relay_bytes, "ms": round(relay_ms, 4), "GB/s": gbs(relay_bytes, relay_ms),
+                         "pct_hbm": round(100 * relay_bytes / (relay_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 1)
+                         if relay_ms > 0 and relay_bytes > 0 else None},
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

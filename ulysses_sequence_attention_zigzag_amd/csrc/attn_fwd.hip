@@ -47,16 +47,53 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane i supplies the address of 4 consecutive bf16 (row i/4 of a
+// 4 x 16 block, columns 4*(i%4)..+3); lane j receives column j of the block,
+// i.e. the 4 values of one column from 4 consecutive rows.
+__device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((__attribute__((address_space(3))) char*)(p)));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// Asynchronous 16-byte global -> LDS copy (gfx950 global_load_lds_dwordx4):
+// lane i's 16 bytes land at lds_wave_base + 16 * i.
+__device__ __forceinline__ void load_to_lds(const void* g, char* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(lds_wave_base), 16, 0, 0);
+}
+
+// LDS tile layout: a K or V tile is BN rows of D bf16 (D*2 bytes), rows
+// packed back to back, each row made of D/8 chunks of 16 bytes.  Chunk c of
+// row r is stored at chunk slot c ^ swz(r).  The swizzles make the two read
+// patterns hit 16 distinct 16-byte bank groups of the 256-byte LDS line:
+//   K (ds_read_b128, 16 lanes read rows r..r+15 at one chunk):
+//     swz_k(r) = (r / RPL) & (CPR - 1)
+//   V (transpose reads, 16 lanes read 4 rows x 2 chunks, 32 lanes 4 x 4):
+//     swz_v(r) = 4 * ((r / RPL) & (CPR / 4 - 1))
+// with CPR = D/8 chunks per row and RPL = 16/CPR rows per 256-byte line.
 template <int D>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnParams p) {
+struct TileLayout {
+  static constexpr int CPR = D / 8;
+  static constexpr int RPL = 16 / CPR;
+  static constexpr int ROWB = D * 2;
+  __device__ static __forceinline__ int swz_k(int r) { return (r / RPL) & (CPR - 1); }
+  __device__ static __forceinline__ int swz_v(int r) { return 4 * ((r / RPL) & (CPR / 4 - 1)); }
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
+  using TL = TileLayout<D>;
   constexpr int BN = kTileN;
   constexpr int KS = D / 16;        // k-steps of the QK^T contraction
   constexpr int DB = D / 32;        // 32-wide blocks of the output's head dim
   constexpr int NB = BN / 32;       // 32-key blocks per tile
-  constexpr int KPAD = D + 8;       // sK row stride (elements)
-  constexpr int VPAD = BN + 4;      // sV row stride (elements), V stored [d][key]
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BN * KPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[D * VPAD];
+  constexpr int TILEB = BN * D * 2; // bytes of one K or V tile
+  constexpr int LPW = TILEB / 1024 / 4;  // direct loads per wave per tensor and tile
+  constexpr int RPI = 1024 / TL::ROWB;   // tile rows per 1 KB load instruction
+  static_assert(TILEB % 4096 == 0, "tile must split into 4 waves x 1 KB loads");
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];  // K0 K1 V0 V1
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -101,8 +138,12 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnParams p) {
   for (int d = 0; d < DB; ++d)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
-  float m = -INFINITY;  // running max of scale*log2(e)*s
-  float lsum = 0.f;     // this lane's share of the running sum
+  // Running max m (log2 domain, scale folded in) and this lane's share of the
+  // running sum.  m is raised lazily: only when a tile's max exceeds it by
+  // more than kRescale, so the exponentials stay <= 2^kRescale.
+  constexpr float kRescale = 8.f;
+  float m = -INFINITY;
+  float lsum = 0.f;
 
   // Positions for per-element masks.
   PosMap qm = p.qmap;
@@ -128,28 +169,61 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnParams p) {
   const uint16_t* kbase = p.k + (int64_t)b * p.kv_batch_stride + (int64_t)it.k_row0 * kv_row_stride + hk * D;
   const uint16_t* vbase = p.v + (int64_t)b * p.kv_batch_stride + (int64_t)it.k_row0 * kv_row_stride + hk * D;
 
-  for (int ri = it.run_begin; ri < it.run_end; ++ri) {
-    const Run run = p.runs[ri];
-    for (int k0 = run.k_begin; k0 < run.k_end; k0 += BN) {
-      const int nk = min(BN, run.k_end - k0);
-      __syncthreads();  // the previous tile is no longer read
-      for (int e = tid; e < BN * D / 8; e += 256) {
-        const int row = e / (D / 8);
-        const int c8 = e - row * (D / 8);
-        uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-        if (row < nk) {
-          kv = *reinterpret_cast<const uint4*>(kbase + (int64_t)(k0 + row) * kv_row_stride + c8 * 8);
-          vv = *reinterpret_cast<const uint4*>(vbase + (int64_t)(k0 + row) * kv_row_stride + c8 * 8);
-        }
-        *reinterpret_cast<uint4*>(&sK[row * KPAD + c8 * 8]) = kv;
-        const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+  // Direct loads of one K and one V tile into LDS buffer `buf`.  Wave w fills
+  // 1 KB slices w*LPW .. w*LPW+LPW-1 of each tile; lane i of a slice writes
+  // physical (row, chunk slot) = (slice*RPI + i / CPR, i % CPR) and so loads
+  // logical chunk slot ^ swz(row) of that row.  Rows past the run's end are
+  // clamped to its last row (finite values; those keys are masked).
+  const int lrow = lane / TL::CPR;
+  const int lslot = lane % TL::CPR;
+  auto issue_tile = [&](int buf, int k0, int kend) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sV[(c8 * 8 + 2 * i) * VPAD + row] = (uint16_t)(w[i] & 0xffffu);
-          sV[(c8 * 8 + 2 * i + 1) * VPAD + row] = (uint16_t)(w[i] >> 16);
+    for (int j = 0; j < LPW; ++j) {
+      const int slice = wid * LPW + j;
+      const int row = slice * RPI + lrow;
+      const int grow = min(k0 + row, kend - 1);
+      const int ck = lslot ^ TL::swz_k(row);
+      const int cv = lslot ^ TL::swz_v(row);
+      load_to_lds(kbase + (int64_t)grow * kv_row_stride + ck * 8, smem + buf * TILEB + slice * 1024);
+      load_to_lds(vbase + (int64_t)grow * kv_row_stride + cv * 8, smem + (2 + buf) * TILEB + slice * 1024);
+    }
+  };
+
+  // Per-lane LDS read offsets (bytes within a tile).
+  //   K: row kb*32 + l32, logical chunk 2*ks + hi.
+  //   V: transpose reads of rows kb*32 + 16*half + 4*hi + 8*second + (lane%16)/4,
+  //      logical chunk 4*d + 2*((lane/16)%2) + (lane%4)/2, 8-byte half lane%2.
+  const int trow = (lane & 15) >> 2;
+  const int vrow0 = 4 * hi + trow;
+  const int vchunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int vhalf8 = (lane & 1) * 8;
+
+  int ri = it.run_begin;
+  if (ri < it.run_end) {
+    Run run = p.runs[ri];
+    int k0 = run.k_begin;
+    int buf = 0;
+    issue_tile(0, k0, run.k_end);
+    while (true) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();  // tile `buf` is in LDS; every wave is done with buffer buf^1
+
+      // next tile (uniform across the workgroup); its loads overlap this tile's math
+      int nk0 = k0 + BN;
+      int nri = ri;
+      Run nrun = run;
+      if (nk0 >= run.k_end) {
+        nri = ri + 1;
+        if (nri < it.run_end) {
+          nrun = p.runs[nri];
+          nk0 = nrun.k_begin;
         }
       }
-      __syncthreads();
+      const bool has_next = nri < it.run_end;
+      if (has_next) issue_tile(buf ^ 1, nk0, nrun.k_end);
+
+      const char* tK = smem + buf * TILEB;
+      const char* tV = smem + (2 + buf) * TILEB;
 
       // S^T[key][q] for the tile's NB blocks of 32 keys
       f32x16 s[NB];
@@ -157,9 +231,11 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnParams p) {
       for (int kb = 0; kb < NB; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+        const int row = kb * 32 + l32;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sK[(kb * 32 + l32) * KPAD + ks * 16 + hi * 8]);
+          const int slot = (2 * ks + hi) ^ TL::swz_k(row);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(tK + row * TL::ROWB + slot * 16);
           s[kb] = mfma32(a, qf[ks], s[kb]);
         }
       }
@@ -178,22 +254,25 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnParams p) {
         }
       }
 
-      // online softmax (log2 domain)
+      // online softmax (log2 domain) with lazy rescaling
       float mt = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float m_new = fmaxf(m, mt * p.scale_log2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m - m_use);
-      m = m_new;
-      lsum *= alpha;
+      mt = fmaxf(mt, __shfl_xor(mt, 32)) * p.scale_log2;
+      if (__builtin_amdgcn_readfirstlane((int)(__ballot(mt > m + kRescale) != 0ull))) {
+        const float m_new = fmaxf(m, mt);
+        // 0 when only m is -inf; lanes that have seen no visible key keep 1
+        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m - m_new);
+        m = m_new;
+        lsum *= alpha;
 #pragma unroll
-      for (int d = 0; d < DB; ++d)
+        for (int d = 0; d < DB; ++d)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+          for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+      }
+      const float m_use = (m == -INFINITY) ? 0.f : m;
 
       bf16x8 pb[NB][2];
 #pragma unroll
@@ -219,14 +298,22 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const AttnParams p) {
         for (int kb = 0; kb < NB; ++kb) {
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
-            const uint16_t* vr = &sV[(d * 32 + l32) * VPAD + kb * 32 + half * 16 + hi * 4];
-            const bf16x4 a0 = *reinterpret_cast<const bf16x4*>(vr);
-            const bf16x4 a1 = *reinterpret_cast<const bf16x4*>(vr + 8);
+            const int r0 = kb * 32 + half * 16 + vrow0;
+            const int r1 = r0 + 8;
+            const int c = 4 * d + vchunk;
+            const bf16x4 a0 = lds_read_tr(tV + r0 * TL::ROWB + ((c ^ TL::swz_v(r0)) * 16) + vhalf8);
+            const bf16x4 a1 = lds_read_tr(tV + r1 * TL::ROWB + ((c ^ TL::swz_v(r1)) * 16) + vhalf8);
             const bf16x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
             o[d] = mfma32(a, pb[kb][half], o[d]);
           }
         }
       }
+
+      if (!has_next) break;
+      ri = nri;
+      run = nrun;
+      k0 = nk0;
+      buf ^= 1;
     }
   }
 

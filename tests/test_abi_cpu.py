@@ -185,13 +185,13 @@ def test_ring_validation_and_workspace():
 
 
 # ---------------------------------------------------------------- planner
-def _check_plan(Lq, Lk, qpos, kpos, vis, accumulate, items, runs, tn):
+def _check_plan(Lq, Lk, qpos, kpos, vis, accumulate, items, runs, tn, tm=128):
     """vis: bool [Lq, Lk] oracle visibility on local indices."""
     covered = torch.zeros(Lq, dtype=torch.int32)
     costs = []
     for it in items.tolist():
         q_row0, t0, rows, qrank, k_row0, krank, rb, re_ = it
-        assert q_row0 == t0 and 0 < rows <= 128
+        assert q_row0 == t0 and 0 < rows <= tm
         covered[t0:t0 + rows] += 1
         keys = torch.zeros(Lk, dtype=torch.int32)
         cost = 0
@@ -246,8 +246,8 @@ def test_planner_against_oracle_visibility(case, accumulate):
             items, runs, tm, tn = usp.plan_block(
                 L, L, 128, mask="positional", qmap=usp.posmap(impl, N, i, S, b), kmap=usp.posmap(impl, N, j, S, b),
                 causal=causal, window=window, n_sink=n_sink, cu_seqlens=cu, accumulate=accumulate)
-            assert tm == 128 and tn == 64
-            _check_plan(L, L, qpos, kpos, vis, accumulate, items, runs, tn)
+            assert tm in (128, 256) and tn == 64
+            _check_plan(L, L, qpos, kpos, vis, accumulate, items, runs, tn, tm)
 
 
 @pytest.mark.parametrize("mask", ["full", "causal", "causal_strict", "empty"])
@@ -259,7 +259,7 @@ def test_planner_explicit_classes(mask, Lq, Lk):
            "empty": torch.zeros(Lq, Lk, dtype=torch.bool)}[mask]
     for acc in (False, True):
         items, runs, tm, tn = usp.plan_block(Lq, Lk, 64, mask=mask, accumulate=acc)
-        _check_plan(Lq, Lk, None, None, vis, acc, items, runs, tn)
+        _check_plan(Lq, Lk, None, None, vis, acc, items, runs, tn, tm)
 
 
 def test_planner_full_tiles_dominate_large_causal():

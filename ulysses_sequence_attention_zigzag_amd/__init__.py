@@ -15,7 +15,9 @@ from typing import Optional, Sequence, Tuple
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libusp.so")
+# USP_LIBRARY names an alternative build of libusp.so (e.g. a tuning variant);
+# by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("USP_LIBRARY") or os.path.join(_PKG, "libusp.so")
 
 IMPL = {"basic": 0, "zigzag": 1, "stripe": 2}
 MASK = {"empty": 0, "full": 1, "causal": 2, "causal_strict": 3, "positional": 4}

@@ -31,32 +31,33 @@ COMMON = [
 ]
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(BUILD, src + ".o")
+def _compile(src: str, extra, csrc: str, build_dir: str) -> str:
+    obj = os.path.join(build_dir, src + ".o")
     lang = ["-x", "hip"]
-    cmd = [HIPCC] + COMMON + list(extra) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + COMMON + list(extra) + lang + ["-c", os.path.join(csrc, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(extra=(), verbose: bool = False) -> str:
-    """Compiles every source and links libusp.so; returns its path."""
+def build(extra=(), verbose: bool = False, csrc: str = CSRC, out: str = LIB) -> str:
+    """Compiles every source of `csrc` and links `out` (libusp.so); returns its path."""
     if not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
-    os.makedirs(BUILD, exist_ok=True)
+    build_dir = BUILD if out == LIB else os.path.join(os.path.dirname(out), "_build")
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, extra, csrc, build_dir), SOURCES))
+    tmp = out + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    shutil.move(tmp, LIB)
+    shutil.move(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

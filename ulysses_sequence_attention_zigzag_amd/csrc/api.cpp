@@ -216,6 +216,19 @@ usp_status setup_block_mask(int64_t Lq, int64_t Lk, usp_mask_class mask, const u
   return USP_OK;
 }
 
+// Items / runs of one block call (explicit class or positional).
+void build_block_plan(const BlockMaskSetup& su, int32_t Lq, int32_t Lk, const int32_t* cu_host,
+                      int accumulate, int32_t tile_m, Plan& plan) {
+  if (!su.empty) {
+    BlockSpec blk{su.qmap, su.kmap, Lq, Lk, 0, 0, tile_m};
+    plan_block(blk, su.ms, cu_host, accumulate, plan);
+  } else if (!accumulate) {
+    // EMPTY without accumulate: items with no runs write O = 0, LSE = -inf
+    for (int32_t t0 = 0; t0 < Lq; t0 += tile_m)
+      plan.items.push_back({t0, t0, std::min<int32_t>(tile_m, Lq - t0), 0, 0, 0, 0, 0});
+  }
+}
+
 std::string map_key(const PosMap& m) {
   char buf[96];
   snprintf(buf, sizeof(buf), "%d.%d.%d.%d.%d.%d", m.kind, m.N, m.rank, m.b, m.L, m.offset);
@@ -324,18 +337,12 @@ usp_status usp_plan_block(int64_t Lq, int64_t Lk, int64_t D, usp_mask_class mask
                                    nseq, 1, &su);
   if (st != USP_OK) return st;
   Plan plan;
-  if (!su.empty) {
-    BlockSpec blk{su.qmap, su.kmap, (int32_t)Lq, (int32_t)Lk, 0, 0};
-    plan_block(blk, su.ms, cu_seqlens_host, accumulate, plan);
-  } else if (!accumulate) {
-    // EMPTY without accumulate: items with no runs write O = 0, LSE = -inf
-    for (int32_t t0 = 0; t0 < Lq; t0 += kTileM)
-      plan.items.push_back({t0, t0, std::min<int32_t>(kTileM, (int32_t)Lq - t0), 0, 0, 0, 0, 0});
-  }
+  const int32_t tm = choose_tile_m(su.qmap);
+  build_block_plan(su, (int32_t)Lq, (int32_t)Lk, cu_seqlens_host, accumulate, tm, plan);
   finalize_plan(plan);
   *n_items = (int64_t)plan.items.size();
   *n_runs = (int64_t)plan.runs.size();
-  if (tile_m) *tile_m = kTileM;
+  if (tile_m) *tile_m = tm;
   if (tile_n) *tile_n = kTileN;
   if (items) {
     USP_CHECK(items_cap >= *n_items, USP_ERR_INVALID_ARG, "items buffer too small");
@@ -364,6 +371,8 @@ usp_status usp_block_attn_fwd(const void* q, const void* k, const void* v, void*
             "cu_seqlens must be given on both host and device, or neither");
   USP_CHECK(B * Lq <= kMaxI32 && B * Lk <= kMaxI32 && Lq * Hq <= kMaxI32 * 8, USP_ERR_UNSUPPORTED, "tensor too large");
   USP_CHECK(std::isfinite(softmax_scale), USP_ERR_INVALID_ARG, "softmax_scale must be finite");
+  USP_CHECK(Lk * Hkv * D * 2 < ((int64_t)1 << 31), USP_ERR_UNSUPPORTED,
+            "one batch row of k/v must be under 2 GiB (32-bit tile offsets)");
   BlockMaskSetup su;
   usp_status st = setup_block_mask(Lq, Lk, mask, qmap, kmap, causal, window, n_sink, cu_seqlens_host,
                                    nseq, B, &su);
@@ -371,18 +380,13 @@ usp_status usp_block_attn_fwd(const void* q, const void* k, const void* v, void*
   if (Lq == 0) return USP_OK;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)D);
 
+  const int32_t tm = choose_tile_m(su.qmap);
   std::string key = "blk|" + std::to_string(Lq) + "|" + std::to_string(Lk) + "|" + map_key(su.qmap) + "|" +
                     map_key(su.kmap) + "|" + mask_key(su.ms) + "|" + cu_key(su.ms.nseq ? cu_seqlens_host : nullptr, nseq) +
-                    "|a" + std::to_string(accumulate) + "|e" + std::to_string(su.empty);
+                    "|a" + std::to_string(accumulate) + "|e" + std::to_string(su.empty) + "|m" + std::to_string(tm);
   DevicePlan dp;
   st = device_plan(key, [&](Plan& plan) {
-    if (!su.empty) {
-      BlockSpec blk{su.qmap, su.kmap, (int32_t)Lq, (int32_t)Lk, 0, 0};
-      plan_block(blk, su.ms, cu_seqlens_host, accumulate, plan);
-    } else if (!accumulate) {
-      for (int32_t t0 = 0; t0 < Lq; t0 += kTileM)
-        plan.items.push_back({t0, t0, std::min<int32_t>(kTileM, (int32_t)Lq - t0), 0, 0, 0, 0, 0});
-    }
+    build_block_plan(su, (int32_t)Lq, (int32_t)Lk, cu_seqlens_host, accumulate, tm, plan);
   }, &dp);
   if (st != USP_OK) return st;
 
@@ -405,6 +409,7 @@ usp_status usp_block_attn_fwd(const void* q, const void* k, const void* v, void*
   p.Hkv = (int32_t)Hkv;
   p.out_f32 = out_dt == USP_DT_F32;
   p.accumulate = accumulate ? 1 : 0;
+  p.tile_m = tm;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.qmap = su.qmap;
   p.kmap = su.kmap;
@@ -458,6 +463,8 @@ usp_status check_ring_args(const usp_ring_args* a) {
     if (st != USP_OK) return st;
   }
   USP_CHECK(a->B * a->S <= kMaxI32, USP_ERR_UNSUPPORTED, "B*S too large");
+  USP_CHECK(L * (a->Hkv / a->ulysses_degree) * a->D * 2 < ((int64_t)1 << 31), USP_ERR_UNSUPPORTED,
+            "one ring rank's k/v rows must be under 2 GiB (32-bit tile offsets)");
   return USP_OK;
 }
 
@@ -597,11 +604,13 @@ usp_status usp_ring_fwd(const usp_ring_args* a, void* workspace, size_t ws_bytes
   usp_posmap pm{a->impl, N, 0, b, S};
   const PosMap base_map = make_map(pm);
 
+  const int32_t tm = choose_tile_m(base_map);
   for (int s = 0; s < N; ++s) {
     const int acc_flag = (s > 0 && a->merge_mode == 0) ? 1 : 0;
     const std::string key = "ring|" + map_key(base_map) + "|" + mask_key(ms) + "|" +
                             cu_key(ms.nseq ? a->cu_seqlens_host : nullptr, a->nseq) + "|r" +
-                            std::to_string(a->rank) + "|s" + std::to_string(s) + "|a" + std::to_string(acc_flag);
+                            std::to_string(a->rank) + "|s" + std::to_string(s) + "|a" + std::to_string(acc_flag) +
+                            "|m" + std::to_string(tm);
     DevicePlan dp;
     st = device_plan(key, [&](Plan& plan) {
       const int i0 = R.one ? a->rank : 0, i1 = R.one ? a->rank + 1 : N;
@@ -616,6 +625,7 @@ usp_status usp_ring_fwd(const usp_ring_args* a, void* workspace, size_t ws_bytes
         blk.Lk = (int32_t)L;
         blk.q_row_base = R.one ? 0 : (int32_t)(i * L);
         blk.k_row_base = (int32_t)(j * L);
+        blk.tile_m = tm;
         plan_block(blk, ms, a->cu_seqlens_host, acc_flag, plan);
       }
     }, &dp);
@@ -641,6 +651,7 @@ usp_status usp_ring_fwd(const usp_ring_args* a, void* workspace, size_t ws_bytes
     p.Hkv = (int32_t)Hkv_l;
     p.out_f32 = 1;
     p.accumulate = acc_flag;
+    p.tile_m = tm;
     p.scale_log2 = scale * 1.4426950408889634f;
     p.qmap = base_map;
     p.kmap = base_map;

@@ -1,7 +1,10 @@
 // Block attention forward for one ring step on gfx950 (CDNA4).
 //
-// One workgroup = 4 waves = 128 query rows of one (batch, head); each wave
-// owns 32 query rows.  Per key tile of 64 keys:
+// One workgroup = 4 waves; each wave owns QB blocks of 32 query rows of one
+// (batch, head), so a workgroup covers 128 (QB = 1) or 256 (QB = 2) rows.
+// With QB = 2 every K and V fragment read from LDS feeds two MFMAs, halving
+// LDS traffic per FLOP (at one wave per SIMD: the wave then needs ~370
+// registers).  Per key tile of 64 keys:
 //   S^T = K Q^T      v_mfma_f32_32x32x16_bf16, K from LDS (A operand),
 //                    Q resident in VGPRs (B operand);
 //   mask             only in partial runs (the planner marks fully visible
@@ -47,6 +50,14 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Floor / ceiling of a / b for b >= 1 (a of either sign).
+__device__ __forceinline__ int32_t floor_div(int32_t a, int32_t b) {
+  if (b == 1) return a;
+  const int32_t q = a / b;
+  return (a % b != 0 && a < 0) ? q - 1 : q;
+}
+__device__ __forceinline__ int32_t ceil_div(int32_t a, int32_t b) { return -floor_div(-a, b); }
+
 // LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
 // lanes, lane i supplies the address of 4 consecutive bf16 (row i/4 of a
 // 4 x 16 block, columns 4*(i%4)..+3); lane j receives column j of the block,
@@ -58,11 +69,10 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
-// Asynchronous 16-byte global -> LDS copy (gfx950 global_load_lds_dwordx4):
-// lane i's 16 bytes land at lds_wave_base + 16 * i.
-__device__ __forceinline__ void load_to_lds(const void* g, char* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(lds_wave_base), 16, 0, 0);
-}
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Word 3 of a raw (unswizzled, stride 0) buffer resource on gfx9-family GPUs.
+constexpr int kBufferRsrcWord3 = 0x00020000;
 
 // LDS tile layout: a K or V tile is BN rows of D bf16 (D*2 bytes), rows
 // packed back to back, each row made of D/8 chunks of 16 bytes.  Chunk c of
@@ -82,17 +92,23 @@ struct TileLayout {
   __device__ static __forceinline__ int swz_v(int r) { return 4 * ((r / RPL) & (CPR / 4 - 1)); }
 };
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
+// LINEAR: key positions step linearly through every run (all layouts except
+// striped blocks of more than one token), which keeps the partial-tile mask
+// to interval compares.
+// LINEAR: key positions step linearly through every run (all layouts except
+// striped blocks of more than one token), which keeps the partial-tile mask
+// to interval compares.  QB: 32-row query blocks per wave.
+template <int D, bool LINEAR, int QB>
+__global__ __launch_bounds__(256, (LINEAR && QB == 1) ? 2 : 1) void attn_fwd_kernel(const AttnParams p) {
   using TL = TileLayout<D>;
   constexpr int BN = kTileN;
   constexpr int KS = D / 16;        // k-steps of the QK^T contraction
   constexpr int DB = D / 32;        // 32-wide blocks of the output's head dim
   constexpr int NB = BN / 32;       // 32-key blocks per tile
   constexpr int TILEB = BN * D * 2; // bytes of one K or V tile
-  constexpr int LPW = TILEB / 1024 / 4;  // direct loads per wave per tensor and tile
-  constexpr int RPI = 1024 / TL::ROWB;   // tile rows per 1 KB load instruction
-  static_assert(TILEB % 4096 == 0, "tile must split into 4 waves x 1 KB loads");
+  constexpr int LPW = TILEB / 1024 / 4;  // 16-byte loads per thread per tensor and tile
+  constexpr int RPI = 1024 / TL::ROWB;   // tile rows per 1 KB slice
+  static_assert(TILEB % 4096 == 0, "tile must split into 4 waves x 1 KB slices");
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];  // K0 K1 V0 V1
 
   const int tid = threadIdx.x;
@@ -114,79 +130,118 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
   const WorkItem it = p.items[item_idx];
   const int hk = h / (p.Hq / p.Hkv);
 
-  const int qr = wid * 32 + l32;              // this lane's query row in the tile
-  const bool qvalid = qr < it.q_rows;
-  const int64_t qrow = (int64_t)it.q_row0 + qr;
+  // This lane's query row of block qb: wid*32*QB + qb*32 + l32.
+  bool qvalid[QB];
+  int64_t qrow[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qr = (wid * QB + qb) * 32 + l32;
+    qvalid[qb] = qr < it.q_rows;
+    qrow[qb] = (int64_t)it.q_row0 + qr;
+  }
 
   // Q fragments (B operand): Q[q][ks*16 + hi*8 .. +7]
-  bf16x8 qf[KS];
-  {
-    const uint16_t* qp = p.q + (int64_t)b * p.q_batch_stride + (qrow * p.Hq + h) * D + hi * 8;
+  bf16x8 qf[QB][KS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const uint16_t* qp = p.q + (int64_t)b * p.q_batch_stride + (qrow[qb] * p.Hq + h) * D + hi * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if (qvalid) {
-        qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
+      if (qvalid[qb]) {
+        qf[qb][ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)0.f;
+        for (int e = 0; e < 8; ++e) qf[qb][ks][e] = (__bf16)0.f;
       }
     }
   }
 
-  f32x16 o[DB];
+  f32x16 o[QB][DB];
 #pragma unroll
-  for (int d = 0; d < DB; ++d)
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[qb][d][r] = 0.f;
   // Running max m (log2 domain, scale folded in) and this lane's share of the
   // running sum.  m is raised lazily: only when a tile's max exceeds it by
   // more than kRescale, so the exponentials stay <= 2^kRescale.
   constexpr float kRescale = 8.f;
-  float m = -INFINITY;
-  float lsum = 0.f;
+  float m[QB], lsum[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = -INFINITY;
+    lsum[qb] = 0.f;
+  }
 
-  // Positions for per-element masks.
+  // Visible key positions of each query: [vis_lo, vis_hi], plus the sinks
+  // [sstart, sink_hi] when a window is set (same sequence, causal band,
+  // window p_q - p_k < W, first n_sink positions of the sequence).
   PosMap qm = p.qmap;
   qm.rank = it.q_rank;
   PosMap km = p.kmap;
   km.rank = it.k_rank;
-  const int32_t pq = position(qm, it.t0 + (qvalid ? qr : 0));
-  int32_t sstart = 0, send = p.mask.S;
-  if (p.mask.nseq > 0) {
+  const bool cw = p.mask.causal || p.mask.window > 0;
+  int32_t sstart[QB], vis_lo[QB], vis_hi[QB], sink_hi[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qr = (wid * QB + qb) * 32 + l32;
+    const int32_t pq = position(qm, it.t0 + (qvalid[qb] ? qr : 0));
+    int32_t s0 = 0, s1 = p.mask.S;
     for (int i = 0; i < p.mask.nseq; ++i) {
       const int32_t lo = p.cu_seqlens[i], up = p.cu_seqlens[i + 1];
       if (pq >= lo && pq < up) {
-        sstart = lo;
-        send = up;
+        s0 = lo;
+        s1 = up;
       }
     }
+    sstart[qb] = s0;
+    vis_hi[qb] = cw ? min(pq, s1 - 1) : s1 - 1;
+    vis_lo[qb] = p.mask.window > 0 ? max(s0, pq - p.mask.window + 1) : s0;
+    sink_hi[qb] = p.mask.window > 0 ? min(s0 + p.mask.n_sink - 1, vis_hi[qb]) : s0 - 1;
   }
-  const bool cw = p.mask.causal || p.mask.window > 0;
-  const int32_t W = p.mask.window;
-  const int32_t nsink = p.mask.n_sink;
+  const int32_t kv_step = km.kind == MAP_STRIPE ? km.N : 1;
 
   const int64_t kv_row_stride = (int64_t)p.Hkv * D;
   const uint16_t* kbase = p.k + (int64_t)b * p.kv_batch_stride + (int64_t)it.k_row0 * kv_row_stride + hk * D;
   const uint16_t* vbase = p.v + (int64_t)b * p.kv_batch_stride + (int64_t)it.k_row0 * kv_row_stride + hk * D;
 
-  // Direct loads of one K and one V tile into LDS buffer `buf`.  Wave w fills
-  // 1 KB slices w*LPW .. w*LPW+LPW-1 of each tile; lane i of a slice writes
-  // physical (row, chunk slot) = (slice*RPI + i / CPR, i % CPR) and so loads
+  // K / V tile staging.  A tile is loaded from global memory into registers
+  // (16 bytes per load, 32-bit offsets from a buffer resource) and then
+  // written to LDS.  Loads and LDS writes are split so that K(t+1) is in
+  // flight during QK^T(t) and V(t+1) during PV(t).  The 256 threads cover the
+  // tile as 1 KB slices: thread (wave w, lane i) handles slices w*LPW + j,
+  // physical (row, chunk slot) = (slice*RPI + i / CPR, i % CPR), and so the
   // logical chunk slot ^ swz(row) of that row.  Rows past the run's end are
-  // clamped to its last row (finite values; those keys are masked).
+  // clamped to its last row (finite values; those keys are masked), so no
+  // load leaves the run.
   const int lrow = lane / TL::CPR;
   const int lslot = lane % TL::CPR;
-  auto issue_tile = [&](int buf, int k0, int kend) {
+  const uint32_t row_bytes = (uint32_t)kv_row_stride * 2;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)kbase, (short)0, 0x7fffffff, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)vbase, (short)0, 0x7fffffff, kBufferRsrcWord3);
+  auto load_k = [&](i32x4 (&r)[LPW], int k0, int kend) {
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
-      const int slice = wid * LPW + j;
-      const int row = slice * RPI + lrow;
-      const int grow = min(k0 + row, kend - 1);
-      const int ck = lslot ^ TL::swz_k(row);
-      const int cv = lslot ^ TL::swz_v(row);
-      load_to_lds(kbase + (int64_t)grow * kv_row_stride + ck * 8, smem + buf * TILEB + slice * 1024);
-      load_to_lds(vbase + (int64_t)grow * kv_row_stride + cv * 8, smem + (2 + buf) * TILEB + slice * 1024);
+      const int row = (wid * LPW + j) * RPI + lrow;
+      const uint32_t off = (uint32_t)min(k0 + row, kend - 1) * row_bytes + (uint32_t)((lslot ^ TL::swz_k(row)) * 16);
+      r[j] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
     }
+  };
+  auto load_v = [&](i32x4 (&r)[LPW], int k0, int kend) {
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const int row = (wid * LPW + j) * RPI + lrow;
+      const uint32_t off = (uint32_t)min(k0 + row, kend - 1) * row_bytes + (uint32_t)((lslot ^ TL::swz_v(row)) * 16);
+      r[j] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
+    }
+  };
+  auto store_tile = [&](char* tile, const i32x4 (&r)[LPW]) {
+#pragma unroll
+    for (int j = 0; j < LPW; ++j)
+      *reinterpret_cast<i32x4*>(tile + (wid * LPW + j) * 1024 + lane * 16) = r[j];
   };
 
   // Per-lane LDS read offsets (bytes within a tile).
@@ -198,17 +253,103 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
   const int vchunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const int vhalf8 = (lane & 1) * 8;
 
+  // S^T[key][q] = K Q^T for one tile in LDS.  Each K fragment serves the QB
+  // query blocks; consecutive MFMAs go to different accumulators.
+  auto qk = [&](const char* tK, f32x16 (&sc)[QB][NB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[qb][kb][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb) {
+        const int row = kb * 32 + l32;
+        const int slot = (2 * ks + hi) ^ TL::swz_k(row);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(tK + row * TL::ROWB + slot * 16);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sc[qb][kb] = mfma32(a, qf[qb][ks], sc[qb][kb]);
+      }
+    }
+  };
+
+  // O^T[d][q] += V^T[d][key] P^T[key][q].  Each V^T fragment serves the QB
+  // query blocks; consecutive MFMAs go to different output blocks.
+  auto pv = [&](const char* tV, const bf16x8 (&pb)[QB][NB][2]) {
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int d = 0; d < DB; ++d) {
+          const int r0 = kb * 32 + half * 16 + vrow0;
+          const int r1 = r0 + 8;
+          const int c = 4 * d + vchunk;
+          const bf16x4 a0 = lds_read_tr(tV + r0 * TL::ROWB + ((c ^ TL::swz_v(r0)) * 16) + vhalf8);
+          const bf16x4 a1 = lds_read_tr(tV + r1 * TL::ROWB + ((c ^ TL::swz_v(r1)) * 16) + vhalf8);
+          const bf16x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) o[qb][d] = mfma32(a, pb[qb][kb][half], o[qb][d]);
+        }
+      }
+    }
+  };
+
+  // Per-element mask of a partial tile starting at key k0.  Element (kb, r)
+  // of this lane is key k0 + du with du = c + 4*hi, c = kb*32 + 8*(r/4) + r%4.
+  // For layouts whose key positions step linearly through a run, the visible
+  // du form at most two intervals (window band, sinks); their bounds are
+  // computed once, shifted by 4*hi, and compared with the compile-time c.
+  auto apply_mask = [&](f32x16 (&sc)[NB], int qb, int k0, int kend) {
+    const int32_t kend_du = kend - 1 - k0;
+    if constexpr (LINEAR) {
+      const int32_t pk0 = position(km, k0);
+      const int32_t sh = 4 * hi;
+      const int32_t lo = ceil_div(vis_lo[qb] - pk0, kv_step) - sh;
+      const int32_t up = min(floor_div(vis_hi[qb] - pk0, kv_step), kend_du) - sh;
+      const int32_t slo = ceil_div(sstart[qb] - pk0, kv_step) - sh;
+      const int32_t sup = min(floor_div(sink_hi[qb] - pk0, kv_step), kend_du) - sh;
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
+          const bool vis = ((c >= lo) & (c <= up)) | ((c >= slo) & (c <= sup));
+          sc[kb][r] = vis ? sc[kb][r] : -INFINITY;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int du = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          const int32_t pk = position(km, k0 + du);
+          const bool vis = (du <= kend_du) & (pk <= vis_hi[qb]) &
+                           ((pk >= vis_lo[qb]) | ((pk >= sstart[qb]) & (pk <= sink_hi[qb])));
+          sc[kb][r] = vis ? sc[kb][r] : -INFINITY;
+        }
+      }
+    }
+  };
+
   int ri = it.run_begin;
   if (ri < it.run_end) {
     Run run = p.runs[ri];
     int k0 = run.k_begin;
     int buf = 0;
-    issue_tile(0, k0, run.k_end);
+    {
+      i32x4 kr[LPW], vr[LPW];
+      load_k(kr, k0, run.k_end);
+      load_v(vr, k0, run.k_end);
+      store_tile(smem, kr);
+      store_tile(smem + 2 * TILEB, vr);
+    }
+    __syncthreads();
     while (true) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();  // tile `buf` is in LDS; every wave is done with buffer buf^1
-
-      // next tile (uniform across the workgroup); its loads overlap this tile's math
+      // next tile (uniform across the workgroup)
       int nk0 = k0 + BN;
       int nri = ri;
       Run nrun = run;
@@ -220,95 +361,73 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
         }
       }
       const bool has_next = nri < it.run_end;
-      if (has_next) issue_tile(buf ^ 1, nk0, nrun.k_end);
 
-      const char* tK = smem + buf * TILEB;
-      const char* tV = smem + (2 + buf) * TILEB;
+      i32x4 kr[LPW];
+      if (has_next) load_k(kr, nk0, nrun.k_end);
 
-      // S^T[key][q] for the tile's NB blocks of 32 keys
-      f32x16 s[NB];
-#pragma unroll
-      for (int kb = 0; kb < NB; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-        const int row = kb * 32 + l32;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int slot = (2 * ks + hi) ^ TL::swz_k(row);
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(tK + row * TL::ROWB + slot * 16);
-          s[kb] = mfma32(a, qf[ks], s[kb]);
-        }
-      }
-
+      f32x16 s[QB][NB];
+      qk(smem + buf * TILEB, s);
       if (!run.full) {
 #pragma unroll
-        for (int kb = 0; kb < NB; ++kb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int u = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            const int32_t pk = position(km, u);
-            const bool vis = u < run.k_end && pk >= sstart && pk < send && (!cw || pk <= pq) &&
-                             (W <= 0 || pq - pk < W || pk - sstart < nsink);
-            if (!vis) s[kb][r] = -INFINITY;
-          }
-        }
+        for (int qb = 0; qb < QB; ++qb) apply_mask(s[qb], qb, k0, run.k_end);
       }
 
       // online softmax (log2 domain) with lazy rescaling
-      float mt = -INFINITY;
+      float alpha[QB];
+      bf16x8 pb[QB][NB][2];
 #pragma unroll
-      for (int kb = 0; kb < NB; ++kb)
+      for (int qb = 0; qb < QB; ++qb) {
+        float mt = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32)) * p.scale_log2;
-      if (__builtin_amdgcn_readfirstlane((int)(__ballot(mt > m + kRescale) != 0ull))) {
-        const float m_new = fmaxf(m, mt);
-        // 0 when only m is -inf; lanes that have seen no visible key keep 1
-        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m - m_new);
-        m = m_new;
-        lsum *= alpha;
+        for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-        for (int d = 0; d < DB; ++d)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
-      }
-      const float m_use = (m == -INFINITY) ? 0.f : m;
-
-      bf16x8 pb[NB][2];
-#pragma unroll
-      for (int kb = 0; kb < NB; ++kb) {
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const float p0 = fast_exp2(s[kb][half * 8 + e] * p.scale_log2 - m_use);
-            const float p1 = fast_exp2(s[kb][half * 8 + e + 1] * p.scale_log2 - m_use);
-            lsum += p0 + p1;
-            const bf16x2 pk2 = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
-            pb[kb][half][e] = pk2[0];
-            pb[kb][half][e + 1] = pk2[1];
-          }
-        }
-      }
-
-      // O^T[d][q] += V^T[d][key] P^T[key][q]
-#pragma unroll
-      for (int d = 0; d < DB; ++d) {
+          for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[qb][kb][r]);
+        mt = fmaxf(mt, __shfl_xor(mt, 32)) * p.scale_log2;
+        const float m_new = (mt > m[qb] + kRescale) ? mt : m[qb];
+        alpha[qb] = (m_new == m[qb] || m_new == -INFINITY) ? 1.f : fast_exp2(m[qb] - m_new);
+        m[qb] = m_new;
+        lsum[qb] *= alpha[qb];
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
 #pragma unroll
         for (int kb = 0; kb < NB; ++kb) {
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
-            const int r0 = kb * 32 + half * 16 + vrow0;
-            const int r1 = r0 + 8;
-            const int c = 4 * d + vchunk;
-            const bf16x4 a0 = lds_read_tr(tV + r0 * TL::ROWB + ((c ^ TL::swz_v(r0)) * 16) + vhalf8);
-            const bf16x4 a1 = lds_read_tr(tV + r1 * TL::ROWB + ((c ^ TL::swz_v(r1)) * 16) + vhalf8);
-            const bf16x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-            o[d] = mfma32(a, pb[kb][half], o[d]);
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+              const float p0 = fast_exp2(s[qb][kb][half * 8 + e] * p.scale_log2 - m_use);
+              const float p1 = fast_exp2(s[qb][kb][half * 8 + e + 1] * p.scale_log2 - m_use);
+              lsum[qb] += p0 + p1;
+              const bf16x2 pk2 = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
+              pb[qb][kb][half][e] = pk2[0];
+              pb[qb][kb][half][e + 1] = pk2[1];
+            }
           }
         }
       }
 
+      // K(t+1) -> LDS (its buffer was last read by QK(t-1), before the barrier)
+      if (has_next) store_tile(smem + (buf ^ 1) * TILEB, kr);
+      i32x4 vr[LPW];
+      if (has_next) load_v(vr, nk0, nrun.k_end);
+
+      bool any_rescale = false;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) any_rescale |= alpha[qb] != 1.f;
+      if (__builtin_amdgcn_readfirstlane((int)(__ballot(any_rescale) != 0ull))) {
+        asm volatile("" ::: "memory");  // keep this a branch (rarely taken)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int d = 0; d < DB; ++d)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[qb][d][r] *= alpha[qb];
+      }
+
+      pv(smem + (2 + buf) * TILEB, pb);
+
+      // V(t+1) -> LDS (its buffer was last read by PV(t-1), before the barrier)
+      if (has_next) store_tile(smem + (2 + (buf ^ 1)) * TILEB, vr);
+      __syncthreads();
       if (!has_next) break;
       ri = nri;
       run = nrun;
@@ -317,57 +436,60 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const AttnParams p) {
     }
   }
 
-  // epilogue
-  const float ltot = lsum + __shfl_xor(lsum, 32);
-  if (!qvalid) return;
-  const float lse_new = ltot > 0.f ? m * kLn2 + logf(ltot) : -INFINITY;
-  float* lse_ptr = p.lse + ((int64_t)b * p.Hq + h) * p.Lq_buf + qrow;
-  const int64_t obase = (int64_t)b * p.o_batch_stride + (qrow * p.Hq + h) * D;
-  float wa = 0.f, wb = ltot > 0.f ? 1.f / ltot : 0.f;
-  float lse_out = lse_new;
-  if (p.accumulate) {
-    const float la = *lse_ptr;
-    const float M = fmaxf(la, lse_new);
-    if (lse_new == -INFINITY || M == -INFINITY) return;  // nothing to merge
-    const float Lm = M + logf(expf(la - M) + expf(lse_new - M));
-    wa = expf(la - Lm);
-    wb *= expf(lse_new - Lm);
-    lse_out = Lm;
-  }
-  if (p.out_f32) {
-    float* op = static_cast<float*>(p.out) + obase;
+  // epilogue: O = O_acc / l, LSE = m ln 2 + ln l; or merge into (out, lse)
 #pragma unroll
-    for (int d = 0; d < DB; ++d) {
+  for (int qb = 0; qb < QB; ++qb) {
+    const float ltot = lsum[qb] + __shfl_xor(lsum[qb], 32);
+    if (!qvalid[qb]) continue;
+    const float lse_new = ltot > 0.f ? m[qb] * kLn2 + logf(ltot) : -INFINITY;
+    float* lse_ptr = p.lse + ((int64_t)b * p.Hq + h) * p.Lq_buf + qrow[qb];
+    const int64_t obase = (int64_t)b * p.o_batch_stride + (qrow[qb] * p.Hq + h) * D;
+    float wa = 0.f, wb = ltot > 0.f ? 1.f / ltot : 0.f;
+    float lse_out = lse_new;
+    if (p.accumulate) {
+      const float la = *lse_ptr;
+      const float M = fmaxf(la, lse_new);
+      if (lse_new == -INFINITY || M == -INFINITY) continue;  // nothing to merge
+      const float Lm = M + logf(expf(la - M) + expf(lse_new - M));
+      wa = expf(la - Lm);
+      wb *= expf(lse_new - Lm);
+      lse_out = Lm;
+    }
+    if (p.out_f32) {
+      float* op = static_cast<float*>(p.out) + obase;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int dd = d * 32 + 8 * g + 4 * hi;
-        float4 v = make_float4(o[d][4 * g] * wb, o[d][4 * g + 1] * wb, o[d][4 * g + 2] * wb,
-                               o[d][4 * g + 3] * wb);
-        if (wa != 0.f) {
-          const float4 a = *reinterpret_cast<const float4*>(op + dd);
-          v.x += wa * a.x;
-          v.y += wa * a.y;
-          v.z += wa * a.z;
-          v.w += wa * a.w;
+      for (int d = 0; d < DB; ++d) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int dd = d * 32 + 8 * g + 4 * hi;
+          float4 v = make_float4(o[qb][d][4 * g] * wb, o[qb][d][4 * g + 1] * wb, o[qb][d][4 * g + 2] * wb,
+                                 o[qb][d][4 * g + 3] * wb);
+          if (wa != 0.f) {
+            const float4 a = *reinterpret_cast<const float4*>(op + dd);
+            v.x += wa * a.x;
+            v.y += wa * a.y;
+            v.z += wa * a.z;
+            v.w += wa * a.w;
+          }
+          *reinterpret_cast<float4*>(op + dd) = v;
         }
-        *reinterpret_cast<float4*>(op + dd) = v;
+      }
+    } else {
+      uint16_t* op = static_cast<uint16_t*>(p.out) + obase;
+#pragma unroll
+      for (int d = 0; d < DB; ++d) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int dd = d * 32 + 8 * g + 4 * hi;
+          const bf16x2 lo = __builtin_convertvector((f32x2){o[qb][d][4 * g] * wb, o[qb][d][4 * g + 1] * wb}, bf16x2);
+          const bf16x2 up = __builtin_convertvector((f32x2){o[qb][d][4 * g + 2] * wb, o[qb][d][4 * g + 3] * wb}, bf16x2);
+          *reinterpret_cast<uint2*>(op + dd) =
+              make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, up));
+        }
       }
     }
-  } else {
-    uint16_t* op = static_cast<uint16_t*>(p.out) + obase;
-#pragma unroll
-    for (int d = 0; d < DB; ++d) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int dd = d * 32 + 8 * g + 4 * hi;
-        const bf16x2 lo = __builtin_convertvector((f32x2){o[d][4 * g] * wb, o[d][4 * g + 1] * wb}, bf16x2);
-        const bf16x2 up = __builtin_convertvector((f32x2){o[d][4 * g + 2] * wb, o[d][4 * g + 3] * wb}, bf16x2);
-        *reinterpret_cast<uint2*>(op + dd) =
-            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, up));
-      }
-    }
+    if (hi == 0) *lse_ptr = lse_out;
   }
-  if (hi == 0) *lse_ptr = lse_out;
 }
 
 }  // namespace
@@ -380,11 +502,25 @@ usp_status launch_attn_fwd(const AttnParams& p, int D, hipStream_t stream) {
     return USP_ERR_UNSUPPORTED;
   }
   const dim3 grid((unsigned)total), block(256);
+  const bool linear = !(p.kmap.kind == MAP_STRIPE && p.kmap.b > 1);
+  const bool wide = p.tile_m == 256;
+  if (!wide && p.tile_m != 128) {
+    set_error("internal: unsupported query tile %d", p.tile_m);
+    return USP_ERR_UNSUPPORTED;
+  }
   TimingScope ts(K_ATTN, stream);
-  if (D == 128)
-    hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, block, 0, stream, p);
-  else
-    hipLaunchKernelGGL(attn_fwd_kernel<64>, grid, block, 0, stream, p);
+#define USP_LAUNCH(DD, LIN, QBB) hipLaunchKernelGGL((attn_fwd_kernel<DD, LIN, QBB>), grid, block, 0, stream, p)
+  // Only 128-row tiles (QB = 1) are instantiated; see choose_tile_m.
+  if (wide) {
+    set_error("internal: 256-row query tiles are not built");
+    return USP_ERR_UNSUPPORTED;
+  }
+  if (D == 128) {
+    if (linear) USP_LAUNCH(128, true, 1); else USP_LAUNCH(128, false, 1);
+  } else {
+    if (linear) USP_LAUNCH(64, true, 1); else USP_LAUNCH(64, false, 1);
+  }
+#undef USP_LAUNCH
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_error("attention launch failed: %s", hipGetErrorString(e));

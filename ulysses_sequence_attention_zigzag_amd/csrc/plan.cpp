@@ -75,8 +75,8 @@ void plan_block(const BlockSpec& blk, const MaskSpec& ms, const int32_t* cu_host
   std::vector<std::pair<int32_t, int32_t>> loc_iv;
 
   for (int qs = 0; qs < nq; ++qs) {
-    for (int32_t t0 = qlo[qs]; t0 < qhi[qs]; t0 += kTileM) {
-      const int32_t rows = std::min<int32_t>(kTileM, qhi[qs] - t0);
+    for (int32_t t0 = qlo[qs]; t0 < qhi[qs]; t0 += blk.tile_m) {
+      const int32_t rows = std::min<int32_t>(blk.tile_m, qhi[qs] - t0);
       const int64_t pq_min = position(blk.qmap, t0);
       const int64_t pq_max = position(blk.qmap, t0 + rows - 1);
       const int32_t s_min = seq.index(pq_min);

@@ -30,6 +30,30 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0       # HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_traffic.txt")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attention launch from the committed counter record
+    (FETCH_SIZE / WRITE_SIZE scaled by the copy-kernel calibration), or None
+    when there is no record for the workload or the kernel source changed
+    since the counters were taken."""
+    import hashlib
+    try:
+        kv = {}
+        for line in open(TRAFFIC_FILE):
+            line = line.strip()
+            if line and not line.startswith("#") and "=" in line:
+                key, val = line.split("=", 1)
+                kv[key.strip()] = val.strip()
+        src = os.path.join(ROOT, kv["kernel_source"])
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv["kernel_source_sha256"]:
+            return None
+        fetch = float(kv[workload + ".fetch_kib_per_launch"]) * 1024 * float(kv["fetch_factor"])
+        write = float(kv[workload + ".write_kib_per_launch"]) * 1024 * float(kv["write_factor"])
+        return int(round(fetch + write))
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def visible_pairs_per_head(w, rank_rows=None) -> int:
@@ -146,6 +170,9 @@ def main():
     ap.add_argument("--merge-mode", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy kernel (float32 negate) over MIB MiB, three times, "
+                         "as the known-size reference for HBM byte counters, and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -161,6 +188,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration > 0:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.randn(n, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"read_bytes": 4 * n, "write_bytes": 4 * n, "launches": 3}}))
+        return
     w = si.WORKLOADS[args.workload]
     t0 = time.perf_counter()
     q, k, v = w.make_inputs()
@@ -232,7 +269,8 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4) if attn_tflops else None,
-            "traffic": None,
+            "traffic": measured_traffic(w.name),
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "kernel": "attn_fwd_kernel<%d>" % w.D,
             "launches_per_step": attn_n // max(1, args.steps),
             "kernel_ms_per_step": round(attn_ms_step, 4),

@@ -270,5 +270,6 @@ def test_planner_full_tiles_dominate_large_causal():
     r = runs.tolist()
     full = sum(x[1] - x[0] for x in r if x[2])
     part = sum(x[1] - x[0] for x in r if not x[2])
-    # 32 q-tiles of 128 rows: full keys sum to 128*(0+...+31), one partial diagonal run each
-    assert part == 32 * 128 and full == 128 * 31 * 32 // 2
+    # n q-tiles of tm rows: tile i sees tm*i keys fully and its tm-key diagonal partially
+    n = (S // N) // tm
+    assert part == n * tm and full == tm * n * (n - 1) // 2

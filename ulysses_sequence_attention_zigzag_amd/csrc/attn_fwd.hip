@@ -1,10 +1,7 @@
 // Block attention forward for one ring step on gfx950 (CDNA4).
 //
-// One workgroup = 4 waves; each wave owns QB blocks of 32 query rows of one
-// (batch, head), so a workgroup covers 128 (QB = 1) or 256 (QB = 2) rows.
-// With QB = 2 every K and V fragment read from LDS feeds two MFMAs, halving
-// LDS traffic per FLOP (at one wave per SIMD: the wave then needs ~370
-// registers).  Per key tile of 64 keys:
+// One workgroup = 8 waves = 256 query rows of one (batch, head); each wave
+// owns 32 rows.  Per key tile of 64 keys:
 //   S^T = K Q^T      v_mfma_f32_32x32x16_bf16, K from LDS (A operand),
 //                    Q resident in VGPRs (B operand);
 //   mask             only in partial runs (the planner marks fully visible
@@ -30,6 +27,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "usp_internal.h"
 
@@ -43,6 +41,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
+
+// MFMAs by which LDS operand reads run ahead in the matrix phase (2, 4, 6
+// and 8 measured on MI355X: 6 is best by ~1.5%, 8 no better).
+constexpr int kPrefetch = 6;
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -95,25 +97,38 @@ struct TileLayout {
 // LINEAR: key positions step linearly through every run (all layouts except
 // striped blocks of more than one token), which keeps the partial-tile mask
 // to interval compares.
-// LINEAR: key positions step linearly through every run (all layouts except
-// striped blocks of more than one token), which keeps the partial-tile mask
-// to interval compares.  QB: 32-row query blocks per wave.
-template <int D, bool LINEAR, int QB>
-__global__ __launch_bounds__(256, (LINEAR && QB == 1) ? 2 : 1) void attn_fwd_kernel(const AttnParams p) {
+//
+// Wave roles.  The workgroup is 8 waves in two groups of 4 (waves 0-3 and
+// 4-7); the hardware places wave w and wave w + 4 on the same SIMD.  Each
+// wave owns 32 query rows.  The groups run the same per-tile program
+//   M(t): PV(t-1), QK(t)        (matrix cores + LDS reads)
+//   V(t): mask + softmax(t)     (vector ALU)
+// shifted by one phase, with a workgroup barrier between phases, so that on
+// every SIMD one wave feeds the matrix core while the other does its softmax:
+//   phase 2t  : group 0 in M(t), group 1 in V(t-1)
+//   phase 2t+1: group 0 in V(t), group 1 in M(t)
+// Group 0 stages the K tiles and group 1 the V tiles: a group issues the
+// global loads of tile t+1 at the start of its M(t) and writes them to LDS
+// during its V(t), into the buffer whose previous tile both groups finished
+// reading two phases earlier.
+template <int D, bool LINEAR>
+__global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
   using TL = TileLayout<D>;
   constexpr int BN = kTileN;
   constexpr int KS = D / 16;        // k-steps of the QK^T contraction
   constexpr int DB = D / 32;        // 32-wide blocks of the output's head dim
   constexpr int NB = BN / 32;       // 32-key blocks per tile
   constexpr int TILEB = BN * D * 2; // bytes of one K or V tile
-  constexpr int LPW = TILEB / 1024 / 4;  // 16-byte loads per thread per tensor and tile
-  constexpr int RPI = 1024 / TL::ROWB;   // tile rows per 1 KB slice
+  constexpr int LPT = TILEB / 4096; // 16-byte loads per thread of the staging group
+  constexpr int RPI = 1024 / TL::ROWB;  // tile rows per 1 KB slice
   static_assert(TILEB % 4096 == 0, "tile must split into 4 waves x 1 KB slices");
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];  // K0 K1 V0 V1
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wid = tid >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wid >> 2;
+  const int wg = wid & 3;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
@@ -130,51 +145,38 @@ __global__ __launch_bounds__(256, (LINEAR && QB == 1) ? 2 : 1) void attn_fwd_ker
   const WorkItem it = p.items[item_idx];
   const int hk = h / (p.Hq / p.Hkv);
 
-  // This lane's query row of block qb: wid*32*QB + qb*32 + l32.
-  bool qvalid[QB];
-  int64_t qrow[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qr = (wid * QB + qb) * 32 + l32;
-    qvalid[qb] = qr < it.q_rows;
-    qrow[qb] = (int64_t)it.q_row0 + qr;
-  }
+  // This lane's query row: wid*32 + l32.
+  const int qr = wid * 32 + l32;
+  const bool qvalid = qr < it.q_rows;
+  const int64_t qrow = (int64_t)it.q_row0 + qr;
 
   // Q fragments (B operand): Q[q][ks*16 + hi*8 .. +7]
-  bf16x8 qf[QB][KS];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const uint16_t* qp = p.q + (int64_t)b * p.q_batch_stride + (qrow[qb] * p.Hq + h) * D + hi * 8;
+  bf16x8 qf[KS];
+  {
+    const uint16_t* qp = p.q + (int64_t)b * p.q_batch_stride + (qrow * p.Hq + h) * D + hi * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if (qvalid[qb]) {
-        qf[qb][ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
+      if (qvalid) {
+        qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qf[qb][ks][e] = (__bf16)0.f;
+        for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)0.f;
       }
     }
   }
 
-  f32x16 o[QB][DB];
+  f32x16 o[DB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
+  for (int d = 0; d < DB; ++d)
 #pragma unroll
-    for (int d = 0; d < DB; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[qb][d][r] = 0.f;
+    for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
   // Running max m (log2 domain, scale folded in) and this lane's share of the
   // running sum.  m is raised lazily: only when a tile's max exceeds it by
   // more than kRescale, so the exponentials stay <= 2^kRescale.
   constexpr float kRescale = 8.f;
-  float m[QB], lsum[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m[qb] = -INFINITY;
-    lsum[qb] = 0.f;
-  }
+  float m = -INFINITY, lsum = 0.f;
 
-  // Visible key positions of each query: [vis_lo, vis_hi], plus the sinks
+  // Visible key positions of this query: [vis_lo, vis_hi], plus the sinks
   // [sstart, sink_hi] when a window is set (same sequence, causal band,
   // window p_q - p_k < W, first n_sink positions of the sequence).
   PosMap qm = p.qmap;
@@ -182,11 +184,9 @@ __global__ __launch_bounds__(256, (LINEAR && QB == 1) ? 2 : 1) void attn_fwd_ker
   PosMap km = p.kmap;
   km.rank = it.k_rank;
   const bool cw = p.mask.causal || p.mask.window > 0;
-  int32_t sstart[QB], vis_lo[QB], vis_hi[QB], sink_hi[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qr = (wid * QB + qb) * 32 + l32;
-    const int32_t pq = position(qm, it.t0 + (qvalid[qb] ? qr : 0));
+  int32_t sstart, vis_lo, vis_hi, sink_hi;
+  {
+    const int32_t pq = position(qm, it.t0 + (qvalid ? qr : 0));
     int32_t s0 = 0, s1 = p.mask.S;
     for (int i = 0; i < p.mask.nseq; ++i) {
       const int32_t lo = p.cu_seqlens[i], up = p.cu_seqlens[i + 1];
@@ -195,10 +195,10 @@ __global__ __launch_bounds__(256, (LINEAR && QB == 1) ? 2 : 1) void attn_fwd_ker
         s1 = up;
       }
     }
-    sstart[qb] = s0;
-    vis_hi[qb] = cw ? min(pq, s1 - 1) : s1 - 1;
-    vis_lo[qb] = p.mask.window > 0 ? max(s0, pq - p.mask.window + 1) : s0;
-    sink_hi[qb] = p.mask.window > 0 ? min(s0 + p.mask.n_sink - 1, vis_hi[qb]) : s0 - 1;
+    sstart = s0;
+    vis_hi = cw ? min(pq, s1 - 1) : s1 - 1;
+    vis_lo = p.mask.window > 0 ? max(s0, pq - p.mask.window + 1) : s0;
+    sink_hi = p.mask.window > 0 ? min(s0 + p.mask.n_sink - 1, vis_hi) : s0 - 1;
   }
   const int32_t kv_step = km.kind == MAP_STRIPE ? km.N : 1;
 
@@ -206,42 +206,33 @@ __global__ __launch_bounds__(256, (LINEAR && QB == 1) ? 2 : 1) void attn_fwd_ker
   const uint16_t* kbase = p.k + (int64_t)b * p.kv_batch_stride + (int64_t)it.k_row0 * kv_row_stride + hk * D;
   const uint16_t* vbase = p.v + (int64_t)b * p.kv_batch_stride + (int64_t)it.k_row0 * kv_row_stride + hk * D;
 
-  // K / V tile staging.  A tile is loaded from global memory into registers
-  // (16 bytes per load, 32-bit offsets from a buffer resource) and then
-  // written to LDS.  Loads and LDS writes are split so that K(t+1) is in
-  // flight during QK^T(t) and V(t+1) during PV(t).  The 256 threads cover the
-  // tile as 1 KB slices: thread (wave w, lane i) handles slices w*LPW + j,
-  // physical (row, chunk slot) = (slice*RPI + i / CPR, i % CPR), and so the
-  // logical chunk slot ^ swz(row) of that row.  Rows past the run's end are
-  // clamped to its last row (finite values; those keys are masked), so no
-  // load leaves the run.
+  // Tile staging by this wave's group (K for group 0, V for group 1).  A
+  // tile is loaded from global memory into registers (16 bytes per load,
+  // 32-bit offsets from a buffer resource) and later written to LDS.  The
+  // group's 256 threads cover the tile as 1 KB slices: thread (wave wg,
+  // lane i) handles slices wg*LPT + j, physical (row, chunk slot) =
+  // (slice*RPI + i / CPR, i % CPR), and so the logical chunk slot ^ swz(row)
+  // of that row.  Rows past the run's end are clamped to its last row
+  // (finite values; those keys are masked), so no load leaves the run.
   const int lrow = lane / TL::CPR;
   const int lslot = lane % TL::CPR;
   const uint32_t row_bytes = (uint32_t)kv_row_stride * 2;
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)kbase, (short)0, 0x7fffffff, kBufferRsrcWord3);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)vbase, (short)0, 0x7fffffff, kBufferRsrcWord3);
-  auto load_k = [&](i32x4 (&r)[LPW], int k0, int kend) {
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(grp ? vbase : kbase), (short)0, 0x7fffffff, kBufferRsrcWord3);
+  char* const stage_tiles = smem + grp * 2 * TILEB;
+  auto load_tile = [&](i32x4 (&r)[LPT], int k0, int kend) {
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-      const int row = (wid * LPW + j) * RPI + lrow;
-      const uint32_t off = (uint32_t)min(k0 + row, kend - 1) * row_bytes + (uint32_t)((lslot ^ TL::swz_k(row)) * 16);
-      r[j] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+    for (int j = 0; j < LPT; ++j) {
+      const int row = (wg * LPT + j) * RPI + lrow;
+      const int sw = grp ? TL::swz_v(row) : TL::swz_k(row);
+      const uint32_t off = (uint32_t)min(k0 + row, kend - 1) * row_bytes + (uint32_t)((lslot ^ sw) * 16);
+      r[j] = __builtin_amdgcn_raw_buffer_load_b128(srs, off, 0, 0);
     }
   };
-  auto load_v = [&](i32x4 (&r)[LPW], int k0, int kend) {
+  auto store_tile = [&](char* tile, const i32x4 (&r)[LPT]) {
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-      const int row = (wid * LPW + j) * RPI + lrow;
-      const uint32_t off = (uint32_t)min(k0 + row, kend - 1) * row_bytes + (uint32_t)((lslot ^ TL::swz_v(row)) * 16);
-      r[j] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
-    }
-  };
-  auto store_tile = [&](char* tile, const i32x4 (&r)[LPW]) {
-#pragma unroll
-    for (int j = 0; j < LPW; ++j)
-      *reinterpret_cast<i32x4*>(tile + (wid * LPW + j) * 1024 + lane * 16) = r[j];
+    for (int j = 0; j < LPT; ++j)
+      *reinterpret_cast<i32x4*>(tile + (wg * LPT + j) * 1024 + lane * 16) = r[j];
   };
 
   // Per-lane LDS read offsets (bytes within a tile).
@@ -253,47 +244,87 @@ __global__ __launch_bounds__(256, (LINEAR && QB == 1) ? 2 : 1) void attn_fwd_ker
   const int vchunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const int vhalf8 = (lane & 1) * 8;
 
-  // S^T[key][q] = K Q^T for one tile in LDS.  Each K fragment serves the QB
-  // query blocks; consecutive MFMAs go to different accumulators.
-  auto qk = [&](const char* tK, f32x16 (&sc)[QB][NB]) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sc[qb][kb][r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < NB; ++kb) {
-        const int row = kb * 32 + l32;
-        const int slot = (2 * ks + hi) ^ TL::swz_k(row);
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(tK + row * TL::ROWB + slot * 16);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sc[qb][kb] = mfma32(a, qf[qb][ks], sc[qb][kb]);
-      }
-    }
+  // Fragment reads.  QK op j = (ks, kb) = (j / NB, j % NB) reads the K
+  // fragment of key block kb, k-step ks; PV op j = (kb, half, d) with d
+  // fastest reads the V^T fragment of head-dim block d, keys
+  // kb*32 + 16*half + (8 keys in the P^T k-order) with two transpose reads.
+  auto read_k = [&](const char* tK, int j) -> bf16x8 {
+    const int ks = j / NB, kb = j % NB;
+    const int row = kb * 32 + l32;
+    const int slot = (2 * ks + hi) ^ TL::swz_k(row);
+    return *reinterpret_cast<const bf16x8*>(tK + row * TL::ROWB + slot * 16);
+  };
+  auto read_v = [&](const char* tV, int j) -> bf16x8 {
+    const int d = j % DB, half = (j / DB) & 1, kb = j / (2 * DB);
+    const int r0 = kb * 32 + half * 16 + vrow0;
+    const int r1 = r0 + 8;
+    const int c = 4 * d + vchunk;
+    const bf16x4 a0 = lds_read_tr(tV + r0 * TL::ROWB + ((c ^ TL::swz_v(r0)) * 16) + vhalf8);
+    const bf16x4 a1 = lds_read_tr(tV + r1 * TL::ROWB + ((c ^ TL::swz_v(r1)) * 16) + vhalf8);
+    return bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
   };
 
-  // O^T[d][q] += V^T[d][key] P^T[key][q].  Each V^T fragment serves the QB
-  // query blocks; consecutive MFMAs go to different output blocks.
-  auto pv = [&](const char* tV, const bf16x8 (&pb)[QB][NB][2]) {
+  // Matrix phase: O^T += V^T P^T for the previous tile (DO_PV), then
+  // S^T = K Q^T for the current one (DO_QK).  Only one wave per SIMD is in
+  // this phase at a time, so LDS latency is hidden inside the wave: operand
+  // fragments are read kPrefetch MFMAs ahead, across the PV -> QK boundary,
+  // and the order is pinned with scheduling groups (DS read 0x100, MFMA 0x8).
+  constexpr int NPV = NB * 2 * DB;  // PV MFMAs per tile
+  constexpr int NQK = KS * NB;      // QK MFMAs per tile
+  constexpr int PF = kPrefetch;
+  static_assert(PF <= NPV && PF <= NQK, "prefetch depth");
+  auto m_phase = [&](auto do_pv_c, auto do_qk_c, const char* tV, const char* tK, f32x16 (&sc)[NB],
+                     const bf16x8 (&pb)[NB][2]) {
+    constexpr bool DO_PV = decltype(do_pv_c)::value;
+    constexpr bool DO_QK = decltype(do_qk_c)::value;
+    bf16x8 fv[NPV], fk[NQK];
+    if constexpr (DO_PV) {
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb) {
+      for (int i = 0; i < PF; ++i) fv[i] = read_v(tV, i);
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-#pragma unroll
-        for (int d = 0; d < DB; ++d) {
-          const int r0 = kb * 32 + half * 16 + vrow0;
-          const int r1 = r0 + 8;
-          const int c = 4 * d + vchunk;
-          const bf16x4 a0 = lds_read_tr(tV + r0 * TL::ROWB + ((c ^ TL::swz_v(r0)) * 16) + vhalf8);
-          const bf16x4 a1 = lds_read_tr(tV + r1 * TL::ROWB + ((c ^ TL::swz_v(r1)) * 16) + vhalf8);
-          const bf16x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) o[qb][d] = mfma32(a, pb[qb][kb][half], o[qb][d]);
-        }
+      for (int i = 0; i < NPV; ++i) {
+        if (i + PF < NPV) fv[i + PF] = read_v(tV, i + PF);
+        else if (DO_QK) fk[i + PF - NPV] = read_k(tK, i + PF - NPV);
+        const int d = i % DB, half = (i / DB) & 1, kb = i / (2 * DB);
+        o[d] = mfma32(fv[i], pb[kb][half], o[d]);
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PF; ++i) fk[i] = read_k(tK, i);
+    }
+    if constexpr (DO_QK) {
+      const f32x16 zero = {};
+#pragma unroll
+      for (int i = 0; i < NQK; ++i) {
+        if (i + PF < NQK) fk[i + PF] = read_k(tK, i + PF);
+        const int ks = i / NB, kb = i % NB;
+        sc[kb] = mfma32(fk[i], qf[ks], ks == 0 ? zero : sc[kb]);
+      }
+    }
+    // scheduling groups, in issue order
+    if constexpr (DO_PV) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
+#pragma unroll
+      for (int i = 0; i < NPV - PF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < PF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if constexpr (DO_QK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    } else {
+      __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+    }
+    if constexpr (DO_QK) {
+#pragma unroll
+      for (int i = 0; i < NQK - PF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < PF; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
   };
 
@@ -302,15 +333,15 @@ __global__ __launch_bounds__(256, (LINEAR && QB == 1) ? 2 : 1) void attn_fwd_ker
   // For layouts whose key positions step linearly through a run, the visible
   // du form at most two intervals (window band, sinks); their bounds are
   // computed once, shifted by 4*hi, and compared with the compile-time c.
-  auto apply_mask = [&](f32x16 (&sc)[NB], int qb, int k0, int kend) {
+  auto apply_mask = [&](f32x16 (&sc)[NB], int k0, int kend) {
     const int32_t kend_du = kend - 1 - k0;
     if constexpr (LINEAR) {
       const int32_t pk0 = position(km, k0);
       const int32_t sh = 4 * hi;
-      const int32_t lo = ceil_div(vis_lo[qb] - pk0, kv_step) - sh;
-      const int32_t up = min(floor_div(vis_hi[qb] - pk0, kv_step), kend_du) - sh;
-      const int32_t slo = ceil_div(sstart[qb] - pk0, kv_step) - sh;
-      const int32_t sup = min(floor_div(sink_hi[qb] - pk0, kv_step), kend_du) - sh;
+      const int32_t lo = ceil_div(vis_lo - pk0, kv_step) - sh;
+      const int32_t up = min(floor_div(vis_hi - pk0, kv_step), kend_du) - sh;
+      const int32_t slo = ceil_div(sstart - pk0, kv_step) - sh;
+      const int32_t sup = min(floor_div(sink_hi - pk0, kv_step), kend_du) - sh;
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb) {
 #pragma unroll
@@ -327,169 +358,170 @@ __global__ __launch_bounds__(256, (LINEAR && QB == 1) ? 2 : 1) void attn_fwd_ker
         for (int r = 0; r < 16; ++r) {
           const int du = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
           const int32_t pk = position(km, k0 + du);
-          const bool vis = (du <= kend_du) & (pk <= vis_hi[qb]) &
-                           ((pk >= vis_lo[qb]) | ((pk >= sstart[qb]) & (pk <= sink_hi[qb])));
+          const bool vis = (du <= kend_du) & (pk <= vis_hi) &
+                           ((pk >= vis_lo) | ((pk >= sstart) & (pk <= sink_hi)));
           sc[kb][r] = vis ? sc[kb][r] : -INFINITY;
         }
       }
     }
   };
 
-  int ri = it.run_begin;
-  if (ri < it.run_end) {
+  // Tiles of this item: the runs' key ranges cut into BN-key tiles.
+  int n_tiles = 0;
+  for (int r = it.run_begin; r < it.run_end; ++r) {
+    const Run rr = p.runs[r];
+    n_tiles += (rr.k_end - rr.k_begin + BN - 1) / BN;
+  }
+
+  if (n_tiles > 0) {
+    // This wave's tile cursor (tile t of its current step).
+    int ri = it.run_begin;
     Run run = p.runs[ri];
     int k0 = run.k_begin;
-    int buf = 0;
     {
-      i32x4 kr[LPW], vr[LPW];
-      load_k(kr, k0, run.k_end);
-      load_v(vr, k0, run.k_end);
-      store_tile(smem, kr);
-      store_tile(smem + 2 * TILEB, vr);
+      i32x4 r0[LPT];
+      load_tile(r0, k0, run.k_end);
+      store_tile(stage_tiles, r0);
     }
     __syncthreads();
-    while (true) {
-      // next tile (uniform across the workgroup)
-      int nk0 = k0 + BN;
-      int nri = ri;
-      Run nrun = run;
+
+    f32x16 s[NB];
+    bf16x8 pb[NB][2];
+    i32x4 stg[LPT];
+    int nri = ri, nk0 = k0;
+    Run nrun = run;
+    // Cursor of tile t+1, and its global loads into stg.
+    auto prefetch_next = [&]() {
+      nk0 = k0 + BN;
+      nri = ri;
+      nrun = run;
       if (nk0 >= run.k_end) {
         nri = ri + 1;
-        if (nri < it.run_end) {
-          nrun = p.runs[nri];
-          nk0 = nrun.k_begin;
-        }
+        nrun = p.runs[nri];
+        nk0 = nrun.k_begin;
       }
-      const bool has_next = nri < it.run_end;
-
-      i32x4 kr[LPW];
-      if (has_next) load_k(kr, nk0, nrun.k_end);
-
-      f32x16 s[QB][NB];
-      qk(smem + buf * TILEB, s);
-      if (!run.full) {
+      load_tile(stg, nk0, nrun.k_end);
+    };
+    // V(t): mask, online softmax (log2 domain, lazy rescale), stage t+1.
+    auto v_phase = [&](int t) {
+      if (!run.full) apply_mask(s, k0, run.k_end);
+      float mt = -INFINITY;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) apply_mask(s[qb], qb, k0, run.k_end);
+      for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, mt),
+                                                         __builtin_bit_cast(unsigned, mt), false, false);
+        mt = fmaxf(__builtin_bit_cast(float, (unsigned)sw[0]), __builtin_bit_cast(float, (unsigned)sw[1]));
       }
-
-      // online softmax (log2 domain) with lazy rescaling
-      float alpha[QB];
-      bf16x8 pb[QB][NB][2];
+      mt *= p.scale_log2;
+      const float m_new = (mt > m + kRescale) ? mt : m;
+      const float alpha = (m_new == m || m_new == -INFINITY) ? 1.f : fast_exp2(m - m_new);
+      m = m_new;
+      lsum *= alpha;
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float mt = -INFINITY;
+      for (int kb = 0; kb < NB; ++kb) {
 #pragma unroll
-        for (int kb = 0; kb < NB; ++kb)
+        for (int half = 0; half < 2; ++half) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[qb][kb][r]);
-        mt = fmaxf(mt, __shfl_xor(mt, 32)) * p.scale_log2;
-        const float m_new = (mt > m[qb] + kRescale) ? mt : m[qb];
-        alpha[qb] = (m_new == m[qb] || m_new == -INFINITY) ? 1.f : fast_exp2(m[qb] - m_new);
-        m[qb] = m_new;
-        lsum[qb] *= alpha[qb];
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-#pragma unroll
-        for (int kb = 0; kb < NB; ++kb) {
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-              const float p0 = fast_exp2(s[qb][kb][half * 8 + e] * p.scale_log2 - m_use);
-              const float p1 = fast_exp2(s[qb][kb][half * 8 + e + 1] * p.scale_log2 - m_use);
-              lsum[qb] += p0 + p1;
-              const bf16x2 pk2 = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
-              pb[qb][kb][half][e] = pk2[0];
-              pb[qb][kb][half][e + 1] = pk2[1];
-            }
+          for (int e = 0; e < 8; e += 2) {
+            const float p0 = fast_exp2(s[kb][half * 8 + e] * p.scale_log2 - m_use);
+            const float p1 = fast_exp2(s[kb][half * 8 + e + 1] * p.scale_log2 - m_use);
+            lsum += p0 + p1;
+            const bf16x2 pk2 = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
+            pb[kb][half][e] = pk2[0];
+            pb[kb][half][e + 1] = pk2[1];
           }
         }
       }
-
-      // K(t+1) -> LDS (its buffer was last read by QK(t-1), before the barrier)
-      if (has_next) store_tile(smem + (buf ^ 1) * TILEB, kr);
-      i32x4 vr[LPW];
-      if (has_next) load_v(vr, nk0, nrun.k_end);
-
-      bool any_rescale = false;
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) any_rescale |= alpha[qb] != 1.f;
-      if (__builtin_amdgcn_readfirstlane((int)(__ballot(any_rescale) != 0ull))) {
+      if (__builtin_amdgcn_readfirstlane((int)(__ballot(alpha != 1.f) != 0ull))) {
         asm volatile("" ::: "memory");  // keep this a branch (rarely taken)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
+        for (int d = 0; d < DB; ++d)
 #pragma unroll
-          for (int d = 0; d < DB; ++d)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[qb][d][r] *= alpha[qb];
+          for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
       }
+      if (t + 1 < n_tiles) {
+        store_tile(stage_tiles + ((t + 1) & 1) * TILEB, stg);
+        ri = nri;
+        run = nrun;
+        k0 = nk0;
+      }
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
 
-      pv(smem + (2 + buf) * TILEB, pb);
-
-      // V(t+1) -> LDS (its buffer was last read by PV(t-1), before the barrier)
-      if (has_next) store_tile(smem + (2 + (buf ^ 1)) * TILEB, vr);
+    // Group 1 starts one phase late (group 0 runs M(0) meanwhile) and group
+    // 0 ends one phase early, so both pass the same number of barriers.
+    if (grp == 1) __syncthreads();
+    if (n_tiles > 1) prefetch_next();
+    m_phase(F_{}, T_{}, nullptr, smem, s, pb);
+    __syncthreads();
+    v_phase(0);
+    __syncthreads();
+    for (int t = 1; t < n_tiles; ++t) {
+      if (t + 1 < n_tiles) prefetch_next();
+      m_phase(T_{}, T_{}, smem + (2 + ((t - 1) & 1)) * TILEB, smem + (t & 1) * TILEB, s, pb);
       __syncthreads();
-      if (!has_next) break;
-      ri = nri;
-      run = nrun;
-      k0 = nk0;
-      buf ^= 1;
+      v_phase(t);
+      __syncthreads();
     }
+    m_phase(T_{}, F_{}, smem + (2 + ((n_tiles - 1) & 1)) * TILEB, nullptr, s, pb);
+    if (grp == 0) __syncthreads();
   }
 
   // epilogue: O = O_acc / l, LSE = m ln 2 + ln l; or merge into (out, lse)
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float ltot = lsum[qb] + __shfl_xor(lsum[qb], 32);
-    if (!qvalid[qb]) continue;
-    const float lse_new = ltot > 0.f ? m[qb] * kLn2 + logf(ltot) : -INFINITY;
-    float* lse_ptr = p.lse + ((int64_t)b * p.Hq + h) * p.Lq_buf + qrow[qb];
-    const int64_t obase = (int64_t)b * p.o_batch_stride + (qrow[qb] * p.Hq + h) * D;
-    float wa = 0.f, wb = ltot > 0.f ? 1.f / ltot : 0.f;
-    float lse_out = lse_new;
-    if (p.accumulate) {
-      const float la = *lse_ptr;
-      const float M = fmaxf(la, lse_new);
-      if (lse_new == -INFINITY || M == -INFINITY) continue;  // nothing to merge
-      const float Lm = M + logf(expf(la - M) + expf(lse_new - M));
-      wa = expf(la - Lm);
-      wb *= expf(lse_new - Lm);
-      lse_out = Lm;
-    }
-    if (p.out_f32) {
-      float* op = static_cast<float*>(p.out) + obase;
-#pragma unroll
-      for (int d = 0; d < DB; ++d) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int dd = d * 32 + 8 * g + 4 * hi;
-          float4 v = make_float4(o[qb][d][4 * g] * wb, o[qb][d][4 * g + 1] * wb, o[qb][d][4 * g + 2] * wb,
-                                 o[qb][d][4 * g + 3] * wb);
-          if (wa != 0.f) {
-            const float4 a = *reinterpret_cast<const float4*>(op + dd);
-            v.x += wa * a.x;
-            v.y += wa * a.y;
-            v.z += wa * a.z;
-            v.w += wa * a.w;
-          }
-          *reinterpret_cast<float4*>(op + dd) = v;
-        }
-      }
-    } else {
-      uint16_t* op = static_cast<uint16_t*>(p.out) + obase;
-#pragma unroll
-      for (int d = 0; d < DB; ++d) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int dd = d * 32 + 8 * g + 4 * hi;
-          const bf16x2 lo = __builtin_convertvector((f32x2){o[qb][d][4 * g] * wb, o[qb][d][4 * g + 1] * wb}, bf16x2);
-          const bf16x2 up = __builtin_convertvector((f32x2){o[qb][d][4 * g + 2] * wb, o[qb][d][4 * g + 3] * wb}, bf16x2);
-          *reinterpret_cast<uint2*>(op + dd) =
-              make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, up));
-        }
-      }
-    }
-    if (hi == 0) *lse_ptr = lse_out;
+  const float ltot = lsum + __shfl_xor(lsum, 32);
+  if (!qvalid) return;
+  const float lse_new = ltot > 0.f ? m * kLn2 + logf(ltot) : -INFINITY;
+  float* lse_ptr = p.lse + ((int64_t)b * p.Hq + h) * p.Lq_buf + qrow;
+  const int64_t obase = (int64_t)b * p.o_batch_stride + (qrow * p.Hq + h) * D;
+  float wa = 0.f, wb = ltot > 0.f ? 1.f / ltot : 0.f;
+  float lse_out = lse_new;
+  if (p.accumulate) {
+    const float la = *lse_ptr;
+    const float M = fmaxf(la, lse_new);
+    if (lse_new == -INFINITY || M == -INFINITY) return;  // nothing to merge
+    const float Lm = M + logf(expf(la - M) + expf(lse_new - M));
+    wa = expf(la - Lm);
+    wb *= expf(lse_new - Lm);
+    lse_out = Lm;
   }
+  if (p.out_f32) {
+    float* op = static_cast<float*>(p.out) + obase;
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dd = d * 32 + 8 * g + 4 * hi;
+        float4 v = make_float4(o[d][4 * g] * wb, o[d][4 * g + 1] * wb, o[d][4 * g + 2] * wb, o[d][4 * g + 3] * wb);
+        if (wa != 0.f) {
+          const float4 a = *reinterpret_cast<const float4*>(op + dd);
+          v.x += wa * a.x;
+          v.y += wa * a.y;
+          v.z += wa * a.z;
+          v.w += wa * a.w;
+        }
+        *reinterpret_cast<float4*>(op + dd) = v;
+      }
+    }
+  } else {
+    uint16_t* op = static_cast<uint16_t*>(p.out) + obase;
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dd = d * 32 + 8 * g + 4 * hi;
+        const bf16x2 lo = __builtin_convertvector((f32x2){o[d][4 * g] * wb, o[d][4 * g + 1] * wb}, bf16x2);
+        const bf16x2 up = __builtin_convertvector((f32x2){o[d][4 * g + 2] * wb, o[d][4 * g + 3] * wb}, bf16x2);
+        *reinterpret_cast<uint2*>(op + dd) =
+            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, up));
+      }
+    }
+  }
+  if (hi == 0) *lse_ptr = lse_out;
 }
 
 }  // namespace
@@ -501,24 +533,18 @@ usp_status launch_attn_fwd(const AttnParams& p, int D, hipStream_t stream) {
     set_error("attention grid too large (%lld workgroups)", (long long)total);
     return USP_ERR_UNSUPPORTED;
   }
-  const dim3 grid((unsigned)total), block(256);
-  const bool linear = !(p.kmap.kind == MAP_STRIPE && p.kmap.b > 1);
-  const bool wide = p.tile_m == 256;
-  if (!wide && p.tile_m != 128) {
+  if (p.tile_m != 256) {
     set_error("internal: unsupported query tile %d", p.tile_m);
     return USP_ERR_UNSUPPORTED;
   }
+  const dim3 grid((unsigned)total), block(512);
+  const bool linear = !(p.kmap.kind == MAP_STRIPE && p.kmap.b > 1);
   TimingScope ts(K_ATTN, stream);
-#define USP_LAUNCH(DD, LIN, QBB) hipLaunchKernelGGL((attn_fwd_kernel<DD, LIN, QBB>), grid, block, 0, stream, p)
-  // Only 128-row tiles (QB = 1) are instantiated; see choose_tile_m.
-  if (wide) {
-    set_error("internal: 256-row query tiles are not built");
-    return USP_ERR_UNSUPPORTED;
-  }
+#define USP_LAUNCH(DD, LIN) hipLaunchKernelGGL((attn_fwd_kernel<DD, LIN>), grid, block, 0, stream, p)
   if (D == 128) {
-    if (linear) USP_LAUNCH(128, true, 1); else USP_LAUNCH(128, false, 1);
+    if (linear) USP_LAUNCH(128, true); else USP_LAUNCH(128, false);
   } else {
-    if (linear) USP_LAUNCH(64, true, 1); else USP_LAUNCH(64, false, 1);
+    if (linear) USP_LAUNCH(64, true); else USP_LAUNCH(64, false);
   }
 #undef USP_LAUNCH
   const hipError_t e = hipGetLastError();

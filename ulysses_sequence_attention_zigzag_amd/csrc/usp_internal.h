@@ -90,18 +90,14 @@ struct Run {
 };
 static_assert(sizeof(Run) == 16, "Run layout");
 
-// Tile shape of the attention kernel: 64 keys per iteration; 128 or 256
-// query rows per workgroup (4 waves x 1 or 2 blocks of 32 rows).
+// Tile shape of the attention kernel: 64 keys per iteration, 256 query rows
+// per workgroup (8 waves of 32 rows).
 constexpr int kTileN = 64;
 
-// Query rows per workgroup for a rank whose rows are `qmap`.  The kernel
-// supports 128 (two waves per SIMD, 238 registers each) and 256 (one wave per
-// SIMD holding two 32-row blocks, which halves LDS traffic per FLOP but needs
-// more than 256 registers and ran at ~63% of the 128-row speed on MI355X);
-// 128 is used.
+// Query rows per workgroup for a rank whose rows are `qmap`.
 inline int32_t choose_tile_m(const PosMap& qmap) {
   (void)qmap;
-  return 128;
+  return 256;
 }
 
 // Host-side plan for one launch (all ranks of one step, or one block call).
@@ -118,7 +114,7 @@ struct BlockSpec {
   int32_t Lk;        // rows of the kv rank
   int32_t q_row_base;
   int32_t k_row_base;
-  int32_t tile_m;    // query rows per item (128 or 256)
+  int32_t tile_m;    // query rows per item
 };
 
 // Appends the items / runs of one block (not yet sorted).
@@ -155,7 +151,7 @@ struct AttnParams {
   int32_t Hkv;
   int32_t out_f32;
   int32_t accumulate;
-  int32_t tile_m;           // query rows per item: 128 or 256
+  int32_t tile_m;           // query rows per item (256)
   float scale_log2;         // softmax_scale * log2(e)
   PosMap qmap;              // rank field overridden per item
   PosMap kmap;

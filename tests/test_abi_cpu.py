@@ -246,7 +246,7 @@ def test_planner_against_oracle_visibility(case, accumulate):
             items, runs, tm, tn = usp.plan_block(
                 L, L, 128, mask="positional", qmap=usp.posmap(impl, N, i, S, b), kmap=usp.posmap(impl, N, j, S, b),
                 causal=causal, window=window, n_sink=n_sink, cu_seqlens=cu, accumulate=accumulate)
-            assert tm in (128, 256) and tn == 64
+            assert tm in (128, 256) and tn == 128
             _check_plan(L, L, qpos, kpos, vis, accumulate, items, runs, tn, tm)
 
 

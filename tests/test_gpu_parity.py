@@ -297,17 +297,21 @@ def test_ring_permuted_input_and_bf16_output(w):
     assert_parity(out, lse, O_ref, L_ref, "bf16 output")
 
 
-def test_ring_deterministic_and_writes_every_row():
-    w = SMALL_RING[3]
+# both attention kernels: positions linear in every run (zigzag, USP) and
+# striped blocks of 4 tokens (per-element positions), all ranks in one launch
+@pytest.mark.parametrize("w", [SMALL_RING[3], SMALL_RING[7]], ids=lambda w: f"{w.name}-b{w.stripe_block}")
+def test_ring_deterministic_and_writes_every_row(w):
     q, k, v = w.make_inputs()
     call = usp.RingCall(q.cuda(), k.cuda(), v.cuda(), impl=w.impl, ring_degree=w.ring_degree,
-                        ulysses_degree=w.ulysses_degree, causal=True, rank=w.rank)
+                        ulysses_degree=w.ulysses_degree, stripe_block=w.stripe_block, causal=True,
+                        rank=w.rank)
     call.out.fill_(float("nan"))
     call.lse.fill_(float("nan"))
     o1, l1 = (t.clone() for t in call.run())
     assert not torch.isnan(o1).any() and not torch.isnan(l1).any()
-    o2, l2 = call.run()
-    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for _ in range(4):
+        o2, l2 = call.run()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
 @pytest.mark.parametrize("name", ["zigzag_causal_small", "ring_swa", "varlen_streaming"])

@@ -1,7 +1,7 @@
 // Block attention forward for one ring step on gfx950 (CDNA4).
 //
 // One workgroup = 8 waves = 256 query rows of one (batch, head); each wave
-// owns 32 rows.  Per key tile of 64 keys:
+// owns 32 rows.  Per key tile (128 keys, or 64 for striped blocks):
 //   S^T = K Q^T      v_mfma_f32_32x32x16_bf16, K from LDS (A operand),
 //                    Q resident in VGPRs (B operand);
 //   mask             only in partial runs (the planner marks fully visible
@@ -33,6 +33,8 @@
 
 namespace usp {
 namespace {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -71,7 +73,6 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // Word 3 of a raw (unswizzled, stride 0) buffer resource on gfx9-family GPUs.
 constexpr int kBufferRsrcWord3 = 0x00020000;
@@ -107,14 +108,25 @@ struct TileLayout {
 // every SIMD one wave feeds the matrix core while the other does its softmax:
 //   phase 2t  : group 0 in M(t), group 1 in V(t-1)
 //   phase 2t+1: group 0 in V(t), group 1 in M(t)
-// Group 0 stages the K tiles and group 1 the V tiles: a group issues the
-// global loads of tile t+1 at the start of its M(t) and writes them to LDS
-// during its V(t), into the buffer whose previous tile both groups finished
-// reading two phases earlier.
+// Group 0 stages the K tiles and group 1 the V tiles: right after the last
+// LDS read of its M(t) a group issues the loads of tile t+1 straight into
+// LDS, into the buffer whose previous tile both groups have finished
+// reading, and waits for them at the end of its V(t), before the barrier
+// that hands the phase over.  Phase barriers carry no memory fence: every
+// LDS read of a matrix phase is consumed by its MFMAs before the phase ends.
 template <int D, bool LINEAR>
 __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
   using TL = TileLayout<D>;
-  constexpr int BN = kTileN;
+  // Keys per tile.  The LINEAR kernel stages its tiles with buffer loads
+  // straight into LDS and runs 128-key tiles; the other kernel (striped
+  // blocks of more than one token) needs more registers for its mask, spills
+  // a little, and keeps the register-staged path with 64-key tiles (a spill
+  // reload tracked by the same counter as an in-flight LDS load is not a
+  // combination this kernel relies on).  The planner's full runs come in
+  // multiples of kTileN, which both divide.
+  constexpr int BN = LINEAR ? 128 : 64;
+  constexpr bool kDma = LINEAR;
+  static_assert(kTileN % BN == 0, "planner granularity");
   constexpr int KS = D / 16;        // k-steps of the QK^T contraction
   constexpr int DB = D / 32;        // 32-wide blocks of the output's head dim
   constexpr int NB = BN / 32;       // 32-key blocks per tile
@@ -206,14 +218,15 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
   const uint16_t* kbase = p.k + (int64_t)b * p.kv_batch_stride + (int64_t)it.k_row0 * kv_row_stride + hk * D;
   const uint16_t* vbase = p.v + (int64_t)b * p.kv_batch_stride + (int64_t)it.k_row0 * kv_row_stride + hk * D;
 
-  // Tile staging by this wave's group (K for group 0, V for group 1).  A
-  // tile is loaded from global memory into registers (16 bytes per load,
-  // 32-bit offsets from a buffer resource) and later written to LDS.  The
-  // group's 256 threads cover the tile as 1 KB slices: thread (wave wg,
-  // lane i) handles slices wg*LPT + j, physical (row, chunk slot) =
-  // (slice*RPI + i / CPR, i % CPR), and so the logical chunk slot ^ swz(row)
-  // of that row.  Rows past the run's end are clamped to its last row
-  // (finite values; those keys are masked), so no load leaves the run.
+  // Tile staging by this wave's group (K for group 0, V for group 1): buffer
+  // loads straight into LDS (16 bytes per lane, 32-bit offsets from a buffer
+  // resource; lane i of a load lands at 16*i past the wave-uniform LDS
+  // address).  The group's 256 threads cover the tile as 1 KB slices:
+  // thread (wave wg, lane i) handles slices wg*LPT + j, physical (row, chunk
+  // slot) = (slice*RPI + i / CPR, i % CPR), and so loads the logical chunk
+  // slot ^ swz(row) of that row.  Rows past the run's end are clamped to its
+  // last row (finite values; those keys are masked), so no load leaves the
+  // run.
   const int lrow = lane / TL::CPR;
   const int lslot = lane % TL::CPR;
   const uint32_t row_bytes = (uint32_t)kv_row_stride * 2;
@@ -233,6 +246,15 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
 #pragma unroll
     for (int j = 0; j < LPT; ++j)
       *reinterpret_cast<i32x4*>(tile + (wg * LPT + j) * 1024 + lane * 16) = r[j];
+  };
+  auto dma_tile = [&](char* tile, int k0, int kend) {
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      const int row = (wg * LPT + j) * RPI + lrow;
+      const int sw = grp ? TL::swz_v(row) : TL::swz_k(row);
+      const uint32_t off = (uint32_t)min(k0 + row, kend - 1) * row_bytes + (uint32_t)((lslot ^ sw) * 16);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (__attribute__((address_space(3))) void*)(tile + (wg * LPT + j) * 1024), 16, off, 0, 0, 0);
+    }
   };
 
   // Per-lane LDS read offsets (bytes within a tile).
@@ -378,7 +400,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
     int ri = it.run_begin;
     Run run = p.runs[ri];
     int k0 = run.k_begin;
-    {
+    if constexpr (kDma) {
+      dma_tile(stage_tiles, k0, run.k_end);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    } else {
       i32x4 r0[LPT];
       load_tile(r0, k0, run.k_end);
       store_tile(stage_tiles, r0);
@@ -387,10 +412,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
 
     f32x16 s[NB];
     bf16x8 pb[NB][2];
-    i32x4 stg[LPT];
+    i32x4 stg[LPT];  // register-staged tile t+1 (kernel without LDS loads)
     int nri = ri, nk0 = k0;
     Run nrun = run;
-    // Cursor of tile t+1, and its global loads into stg.
+    // Cursor of tile t+1 (and, register-staged, its global loads).
     auto prefetch_next = [&]() {
       nk0 = k0 + BN;
       nri = ri;
@@ -400,9 +425,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
         nrun = p.runs[nri];
         nk0 = nrun.k_begin;
       }
-      load_tile(stg, nk0, nrun.k_end);
+      if constexpr (!kDma) load_tile(stg, nk0, nrun.k_end);
     };
-    // V(t): mask, online softmax (log2 domain, lazy rescale), stage t+1.
+    // V(t): mask, online softmax (log2 domain, lazy rescale); tile t+1 lands.
     auto v_phase = [&](int t) {
       if (!run.full) apply_mask(s, k0, run.k_end);
       float mt = -INFINITY;
@@ -444,7 +469,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
           for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
       }
       if (t + 1 < n_tiles) {
-        store_tile(stage_tiles + ((t + 1) & 1) * TILEB, stg);
+        if constexpr (kDma)
+          __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this group's tile t+1 is in LDS
+        else
+          store_tile(stage_tiles + ((t + 1) & 1) * TILEB, stg);
         ri = nri;
         run = nrun;
         k0 = nk0;
@@ -453,23 +481,38 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
     using T_ = std::true_type;
     using F_ = std::false_type;
 
+    // Phase barrier: no memory fence (the matrix phase's LDS reads are all
+    // consumed by its MFMAs before it ends, and tile loads are waited for
+    // explicitly), only a compiler ordering point.
+    auto phase_barrier = [&]() {
+      if constexpr (kDma)
+        asm volatile("s_barrier" ::: "memory");
+      else
+        __syncthreads();  // also completes this wave's LDS stores of the staged tile
+    };
     // Group 1 starts one phase late (group 0 runs M(0) meanwhile) and group
     // 0 ends one phase early, so both pass the same number of barriers.
-    if (grp == 1) __syncthreads();
+    if (grp == 1) phase_barrier();
     if (n_tiles > 1) prefetch_next();
     m_phase(F_{}, T_{}, nullptr, smem, s, pb);
-    __syncthreads();
+    if constexpr (kDma) {
+      if (n_tiles > 1) dma_tile(stage_tiles + TILEB, nk0, nrun.k_end);
+    }
+    phase_barrier();
     v_phase(0);
-    __syncthreads();
+    phase_barrier();
     for (int t = 1; t < n_tiles; ++t) {
       if (t + 1 < n_tiles) prefetch_next();
       m_phase(T_{}, T_{}, smem + (2 + ((t - 1) & 1)) * TILEB, smem + (t & 1) * TILEB, s, pb);
-      __syncthreads();
+      if constexpr (kDma) {
+        if (t + 1 < n_tiles) dma_tile(stage_tiles + ((t + 1) & 1) * TILEB, nk0, nrun.k_end);
+      }
+      phase_barrier();
       v_phase(t);
-      __syncthreads();
+      phase_barrier();
     }
     m_phase(T_{}, F_{}, smem + (2 + ((n_tiles - 1) & 1)) * TILEB, nullptr, s, pb);
-    if (grp == 0) __syncthreads();
+    if (grp == 0) phase_barrier();
   }
 
   // epilogue: O = O_acc / l, LSE = m ln 2 + ln l; or merge into (out, lse)

@@ -90,9 +90,10 @@ struct Run {
 };
 static_assert(sizeof(Run) == 16, "Run layout");
 
-// Tile shape of the attention kernel: 64 keys per iteration, 256 query rows
-// per workgroup (8 waves of 32 rows).
-constexpr int kTileN = 64;
+// Key granularity of the planner's full runs (their lengths are multiples
+// of it) and the largest key tile of the attention kernel (128 keys; 256
+// query rows per workgroup, 8 waves of 32 rows).
+constexpr int kTileN = 128;
 
 // Query rows per workgroup for a rank whose rows are `qmap`.
 inline int32_t choose_tile_m(const PosMap& qmap) {

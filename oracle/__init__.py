@@ -13,8 +13,10 @@ Modules
   ring_ref       the ring-decomposed float64 reference: per (rank, step)
                  block attention with its partial output and log-sum-exp, and
                  the associative max/logsumexp merge of partials
+  backward_ref   the gradients (dQ, dK, dV) of masked softmax attention from
+                 the chain rule, per ring step and summed over the ring
 
 Every function is pinned by ``tests/test_oracle_*.py`` against brute force,
 a library routine, closed forms, or values and invariants the pages state.
 """
-from . import index_ref, attention_ref, ring_ref  # noqa: F401
+from . import index_ref, attention_ref, ring_ref, backward_ref  # noqa: F401

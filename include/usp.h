@@ -158,6 +158,44 @@ usp_status usp_block_attn_fwd(const void* q, const void* k, const void* v, void*
                               const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int nseq,
                               usp_dtype out_dt, int accumulate, void* stream);
 
+/* ------------------------------------------------------------- backward
+ * The backward of block attention, as the ring runs it [LCA "Ring
+ * Attention": the backward passes the same KV pieces, and their gradients,
+ * around the ring, from the saved output and log-sum-exp].  With the final
+ * (merged over all steps) output O and LSE of the query rows, one step's
+ * gradient terms for every visible (query t, key u) of one (batch, head) are
+ *   P = exp(s - LSE_t),  dP = <dO_t, v_u>,  dS = P (dP - delta_t),
+ *   dQ_t += softmax_scale * sum_u dS k_u,
+ *   dK_u += softmax_scale * sum_t dS q_t,   dV_u += sum_t P dO_t,
+ * with s as in usp_block_attn_fwd (bf16 products, f32 accumulation) and
+ * delta_t = <dO_t, O_t>.  Because P uses the final LSE, the terms of the
+ * ring steps add up to the gradients of the whole attention.
+ *
+ * usp_attn_bwd_preprocess: delta [B,H,L] f32 = rowsum(dout * out), with out
+ *   [B,L,H,D] in out_dt (bf16 or f32) and dout [B,L,H,D] bf16; D a multiple
+ *   of 8 up to 256.
+ * usp_block_attn_bwd: q, dout [B,Lq,Hq,D] and k, v [B,Lk,Hkv,D] bf16; lse
+ *   and delta [B,Hq,Lq] f32 (a row with LSE = -inf contributes nothing);
+ *   dq [B,Lq,Hq,D], dk, dv [B,Lk,Hkv,D] f32 are ACCUMULATED into (+=): the
+ *   caller zeroes them once and calls once per ring step.  dK / dV of a KV
+ *   head sum over the query heads sharing it (GQA / MQA).  Mask arguments,
+ *   softmax_scale, cu_seqlens and D are as in usp_block_attn_fwd; EMPTY
+ *   leaves the gradients unchanged.  dq must not alias dk or dv.  Each
+ *   gradient element is written by one workgroup (deterministic, no
+ *   atomics).  The first call with a new shape/mask builds and uploads its
+ *   tile plans (synchronous copies); later calls reuse them. */
+usp_status usp_attn_bwd_preprocess(const void* out, usp_dtype out_dt, const void* dout, float* delta,
+                                   int64_t B, int64_t L, int64_t H, int64_t D, void* stream);
+
+usp_status usp_block_attn_bwd(const void* q, const void* k, const void* v, const void* dout,
+                              const float* lse, const float* delta, float* dq, float* dk, float* dv,
+                              int64_t B, int64_t Lq, int64_t Lk, int64_t Hq, int64_t Hkv, int64_t D,
+                              float softmax_scale, usp_mask_class mask,
+                              const usp_posmap* qmap, const usp_posmap* kmap,
+                              int causal, int window, int n_sink,
+                              const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int nseq,
+                              void* stream);
+
 /* ---------------------------------------------------------------- merge
  * In-place associative combine of a partial into a running result, rows
  * [row_begin, row_end) of the sequence axis [LCA "Tree Attention": max and
@@ -234,6 +272,21 @@ usp_status usp_plan_block(int64_t Lq, int64_t Lk, int64_t D, usp_mask_class mask
                           int32_t* items, int64_t items_cap, int32_t* runs, int64_t runs_cap,
                           int64_t* n_items, int64_t* n_runs, int32_t* tile_m, int32_t* tile_n);
 
+/* The transposed plan usp_block_attn_bwd's dK / dV kernel runs (host only,
+ * no device work): one item per tile of *tile_k keys of the KV rank, 8 int32
+ * each: {first key row, its local key index, keys in the tile, KV rank,
+ * first query row (0), query rank, run_begin, run_end}; runs {t_begin,
+ * t_end, full, 0} of local query rows, `full` = 1 when every key of the item
+ * is visible to every query row of the run (length a multiple of *tile_q).
+ * Query rows outside every run see no key of the item; tiles no query sees
+ * get no item.  Items come ordered by decreasing work. */
+usp_status usp_plan_block_kv(int64_t Lq, int64_t Lk, int64_t D, usp_mask_class mask,
+                             const usp_posmap* qmap, const usp_posmap* kmap,
+                             int causal, int window, int n_sink,
+                             const int32_t* cu_seqlens_host, int nseq,
+                             int32_t* items, int64_t items_cap, int32_t* runs, int64_t runs_cap,
+                             int64_t* n_items, int64_t* n_runs, int32_t* tile_k, int32_t* tile_q);
+
 /* ---------------------------------------------------- kernel timing
  * Instrumentation for benchmarks.  While enabled, every kernel launch of the
  * library is bracketed by two hipEvents recorded on its stream; read sums
@@ -244,7 +297,10 @@ typedef enum {
   USP_KERNEL_ATTN = 0,      /* block attention (usp_block_attn_fwd and ring steps) */
   USP_KERNEL_PERMUTE = 1,   /* token permutation, output reorder / conversion      */
   USP_KERNEL_RELAYOUT = 2,  /* Ulysses relayout                                     */
-  USP_KERNEL_MERGE = 3      /* separate LSE merge                                   */
+  USP_KERNEL_MERGE = 3,     /* separate LSE merge                                   */
+  USP_KERNEL_BWD_DQ = 4,    /* backward: dQ kernel of usp_block_attn_bwd            */
+  USP_KERNEL_BWD_DKDV = 5,  /* backward: dK / dV kernel of usp_block_attn_bwd       */
+  USP_KERNEL_BWD_DELTA = 6  /* backward: usp_attn_bwd_preprocess                    */
 } usp_kernel_class;
 
 usp_status usp_timing_enable(int enable);

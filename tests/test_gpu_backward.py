@@ -1,0 +1,267 @@
+"""GPU parity of the backward entry points against the float64 oracle
+(oracle/backward_ref.py).
+
+Bar (derived from the arithmetic): the kernels take bf16 q, k, v, dO, round
+P and dS to bf16 before the gradient products (relative error at most 2^-9
+each) and accumulate in fp32, so an entry's error is at most about
+2^-9 * sum |terms| and in practice far less; the bar is
+    max |grad - ref| <= 1e-2 * max |ref|      per gradient tensor,
+which a dropped term, a wrong sign, a wrong mask or a transposed operand
+exceeds by an order of magnitude.  delta (fp32 sum of bf16 x bf16/f32
+products) must be within 1e-5 * sum |dO * O| per row.  LSE and delta given to
+the kernels come from the oracle's forward in float64, rounded to f32.
+"""
+import sys
+
+import pytest
+import torch
+
+import seeded_inputs as si
+import ulysses_sequence_attention_zigzag_amd as usp
+from oracle import index_ref as ix
+from oracle.attention_ref import attention_ref
+from oracle.backward_ref import block_attention_bwd_ref, ring_backward_ref
+from oracle.ring_ref import block_attention_ref
+
+pytestmark = pytest.mark.gpu
+
+GRAD_TOL = 1e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a device"
+    usp.lib()  # raises if libusp.so is missing
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def assert_grad(got, ref, what):
+    g = got.detach().cpu().double()
+    assert not torch.isnan(g).any(), f"{what}: NaN"
+    scale = float(ref.abs().max()) if ref.numel() else 0.0
+    err = float((g - ref).abs().max()) if ref.numel() else 0.0
+    say(f"  {what}: max|ref|={scale:.3e} max|err|={err:.3e} ({err / max(scale, 1e-30):.2e} rel)")
+    if scale == 0.0:
+        assert err == 0.0, f"{what}: expected zeros"
+    else:
+        assert err <= GRAD_TOL * scale, f"{what}: error {err} > {GRAD_TOL} * {scale}"
+
+
+def _inputs(B, Lq, Lk, Hq, Hkv, D, seed):
+    q = si.randn_bf16((B, Lq, Hq, D), seed, 0)
+    k = si.randn_bf16((B, Lk, Hkv, D), seed, 1)
+    v = si.randn_bf16((B, Lk, Hkv, D), seed, 2)
+    do = si.randn_bf16((B, Lq, Hq, D), seed, 3)
+    return q, k, v, do
+
+
+def _delta(do, O):
+    return (do.double() * O.double()).sum(-1).transpose(1, 2).contiguous()   # [B,H,L]
+
+
+# ---------------------------------------------------------------- delta
+@pytest.mark.parametrize("B,L,H,D", [(1, 1, 1, 64), (2, 333, 3, 128), (1, 1000, 4, 64)])
+@pytest.mark.parametrize("odt", [torch.float32, torch.bfloat16])
+def test_preprocess_delta(B, L, H, D, odt):
+    say(f"delta B={B} L={L} H={H} D={D} {odt}")
+    o = si.randn_bf16((B, L, H, D), 3, 0).to(odt)
+    do = si.randn_bf16((B, L, H, D), 3, 1)
+    delta = usp.attn_bwd_preprocess(o.cuda(), do.cuda())
+    ref = _delta(do, o)
+    bound = 1e-5 * (do.double() * o.double()).abs().sum(-1).transpose(1, 2)
+    err = (delta.cpu().double() - ref).abs()
+    say(f"  max err {float(err.max()):.3e}")
+    assert (err <= bound + 1e-30).all()
+
+
+# ---------------------------------------------------------------- block backward
+EXPLICIT = [
+    # mask, B, Lq, Lk, Hq, Hkv, D
+    ("full", 1, 32, 32, 1, 1, 64),
+    ("full", 2, 300, 200, 4, 2, 128),
+    ("causal", 1, 256, 256, 2, 2, 64),
+    ("causal", 2, 333, 333, 4, 1, 128),
+    ("causal_strict", 1, 300, 300, 3, 1, 128),
+    ("causal_strict", 1, 257, 257, 2, 2, 64),
+    ("full", 1, 64, 1000, 2, 1, 128),
+]
+
+
+def _explicit_pos(mask, Lq, Lk):
+    if mask == "full":
+        return list(range(Lq)), list(range(Lk)), False
+    if mask == "causal":
+        return list(range(Lq)), list(range(Lk)), True
+    return list(range(Lq)), list(range(1, Lk + 1)), True
+
+
+@pytest.mark.parametrize("case", EXPLICIT)
+def test_block_bwd_explicit_classes(case):
+    mask, B, Lq, Lk, Hq, Hkv, D = case
+    say(f"block_bwd explicit {case}")
+    q, k, v, do = _inputs(B, Lq, Lk, Hq, Hkv, D, seed=21)
+    scale = D ** -0.5
+    pq, pk, causal = _explicit_pos(mask, Lq, Lk)
+    O, LSE = block_attention_ref(q, k, v, pq, pk, scale=scale, causal=causal, window=0, n_sink=0)
+    delta = _delta(do, O)
+    rq, rk, rv = block_attention_bwd_ref(q, k, v, do, LSE, delta, pq, pk, scale=scale, causal=causal, window=0,
+                                         n_sink=0)
+    dq, dk, dv = usp.block_attn_bwd(q.cuda(), k.cuda(), v.cuda(), do.cuda(), LSE.float().cuda(),
+                                    delta.float().cuda(), mask=mask)
+    torch.cuda.synchronize()
+    assert_grad(dq, rq, "dq")
+    assert_grad(dk, rk, "dk")
+    assert_grad(dv, rv, "dv")
+
+
+def test_block_bwd_accumulates_and_empty_is_noop():
+    say("block_bwd accumulate / empty")
+    B, L, Hq, Hkv, D = 1, 200, 2, 1, 64
+    q, k, v, do = _inputs(B, L, L, Hq, Hkv, D, seed=23)
+    pos = list(range(L))
+    O, LSE = block_attention_ref(q, k, v, pos, pos, scale=D ** -0.5, causal=True, window=0, n_sink=0)
+    delta = _delta(do, O)
+    rq, rk, rv = block_attention_bwd_ref(q, k, v, do, LSE, delta, pos, pos, scale=D ** -0.5, causal=True,
+                                         window=0, n_sink=0)
+    g = torch.Generator().manual_seed(5)
+    init = [torch.randn(t.shape, generator=g, dtype=torch.float32) for t in (rq, rk, rv)]
+    dq, dk, dv = (t.clone().cuda() for t in init)
+    args = (q.cuda(), k.cuda(), v.cuda(), do.cuda(), LSE.float().cuda(), delta.float().cuda())
+    usp.block_attn_bwd(*args, dq=dq, dk=dk, dv=dv, mask="causal")
+    before = [t.clone() for t in (dq, dk, dv)]
+    usp.block_attn_bwd(*args, dq=dq, dk=dk, dv=dv, mask="empty")
+    torch.cuda.synchronize()
+    for a, b in zip(before, (dq, dk, dv)):
+        assert torch.equal(a, b)
+    for got, i0, ref, name in zip((dq, dk, dv), init, (rq, rk, rv), ("dq", "dk", "dv")):
+        assert_grad(got.cpu() - i0, ref, name + " accumulated")
+
+
+def _forward_ref(q, k, v, scale, causal, window, n_sink, cu):
+    """Float64 (O [B,S,H,D], LSE [B,H,S]) of natural-order q, k, v (varlen: B = 1)."""
+    if cu is None:
+        return attention_ref(q, k, v, softmax_scale=scale, causal=causal, window=window, n_sink=n_sink)
+    O, LSE = attention_ref(q[0], k[0], v[0], softmax_scale=scale, causal=causal, window=window, n_sink=n_sink,
+                           cu_seqlens=cu)
+    return O.unsqueeze(0), LSE.unsqueeze(0)
+
+
+POSITIONAL = [
+    # impl, S, N, b, causal, window, n_sink, cu, Hq, Hkv, D
+    ("zigzag", 1024, 4, 1, True, 0, 0, None, 4, 4, 64),
+    ("zigzag", 2 * 4 * 200, 4, 1, True, 0, 0, None, 4, 2, 128),
+    ("stripe", 2048, 8, 1, True, 0, 0, None, 4, 1, 128),
+    ("stripe", 1536, 4, 3, True, 0, 0, None, 2, 1, 64),
+    ("basic", 4096, 4, 1, False, 300, 0, None, 2, 2, 128),
+    ("basic", 4096, 4, 1, False, 300, 4, [0, 512, 2000, 4096], 2, 2, 128),
+    ("basic", 3000, 3, 1, True, 0, 0, [0, 1, 700, 701, 2900, 3000], 2, 1, 64),
+    ("zigzag", 3072, 4, 1, False, 300, 2, None, 2, 2, 128),
+]
+
+
+@pytest.mark.parametrize("case", POSITIONAL)
+def test_block_bwd_positional_steps(case):
+    impl, S, N, b, causal, window, n_sink, cu, Hq, Hkv, D = case
+    say(f"block_bwd positional {case}")
+    B, scale = 1, 0.1
+    q, k, v, do = _inputs(B, S, S, Hq, Hkv, D, seed=25)
+    O, LSE = _forward_ref(q, k, v, scale, causal, window, n_sink, cu)
+    delta = _delta(do, O)
+    i = N - 1
+    pos_q = ix.rank_positions(impl, S, N, i, b)
+    qi, doi = q[:, pos_q].contiguous(), do[:, pos_q].contiguous()
+    lse_i, del_i = LSE[:, :, pos_q].contiguous(), delta[:, :, pos_q].contiguous()
+    for j in sorted({0, i, (i + 1) % N, N // 2}):
+        pos_k = ix.rank_positions(impl, S, N, j, b)
+        kj, vj = k[:, pos_k].contiguous(), v[:, pos_k].contiguous()
+        rq, rk, rv = block_attention_bwd_ref(qi, kj, vj, doi, lse_i, del_i, pos_q, pos_k, scale=scale,
+                                             causal=causal, window=window, n_sink=n_sink, cu_seqlens=cu)
+        dq, dk, dv = usp.block_attn_bwd(qi.cuda(), kj.cuda(), vj.cuda(), doi.cuda(), lse_i.float().cuda(),
+                                        del_i.float().cuda(), qmap=usp.posmap(impl, N, i, S, b),
+                                        kmap=usp.posmap(impl, N, j, S, b), causal=causal, window=window,
+                                        n_sink=n_sink, cu_seqlens=cu, softmax_scale=scale)
+        torch.cuda.synchronize()
+        assert_grad(dq, rq, f"i={i} j={j} dq")
+        assert_grad(dk, rk, f"i={i} j={j} dk")
+        assert_grad(dv, rv, f"i={i} j={j} dv")
+
+
+# ---------------------------------------------------------------- ring of block calls
+RING = [
+    # impl, S, N, b, causal, window, n_sink, cu, Hq, Hkv, D
+    ("zigzag", 1200, 3, 1, True, 0, 0, None, 2, 1, 128),
+    ("zigzag", 1024, 4, 1, True, 0, 0, None, 4, 2, 64),
+    ("stripe", 2048, 4, 1, True, 0, 0, None, 4, 1, 128),
+    ("stripe", 1536, 4, 3, True, 0, 0, None, 2, 2, 64),
+    ("basic", 2048, 4, 1, False, 250, 4, [0, 128, 1000, 2048], 2, 2, 128),
+]
+
+
+def _ring_gpu(impl, S, N, b, causal, window, n_sink, cu, q, k, v, do, LSE, delta, scale):
+    """The backward ring on one device: host i at round s meets KV piece
+    (i - s) mod N; dQ stays with host i, dK / dV with the piece."""
+    pos = [ix.rank_positions(impl, S, N, r, b) for r in range(N)]
+    dev = lambda t: t.contiguous().cuda()  # noqa: E731
+    qs = [dev(q[:, p]) for p in pos]
+    dos = [dev(do[:, p]) for p in pos]
+    ks = [dev(k[:, p]) for p in pos]
+    vs = [dev(v[:, p]) for p in pos]
+    lses = [dev(LSE[:, :, p].float()) for p in pos]
+    dels = [dev(delta[:, :, p].float()) for p in pos]
+    dq = [torch.zeros(t.shape, dtype=torch.float32, device="cuda") for t in qs]
+    dk = [torch.zeros(t.shape, dtype=torch.float32, device="cuda") for t in ks]
+    dv = [torch.zeros(t.shape, dtype=torch.float32, device="cuda") for t in ks]
+    for s in range(N):
+        for i in range(N):
+            j = (i - s) % N
+            usp.block_attn_bwd(qs[i], ks[j], vs[j], dos[i], lses[i], dels[i], dq=dq[i], dk=dk[j], dv=dv[j],
+                               qmap=usp.posmap(impl, N, i, S, b), kmap=usp.posmap(impl, N, j, S, b),
+                               causal=causal, window=window, n_sink=n_sink, cu_seqlens=cu, softmax_scale=scale)
+    torch.cuda.synchronize()
+    out = []
+    for parts, like in ((dq, q), (dk, k), (dv, v)):
+        full = torch.zeros(like.shape, dtype=torch.float64)
+        for r in range(N):
+            full[:, pos[r]] = parts[r].cpu().double()
+        out.append(full)
+    return out
+
+
+@pytest.mark.parametrize("case", RING)
+def test_ring_bwd_of_block_calls(case):
+    impl, S, N, b, causal, window, n_sink, cu, Hq, Hkv, D = case
+    say(f"ring_bwd {case}")
+    scale = D ** -0.5
+    q, k, v, do = _inputs(1, S, S, Hq, Hkv, D, seed=27)
+    O, LSE = _forward_ref(q, k, v, scale, causal, window, n_sink, cu)
+    if cu is None:
+        ref = ring_backward_ref(q, k, v, do, impl=impl, N=N, stripe_block=b, softmax_scale=scale, causal=causal,
+                                window=window, n_sink=n_sink)
+    else:
+        ref = [t.unsqueeze(0) for t in ring_backward_ref(q[0], k[0], v[0], do[0], impl=impl, N=N,
+                                                         stripe_block=b, softmax_scale=scale, causal=causal,
+                                                         window=window, n_sink=n_sink, cu_seqlens=cu)]
+    delta = _delta(do, O)
+    got = _ring_gpu(impl, S, N, b, causal, window, n_sink, cu, q, k, v, do, LSE, delta, scale)
+    for g, r, name in zip(got, ref, ("dq", "dk", "dv")):
+        assert_grad(g, r, name)
+
+
+def test_block_bwd_deterministic():
+    say("block_bwd deterministic")
+    impl, S, N = "zigzag", 4096, 2
+    L = S // N
+    q, k, v, do = _inputs(1, L, L, 4, 1, 128, seed=29)
+    lse = torch.full((1, 4, L), 9.0)
+    delta = torch.randn((1, 4, L), generator=torch.Generator().manual_seed(3))
+    args = [t.cuda() for t in (q, k, v, do, lse, delta)]
+    kw = dict(qmap=usp.posmap(impl, N, 1, S), kmap=usp.posmap(impl, N, 0, S), causal=True)
+    first = usp.block_attn_bwd(*args, **kw)
+    for _ in range(3):
+        again = usp.block_attn_bwd(*args, **kw)
+        for a, b in zip(first, again):
+            assert torch.equal(a, b)

@@ -71,6 +71,13 @@ _SIGS = {
                         _I32, _P, _I32, _I32, _P, _I64, _P, _I64, ctypes.POINTER(_I64),
                         ctypes.POINTER(_I64), ctypes.POINTER(ctypes.c_int32),
                         ctypes.POINTER(ctypes.c_int32)], _I32),
+    "usp_plan_block_kv": ([_I64, _I64, _I64, _I32, ctypes.POINTER(PosMap), ctypes.POINTER(PosMap), _I32, _I32,
+                           _I32, _P, _I32, _P, _I64, _P, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64),
+                           ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)], _I32),
+    "usp_attn_bwd_preprocess": ([_P, _I32, _P, _P, _I64, _I64, _I64, _I64, _P], _I32),
+    "usp_block_attn_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64,
+                            ctypes.c_float, _I32, ctypes.POINTER(PosMap), ctypes.POINTER(PosMap), _I32, _I32,
+                            _I32, _P, _P, _I32, _P], _I32),
     "usp_timing_enable": ([_I32], _I32),
     "usp_timing_reset": ([], _I32),
     "usp_timing_read": ([_I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64)], _I32),
@@ -193,6 +200,59 @@ def block_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, mask: s
     return out, lse
 
 
+def attn_bwd_preprocess(out: torch.Tensor, dout: torch.Tensor, delta: Optional[torch.Tensor] = None,
+                        stream=None) -> torch.Tensor:
+    """delta [B,H,L] f32 = rowsum(dout * out) (usp_attn_bwd_preprocess); out [B,L,H,D] bf16 or f32,
+    dout [B,L,H,D] bf16."""
+    B, L, H, D = out.shape
+    if tuple(dout.shape) != (B, L, H, D):
+        raise ValueError("dout must have the shape of out")
+    if delta is None:
+        delta = torch.empty((B, H, L), dtype=torch.float32, device=out.device)
+    _check(lib().usp_attn_bwd_preprocess(_dev(out, None, "out"), DT[out.dtype], _dev(dout, torch.bfloat16, "dout"),
+                                         _dev(delta, torch.float32, "delta"), B, L, H, D, _stream(stream)))
+    return delta
+
+
+def block_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor,
+                   delta: torch.Tensor, *, dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                   dv: Optional[torch.Tensor] = None, mask: str = "positional", qmap: Optional[PosMap] = None,
+                   kmap: Optional[PosMap] = None, causal: bool = False, window: int = 0, n_sink: int = 0,
+                   cu_seqlens=None, softmax_scale: float = 0.0,
+                   stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """One ring step's gradient terms (usp_block_attn_bwd), ADDED into f32 dq [B,Lq,Hq,D] and dk, dv
+    [B,Lk,Hkv,D] (zero-initialised here when not given).  q, dout [B,Lq,Hq,D], k/v [B,Lk,Hkv,D] bf16;
+    lse, delta [B,Hq,Lq] f32 of the final forward."""
+    B, Lq, Hq, D = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    if tuple(dout.shape) != (B, Lq, Hq, D):
+        raise ValueError("dout must have the shape of q")
+    for name, t in (("lse", lse), ("delta", delta)):
+        if tuple(t.shape) != (B, Hq, Lq):
+            raise ValueError(f"{name} must be [B,Hq,Lq]")
+    if dq is None:
+        dq = torch.zeros((B, Lq, Hq, D), dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.zeros((B, Lk, Hkv, D), dtype=torch.float32, device=q.device)
+    if dv is None:
+        dv = torch.zeros((B, Lk, Hkv, D), dtype=torch.float32, device=q.device)
+    for name, t, shp in (("dq", dq, (B, Lq, Hq, D)), ("dk", dk, (B, Lk, Hkv, D)), ("dv", dv, (B, Lk, Hkv, D))):
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{name} must be {list(shp)}")
+    cu_dev, cu_host, nseq, keep = _cu(cu_seqlens, q.device)
+    _check(lib().usp_block_attn_bwd(
+        _dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"),
+        _dev(dout, torch.bfloat16, "dout"), _dev(lse, torch.float32, "lse"), _dev(delta, torch.float32, "delta"),
+        _dev(dq, torch.float32, "dq"), _dev(dk, torch.float32, "dk"), _dev(dv, torch.float32, "dv"),
+        B, Lq, Lk, Hq, Hkv, D, float(softmax_scale), MASK[mask], ctypes.byref(qmap) if qmap else None,
+        ctypes.byref(kmap) if kmap else None, int(causal), int(window), int(n_sink),
+        ctypes.c_void_p(cu_dev.data_ptr()) if cu_dev is not None else None,
+        ctypes.c_void_p(cu_host.data_ptr()) if cu_host is not None else None, nseq, _stream(stream)))
+    if keep is not None:
+        torch.cuda.current_stream().synchronize()  # cu_seqlens copies must outlive the launch
+    return dq, dk, dv
+
+
 def lse_merge(out_acc: torch.Tensor, lse_acc: torch.Tensor, out_part: torch.Tensor, lse_part: torch.Tensor,
               row_begin: int = 0, row_end: Optional[int] = None, stream=None) -> None:
     """In-place merge of (out_part, lse_part) into (out_acc, lse_acc)."""
@@ -273,7 +333,8 @@ def ring_fwd(q, k, v, **kw) -> Tuple[torch.Tensor, torch.Tensor]:
 
 
 # ---------------------------------------------------------------- timing
-KERNEL_CLASSES = {"attn": 0, "permute": 1, "relayout": 2, "merge": 3}
+KERNEL_CLASSES = {"attn": 0, "permute": 1, "relayout": 2, "merge": 3, "bwd_dq": 4, "bwd_dkdv": 5,
+                  "bwd_delta": 6}
 
 
 def timing_enable(on: bool = True) -> None:
@@ -315,3 +376,27 @@ def plan_block(Lq: int, Lk: int, D: int = 128, *, mask: str = "positional", qmap
                             ctypes.c_void_p(runs.data_ptr()), nr.value, ctypes.byref(ni), ctypes.byref(nr),
                             ctypes.byref(tm), ctypes.byref(tn)))
     return items[:ni.value], runs[:nr.value], tm.value, tn.value
+
+
+def plan_block_kv(Lq: int, Lk: int, D: int = 128, *, mask: str = "positional", qmap: Optional[PosMap] = None,
+                  kmap: Optional[PosMap] = None, causal: bool = False, window: int = 0, n_sink: int = 0,
+                  cu_seqlens=None):
+    """Host-only transposed plan of the dK / dV kernel (usp_plan_block_kv):
+    (items [n,8] int32, runs [m,4] int32, tile_k, tile_q)."""
+    L = lib()
+    cu_host = None if cu_seqlens is None else torch.tensor(list(cu_seqlens), dtype=torch.int32)
+    nseq = 0 if cu_host is None else cu_host.numel() - 1
+    cu_p = ctypes.c_void_p(cu_host.data_ptr()) if cu_host is not None else None
+    ni, nr = _I64(0), _I64(0)
+    tk, tq = ctypes.c_int32(0), ctypes.c_int32(0)
+    qm = ctypes.byref(qmap) if qmap else None
+    km = ctypes.byref(kmap) if kmap else None
+    _check(L.usp_plan_block_kv(Lq, Lk, D, MASK[mask], qm, km, int(causal), int(window), int(n_sink), cu_p, nseq,
+                               None, 0, None, 0, ctypes.byref(ni), ctypes.byref(nr), ctypes.byref(tk),
+                               ctypes.byref(tq)))
+    items = torch.zeros((max(1, ni.value), 8), dtype=torch.int32)
+    runs = torch.zeros((max(1, nr.value), 4), dtype=torch.int32)
+    _check(L.usp_plan_block_kv(Lq, Lk, D, MASK[mask], qm, km, int(causal), int(window), int(n_sink), cu_p, nseq,
+                               ctypes.c_void_p(items.data_ptr()), ni.value, ctypes.c_void_p(runs.data_ptr()),
+                               nr.value, ctypes.byref(ni), ctypes.byref(nr), ctypes.byref(tk), ctypes.byref(tq)))
+    return items[:ni.value], runs[:nr.value], tk.value, tq.value

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libusp.so")
-SOURCES = ["api.cpp", "plan.cpp", "timing.cpp", "permute.hip", "lse_merge.hip", "attn_fwd.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "timing.cpp", "permute.hip", "lse_merge.hip", "attn_fwd.hip", "attn_bwd.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -355,6 +355,39 @@ usp_status usp_plan_block(int64_t Lq, int64_t Lk, int64_t D, usp_mask_class mask
   return USP_OK;
 }
 
+usp_status usp_plan_block_kv(int64_t Lq, int64_t Lk, int64_t D, usp_mask_class mask, const usp_posmap* qmap,
+                             const usp_posmap* kmap, int causal, int window, int n_sink,
+                             const int32_t* cu_seqlens_host, int nseq, int32_t* items, int64_t items_cap,
+                             int32_t* runs, int64_t runs_cap, int64_t* n_items, int64_t* n_runs,
+                             int32_t* tile_k, int32_t* tile_q) {
+  USP_CHECK(n_items && n_runs, USP_ERR_INVALID_ARG, "null count pointer");
+  USP_CHECK(Lq >= 0 && Lk >= 0 && Lq <= kMaxI32 / 2 && Lk <= kMaxI32 / 2, USP_ERR_INVALID_ARG, "bad Lq/Lk");
+  USP_CHECK(D == 64 || D == 128, USP_ERR_UNSUPPORTED, "head_dim must be 64 or 128, got %lld", (long long)D);
+  BlockMaskSetup su;
+  usp_status st = setup_block_mask(Lq, Lk, mask, qmap, kmap, causal, window, n_sink, cu_seqlens_host,
+                                   nseq, 1, &su);
+  if (st != USP_OK) return st;
+  Plan plan;
+  if (!su.empty) {
+    BlockSpec blk{su.qmap, su.kmap, (int32_t)Lq, (int32_t)Lk, 0, 0, kBwdTileM};
+    plan_block_kv(blk, su.ms, cu_seqlens_host, kBwdTileK, kBwdTileQ, plan);
+  }
+  finalize_plan(plan);
+  *n_items = (int64_t)plan.items.size();
+  *n_runs = (int64_t)plan.runs.size();
+  if (tile_k) *tile_k = kBwdTileK;
+  if (tile_q) *tile_q = kBwdTileQ;
+  if (items) {
+    USP_CHECK(items_cap >= *n_items, USP_ERR_INVALID_ARG, "items buffer too small");
+    std::memcpy(items, plan.items.data(), plan.items.size() * sizeof(WorkItem));
+  }
+  if (runs) {
+    USP_CHECK(runs_cap >= *n_runs, USP_ERR_INVALID_ARG, "runs buffer too small");
+    std::memcpy(runs, plan.runs.data(), plan.runs.size() * sizeof(Run));
+  }
+  return USP_OK;
+}
+
 usp_status usp_block_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                               int64_t B, int64_t Lq, int64_t Lk, int64_t Hq, int64_t Hkv, int64_t D,
                               float softmax_scale, usp_mask_class mask, const usp_posmap* qmap,
@@ -415,6 +448,87 @@ usp_status usp_block_attn_fwd(const void* q, const void* k, const void* v, void*
   p.kmap = su.kmap;
   p.mask = su.ms;
   return launch_attn_fwd(p, (int)D, as_stream(stream));
+}
+
+usp_status usp_attn_bwd_preprocess(const void* out, usp_dtype out_dt, const void* dout, float* delta,
+                                   int64_t B, int64_t L, int64_t H, int64_t D, void* stream) {
+  USP_CHECK(out && dout && delta, USP_ERR_INVALID_ARG, "null tensor pointer");
+  USP_CHECK(B >= 0 && L >= 0 && H >= 1, USP_ERR_INVALID_ARG, "bad sizes");
+  USP_CHECK(D >= 8 && D % 8 == 0 && D <= 256, USP_ERR_UNSUPPORTED, "head_dim must be a multiple of 8 in [8, 256]");
+  USP_CHECK(out_dt == USP_DT_BF16 || out_dt == USP_DT_F32, USP_ERR_INVALID_ARG, "bad out dtype");
+  USP_CHECK(B * L * H <= kMaxI32 * 8, USP_ERR_UNSUPPORTED, "tensor too large");
+  USP_CHECK(L <= kMaxI32, USP_ERR_UNSUPPORTED, "sequence too long");
+  return launch_bwd_delta(out, out_dt == USP_DT_F32, static_cast<const uint16_t*>(dout), delta, B, L, H, D,
+                          as_stream(stream));
+}
+
+usp_status usp_block_attn_bwd(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                              const float* delta, float* dq, float* dk, float* dv, int64_t B, int64_t Lq,
+                              int64_t Lk, int64_t Hq, int64_t Hkv, int64_t D, float softmax_scale,
+                              usp_mask_class mask, const usp_posmap* qmap, const usp_posmap* kmap, int causal,
+                              int window, int n_sink, const int32_t* cu_seqlens_dev,
+                              const int32_t* cu_seqlens_host, int nseq, void* stream) {
+  USP_CHECK(q && k && v && dout && lse && delta && dq && dk && dv, USP_ERR_INVALID_ARG, "null tensor pointer");
+  USP_CHECK(B >= 1 && Lq >= 0 && Lk >= 0 && Hq >= 1 && Hkv >= 1, USP_ERR_INVALID_ARG, "bad sizes");
+  USP_CHECK(D == 64 || D == 128, USP_ERR_UNSUPPORTED, "head_dim must be 64 or 128, got %lld", (long long)D);
+  USP_CHECK(Hq % Hkv == 0, USP_ERR_INVALID_ARG, "Hq (%lld) must be a multiple of Hkv (%lld)", (long long)Hq, (long long)Hkv);
+  USP_CHECK((cu_seqlens_host == nullptr) == (cu_seqlens_dev == nullptr), USP_ERR_INVALID_ARG,
+            "cu_seqlens must be given on both host and device, or neither");
+  USP_CHECK(B * Lq <= kMaxI32 && B * Lk <= kMaxI32 && Lq * Hq <= kMaxI32 * 8, USP_ERR_UNSUPPORTED, "tensor too large");
+  USP_CHECK(std::isfinite(softmax_scale), USP_ERR_INVALID_ARG, "softmax_scale must be finite");
+  USP_CHECK(Lk * Hkv * D * 2 < ((int64_t)1 << 31) && Lq * Hq * D * 2 < ((int64_t)1 << 31), USP_ERR_UNSUPPORTED,
+            "one batch row of q or k/v must be under 2 GiB (32-bit tile offsets)");
+  BlockMaskSetup su;
+  usp_status st = setup_block_mask(Lq, Lk, mask, qmap, kmap, causal, window, n_sink, cu_seqlens_host,
+                                   nseq, B, &su);
+  if (st != USP_OK) return st;
+  if (Lq == 0 || Lk == 0 || su.empty) return USP_OK;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)D);
+
+  const std::string base = std::to_string(Lq) + "|" + std::to_string(Lk) + "|" + map_key(su.qmap) + "|" +
+                           map_key(su.kmap) + "|" + mask_key(su.ms) + "|" +
+                           cu_key(su.ms.nseq ? cu_seqlens_host : nullptr, nseq);
+  DevicePlan dpq, dpk;
+  st = device_plan("bwdq|" + base, [&](Plan& plan) {
+    build_block_plan(su, (int32_t)Lq, (int32_t)Lk, cu_seqlens_host, 1, kBwdTileM, plan);
+  }, &dpq);
+  if (st != USP_OK) return st;
+  st = device_plan("bwdkv|" + base, [&](Plan& plan) {
+    BlockSpec blk{su.qmap, su.kmap, (int32_t)Lq, (int32_t)Lk, 0, 0, kBwdTileM};
+    plan_block_kv(blk, su.ms, cu_seqlens_host, kBwdTileK, kBwdTileQ, plan);
+  }, &dpk);
+  if (st != USP_OK) return st;
+
+  BwdParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.lse = lse;
+  p.delta = delta;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.cu_seqlens = su.ms.nseq ? cu_seqlens_dev : nullptr;
+  p.q_batch_stride = Lq * Hq * D;
+  p.kv_batch_stride = Lk * Hkv * D;
+  p.Lq_buf = (int32_t)Lq;
+  p.B = (int32_t)B;
+  p.Hq = (int32_t)Hq;
+  p.Hkv = (int32_t)Hkv;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.qmap = su.qmap;
+  p.kmap = su.kmap;
+  p.mask = su.ms;
+  BwdParams pq = p, pk = p;
+  pq.items = dpq.items;
+  pq.runs = dpq.runs;
+  pq.n_items = dpq.n_items;
+  pk.items = dpk.items;
+  pk.runs = dpk.runs;
+  pk.n_items = dpk.n_items;
+  return launch_bwd(pq, pk, (int)D, as_stream(stream));
 }
 
 // ------------------------------------------------------------ virtual ring

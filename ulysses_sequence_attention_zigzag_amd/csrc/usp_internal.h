@@ -121,6 +121,15 @@ struct BlockSpec {
 // Appends the items / runs of one block (not yet sorted).
 void plan_block(const BlockSpec& blk, const MaskSpec& ms, const int32_t* cu_host, int accumulate,
                 Plan& plan);
+// Transposed plan for the dK / dV kernel: one item per tile of `tile_k` keys
+// of the KV rank (inside one of its monotone pieces), with runs of local
+// query rows; item fields: q_row0 = first key row in the k/v buffers, t0 =
+// its local key index, q_rows = keys in the tile, q_rank = KV rank, k_row0 =
+// row of local query 0 of the query rank in the q buffers, k_rank = query
+// rank.  Full runs are multiples of `q_gran` rows.  Tiles no query sees get
+// no item.
+void plan_block_kv(const BlockSpec& blk, const MaskSpec& ms, const int32_t* cu_host, int32_t tile_k,
+                   int32_t q_gran, Plan& plan);
 // Orders items by decreasing work (stable).
 void finalize_plan(Plan& plan);
 
@@ -161,6 +170,41 @@ struct AttnParams {
 
 // Launchers (return USP_ERR_HIP on launch failure).
 usp_status launch_attn_fwd(const AttnParams& p, int D, hipStream_t stream);
+// Backward kernels' parameters (passed by value): the dQ kernel reads the
+// forward plan (tile_m = kBwdTileM), the dK / dV kernel the transposed plan
+// (tile_k = kBwdTileK, query granularity kBwdTileQ).
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dout;
+  const float* lse;          // [B, Hq, Lq_buf]
+  const float* delta;        // [B, Hq, Lq_buf]
+  float* dq;                 // [B, Lq, Hq, D], accumulated into
+  float* dk;                 // [B, Lk, Hkv, D], accumulated into
+  float* dv;
+  const WorkItem* items;
+  const Run* runs;
+  const int32_t* cu_seqlens;
+  int64_t q_batch_stride;    // elements between batch rows of q / dout / dq
+  int64_t kv_batch_stride;   // elements between batch rows of k / v / dk / dv
+  int32_t Lq_buf;
+  int32_t n_items;
+  int32_t B;
+  int32_t Hq;
+  int32_t Hkv;
+  float scale;               // softmax_scale
+  float scale_log2;          // softmax_scale * log2(e)
+  PosMap qmap;
+  PosMap kmap;
+  MaskSpec mask;
+};
+constexpr int kBwdTileM = 128;  // query rows per dQ workgroup
+constexpr int kBwdTileK = 128;  // keys per dK / dV workgroup
+constexpr int kBwdTileQ = 64;   // query rows per dK / dV iteration
+usp_status launch_bwd(const BwdParams& pq, const BwdParams& pkv, int D, hipStream_t stream);
+usp_status launch_bwd_delta(const void* out, int out_f32, const uint16_t* dout, float* delta, int64_t B,
+                            int64_t L, int64_t H, int64_t D, hipStream_t stream);
 
 // Generic row gather: out row i (of n_out rows per outer slice) copies
 // row src(i) of `in`; see permute.hip for the index kinds.
@@ -196,7 +240,15 @@ usp_status launch_lse_merge(float* out_acc, float* lse_acc, const float* out_par
 void set_error(const char* fmt, ...);
 
 // Kernel classes of the timing facility (usp_timing_*).
-enum KernelClass : int { K_ATTN = 0, K_PERMUTE = 1, K_RELAYOUT = 2, K_MERGE = 3 };
+enum KernelClass : int {
+  K_ATTN = 0,
+  K_PERMUTE = 1,
+  K_RELAYOUT = 2,
+  K_MERGE = 3,
+  K_BWD_DQ = 4,
+  K_BWD_DKDV = 5,
+  K_BWD_DELTA = 6
+};
 
 // Brackets one launch with hipEvents on `stream` while timing is enabled.
 class TimingScope {

@@ -256,6 +256,40 @@ size_t usp_ring_fwd_workspace_size(const usp_ring_args* a);
  * by the caller, 256-byte aligned. */
 usp_status usp_ring_fwd(const usp_ring_args* a, void* workspace, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------ virtual ring backward
+ * The backward of usp_ring_fwd on one device [LCA "Ring Attention": the
+ * backward runs the same ring from the saved output and LSE, dK / dV of a
+ * KV piece accumulating as it travels].  `fwd` holds the forward call's
+ * arguments unchanged (merge_mode is ignored); its out and lse are now
+ * INPUTS: the forward's results, in the order and dtype it wrote them.
+ * dout (bf16) has the shape and order of fwd.out.  Outputs, f32,
+ * overwritten:
+ *   rank == -1: dq [B,S,Hq,D], dk / dv [B,S,Hkv,D], the full gradients, in
+ *     the input's order;
+ *   rank >= 0 : dq [B,L,Hq/ud,D] of the rank's rows in its local order
+ *     (complete: the rank meets every KV piece), and dk / dv
+ *     [B,S,Hkv/ud,D] in rank-major order (piece j at rows j*L): the
+ *     contributions of this rank's queries to every piece, which a real ring
+ *     would sum over the hosts.
+ * Steps: staging of q, k, v as in usp_ring_fwd; delta =
+ * usp_attn_bwd_preprocess(out, dout); N steps of usp_block_attn_bwd (every
+ * host of a step in one launch per kernel); natural-order outputs are
+ * un-permuted at the end. */
+typedef struct usp_ring_bwd_args {
+  usp_ring_args fwd;
+  const void* dout;
+  float* dq;
+  float* dk;
+  float* dv;
+} usp_ring_bwd_args;
+
+/* Bytes of device workspace usp_ring_bwd needs (0 for invalid arguments). */
+size_t usp_ring_bwd_workspace_size(const usp_ring_bwd_args* a);
+
+/* Runs the backward ring.  workspace: caller-owned device memory of at least
+ * usp_ring_bwd_workspace_size(a) bytes, 256-byte aligned. */
+usp_status usp_ring_bwd(const usp_ring_bwd_args* a, void* workspace, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------ tile scheduler
  * Host-only inspection of the tile plan usp_block_attn_fwd would run (no
  * device work).  Items are 8 int32 each: {q_row0, t0, q_rows, q_rank, k_row0,

@@ -162,3 +162,38 @@ def test_kv_planner_full_runs_dominate_large_causal():
     n = L // tk
     # each key tile sees its own tk rows partially and the rest after it fully
     assert part == n * tk and full == sum(L - (i + 1) * tk for i in range(n))
+
+
+# ------------------------------------------------------- ring backward
+def test_ring_bwd_validation_and_workspace():
+    from test_abi_cpu import _ring_args
+    L = usp.lib()
+
+    def bargs(**kw):
+        grads = {n: kw.pop(n, 0x20000) for n in ("dout", "dq", "dk", "dv")}
+        b = usp.RingBwdArgs()
+        b.fwd = _ring_args(**kw)
+        b.dout, b.dq, b.dk, b.dv = grads["dout"], grads["dq"], grads["dk"], grads["dv"]
+        return b
+
+    for kw, code, word in [(dict(S=1020), 1, "zigzag"), (dict(D=80), 2, "head_dim"), (dict(q=None), 1, "null"),
+                           (dict(dq=None), 1, "gradient"), (dict(dout=None), 1, "gradient")]:
+        b = bargs(**kw)
+        if "dq" not in kw and "dout" not in kw:
+            assert L.usp_ring_bwd_workspace_size(ctypes.byref(b)) == 0
+        st, msg = _status(L.usp_ring_bwd, ctypes.byref(b), None, 0, None)
+        assert st == code and word in msg, (kw, st, msg)
+    # natural-order zigzag, all ranks: permuted q, k, v (bf16), delta (natural and
+    # rank-major), permuted dout and LSE, and three f32 accumulators
+    b = bargs()
+    need = L.usp_ring_bwd_workspace_size(ctypes.byref(b))
+    S, Hq, Hkv, D = 1024, 8, 2, 128
+    expect = S * (Hq + 2 * Hkv) * D * 2 + 2 * Hq * S * 4 + S * Hq * D * 2 + Hq * S * 4 + S * (Hq + 2 * Hkv) * D * 4
+    assert expect <= need <= expect + 16 * 256
+    st, msg = _status(L.usp_ring_bwd, ctypes.byref(b), None, 0, None)
+    assert st == 3 and "workspace" in msg
+    st, msg = _status(L.usp_ring_bwd, ctypes.byref(b), ctypes.c_void_p(0x10010), need, None)
+    assert st == 3 and "aligned" in msg
+    # basic layout, rank-major input: only delta
+    b = bargs(impl=0, input_order=1)
+    assert L.usp_ring_bwd_workspace_size(ctypes.byref(b)) == ((Hq * S * 4 + 255) // 256) * 256

@@ -20,7 +20,7 @@ import seeded_inputs as si
 import ulysses_sequence_attention_zigzag_amd as usp
 from oracle import index_ref as ix
 from oracle.attention_ref import attention_ref
-from oracle.backward_ref import block_attention_bwd_ref, ring_backward_ref
+from oracle.backward_ref import attention_bwd_ref, block_attention_bwd_ref, ring_backward_ref
 from oracle.ring_ref import block_attention_ref
 
 pytestmark = pytest.mark.gpu
@@ -265,3 +265,84 @@ def test_block_bwd_deterministic():
         again = usp.block_attn_bwd(*args, **kw)
         for a, b in zip(first, again):
             assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------- virtual ring backward
+RING_BWD = [
+    si.WORKLOADS["zigzag_causal_small"],
+    si.WORKLOADS["ring_swa"].scaled(B=1, S=2048, Hq=4, Hkv=4, window=300),
+    si.WORKLOADS["varlen_streaming"].scaled(S=2048, Hq=4, Hkv=4, window=250, cu_seqlens=[0, 128, 1000, 2048]),
+    si.WORKLOADS["usp_zigzag_gqa"].scaled(S=4096, Hq=8, Hkv=4),
+    si.WORKLOADS["usp_zigzag_gqa"].scaled(S=4096, Hq=8, Hkv=4, rank=3, ulysses_rank=1),
+    si.WORKLOADS["stripe_mqa"].scaled(S=8192, Hq=4, Hkv=1, rank=7),
+    si.WORKLOADS["stripe_mqa"].scaled(S=4096, Hq=2, Hkv=1, stripe_block=4, ring_degree=4, rank=-1),
+    si.WORKLOADS["zigzag_causal_small"].scaled(rank=-1, ring_degree=3, S=1200, Hq=2, Hkv=1, D=128),
+]
+
+
+def _ring_bwd_expected(w: si.Workload, q, k, v):
+    """Oracle (O, LSE) in the forward's output format, dout of that shape,
+    and the expected (dq, dk, dv) in usp_ring_bwd's output format."""
+    kw = dict(softmax_scale=w.scale, causal=w.causal, window=w.window, n_sink=w.n_sink, cu_seqlens=w.cu_seqlens)
+    if w.rank < 0:
+        O, LSE = attention_ref(q, k, v, **kw)
+        dout = si.randn_bf16(tuple(O.shape), w.seed, 3)
+        dq, dk, dv, _, _ = attention_bwd_ref(q, k, v, dout, **kw)
+        return O, LSE, dout, (dq, dk, dv)
+    N, ud, u = w.ring_degree, w.ulysses_degree, w.ulysses_rank
+    Hl, Hkl = w.Hq // ud, w.Hkv // ud
+    heads, kvh = list(range(u * Hl, (u + 1) * Hl)), list(range(u * Hkl, (u + 1) * Hkl))
+    pos = [ix.rank_positions(w.impl, w.S, N, r, w.stripe_block) for r in range(N)]
+    O, LSE = attention_ref(q, k, v, rows=pos[w.rank], heads=heads, **kw)
+    dout = si.randn_bf16(tuple(O.shape), w.seed, 3)
+    qi = q[:, pos[w.rank]][:, :, heads].contiguous()
+    ks, vs = k[:, :, kvh].contiguous(), v[:, :, kvh].contiguous()
+    dq, dk, dv = block_attention_bwd_ref(qi, ks, vs, dout, LSE, _delta(dout, O), pos[w.rank], list(range(w.S)),
+                                         scale=w.scale, causal=w.causal, window=w.window, n_sink=w.n_sink,
+                                         cu_seqlens=w.cu_seqlens)
+    perm = [p for r in range(N) for p in pos[r]]          # rank-major row order
+    return O, LSE, dout, (dq, dk[:, perm], dv[:, perm])
+
+
+@pytest.mark.parametrize("w", RING_BWD, ids=lambda w: f"{w.name}-S{w.S}-r{w.rank}-u{w.ulysses_rank}")
+def test_ring_bwd_oracle_forward(w):
+    """usp_ring_bwd given the oracle's forward output and LSE."""
+    say(f"ring_bwd {w.name} S={w.S} rank={w.rank} u={w.ulysses_rank}")
+    q, k, v = w.make_inputs()
+    O, LSE, dout, ref = _ring_bwd_expected(w, q, k, v)
+    fwd = usp.RingCall(q.cuda(), k.cuda(), v.cuda(), impl=w.impl, ring_degree=w.ring_degree,
+                       ulysses_degree=w.ulysses_degree, stripe_block=w.stripe_block, causal=w.causal,
+                       window=w.window, n_sink=w.n_sink, cu_seqlens=w.cu_seqlens,
+                       softmax_scale=w.softmax_scale or 0.0, rank=w.rank, ulysses_rank=w.ulysses_rank)
+    fwd.out.copy_(O.float())
+    fwd.lse.copy_(LSE.float())
+    bwd = usp.RingBwdCall(fwd, dout.cuda())
+    got = bwd.run()
+    torch.cuda.synchronize()
+    for g, r, name in zip(got, ref, ("dq", "dk", "dv")):
+        assert tuple(g.shape) == tuple(r.shape), (name, g.shape, r.shape)
+        assert_grad(g, r, name)
+    # a second run overwrites (does not accumulate into) the outputs
+    again = bwd.run()
+    torch.cuda.synchronize()
+    for a_, b_ in zip(got, again):
+        assert torch.equal(a_, b_)
+
+
+@pytest.mark.parametrize("w", [RING_BWD[0], RING_BWD[3], RING_BWD[6]],
+                         ids=lambda w: f"{w.name}-S{w.S}-r{w.rank}")
+def test_ring_fwd_then_bwd_end_to_end(w):
+    """usp_ring_fwd then usp_ring_bwd on the device (bf16 forward output)."""
+    say(f"ring fwd+bwd {w.name} S={w.S} rank={w.rank}")
+    q, k, v = w.make_inputs()
+    _, _, dout, ref = _ring_bwd_expected(w, q, k, v)
+    fwd = usp.RingCall(q.cuda(), k.cuda(), v.cuda(), impl=w.impl, ring_degree=w.ring_degree,
+                       ulysses_degree=w.ulysses_degree, stripe_block=w.stripe_block, causal=w.causal,
+                       window=w.window, n_sink=w.n_sink, cu_seqlens=w.cu_seqlens,
+                       softmax_scale=w.softmax_scale or 0.0, rank=w.rank, ulysses_rank=w.ulysses_rank,
+                       out_dtype=torch.bfloat16)
+    fwd.run()
+    got = usp.RingBwdCall(fwd, dout.cuda()).run()
+    torch.cuda.synchronize()
+    for g, r, name in zip(got, ref, ("dq", "dk", "dv")):
+        assert_grad(g, r, name)

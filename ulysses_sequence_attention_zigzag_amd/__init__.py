@@ -51,6 +51,11 @@ class RingArgs(ctypes.Structure):
                 ("merge_mode", ctypes.c_int32)]
 
 
+class RingBwdArgs(ctypes.Structure):
+    _fields_ = [("fwd", RingArgs), ("dout", ctypes.c_void_p), ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p),
+                ("dv", ctypes.c_void_p)]
+
+
 _lib = None
 
 _I64 = ctypes.c_int64
@@ -67,6 +72,8 @@ _SIGS = {
     "usp_lse_merge": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P], _I32),
     "usp_ring_fwd_workspace_size": ([ctypes.POINTER(RingArgs)], ctypes.c_size_t),
     "usp_ring_fwd": ([ctypes.POINTER(RingArgs), _P, ctypes.c_size_t, _P], _I32),
+    "usp_ring_bwd_workspace_size": ([ctypes.POINTER(RingBwdArgs)], ctypes.c_size_t),
+    "usp_ring_bwd": ([ctypes.POINTER(RingBwdArgs), _P, ctypes.c_size_t, _P], _I32),
     "usp_plan_block": ([_I64, _I64, _I64, _I32, ctypes.POINTER(PosMap), ctypes.POINTER(PosMap), _I32, _I32,
                         _I32, _P, _I32, _I32, _P, _I64, _P, _I64, ctypes.POINTER(_I64),
                         ctypes.POINTER(_I64), ctypes.POINTER(ctypes.c_int32),
@@ -322,6 +329,45 @@ class RingCall:
         ws = ctypes.c_void_p(self.workspace.data_ptr()) if self.workspace is not None else None
         _check(lib().usp_ring_fwd(ctypes.byref(self.args), ws, self.ws_bytes, _stream(stream)))
         return self.out, self.lse
+
+
+class RingBwdCall:
+    """A prepared usp_ring_bwd call for the forward described by ``fwd`` (a
+    RingCall that has run): dout has the shape of fwd.out; gradients are
+    allocated once; ``run()`` only enqueues the kernels."""
+
+    def __init__(self, fwd: RingCall, dout: torch.Tensor):
+        if tuple(dout.shape) != tuple(fwd.out.shape):
+            raise ValueError("dout must have the shape of the forward output")
+        a = fwd.args
+        self.fwd, self.dout = fwd, dout
+        dev = fwd.q.device
+        varlen = fwd.q.dim() == 3
+        N, ud = a.ring_degree, a.ulysses_degree
+        L = a.S // N
+        if a.rank < 0:
+            dq_shape, kv_rows = (a.B, a.S, a.Hq, a.D), a.S
+        else:
+            dq_shape, kv_rows = (a.B, L, a.Hq // ud, a.D), a.S
+        kv_shape = (a.B, kv_rows, a.Hkv // ud, a.D)
+        if varlen:
+            dq_shape, kv_shape = dq_shape[1:], kv_shape[1:]
+        self.dq = torch.empty(dq_shape, dtype=torch.float32, device=dev)
+        self.dk = torch.empty(kv_shape, dtype=torch.float32, device=dev)
+        self.dv = torch.empty(kv_shape, dtype=torch.float32, device=dev)
+        b = RingBwdArgs()
+        b.fwd = a
+        b.dout = _dev(dout, torch.bfloat16, "dout").value
+        b.dq, b.dk, b.dv = self.dq.data_ptr(), self.dk.data_ptr(), self.dv.data_ptr()
+        self.args = b
+        nbytes = lib().usp_ring_bwd_workspace_size(ctypes.byref(b))
+        self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        self.ws_bytes = nbytes
+
+    def run(self, stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+        _check(lib().usp_ring_bwd(ctypes.byref(self.args), ctypes.c_void_p(self.workspace.data_ptr()),
+                                  self.ws_bytes, _stream(stream)))
+        return self.dq, self.dk, self.dv
 
 
 def ring_fwd(q, k, v, **kw) -> Tuple[torch.Tensor, torch.Tensor]:

@@ -511,6 +511,7 @@ usp_status usp_block_attn_bwd(const void* q, const void* k, const void* v, const
   p.dv = dv;
   p.cu_seqlens = su.ms.nseq ? cu_seqlens_dev : nullptr;
   p.q_batch_stride = Lq * Hq * D;
+  p.g_batch_stride = Lq * Hq * D;
   p.kv_batch_stride = Lk * Hkv * D;
   p.Lq_buf = (int32_t)Lq;
   p.B = (int32_t)B;
@@ -627,26 +628,24 @@ RingLayout ring_layout(const usp_ring_args* a) {
   return r;
 }
 
-}  // namespace
+// Steps 1-2 of the ring (shared by forward and backward): token order
+// (rank-major q, or ring rank r's rows; k, v), then the Ulysses seq -> head
+// relayout for Ulysses rank u.  Uses the workspace regions of `R`.
+struct Staged {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t q_batch_rows;  // rows between batches in the q buffer
+  int64_t q_row_off;     // first row of the rank's q rows
+  int64_t Hq_l, Hkv_l;   // heads after the Ulysses split
+};
 
-size_t usp_ring_fwd_workspace_size(const usp_ring_args* a) {
-  if (check_ring_args(a) != USP_OK) return 0;
-  return ring_layout(a).total;
-}
-
-usp_status usp_ring_fwd(const usp_ring_args* a, void* workspace, size_t ws_bytes, void* stream_) {
-  usp_status st = check_ring_args(a);
-  if (st != USP_OK) return st;
-  const RingLayout R = ring_layout(a);
-  USP_CHECK(R.total == 0 || (workspace && ws_bytes >= R.total), USP_ERR_WORKSPACE,
-            "workspace of %zu bytes needed, %zu given", R.total, workspace ? ws_bytes : (size_t)0);
-  USP_CHECK(((uintptr_t)workspace & 255) == 0, USP_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  hipStream_t stream = as_stream(stream_);
-  char* ws = static_cast<char*>(workspace);
+usp_status stage_ring_inputs(const usp_ring_args* a, const RingLayout& R, char* ws, hipStream_t stream,
+                             Staged* out) {
+  usp_status st = USP_OK;
   const int N = a->ring_degree, ud = a->ulysses_degree, u = a->ulysses_rank;
   const int64_t B = a->B, S = a->S, D = a->D, L = R.L;
   const int b = a->impl == USP_RING_STRIPE ? a->stripe_block : 1;
-
   // 1. token order: rank-major q (or ring rank r's rows), k, v
   const uint16_t* qsrc = static_cast<const uint16_t*>(a->q);
   const uint16_t* ksrc = static_cast<const uint16_t*>(a->k);
@@ -701,6 +700,92 @@ usp_status usp_ring_fwd(const usp_ring_args* a, void* workspace, size_t ws_bytes
     Hq_l = R.Hq_l;
     Hkv_l = R.Hkv_l;
   }
+
+  *out = Staged{qsrc, ksrc, vsrc, q_batch_rows, q_row_off, Hq_l, Hkv_l};
+  return USP_OK;
+}
+
+// Workspace of the backward ring: the forward's staging regions (permuted /
+// relayouted q, k, v), delta, and -- when the caller's tensors are in
+// natural order but the ring runs rank-major (all ranks, non-basic layout)
+// -- rank-major copies of dout and LSE and rank-major f32 gradient
+// accumulators that are un-permuted into the outputs at the end.
+struct RingBwdLayout {
+  RingLayout base;        // only the staging offsets of the forward layout are used
+  bool reorder;           // all ranks, natural-order tensors, non-basic layout
+  size_t off_delta, off_delta_nat, off_dop, off_lsep, off_dq, off_dk, off_dv;
+  size_t total;
+};
+
+RingBwdLayout ring_bwd_layout(const usp_ring_args* a) {
+  RingBwdLayout r;
+  const size_t NONE = SIZE_MAX;
+  r.base = ring_layout(a);
+  RingLayout& R = r.base;
+  const size_t D = (size_t)a->D, B = (size_t)a->B, S = (size_t)a->S;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  // the staging regions, as the forward lays them out; no forward accumulators
+  R.off_qp = R.off_kp = R.off_vp = R.off_ql = R.off_kl = R.off_vl = NONE;
+  R.off_oacc = R.off_lacc = R.off_opart = R.off_lpart = NONE;
+  if (R.need_perm) {
+    R.off_qp = take(B * (size_t)R.q_rows * a->Hq * D * 2);
+    R.off_kp = take(B * S * a->Hkv * D * 2);
+    R.off_vp = take(B * S * a->Hkv * D * 2);
+  }
+  if (a->ulysses_degree > 1) {
+    R.off_ql = take(B * (size_t)R.L * R.Hq_l * D * 2);
+    R.off_kl = take(B * S * R.Hkv_l * D * 2);
+    R.off_vl = take(B * S * R.Hkv_l * D * 2);
+  }
+  r.reorder = R.need_perm && !R.one;
+  r.off_delta = take(B * (size_t)R.Hq_l * R.q_rows * 4);
+  r.off_delta_nat = r.off_dop = r.off_lsep = r.off_dq = r.off_dk = r.off_dv = NONE;
+  if (r.reorder) {
+    r.off_delta_nat = take(B * (size_t)a->Hq * S * 4);
+    r.off_dop = take(B * S * a->Hq * D * 2);
+    r.off_lsep = take(B * (size_t)a->Hq * S * 4);
+    r.off_dq = take(B * S * a->Hq * D * 4);
+    r.off_dk = take(B * S * a->Hkv * D * 4);
+    r.off_dv = take(B * S * a->Hkv * D * 4);
+  }
+  R.total = off;
+  r.total = off;
+  return r;
+}
+
+}  // namespace
+
+size_t usp_ring_fwd_workspace_size(const usp_ring_args* a) {
+  if (check_ring_args(a) != USP_OK) return 0;
+  return ring_layout(a).total;
+}
+
+usp_status usp_ring_fwd(const usp_ring_args* a, void* workspace, size_t ws_bytes, void* stream_) {
+  usp_status st = check_ring_args(a);
+  if (st != USP_OK) return st;
+  const RingLayout R = ring_layout(a);
+  USP_CHECK(R.total == 0 || (workspace && ws_bytes >= R.total), USP_ERR_WORKSPACE,
+            "workspace of %zu bytes needed, %zu given", R.total, workspace ? ws_bytes : (size_t)0);
+  USP_CHECK(((uintptr_t)workspace & 255) == 0, USP_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  hipStream_t stream = as_stream(stream_);
+  char* ws = static_cast<char*>(workspace);
+  const int N = a->ring_degree;
+  const int64_t B = a->B, S = a->S, D = a->D, L = R.L;
+  const int b = a->impl == USP_RING_STRIPE ? a->stripe_block : 1;
+
+  Staged stg;
+  st = stage_ring_inputs(a, R, ws, stream, &stg);
+  if (st != USP_OK) return st;
+  const uint16_t* qsrc = stg.q;
+  const uint16_t* ksrc = stg.k;
+  const uint16_t* vsrc = stg.v;
+  const int64_t q_batch_rows = stg.q_batch_rows, q_row_off = stg.q_row_off;
+  const int64_t Hq_l = stg.Hq_l, Hkv_l = stg.Hkv_l;
 
   // 3. ring steps
   float* oacc = R.out_is_acc ? static_cast<float*>(a->out) : reinterpret_cast<float*>(ws + R.off_oacc);
@@ -797,6 +882,166 @@ usp_status usp_ring_fwd(const usp_ring_args* a, void* workspace, size_t ws_bytes
     }
     if (st != USP_OK) return st;
     st = launch_permute(lacc, a->lse, B * Hq_l, R.q_rows, R.q_rows, 4, gs, stream);
+    if (st != USP_OK) return st;
+  }
+  return USP_OK;
+}
+
+size_t usp_ring_bwd_workspace_size(const usp_ring_bwd_args* a) {
+  if (!a || check_ring_args(&a->fwd) != USP_OK) return 0;
+  return ring_bwd_layout(&a->fwd).total;
+}
+
+usp_status usp_ring_bwd(const usp_ring_bwd_args* ba, void* workspace, size_t ws_bytes, void* stream_) {
+  USP_CHECK(ba, USP_ERR_INVALID_ARG, "null args");
+  const usp_ring_args* a = &ba->fwd;
+  usp_status st = check_ring_args(a);
+  if (st != USP_OK) return st;
+  USP_CHECK(ba->dout && ba->dq && ba->dk && ba->dv, USP_ERR_INVALID_ARG, "null gradient pointer");
+  const RingBwdLayout RB = ring_bwd_layout(a);
+  const RingLayout& R = RB.base;
+  USP_CHECK(workspace && ws_bytes >= RB.total, USP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
+            RB.total, workspace ? ws_bytes : (size_t)0);
+  USP_CHECK(((uintptr_t)workspace & 255) == 0, USP_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  hipStream_t stream = as_stream(stream_);
+  char* ws = static_cast<char*>(workspace);
+  const int N = a->ring_degree;
+  const int64_t B = a->B, S = a->S, D = a->D, L = R.L;
+  const int b = a->impl == USP_RING_STRIPE ? a->stripe_block : 1;
+
+  // 1-2. the forward's staging of q, k, v
+  Staged stg;
+  st = stage_ring_inputs(a, R, ws, stream, &stg);
+  if (st != USP_OK) return st;
+  const int64_t Hq_l = stg.Hq_l, Hkv_l = stg.Hkv_l;
+
+  // delta = rowsum(dO * O) over the rows the ring visits, in their order;
+  // dout and LSE in that order too
+  float* delta = reinterpret_cast<float*>(ws + RB.off_delta);
+  const uint16_t* dout = static_cast<const uint16_t*>(ba->dout);
+  const float* lse = a->lse;
+  const usp_dtype odt = (usp_dtype)a->out_dtype;
+  if (RB.reorder) {
+    float* dn = reinterpret_cast<float*>(ws + RB.off_delta_nat);
+    uint16_t* dop = reinterpret_cast<uint16_t*>(ws + RB.off_dop);
+    float* lsep = reinterpret_cast<float*>(ws + RB.off_lsep);
+    st = launch_bwd_delta(a->out, odt == USP_DT_F32, dout, dn, B, S, a->Hq, D, stream);
+    if (st == USP_OK)
+      st = usp_permute(dn, delta, B * a->Hq, S, 1, USP_DT_F32, (usp_ring_impl)a->impl, N, 1, b, -1, 0, stream);
+    if (st == USP_OK)
+      st = usp_permute(a->lse, lsep, B * a->Hq, S, 1, USP_DT_F32, (usp_ring_impl)a->impl, N, 1, b, -1, 0, stream);
+    if (st == USP_OK)
+      st = usp_permute(ba->dout, dop, B, S, a->Hq * D, USP_DT_BF16, (usp_ring_impl)a->impl, N, 1, b, -1, 0, stream);
+    if (st != USP_OK) return st;
+    dout = dop;
+    lse = lsep;
+  } else {
+    st = launch_bwd_delta(a->out, odt == USP_DT_F32, dout, delta, B, R.q_rows, Hq_l, D, stream);
+    if (st != USP_OK) return st;
+  }
+
+  // gradient accumulators
+  float* dq = RB.reorder ? reinterpret_cast<float*>(ws + RB.off_dq) : ba->dq;
+  float* dk = RB.reorder ? reinterpret_cast<float*>(ws + RB.off_dk) : ba->dk;
+  float* dv = RB.reorder ? reinterpret_cast<float*>(ws + RB.off_dv) : ba->dv;
+  st = launch_fill_zero(dq, B * R.q_rows * Hq_l * D, stream);
+  if (st == USP_OK) st = launch_fill_zero(dk, B * S * Hkv_l * D, stream);
+  if (st == USP_OK) st = launch_fill_zero(dv, B * S * Hkv_l * D, stream);
+  if (st != USP_OK) return st;
+
+  // 3. ring steps: host i meets KV piece j = (i - s) mod N; one launch per
+  // kernel per step covers every host of the step (their dq rows and dk / dv
+  // pieces are disjoint)
+  const float scale = a->softmax_scale > 0.f ? a->softmax_scale : 1.0f / std::sqrt((float)D);
+  MaskSpec ms;
+  ms.causal = a->causal ? 1 : 0;
+  ms.window = a->window;
+  ms.n_sink = a->n_sink;
+  ms.nseq = a->cu_seqlens_host ? a->nseq : 0;
+  ms.S = (int32_t)S;
+  usp_posmap pm{a->impl, N, 0, b, S};
+  const PosMap base_map = make_map(pm);
+  for (int s = 0; s < N; ++s) {
+    const std::string key = map_key(base_map) + "|" + mask_key(ms) + "|" +
+                            cu_key(ms.nseq ? a->cu_seqlens_host : nullptr, a->nseq) + "|r" +
+                            std::to_string(a->rank) + "|s" + std::to_string(s);
+    auto blocks = [&](auto&& add) {
+      const int i0 = R.one ? a->rank : 0, i1 = R.one ? a->rank + 1 : N;
+      for (int i = i0; i < i1; ++i) {
+        const int j = ((i - s) % N + N) % N;
+        BlockSpec blk;
+        blk.qmap = base_map;
+        blk.qmap.rank = i;
+        blk.kmap = base_map;
+        blk.kmap.rank = j;
+        blk.Lq = (int32_t)L;
+        blk.Lk = (int32_t)L;
+        blk.q_row_base = R.one ? 0 : (int32_t)(i * L);
+        blk.k_row_base = (int32_t)(j * L);
+        blk.tile_m = kBwdTileM;
+        add(blk);
+      }
+    };
+    DevicePlan dpq, dpk;
+    st = device_plan("rbq|" + key, [&](Plan& plan) {
+      blocks([&](const BlockSpec& blk) { plan_block(blk, ms, a->cu_seqlens_host, 1, plan); });
+    }, &dpq);
+    if (st != USP_OK) return st;
+    st = device_plan("rbk|" + key, [&](Plan& plan) {
+      blocks([&](const BlockSpec& blk) {
+        plan_block_kv(blk, ms, a->cu_seqlens_host, kBwdTileK, kBwdTileQ, plan);
+      });
+    }, &dpk);
+    if (st != USP_OK) return st;
+
+    BwdParams p{};
+    p.q = stg.q + stg.q_row_off * Hq_l * D;
+    p.k = stg.k;
+    p.v = stg.v;
+    p.dout = dout;
+    p.lse = lse;
+    p.delta = delta;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.cu_seqlens = ms.nseq ? a->cu_seqlens_dev : nullptr;
+    p.q_batch_stride = stg.q_batch_rows * Hq_l * D;
+    p.g_batch_stride = R.q_rows * Hq_l * D;
+    p.kv_batch_stride = S * Hkv_l * D;
+    p.Lq_buf = (int32_t)R.q_rows;
+    p.B = (int32_t)B;
+    p.Hq = (int32_t)Hq_l;
+    p.Hkv = (int32_t)Hkv_l;
+    p.scale = scale;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    p.qmap = base_map;
+    p.kmap = base_map;
+    p.mask = ms;
+    BwdParams pq = p, pk = p;
+    pq.items = dpq.items;
+    pq.runs = dpq.runs;
+    pq.n_items = dpq.n_items;
+    pk.items = dpk.items;
+    pk.runs = dpk.runs;
+    pk.n_items = dpk.n_items;
+    st = launch_bwd(pq, pk, (int)D, stream);
+    if (st != USP_OK) return st;
+  }
+
+  // 4. natural order for the caller's tensors
+  if (RB.reorder) {
+    GatherSpec gs{};
+    gs.impl = a->impl;
+    gs.N = N;
+    gs.ud = 1;
+    gs.b = b;
+    gs.g = 0;
+    gs.L = (int32_t)L;
+    gs.S = (int32_t)S;
+    gs.kind = G_UNPERMUTE;
+    st = launch_permute(dq, ba->dq, B, S, S, a->Hq * D * 4, gs, stream);
+    if (st == USP_OK) st = launch_permute(dk, ba->dk, B, S, S, a->Hkv * D * 4, gs, stream);
+    if (st == USP_OK) st = launch_permute(dv, ba->dv, B, S, S, a->Hkv * D * 4, gs, stream);
     if (st != USP_OK) return st;
   }
   return USP_OK;

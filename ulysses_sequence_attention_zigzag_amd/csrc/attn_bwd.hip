@@ -100,6 +100,11 @@ __device__ __forceinline__ bf16x8 frag_tr(const char* t, int kb, int half, int d
   return bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
 }
 
+__global__ __launch_bounds__(256) void fill_zero_kernel(float4* p, int64_t n4) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256)
+    p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
 // ------------------------------------------------------------------ delta
 // delta[b, h, t] = sum_d dO[b, t, h, d] * O[b, t, h, d]; one thread per row.
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const void* out, int out_f32, const uint16_t* dout,
@@ -168,11 +173,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const BwdParams p) {
   bf16x8 qf[KS], dof[KS];
   {
     const int64_t off = (int64_t)b * p.q_batch_stride + (qrow * p.Hq + h) * D + hi * 8;
+    const int64_t goff = (int64_t)b * p.g_batch_stride + (qrow * p.Hq + h) * D + hi * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (qvalid) {
         qf[ks] = *reinterpret_cast<const bf16x8*>(p.q + off + ks * 16);
-        dof[ks] = *reinterpret_cast<const bf16x8*>(p.dout + off + ks * 16);
+        dof[ks] = *reinterpret_cast<const bf16x8*>(p.dout + goff + ks * 16);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) qf[ks][e] = dof[ks][e] = (__bf16)0.f;
@@ -309,7 +315,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const BwdParams p) {
 
   // dq[b, row, h, :] += scale * dQ (this lane: query qrow, head-dim rows of dQ^T)
   if (!qvalid || it.run_begin == it.run_end) return;
-  float* op = p.dq + (int64_t)b * p.q_batch_stride + (qrow * p.Hq + h) * D;
+  float* op = p.dq + (int64_t)b * p.g_batch_stride + (qrow * p.Hq + h) * D;
   const float sc = p.scale;
 #pragma unroll
   for (int d = 0; d < DB; ++d) {
@@ -412,7 +418,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   for (int gi = 0; gi < group; ++gi) {
     const int h = hk * group + gi;
     const uint16_t* qbase = p.q + (int64_t)b * p.q_batch_stride + (int64_t)it.k_row0 * p.Hq * D + h * D;
-    const uint16_t* obase = p.dout + (int64_t)b * p.q_batch_stride + (int64_t)it.k_row0 * p.Hq * D + h * D;
+    const uint16_t* obase = p.dout + (int64_t)b * p.g_batch_stride + (int64_t)it.k_row0 * p.Hq * D + h * D;
     const uint32_t qrow_bytes = (uint32_t)p.Hq * D * 2;
     const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void*)qbase, (short)0, 0x7fffffff, kBufferRsrcWord3);
     const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc((void*)obase, (short)0, 0x7fffffff, kBufferRsrcWord3);
@@ -530,6 +536,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
 }
 
 }  // namespace
+
+usp_status launch_fill_zero(float* p, int64_t n, hipStream_t stream) {
+  // n is a multiple of 4 and p 16-byte aligned (the callers' f32 tensors of D >= 64 columns)
+  if (n <= 0) return USP_OK;
+  const int64_t n4 = n / 4;
+  const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, 8192);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, reinterpret_cast<float4*>(p), n4);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("fill launch failed: %s", hipGetErrorString(e));
+    return USP_ERR_HIP;
+  }
+  return USP_OK;
+}
 
 usp_status launch_bwd_delta(const void* out, int out_f32, const uint16_t* dout, float* delta, int64_t B,
                             int64_t L, int64_t H, int64_t D, hipStream_t stream) {

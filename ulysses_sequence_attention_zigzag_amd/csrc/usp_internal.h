@@ -186,7 +186,8 @@ struct BwdParams {
   const WorkItem* items;
   const Run* runs;
   const int32_t* cu_seqlens;
-  int64_t q_batch_stride;    // elements between batch rows of q / dout / dq
+  int64_t q_batch_stride;    // elements between batch rows of q
+  int64_t g_batch_stride;    // elements between batch rows of dout / dq
   int64_t kv_batch_stride;   // elements between batch rows of k / v / dk / dv
   int32_t Lq_buf;
   int32_t n_items;
@@ -203,6 +204,7 @@ constexpr int kBwdTileM = 128;  // query rows per dQ workgroup
 constexpr int kBwdTileK = 128;  // keys per dK / dV workgroup
 constexpr int kBwdTileQ = 64;   // query rows per dK / dV iteration
 usp_status launch_bwd(const BwdParams& pq, const BwdParams& pkv, int D, hipStream_t stream);
+usp_status launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 usp_status launch_bwd_delta(const void* out, int out_f32, const uint16_t* dout, float* delta, int64_t B,
                             int64_t L, int64_t H, int64_t D, hipStream_t stream);
 

@@ -161,6 +161,90 @@ def cpu_baseline(w, q, k, v, budget_s: float):
     }
 
 
+def cpu_baseline_bwd(w, q, k, v, dout, budget_s: float):
+    """Times the float64 oracle's backward on a seeded sample of the
+    workload's query rows: their forward (O, LSE), delta, and their gradient
+    terms against every key (dQ of the rows, their dK / dV contributions).
+    Counted like the GPU value: 10 * D per visible pair."""
+    import torch
+    from oracle import index_ref as ix
+    from oracle.attention_ref import attention_ref
+    from oracle.backward_ref import block_attention_bwd_ref
+
+    threads = torch.get_num_threads()
+    varlen = w.cu_seqlens is not None
+    qb, kb, vb = (t.unsqueeze(0) if varlen else t for t in (q, k, v))
+    db = dout.unsqueeze(0) if varlen else dout
+    if w.rank >= 0:
+        pos = ix.rank_positions(w.impl, w.S, w.ring_degree, w.rank, w.stripe_block)
+        Hl, Hkl = w.Hq // w.ulysses_degree, w.Hkv // w.ulysses_degree
+        heads = list(range(w.ulysses_rank * Hl, (w.ulysses_rank + 1) * Hl))
+        kvh = list(range(w.ulysses_rank * Hkl, (w.ulysses_rank + 1) * Hkl))
+        local = True
+    else:
+        pos = list(range(w.S))
+        heads, kvh = list(range(w.Hq)), list(range(w.Hkv))
+        local = False
+    kh, vh = kb[:, :, kvh], vb[:, :, kvh]
+    g = torch.Generator().manual_seed(4243)
+    order = torch.randperm(len(pos), generator=g).tolist()
+    kw = dict(softmax_scale=w.scale, causal=w.causal, window=w.window, n_sink=w.n_sink, cu_seqlens=w.cu_seqlens)
+    done, flops, t_used, n = 0, 0.0, 0.0, 2
+    all_pos = list(range(w.S))
+    bmul = 1 if varlen else w.B
+    while t_used < budget_s and done < len(order):
+        idx = order[done:done + n]
+        rows = [pos[i] for i in idx]
+        t0 = time.perf_counter()
+        O, LSE = attention_ref(q, k, v, rows=rows, heads=heads, **kw)
+        if varlen:
+            O, LSE = O.unsqueeze(0), LSE.unsqueeze(0)
+        d_rows = db[:, idx] if local else db[:, rows][:, :, heads]
+        delta = (d_rows.double() * O).sum(-1).transpose(1, 2)
+        qr = qb[:, rows][:, :, heads]
+        block_attention_bwd_ref(qr, kh, vh, d_rows, LSE, delta, rows, all_pos, scale=w.scale, causal=w.causal,
+                                window=w.window, n_sink=w.n_sink, cu_seqlens=w.cu_seqlens)
+        dt = time.perf_counter() - t0
+        t_used += dt
+        done += len(rows)
+        flops += 10.0 * w.D * len(heads) * bmul * float(visible_pairs_for_rows(w, rows))
+        per_row = dt / max(1, len(rows))
+        n = max(1, min(1024, int(0.3 * max(0.0, budget_s - t_used) / max(per_row, 1e-6))))
+    return {
+        "value": flops / t_used / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} of {len(pos)} query rows x {len(heads)} heads against every key: forward, delta "
+                  f"and backward, float64 torch CPU, {t_used:.1f} s",
+    }
+
+
+def visible_pairs_for_rows(w, rows) -> int:
+    """Visible keys summed over the given global query positions."""
+    total = 0
+    for p in rows:
+        if w.window > 0:
+            s = 0
+            if w.cu_seqlens is not None:
+                s = max(c for c in w.cu_seqlens[:-1] if c <= p)
+            off = p - s
+            total += min(w.window, off + 1) + max(0, min(w.n_sink, off - w.window + 1))
+        elif w.causal:
+            s = 0
+            if w.cu_seqlens is not None:
+                s = max(c for c in w.cu_seqlens[:-1] if c <= p)
+            total += p - s + 1
+        else:
+            if w.cu_seqlens is not None:
+                s = max(c for c in w.cu_seqlens[:-1] if c <= p)
+                e = min(c for c in w.cu_seqlens[1:] if c > p)
+                total += e - s
+            else:
+                total += w.S
+    return total
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,6 +254,8 @@ def main():
     ap.add_argument("--merge-mode", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="which", choices=["forward", "backward"], default="forward",
+                    help="forward: usp_ring_fwd (default); backward: usp_ring_bwd of that forward")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy kernel (float32 negate) over MIB MiB, three times, "
                          "as the known-size reference for HBM byte counters, and exit")
@@ -204,6 +290,8 @@ def main():
     t_gen = time.perf_counter() - t0
     print(f"# inputs generated in {t_gen:.1f}s", file=sys.stderr, flush=True)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    if args.which == "backward":
+        return bench_backward(args, w, q, k, v, qd, kd, vd)
     call = usp.RingCall(qd, kd, vd, impl=w.impl, ring_degree=w.ring_degree, ulysses_degree=w.ulysses_degree,
                         stripe_block=w.stripe_block, causal=w.causal, window=w.window, n_sink=w.n_sink,
                         cu_seqlens=w.cu_seqlens, softmax_scale=w.softmax_scale or 0.0, rank=w.rank,
@@ -287,6 +375,97 @@ def main():
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+def bench_backward(args, w, q, k, v, qd, kd, vd):
+    """Times usp_ring_bwd over the workload: the forward runs once untimed;
+    a step is the whole backward (staging of q, k, v, delta, every ring
+    step's dQ and dK / dV kernels, output order)."""
+    import torch
+
+    import seeded_inputs as si
+    import ulysses_sequence_attention_zigzag_amd as usp
+
+    fwd = usp.RingCall(qd, kd, vd, impl=w.impl, ring_degree=w.ring_degree, ulysses_degree=w.ulysses_degree,
+                       stripe_block=w.stripe_block, causal=w.causal, window=w.window, n_sink=w.n_sink,
+                       cu_seqlens=w.cu_seqlens, softmax_scale=w.softmax_scale or 0.0, rank=w.rank,
+                       ulysses_rank=w.ulysses_rank)
+    fwd.run()
+    dout = si.randn_bf16(tuple(fwd.out.shape), w.seed, 3)
+    call = usp.RingBwdCall(fwd, dout.cuda())
+    for _ in range(args.warmup):
+        call.run()
+    torch.cuda.synchronize()
+    print("# warmup done", file=sys.stderr, flush=True)
+    classes = ("bwd_dq", "bwd_dkdv", "bwd_delta", "permute", "relayout")
+    usp.timing_reset()
+    usp.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call.run()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    usp.timing_enable(False)
+    ms_step = elapsed * 1e3 / args.steps
+    kt = {c: usp.timing_read(c) for c in classes}
+    usp.timing_reset()
+
+    Hl = w.Hq // w.ulysses_degree
+    bmul = 1 if w.cu_seqlens is not None else w.B
+    pairs = visible_pairs_per_head(w)
+    unit_flops = w.D * Hl * bmul * pairs
+    flops = 10.0 * unit_flops
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    kernels = {}
+    for name, cls, per_pair in (("bwd_dkdv_kernel<%d>" % w.D, "bwd_dkdv", 8), ("bwd_dq_kernel<%d>" % w.D,
+                                                                            "bwd_dq", 6)):
+        ms = kt[cls][0] / args.steps
+        ach = per_pair * unit_flops / (ms * 1e-3) / 1e12 if ms > 0 else None
+        kernels[name] = {"ms_per_step": round(ms, 4), "launches_per_step": kt[cls][1] // max(1, args.steps),
+                         "flop_per_pair": per_pair * w.D, "TFLOP/s": round(ach, 2) if ach else None}
+    dom = max(kernels, key=lambda n: kernels[n]["ms_per_step"])
+    ach = kernels[dom]["TFLOP/s"]
+    rec = {
+        "metric": "masked-attention backward TFLOPS (10*D FLOP per visible pair, % of dense bf16 MFMA peak)",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "pass": "backward",
+            "B": w.B, "S_global": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+            "ring_impl": w.impl, "ring_degree": w.ring_degree, "ulysses_degree": w.ulysses_degree,
+            "rank": w.rank, "ulysses_rank": w.ulysses_rank, "causal": w.causal, "window": w.window,
+            "n_sink": w.n_sink, "cu_seqlens": w.cu_seqlens,
+            "algorithmic_tflop_per_step": round(flops / 1e12, 4),
+        },
+        "pct_peak_end_to_end": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": ach,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(ach / PEAK_BF16_TFLOPS, 4) if ach else None,
+            "traffic": None,
+            "kernel": dom,
+            "launches_per_step": kernels[dom]["launches_per_step"],
+            "kernel_ms_per_step": kernels[dom]["ms_per_step"],
+        },
+        "kernels": kernels,
+        "other_ms_per_step": {c: round(kt[c][0] / args.steps, 4) for c in ("bwd_delta", "permute", "relayout")},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_bwd(w, q, k, v, dout, args.cpu_budget)
     print(json.dumps(rec), flush=True)
 
 

@@ -899,6 +899,10 @@ usp_status usp_ring_bwd(const usp_ring_bwd_args* ba, void* workspace, size_t ws_
   if (st != USP_OK) return st;
   USP_CHECK(ba->dout && ba->dq && ba->dk && ba->dv, USP_ERR_INVALID_ARG, "null gradient pointer");
   const RingBwdLayout RB = ring_bwd_layout(a);
+  USP_CHECK(RB.base.L * RB.base.Hq_l * a->D * 2 < ((int64_t)1 << 31) &&
+                RB.base.q_rows * RB.base.Hq_l * 4 < ((int64_t)1 << 31),
+            USP_ERR_UNSUPPORTED, "one ring rank's q rows and one batch row of LSE must be under 2 GiB "
+            "(32-bit tile offsets)");
   const RingLayout& R = RB.base;
   USP_CHECK(workspace && ws_bytes >= RB.total, USP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
             RB.total, workspace ? ws_bytes : (size_t)0);

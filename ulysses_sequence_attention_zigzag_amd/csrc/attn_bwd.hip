@@ -28,6 +28,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "usp_internal.h"
 
@@ -42,7 +43,26 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.44269504088896340736f;
+// LDS fragment reads in flight ahead of the MFMAs that use them, and VALU
+// instructions placed after each MFMA of the phases that overlap a softmax
+constexpr int kPF = 4;
+constexpr int kDqValuA = 5;
+constexpr int kDqValuC = 10;
+constexpr int kKvValuA = 6;
+constexpr int kKvValuC = 6;
 constexpr int kBufferRsrcWord3 = 0x00020000;  // raw buffer resource word 3 (gfx9 family)
+
+// Scheduling group of n DS reads / n VALU instructions; n is a constant
+// after unrolling, so the switch folds away.
+__device__ __forceinline__ void sched_ds_read(int n) {
+  switch (n) {
+    case 1: __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); break;
+    case 2: __builtin_amdgcn_sched_group_barrier(0x100, 2, 0); break;
+    case 3: __builtin_amdgcn_sched_group_barrier(0x100, 3, 0); break;
+    case 4: __builtin_amdgcn_sched_group_barrier(0x100, 4, 0); break;
+    default: break;
+  }
+}
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -55,6 +75,64 @@ __device__ __forceinline__ int32_t floor_div(int32_t a, int32_t b) {
 }
 __device__ __forceinline__ int32_t ceil_div(int32_t a, int32_t b) { return -floor_div(-a, b); }
 
+// Smallest local row t with position(m, t) >= P, for a row t_ref of the
+// same monotone piece (positions increase with t across a whole basic,
+// stripe or affine rank, and within each chunk of a zigzag rank, where
+// they are consecutive).  Stripe: the rank holds blocks j*N + rank (block
+// j at rows j*b ..); P in one of them maps to its row, otherwise to the
+// first row of the rank's next block.  Exact for every t of the piece;
+// callers clamp to the rows they hold.
+__device__ __forceinline__ int32_t first_row_at_least(const PosMap& m, int32_t t_ref, int32_t P) {
+  if (m.kind == MAP_STRIPE) {
+    const int32_t beta = floor_div(P, m.b);
+    const int32_t o = P - beta * m.b;
+    const int32_t j = floor_div(beta - m.rank, m.N);
+    return (j * m.N + m.rank == beta) ? j * m.b + o : (j + 1) * m.b;
+  }
+  return t_ref + (P - position(m, t_ref));
+}
+
+// Raw buffer resource of `base` (no stride, 2^31 - 1 bytes, no swizzle),
+// wave-uniform so it lives in SGPRs.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r[2] = 0x7fffffff;
+  r[3] = kBufferRsrcWord3;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)p);
+}
+
+// Global -> LDS copies (buffer loads to LDS): lane i's 16 (or 4) bytes at
+// byte offset voff of the buffer land at LDS address lds + 16*i (4*i).
+// They are issued through inline assembly so that the compiler does not
+// order later LDS reads of other addresses behind them; the kernels wait
+// for them explicitly (s_waitcnt vmcnt(0), then a barrier) before reading
+// their destination, and never read a destination while a copy into it may
+// be in flight.
+// M0 (the LDS destination) is saved and restored around each copy.
+__device__ __forceinline__ void copy16_to_lds(const i32x4& rsrc, uint32_t lds, uint32_t voff) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane((int)lds)), "v"(voff), "s"(rsrc));
+}
+__device__ __forceinline__ void copy4_to_lds(const i32x4& rsrc, uint32_t lds, uint32_t voff) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane((int)lds)), "v"(voff), "s"(rsrc));
+}
+
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane i supplies the
 // address of 4 consecutive bf16 (row i/4 of a 4 x 16 block); lane j receives
 // column j of the block.
@@ -65,16 +143,22 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
-// LDS tile of R rows x D bf16 with 16-byte chunk c of row r at slot
-// c ^ swz(r), swz(r) = 4 * ((r / RPL) & (CPR / 4 - 1)): conflict-free for the
-// transpose reads (4 rows x 2 chunks per 16 lanes); plain 16-byte reads of
-// one chunk by 16 consecutive rows see some bank conflicts.
+// LDS tile of R rows x D bf16 (CPR 16-byte chunks per row, RPL rows per
+// 256-byte bank line) with chunk c of row r at slot c ^ swz(r),
+//   swz(r) = 4 * ((r / RPL) % (CPR / 4)) + (r / (RPL * CPR / 4)) % 4.
+// Both read patterns hit distinct bank slots: a plain 16-byte read of one
+// chunk by 16 consecutive rows (swz takes 16 distinct values over the rows
+// of each bank-line position), and a transpose read of 4 consecutive rows x
+// 4 aligned chunks (swz / 4 differs between the rows sharing a line
+// position).
 template <int D>
 struct BwdTile {
   static constexpr int CPR = D / 8;
   static constexpr int RPL = 16 / CPR;
   static constexpr int ROWB = D * 2;
-  __device__ static __forceinline__ int swz(int r) { return 4 * ((r / RPL) & (CPR / 4 - 1)); }
+  __device__ static __forceinline__ int swz(int r) {
+    return 4 * ((r / RPL) & (CPR / 4 - 1)) + ((r / (RPL * CPR / 4)) & 3);
+  }
   // 16-byte fragment: row r, logical chunk c
   __device__ static __forceinline__ bf16x8 frag(const char* t, int r, int c) {
     return *reinterpret_cast<const bf16x8*>(t + r * ROWB + ((c ^ swz(r)) * 16));
@@ -135,20 +219,25 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const void* out, int out
 }
 
 // -------------------------------------------------------------------- dQ
-template <int D, bool LINEAR>
+// Per 64-key tile and wave (32 query rows, one per lane):
+//   A(kb): S^T and dP^T of key block kb (32 keys) = K Q^T, V dO^T;
+//   B(kb): dS^T = exp2(S^T c - lse2) (dP^T - delta) -> bf16 (B-operand order);
+//   C(kb): dQ^T += K^T dS^T.
+// Issue order A0 A1 B0 C0 B1 C1, with B0's VALU work placed between A1's
+// MFMAs and B1's between C0's, and every LDS fragment read issued kPF
+// MFMAs ahead of its use.
+template <int D>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const BwdParams p) {
   using T = BwdTile<D>;
   constexpr int BN = 64;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int NB = BN / 32;
   constexpr int TILEB = BN * D * 2;
   constexpr int LPW = TILEB / 4096;
   constexpr int RPI = 1024 / T::ROWB;
+  constexpr int PF = kPF;
   static_assert(kTileN % BN == 0, "planner granularity");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * TILEB];  // K, V
-  char* const tK = smem;
-  char* const tV = smem + TILEB;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILEB];  // two buffers of (K, V)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -221,96 +310,158 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const BwdParams p) {
     vis_lo = p.mask.window > 0 ? max(s0, pq - p.mask.window + 1) : s0;
     sink_hi = p.mask.window > 0 ? min(s0 + p.mask.n_sink - 1, vis_hi) : s0 - 1;
   }
-  const int32_t kv_step = km.kind == MAP_STRIPE ? km.N : 1;
 
   const int64_t kv_row_stride = (int64_t)p.Hkv * D;
   const uint16_t* kbase = p.k + (int64_t)b * p.kv_batch_stride + (int64_t)it.k_row0 * kv_row_stride + hk * D;
   const uint16_t* vbase = p.v + (int64_t)b * p.kv_batch_stride + (int64_t)it.k_row0 * kv_row_stride + hk * D;
   const uint32_t row_bytes = (uint32_t)kv_row_stride * 2;
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, 0x7fffffff, kBufferRsrcWord3);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, 0x7fffffff, kBufferRsrcWord3);
+  const i32x4 krs = buffer_rsrc(kbase);
+  const i32x4 vrs = buffer_rsrc(vbase);
   const int lrow = lane / T::CPR;
   const int lslot = lane % T::CPR;
-
   const float c = p.scale_log2;
-  for (int ri = it.run_begin; ri < it.run_end; ++ri) {
-    const Run run = p.runs[ri];
-    for (int k0 = run.k_begin; k0 < run.k_end; k0 += BN) {
-      i32x4 kr[LPW], vr[LPW];
-#pragma unroll
-      for (int j = 0; j < LPW; ++j) {
-        const int row = (wid * LPW + j) * RPI + lrow;
-        const uint32_t off = (uint32_t)min(k0 + row, run.k_end - 1) * row_bytes + (uint32_t)((lslot ^ T::swz(row)) * 16);
-        kr[j] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
-        vr[j] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
-      }
-      __syncthreads();  // the previous tile's reads are done
-#pragma unroll
-      for (int j = 0; j < LPW; ++j) {
-        *reinterpret_cast<i32x4*>(tK + (wid * LPW + j) * 1024 + lane * 16) = kr[j];
-        *reinterpret_cast<i32x4*>(tV + (wid * LPW + j) * 1024 + lane * 16) = vr[j];
-      }
-      __syncthreads();
 
-      // S^T = K Q^T and dP^T = V dO^T (keys x queries)
-      f32x16 st[NB], dpt[NB];
+  // The workgroup walks the key tiles of its runs with two LDS buffers: tile
+  // n + 1 is copied global -> LDS directly (buffer loads to LDS) while tile
+  // n is computed.  Thread (wave wid, lane i) copies slices wid*LPW + j of K
+  // and V: physical (row, chunk slot) = (slice*RPI + i / CPR, i % CPR), i.e.
+  // logical chunk slot ^ swz(row); rows past the run's end are clamped to its
+  // last row (masked in partial runs; full runs are multiples of BN keys).
+  auto dma = [&](char* buf, int k0, int kend) {
 #pragma unroll
-      for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st[kb][r] = dpt[kb][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int kb = 0; kb < NB; ++kb) {
-          st[kb] = mfma32(T::frag(tK, kb * 32 + l32, 2 * ks + hi), qf[ks], st[kb]);
-          dpt[kb] = mfma32(T::frag(tV, kb * 32 + l32, 2 * ks + hi), dof[ks], dpt[kb]);
-        }
-      }
-      if (!run.full) {
-        const int32_t kend_du = run.k_end - 1 - k0;
-#pragma unroll
-        for (int kb = 0; kb < NB; ++kb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int du = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            bool vis;
-            if constexpr (LINEAR) {
-              const int32_t pk = position(km, k0) + du * kv_step;
-              vis = (du <= kend_du) & (pk <= vis_hi) & ((pk >= vis_lo) | ((pk >= sstart) & (pk <= sink_hi)));
-            } else {
-              const int32_t pk = position(km, k0 + du);
-              vis = (du <= kend_du) & (pk <= vis_hi) & ((pk >= vis_lo) | ((pk >= sstart) & (pk <= sink_hi)));
-            }
-            st[kb][r] = vis ? st[kb][r] : -INFINITY;
-          }
-        }
-      }
-      // dS^T = P^T (dP^T - delta), bf16, in the k-order of a B operand
-      bf16x8 dsb[NB][2];
-#pragma unroll
-      for (int kb = 0; kb < NB; ++kb) {
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(st[kb][half * 8 + e] * c - lse2);
-            const float p1 = __builtin_amdgcn_exp2f(st[kb][half * 8 + e + 1] * c - lse2);
-            const float d0 = p0 * (dpt[kb][half * 8 + e] - dl);
-            const float d1 = p1 * (dpt[kb][half * 8 + e + 1] - dl);
-            const bf16x2 pk2 = __builtin_convertvector((f32x2){d0, d1}, bf16x2);
-            dsb[kb][half][e] = pk2[0];
-            dsb[kb][half][e + 1] = pk2[1];
-          }
-        }
-      }
-      // dQ^T += K^T dS^T
-#pragma unroll
-      for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-          for (int d = 0; d < DB; ++d) dqt[d] = mfma32(frag_tr<D>(tK, kb, half, d, lane), dsb[kb][half], dqt[d]);
+    for (int j = 0; j < LPW; ++j) {
+      const int row = (wid * LPW + j) * RPI + lrow;
+      const uint32_t off = (uint32_t)min(k0 + row, kend - 1) * row_bytes + (uint32_t)((lslot ^ T::swz(row)) * 16);
+      copy16_to_lds(krs, lds_addr(buf + (wid * LPW + j) * 1024), off);
+      copy16_to_lds(vrs, lds_addr(buf + TILEB + (wid * LPW + j) * 1024), off);
     }
+  };
+
+  // One tile.  FULL: every pair visible (no mask).  Otherwise element r of
+  // key block kb is key k0 + du, du = kb*32 + 8*(r/4) + 4*hi + r%4; key
+  // positions increase through the run, so this lane's visible keys (window
+  // band, sinks) are at most two intervals of du, found once per tile.
+  auto tile = [&](auto full_c, const char* tK, int k0, int kend) {
+    constexpr bool FULL = decltype(full_c)::value;
+    const char* tV = tK + TILEB;
+    int32_t lo = 0, up = 0, slo = 0, sup = -1;
+    if constexpr (!FULL) {
+      const int32_t last = kend - 1 - k0;
+      const int32_t sh = k0 + 4 * hi;
+      lo = first_row_at_least(km, k0, vis_lo) - sh;
+      up = min(first_row_at_least(km, k0, vis_hi + 1) - 1 - k0, last) - 4 * hi;
+      slo = first_row_at_least(km, k0, sstart) - sh;
+      sup = min(first_row_at_least(km, k0, sink_hi + 1) - 1 - k0, last) - 4 * hi;
+    }
+    auto visible = [&](int kb, int r) -> bool {
+      if constexpr (FULL) {
+        return true;
+      } else {
+        const int cc = kb * 32 + 8 * (r >> 2) + (r & 3);
+        return ((cc >= lo) & (cc <= up)) | ((cc >= slo) & (cc <= sup));
+      }
+    };
+    // fragment streams: A phase i -> (K or V row kb*32 + l32, chunk 2*(i/2)+hi);
+    // C phase j -> K^T block (kb, half, d)
+    auto read_a = [&](int i) {
+      const int kb = i / (2 * KS), w = i % (2 * KS);
+      return T::frag((w & 1) ? tV : tK, kb * 32 + l32, 2 * (w >> 1) + hi);
+    };
+    auto read_c = [&](int j) {
+      const int kb = j / (2 * DB), half = (j / DB) & 1, d = j % DB;
+      return frag_tr<D>(tK, kb, half, d, lane);
+    };
+    constexpr int NA = 2 * 2 * KS;   // A0 + A1 MFMAs
+    constexpr int NC = 2 * 2 * DB;   // C0 + C1 MFMAs
+    f32x16 st[2], dpt[2];
+    bf16x8 fa[NA], fc[NC];
+    bf16x8 dsb[2][2];
+    const f32x16 zero = {};
+#pragma unroll
+    for (int i = 0; i < PF; ++i) fa[i] = read_a(i);
+    // A0, A1 (B0 follows in program order; the groups below interleave it)
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      if (i + PF < NA) fa[i + PF] = read_a(i + PF);
+      else fc[i + PF - NA] = read_c(i + PF - NA);
+      const int kb = i / (2 * KS), w = i % (2 * KS), ks = w >> 1;
+      if (w & 1) dpt[kb] = mfma32(fa[i], dof[ks], ks == 0 ? zero : dpt[kb]);
+      else st[kb] = mfma32(fa[i], qf[ks], ks == 0 ? zero : st[kb]);
+    }
+    auto softmax = [&](int kb) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const int r0 = half * 8 + e, r1 = r0 + 1;
+          float p0 = __builtin_amdgcn_exp2f(st[kb][r0] * c - lse2);
+          float p1 = __builtin_amdgcn_exp2f(st[kb][r1] * c - lse2);
+          if constexpr (!FULL) {
+            p0 = visible(kb, r0) ? p0 : 0.f;
+            p1 = visible(kb, r1) ? p1 : 0.f;
+          }
+          const float d0 = p0 * (dpt[kb][r0] - dl);
+          const float d1 = p1 * (dpt[kb][r1] - dl);
+          const bf16x2 pk2 = __builtin_convertvector((f32x2){d0, d1}, bf16x2);
+          dsb[kb][half][e] = pk2[0];
+          dsb[kb][half][e + 1] = pk2[1];
+        }
+      }
+    };
+    softmax(0);
+    softmax(1);
+    // C0, C1
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      if (j + PF < NC) fc[j + PF] = read_c(j + PF);
+      const int kb = j / (2 * DB), half = (j / DB) & 1, d = j % DB;
+      dqt[d] = mfma32(fc[j], dsb[kb][half], dqt[d]);
+    }
+    // scheduling groups, in issue order: A0 (MFMA, read), A1 (MFMA, read,
+    // B0's VALU), C0 (MFMA, reads, B1's VALU), C1 (MFMA, reads); a frag_tr
+    // is two DS reads
+    constexpr int NA0 = 2 * KS;
+    constexpr int NC0 = 2 * DB;
+    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      sched_ds_read((i + PF < NA) ? 1 : 2);
+      if (i >= NA0) __builtin_amdgcn_sched_group_barrier(0x002, kDqValuA, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (j + PF < NC) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if (j < NC0) __builtin_amdgcn_sched_group_barrier(0x002, kDqValuC, 0);
+    }
+  };
+
+  int n_tiles = 0;
+  for (int ri = it.run_begin; ri < it.run_end; ++ri) {
+    const Run r = p.runs[ri];
+    n_tiles += (r.k_end - r.k_begin + BN - 1) / BN;
+  }
+  int c_ri = it.run_begin;
+  Run c_run = n_tiles > 0 ? p.runs[c_ri] : Run{0, 0, 0, 0};
+  int c_k0 = c_run.k_begin;
+  if (n_tiles > 0) dma(smem, c_k0, c_run.k_end);
+  for (int n = 0; n < n_tiles; ++n) {
+    const int k0 = c_k0;
+    const Run run = c_run;
+    const char* tK = smem + (n & 1) * 2 * TILEB;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile n are in LDS
+    __syncthreads();                     // every wave's copies landed; tile n - 1's buffer is free
+    if (n + 1 < n_tiles) {
+      c_k0 += BN;
+      if (c_k0 >= c_run.k_end) {
+        c_run = p.runs[++c_ri];
+        c_k0 = c_run.k_begin;
+      }
+      dma(smem + ((n + 1) & 1) * 2 * TILEB, c_k0, c_run.k_end);
+    }
+    if (run.full) tile(std::true_type{}, tK, k0, run.k_end);
+    else tile(std::false_type{}, tK, k0, run.k_end);
   }
 
   // dq[b, row, h, :] += scale * dQ (this lane: query qrow, head-dim rows of dQ^T)
@@ -338,21 +489,28 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const BwdParams p) {
 // q_rank = KV rank, k_row0 = row of local query 0 of the query rank in the
 // q/dout buffers, k_rank = query rank; runs: local query rows
 // [k_begin, k_end) and whether every pair of the run is visible.
+//
+// The workgroup walks one flat sequence of query tiles ((run, 64-row tile)
+// backwards, query head of the KV group innermost) with two LDS buffers: tile n + 1 (Q, dO, LSE,
+// delta) is copied global -> LDS directly (buffer loads to LDS) while tile
+// n is computed.  Per tile and wave (32 keys, one per lane):
+//   A(qb): S and dP of query block qb (32 rows) = Q K^T, dO V^T;
+//   B(qb): P = exp2(S c - LSE log2 e), dS = P (dP - delta) -> bf16;
+//   C(qb): dV^T += dO^T P, dK^T += Q^T dS.
+// Issue order A0 A1 B0 B1 C0 C1, with B0's VALU work placed between A1's
+// MFMAs and B1's between C0's, and LDS fragment reads kPF MFMAs ahead.
 template <int D>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   using T = BwdTile<D>;
-  constexpr int BQ = 64;            // query rows per iteration
+  constexpr int BQ = 64;            // query rows per tile
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int NQB = BQ / 32;
   constexpr int TILEB = BQ * D * 2;
   constexpr int LPW = TILEB / 4096;
   constexpr int RPI = 1024 / T::ROWB;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * TILEB + 2 * BQ * 4];  // Q, dO, LSE2, delta
-  char* const tQ = smem;
-  char* const tO = smem + TILEB;
-  float* const sl = reinterpret_cast<float*>(smem + 2 * TILEB);
-  float* const sd = sl + BQ;
+  constexpr int BUFB = 2 * TILEB + 2 * BQ * 4;  // Q, dO, LSE, delta
+  constexpr int PF = kPF;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * BUFB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -360,9 +518,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  const int total = p.n_items * p.Hkv * p.B;
-  int bid = blockIdx.x;
-  if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+  // Items come sorted by decreasing work and the hardware deals consecutive
+  // workgroups round-robin to the 8 XCDs, so the plain order gives every XCD
+  // an even share of large and small items (with one KV head, a contiguous
+  // block per XCD would hand one XCD all the largest).
+  const int bid = blockIdx.x;
   const int hb = bid / p.n_items;
   const int item_idx = bid - hb * p.n_items;
   const int hk = hb % p.Hkv;
@@ -374,6 +534,48 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   const bool kvalid = kr_ < it.q_rows;
   const int64_t krow = (int64_t)it.q_row0 + kr_;
   const int64_t kv_row_stride = (int64_t)p.Hkv * D;
+
+  // query tiles of this item: group heads x runs x ceil(run / BQ)
+  int tiles_per_head = 0;
+  for (int ri = it.run_begin; ri < it.run_end; ++ri) {
+    const Run r = p.runs[ri];
+    tiles_per_head += (r.k_end - r.k_begin + BQ - 1) / BQ;
+  }
+  const int n_tiles = tiles_per_head * group;
+
+  // copy sources: heads hk*group .. hk*group+group-1 of the query rank's rows
+  const int h0 = hk * group;
+  const uint16_t* qbase = p.q + (int64_t)b * p.q_batch_stride + (int64_t)it.k_row0 * p.Hq * D + h0 * D;
+  const uint16_t* obase = p.dout + (int64_t)b * p.g_batch_stride + (int64_t)it.k_row0 * p.Hq * D + h0 * D;
+  const float* lbase = p.lse + ((int64_t)b * p.Hq + h0) * p.Lq_buf + it.k_row0;
+  const float* dbase = p.delta + ((int64_t)b * p.Hq + h0) * p.Lq_buf + it.k_row0;
+  const uint32_t qrow_bytes = (uint32_t)p.Hq * D * 2;
+  const i32x4 qrs = buffer_rsrc(qbase);
+  const i32x4 ors = buffer_rsrc(obase);
+  const i32x4 lrs = buffer_rsrc(wid == 1 ? (const void*)dbase : (const void*)lbase);
+  const int lrow = lane / T::CPR;
+  const int lslot = lane % T::CPR;
+
+  // Thread (wave wid, lane i) copies slices wid*LPW + j of Q and dO: physical
+  // (row, chunk slot) = (slice*RPI + i / CPR, i % CPR), i.e. logical chunk
+  // slot ^ swz(row) of that row; waves 0 and 1 copy the 64 LSE / delta
+  // values.  Rows past the run's end are clamped to its last row (they are
+  // masked in the partial runs that have them; full runs are multiples of
+  // BQ rows).
+  auto dma = [&](char* buf, int gi, int t0, int tend) {
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const int row = (wid * LPW + j) * RPI + lrow;
+      const uint32_t off = (uint32_t)min(t0 + row, tend - 1) * qrow_bytes + (uint32_t)(gi * D * 2) +
+                           (uint32_t)((lslot ^ T::swz(row)) * 16);
+      copy16_to_lds(qrs, lds_addr(buf + (wid * LPW + j) * 1024), off);
+      copy16_to_lds(ors, lds_addr(buf + TILEB + (wid * LPW + j) * 1024), off);
+    }
+    if (wid < 2) {
+      const uint32_t off = (uint32_t)(gi * p.Lq_buf + min(t0 + lane, tend - 1)) * 4u;
+      copy4_to_lds(lrs, lds_addr(buf + 2 * TILEB + wid * BQ * 4), off);
+    }
+  };
 
   bf16x8 kf[KS], vf[KS];
   {
@@ -395,7 +597,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dkt[d][r] = dvt[d][r] = 0.f;
 
-  // this lane's key position and the sequence it belongs to
+  // This lane's key position pk; the query positions that see it form one
+  // interval [lo_p, hi_p]: same sequence, p_q >= p_k under causal / window,
+  // and p_q - p_k < W unless the key is one of its sequence's sinks.
   PosMap qm = p.qmap;
   qm.rank = it.k_rank;
   PosMap km = p.kmap;
@@ -410,104 +614,154 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
     }
   }
   const bool cw = p.mask.causal || p.mask.window > 0;
-
-  const int lrow = lane / T::CPR;
-  const int lslot = lane % T::CPR;
+  const bool sink = p.mask.window > 0 && pk - ks0 < p.mask.n_sink;
+  const int32_t lo_p = cw ? max(ks0, pk) : ks0;
+  const int32_t hi_p = (p.mask.window > 0 && !sink) ? min(ks1 - 1, pk + p.mask.window - 1) : ks1 - 1;
   const float c = p.scale_log2;
 
-  for (int gi = 0; gi < group; ++gi) {
-    const int h = hk * group + gi;
-    const uint16_t* qbase = p.q + (int64_t)b * p.q_batch_stride + (int64_t)it.k_row0 * p.Hq * D + h * D;
-    const uint16_t* obase = p.dout + (int64_t)b * p.g_batch_stride + (int64_t)it.k_row0 * p.Hq * D + h * D;
-    const uint32_t qrow_bytes = (uint32_t)p.Hq * D * 2;
-    const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void*)qbase, (short)0, 0x7fffffff, kBufferRsrcWord3);
-    const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc((void*)obase, (short)0, 0x7fffffff, kBufferRsrcWord3);
-    const float* lse_h = p.lse + ((int64_t)b * p.Hq + h) * p.Lq_buf + it.k_row0;
-    const float* del_h = p.delta + ((int64_t)b * p.Hq + h) * p.Lq_buf + it.k_row0;
-
-    for (int ri = it.run_begin; ri < it.run_end; ++ri) {
-      const Run run = p.runs[ri];
-      for (int t0 = run.k_begin; t0 < run.k_end; t0 += BQ) {
-        i32x4 qr4[LPW], or4[LPW];
-#pragma unroll
-        for (int j = 0; j < LPW; ++j) {
-          const int row = (wid * LPW + j) * RPI + lrow;
-          const uint32_t roff = (uint32_t)min(t0 + row, run.k_end - 1) * qrow_bytes + (uint32_t)((lslot ^ T::swz(row)) * 16);
-          qr4[j] = __builtin_amdgcn_raw_buffer_load_b128(qrs, roff, 0, 0);
-          or4[j] = __builtin_amdgcn_raw_buffer_load_b128(ors, roff, 0, 0);
-        }
-        float lv = INFINITY, dv_ = 0.f;
-        if (tid < BQ && t0 + tid < run.k_end) {
-          const float l = lse_h[t0 + tid];
-          lv = l == -INFINITY ? INFINITY : l * kLog2e;
-          dv_ = del_h[t0 + tid];
-        }
-        __syncthreads();  // the previous query tile's reads are done
-#pragma unroll
-        for (int j = 0; j < LPW; ++j) {
-          *reinterpret_cast<i32x4*>(tQ + (wid * LPW + j) * 1024 + lane * 16) = qr4[j];
-          *reinterpret_cast<i32x4*>(tO + (wid * LPW + j) * 1024 + lane * 16) = or4[j];
-        }
-        if (tid < BQ) {
-          sl[tid] = lv;
-          sd[tid] = dv_;
-        }
-        __syncthreads();
-
-        // S = Q K^T and dP = dO V^T (queries x keys): lane = key, 16 queries
-        f32x16 s[NQB], dp[NQB];
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[qb][r] = dp[qb][r] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) {
-            s[qb] = mfma32(T::frag(tQ, qb * 32 + l32, 2 * ks + hi), kf[ks], s[qb]);
-            dp[qb] = mfma32(T::frag(tO, qb * 32 + l32, 2 * ks + hi), vf[ks], dp[qb]);
-          }
-        }
-        bf16x8 pb[NQB][2], dsb[NQB][2];
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int q4 = qb * 32 + 8 * g + 4 * hi;  // 4 consecutive queries
-            const float4 l4 = *reinterpret_cast<const float4*>(sl + q4);
-            const float4 d4 = *reinterpret_cast<const float4*>(sd + q4);
-            const float lq[4] = {l4.x, l4.y, l4.z, l4.w};
-            const float dq4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * g + e;
-              float x = s[qb][r];
-              if (!run.full) {
-                const int32_t pq = position(qm, t0 + q4 + e);
-                const bool vis = (pq >= ks0) & (pq < ks1) & (!cw | (pk <= pq)) &
-                                 ((p.mask.window <= 0) | (pq - pk < p.mask.window) |
-                                  ((pk - ks0 < p.mask.n_sink) & (pk <= pq)));
-                x = vis ? x : -INFINITY;
-              }
-              const float pr = __builtin_amdgcn_exp2f(x * c - lq[e]);
-              const float ds = pr * (dp[qb][r] - dq4[e]);
-              pb[qb][r >> 3][r & 7] = (__bf16)pr;
-              dsb[qb][r >> 3][r & 7] = (__bf16)ds;
-            }
-          }
-        }
-        // dV^T += dO^T P and dK^T += Q^T dS (head dim x keys)
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-          for (int half = 0; half < 2; ++half)
-#pragma unroll
-            for (int d = 0; d < DB; ++d) {
-              dvt[d] = mfma32(frag_tr<D>(tO, qb, half, d, lane), pb[qb][half], dvt[d]);
-              dkt[d] = mfma32(frag_tr<D>(tQ, qb, half, d, lane), dsb[qb][half], dkt[d]);
-            }
-      }
+  // One tile.  FULL: every pair visible.  Otherwise element r of query
+  // block qb is local row t0 + qb*32 + 8*(r/4) + 4*hi + r%4; query
+  // positions increase through the run, so the rows that see this lane's
+  // key are one interval, found once per tile.
+  auto tile = [&](auto full_c, const char* buf, int t0, int tend) {
+    constexpr bool FULL = decltype(full_c)::value;
+    const char* tQ = buf;
+    const char* tO = buf + TILEB;
+    const float* sl = reinterpret_cast<const float*>(buf + 2 * TILEB);
+    const float* sd = sl + BQ;
+    int32_t lo = 0, up = 0;
+    if constexpr (!FULL) {
+      lo = first_row_at_least(qm, t0, lo_p) - t0 - 4 * hi;
+      up = min(first_row_at_least(qm, t0, hi_p + 1) - 1, tend - 1) - t0 - 4 * hi;
     }
+    auto visible = [&](int qb, int r) -> bool {
+      if constexpr (FULL) {
+        return true;
+      } else {
+        const int cc = qb * 32 + 8 * (r >> 2) + (r & 3);
+        return (cc >= lo) & (cc <= up);
+      }
+    };
+    auto read_a = [&](int i) {
+      const int qb = i / (2 * KS), w = i % (2 * KS);
+      return T::frag((w & 1) ? tO : tQ, qb * 32 + l32, 2 * (w >> 1) + hi);
+    };
+    // C stream j: (qb, half, d, which): which 0 -> dO^T for dV, 1 -> Q^T for dK
+    auto read_c = [&](int j) {
+      const int qb = j / (4 * DB), r = j % (4 * DB), half = r / (2 * DB), d = (r / 2) % DB;
+      return frag_tr<D>((r & 1) ? tQ : tO, qb, half, d, lane);
+    };
+    constexpr int NA = 2 * 2 * KS;
+    constexpr int NC = 2 * 4 * DB;
+    f32x16 s[2], dp[2];
+    bf16x8 fa[NA], fc[NC];
+    bf16x8 pb[2][2], dsb[2][2];
+    const f32x16 zero = {};
+    // LSE and delta of this lane's 16 query rows per block (rows
+    // qb*32 + 8*g + 4*hi + 0..3 for g = 0..3)
+    float4 l4[2][4], d4[2][4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        l4[qb][g] = *reinterpret_cast<const float4*>(sl + qb * 32 + 8 * g + 4 * hi);
+        d4[qb][g] = *reinterpret_cast<const float4*>(sd + qb * 32 + 8 * g + 4 * hi);
+      }
+#pragma unroll
+    for (int i = 0; i < PF; ++i) fa[i] = read_a(i);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      if (i + PF < NA) fa[i + PF] = read_a(i + PF);
+      else fc[i + PF - NA] = read_c(i + PF - NA);
+      const int qb = i / (2 * KS), w = i % (2 * KS), ks = w >> 1;
+      if (w & 1) dp[qb] = mfma32(fa[i], vf[ks], ks == 0 ? zero : dp[qb]);
+      else s[qb] = mfma32(fa[i], kf[ks], ks == 0 ? zero : s[qb]);
+    }
+    auto softmax = [&](int qb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float lq[4] = {l4[qb][g].x, l4[qb][g].y, l4[qb][g].z, l4[qb][g].w};
+        const float dq4[4] = {d4[qb][g].x, d4[qb][g].y, d4[qb][g].z, d4[qb][g].w};
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+          const int r0 = 4 * g + e, r1 = r0 + 1;
+          float p0 = __builtin_amdgcn_exp2f(s[qb][r0] * c - lq[e] * kLog2e);
+          float p1 = __builtin_amdgcn_exp2f(s[qb][r1] * c - lq[e + 1] * kLog2e);
+          if constexpr (!FULL) {
+            p0 = visible(qb, r0) ? p0 : 0.f;
+            p1 = visible(qb, r1) ? p1 : 0.f;
+          }
+          const float d0 = p0 * (dp[qb][r0] - dq4[e]);
+          const float d1 = p1 * (dp[qb][r1] - dq4[e + 1]);
+          const bf16x2 pp = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
+          const bf16x2 dd = __builtin_convertvector((f32x2){d0, d1}, bf16x2);
+          pb[qb][r0 >> 3][r0 & 7] = pp[0];
+          pb[qb][r0 >> 3][r1 & 7] = pp[1];
+          dsb[qb][r0 >> 3][r0 & 7] = dd[0];
+          dsb[qb][r0 >> 3][r1 & 7] = dd[1];
+        }
+      }
+    };
+    softmax(0);
+    softmax(1);
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      if (j + PF < NC) fc[j + PF] = read_c(j + PF);
+      const int qb = j / (4 * DB), r = j % (4 * DB), half = r / (2 * DB), d = (r / 2) % DB;
+      if (r & 1) dkt[d] = mfma32(fc[j], dsb[qb][half], dkt[d]);
+      else dvt[d] = mfma32(fc[j], pb[qb][half], dvt[d]);
+    }
+    // scheduling groups, in issue order: the LSE / delta reads, A0 (MFMA,
+    // read), A1 (MFMA, read, B0's VALU), C0 (MFMA, reads, B1's VALU), C1
+    // (MFMA, reads)
+    constexpr int NA0 = 2 * KS;
+    constexpr int NC0 = 4 * DB;
+    __builtin_amdgcn_sched_group_barrier(0x100, 16 + PF, 0);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      sched_ds_read((i + PF < NA) ? 1 : 2);
+      if (i >= NA0) __builtin_amdgcn_sched_group_barrier(0x002, kKvValuA, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (j + PF < NC) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if (j < NC0) __builtin_amdgcn_sched_group_barrier(0x002, kKvValuC, 0);
+    }
+  };
+
+  // Tile order: query tiles from the last run's last tile backwards, the
+  // group's query heads innermost.  Under a causal mask every key tile's
+  // query range ends at the rank's last row, so the workgroups resident at
+  // one time start at the same rows and stream the same Q / dO tiles at
+  // about the same time (shared through L2 instead of refetched).
+  auto last_tile = [](const Run& r) { return r.k_begin + ((r.k_end - r.k_begin - 1) / BQ) * BQ; };
+  int c_gi = 0, c_ri = it.run_end - 1;
+  Run c_run = p.runs[c_ri];
+  int c_t0 = last_tile(c_run);
+  dma(smem, c_gi, c_t0, c_run.k_end);
+
+  for (int n = 0; n < n_tiles; ++n) {
+    const int t0 = c_t0;
+    const int t_end = c_run.k_end;
+    const bool full = c_run.full != 0;
+    const char* buf = smem + (n & 1) * BUFB;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile n are in LDS
+    __syncthreads();                     // every wave's copies landed; tile n - 1's buffer is free
+    if (n + 1 < n_tiles) {
+      if (++c_gi == group) {
+        c_gi = 0;
+        c_t0 -= BQ;
+        if (c_t0 < c_run.k_begin) {
+          c_run = p.runs[--c_ri];
+          c_t0 = last_tile(c_run);
+        }
+      }
+      dma(smem + ((n + 1) & 1) * BUFB, c_gi, c_t0, c_run.k_end);
+    }
+    if (full) tile(std::true_type{}, buf, t0, t_end);
+    else tile(std::false_type{}, buf, t0, t_end);
   }
 
   if (!kvalid || it.run_begin == it.run_end) return;
@@ -569,7 +823,6 @@ usp_status launch_bwd_delta(const void* out, int out_f32, const uint16_t* dout, 
 }
 
 usp_status launch_bwd(const BwdParams& pq, const BwdParams& pkv, int D, hipStream_t stream) {
-  const bool linear = !(pq.kmap.kind == MAP_STRIPE && pq.kmap.b > 1);
   const int64_t nq = (int64_t)pq.n_items * pq.Hq * pq.B;
   const int64_t nk = (int64_t)pkv.n_items * pkv.Hkv * pkv.B;
   if (nq > 0x7fffffff || nk > 0x7fffffff) {
@@ -578,13 +831,8 @@ usp_status launch_bwd(const BwdParams& pq, const BwdParams& pkv, int D, hipStrea
   }
   if (nq > 0) {
     TimingScope ts(K_BWD_DQ, stream);
-    if (D == 128) {
-      if (linear) hipLaunchKernelGGL((bwd_dq_kernel<128, true>), dim3((unsigned)nq), dim3(256), 0, stream, pq);
-      else hipLaunchKernelGGL((bwd_dq_kernel<128, false>), dim3((unsigned)nq), dim3(256), 0, stream, pq);
-    } else {
-      if (linear) hipLaunchKernelGGL((bwd_dq_kernel<64, true>), dim3((unsigned)nq), dim3(256), 0, stream, pq);
-      else hipLaunchKernelGGL((bwd_dq_kernel<64, false>), dim3((unsigned)nq), dim3(256), 0, stream, pq);
-    }
+    if (D == 128) hipLaunchKernelGGL((bwd_dq_kernel<128>), dim3((unsigned)nq), dim3(256), 0, stream, pq);
+    else hipLaunchKernelGGL((bwd_dq_kernel<64>), dim3((unsigned)nq), dim3(256), 0, stream, pq);
   }
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && nk > 0) {

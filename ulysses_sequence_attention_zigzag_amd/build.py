@@ -18,7 +18,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libusp.so")
-SOURCES = ["api.cpp", "plan.cpp", "timing.cpp", "permute.hip", "lse_merge.hip", "attn_fwd.hip", "attn_bwd.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "timing.cpp", "permute.hip", "lse_merge.hip", "attn_fwd.hip", "attn_bwd.hip",
+           "attn_bwd_dq.hip"]
+# per-source flags: the dQ kernel is built with VGPR-form MFMAs
+SOURCE_FLAGS = {"attn_bwd_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -34,7 +37,7 @@ COMMON = [
 def _compile(src: str, extra, csrc: str, build_dir: str) -> str:
     obj = os.path.join(build_dir, src + ".o")
     lang = ["-x", "hip"]
-    cmd = [HIPCC] + COMMON + list(extra) + lang + ["-c", os.path.join(csrc, src), "-o", obj]
+    cmd = [HIPCC] + COMMON + SOURCE_FLAGS.get(src, []) + list(extra) + lang + ["-c", os.path.join(csrc, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

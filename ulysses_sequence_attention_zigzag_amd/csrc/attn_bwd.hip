@@ -25,164 +25,10 @@
 //   B: col j = l % 32, the same 8 k values;
 //   C: acc[r] = C[8*(r/4) + 4*(l/32) + r%4][l % 32], r = 0..15.
 
-#include <hip/hip_runtime.h>
-
-#include <cmath>
-#include <type_traits>
-
-#include "usp_internal.h"
+#include "bwd_common.h"
 
 namespace usp {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-constexpr float kLog2e = 1.44269504088896340736f;
-// LDS fragment reads in flight ahead of the MFMAs that use them, and VALU
-// instructions placed after each MFMA of the phases that overlap a softmax
-constexpr int kPF = 4;
-constexpr int kDqValuA = 5;
-constexpr int kDqValuC = 10;
-constexpr int kKvValuA = 6;
-constexpr int kKvValuC = 6;
-constexpr int kBufferRsrcWord3 = 0x00020000;  // raw buffer resource word 3 (gfx9 family)
-
-// Scheduling group of n DS reads / n VALU instructions; n is a constant
-// after unrolling, so the switch folds away.
-__device__ __forceinline__ void sched_ds_read(int n) {
-  switch (n) {
-    case 1: __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); break;
-    case 2: __builtin_amdgcn_sched_group_barrier(0x100, 2, 0); break;
-    case 3: __builtin_amdgcn_sched_group_barrier(0x100, 3, 0); break;
-    case 4: __builtin_amdgcn_sched_group_barrier(0x100, 4, 0); break;
-    default: break;
-  }
-}
-
-__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ int32_t floor_div(int32_t a, int32_t b) {
-  if (b == 1) return a;
-  const int32_t q = a / b;
-  return (a % b != 0 && a < 0) ? q - 1 : q;
-}
-__device__ __forceinline__ int32_t ceil_div(int32_t a, int32_t b) { return -floor_div(-a, b); }
-
-// Smallest local row t with position(m, t) >= P, for a row t_ref of the
-// same monotone piece (positions increase with t across a whole basic,
-// stripe or affine rank, and within each chunk of a zigzag rank, where
-// they are consecutive).  Stripe: the rank holds blocks j*N + rank (block
-// j at rows j*b ..); P in one of them maps to its row, otherwise to the
-// first row of the rank's next block.  Exact for every t of the piece;
-// callers clamp to the rows they hold.
-__device__ __forceinline__ int32_t first_row_at_least(const PosMap& m, int32_t t_ref, int32_t P) {
-  if (m.kind == MAP_STRIPE) {
-    const int32_t beta = floor_div(P, m.b);
-    const int32_t o = P - beta * m.b;
-    const int32_t j = floor_div(beta - m.rank, m.N);
-    return (j * m.N + m.rank == beta) ? j * m.b + o : (j + 1) * m.b;
-  }
-  return t_ref + (P - position(m, t_ref));
-}
-
-// Raw buffer resource of `base` (no stride, 2^31 - 1 bytes, no swizzle),
-// wave-uniform so it lives in SGPRs.
-__device__ __forceinline__ i32x4 buffer_rsrc(const void* base) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
-  r[2] = 0x7fffffff;
-  r[3] = kBufferRsrcWord3;
-  return r;
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)p);
-}
-
-// Global -> LDS copies (buffer loads to LDS): lane i's 16 (or 4) bytes at
-// byte offset voff of the buffer land at LDS address lds + 16*i (4*i).
-// They are issued through inline assembly so that the compiler does not
-// order later LDS reads of other addresses behind them; the kernels wait
-// for them explicitly (s_waitcnt vmcnt(0), then a barrier) before reading
-// their destination, and never read a destination while a copy into it may
-// be in flight.
-// M0 (the LDS destination) is saved and restored around each copy.
-__device__ __forceinline__ void copy16_to_lds(const i32x4& rsrc, uint32_t lds, uint32_t voff) {
-  int saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(__builtin_amdgcn_readfirstlane((int)lds)), "v"(voff), "s"(rsrc));
-}
-__device__ __forceinline__ void copy4_to_lds(const i32x4& rsrc, uint32_t lds, uint32_t voff) {
-  int saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-      "buffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(__builtin_amdgcn_readfirstlane((int)lds)), "v"(voff), "s"(rsrc));
-}
-
-// ds_read_b64_tr_b16: within each group of 16 lanes, lane i supplies the
-// address of 4 consecutive bf16 (row i/4 of a 4 x 16 block); lane j receives
-// column j of the block.
-__device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
-  typedef short s16x4 __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((__attribute__((address_space(3))) char*)(p)));
-  return __builtin_bit_cast(bf16x4, v);
-}
-
-// LDS tile of R rows x D bf16 (CPR 16-byte chunks per row, RPL rows per
-// 256-byte bank line) with chunk c of row r at slot c ^ swz(r),
-//   swz(r) = 4 * ((r / RPL) % (CPR / 4)) + (r / (RPL * CPR / 4)) % 4.
-// Both read patterns hit distinct bank slots: a plain 16-byte read of one
-// chunk by 16 consecutive rows (swz takes 16 distinct values over the rows
-// of each bank-line position), and a transpose read of 4 consecutive rows x
-// 4 aligned chunks (swz / 4 differs between the rows sharing a line
-// position).
-template <int D>
-struct BwdTile {
-  static constexpr int CPR = D / 8;
-  static constexpr int RPL = 16 / CPR;
-  static constexpr int ROWB = D * 2;
-  __device__ static __forceinline__ int swz(int r) {
-    return 4 * ((r / RPL) & (CPR / 4 - 1)) + ((r / (RPL * CPR / 4)) & 3);
-  }
-  // 16-byte fragment: row r, logical chunk c
-  __device__ static __forceinline__ bf16x8 frag(const char* t, int r, int c) {
-    return *reinterpret_cast<const bf16x8*>(t + r * ROWB + ((c ^ swz(r)) * 16));
-  }
-};
-
-// Transposed fragment of a tile (rows = the contraction index): for MFMA
-// half `half` of 32-row block kb, head-dim block d, the 8 rows
-// kb*32 + 16*half + {0..3, 8..11} + 4*(l/32) of column d*32 + l%32, in the
-// k-order of a C-layout operand.
-template <int D>
-__device__ __forceinline__ bf16x8 frag_tr(const char* t, int kb, int half, int d, int lane) {
-  using T = BwdTile<D>;
-  const int hi = lane >> 5;
-  const int row0 = 4 * hi + ((lane & 15) >> 2);
-  const int chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  const int h8 = (lane & 1) * 8;
-  const int r0 = kb * 32 + half * 16 + row0;
-  const int r1 = r0 + 8;
-  const int c = 4 * d + chunk;
-  const bf16x4 a0 = lds_read_tr(t + r0 * T::ROWB + ((c ^ T::swz(r0)) * 16) + h8);
-  const bf16x4 a1 = lds_read_tr(t + r1 * T::ROWB + ((c ^ T::swz(r1)) * 16) + h8);
-  return bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-}
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float4* p, int64_t n4) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256)
@@ -216,271 +62,6 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const void* out, int out
     }
   }
   delta[(b * H + h) * L + t] = acc;
-}
-
-// -------------------------------------------------------------------- dQ
-// Per 64-key tile and wave (32 query rows, one per lane):
-//   A(kb): S^T and dP^T of key block kb (32 keys) = K Q^T, V dO^T;
-//   B(kb): dS^T = exp2(S^T c - lse2) (dP^T - delta) -> bf16 (B-operand order);
-//   C(kb): dQ^T += K^T dS^T.
-// Issue order A0 A1 B0 C0 B1 C1, with B0's VALU work placed between A1's
-// MFMAs and B1's between C0's, and every LDS fragment read issued kPF
-// MFMAs ahead of its use.
-template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const BwdParams p) {
-  using T = BwdTile<D>;
-  constexpr int BN = 64;
-  constexpr int KS = D / 16;
-  constexpr int DB = D / 32;
-  constexpr int TILEB = BN * D * 2;
-  constexpr int LPW = TILEB / 4096;
-  constexpr int RPI = 1024 / T::ROWB;
-  constexpr int PF = kPF;
-  static_assert(kTileN % BN == 0, "planner granularity");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILEB];  // two buffers of (K, V)
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wid = tid >> 6;
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
-
-  const int total = p.n_items * p.Hq * p.B;
-  int bid = blockIdx.x;
-  if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
-  const int hb = bid / p.n_items;
-  const int item_idx = bid - hb * p.n_items;
-  const int h = hb % p.Hq;
-  const int b = hb / p.Hq;
-  const WorkItem it = p.items[item_idx];
-  const int hk = h / (p.Hq / p.Hkv);
-
-  const int qr = wid * 32 + l32;
-  const bool qvalid = qr < it.q_rows;
-  const int64_t qrow = (int64_t)it.q_row0 + qr;
-
-  bf16x8 qf[KS], dof[KS];
-  {
-    const int64_t off = (int64_t)b * p.q_batch_stride + (qrow * p.Hq + h) * D + hi * 8;
-    const int64_t goff = (int64_t)b * p.g_batch_stride + (qrow * p.Hq + h) * D + hi * 8;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (qvalid) {
-        qf[ks] = *reinterpret_cast<const bf16x8*>(p.q + off + ks * 16);
-        dof[ks] = *reinterpret_cast<const bf16x8*>(p.dout + goff + ks * 16);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[ks][e] = dof[ks][e] = (__bf16)0.f;
-      }
-    }
-  }
-  // exp2 subtrahend (LSE in log2 units; +inf gives P = 0) and delta of this row
-  float lse2 = INFINITY, dl = 0.f;
-  if (qvalid) {
-    const int64_t li = ((int64_t)b * p.Hq + h) * p.Lq_buf + qrow;
-    const float l = p.lse[li];
-    lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
-    dl = p.delta[li];
-  }
-
-  f32x16 dqt[DB];
-#pragma unroll
-  for (int d = 0; d < DB; ++d)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dqt[d][r] = 0.f;
-
-  PosMap qm = p.qmap;
-  qm.rank = it.q_rank;
-  PosMap km = p.kmap;
-  km.rank = it.k_rank;
-  const bool cw = p.mask.causal || p.mask.window > 0;
-  int32_t sstart, vis_lo, vis_hi, sink_hi;
-  {
-    const int32_t pq = position(qm, it.t0 + (qvalid ? qr : 0));
-    int32_t s0 = 0, s1 = p.mask.S;
-    for (int i = 0; i < p.mask.nseq; ++i) {
-      const int32_t lo = p.cu_seqlens[i], up = p.cu_seqlens[i + 1];
-      if (pq >= lo && pq < up) {
-        s0 = lo;
-        s1 = up;
-      }
-    }
-    sstart = s0;
-    vis_hi = cw ? min(pq, s1 - 1) : s1 - 1;
-    vis_lo = p.mask.window > 0 ? max(s0, pq - p.mask.window + 1) : s0;
-    sink_hi = p.mask.window > 0 ? min(s0 + p.mask.n_sink - 1, vis_hi) : s0 - 1;
-  }
-
-  const int64_t kv_row_stride = (int64_t)p.Hkv * D;
-  const uint16_t* kbase = p.k + (int64_t)b * p.kv_batch_stride + (int64_t)it.k_row0 * kv_row_stride + hk * D;
-  const uint16_t* vbase = p.v + (int64_t)b * p.kv_batch_stride + (int64_t)it.k_row0 * kv_row_stride + hk * D;
-  const uint32_t row_bytes = (uint32_t)kv_row_stride * 2;
-  const i32x4 krs = buffer_rsrc(kbase);
-  const i32x4 vrs = buffer_rsrc(vbase);
-  const int lrow = lane / T::CPR;
-  const int lslot = lane % T::CPR;
-  const float c = p.scale_log2;
-
-  // The workgroup walks the key tiles of its runs with two LDS buffers: tile
-  // n + 1 is copied global -> LDS directly (buffer loads to LDS) while tile
-  // n is computed.  Thread (wave wid, lane i) copies slices wid*LPW + j of K
-  // and V: physical (row, chunk slot) = (slice*RPI + i / CPR, i % CPR), i.e.
-  // logical chunk slot ^ swz(row); rows past the run's end are clamped to its
-  // last row (masked in partial runs; full runs are multiples of BN keys).
-  auto dma = [&](char* buf, int k0, int kend) {
-#pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-      const int row = (wid * LPW + j) * RPI + lrow;
-      const uint32_t off = (uint32_t)min(k0 + row, kend - 1) * row_bytes + (uint32_t)((lslot ^ T::swz(row)) * 16);
-      copy16_to_lds(krs, lds_addr(buf + (wid * LPW + j) * 1024), off);
-      copy16_to_lds(vrs, lds_addr(buf + TILEB + (wid * LPW + j) * 1024), off);
-    }
-  };
-
-  // One tile.  FULL: every pair visible (no mask).  Otherwise element r of
-  // key block kb is key k0 + du, du = kb*32 + 8*(r/4) + 4*hi + r%4; key
-  // positions increase through the run, so this lane's visible keys (window
-  // band, sinks) are at most two intervals of du, found once per tile.
-  auto tile = [&](auto full_c, const char* tK, int k0, int kend) {
-    constexpr bool FULL = decltype(full_c)::value;
-    const char* tV = tK + TILEB;
-    int32_t lo = 0, up = 0, slo = 0, sup = -1;
-    if constexpr (!FULL) {
-      const int32_t last = kend - 1 - k0;
-      const int32_t sh = k0 + 4 * hi;
-      lo = first_row_at_least(km, k0, vis_lo) - sh;
-      up = min(first_row_at_least(km, k0, vis_hi + 1) - 1 - k0, last) - 4 * hi;
-      slo = first_row_at_least(km, k0, sstart) - sh;
-      sup = min(first_row_at_least(km, k0, sink_hi + 1) - 1 - k0, last) - 4 * hi;
-    }
-    auto visible = [&](int kb, int r) -> bool {
-      if constexpr (FULL) {
-        return true;
-      } else {
-        const int cc = kb * 32 + 8 * (r >> 2) + (r & 3);
-        return ((cc >= lo) & (cc <= up)) | ((cc >= slo) & (cc <= sup));
-      }
-    };
-    // fragment streams: A phase i -> (K or V row kb*32 + l32, chunk 2*(i/2)+hi);
-    // C phase j -> K^T block (kb, half, d)
-    auto read_a = [&](int i) {
-      const int kb = i / (2 * KS), w = i % (2 * KS);
-      return T::frag((w & 1) ? tV : tK, kb * 32 + l32, 2 * (w >> 1) + hi);
-    };
-    auto read_c = [&](int j) {
-      const int kb = j / (2 * DB), half = (j / DB) & 1, d = j % DB;
-      return frag_tr<D>(tK, kb, half, d, lane);
-    };
-    constexpr int NA = 2 * 2 * KS;   // A0 + A1 MFMAs
-    constexpr int NC = 2 * 2 * DB;   // C0 + C1 MFMAs
-    f32x16 st[2], dpt[2];
-    bf16x8 fa[NA], fc[NC];
-    bf16x8 dsb[2][2];
-    const f32x16 zero = {};
-#pragma unroll
-    for (int i = 0; i < PF; ++i) fa[i] = read_a(i);
-    // A0, A1 (B0 follows in program order; the groups below interleave it)
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      if (i + PF < NA) fa[i + PF] = read_a(i + PF);
-      else fc[i + PF - NA] = read_c(i + PF - NA);
-      const int kb = i / (2 * KS), w = i % (2 * KS), ks = w >> 1;
-      if (w & 1) dpt[kb] = mfma32(fa[i], dof[ks], ks == 0 ? zero : dpt[kb]);
-      else st[kb] = mfma32(fa[i], qf[ks], ks == 0 ? zero : st[kb]);
-    }
-    auto softmax = [&](int kb) {
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const int r0 = half * 8 + e, r1 = r0 + 1;
-          float p0 = __builtin_amdgcn_exp2f(st[kb][r0] * c - lse2);
-          float p1 = __builtin_amdgcn_exp2f(st[kb][r1] * c - lse2);
-          if constexpr (!FULL) {
-            p0 = visible(kb, r0) ? p0 : 0.f;
-            p1 = visible(kb, r1) ? p1 : 0.f;
-          }
-          const float d0 = p0 * (dpt[kb][r0] - dl);
-          const float d1 = p1 * (dpt[kb][r1] - dl);
-          const bf16x2 pk2 = __builtin_convertvector((f32x2){d0, d1}, bf16x2);
-          dsb[kb][half][e] = pk2[0];
-          dsb[kb][half][e + 1] = pk2[1];
-        }
-      }
-    };
-    softmax(0);
-    softmax(1);
-    // C0, C1
-#pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      if (j + PF < NC) fc[j + PF] = read_c(j + PF);
-      const int kb = j / (2 * DB), half = (j / DB) & 1, d = j % DB;
-      dqt[d] = mfma32(fc[j], dsb[kb][half], dqt[d]);
-    }
-    // scheduling groups, in issue order: A0 (MFMA, read), A1 (MFMA, read,
-    // B0's VALU), C0 (MFMA, reads, B1's VALU), C1 (MFMA, reads); a frag_tr
-    // is two DS reads
-    constexpr int NA0 = 2 * KS;
-    constexpr int NC0 = 2 * DB;
-    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      sched_ds_read((i + PF < NA) ? 1 : 2);
-      if (i >= NA0) __builtin_amdgcn_sched_group_barrier(0x002, kDqValuA, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (j + PF < NC) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      if (j < NC0) __builtin_amdgcn_sched_group_barrier(0x002, kDqValuC, 0);
-    }
-  };
-
-  int n_tiles = 0;
-  for (int ri = it.run_begin; ri < it.run_end; ++ri) {
-    const Run r = p.runs[ri];
-    n_tiles += (r.k_end - r.k_begin + BN - 1) / BN;
-  }
-  int c_ri = it.run_begin;
-  Run c_run = n_tiles > 0 ? p.runs[c_ri] : Run{0, 0, 0, 0};
-  int c_k0 = c_run.k_begin;
-  if (n_tiles > 0) dma(smem, c_k0, c_run.k_end);
-  for (int n = 0; n < n_tiles; ++n) {
-    const int k0 = c_k0;
-    const Run run = c_run;
-    const char* tK = smem + (n & 1) * 2 * TILEB;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile n are in LDS
-    __syncthreads();                     // every wave's copies landed; tile n - 1's buffer is free
-    if (n + 1 < n_tiles) {
-      c_k0 += BN;
-      if (c_k0 >= c_run.k_end) {
-        c_run = p.runs[++c_ri];
-        c_k0 = c_run.k_begin;
-      }
-      dma(smem + ((n + 1) & 1) * 2 * TILEB, c_k0, c_run.k_end);
-    }
-    if (run.full) tile(std::true_type{}, tK, k0, run.k_end);
-    else tile(std::false_type{}, tK, k0, run.k_end);
-  }
-
-  // dq[b, row, h, :] += scale * dQ (this lane: query qrow, head-dim rows of dQ^T)
-  if (!qvalid || it.run_begin == it.run_end) return;
-  float* op = p.dq + (int64_t)b * p.g_batch_stride + (qrow * p.Hq + h) * D;
-  const float sc = p.scale;
-#pragma unroll
-  for (int d = 0; d < DB; ++d) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int dd = d * 32 + 8 * g + 4 * hi;
-      float4 a = *reinterpret_cast<const float4*>(op + dd);
-      a.x += sc * dqt[d][4 * g];
-      a.y += sc * dqt[d][4 * g + 1];
-      a.z += sc * dqt[d][4 * g + 2];
-      a.w += sc * dqt[d][4 * g + 3];
-      *reinterpret_cast<float4*>(op + dd) = a;
-    }
-  }
 }
 
 // ------------------------------------------------------------------ dK dV
@@ -829,11 +410,7 @@ usp_status launch_bwd(const BwdParams& pq, const BwdParams& pkv, int D, hipStrea
     set_error("backward grid too large");
     return USP_ERR_UNSUPPORTED;
   }
-  if (nq > 0) {
-    TimingScope ts(K_BWD_DQ, stream);
-    if (D == 128) hipLaunchKernelGGL((bwd_dq_kernel<128>), dim3((unsigned)nq), dim3(256), 0, stream, pq);
-    else hipLaunchKernelGGL((bwd_dq_kernel<64>), dim3((unsigned)nq), dim3(256), 0, stream, pq);
-  }
+  if (nq > 0) launch_bwd_dq(pq, D, (unsigned)nq, stream);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && nk > 0) {
     TimingScope ts(K_BWD_DKDV, stream);

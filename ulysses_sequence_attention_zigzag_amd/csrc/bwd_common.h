@@ -1,0 +1,181 @@
+// Device helpers shared by the backward kernels (attn_bwd.hip: dK / dV,
+// delta; attn_bwd_dq.hip: dQ).  Everything here has internal linkage.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <type_traits>
+
+#include "usp_internal.h"
+
+namespace usp {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.44269504088896340736f;
+// LDS fragment reads in flight ahead of the MFMAs that use them, and VALU
+// instructions placed after each MFMA of the phases that overlap a softmax
+// (build-time overridable for tuning sweeps)
+#ifndef USP_BWD_PF
+#define USP_BWD_PF 4
+#endif
+#ifndef USP_BWD_DQ_VALU_A
+#define USP_BWD_DQ_VALU_A 5
+#endif
+#ifndef USP_BWD_DQ_VALU_C
+#define USP_BWD_DQ_VALU_C 10
+#endif
+#ifndef USP_BWD_KV_VALU_A
+#define USP_BWD_KV_VALU_A 6
+#endif
+#ifndef USP_BWD_KV_VALU_C
+#define USP_BWD_KV_VALU_C 6
+#endif
+constexpr int kPF = USP_BWD_PF;
+constexpr int kDqValuA = USP_BWD_DQ_VALU_A;
+constexpr int kDqValuC = USP_BWD_DQ_VALU_C;
+constexpr int kKvValuA = USP_BWD_KV_VALU_A;
+constexpr int kKvValuC = USP_BWD_KV_VALU_C;
+constexpr int kBufferRsrcWord3 = 0x00020000;  // raw buffer resource word 3 (gfx9 family)
+
+// Scheduling group of n DS reads / n VALU instructions; n is a constant
+// after unrolling, so the switch folds away.
+__device__ __forceinline__ void sched_ds_read(int n) {
+  switch (n) {
+    case 1: __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); break;
+    case 2: __builtin_amdgcn_sched_group_barrier(0x100, 2, 0); break;
+    case 3: __builtin_amdgcn_sched_group_barrier(0x100, 3, 0); break;
+    case 4: __builtin_amdgcn_sched_group_barrier(0x100, 4, 0); break;
+    default: break;
+  }
+}
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int32_t floor_div(int32_t a, int32_t b) {
+  if (b == 1) return a;
+  const int32_t q = a / b;
+  return (a % b != 0 && a < 0) ? q - 1 : q;
+}
+__device__ __forceinline__ int32_t ceil_div(int32_t a, int32_t b) { return -floor_div(-a, b); }
+
+// Smallest local row t with position(m, t) >= P, for a row t_ref of the
+// same monotone piece (positions increase with t across a whole basic,
+// stripe or affine rank, and within each chunk of a zigzag rank, where
+// they are consecutive).  Stripe: the rank holds blocks j*N + rank (block
+// j at rows j*b ..); P in one of them maps to its row, otherwise to the
+// first row of the rank's next block.  Exact for every t of the piece;
+// callers clamp to the rows they hold.
+__device__ __forceinline__ int32_t first_row_at_least(const PosMap& m, int32_t t_ref, int32_t P) {
+  if (m.kind == MAP_STRIPE) {
+    const int32_t beta = floor_div(P, m.b);
+    const int32_t o = P - beta * m.b;
+    const int32_t j = floor_div(beta - m.rank, m.N);
+    return (j * m.N + m.rank == beta) ? j * m.b + o : (j + 1) * m.b;
+  }
+  return t_ref + (P - position(m, t_ref));
+}
+
+// Raw buffer resource of `base` (no stride, 2^31 - 1 bytes, no swizzle),
+// wave-uniform so it lives in SGPRs.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r[2] = 0x7fffffff;
+  r[3] = kBufferRsrcWord3;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)p);
+}
+
+// Global -> LDS copies (buffer loads to LDS): lane i's 16 (or 4) bytes at
+// byte offset voff of the buffer land at LDS address lds + 16*i (4*i).
+// They are issued through inline assembly so that the compiler does not
+// order later LDS reads of other addresses behind them; the kernels wait
+// for them explicitly (s_waitcnt vmcnt(0), then a barrier) before reading
+// their destination, and never read a destination while a copy into it may
+// be in flight.
+// M0 (the LDS destination) is saved and restored around each copy.
+__device__ __forceinline__ void copy16_to_lds(const i32x4& rsrc, uint32_t lds, uint32_t voff) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane((int)lds)), "v"(voff), "s"(rsrc));
+}
+__device__ __forceinline__ void copy4_to_lds(const i32x4& rsrc, uint32_t lds, uint32_t voff) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane((int)lds)), "v"(voff), "s"(rsrc));
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i supplies the
+// address of 4 consecutive bf16 (row i/4 of a 4 x 16 block); lane j receives
+// column j of the block.
+__device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((__attribute__((address_space(3))) char*)(p)));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// LDS tile of R rows x D bf16 (CPR 16-byte chunks per row, RPL rows per
+// 256-byte bank line) with chunk c of row r at slot c ^ swz(r),
+//   swz(r) = 4 * ((r / RPL) % (CPR / 4)) + (r / (RPL * CPR / 4)) % 4.
+// Both read patterns hit distinct bank slots: a plain 16-byte read of one
+// chunk by 16 consecutive rows (swz takes 16 distinct values over the rows
+// of each bank-line position), and a transpose read of 4 consecutive rows x
+// 4 aligned chunks (swz / 4 differs between the rows sharing a line
+// position).
+template <int D>
+struct BwdTile {
+  static constexpr int CPR = D / 8;
+  static constexpr int RPL = 16 / CPR;
+  static constexpr int ROWB = D * 2;
+  __device__ static __forceinline__ int swz(int r) {
+    return 4 * ((r / RPL) & (CPR / 4 - 1)) + ((r / (RPL * CPR / 4)) & 3);
+  }
+  // 16-byte fragment: row r, logical chunk c
+  __device__ static __forceinline__ bf16x8 frag(const char* t, int r, int c) {
+    return *reinterpret_cast<const bf16x8*>(t + r * ROWB + ((c ^ swz(r)) * 16));
+  }
+};
+
+// Transposed fragment of a tile (rows = the contraction index): for MFMA
+// half `half` of 32-row block kb, head-dim block d, the 8 rows
+// kb*32 + 16*half + {0..3, 8..11} + 4*(l/32) of column d*32 + l%32, in the
+// k-order of a C-layout operand.
+template <int D>
+__device__ __forceinline__ bf16x8 frag_tr(const char* t, int kb, int half, int d, int lane) {
+  using T = BwdTile<D>;
+  const int hi = lane >> 5;
+  const int row0 = 4 * hi + ((lane & 15) >> 2);
+  const int chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int h8 = (lane & 1) * 8;
+  const int r0 = kb * 32 + half * 16 + row0;
+  const int r1 = r0 + 8;
+  const int c = 4 * d + chunk;
+  const bf16x4 a0 = lds_read_tr(t + r0 * T::ROWB + ((c ^ T::swz(r0)) * 16) + h8);
+  const bf16x4 a1 = lds_read_tr(t + r1 * T::ROWB + ((c ^ T::swz(r1)) * 16) + h8);
+  return bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+}
+
+}  // namespace
+}  // namespace usp

@@ -204,6 +204,8 @@ constexpr int kBwdTileM = 128;  // query rows per dQ workgroup
 constexpr int kBwdTileK = 128;  // keys per dK / dV workgroup
 constexpr int kBwdTileQ = 64;   // query rows per dK / dV iteration
 usp_status launch_bwd(const BwdParams& pq, const BwdParams& pkv, int D, hipStream_t stream);
+// Enqueues the dQ kernel alone (no error check; launch_bwd checks).
+void launch_bwd_dq(const BwdParams& p, int D, unsigned grid, hipStream_t stream);
 usp_status launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 usp_status launch_bwd_delta(const void* out, int out_f32, const uint16_t* dout, float* delta, int64_t B,
                             int64_t L, int64_t H, int64_t D, hipStream_t stream);

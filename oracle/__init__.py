@@ -15,8 +15,10 @@ Modules
                  the associative max/logsumexp merge of partials
   backward_ref   the gradients (dQ, dK, dV) of masked softmax attention from
                  the chain rule, per ring step and summed over the ring
+  decode_ref     decode-time attention of new queries over a KV cache, the
+                 partials of cache pieces, and their pairwise tree merge
 
 Every function is pinned by ``tests/test_oracle_*.py`` against brute force,
 a library routine, closed forms, or values and invariants the pages state.
 """
-from . import index_ref, attention_ref, ring_ref, backward_ref  # noqa: F401
+from . import index_ref, attention_ref, ring_ref, backward_ref, decode_ref  # noqa: F401

@@ -196,6 +196,40 @@ usp_status usp_block_attn_bwd(const void* q, const void* k, const void* v, const
                               const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int nseq,
                               void* stream);
 
+/* --------------------------------------------------------------- decode
+ * Decode-time attention over a KV cache, as flash decoding: the cache is cut
+ * into pieces of split_keys keys whose partial (O, LSE) are computed
+ * independently, then combined [LCA "Ring Attention": flash decoding as
+ * ring attention at inference; "Tree Attention": the combine is associative
+ * and can run as a tree reduction].
+ *
+ * q [B,Lq,Hq,D] bf16: Lq new queries per batch row, sitting at the last Lq
+ * positions of that row's cache (query t at kv_len - Lq + t); k, v
+ * [B,S,Hkv,D] bf16: the cache, row b valid for keys 0 .. kv_len[b]-1
+ * (kv_lens NULL: every row holds S keys; otherwise given on device and on
+ * host, values in [Lq, S]).  Visibility: causal, and with window > 0 the
+ * window / n_sink rule of usp_block_attn_fwd (positions from 0 per row).
+ * (Hq/Hkv)*Lq must not exceed 32; D is 64 or 128; split_keys is a positive
+ * multiple of 32.  softmax_scale <= 0 selects 1/sqrt(D).
+ *
+ * usp_decode_split_fwd writes, for n = ceil(S / split_keys) pieces, the
+ *   partials out_part [n,B,Lq,Hq,D] and lse_part [n,B,Hq,Lq] (f32) of keys
+ *   [i*split_keys, (i+1)*split_keys) of each row (LSE = -inf, O = 0 for a
+ *   piece with no visible key).  Reads every valid K / V byte once.
+ * usp_decode_merge combines the n partials of every (row, query, head):
+ *   groups of threads fold interleaved pieces, then pairwise rounds combine
+ *   the groups; out [B,Lq,Hq,D] (out_dt) and lse [B,Hq,Lq] f32. */
+usp_status usp_decode_split_fwd(const void* q, const void* k, const void* v,
+                                const int32_t* kv_lens_dev, const int32_t* kv_lens_host,
+                                float* out_part, float* lse_part,
+                                int64_t B, int64_t Lq, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
+                                int64_t split_keys, float softmax_scale, int window, int n_sink,
+                                void* stream);
+
+usp_status usp_decode_merge(const float* out_part, const float* lse_part, int64_t n_split,
+                            int64_t B, int64_t Lq, int64_t Hq, int64_t D,
+                            void* out, usp_dtype out_dt, float* lse, void* stream);
+
 /* ---------------------------------------------------------------- merge
  * In-place associative combine of a partial into a running result, rows
  * [row_begin, row_end) of the sequence axis [LCA "Tree Attention": max and
@@ -334,7 +368,9 @@ typedef enum {
   USP_KERNEL_MERGE = 3,     /* separate LSE merge                                   */
   USP_KERNEL_BWD_DQ = 4,    /* backward: dQ kernel of usp_block_attn_bwd            */
   USP_KERNEL_BWD_DKDV = 5,  /* backward: dK / dV kernel of usp_block_attn_bwd       */
-  USP_KERNEL_BWD_DELTA = 6  /* backward: usp_attn_bwd_preprocess                    */
+  USP_KERNEL_BWD_DELTA = 6, /* backward: usp_attn_bwd_preprocess                    */
+  USP_KERNEL_DECODE = 7,    /* decode: usp_decode_split_fwd                         */
+  USP_KERNEL_DECODE_MERGE = 8 /* decode: usp_decode_merge                           */
 } usp_kernel_class;
 
 usp_status usp_timing_enable(int enable);

@@ -85,6 +85,9 @@ _SIGS = {
     "usp_block_attn_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64,
                             ctypes.c_float, _I32, ctypes.POINTER(PosMap), ctypes.POINTER(PosMap), _I32, _I32,
                             _I32, _P, _P, _I32, _P], _I32),
+    "usp_decode_split_fwd": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64, ctypes.c_float,
+                              _I32, _I32, _P], _I32),
+    "usp_decode_merge": ([_P, _P, _I64, _I64, _I64, _I64, _I64, _P, _I32, _P, _P], _I32),
     "usp_timing_enable": ([_I32], _I32),
     "usp_timing_reset": ([], _I32),
     "usp_timing_read": ([_I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64)], _I32),
@@ -260,6 +263,54 @@ def block_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torc
     return dq, dk, dv
 
 
+def decode_split_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, kv_lens=None, split_keys: int = 256,
+                     window: int = 0, n_sink: int = 0, softmax_scale: float = 0.0, out_part=None, lse_part=None,
+                     stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Partials of the cache pieces (usp_decode_split_fwd): q [B,Lq,Hq,D], cache k / v [B,S,Hkv,D] bf16.
+    Returns (out_part [n,B,Lq,Hq,D], lse_part [n,B,Hq,Lq]) f32."""
+    B, Lq, Hq, D = q.shape
+    S, Hkv = k.shape[1], k.shape[2]
+    n = (S + split_keys - 1) // split_keys
+    if out_part is None:
+        out_part = torch.empty((n, B, Lq, Hq, D), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((n, B, Hq, Lq), dtype=torch.float32, device=q.device)
+    lens_host = lens_dev = None
+    if kv_lens is not None:
+        lens_host = torch.tensor([int(x) for x in kv_lens], dtype=torch.int32)
+        lens_dev = lens_host.to(q.device)
+    _check(lib().usp_decode_split_fwd(
+        _dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"),
+        ctypes.c_void_p(lens_dev.data_ptr()) if lens_dev is not None else None,
+        ctypes.c_void_p(lens_host.data_ptr()) if lens_host is not None else None,
+        _dev(out_part, torch.float32, "out_part"), _dev(lse_part, torch.float32, "lse_part"),
+        B, Lq, S, Hq, Hkv, D, split_keys, float(softmax_scale), int(window), int(n_sink), _stream(stream)))
+    if lens_dev is not None:
+        torch.cuda.current_stream().synchronize()  # the kv_lens copy must outlive the launch
+    return out_part, lse_part
+
+
+def decode_merge(out_part: torch.Tensor, lse_part: torch.Tensor, *, out_dtype=torch.float32, out=None, lse=None,
+                 stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Combines the piece partials (usp_decode_merge): out [B,Lq,Hq,D], lse [B,Hq,Lq]."""
+    n, B, Lq, Hq, D = out_part.shape
+    if out is None:
+        out = torch.empty((B, Lq, Hq, D), dtype=out_dtype, device=out_part.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=out_part.device)
+    _check(lib().usp_decode_merge(_dev(out_part, torch.float32, "out_part"), _dev(lse_part, torch.float32, "lse_part"),
+                                  n, B, Lq, Hq, D, _dev(out, None, "out"), DT[out.dtype], _dev(lse, torch.float32, "lse"),
+                                  _stream(stream)))
+    return out, lse
+
+
+def decode_fwd(q, k, v, **kw) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Split-KV decode then the merge; keyword arguments of decode_split_fwd plus out_dtype."""
+    out_dtype = kw.pop("out_dtype", torch.float32)
+    parts = decode_split_fwd(q, k, v, **kw)
+    return decode_merge(*parts, out_dtype=out_dtype)
+
+
 def lse_merge(out_acc: torch.Tensor, lse_acc: torch.Tensor, out_part: torch.Tensor, lse_part: torch.Tensor,
               row_begin: int = 0, row_end: Optional[int] = None, stream=None) -> None:
     """In-place merge of (out_part, lse_part) into (out_acc, lse_acc)."""
@@ -380,7 +431,7 @@ def ring_fwd(q, k, v, **kw) -> Tuple[torch.Tensor, torch.Tensor]:
 
 # ---------------------------------------------------------------- timing
 KERNEL_CLASSES = {"attn": 0, "permute": 1, "relayout": 2, "merge": 3, "bwd_dq": 4, "bwd_dkdv": 5,
-                  "bwd_delta": 6}
+                  "bwd_delta": 6, "decode": 7, "decode_merge": 8}
 
 
 def timing_enable(on: bool = True) -> None:

@@ -532,6 +532,64 @@ usp_status usp_block_attn_bwd(const void* q, const void* k, const void* v, const
   return launch_bwd(pq, pk, (int)D, as_stream(stream));
 }
 
+usp_status usp_decode_split_fwd(const void* q, const void* k, const void* v, const int32_t* kv_lens_dev,
+                                const int32_t* kv_lens_host, float* out_part, float* lse_part, int64_t B, int64_t Lq,
+                                int64_t S, int64_t Hq, int64_t Hkv, int64_t D, int64_t split_keys,
+                                float softmax_scale, int window, int n_sink, void* stream) {
+  USP_CHECK(q && k && v && out_part && lse_part, USP_ERR_INVALID_ARG, "null tensor pointer");
+  USP_CHECK(B >= 1 && Lq >= 1 && S >= 1 && Hq >= 1 && Hkv >= 1, USP_ERR_INVALID_ARG, "bad sizes");
+  USP_CHECK(D == 64 || D == 128, USP_ERR_UNSUPPORTED, "head_dim must be 64 or 128, got %lld", (long long)D);
+  USP_CHECK(Hq % Hkv == 0, USP_ERR_INVALID_ARG, "Hq (%lld) must be a multiple of Hkv (%lld)", (long long)Hq, (long long)Hkv);
+  USP_CHECK((Hq / Hkv) * Lq <= 32, USP_ERR_UNSUPPORTED,
+            "decode serves at most 32 queries per KV head (Hq/Hkv = %lld times Lq = %lld)", (long long)(Hq / Hkv),
+            (long long)Lq);
+  USP_CHECK(Lq <= S, USP_ERR_INVALID_ARG, "Lq (%lld) exceeds the cache length %lld", (long long)Lq, (long long)S);
+  USP_CHECK(split_keys >= 32 && split_keys % 32 == 0 && split_keys <= kMaxI32, USP_ERR_INVALID_ARG,
+            "split_keys must be a positive multiple of 32, got %lld", (long long)split_keys);
+  USP_CHECK(window >= 0 && n_sink >= 0, USP_ERR_INVALID_ARG, "window and n_sink must be >= 0");
+  USP_CHECK(std::isfinite(softmax_scale), USP_ERR_INVALID_ARG, "softmax_scale must be finite");
+  USP_CHECK((kv_lens_dev == nullptr) == (kv_lens_host == nullptr), USP_ERR_INVALID_ARG,
+            "kv_lens must be given on both host and device, or neither");
+  USP_CHECK(S * Hkv * D * 2 < ((int64_t)1 << 31), USP_ERR_UNSUPPORTED,
+            "one batch row of the k/v cache must be under 2 GiB (32-bit tile offsets)");
+  USP_CHECK(B <= 65535 && Hkv <= 65535 && B * Lq * Hq <= kMaxI32, USP_ERR_UNSUPPORTED, "too many rows or heads");
+  if (kv_lens_host)
+    for (int64_t b = 0; b < B; ++b)
+      USP_CHECK(kv_lens_host[b] >= Lq && kv_lens_host[b] <= S, USP_ERR_INVALID_ARG,
+                "kv_lens[%lld] = %d outside [Lq, S] = [%lld, %lld]", (long long)b, kv_lens_host[b], (long long)Lq,
+                (long long)S);
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)D);
+  DecodeParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.kv_lens = kv_lens_dev;
+  p.out_part = out_part;
+  p.lse_part = lse_part;
+  p.B = (int32_t)B;
+  p.Lq = (int32_t)Lq;
+  p.S = (int32_t)S;
+  p.Hq = (int32_t)Hq;
+  p.Hkv = (int32_t)Hkv;
+  p.n_split = (int32_t)((S + split_keys - 1) / split_keys);
+  p.split_keys = (int32_t)split_keys;
+  p.window = window;
+  p.n_sink = n_sink;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  return launch_decode_split(p, (int)D, as_stream(stream));
+}
+
+usp_status usp_decode_merge(const float* out_part, const float* lse_part, int64_t n_split, int64_t B, int64_t Lq,
+                            int64_t Hq, int64_t D, void* out, usp_dtype out_dt, float* lse, void* stream) {
+  USP_CHECK(out_part && lse_part && out && lse, USP_ERR_INVALID_ARG, "null tensor pointer");
+  USP_CHECK(n_split >= 1 && n_split <= kMaxI32 && B >= 1 && Lq >= 1 && Hq >= 1, USP_ERR_INVALID_ARG, "bad sizes");
+  USP_CHECK(D == 64 || D == 128, USP_ERR_UNSUPPORTED, "head_dim must be 64 or 128, got %lld", (long long)D);
+  USP_CHECK(out_dt == USP_DT_BF16 || out_dt == USP_DT_F32, USP_ERR_INVALID_ARG, "bad out dtype");
+  USP_CHECK(B * Lq * Hq <= kMaxI32, USP_ERR_UNSUPPORTED, "too many rows");
+  return launch_decode_merge(out_part, lse_part, (int32_t)n_split, (int32_t)B, (int32_t)Lq, (int32_t)Hq, (int)D, out,
+                             out_dt == USP_DT_F32, lse, as_stream(stream));
+}
+
 // ------------------------------------------------------------ virtual ring
 namespace {
 

@@ -25,7 +25,7 @@
 //   B: col j = l % 32, the same 8 k values;
 //   C: acc[r] = C[8*(r/4) + 4*(l/32) + r%4][l % 32], r = 0..15.
 
-#include "bwd_common.h"
+#include "mfma_common.h"
 
 namespace usp {
 namespace {
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const void* out, int out
 // MFMAs and B1's between C0's, and LDS fragment reads kPF MFMAs ahead.
 template <int D>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
-  using T = BwdTile<D>;
+  using T = SwzTile<D>;
   constexpr int BQ = 64;            // query rows per tile
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;

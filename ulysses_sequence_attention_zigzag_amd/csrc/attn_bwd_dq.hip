@@ -4,7 +4,7 @@
 // feed VALU softmax work directly and the dQ accumulators stay put, where the
 // AGPR form would copy them between register files every tile.
 
-#include "bwd_common.h"
+#include "mfma_common.h"
 
 namespace usp {
 namespace {
@@ -19,7 +19,7 @@ namespace {
 // MFMAs ahead of its use.
 template <int D>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const BwdParams p) {
-  using T = BwdTile<D>;
+  using T = SwzTile<D>;
   constexpr int BN = 64;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;

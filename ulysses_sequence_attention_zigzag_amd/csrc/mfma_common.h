@@ -1,5 +1,6 @@
-// Device helpers shared by the backward kernels (attn_bwd.hip: dK / dV,
-// delta; attn_bwd_dq.hip: dQ).  Everything here has internal linkage.
+// Device helpers shared by the MFMA kernels that stage tiles through LDS
+// (backward: attn_bwd.hip, attn_bwd_dq.hip; decode: decode.hip).  Everything
+// here has internal linkage.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -145,7 +146,7 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
 // 4 aligned chunks (swz / 4 differs between the rows sharing a line
 // position).
 template <int D>
-struct BwdTile {
+struct SwzTile {
   static constexpr int CPR = D / 8;
   static constexpr int RPL = 16 / CPR;
   static constexpr int ROWB = D * 2;
@@ -164,7 +165,7 @@ struct BwdTile {
 // k-order of a C-layout operand.
 template <int D>
 __device__ __forceinline__ bf16x8 frag_tr(const char* t, int kb, int half, int d, int lane) {
-  using T = BwdTile<D>;
+  using T = SwzTile<D>;
   const int hi = lane >> 5;
   const int row0 = 4 * hi + ((lane & 15) >> 2);
   const int chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);

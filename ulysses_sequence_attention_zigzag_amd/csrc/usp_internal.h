@@ -207,6 +207,24 @@ usp_status launch_bwd(const BwdParams& pq, const BwdParams& pkv, int D, hipStrea
 // Enqueues the dQ kernel alone (no error check; launch_bwd checks).
 void launch_bwd_dq(const BwdParams& p, int D, unsigned grid, hipStream_t stream);
 usp_status launch_fill_zero(float* p, int64_t n, hipStream_t stream);
+
+// Decode over a KV cache, split into pieces of split_keys keys (a multiple
+// of 32); one wave per (piece, batch row, KV head).
+struct DecodeParams {
+  const uint16_t* q;       // [B, Lq, Hq, D]
+  const uint16_t* k;       // [B, S, Hkv, D]
+  const uint16_t* v;
+  const int32_t* kv_lens;  // [B] valid cache length per row, or nullptr (all S)
+  float* out_part;         // [n_split, B, Lq, Hq, D]
+  float* lse_part;         // [n_split, B, Hq, Lq]
+  int32_t B, Lq, S, Hq, Hkv;
+  int32_t n_split, split_keys;
+  int32_t window, n_sink;
+  float scale_log2;        // softmax_scale * log2(e)
+};
+usp_status launch_decode_split(const DecodeParams& p, int D, hipStream_t stream);
+usp_status launch_decode_merge(const float* out_part, const float* lse_part, int32_t n_split, int32_t B, int32_t Lq,
+                               int32_t Hq, int D, void* out, int out_f32, float* lse, hipStream_t stream);
 usp_status launch_bwd_delta(const void* out, int out_f32, const uint16_t* dout, float* delta, int64_t B,
                             int64_t L, int64_t H, int64_t D, hipStream_t stream);
 
@@ -251,7 +269,9 @@ enum KernelClass : int {
   K_MERGE = 3,
   K_BWD_DQ = 4,
   K_BWD_DKDV = 5,
-  K_BWD_DELTA = 6
+  K_BWD_DELTA = 6,
+  K_DECODE = 7,
+  K_DECODE_MERGE = 8
 };
 
 // Brackets one launch with hipEvents on `stream` while timing is enabled.

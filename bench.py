@@ -254,8 +254,12 @@ def main():
     ap.add_argument("--merge-mode", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="which", choices=["forward", "backward"], default="forward",
-                    help="forward: usp_ring_fwd (default); backward: usp_ring_bwd of that forward")
+    ap.add_argument("--pass", dest="which", choices=["forward", "backward", "decode"], default="forward",
+                    help="forward: usp_ring_fwd (default); backward: usp_ring_bwd of that forward; "
+                         "decode: split-KV decode + merge over a KV cache (--workload decode_gqa_128k or "
+                         "decode_mqa_1m)")
+    ap.add_argument("--split-keys", type=int, default=0,
+                    help="decode: keys per cache piece (0: the binding's default_split_keys)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy kernel (float32 negate) over MIB MiB, three times, "
                          "as the known-size reference for HBM byte counters, and exit")
@@ -284,6 +288,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration": {"read_bytes": 4 * n, "write_bytes": 4 * n, "launches": 3}}))
         return
+    if args.which == "decode":
+        return bench_decode(args)
     w = si.WORKLOADS[args.workload]
     t0 = time.perf_counter()
     q, k, v = w.make_inputs()
@@ -466,6 +472,123 @@ def bench_backward(args, w, q, k, v, qd, kd, vd):
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline_bwd(w, q, k, v, dout, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+# Decode workloads: one new token per sequence over a full KV cache, with
+# the head counts of the two large ring workloads (global heads: decoding
+# runs after the sequence-parallel prefill, on the gathered cache).
+DECODE_WORKLOADS = {
+    "decode_gqa_128k": dict(B=4, S=131072, Lq=1, Hq=32, Hkv=8, D=128, seed=2001),
+    "decode_mqa_1m": dict(B=1, S=1048576, Lq=1, Hq=8, Hkv=1, D=128, seed=2002),
+}
+
+
+def cpu_baseline_decode(cfg, q, k, v, budget_s: float):
+    """Times the float64 oracle's decode on whole (batch row, KV head) units
+    of the workload: bytes of K / V attended per second."""
+    import torch
+    from oracle.decode_ref import decode_ref
+
+    threads = torch.get_num_threads()
+    B, Hkv, group = cfg["B"], cfg["Hkv"], cfg["Hq"] // cfg["Hkv"]
+    done, t_used, nbytes = 0, 0.0, 0
+    units = [(b, g) for b in range(B) for g in range(Hkv)]
+    while t_used < budget_s and done < len(units):
+        b, g = units[done]
+        qs = q[b:b + 1, :, g * group:(g + 1) * group]
+        ks, vs = k[b:b + 1, :, g:g + 1], v[b:b + 1, :, g:g + 1]
+        t0 = time.perf_counter()
+        decode_ref(qs, ks, vs)
+        t_used += time.perf_counter() - t0
+        nbytes += 2 * ks.numel() * 2
+        done += 1
+    return {"value": nbytes / t_used / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {len(units)} (batch row, KV head) units, whole cache, float64 torch CPU, "
+                      f"{t_used:.1f} s"}
+
+
+def bench_decode(args):
+    """Times one decode step (usp_decode_split_fwd + usp_decode_merge) over a
+    KV cache resident in HBM; the split kernel is HBM-bound."""
+    import torch
+
+    import seeded_inputs as si
+    import ulysses_sequence_attention_zigzag_amd as usp
+
+    name = args.workload if args.workload in DECODE_WORKLOADS else "decode_gqa_128k"
+    cfg = DECODE_WORKLOADS[name]
+    B, S, Lq, Hq, Hkv, D = (cfg[x] for x in ("B", "S", "Lq", "Hq", "Hkv", "D"))
+    q = si.randn_bf16((B, Lq, Hq, D), cfg["seed"], 0)
+    k = si.randn_bf16((B, S, Hkv, D), cfg["seed"], 1)
+    v = si.randn_bf16((B, S, Hkv, D), cfg["seed"], 2)
+    print("# inputs generated", file=sys.stderr, flush=True)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    split = args.split_keys or usp.default_split_keys(B, S, Hkv)
+    n = (S + split - 1) // split
+    op = torch.empty((n, B, Lq, Hq, D), dtype=torch.float32, device="cuda")
+    lp = torch.empty((n, B, Hq, Lq), dtype=torch.float32, device="cuda")
+    out = torch.empty((B, Lq, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device="cuda")
+
+    def step():
+        usp.decode_split_fwd(qd, kd, vd, split_keys=split, out_part=op, lse_part=lp)
+        usp.decode_merge(op, lp, out=out, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    usp.timing_reset()
+    usp.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    usp.timing_enable(False)
+    ms_step = elapsed * 1e3 / args.steps
+    split_ms, split_n = usp.timing_read("decode")
+    merge_ms, _ = usp.timing_read("decode_merge")
+    usp.timing_reset()
+    split_ms /= args.steps
+    merge_ms /= args.steps
+    kv_bytes = 2 * B * S * Hkv * D * 2
+    part_bytes = n * B * Lq * Hq * (D + 1) * 4
+    split_bytes = kv_bytes + B * Lq * Hq * D * 2 + part_bytes          # read K, V, q; write partials
+    step_bytes = split_bytes + part_bytes + B * Lq * Hq * (D + 1) * 4   # + merge reads partials, writes out / lse
+    achieved = split_bytes / (split_ms * 1e-3) / 1e9
+    rec = {
+        "metric": "decode HBM GB/s (K/V cache read once per step, % of HBM peak)",
+        "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "pass": "decode", "B": B, "S_cache": S, "Lq": Lq, "Hq": Hq, "Hkv": Hkv, "D": D,
+                   "split_keys": split, "pieces": n, "algorithmic_bytes_per_step": step_bytes},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "kernel": "decode_split_kernel<%d>" % D,
+            "launches_per_step": split_n // max(1, args.steps),
+            "kernel_ms_per_step": round(split_ms, 4),
+        },
+        "merge_ms_per_step": round(merge_ms, 4),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_decode(cfg, q, k, v, args.cpu_budget)
     print(json.dumps(rec), flush=True)
 
 

@@ -218,7 +218,10 @@ usp_status usp_block_attn_bwd(const void* q, const void* k, const void* v, const
  *   piece with no visible key).  Reads every valid K / V byte once.
  * usp_decode_merge combines the n partials of every (row, query, head):
  *   groups of threads fold interleaved pieces, then pairwise rounds combine
- *   the groups; out [B,Lq,Hq,D] (out_dt) and lse [B,Hq,Lq] f32. */
+ *   the groups; out [B,Lq,Hq,D] (out_dt) and lse [B,Hq,Lq] f32.  With more
+ *   than 64 pieces a first pass folds chunks of 64 pieces into each chunk's
+ *   first piece, so out_part / lse_part are scratch: their contents are
+ *   undefined after the call. */
 usp_status usp_decode_split_fwd(const void* q, const void* k, const void* v,
                                 const int32_t* kv_lens_dev, const int32_t* kv_lens_host,
                                 float* out_part, float* lse_part,
@@ -226,7 +229,7 @@ usp_status usp_decode_split_fwd(const void* q, const void* k, const void* v,
                                 int64_t split_keys, float softmax_scale, int window, int n_sink,
                                 void* stream);
 
-usp_status usp_decode_merge(const float* out_part, const float* lse_part, int64_t n_split,
+usp_status usp_decode_merge(float* out_part, float* lse_part, int64_t n_split,
                             int64_t B, int64_t Lq, int64_t Hq, int64_t D,
                             void* out, usp_dtype out_dt, float* lse, void* stream);
 

@@ -57,6 +57,7 @@ CASES = [
     (2, 2048, 4, 8, 1, 128, [2048, 1500], 256, 0, 0),     # 32 queries per KV head
     (1, 96, 1, 2, 2, 64, None, 32, 40, 2),
     (2, 700, 3, 6, 2, 128, [700, 3], 96, 0, 0),           # pieces beyond a short row
+    (1, 9000, 1, 8, 2, 64, None, 32, 0, 0),               # 282 pieces: two merge passes, ragged last chunk
 ]
 
 
@@ -75,7 +76,7 @@ def test_decode_split_and_merge(case):
     for i in range(op.shape[0]):
         _check(op[i], lp[i], Op_ref[i], Lp_ref[i], f"piece {i}")
     O_ref, L_ref = decode_ref(q, k, v, lens, softmax_scale=scale, window=window, n_sink=n_sink)
-    out, lse = usp.decode_merge(op, lp)
+    out, lse = usp.decode_merge(op.clone(), lp.clone())
     _check(out, lse, O_ref, L_ref, "merged")
     outb, lseb = usp.decode_fwd(q.cuda(), k.cuda(), v.cuda(), kv_lens=lens, split_keys=split, window=window,
                                 n_sink=n_sink, out_dtype=torch.bfloat16)

@@ -263,13 +263,22 @@ def block_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torc
     return dq, dk, dv
 
 
-def decode_split_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, kv_lens=None, split_keys: int = 256,
+def default_split_keys(B: int, S: int, Hkv: int) -> int:
+    """Keys per cache piece: up to 1024 (longer streams per wave, fewer partials), but small enough that
+    the split kernel runs at least ~1024 waves (one per SIMD of the 256 CUs), since one wave handles one
+    (piece, batch row, KV head)."""
+    return max(32, min(1024, (S * B * Hkv // 1024) // 32 * 32))
+
+
+def decode_split_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, kv_lens=None, split_keys: Optional[int] = None,
                      window: int = 0, n_sink: int = 0, softmax_scale: float = 0.0, out_part=None, lse_part=None,
                      stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Partials of the cache pieces (usp_decode_split_fwd): q [B,Lq,Hq,D], cache k / v [B,S,Hkv,D] bf16.
     Returns (out_part [n,B,Lq,Hq,D], lse_part [n,B,Hq,Lq]) f32."""
     B, Lq, Hq, D = q.shape
     S, Hkv = k.shape[1], k.shape[2]
+    if split_keys is None:
+        split_keys = default_split_keys(B, S, Hkv)
     n = (S + split_keys - 1) // split_keys
     if out_part is None:
         out_part = torch.empty((n, B, Lq, Hq, D), dtype=torch.float32, device=q.device)
@@ -292,7 +301,8 @@ def decode_split_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, kv_le
 
 def decode_merge(out_part: torch.Tensor, lse_part: torch.Tensor, *, out_dtype=torch.float32, out=None, lse=None,
                  stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Combines the piece partials (usp_decode_merge): out [B,Lq,Hq,D], lse [B,Hq,Lq]."""
+    """Combines the piece partials (usp_decode_merge): out [B,Lq,Hq,D], lse [B,Hq,Lq].  out_part and
+    lse_part are scratch (overwritten when there are more than 64 pieces)."""
     n, B, Lq, Hq, D = out_part.shape
     if out is None:
         out = torch.empty((B, Lq, Hq, D), dtype=out_dtype, device=out_part.device)

@@ -579,7 +579,7 @@ usp_status usp_decode_split_fwd(const void* q, const void* k, const void* v, con
   return launch_decode_split(p, (int)D, as_stream(stream));
 }
 
-usp_status usp_decode_merge(const float* out_part, const float* lse_part, int64_t n_split, int64_t B, int64_t Lq,
+usp_status usp_decode_merge(float* out_part, float* lse_part, int64_t n_split, int64_t B, int64_t Lq,
                             int64_t Hq, int64_t D, void* out, usp_dtype out_dt, float* lse, void* stream) {
   USP_CHECK(out_part && lse_part && out && lse, USP_ERR_INVALID_ARG, "null tensor pointer");
   USP_CHECK(n_split >= 1 && n_split <= kMaxI32 && B >= 1 && Lq >= 1 && Hq >= 1, USP_ERR_INVALID_ARG, "bad sizes");

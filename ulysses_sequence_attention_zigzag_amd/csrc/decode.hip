@@ -13,7 +13,8 @@
 //   cache is read once per decode step.
 // decode_merge_kernel: per (batch row, query, head), the piece partials are
 //   folded by groups of threads (pieces g, g + G, ...) and the G group
-//   results combined pairwise in log2(G) rounds.
+//   results combined pairwise in log2(G) rounds; many pieces go through a
+//   first pass over chunks of 64 pieces (in place) and a final pass.
 
 #include "mfma_common.h"
 
@@ -195,18 +196,22 @@ __device__ __forceinline__ void merge_into(float4& o, float& l, const float4& ob
   l = L;
 }
 
-// One workgroup per (batch row, query, head); TPR = D/4 threads hold one
-// float4 of a row, G = 256 / TPR groups fold pieces g, g + G, ... and the G
-// results are combined pairwise in log2(G) rounds through LDS.
-template <int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(const float* out_part, const float* lse_part,
-                                                           int32_t n_split, int32_t B, int32_t Lq, int32_t Hq,
-                                                           void* out, int32_t out_f32, float* lse) {
+// One workgroup per (batch row, query, head) and chunk of pieces: pieces
+// first + stride * i for i < count.  TPR = D/4 threads hold one float4 of a
+// row; G = 256 / TPR groups fold pieces g, g + G, ... and the G results are
+// combined pairwise in log2(G) rounds through LDS.  FINAL writes out / lse;
+// otherwise the result replaces the chunk's first piece (only this
+// workgroup reads that slot, and it has read its pieces before it writes).
+template <int D, bool FINAL>
+__global__ __launch_bounds__(256) void decode_merge_kernel(float* out_part, float* lse_part, int32_t n_split,
+                                                           int32_t chunk, int32_t stride, int32_t B, int32_t Lq,
+                                                           int32_t Hq, void* out, int32_t out_f32, float* lse) {
   constexpr int TPR = D / 4;
   constexpr int G = 256 / TPR;
   __shared__ float4 so[256];
   __shared__ float sl[G];
   const int row = blockIdx.x;  // (b * Lq + t) * Hq + h
+  const int first = blockIdx.y * chunk * stride;
   const int h = row % Hq;
   const int bt = row / Hq;
   const int t = bt % Lq;
@@ -220,9 +225,11 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* out_part
 
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   float l = -INFINITY;
-  for (int i = g; i < n_split; i += G) {
-    const float li = lse_part[i * piece_l + lidx];
-    const float4 oi = *reinterpret_cast<const float4*>(out_part + i * piece_o + (int64_t)row * D + 4 * j);
+  for (int i = g; i < chunk; i += G) {
+    const int64_t piece = first + (int64_t)i * stride;
+    if (piece >= n_split) break;
+    const float li = lse_part[piece * piece_l + lidx];
+    const float4 oi = *reinterpret_cast<const float4*>(out_part + piece * piece_o + (int64_t)row * D + 4 * j);
     merge_into(o, l, oi, li);
   }
   so[tid] = o;
@@ -250,15 +257,20 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* out_part
   if (g != 0) return;
   const float4 r = so[j];
   const float lt = sl[0];
-  if (out_f32) {
-    *reinterpret_cast<float4*>(static_cast<float*>(out) + (int64_t)row * D + 4 * j) = r;
+  if constexpr (FINAL) {
+    if (out_f32) {
+      *reinterpret_cast<float4*>(static_cast<float*>(out) + (int64_t)row * D + 4 * j) = r;
+    } else {
+      const bf16x2 a = __builtin_convertvector((f32x2){r.x, r.y}, bf16x2);
+      const bf16x2 c2 = __builtin_convertvector((f32x2){r.z, r.w}, bf16x2);
+      bf16x4 v4 = {a[0], a[1], c2[0], c2[1]};
+      *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(out) + (int64_t)row * D + 4 * j) = v4;
+    }
+    if (j == 0) lse[lidx] = lt;
   } else {
-    const bf16x2 a = __builtin_convertvector((f32x2){r.x, r.y}, bf16x2);
-    const bf16x2 c2 = __builtin_convertvector((f32x2){r.z, r.w}, bf16x2);
-    bf16x4 v4 = {a[0], a[1], c2[0], c2[1]};
-    *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(out) + (int64_t)row * D + 4 * j) = v4;
+    *reinterpret_cast<float4*>(out_part + (int64_t)first * piece_o + (int64_t)row * D + 4 * j) = r;
+    if (j == 0) lse_part[(int64_t)first * piece_l + lidx] = lt;
   }
-  if (j == 0) lse[lidx] = lt;
 }
 
 }  // namespace
@@ -278,18 +290,34 @@ usp_status launch_decode_split(const DecodeParams& p, int D, hipStream_t stream)
   return USP_OK;
 }
 
-usp_status launch_decode_merge(const float* out_part, const float* lse_part, int32_t n_split, int32_t B, int32_t Lq,
-                               int32_t Hq, int D, void* out, int out_f32, float* lse, hipStream_t stream) {
+usp_status launch_decode_merge(float* out_part, float* lse_part, int32_t n_split, int32_t B, int32_t Lq, int32_t Hq,
+                               int D, void* out, int out_f32, float* lse, hipStream_t stream) {
   const unsigned rows = (unsigned)((int64_t)B * Lq * Hq);
   if (rows == 0) return USP_OK;
+  // above kMergeChunk pieces, a first pass folds chunks of kMergeChunk pieces
+  // in place (rows x chunks workgroups), then the final pass merges the
+  // chunk results (stride kMergeChunk)
+  constexpr int kMergeChunk = 64;
   {
     TimingScope ts(K_DECODE_MERGE, stream);
+    int32_t count = n_split, stride = 1;
+    if (n_split > kMergeChunk) {
+      const unsigned chunks = (unsigned)((n_split + kMergeChunk - 1) / kMergeChunk);
+      if (D == 128)
+        hipLaunchKernelGGL((decode_merge_kernel<128, false>), dim3(rows, chunks), dim3(256), 0, stream, out_part,
+                           lse_part, n_split, kMergeChunk, 1, B, Lq, Hq, nullptr, 0, nullptr);
+      else
+        hipLaunchKernelGGL((decode_merge_kernel<64, false>), dim3(rows, chunks), dim3(256), 0, stream, out_part,
+                           lse_part, n_split, kMergeChunk, 1, B, Lq, Hq, nullptr, 0, nullptr);
+      count = (int32_t)chunks;
+      stride = kMergeChunk;
+    }
     if (D == 128)
-      hipLaunchKernelGGL((decode_merge_kernel<128>), dim3(rows), dim3(256), 0, stream, out_part, lse_part, n_split, B,
-                         Lq, Hq, out, out_f32, lse);
+      hipLaunchKernelGGL((decode_merge_kernel<128, true>), dim3(rows, 1), dim3(256), 0, stream, out_part, lse_part,
+                         n_split, count, stride, B, Lq, Hq, out, out_f32, lse);
     else
-      hipLaunchKernelGGL((decode_merge_kernel<64>), dim3(rows), dim3(256), 0, stream, out_part, lse_part, n_split, B,
-                         Lq, Hq, out, out_f32, lse);
+      hipLaunchKernelGGL((decode_merge_kernel<64, true>), dim3(rows, 1), dim3(256), 0, stream, out_part, lse_part,
+                         n_split, count, stride, B, Lq, Hq, out, out_f32, lse);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {

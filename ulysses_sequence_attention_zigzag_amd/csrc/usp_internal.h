@@ -223,7 +223,7 @@ struct DecodeParams {
   float scale_log2;        // softmax_scale * log2(e)
 };
 usp_status launch_decode_split(const DecodeParams& p, int D, hipStream_t stream);
-usp_status launch_decode_merge(const float* out_part, const float* lse_part, int32_t n_split, int32_t B, int32_t Lq,
+usp_status launch_decode_merge(float* out_part, float* lse_part, int32_t n_split, int32_t B, int32_t Lq,
                                int32_t Hq, int D, void* out, int out_f32, float* lse, hipStream_t stream);
 usp_status launch_bwd_delta(const void* out, int out_f32, const uint16_t* dout, float* delta, int64_t B,
                             int64_t L, int64_t H, int64_t D, hipStream_t stream);

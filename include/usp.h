@@ -255,8 +255,10 @@ usp_status usp_lse_merge(float* out_acc, float* lse_acc, const float* out_part, 
  *
  * Inputs q [B,S,Hq,D], k/v [B,S,Hkv,D] bf16 hold the whole sequence, in
  * natural order (input_order 0; permuted on the device first) or already
- * rank-major (input_order 1).  Varlen (cu_seqlens set) requires BASIC and
- * B = 1.
+ * rank-major (input_order 1).  Varlen (cu_seqlens set) requires B = 1;
+ * the ring layout (basic, zigzag or stripe) then applies to the packed token
+ * axis, as the basic layout's contiguous split does [SWA varlen example],
+ * with every mask taken from global positions and cu_seqlens.
  * Outputs:
  *   rank == -1: every rank; out [B,S,Hq,D] (out_dtype) and lse [B,Hq,S] in
  *     the input's order (ud must be 1: the head split does not change the

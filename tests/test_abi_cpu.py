@@ -114,8 +114,8 @@ def test_block_attn_validation():
     assert st == 1 and "Lq == Lk" in msg
     cu = torch.tensor([0, 100, 512], dtype=torch.int32)
     st, msg = _attn(mask=usp.MASK["positional"], qmap=ctypes.byref(qm), kmap=ctypes.byref(km), Lq=128, Lk=128,
-                    cud=FAKE, cuh=ctypes.c_void_p(cu.data_ptr()), nseq=2, causal=1)
-    assert st == 2 and "basic" in msg
+                    cud=FAKE, cuh=ctypes.c_void_p(cu.data_ptr()), nseq=2, causal=1, B=2)
+    assert st == 1 and "B == 1" in msg
     qb = usp.posmap("basic", 4, 0, 512)
     kb = usp.posmap("basic", 4, 1, 512)
     bad = torch.tensor([0, 300, 200], dtype=torch.int32)
@@ -177,11 +177,15 @@ def test_ring_validation_and_workspace():
     # pre-permuted f32 output of basic layout accumulates in place: no workspace
     a = _ring_args(impl=0, input_order=1, out_dtype=1)
     assert L.usp_ring_fwd_workspace_size(ctypes.byref(a)) == 0
-    # varlen only with the basic layout
-    cu = torch.tensor([0, 500, 1024], dtype=torch.int32)
+    # varlen: cu_seqlens must end at S (and B must be 1)
+    cu = torch.tensor([0, 500, 1000], dtype=torch.int32)
     a = _ring_args(cu_seqlens_dev=0x10000, cu_seqlens_host=cu.data_ptr(), nseq=2)
     st, msg = _status(L.usp_ring_fwd, ctypes.byref(a), None, 0, None)
-    assert st == 2 and "basic" in msg
+    assert st == 1 and "cu_seqlens" in msg
+    cu = torch.tensor([0, 500, 1024], dtype=torch.int32)
+    a = _ring_args(cu_seqlens_dev=0x10000, cu_seqlens_host=cu.data_ptr(), nseq=2, B=2)
+    st, msg = _status(L.usp_ring_fwd, ctypes.byref(a), None, 0, None)
+    assert st == 1 and "B == 1" in msg
 
 
 # ---------------------------------------------------------------- planner
@@ -230,6 +234,9 @@ CASES = [
     ("basic", 3000, 3, 1, False, 130, 7, [0, 100, 1234, 3000]),
     ("zigzag", 1200, 3, 1, False, 0, 0, None),
     ("zigzag", 3072, 4, 1, False, 300, 2, None),
+    ("zigzag", 4096, 4, 1, True, 0, 0, [0, 1, 700, 701, 2900, 4096]),      # varlen, packed-axis layout
+    ("stripe", 3072, 4, 3, False, 200, 3, [0, 1000, 1100, 3072]),
+    ("stripe", 2048, 8, 1, True, 0, 0, [0, 333, 2048]),
 ]
 
 

@@ -119,6 +119,9 @@ CASES = [
     ("basic", 3000, 3, 1, False, 130, 7, [0, 100, 1234, 3000]),
     ("zigzag", 1200, 3, 1, False, 0, 0, None),
     ("zigzag", 3072, 4, 1, False, 300, 2, None),
+    ("zigzag", 4096, 4, 1, True, 0, 0, [0, 1, 700, 701, 2900, 4096]),      # varlen, packed-axis layout
+    ("stripe", 3072, 4, 3, False, 200, 3, [0, 1000, 1100, 3072]),
+    ("stripe", 2048, 8, 1, True, 0, 0, [0, 333, 2048]),
     ("basic", 2048, 2, 1, False, 64, 200, [0, 150, 1100, 2048]),   # sink runs wider than a tile
 ]
 

@@ -198,6 +198,8 @@ RING = [
     ("stripe", 2048, 4, 1, True, 0, 0, None, 4, 1, 128),
     ("stripe", 1536, 4, 3, True, 0, 0, None, 2, 2, 64),
     ("basic", 2048, 4, 1, False, 250, 4, [0, 128, 1000, 2048], 2, 2, 128),
+    ("zigzag", 2048, 4, 1, True, 0, 0, [0, 128, 1000, 2048], 2, 1, 128),
+    ("stripe", 1536, 4, 3, False, 200, 3, [0, 700, 1536], 2, 2, 64),
 ]
 
 
@@ -277,6 +279,10 @@ RING_BWD = [
     si.WORKLOADS["stripe_mqa"].scaled(S=8192, Hq=4, Hkv=1, rank=7),
     si.WORKLOADS["stripe_mqa"].scaled(S=4096, Hq=2, Hkv=1, stripe_block=4, ring_degree=4, rank=-1),
     si.WORKLOADS["zigzag_causal_small"].scaled(rank=-1, ring_degree=3, S=1200, Hq=2, Hkv=1, D=128),
+    si.WORKLOADS["varlen_streaming"].scaled(S=2048, Hq=4, Hkv=2, window=250, cu_seqlens=[0, 128, 1000, 2048],
+                                            impl="zigzag"),
+    si.WORKLOADS["varlen_streaming"].scaled(S=2048, Hq=4, Hkv=1, window=0, n_sink=0, causal=True,
+                                            cu_seqlens=[0, 700, 701, 2048], impl="stripe", stripe_block=4),
 ]
 
 

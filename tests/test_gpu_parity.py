@@ -269,6 +269,11 @@ SMALL_RING = [
     si.WORKLOADS["stripe_mqa"].scaled(S=8192, Hq=4, Hkv=1, rank=7),
     si.WORKLOADS["stripe_mqa"].scaled(S=4096, Hq=2, Hkv=1, stripe_block=4, ring_degree=4, rank=-1),
     si.WORKLOADS["zigzag_causal_small"].scaled(rank=-1, ring_degree=3, S=1200, Hq=2, Hkv=1, D=128),
+    # varlen with the zigzag / stripe layouts over the packed token axis
+    si.WORKLOADS["varlen_streaming"].scaled(S=2048, Hq=4, Hkv=2, window=250, cu_seqlens=[0, 128, 1000, 2048],
+                                            impl="zigzag"),
+    si.WORKLOADS["varlen_streaming"].scaled(S=2048, Hq=4, Hkv=1, window=0, n_sink=0, causal=True,
+                                            cu_seqlens=[0, 700, 701, 2048], impl="stripe", stripe_block=4),
 ]
 
 

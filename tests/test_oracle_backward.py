@@ -122,6 +122,17 @@ def test_ring_decomposition_varlen():
         assert torch.allclose(a, r, atol=1e-12, rtol=1e-12)
 
 
+@pytest.mark.parametrize("impl,N,b", [("zigzag", 4, 1), ("stripe", 2, 3)])
+def test_ring_decomposition_varlen_any_layout(impl, N, b):
+    S, H, D = 48, 2, 4
+    cu = [0, 9, 25, 48]
+    q, k, v, do = (_rand(S, H, D, seed=s) for s in (35, 36, 37, 38))
+    full = attention_bwd_ref(q, k, v, do, causal=True, cu_seqlens=cu)[:3]
+    ring = ring_backward_ref(q, k, v, do, impl=impl, N=N, stripe_block=b, causal=True, cu_seqlens=cu)
+    for a, r in zip(full, ring):
+        assert torch.allclose(a, r, atol=1e-12, rtol=1e-12)
+
+
 def test_zero_upstream_gradient():
     q, k, v = (_rand(1, 10, 2, 4, seed=s) for s in (41, 42, 43))
     grads = attention_bwd_ref(q, k, v, torch.zeros(1, 10, 2, 4, dtype=torch.float64), causal=True)[:3]

@@ -78,6 +78,18 @@ def test_ring_varlen_equals_full():
     assert saw_empty
 
 
+@pytest.mark.parametrize("impl,N,b", [("zigzag", 4, 1), ("zigzag", 2, 1), ("stripe", 4, 1), ("stripe", 2, 3)])
+@pytest.mark.parametrize("kw", [dict(causal=True), dict(window=6, n_sink=2), dict()])
+def test_ring_varlen_any_layout_equals_full(impl, N, b, kw):
+    # the ring layout applied to the packed token axis, masks from global positions
+    cu = [0, 5, 19, 20, 48]
+    q, k, v = _inputs(1, 48, 4, 2, 8, seed=32)
+    O, L = attention_ref(q[0], k[0], v[0], cu_seqlens=cu, **kw)
+    Or, Lr = ring_forward_ref(q[0], k[0], v[0], impl=impl, N=N, stripe_block=b, cu_seqlens=cu, **kw)
+    _close(O, Or)
+    _close(L, Lr)
+
+
 def test_ring_one_host_is_plain_attention():
     q, k, v = _inputs(1, 12, 2, 2, 8, seed=37)
     O, L = attention_ref(q, k, v, causal=True)

@@ -201,8 +201,6 @@ usp_status setup_block_mask(int64_t Lq, int64_t Lk, usp_mask_class mask, const u
       s.ms.S = (int32_t)qmap->S_global;
       if (cu_host) {
         USP_CHECK(B == 1, USP_ERR_INVALID_ARG, "varlen (cu_seqlens) needs B == 1");
-        USP_CHECK(qmap->impl == USP_RING_BASIC, USP_ERR_UNSUPPORTED,
-                  "varlen is supported with the basic layout only");
         st = check_cu(cu_host, nseq, qmap->S_global);
         if (st != USP_OK) return st;
         s.ms.nseq = nseq;
@@ -630,7 +628,6 @@ usp_status check_ring_args(const usp_ring_args* a) {
   USP_CHECK((a->cu_seqlens_host == nullptr) == (a->cu_seqlens_dev == nullptr), USP_ERR_INVALID_ARG,
             "cu_seqlens must be given on both host and device, or neither");
   if (a->cu_seqlens_host) {
-    USP_CHECK(a->impl == USP_RING_BASIC, USP_ERR_UNSUPPORTED, "varlen is supported with the basic layout only");
     USP_CHECK(a->B == 1, USP_ERR_INVALID_ARG, "varlen needs B == 1");
     st = check_cu(a->cu_seqlens_host, a->nseq, a->S);
     if (st != USP_OK) return st;

@@ -266,7 +266,12 @@ usp_status usp_lse_merge(float* out_acc, float* lse_acc, const float* out_part, 
  *   rank >= 0 : ring rank `rank`'s share for Ulysses rank `ulysses_rank`:
  *     out [B,L,Hq/ud,D] and lse [B,Hq/ud,L] in that rank's local row order.
  * merge_mode 0 merges in the attention kernel's epilogue; 1 writes each
- * step's partial to the workspace and runs usp_lse_merge. */
+ * step's partial to the workspace and runs usp_lse_merge.
+ * qkv_packed = 1 takes q, k, v from one packed [B,S,3,H,D] tensor (varlen
+ * [T,3,H,D]) in the same order convention, as [YC]'s QKV-packed attention
+ * (multi-head only: [YC] "Some Conclusions" 2); the slices are copied into
+ * the workspace while they are put in ring order.  With usp_ring_bwd the
+ * gradients are still returned as separate dq, dk, dv. */
 typedef struct usp_ring_args {
   const void* q;
   const void* k;
@@ -285,6 +290,10 @@ typedef struct usp_ring_args {
   int32_t input_order;               /* 0 natural, 1 rank-major            */
   int32_t out_dtype;                 /* usp_dtype                          */
   int32_t merge_mode;                /* 0 fused epilogue, 1 separate merge */
+  int32_t qkv_packed;                /* 1: q points to a packed [B,S,3,H,D]
+                                        tensor (q, k, v of a token stored
+                                        one after the other; Hq == Hkv == H;
+                                        k and v are ignored)               */
 } usp_ring_args;
 
 /* Bytes of device workspace usp_ring_fwd needs for these arguments. */

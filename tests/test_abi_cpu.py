@@ -177,6 +177,18 @@ def test_ring_validation_and_workspace():
     # pre-permuted f32 output of basic layout accumulates in place: no workspace
     a = _ring_args(impl=0, input_order=1, out_dtype=1)
     assert L.usp_ring_fwd_workspace_size(ctypes.byref(a)) == 0
+    # packed qkv: multi-head only; the copies of q, k, v always take workspace
+    a = _ring_args(qkv_packed=1)
+    st, msg = _status(L.usp_ring_fwd, ctypes.byref(a), None, 0, None)
+    assert st == 1 and "Hq == Hkv" in msg
+    a = _ring_args(qkv_packed=2)
+    st, msg = _status(L.usp_ring_fwd, ctypes.byref(a), None, 0, None)
+    assert st == 1 and "qkv_packed" in msg
+    a = _ring_args(qkv_packed=1, Hkv=8, k=None, v=None, impl=0, input_order=1, out_dtype=1)
+    need = L.usp_ring_fwd_workspace_size(ctypes.byref(a))
+    assert need >= 3 * 1024 * 8 * 128 * 2
+    st, msg = _status(L.usp_ring_fwd, ctypes.byref(a), None, 0, None)
+    assert st == 3 and "workspace" in msg
     # varlen: cu_seqlens must end at S (and B must be 1)
     cu = torch.tensor([0, 500, 1000], dtype=torch.int32)
     a = _ring_args(cu_seqlens_dev=0x10000, cu_seqlens_host=cu.data_ptr(), nseq=2)

@@ -352,3 +352,25 @@ def test_ring_fwd_then_bwd_end_to_end(w):
     torch.cuda.synchronize()
     for g, r, name in zip(got, ref, ("dq", "dk", "dv")):
         assert_grad(g, r, name)
+
+
+@pytest.mark.parametrize("w", [RING_BWD[0], RING_BWD[2], si.WORKLOADS["usp_zigzag_gqa"].scaled(S=4096, Hq=4, Hkv=4,
+                                                                                           rank=1, ulysses_rank=1)],
+                         ids=lambda w: f"{w.name}-S{w.S}-r{w.rank}")
+def test_ring_bwd_packed_qkv(w):
+    """usp_ring_bwd of a packed-qkv forward (oracle forward output and LSE given)."""
+    say(f"ring_bwd packed {w.name} S={w.S} rank={w.rank}")
+    q, k, v = w.make_inputs()
+    O, LSE, dout, ref = _ring_bwd_expected(w, q, k, v)
+    qkv = torch.stack([q, k, v], dim=-3).contiguous()
+    fwd = usp.RingCall(qkv.cuda(), None, None, impl=w.impl, ring_degree=w.ring_degree,
+                       ulysses_degree=w.ulysses_degree, stripe_block=w.stripe_block, causal=w.causal,
+                       window=w.window, n_sink=w.n_sink, cu_seqlens=w.cu_seqlens,
+                       softmax_scale=w.softmax_scale or 0.0, rank=w.rank, ulysses_rank=w.ulysses_rank,
+                       qkv_packed=True)
+    fwd.out.copy_(O.float())
+    fwd.lse.copy_(LSE.float())
+    got = usp.RingBwdCall(fwd, dout.cuda()).run()
+    torch.cuda.synchronize()
+    for g, r, name in zip(got, ref, ("dq", "dk", "dv")):
+        assert_grad(g, r, name)

@@ -359,3 +359,28 @@ def test_large_workloads_full_size_sampled_rows(name, n_rows):
     O_ref, L_ref = _oracle_share(w, q, k, v, rows=rows)
     idx = torch.tensor(rows)
     assert_parity(out.cpu()[:, idx], lse.cpu()[:, :, idx], O_ref, L_ref, f"{name} sampled")
+
+
+# ---------------------------------------------------------------- packed qkv input
+PACKED = [
+    si.WORKLOADS["zigzag_causal_small"],
+    si.WORKLOADS["usp_zigzag_gqa"].scaled(S=4096, Hq=8, Hkv=8),
+    si.WORKLOADS["usp_zigzag_gqa"].scaled(S=4096, Hq=4, Hkv=4, rank=2, ulysses_rank=1),
+    si.WORKLOADS["varlen_streaming"].scaled(S=2048, Hq=4, Hkv=4, window=250, cu_seqlens=[0, 128, 1000, 2048]),
+]
+
+
+@pytest.mark.parametrize("w", PACKED, ids=lambda w: f"{w.name}-S{w.S}-r{w.rank}")
+def test_ring_packed_qkv(w):
+    say(f"packed qkv {w.name} S={w.S} rank={w.rank}")
+    q, k, v = w.make_inputs()
+    O_ref, L_ref = _oracle_share(w, q, k, v)
+    qkv = torch.stack([q, k, v], dim=-3).contiguous()          # [B,S,3,H,D] or [T,3,H,D]
+    call = usp.RingCall(qkv.cuda(), None, None, impl=w.impl, ring_degree=w.ring_degree,
+                        ulysses_degree=w.ulysses_degree, stripe_block=w.stripe_block, causal=w.causal,
+                        window=w.window, n_sink=w.n_sink, cu_seqlens=w.cu_seqlens,
+                        softmax_scale=w.softmax_scale or 0.0, rank=w.rank, ulysses_rank=w.ulysses_rank,
+                        qkv_packed=True)
+    out, lse = call.run()
+    torch.cuda.synchronize()
+    assert_parity(out, lse, O_ref, L_ref, "packed")

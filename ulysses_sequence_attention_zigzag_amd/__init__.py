@@ -48,7 +48,7 @@ class RingArgs(ctypes.Structure):
                 ("ulysses_degree", ctypes.c_int32), ("stripe_block", ctypes.c_int32),
                 ("rank", ctypes.c_int32), ("ulysses_rank", ctypes.c_int32),
                 ("input_order", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
-                ("merge_mode", ctypes.c_int32)]
+                ("merge_mode", ctypes.c_int32), ("qkv_packed", ctypes.c_int32)]
 
 
 class RingBwdArgs(ctypes.Structure):
@@ -335,13 +335,22 @@ class RingCall:
     """A prepared usp_ring_fwd call: arguments, outputs and workspace are
     allocated once; ``run()`` only enqueues the kernels."""
 
-    def __init__(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, impl: str, ring_degree: int,
-                 ulysses_degree: int = 1, stripe_block: int = 1, causal: bool = False, window: int = 0,
-                 n_sink: int = 0, cu_seqlens=None, softmax_scale: float = 0.0, rank: int = -1,
+    def __init__(self, q: torch.Tensor, k: Optional[torch.Tensor], v: Optional[torch.Tensor], *, impl: str,
+                 ring_degree: int, ulysses_degree: int = 1, stripe_block: int = 1, causal: bool = False,
+                 window: int = 0, n_sink: int = 0, cu_seqlens=None, softmax_scale: float = 0.0, rank: int = -1,
                  ulysses_rank: int = 0, input_order: str = "natural", out_dtype=torch.float32,
-                 merge_mode: int = 0):
+                 merge_mode: int = 0, qkv_packed: bool = False):
+        """q, k, v as [B,S,H,D] (varlen [T,H,D]); with qkv_packed, q is the packed [B,S,3,H,D] (varlen
+        [T,3,H,D]) tensor and k, v are None."""
         varlen = cu_seqlens is not None
-        if varlen:
+        if qkv_packed:
+            if varlen:
+                S, _, Hq, D = q.shape
+                B = 1
+            else:
+                B, S, _, Hq, D = q.shape
+            Hkv = Hq
+        elif varlen:
             S, Hq, D = q.shape
             B = 1
             Hkv = k.shape[1]
@@ -363,8 +372,10 @@ class RingCall:
         cu_dev, cu_host, nseq, _ = _cu(cu_seqlens, q.device)
         self._cu = (cu_dev, cu_host)
         a = RingArgs()
-        a.q, a.k, a.v = (_dev(q, torch.bfloat16, "q").value, _dev(k, torch.bfloat16, "k").value,
-                         _dev(v, torch.bfloat16, "v").value)
+        a.q = _dev(q, torch.bfloat16, "q").value
+        a.k = None if qkv_packed else _dev(k, torch.bfloat16, "k").value
+        a.v = None if qkv_packed else _dev(v, torch.bfloat16, "v").value
+        a.qkv_packed = int(bool(qkv_packed))
         a.out, a.lse = self.out.data_ptr(), self.lse.data_ptr()
         a.B, a.S, a.Hq, a.Hkv, a.D = B, S, Hq, Hkv, D
         a.softmax_scale = float(softmax_scale)
@@ -403,7 +414,7 @@ class RingBwdCall:
         a = fwd.args
         self.fwd, self.dout = fwd, dout
         dev = fwd.q.device
-        varlen = fwd.q.dim() == 3
+        varlen = fwd._cu[0] is not None
         N, ud = a.ring_degree, a.ulysses_degree
         L = a.S // N
         if a.rank < 0:

@@ -594,6 +594,7 @@ namespace {
 struct RingLayout {
   bool one;          // one rank's share
   bool need_perm;    // natural-order input with a non-basic layout
+  bool copy_in;      // q, k, v copied into the workspace (permutation or packed input)
   int64_t L, Ls;     // rows per ring rank, per Ulysses piece
   int64_t Hq_l, Hkv_l;
   int64_t q_rows;    // rows of the q buffer the kernel reads (per batch)
@@ -605,8 +606,12 @@ struct RingLayout {
 
 usp_status check_ring_args(const usp_ring_args* a) {
   USP_CHECK(a, USP_ERR_INVALID_ARG, "null args");
-  USP_CHECK(a->q && a->k && a->v && a->out && a->lse, USP_ERR_INVALID_ARG, "null tensor pointer");
+  USP_CHECK(a->qkv_packed == 0 || a->qkv_packed == 1, USP_ERR_INVALID_ARG, "qkv_packed must be 0 or 1");
+  USP_CHECK(a->q && (a->qkv_packed || (a->k && a->v)) && a->out && a->lse, USP_ERR_INVALID_ARG,
+            "null tensor pointer");
   USP_CHECK(a->B >= 1 && a->Hq >= 1 && a->Hkv >= 1, USP_ERR_INVALID_ARG, "bad sizes");
+  USP_CHECK(!a->qkv_packed || a->Hq == a->Hkv, USP_ERR_INVALID_ARG,
+            "packed qkv needs Hq == Hkv (GQA / MQA use separate q, k, v)");
   USP_CHECK(a->D == 64 || a->D == 128, USP_ERR_UNSUPPORTED, "head_dim must be 64 or 128, got %lld", (long long)a->D);
   USP_CHECK(a->Hq % a->Hkv == 0, USP_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
   usp_status st = check_layout(a->impl, a->S, a->ring_degree, a->stripe_block);
@@ -643,6 +648,7 @@ RingLayout ring_layout(const usp_ring_args* a) {
   const size_t NONE = SIZE_MAX;
   r.one = a->rank >= 0;
   r.need_perm = a->input_order == 0 && a->impl != USP_RING_BASIC;
+  r.copy_in = r.need_perm || a->qkv_packed;
   r.L = a->S / a->ring_degree;
   const int ud = a->ulysses_degree;
   r.Ls = r.L / ud;
@@ -658,7 +664,7 @@ RingLayout ring_layout(const usp_ring_args* a) {
     return o;
   };
   const size_t D = (size_t)a->D, B = (size_t)a->B, S = (size_t)a->S;
-  if (r.need_perm) {
+  if (r.copy_in) {
     r.off_qp = take(B * (size_t)r.q_rows * a->Hq * D * 2);
     r.off_kp = take(B * S * a->Hkv * D * 2);
     r.off_vp = take(B * S * a->Hkv * D * 2);
@@ -707,7 +713,39 @@ usp_status stage_ring_inputs(const usp_ring_args* a, const RingLayout& R, char* 
   const uint16_t* vsrc = static_cast<const uint16_t*>(a->v);
   int64_t q_batch_rows = S;   // rows between batches in the q buffer
   int64_t q_row_off = 0;      // first row of the rank's q rows
-  if (R.need_perm) {
+  if (a->qkv_packed) {
+    // rows of the packed [B,S,3,H,D] tensor hold q, k, v one after the other:
+    // copy each slice out (and into rank-major order when the input is
+    // natural-order with a non-basic layout; the rank's rows only for q in
+    // one-rank mode)
+    const int64_t H = a->Hq, slice = H * D * 2;
+    const char* base = static_cast<const char*>(a->q);
+    auto spec = [&](bool extract) {
+      GatherSpec gs{};
+      gs.impl = R.need_perm ? a->impl : USP_RING_BASIC;
+      gs.N = N;
+      gs.ud = 1;
+      gs.b = R.need_perm ? b : 1;
+      gs.g = extract ? a->rank : 0;
+      gs.L = (int32_t)L;
+      gs.S = (int32_t)S;
+      gs.kind = extract ? G_EXTRACT : G_PERMUTE;
+      return gs;
+    };
+    uint16_t* qp = reinterpret_cast<uint16_t*>(ws + R.off_qp);
+    uint16_t* kp = reinterpret_cast<uint16_t*>(ws + R.off_kp);
+    uint16_t* vp = reinterpret_cast<uint16_t*>(ws + R.off_vp);
+    st = launch_permute_strided(base + slice, kp, B, S, S, slice, 3 * slice, slice, spec(false), stream);
+    if (st == USP_OK)
+      st = launch_permute_strided(base + 2 * slice, vp, B, S, S, slice, 3 * slice, slice, spec(false), stream);
+    if (st == USP_OK)
+      st = launch_permute_strided(base, qp, B, S, R.q_rows, slice, 3 * slice, slice, spec(R.one), stream);
+    if (st != USP_OK) return st;
+    qsrc = qp;
+    ksrc = kp;
+    vsrc = vp;
+    q_batch_rows = R.q_rows;
+  } else if (R.need_perm) {
     uint16_t* qp = reinterpret_cast<uint16_t*>(ws + R.off_qp);
     uint16_t* kp = reinterpret_cast<uint16_t*>(ws + R.off_kp);
     uint16_t* vp = reinterpret_cast<uint16_t*>(ws + R.off_vp);
@@ -787,7 +825,7 @@ RingBwdLayout ring_bwd_layout(const usp_ring_args* a) {
   // the staging regions, as the forward lays them out; no forward accumulators
   R.off_qp = R.off_kp = R.off_vp = R.off_ql = R.off_kl = R.off_vl = NONE;
   R.off_oacc = R.off_lacc = R.off_opart = R.off_lpart = NONE;
-  if (R.need_perm) {
+  if (R.copy_in) {
     R.off_qp = take(B * (size_t)R.q_rows * a->Hq * D * 2);
     R.off_kp = take(B * S * a->Hkv * D * 2);
     R.off_vp = take(B * S * a->Hkv * D * 2);

@@ -44,11 +44,15 @@ __device__ __forceinline__ int32_t mapped_row(const GatherSpec& gs, int32_t i) {
 // Rows are processed by groups of (1 << log_tpr) threads; each block covers
 // (256 >> log_tpr) task rows.  Gather kinds read row map(i) and write row i;
 // scatter kinds read row i and write row map(i).
+// A row is units_per_row units; consecutive rows sit in_stride / out_stride
+// units apart (equal to units_per_row for dense tensors; larger to read one
+// slice of each row of a packed tensor).
 template <int UB>
 __global__ __launch_bounds__(256) void permute_rows_kernel(const char* __restrict__ in,
                                                            char* __restrict__ out, int64_t n_task_rows,
                                                            int32_t S_task, int64_t S_in, int64_t S_out,
-                                                           int32_t units_per_row, int32_t log_tpr,
+                                                           int32_t units_per_row, int64_t in_stride,
+                                                           int64_t out_stride, int32_t log_tpr,
                                                            GatherSpec gs) {
   using U = typename UnitT<UB>::type;
   const int32_t tpr = 1 << log_tpr;
@@ -61,8 +65,8 @@ __global__ __launch_bounds__(256) void permute_rows_kernel(const char* __restric
   const bool scatter = gs.kind == G_UNPERMUTE || gs.kind == G_INSERT;
   const int64_t src_row = o * S_in + (scatter ? i : m);
   const int64_t dst_row = o * S_out + (scatter ? m : i);
-  const U* src = reinterpret_cast<const U*>(in) + src_row * units_per_row;
-  U* dst = reinterpret_cast<U*>(out) + dst_row * units_per_row;
+  const U* src = reinterpret_cast<const U*>(in) + src_row * in_stride;
+  U* dst = reinterpret_cast<U*>(out) + dst_row * out_stride;
   for (int32_t c = lane; c < units_per_row; c += tpr) dst[c] = src[c];
 }
 
@@ -146,12 +150,20 @@ usp_status check_launch(const char* what) {
 
 usp_status launch_permute(const void* in, void* out, int64_t outer, int64_t S_in, int64_t S_out,
                           int64_t row_bytes, const GatherSpec& gs, hipStream_t stream) {
+  return launch_permute_strided(in, out, outer, S_in, S_out, row_bytes, row_bytes, row_bytes, gs, stream);
+}
+
+usp_status launch_permute_strided(const void* in, void* out, int64_t outer, int64_t S_in, int64_t S_out,
+                                  int64_t row_bytes, int64_t in_row_stride, int64_t out_row_stride,
+                                  const GatherSpec& gs, hipStream_t stream) {
   const bool extract_like = gs.kind == G_EXTRACT || gs.kind == G_INSERT;
   const int64_t S_task = extract_like ? (int64_t)gs.L / gs.ud : (gs.kind == G_PERMUTE ? S_out : S_in);
   const int64_t n_rows = outer * S_task;
   if (n_rows == 0 || row_bytes == 0) return USP_OK;
-  const int ub = unit_bytes_for(row_bytes, (uintptr_t)in, (uintptr_t)out);
+  int ub = unit_bytes_for(row_bytes, (uintptr_t)in, (uintptr_t)out);
+  while (ub > 2 && ((in_row_stride | out_row_stride) % ub)) ub >>= 1;
   const int64_t upr = row_bytes / ub;
+  const int64_t in_st = in_row_stride / ub, out_st = out_row_stride / ub;
   const int ltpr = log_tpr_for(upr);
   const int64_t rows_per_block = 256 >> ltpr;
   const int64_t blocks = (n_rows + rows_per_block - 1) / rows_per_block;
@@ -160,10 +172,10 @@ usp_status launch_permute(const void* in, void* out, int64_t outer, int64_t S_in
   char* o8 = static_cast<char*>(out);
   TimingScope ts(K_PERMUTE, stream);
   switch (ub) {
-    case 16: hipLaunchKernelGGL(permute_rows_kernel<16>, grid, block, 0, stream, i8, o8, n_rows, (int32_t)S_task, S_in, S_out, (int32_t)upr, ltpr, gs); break;
-    case 8: hipLaunchKernelGGL(permute_rows_kernel<8>, grid, block, 0, stream, i8, o8, n_rows, (int32_t)S_task, S_in, S_out, (int32_t)upr, ltpr, gs); break;
-    case 4: hipLaunchKernelGGL(permute_rows_kernel<4>, grid, block, 0, stream, i8, o8, n_rows, (int32_t)S_task, S_in, S_out, (int32_t)upr, ltpr, gs); break;
-    default: hipLaunchKernelGGL(permute_rows_kernel<2>, grid, block, 0, stream, i8, o8, n_rows, (int32_t)S_task, S_in, S_out, (int32_t)upr, ltpr, gs); break;
+    case 16: hipLaunchKernelGGL(permute_rows_kernel<16>, grid, block, 0, stream, i8, o8, n_rows, (int32_t)S_task, S_in, S_out, (int32_t)upr, in_st, out_st, ltpr, gs); break;
+    case 8: hipLaunchKernelGGL(permute_rows_kernel<8>, grid, block, 0, stream, i8, o8, n_rows, (int32_t)S_task, S_in, S_out, (int32_t)upr, in_st, out_st, ltpr, gs); break;
+    case 4: hipLaunchKernelGGL(permute_rows_kernel<4>, grid, block, 0, stream, i8, o8, n_rows, (int32_t)S_task, S_in, S_out, (int32_t)upr, in_st, out_st, ltpr, gs); break;
+    default: hipLaunchKernelGGL(permute_rows_kernel<2>, grid, block, 0, stream, i8, o8, n_rows, (int32_t)S_task, S_in, S_out, (int32_t)upr, in_st, out_st, ltpr, gs); break;
   }
   return check_launch("permute");
 }

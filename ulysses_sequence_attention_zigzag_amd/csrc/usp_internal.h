@@ -243,6 +243,12 @@ struct GatherSpec {
 enum GatherKind : int32_t { G_PERMUTE = 0, G_UNPERMUTE = 1, G_EXTRACT = 2, G_INSERT = 3 };
 usp_status launch_permute(const void* in, void* out, int64_t outer, int64_t S_in, int64_t S_out,
                           int64_t row_bytes, const GatherSpec& gs, hipStream_t stream);
+// Same with row strides (bytes between consecutive rows) of the input and
+// the output: copies row_bytes of each row (a slice of a packed row when the
+// stride is larger).
+usp_status launch_permute_strided(const void* in, void* out, int64_t outer, int64_t S_in, int64_t S_out,
+                                  int64_t row_bytes, int64_t in_row_stride, int64_t out_row_stride,
+                                  const GatherSpec& gs, hipStream_t stream);
 // Same as launch_permute with fp32 -> bf16 conversion (row_elems fp32 in, bf16 out).
 usp_status launch_permute_f32_to_bf16(const float* in, uint16_t* out, int64_t outer, int64_t S_in,
                                       int64_t S_out, int64_t row_elems, const GatherSpec& gs,

@@ -68,6 +68,20 @@ def visibility(pos_q: torch.Tensor, pos_k: torch.Tensor, *, causal: bool, window
     return vis
 
 
+def apply_score_mods(s: torch.Tensor, pos_q: torch.Tensor, pos_k: torch.Tensor, *, softcap: float = 0.0,
+                     alibi_slopes: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The score modifiers of the attention call (YunChang README, "2. Usage": ``softcap`` and
+    ``alibi_slopes`` arguments, read with flash-attention's meaning): scaled scores s [H,r,K] of the
+    heads whose slopes are given ([H]) become softcap * tanh(s / softcap) when softcap > 0, then
+    minus slope_h * |p_q - p_k| on global positions."""
+    if softcap > 0:
+        s = softcap * torch.tanh(s / softcap)
+    if alibi_slopes is not None:
+        dist = (pos_q.long()[:, None] - pos_k.long()[None, :]).abs().to(torch.float64)      # [r,K]
+        s = s - alibi_slopes.to(torch.float64).view(-1, 1, 1) * dist.unsqueeze(0)
+    return s
+
+
 def _as_batched(x: torch.Tensor, varlen: bool) -> torch.Tensor:
     return x.unsqueeze(0) if varlen else x
 
@@ -78,12 +92,14 @@ def attention_ref(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
                   cu_seqlens: Optional[Sequence[int]] = None,
                   rows: Optional[Sequence[int]] = None,
                   heads: Optional[Sequence[int]] = None,
+                  softcap: float = 0.0, alibi_slopes: Optional[torch.Tensor] = None,
                   block_bytes: int = 1 << 28):
     """Masked softmax attention in float64 over natural-order tensors.
 
     q [B,S,Hq,D], k/v [B,S,Hkv,D]; with ``cu_seqlens`` q is [T,Hq,D] and k/v
     [T,Hkv,D].  ``rows`` restricts the computation to those query positions,
-    ``heads`` to those query heads (outputs keep that order).
+    ``heads`` to those query heads (outputs keep that order).  ``softcap`` and
+    ``alibi_slopes`` ([Hq]) modify the scaled scores (apply_score_mods).
 
     Returns (O, LSE) in float64: O [B,R,H',D] and LSE [B,H',R]; varlen drops B.
     """
@@ -121,6 +137,9 @@ def attention_ref(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
             k_lo, k_hi = int(cols[0]), int(cols[-1]) + 1    # invisible columns add exp(-inf)=0
             qh = qb[b, pr][:, heads_t].to(torch.float64).permute(1, 0, 2)      # [H,r,D]
             s = torch.matmul(qh, kh[:, k_lo:k_hi].transpose(1, 2)) * scale     # [H,r,K]
+            if softcap > 0 or alibi_slopes is not None:
+                s = apply_score_mods(s, pr, pos_k_all[k_lo:k_hi], softcap=softcap,
+                                     alibi_slopes=None if alibi_slopes is None else alibi_slopes[heads_t])
             s = s.masked_fill(~mask[:, k_lo:k_hi].unsqueeze(0), -math.inf)
             m = s.amax(dim=2, keepdim=True)
             has = torch.isfinite(m)

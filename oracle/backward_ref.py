@@ -29,7 +29,7 @@ from typing import Optional, Sequence, Tuple
 
 import torch
 
-from .attention_ref import visibility
+from .attention_ref import apply_score_mods, visibility
 from .index_ref import rank_positions
 from .ring_ref import ring_forward_ref
 
@@ -37,11 +37,13 @@ from .ring_ref import ring_forward_ref
 def block_attention_bwd_ref(q_loc: torch.Tensor, k_loc: torch.Tensor, v_loc: torch.Tensor,
                             dout_loc: torch.Tensor, lse_loc: torch.Tensor, delta_loc: torch.Tensor,
                             pos_q: Sequence[int], pos_k: Sequence[int], *, scale: float, causal: bool,
-                            window: int, n_sink: int, cu_seqlens: Optional[Sequence[int]] = None):
+                            window: int, n_sink: int, cu_seqlens: Optional[Sequence[int]] = None,
+                            softcap: float = 0.0, alibi_slopes: Optional[torch.Tensor] = None):
     """One ring step's gradient terms.  q_loc / dout_loc [B,Lq,Hq,D], k_loc /
     v_loc [B,Lk,Hkv,D], lse_loc / delta_loc [B,Hq,Lq] (the final LSE and delta
     of those query rows).  Returns (dq [B,Lq,Hq,D], dk [B,Lk,Hkv,D], dv) in
-    float64."""
+    float64.  With softcap the score is c * tanh(s / c), whose derivative
+    1 - tanh^2 multiplies dS; the ALiBi bias is constant in q and k."""
     B, Lq, Hq, D = q_loc.shape
     Lk, Hkv = k_loc.shape[1], k_loc.shape[2]
     group = Hq // Hkv
@@ -58,12 +60,19 @@ def block_attention_bwd_ref(q_loc: torch.Tensor, k_loc: torch.Tensor, v_loc: tor
             lse = lse_loc[b, h].double().unsqueeze(1)
             delta = delta_loc[b, h].double().unsqueeze(1)
             s = (qh @ kh.T) * scale
+            t = torch.tanh(s / softcap) if softcap > 0 else None
+            if softcap > 0 or alibi_slopes is not None:
+                s = apply_score_mods(s.unsqueeze(0), torch.tensor(list(pos_q)), torch.tensor(list(pos_k)),
+                                     softcap=softcap,
+                                     alibi_slopes=None if alibi_slopes is None else alibi_slopes[h:h + 1])[0]
             # rows with no visible key anywhere have LSE = -inf: P = 0 there
             lse_safe = torch.where(torch.isfinite(lse), lse, torch.zeros_like(lse))
             p = torch.where(mask & torch.isfinite(lse), torch.exp(s - lse_safe), torch.zeros_like(s))
             dv[b, :, g] += p.T @ doh
             dp = doh @ vh.T
             ds = p * (dp - delta)
+            if t is not None:
+                ds = ds * (1.0 - t * t)
             dq[b, :, h] = scale * (ds @ kh)
             dk[b, :, g] += scale * (ds.T @ qh)
     return dq, dk, dv
@@ -71,7 +80,8 @@ def block_attention_bwd_ref(q_loc: torch.Tensor, k_loc: torch.Tensor, v_loc: tor
 
 def attention_bwd_ref(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor, *,
                       softmax_scale: Optional[float] = None, causal: bool = False, window: int = 0,
-                      n_sink: int = 0, cu_seqlens: Optional[Sequence[int]] = None):
+                      n_sink: int = 0, cu_seqlens: Optional[Sequence[int]] = None, softcap: float = 0.0,
+                      alibi_slopes: Optional[torch.Tensor] = None):
     """Unpartitioned gradients of natural-order attention ([B,S,H,D], or varlen
     [T,H,D] with cu_seqlens).  Returns (dq, dk, dv, O, LSE) in float64."""
     varlen = cu_seqlens is not None
@@ -80,13 +90,14 @@ def attention_bwd_ref(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: t
     scale = D ** -0.5 if softmax_scale is None else float(softmax_scale)
     O, LSE = ring_forward_ref(qb[0] if varlen else qb, kb[0] if varlen else kb, vb[0] if varlen else vb,
                               impl="basic", N=1, softmax_scale=scale, causal=causal, window=window,
-                              n_sink=n_sink, cu_seqlens=cu_seqlens)
+                              n_sink=n_sink, cu_seqlens=cu_seqlens, softcap=softcap, alibi_slopes=alibi_slopes)
     Ob = O.unsqueeze(0) if varlen else O
     Lb = LSE.unsqueeze(0) if varlen else LSE
     delta = (db.double() * Ob).sum(-1).transpose(1, 2)               # [B,Hq,S]
     pos = list(range(S))
     dq, dk, dv = block_attention_bwd_ref(qb, kb, vb, db, Lb, delta, pos, pos, scale=scale, causal=causal,
-                                         window=window, n_sink=n_sink, cu_seqlens=cu_seqlens)
+                                         window=window, n_sink=n_sink, cu_seqlens=cu_seqlens, softcap=softcap,
+                                         alibi_slopes=alibi_slopes)
     if varlen:
         dq, dk, dv = dq[0], dk[0], dv[0]
     return dq, dk, dv, O, LSE
@@ -95,7 +106,8 @@ def attention_bwd_ref(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: t
 def ring_backward_ref(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor, *, impl: str,
                       N: int, stripe_block: int = 1, softmax_scale: Optional[float] = None,
                       causal: bool = False, window: int = 0, n_sink: int = 0,
-                      cu_seqlens: Optional[Sequence[int]] = None):
+                      cu_seqlens: Optional[Sequence[int]] = None, softcap: float = 0.0,
+                      alibi_slopes: Optional[torch.Tensor] = None):
     """The backward run as the ring runs the forward: host i, round s, KV piece
     j = (i - s) mod N; each step's dQ stays on host i, its dK / dV belong to
     piece j.  Natural-order (dq, dk, dv) in float64."""
@@ -105,7 +117,8 @@ def ring_backward_ref(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: t
     Hkv = kb.shape[2]
     scale = D ** -0.5 if softmax_scale is None else float(softmax_scale)
     O, LSE = ring_forward_ref(q, k, v, impl=impl, N=N, stripe_block=stripe_block, softmax_scale=scale,
-                              causal=causal, window=window, n_sink=n_sink, cu_seqlens=cu_seqlens)
+                              causal=causal, window=window, n_sink=n_sink, cu_seqlens=cu_seqlens, softcap=softcap,
+                              alibi_slopes=alibi_slopes)
     Ob = O.unsqueeze(0) if varlen else O
     Lb = LSE.unsqueeze(0) if varlen else LSE
     delta = (db.double() * Ob).sum(-1).transpose(1, 2)
@@ -119,7 +132,7 @@ def ring_backward_ref(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: t
             gq, gk, gv = block_attention_bwd_ref(qb[:, pos[i]], kb[:, pos[j]], vb[:, pos[j]], db[:, pos[i]],
                                                  Lb[:, :, pos[i]], delta[:, :, pos[i]], pos[i], pos[j],
                                                  scale=scale, causal=causal, window=window, n_sink=n_sink,
-                                                 cu_seqlens=cu_seqlens)
+                                                 cu_seqlens=cu_seqlens, softcap=softcap, alibi_slopes=alibi_slopes)
             dq[:, pos[i]] += gq
             dk[:, pos[j]] += gk
             dv[:, pos[j]] += gv

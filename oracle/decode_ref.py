@@ -30,7 +30,8 @@ def _lens(kv_lens: Optional[Sequence[int]], B: int, S: int) -> List[int]:
 
 
 def decode_ref(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_lens: Optional[Sequence[int]] = None, *,
-               softmax_scale: Optional[float] = None, window: int = 0, n_sink: int = 0):
+               softmax_scale: Optional[float] = None, window: int = 0, n_sink: int = 0, softcap: float = 0.0,
+               alibi_slopes: Optional[torch.Tensor] = None):
     """q [B,Lq,Hq,D], cache k / v [B,S,Hkv,D] (row b valid up to kv_lens[b],
     default S).  Returns (O [B,Lq,Hq,D], LSE [B,Hq,Lq]) in float64: the
     definition, one block over each row's whole cache."""
@@ -44,13 +45,15 @@ def decode_ref(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_lens: Optio
         n = lens[b]
         pos_q = [n - Lq + t for t in range(Lq)]
         o, l = block_attention_ref(q[b:b + 1], k[b:b + 1, :n], v[b:b + 1, :n], pos_q, list(range(n)),
-                                   scale=scale, causal=True, window=window, n_sink=n_sink)
+                                   scale=scale, causal=True, window=window, n_sink=n_sink, softcap=softcap,
+                                   alibi_slopes=alibi_slopes)
         O[b], LSE[b] = o[0], l[0]
     return O, LSE
 
 
 def decode_split_ref(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_lens: Optional[Sequence[int]] = None, *,
-                     split_keys: int, softmax_scale: Optional[float] = None, window: int = 0, n_sink: int = 0):
+                     split_keys: int, softmax_scale: Optional[float] = None, window: int = 0, n_sink: int = 0,
+                     softcap: float = 0.0, alibi_slopes: Optional[torch.Tensor] = None):
     """Partials of the cache pieces [i*split_keys, (i+1)*split_keys) (cut at
     each row's kv_len): (O [n,B,Lq,Hq,D], LSE [n,B,Hq,Lq]) in float64; a piece
     with no visible key has LSE = -inf and O = 0."""
@@ -69,7 +72,7 @@ def decode_split_ref(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_lens:
             pos_q = [lens[b] - Lq + t for t in range(Lq)]
             o, l = block_attention_ref(q[b:b + 1], k[b:b + 1, lo:hi], v[b:b + 1, lo:hi], pos_q,
                                        list(range(lo, hi)), scale=scale, causal=True, window=window,
-                                       n_sink=n_sink)
+                                       n_sink=n_sink, softcap=softcap, alibi_slopes=alibi_slopes)
             O[i, b], LSE[i, b] = o[0], l[0]
     return O, LSE
 

@@ -25,17 +25,19 @@ from typing import List, Optional, Sequence, Tuple
 
 import torch
 
-from .attention_ref import visibility
+from .attention_ref import apply_score_mods, visibility
 from .index_ref import rank_positions
 
 
 def block_attention_ref(q_loc: torch.Tensor, k_loc: torch.Tensor, v_loc: torch.Tensor,
                         pos_q: Sequence[int], pos_k: Sequence[int], *, scale: float,
                         causal: bool, window: int, n_sink: int,
-                        cu_seqlens: Optional[Sequence[int]] = None):
+                        cu_seqlens: Optional[Sequence[int]] = None, softcap: float = 0.0,
+                        alibi_slopes: Optional[torch.Tensor] = None):
     """One ring step: q_loc [B,Lq,Hq,D] against k_loc/v_loc [B,Lk,Hkv,D] whose
     rows sit at global positions pos_q / pos_k.  Returns the partial
-    (O [B,Lq,Hq,D], LSE [B,Hq,Lq]) in float64."""
+    (O [B,Lq,Hq,D], LSE [B,Hq,Lq]) in float64.  softcap / alibi_slopes ([Hq])
+    as in attention_ref."""
     B, Lq, Hq, D = q_loc.shape
     Hkv = k_loc.shape[2]
     group = Hq // Hkv
@@ -49,6 +51,10 @@ def block_attention_ref(q_loc: torch.Tensor, k_loc: torch.Tensor, v_loc: torch.T
             kh = k_loc[b, :, h // group].double()     # [Lk,D]
             vh = v_loc[b, :, h // group].double()
             s = (qh @ kh.T) * scale
+            if softcap > 0 or alibi_slopes is not None:
+                s = apply_score_mods(s.unsqueeze(0), torch.tensor(list(pos_q)), torch.tensor(list(pos_k)),
+                                     softcap=softcap,
+                                     alibi_slopes=None if alibi_slopes is None else alibi_slopes[h:h + 1])[0]
             s[~mask] = -math.inf
             live = mask.any(1)                        # rows with at least one visible key
             if not bool(live.any()):
@@ -81,7 +87,8 @@ def ring_forward_ref(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, impl:
                      stripe_block: int = 1, softmax_scale: Optional[float] = None,
                      causal: bool = False, window: int = 0, n_sink: int = 0,
                      cu_seqlens: Optional[Sequence[int]] = None,
-                     return_partials: bool = False):
+                     return_partials: bool = False, softcap: float = 0.0,
+                     alibi_slopes: Optional[torch.Tensor] = None):
     """Virtual ring over N hosts on natural-order q/k/v ([B,S,H,D] or varlen
     [T,H,D]).  Returns the natural-order (O, LSE) in float64 and, if asked,
     partials[i][s] = (j, O_s, LSE_s) in host i's local order."""
@@ -103,7 +110,8 @@ def ring_forward_ref(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, impl:
             j = (i - s) % N
             part = block_attention_ref(qi, kb[:, pos[j]], vb[:, pos[j]], pos[i], pos[j],
                                        scale=scale, causal=causal, window=window,
-                                       n_sink=n_sink, cu_seqlens=cu_seqlens)
+                                       n_sink=n_sink, cu_seqlens=cu_seqlens, softcap=softcap,
+                                       alibi_slopes=alibi_slopes)
             steps.append((j, part[0], part[1]))
             acc = part if acc is None else merge_ref(acc[0], acc[1], part[0], part[1])
         partials.append(steps)

@@ -149,14 +149,27 @@ usp_status usp_ulysses_relayout(void* const* shards, void* local, int64_t B, int
  * rescale of usp_lse_merge.  D must be 64 or 128.  cu_seqlens_host (nseq+1
  * int32, host) plans the tiles; cu_seqlens_dev (same values, device) is read
  * by the kernel.  The first call with a new shape/mask builds and uploads a
- * tile plan (one synchronous copy); later calls reuse it. */
+ * tile plan (one synchronous copy); later calls reuse it.
+ *
+ * Score modifiers, applied to s in this order before the mask and softmax
+ * (both off with softcap = 0 and alibi_slopes = NULL):
+ *   softcap > 0: s = softcap * tanh(s / softcap) (logit soft-capping: the
+ *     softcap argument of [YC] "2. Usage", read with flash-attention's
+ *     meaning);
+ *   alibi_slopes (device, Hq f32, one per query head of this call): s -=
+ *     slope_h * |p_q - p_k| on global positions (the alibi_slopes
+ *     argument of [YC] "2. Usage", same reading); POSITIONAL mask only.
+ * The returned LSE is that of the modified scores.  A negative or non-finite
+ * softcap is USP_ERR_INVALID_ARG; ALiBi over more than 2^22 positions
+ * (S, or the varlen token count) is USP_ERR_UNSUPPORTED. */
 usp_status usp_block_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                               int64_t B, int64_t Lq, int64_t Lk, int64_t Hq, int64_t Hkv, int64_t D,
                               float softmax_scale, usp_mask_class mask,
                               const usp_posmap* qmap, const usp_posmap* kmap,
                               int causal, int window, int n_sink,
                               const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int nseq,
-                              usp_dtype out_dt, int accumulate, void* stream);
+                              usp_dtype out_dt, int accumulate, float softcap, const float* alibi_slopes,
+                              void* stream);
 
 /* ------------------------------------------------------------- backward
  * The backward of block attention, as the ring runs it [LCA "Ring
@@ -183,7 +196,10 @@ usp_status usp_block_attn_fwd(const void* q, const void* k, const void* v, void*
  *   leaves the gradients unchanged.  dq must not alias dk or dv.  Each
  *   gradient element is written by one workgroup (deterministic, no
  *   atomics).  The first call with a new shape/mask builds and uploads its
- *   tile plans (synchronous copies); later calls reuse them. */
+ *   tile plans (synchronous copies); later calls reuse them.  softcap and
+ *   alibi_slopes are those of the forward (s above is the modified score,
+ *   and with softcap dS is multiplied by the derivative 1 - tanh^2 of the
+ *   cap before it reaches dQ and dK). */
 usp_status usp_attn_bwd_preprocess(const void* out, usp_dtype out_dt, const void* dout, float* delta,
                                    int64_t B, int64_t L, int64_t H, int64_t D, void* stream);
 
@@ -194,7 +210,7 @@ usp_status usp_block_attn_bwd(const void* q, const void* k, const void* v, const
                               const usp_posmap* qmap, const usp_posmap* kmap,
                               int causal, int window, int n_sink,
                               const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int nseq,
-                              void* stream);
+                              float softcap, const float* alibi_slopes, void* stream);
 
 /* --------------------------------------------------------------- decode
  * Decode-time attention over a KV cache, as flash decoding: the cache is cut
@@ -271,7 +287,9 @@ usp_status usp_lse_merge(float* out_acc, float* lse_acc, const float* out_part, 
  * [T,3,H,D]) in the same order convention, as [YC]'s QKV-packed attention
  * (multi-head only: [YC] "Some Conclusions" 2); the slices are copied into
  * the workspace while they are put in ring order.  With usp_ring_bwd the
- * gradients are still returned as separate dq, dk, dv. */
+ * gradients are still returned as separate dq, dk, dv.  softcap and
+ * alibi_slopes are the score modifiers of usp_block_attn_fwd, positions
+ * global. */
 typedef struct usp_ring_args {
   const void* q;
   const void* k;
@@ -294,6 +312,10 @@ typedef struct usp_ring_args {
                                         tensor (q, k, v of a token stored
                                         one after the other; Hq == Hkv == H;
                                         k and v are ignored)               */
+  float softcap;                     /* score soft-cap, 0: off             */
+  const float* alibi_slopes;         /* device, Hq f32 over ALL heads (the
+                                        Ulysses rank reads its own group),
+                                        or NULL                            */
 } usp_ring_args;
 
 /* Bytes of device workspace usp_ring_fwd needs for these arguments. */

@@ -85,12 +85,13 @@ def test_relayout_validation():
 def _attn(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE2, lse=FAKE2, B=1, Lq=64, Lk=64, Hq=4, Hkv=2, D=128, scale=0.0,
              mask=usp.MASK["causal"], qmap=None, kmap=None, causal=0, window=0, n_sink=0, cud=None, cuh=None,
-             nseq=0, dt=1, acc=0)
+             nseq=0, dt=1, acc=0, softcap=0.0, alibi=None)
     a.update(kw)
     L = usp.lib()
     return _status(L.usp_block_attn_fwd, a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Lq"], a["Lk"],
                    a["Hq"], a["Hkv"], a["D"], a["scale"], a["mask"], a["qmap"], a["kmap"], a["causal"],
-                   a["window"], a["n_sink"], a["cud"], a["cuh"], a["nseq"], a["dt"], a["acc"], None)
+                   a["window"], a["n_sink"], a["cud"], a["cuh"], a["nseq"], a["dt"], a["acc"], a["softcap"],
+                   a["alibi"], None)
 
 
 def test_block_attn_validation():
@@ -124,6 +125,18 @@ def test_block_attn_validation():
     assert st == 1 and "cu_seqlens" in msg
     st, msg = _attn(window=-1, mask=usp.MASK["positional"], qmap=ctypes.byref(qb), kmap=ctypes.byref(kb), Lq=128, Lk=128)
     assert st == 1 and "window" in msg
+    # score modifiers: softcap finite and >= 0; ALiBi needs global positions, at most 2^22 of them
+    for cap in (-1.0, float("nan"), float("inf")):
+        st, msg = _attn(softcap=cap)
+        assert st == 1 and "softcap" in msg, cap
+    st, msg = _attn(alibi=FAKE)
+    assert st == 1 and "POSITIONAL" in msg
+    S = 1 << 23
+    qb = usp.posmap("basic", 8, 0, S)
+    kb = usp.posmap("basic", 8, 1, S)
+    st, msg = _attn(mask=usp.MASK["positional"], qmap=ctypes.byref(qb), kmap=ctypes.byref(kb), Lq=S // 8,
+                    Lk=S // 8, alibi=FAKE)
+    assert st == 2 and "ALiBi" in msg
 
 
 def test_merge_validation():
@@ -157,6 +170,10 @@ def test_ring_validation_and_workspace():
         (dict(rank=4), 1, "rank"),
         (dict(merge_mode=3), 1, "merge_mode"),
         (dict(q=None), 1, "null"),
+    ]
+    cases += [
+        (dict(softcap=-2.0), 1, "softcap"),
+        (dict(S=1 << 23, alibi_slopes=0x10000), 2, "ALiBi"),
     ]
     for kw, code, word in cases:
         a = _ring_args(**kw)

@@ -30,11 +30,12 @@ def _status(fn, *args):
 def _bwd(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, do=FAKE, lse=FAKE, delta=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1, Lq=128,
              Lk=128, Hq=4, Hkv=2, D=128, scale=0.0, mask=usp.MASK["causal"], qmap=None, kmap=None, causal=0,
-             window=0, n_sink=0, cud=None, cuh=None, nseq=0)
+             window=0, n_sink=0, cud=None, cuh=None, nseq=0, softcap=0.0, alibi=None)
     a.update(kw)
     return _status(usp.lib().usp_block_attn_bwd, a["q"], a["k"], a["v"], a["do"], a["lse"], a["delta"], a["dq"],
                    a["dk"], a["dv"], a["B"], a["Lq"], a["Lk"], a["Hq"], a["Hkv"], a["D"], a["scale"], a["mask"],
-                   a["qmap"], a["kmap"], a["causal"], a["window"], a["n_sink"], a["cud"], a["cuh"], a["nseq"], None)
+                   a["qmap"], a["kmap"], a["causal"], a["window"], a["n_sink"], a["cud"], a["cuh"], a["nseq"],
+                   a["softcap"], a["alibi"], None)
 
 
 def test_block_attn_bwd_validation():
@@ -59,6 +60,11 @@ def test_block_attn_bwd_validation():
     st, msg = _bwd(mask=usp.MASK["positional"], qmap=ctypes.byref(qm), kmap=ctypes.byref(km),
                    cud=None, cuh=ctypes.c_void_p(cu.data_ptr()), nseq=2)
     assert st == 1 and "both" in msg
+    # score modifiers are checked before anything is enqueued
+    st, msg = _bwd(softcap=-0.5)
+    assert st == 1 and "softcap" in msg
+    st, msg = _bwd(alibi=FAKE)
+    assert st == 1 and "POSITIONAL" in msg
     # an EMPTY mask adds nothing and enqueues nothing
     st, msg = _bwd(mask=usp.MASK["empty"])
     assert st == 0

@@ -48,7 +48,8 @@ class RingArgs(ctypes.Structure):
                 ("ulysses_degree", ctypes.c_int32), ("stripe_block", ctypes.c_int32),
                 ("rank", ctypes.c_int32), ("ulysses_rank", ctypes.c_int32),
                 ("input_order", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
-                ("merge_mode", ctypes.c_int32), ("qkv_packed", ctypes.c_int32)]
+                ("merge_mode", ctypes.c_int32), ("qkv_packed", ctypes.c_int32),
+                ("softcap", ctypes.c_float), ("alibi_slopes", ctypes.c_void_p)]
 
 
 class RingBwdArgs(ctypes.Structure):
@@ -68,7 +69,7 @@ _SIGS = {
     "usp_ulysses_relayout": ([_P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P], _I32),
     "usp_block_attn_fwd": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, ctypes.c_float, _I32,
                             ctypes.POINTER(PosMap), ctypes.POINTER(PosMap), _I32, _I32, _I32, _P, _P, _I32,
-                            _I32, _I32, _P], _I32),
+                            _I32, _I32, ctypes.c_float, _P, _P], _I32),
     "usp_lse_merge": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P], _I32),
     "usp_ring_fwd_workspace_size": ([ctypes.POINTER(RingArgs)], ctypes.c_size_t),
     "usp_ring_fwd": ([ctypes.POINTER(RingArgs), _P, ctypes.c_size_t, _P], _I32),
@@ -84,7 +85,7 @@ _SIGS = {
     "usp_attn_bwd_preprocess": ([_P, _I32, _P, _P, _I64, _I64, _I64, _I64, _P], _I32),
     "usp_block_attn_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64,
                             ctypes.c_float, _I32, ctypes.POINTER(PosMap), ctypes.POINTER(PosMap), _I32, _I32,
-                            _I32, _P, _P, _I32, _P], _I32),
+                            _I32, _P, _P, _I32, ctypes.c_float, _P, _P], _I32),
     "usp_decode_split_fwd": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64, ctypes.c_float,
                               _I32, _I32, _P], _I32),
     "usp_decode_merge": ([_P, _P, _I64, _I64, _I64, _I64, _I64, _P, _I32, _P, _P], _I32),
@@ -184,12 +185,23 @@ def _cu(cu_seqlens, device):
     return dev, host, host.numel() - 1, (dev, host)
 
 
+def _slopes(alibi_slopes: Optional[torch.Tensor], H: int):
+    """Device pointer of an [H] f32 slope vector (None when not given)."""
+    if alibi_slopes is None:
+        return None
+    if tuple(alibi_slopes.shape) != (H,):
+        raise ValueError(f"alibi_slopes must be [{H}]")
+    return _dev(alibi_slopes, torch.float32, "alibi_slopes")
+
+
 def block_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, mask: str = "positional",
                    qmap: Optional[PosMap] = None, kmap: Optional[PosMap] = None, causal: bool = False,
                    window: int = 0, n_sink: int = 0, cu_seqlens=None, softmax_scale: float = 0.0,
                    out_dtype=torch.float32, accumulate: bool = False, out: Optional[torch.Tensor] = None,
-                   lse: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """One ring step (usp_block_attn_fwd).  q [B,Lq,Hq,D], k/v [B,Lk,Hkv,D] bf16."""
+                   lse: Optional[torch.Tensor] = None, softcap: float = 0.0,
+                   alibi_slopes: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """One ring step (usp_block_attn_fwd).  q [B,Lq,Hq,D], k/v [B,Lk,Hkv,D] bf16; alibi_slopes [Hq] f32 on
+    the device."""
     B, Lq, Hq, D = q.shape
     Lk, Hkv = k.shape[1], k.shape[2]
     if out is None:
@@ -204,7 +216,7 @@ def block_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, mask: s
         ctypes.byref(kmap) if kmap else None, int(causal), int(window), int(n_sink),
         ctypes.c_void_p(cu_dev.data_ptr()) if cu_dev is not None else None,
         ctypes.c_void_p(cu_host.data_ptr()) if cu_host is not None else None, nseq,
-        DT[out.dtype], int(accumulate), _stream(stream)))
+        DT[out.dtype], int(accumulate), float(softcap), _slopes(alibi_slopes, Hq), _stream(stream)))
     if keep is not None:
         torch.cuda.current_stream().synchronize()  # cu_seqlens copies must outlive the launch
     return out, lse
@@ -228,7 +240,8 @@ def block_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torc
                    delta: torch.Tensor, *, dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
                    dv: Optional[torch.Tensor] = None, mask: str = "positional", qmap: Optional[PosMap] = None,
                    kmap: Optional[PosMap] = None, causal: bool = False, window: int = 0, n_sink: int = 0,
-                   cu_seqlens=None, softmax_scale: float = 0.0,
+                   cu_seqlens=None, softmax_scale: float = 0.0, softcap: float = 0.0,
+                   alibi_slopes: Optional[torch.Tensor] = None,
                    stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """One ring step's gradient terms (usp_block_attn_bwd), ADDED into f32 dq [B,Lq,Hq,D] and dk, dv
     [B,Lk,Hkv,D] (zero-initialised here when not given).  q, dout [B,Lq,Hq,D], k/v [B,Lk,Hkv,D] bf16;
@@ -257,7 +270,8 @@ def block_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torc
         B, Lq, Lk, Hq, Hkv, D, float(softmax_scale), MASK[mask], ctypes.byref(qmap) if qmap else None,
         ctypes.byref(kmap) if kmap else None, int(causal), int(window), int(n_sink),
         ctypes.c_void_p(cu_dev.data_ptr()) if cu_dev is not None else None,
-        ctypes.c_void_p(cu_host.data_ptr()) if cu_host is not None else None, nseq, _stream(stream)))
+        ctypes.c_void_p(cu_host.data_ptr()) if cu_host is not None else None, nseq, float(softcap),
+        _slopes(alibi_slopes, Hq), _stream(stream)))
     if keep is not None:
         torch.cuda.current_stream().synchronize()  # cu_seqlens copies must outlive the launch
     return dq, dk, dv
@@ -339,9 +353,10 @@ class RingCall:
                  ring_degree: int, ulysses_degree: int = 1, stripe_block: int = 1, causal: bool = False,
                  window: int = 0, n_sink: int = 0, cu_seqlens=None, softmax_scale: float = 0.0, rank: int = -1,
                  ulysses_rank: int = 0, input_order: str = "natural", out_dtype=torch.float32,
-                 merge_mode: int = 0, qkv_packed: bool = False):
+                 merge_mode: int = 0, qkv_packed: bool = False, softcap: float = 0.0,
+                 alibi_slopes: Optional[torch.Tensor] = None):
         """q, k, v as [B,S,H,D] (varlen [T,H,D]); with qkv_packed, q is the packed [B,S,3,H,D] (varlen
-        [T,3,H,D]) tensor and k, v are None."""
+        [T,3,H,D]) tensor and k, v are None.  alibi_slopes: [Hq] f32 on the device, over all heads."""
         varlen = cu_seqlens is not None
         if qkv_packed:
             if varlen:
@@ -388,6 +403,10 @@ class RingCall:
         a.input_order = {"natural": 0, "permuted": 1}[input_order]
         a.out_dtype = DT[out_dtype]
         a.merge_mode = merge_mode
+        a.softcap = float(softcap)
+        sp = _slopes(alibi_slopes, Hq)
+        a.alibi_slopes = sp.value if sp is not None else None
+        self.alibi_slopes = alibi_slopes
         self.args = a
         nbytes = lib().usp_ring_fwd_workspace_size(ctypes.byref(a))
         if nbytes == 0:

@@ -227,6 +227,26 @@ void build_block_plan(const BlockMaskSetup& su, int32_t Lq, int32_t Lk, const in
   }
 }
 
+// Score modifiers in the kernels' raw-score units (ScoreMods).
+usp_status make_mods(float softcap, const float* alibi, usp_mask_class mask, int64_t S, float scale,
+                     ScoreMods* out) {
+  USP_CHECK(std::isfinite(softcap) && softcap >= 0.f, USP_ERR_INVALID_ARG, "softcap must be finite and >= 0");
+  USP_CHECK(!alibi || mask == USP_MASK_POSITIONAL, USP_ERR_INVALID_ARG,
+            "ALiBi needs the POSITIONAL mask class (global positions)");
+  USP_CHECK(!alibi || S <= kMaxAlibiPositions, USP_ERR_UNSUPPORTED,
+            "ALiBi distances are computed in f32: at most %lld positions, got %lld",
+            (long long)kMaxAlibiPositions, (long long)S);
+  ScoreMods m{};
+  if (softcap > 0.f) {
+    m.a = softcap / scale;
+    m.b2 = 2.f * scale * 1.4426950408889634f / softcap;
+  }
+  m.inv_scale = 1.f / scale;
+  m.alibi = alibi;
+  *out = m;
+  return USP_OK;
+}
+
 std::string map_key(const PosMap& m) {
   char buf[96];
   snprintf(buf, sizeof(buf), "%d.%d.%d.%d.%d.%d", m.kind, m.N, m.rank, m.b, m.L, m.offset);
@@ -391,7 +411,8 @@ usp_status usp_block_attn_fwd(const void* q, const void* k, const void* v, void*
                               float softmax_scale, usp_mask_class mask, const usp_posmap* qmap,
                               const usp_posmap* kmap, int causal, int window, int n_sink,
                               const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int nseq,
-                              usp_dtype out_dt, int accumulate, void* stream) {
+                              usp_dtype out_dt, int accumulate, float softcap, const float* alibi_slopes,
+                              void* stream) {
   USP_CHECK(q && k && v && out && lse, USP_ERR_INVALID_ARG, "null tensor pointer");
   USP_CHECK(B >= 1 && Lq >= 0 && Lk >= 0 && Hq >= 1 && Hkv >= 1, USP_ERR_INVALID_ARG, "bad sizes");
   USP_CHECK(D == 64 || D == 128, USP_ERR_UNSUPPORTED, "head_dim must be 64 or 128, got %lld", (long long)D);
@@ -408,8 +429,11 @@ usp_status usp_block_attn_fwd(const void* q, const void* k, const void* v, void*
   usp_status st = setup_block_mask(Lq, Lk, mask, qmap, kmap, causal, window, n_sink, cu_seqlens_host,
                                    nseq, B, &su);
   if (st != USP_OK) return st;
-  if (Lq == 0) return USP_OK;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)D);
+  ScoreMods mods;
+  st = make_mods(softcap, alibi_slopes, mask, su.ms.S, scale, &mods);
+  if (st != USP_OK) return st;
+  if (Lq == 0) return USP_OK;
 
   const int32_t tm = choose_tile_m(su.qmap);
   std::string key = "blk|" + std::to_string(Lq) + "|" + std::to_string(Lk) + "|" + map_key(su.qmap) + "|" +
@@ -445,6 +469,7 @@ usp_status usp_block_attn_fwd(const void* q, const void* k, const void* v, void*
   p.qmap = su.qmap;
   p.kmap = su.kmap;
   p.mask = su.ms;
+  p.mods = mods;
   return launch_attn_fwd(p, (int)D, as_stream(stream));
 }
 
@@ -465,7 +490,8 @@ usp_status usp_block_attn_bwd(const void* q, const void* k, const void* v, const
                               int64_t Lk, int64_t Hq, int64_t Hkv, int64_t D, float softmax_scale,
                               usp_mask_class mask, const usp_posmap* qmap, const usp_posmap* kmap, int causal,
                               int window, int n_sink, const int32_t* cu_seqlens_dev,
-                              const int32_t* cu_seqlens_host, int nseq, void* stream) {
+                              const int32_t* cu_seqlens_host, int nseq, float softcap,
+                              const float* alibi_slopes, void* stream) {
   USP_CHECK(q && k && v && dout && lse && delta && dq && dk && dv, USP_ERR_INVALID_ARG, "null tensor pointer");
   USP_CHECK(B >= 1 && Lq >= 0 && Lk >= 0 && Hq >= 1 && Hkv >= 1, USP_ERR_INVALID_ARG, "bad sizes");
   USP_CHECK(D == 64 || D == 128, USP_ERR_UNSUPPORTED, "head_dim must be 64 or 128, got %lld", (long long)D);
@@ -480,8 +506,11 @@ usp_status usp_block_attn_bwd(const void* q, const void* k, const void* v, const
   usp_status st = setup_block_mask(Lq, Lk, mask, qmap, kmap, causal, window, n_sink, cu_seqlens_host,
                                    nseq, B, &su);
   if (st != USP_OK) return st;
-  if (Lq == 0 || Lk == 0 || su.empty) return USP_OK;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)D);
+  ScoreMods mods;
+  st = make_mods(softcap, alibi_slopes, mask, su.ms.S, scale, &mods);
+  if (st != USP_OK) return st;
+  if (Lq == 0 || Lk == 0 || su.empty) return USP_OK;
 
   const std::string base = std::to_string(Lq) + "|" + std::to_string(Lk) + "|" + map_key(su.qmap) + "|" +
                            map_key(su.kmap) + "|" + mask_key(su.ms) + "|" +
@@ -520,6 +549,7 @@ usp_status usp_block_attn_bwd(const void* q, const void* k, const void* v, const
   p.qmap = su.qmap;
   p.kmap = su.kmap;
   p.mask = su.ms;
+  p.mods = mods;
   BwdParams pq = p, pk = p;
   pq.items = dpq.items;
   pq.runs = dpq.runs;
@@ -630,6 +660,10 @@ usp_status check_ring_args(const usp_ring_args* a) {
   USP_CHECK(a->out_dtype == USP_DT_BF16 || a->out_dtype == USP_DT_F32, USP_ERR_INVALID_ARG, "bad out dtype");
   USP_CHECK(a->merge_mode == 0 || a->merge_mode == 1, USP_ERR_INVALID_ARG, "merge_mode must be 0 or 1");
   USP_CHECK(std::isfinite(a->softmax_scale), USP_ERR_INVALID_ARG, "softmax_scale must be finite");
+  USP_CHECK(std::isfinite(a->softcap) && a->softcap >= 0.f, USP_ERR_INVALID_ARG, "softcap must be finite and >= 0");
+  USP_CHECK(!a->alibi_slopes || a->S <= kMaxAlibiPositions, USP_ERR_UNSUPPORTED,
+            "ALiBi distances are computed in f32: at most %lld positions, got %lld",
+            (long long)kMaxAlibiPositions, (long long)a->S);
   USP_CHECK((a->cu_seqlens_host == nullptr) == (a->cu_seqlens_dev == nullptr), USP_ERR_INVALID_ARG,
             "cu_seqlens must be given on both host and device, or neither");
   if (a->cu_seqlens_host) {
@@ -641,6 +675,12 @@ usp_status check_ring_args(const usp_ring_args* a) {
   USP_CHECK(L * (a->Hkv / a->ulysses_degree) * a->D * 2 < ((int64_t)1 << 31), USP_ERR_UNSUPPORTED,
             "one ring rank's k/v rows must be under 2 GiB (32-bit tile offsets)");
   return USP_OK;
+}
+
+// The ring's score modifiers: the slopes of this Ulysses rank's head group.
+usp_status ring_mods(const usp_ring_args* a, int64_t Hq_l, float scale, ScoreMods* out) {
+  const float* slopes = a->alibi_slopes ? a->alibi_slopes + (int64_t)a->ulysses_rank * Hq_l : nullptr;
+  return make_mods(a->softcap, slopes, USP_MASK_POSITIONAL, a->S, scale, out);
 }
 
 RingLayout ring_layout(const usp_ring_args* a) {
@@ -886,6 +926,9 @@ usp_status usp_ring_fwd(const usp_ring_args* a, void* workspace, size_t ws_bytes
   float* opart = a->merge_mode ? reinterpret_cast<float*>(ws + R.off_opart) : nullptr;
   float* lpart = a->merge_mode ? reinterpret_cast<float*>(ws + R.off_lpart) : nullptr;
   const float scale = a->softmax_scale > 0.f ? a->softmax_scale : 1.0f / std::sqrt((float)D);
+  ScoreMods mods;
+  st = ring_mods(a, Hq_l, scale, &mods);
+  if (st != USP_OK) return st;
 
   MaskSpec ms;
   ms.causal = a->causal ? 1 : 0;
@@ -948,6 +991,7 @@ usp_status usp_ring_fwd(const usp_ring_args* a, void* workspace, size_t ws_bytes
     p.qmap = base_map;
     p.kmap = base_map;
     p.mask = ms;
+    p.mods = mods;
     st = launch_attn_fwd(p, (int)D, stream);
     if (st != USP_OK) return st;
     if (to_part) {
@@ -1050,6 +1094,9 @@ usp_status usp_ring_bwd(const usp_ring_bwd_args* ba, void* workspace, size_t ws_
   // kernel per step covers every host of the step (their dq rows and dk / dv
   // pieces are disjoint)
   const float scale = a->softmax_scale > 0.f ? a->softmax_scale : 1.0f / std::sqrt((float)D);
+  ScoreMods mods;
+  st = ring_mods(a, Hq_l, scale, &mods);
+  if (st != USP_OK) return st;
   MaskSpec ms;
   ms.causal = a->causal ? 1 : 0;
   ms.window = a->window;
@@ -1114,6 +1161,7 @@ usp_status usp_ring_bwd(const usp_ring_bwd_args* ba, void* workspace, size_t ws_
     p.qmap = base_map;
     p.kmap = base_map;
     p.mask = ms;
+    p.mods = mods;
     BwdParams pq = p, pk = p;
     pq.items = dpq.items;
     pq.runs = dpq.runs;

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const void* out, int out
 //   C(qb): dV^T += dO^T P, dK^T += Q^T dS.
 // Issue order A0 A1 B0 B1 C0 C1, with B0's VALU work placed between A1's
 // MFMAs and B1's between C0's, and LDS fragment reads kPF MFMAs ahead.
-template <int D>
+template <int D, int MODS>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   using T = SwzTile<D>;
   constexpr int BQ = 64;            // query rows per tile
@@ -199,12 +199,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   const int32_t lo_p = cw ? max(ks0, pk) : ks0;
   const int32_t hi_p = (p.mask.window > 0 && !sink) ? min(ks1 - 1, pk + p.mask.window - 1) : ks1 - 1;
   const float c = p.scale_log2;
+  // ALiBi distances in f32 (positions below 2^22 are exact): a row t of the
+  // query rank is at t + floor(t / b) (N - 1) b + rank b under the stripe
+  // layout and at t + (p(t0) - t0) inside a monotone piece of the others
+  // (inv_b = 0 there), so p_q - p_k = floor((t + 0.5) inv_b) nb1 + t + rb.
+  // rb of a tile: rb0, or rb1 for a tile in the second zigzag chunk.
+  const bool qstripe = qm.kind == MAP_STRIPE;
+  const float inv_b = qstripe ? 1.f / (float)qm.b : 0.f;
+  const float nb1 = qstripe ? (float)((qm.N - 1) * qm.b) : 0.f;
+  const int32_t qhalf = qm.kind == MAP_ZIGZAG ? qm.L >> 1 : 0x7fffffff;
+  const float rb0 = (float)((qstripe ? qm.rank * qm.b : position(qm, 0)) - pk);
+  const float rb1 = qm.kind == MAP_ZIGZAG ? (float)(position(qm, qhalf) - qhalf - pk) : rb0;
 
   // One tile.  FULL: every pair visible.  Otherwise element r of query
   // block qb is local row t0 + qb*32 + 8*(r/4) + 4*hi + r%4; query
   // positions increase through the run, so the rows that see this lane's
   // key are one interval, found once per tile.
-  auto tile = [&](auto full_c, const char* buf, int t0, int tend) {
+  auto tile = [&](auto full_c, const char* buf, int t0, int tend, int gi) {
     constexpr bool FULL = decltype(full_c)::value;
     const char* tQ = buf;
     const char* tO = buf + TILEB;
@@ -258,7 +269,35 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
       if (w & 1) dp[qb] = mfma32(fa[i], vf[ks], ks == 0 ? zero : dp[qb]);
       else s[qb] = mfma32(fa[i], kf[ks], ks == 0 ? zero : s[qb]);
     }
+    // Score modifiers of element r of block qb (raw units, as the
+    // forward): softcap a - 2a rc with rc = 1 / (exp2(s b2) + 1), whose
+    // derivative factor 1 - tanh^2 = 4 rc (1 - rc) scales dS; then ALiBi.
+    float slope = 0.f, abase = 0.f, rb = 0.f;
+    if constexpr ((MODS & 2) != 0) {
+      slope = p.mods.alibi[h0 + gi] * p.mods.inv_scale;
+      abase = (float)(t0 + 4 * hi);
+      rb = t0 >= qhalf ? rb1 : rb0;
+    }
+    auto mods = [&](int qb, int r, float& sv, float& f, float ab) {
+      if constexpr ((MODS & 1) != 0) {
+        const float rc = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(sv * p.mods.b2) + 1.f);
+        sv = p.mods.a - 2.f * p.mods.a * rc;
+        f = 4.f * rc * (1.f - rc);
+      }
+      if constexpr ((MODS & 2) != 0) {
+        // row index t (the constant is added first so that it folds into one
+        // instruction)
+        const float t = ab + (float)(qb * 32 + 8 * (r >> 2) + (r & 3));
+        const float dd = __builtin_floorf((t + 0.5f) * inv_b) * nb1 + (t + rb);
+        sv -= slope * __builtin_fabsf(dd);
+      }
+    };
     auto softmax = [&](int qb) {
+      // The bias terms depend on nothing the MFMAs produce; the empty asm
+      // keeps the compiler from hoisting all of them into live registers
+      // ahead of the matrix products.
+      float ab = abase;
+      if constexpr ((MODS & 2) != 0) asm volatile("" : "+v"(ab));
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const float lq[4] = {l4[qb][g].x, l4[qb][g].y, l4[qb][g].z, l4[qb][g].w};
@@ -266,14 +305,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 4; e += 2) {
           const int r0 = 4 * g + e, r1 = r0 + 1;
-          float p0 = __builtin_amdgcn_exp2f(s[qb][r0] * c - lq[e] * kLog2e);
-          float p1 = __builtin_amdgcn_exp2f(s[qb][r1] * c - lq[e + 1] * kLog2e);
+          float s0 = s[qb][r0], s1 = s[qb][r1], f0 = 1.f, f1 = 1.f;
+          if constexpr (MODS != 0) {
+            mods(qb, r0, s0, f0, ab);
+            mods(qb, r1, s1, f1, ab);
+          }
+          float p0 = __builtin_amdgcn_exp2f(s0 * c - lq[e] * kLog2e);
+          float p1 = __builtin_amdgcn_exp2f(s1 * c - lq[e + 1] * kLog2e);
           if constexpr (!FULL) {
             p0 = visible(qb, r0) ? p0 : 0.f;
             p1 = visible(qb, r1) ? p1 : 0.f;
           }
-          const float d0 = p0 * (dp[qb][r0] - dq4[e]);
-          const float d1 = p1 * (dp[qb][r1] - dq4[e + 1]);
+          float d0 = p0 * (dp[qb][r0] - dq4[e]);
+          float d1 = p1 * (dp[qb][r1] - dq4[e + 1]);
+          if constexpr ((MODS & 1) != 0) {
+            d0 *= f0;
+            d1 *= f1;
+          }
           const bf16x2 pp = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
           const bf16x2 dd = __builtin_convertvector((f32x2){d0, d1}, bf16x2);
           pb[qb][r0 >> 3][r0 & 7] = pp[0];
@@ -324,6 +372,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   dma(smem, c_gi, c_t0, c_run.k_end);
 
   for (int n = 0; n < n_tiles; ++n) {
+    const int gi = c_gi;
     const int t0 = c_t0;
     const int t_end = c_run.k_end;
     const bool full = c_run.full != 0;
@@ -341,8 +390,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
       }
       dma(smem + ((n + 1) & 1) * BUFB, c_gi, c_t0, c_run.k_end);
     }
-    if (full) tile(std::true_type{}, buf, t0, t_end);
-    else tile(std::false_type{}, buf, t0, t_end);
+    if (full) tile(std::true_type{}, buf, t0, t_end, gi);
+    else tile(std::false_type{}, buf, t0, t_end, gi);
   }
 
   if (!kvalid || it.run_begin == it.run_end) return;
@@ -414,8 +463,18 @@ usp_status launch_bwd(const BwdParams& pq, const BwdParams& pkv, int D, hipStrea
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && nk > 0) {
     TimingScope ts(K_BWD_DKDV, stream);
-    if (D == 128) hipLaunchKernelGGL((bwd_dkdv_kernel<128>), dim3((unsigned)nk), dim3(256), 0, stream, pkv);
-    else hipLaunchKernelGGL((bwd_dkdv_kernel<64>), dim3((unsigned)nk), dim3(256), 0, stream, pkv);
+    const int mods = mods_variant(pkv.mods);
+#define USP_LAUNCH_KV(DD, M) hipLaunchKernelGGL((bwd_dkdv_kernel<DD, M>), dim3((unsigned)nk), dim3(256), 0, stream, pkv)
+#define USP_LAUNCH_KV_M(DD)                  \
+  switch (mods) {                            \
+    case 0: USP_LAUNCH_KV(DD, 0); break;     \
+    case 1: USP_LAUNCH_KV(DD, 1); break;     \
+    case 2: USP_LAUNCH_KV(DD, 2); break;     \
+    default: USP_LAUNCH_KV(DD, 3); break;    \
+  }
+    if (D == 128) { USP_LAUNCH_KV_M(128) } else { USP_LAUNCH_KV_M(64) }
+#undef USP_LAUNCH_KV_M
+#undef USP_LAUNCH_KV
     e = hipGetLastError();
   }
   if (e != hipSuccess) {

@@ -17,7 +17,7 @@ namespace {
 // Issue order A0 A1 B0 C0 B1 C1, with B0's VALU work placed between A1's
 // MFMAs and B1's between C0's, and every LDS fragment read issued kPF
 // MFMAs ahead of its use.
-template <int D>
+template <int D, int MODS>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const BwdParams p) {
   using T = SwzTile<D>;
   constexpr int BN = 64;
@@ -86,8 +86,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const BwdParams p) {
   km.rank = it.k_rank;
   const bool cw = p.mask.causal || p.mask.window > 0;
   int32_t sstart, vis_lo, vis_hi, sink_hi;
+  const int32_t pq_row = position(qm, it.t0 + (qvalid ? qr : 0));
   {
-    const int32_t pq = position(qm, it.t0 + (qvalid ? qr : 0));
+    const int32_t pq = pq_row;
     int32_t s0 = 0, s1 = p.mask.S;
     for (int i = 0; i < p.mask.nseq; ++i) {
       const int32_t lo = p.cu_seqlens[i], up = p.cu_seqlens[i + 1];
@@ -111,6 +112,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const BwdParams p) {
   const int lrow = lane / T::CPR;
   const int lslot = lane % T::CPR;
   const float c = p.scale_log2;
+  // ALiBi distances in f32 (positions below 2^22 are exact): a key t of the
+  // key rank is at t + floor(t / b) (N - 1) b + rank b under the stripe
+  // layout and at t + (p(k0) - k0) inside a run of the others (inv_b = 0
+  // there), so p_k - p_q = floor((t + 0.5) inv_b) nb1 + t + rb.
+  // rb of a tile: rb0, or rb1 for a tile in the second zigzag chunk.
+  const bool kstripe = km.kind == MAP_STRIPE;
+  const float inv_b = kstripe ? 1.f / (float)km.b : 0.f;
+  const float nb1 = kstripe ? (float)((km.N - 1) * km.b) : 0.f;
+  const int32_t khalf = km.kind == MAP_ZIGZAG ? km.L >> 1 : 0x7fffffff;
+  const float rb0 = (float)((kstripe ? km.rank * km.b : position(km, 0)) - pq_row);
+  const float rb1 = km.kind == MAP_ZIGZAG ? (float)(position(km, khalf) - khalf - pq_row) : rb0;
+  const float slope = (MODS & 2) ? p.mods.alibi[h] * p.mods.inv_scale : 0.f;
 
   // The workgroup walks the key tiles of its runs with two LDS buffers: tile
   // n + 1 is copied global -> LDS directly (buffer loads to LDS) while tile
@@ -179,20 +192,56 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const BwdParams p) {
       if (w & 1) dpt[kb] = mfma32(fa[i], dof[ks], ks == 0 ? zero : dpt[kb]);
       else st[kb] = mfma32(fa[i], qf[ks], ks == 0 ? zero : st[kb]);
     }
+    // Score modifiers of element r of key block kb (raw units, as the
+    // forward): softcap a - 2a rc with rc = 1 / (exp2(s b2) + 1), whose
+    // derivative factor 1 - tanh^2 = 4 rc (1 - rc) scales dS; then ALiBi.
+    float abase = 0.f, rb = 0.f;
+    if constexpr ((MODS & 2) != 0) {
+      abase = (float)(k0 + 4 * hi);
+      rb = k0 >= khalf ? rb1 : rb0;
+    }
+    auto mods = [&](int kb, int r, float& sv, float& f, float ab) {
+      if constexpr ((MODS & 1) != 0) {
+        const float rc = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(sv * p.mods.b2) + 1.f);
+        sv = p.mods.a - 2.f * p.mods.a * rc;
+        f = 4.f * rc * (1.f - rc);
+      }
+      if constexpr ((MODS & 2) != 0) {
+        // key index t (the constant is added first so that it folds into one
+        // instruction)
+        const float t = ab + (float)(kb * 32 + 8 * (r >> 2) + (r & 3));
+        const float dd = __builtin_floorf((t + 0.5f) * inv_b) * nb1 + (t + rb);
+        sv -= slope * __builtin_fabsf(dd);
+      }
+    };
     auto softmax = [&](int kb) {
+      // The bias terms depend on nothing the MFMAs produce; the empty asm
+      // keeps the compiler from hoisting all of them into live registers
+      // ahead of the matrix products.
+      float ab = abase;
+      if constexpr ((MODS & 2) != 0) asm volatile("" : "+v"(ab));
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const int r0 = half * 8 + e, r1 = r0 + 1;
-          float p0 = __builtin_amdgcn_exp2f(st[kb][r0] * c - lse2);
-          float p1 = __builtin_amdgcn_exp2f(st[kb][r1] * c - lse2);
+          float s0 = st[kb][r0], s1 = st[kb][r1], f0 = 1.f, f1 = 1.f;
+          if constexpr (MODS != 0) {
+            mods(kb, r0, s0, f0, ab);
+            mods(kb, r1, s1, f1, ab);
+          }
+          float p0 = __builtin_amdgcn_exp2f(s0 * c - lse2);
+          float p1 = __builtin_amdgcn_exp2f(s1 * c - lse2);
           if constexpr (!FULL) {
             p0 = visible(kb, r0) ? p0 : 0.f;
             p1 = visible(kb, r1) ? p1 : 0.f;
           }
-          const float d0 = p0 * (dpt[kb][r0] - dl);
-          const float d1 = p1 * (dpt[kb][r1] - dl);
+          float d0 = p0 * (dpt[kb][r0] - dl);
+          float d1 = p1 * (dpt[kb][r1] - dl);
+          if constexpr ((MODS & 1) != 0) {
+            d0 *= f0;
+            d1 *= f1;
+          }
           const bf16x2 pk2 = __builtin_convertvector((f32x2){d0, d1}, bf16x2);
           dsb[kb][half][e] = pk2[0];
           dsb[kb][half][e + 1] = pk2[1];
@@ -278,8 +327,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const BwdParams p) {
 
 void launch_bwd_dq(const BwdParams& p, int D, unsigned grid, hipStream_t stream) {
   TimingScope ts(K_BWD_DQ, stream);
-  if (D == 128) hipLaunchKernelGGL((bwd_dq_kernel<128>), dim3(grid), dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL((bwd_dq_kernel<64>), dim3(grid), dim3(256), 0, stream, p);
+  const int mods = mods_variant(p.mods);
+#define USP_LAUNCH_Q(DD, M) hipLaunchKernelGGL((bwd_dq_kernel<DD, M>), dim3(grid), dim3(256), 0, stream, p)
+#define USP_LAUNCH_Q_M(DD)                  \
+  switch (mods) {                           \
+    case 0: USP_LAUNCH_Q(DD, 0); break;     \
+    case 1: USP_LAUNCH_Q(DD, 1); break;     \
+    case 2: USP_LAUNCH_Q(DD, 2); break;     \
+    default: USP_LAUNCH_Q(DD, 3); break;    \
+  }
+  if (D == 128) { USP_LAUNCH_Q_M(128) } else { USP_LAUNCH_Q_M(64) }
+#undef USP_LAUNCH_Q_M
+#undef USP_LAUNCH_Q
 }
 
 }  // namespace usp

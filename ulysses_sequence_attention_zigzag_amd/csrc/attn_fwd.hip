@@ -114,7 +114,7 @@ struct TileLayout {
 // reading, and waits for them at the end of its V(t), before the barrier
 // that hands the phase over.  Phase barriers carry no memory fence: every
 // LDS read of a matrix phase is consumed by its MFMAs before the phase ends.
-template <int D, bool LINEAR>
+template <int D, bool LINEAR, int MODS>
 __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
   using TL = TileLayout<D>;
   // Keys per tile.  The LINEAR kernel stages its tiles with buffer loads
@@ -197,8 +197,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
   km.rank = it.k_rank;
   const bool cw = p.mask.causal || p.mask.window > 0;
   int32_t sstart, vis_lo, vis_hi, sink_hi;
+  const int32_t pq_row = position(qm, it.t0 + (qvalid ? qr : 0));
   {
-    const int32_t pq = position(qm, it.t0 + (qvalid ? qr : 0));
+    const int32_t pq = pq_row;
     int32_t s0 = 0, s1 = p.mask.S;
     for (int i = 0; i < p.mask.nseq; ++i) {
       const int32_t lo = p.cu_seqlens[i], up = p.cu_seqlens[i + 1];
@@ -350,6 +351,50 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
     }
   };
 
+  // Score modifiers (MODS bit 0: softcap, bit 1: ALiBi) on the raw scores of
+  // the tile at key k0, before the mask: softcap a - 2a / (exp2(s b2) + 1)
+  // (= c tanh(s scale / c) / scale), then minus slope_h |p_q - p_k| / scale.
+  // ALiBi distances in f32 (positions below 2^22 are exact): key t of the
+  // key rank is at t + floor(t / b) (N - 1) b + rank b under the stripe
+  // layout and at t + (p(k0) - k0) inside a run of the others (inv_b = 0
+  // there), so p_k - p_q = floor((t + 0.5) inv_b) nb1 + t + rb.
+  const float slope_raw = (MODS & 2) ? p.mods.alibi[h] * p.mods.inv_scale : 0.f;
+  // rb of a tile: rb0, or rb1 for a tile in the second zigzag chunk.
+  const bool kstripe = km.kind == MAP_STRIPE;
+  const float inv_b = kstripe ? 1.f / (float)km.b : 0.f;
+  const float nb1 = kstripe ? (float)((km.N - 1) * km.b) : 0.f;
+  const int32_t khalf = km.kind == MAP_ZIGZAG ? km.L >> 1 : 0x7fffffff;
+  const float rb0 = (float)((kstripe ? km.rank * km.b : position(km, 0)) - pq_row);
+  const float rb1 = km.kind == MAP_ZIGZAG ? (float)(position(km, khalf) - khalf - pq_row) : rb0;
+  auto apply_mods = [&](f32x16 (&sc)[NB], int k0) {
+    if constexpr ((MODS & 1) != 0) {
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = __builtin_amdgcn_exp2f(sc[kb][r] * p.mods.b2);
+          sc[kb][r] = p.mods.a - 2.f * p.mods.a * __builtin_amdgcn_rcpf(e + 1.f);
+        }
+    }
+    if constexpr ((MODS & 2) != 0) {
+      // element (kb, r) is key t = k0 + 4*hi + kb*32 + 8*(r/4) + r%4 (the
+      // constant is added first so that it folds into one instruction); the
+      // empty asm keeps the compiler from hoisting the bias terms ahead of
+      // the matrix products.
+      float ab = (float)(k0 + 4 * hi);
+      const float rb = k0 >= khalf ? rb1 : rb0;
+      asm volatile("" : "+v"(ab));
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float t = ab + (float)(kb * 32 + 8 * (r >> 2) + (r & 3));
+          const float dd = __builtin_floorf((t + 0.5f) * inv_b) * nb1 + (t + rb);
+          sc[kb][r] -= slope_raw * __builtin_fabsf(dd);
+        }
+    }
+  };
+
   // Per-element mask of a partial tile starting at key k0.  Element (kb, r)
   // of this lane is key k0 + du with du = c + 4*hi, c = kb*32 + 8*(r/4) + r%4.
   // For layouts whose key positions step linearly through a run, the visible
@@ -429,6 +474,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
     };
     // V(t): mask, online softmax (log2 domain, lazy rescale); tile t+1 lands.
     auto v_phase = [&](int t) {
+      if constexpr (MODS != 0) apply_mods(s, k0);
       if (!run.full) apply_mask(s, k0, run.k_end);
       float mt = -INFINITY;
 #pragma unroll
@@ -583,12 +629,21 @@ usp_status launch_attn_fwd(const AttnParams& p, int D, hipStream_t stream) {
   const dim3 grid((unsigned)total), block(512);
   const bool linear = !(p.kmap.kind == MAP_STRIPE && p.kmap.b > 1);
   TimingScope ts(K_ATTN, stream);
-#define USP_LAUNCH(DD, LIN) hipLaunchKernelGGL((attn_fwd_kernel<DD, LIN>), grid, block, 0, stream, p)
-  if (D == 128) {
-    if (linear) USP_LAUNCH(128, true); else USP_LAUNCH(128, false);
-  } else {
-    if (linear) USP_LAUNCH(64, true); else USP_LAUNCH(64, false);
+  const int mods = mods_variant(p.mods);
+#define USP_LAUNCH(DD, LIN, M) hipLaunchKernelGGL((attn_fwd_kernel<DD, LIN, M>), grid, block, 0, stream, p)
+#define USP_LAUNCH_M(DD, LIN)                     \
+  switch (mods) {                                  \
+    case 0: USP_LAUNCH(DD, LIN, 0); break;         \
+    case 1: USP_LAUNCH(DD, LIN, 1); break;         \
+    case 2: USP_LAUNCH(DD, LIN, 2); break;         \
+    default: USP_LAUNCH(DD, LIN, 3); break;        \
   }
+  if (D == 128) {
+    if (linear) { USP_LAUNCH_M(128, true) } else { USP_LAUNCH_M(128, false) }
+  } else {
+    if (linear) { USP_LAUNCH_M(64, true) } else { USP_LAUNCH_M(64, false) }
+  }
+#undef USP_LAUNCH_M
 #undef USP_LAUNCH
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {

@@ -141,6 +141,26 @@ struct DevicePlan {
   int32_t n_runs = 0;
 };
 
+// Score modifiers of the attention call, in the kernels' raw-score units
+// (scores before softmax_scale): with softcap c > 0 the scaled score s*scale
+// becomes c * tanh(s*scale / c), i.e. the raw score becomes
+// a - 2a / (exp2(s * b2) + 1) with a = c / scale and b2 = 2 * scale *
+// log2(e) / c; ALiBi subtracts slope_h * |p_q - p_k| / scale.
+struct ScoreMods {
+  float a;               // softcap / scale (0: no softcap)
+  float b2;              // 2 * scale * log2(e) / softcap
+  float inv_scale;       // 1 / scale
+  const float* alibi;    // slope per query head of this call's heads, or nullptr
+};
+
+// ALiBi distances are formed in f32 from row indices, with the stripe
+// layout's block index taken as floor((t + 0.5) / b): exact while positions
+// stay below 2^22.
+constexpr int64_t kMaxAlibiPositions = int64_t(1) << 22;
+
+// Kernel variant of a call's score modifiers: bit 0 softcap, bit 1 ALiBi.
+inline int mods_variant(const ScoreMods& m) { return (m.a > 0.f ? 1 : 0) | (m.alibi ? 2 : 0); }
+
 // Attention kernel parameters (passed by value).
 struct AttnParams {
   const uint16_t* q;
@@ -166,6 +186,7 @@ struct AttnParams {
   PosMap qmap;              // rank field overridden per item
   PosMap kmap;
   MaskSpec mask;
+  ScoreMods mods;
 };
 
 // Launchers (return USP_ERR_HIP on launch failure).
@@ -199,6 +220,7 @@ struct BwdParams {
   PosMap qmap;
   PosMap kmap;
   MaskSpec mask;
+  ScoreMods mods;
 };
 constexpr int kBwdTileM = 128;  // query rows per dQ workgroup
 constexpr int kBwdTileK = 128;  // keys per dK / dV workgroup

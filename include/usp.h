@@ -226,7 +226,10 @@ usp_status usp_block_attn_bwd(const void* q, const void* k, const void* v, const
  * host, values in [Lq, S]).  Visibility: causal, and with window > 0 the
  * window / n_sink rule of usp_block_attn_fwd (positions from 0 per row).
  * (Hq/Hkv)*Lq must not exceed 32; D is 64 or 128; split_keys is a positive
- * multiple of 32.  softmax_scale <= 0 selects 1/sqrt(D).
+ * multiple of 32.  softmax_scale <= 0 selects 1/sqrt(D).  softcap and
+ * alibi_slopes (device, Hq f32) are the score modifiers of
+ * usp_block_attn_fwd, with the same per-row positions (ALiBi needs S <=
+ * 2^22).
  *
  * usp_decode_split_fwd writes, for n = ceil(S / split_keys) pieces, the
  *   partials out_part [n,B,Lq,Hq,D] and lse_part [n,B,Hq,Lq] (f32) of keys
@@ -243,7 +246,7 @@ usp_status usp_decode_split_fwd(const void* q, const void* k, const void* v,
                                 float* out_part, float* lse_part,
                                 int64_t B, int64_t Lq, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
                                 int64_t split_keys, float softmax_scale, int window, int n_sink,
-                                void* stream);
+                                float softcap, const float* alibi_slopes, void* stream);
 
 usp_status usp_decode_merge(float* out_part, float* lse_part, int64_t n_split,
                             int64_t B, int64_t Lq, int64_t Hq, int64_t D,

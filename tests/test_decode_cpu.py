@@ -15,11 +15,11 @@ FAKE = ctypes.c_void_p(0x10000)
 
 def _split(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, ld=None, lh=None, op=FAKE, lp=FAKE, B=2, Lq=1, S=1024, Hq=8, Hkv=2, D=128,
-             split=256, scale=0.0, window=0, n_sink=0)
+             split=256, scale=0.0, window=0, n_sink=0, cap=0.0, alibi=None)
     a.update(kw)
     st = usp.lib().usp_decode_split_fwd(a["q"], a["k"], a["v"], a["ld"], a["lh"], a["op"], a["lp"], a["B"], a["Lq"],
                                         a["S"], a["Hq"], a["Hkv"], a["D"], a["split"], a["scale"], a["window"],
-                                        a["n_sink"], None)
+                                        a["n_sink"], a["cap"], a["alibi"], None)
     return st, usp.lib().usp_last_error().decode()
 
 
@@ -47,6 +47,10 @@ def test_decode_split_validation():
     assert st == 1 and "both" in msg
     st, msg = _split(scale=float("inf"))
     assert st == 1 and "finite" in msg
+    st, msg = _split(cap=-1.0)
+    assert st == 1 and "softcap" in msg
+    st, msg = _split(S=(1 << 22) + 32, Hkv=1, D=64, alibi=FAKE)
+    assert st == 2 and "ALiBi" in msg
 
 
 def test_decode_merge_validation():

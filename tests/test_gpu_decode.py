@@ -95,3 +95,30 @@ def test_decode_large_cache_and_determinism():
     for _ in range(3):
         o2, l2 = usp.decode_fwd(qd, kd, vd, kv_lens=[S, 40000], split_keys=256)
         assert torch.equal(out, o2) and torch.equal(lse, l2)
+
+
+def _slopes(H):
+    return torch.tensor([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=torch.float32)
+
+
+@pytest.mark.parametrize("softcap,alibi", [(1.5, False), (0.0, True), (1.5, True)], ids=str)
+@pytest.mark.parametrize("case", [CASES[0], CASES[1], CASES[2], CASES[3]])
+def test_decode_score_mods(case, softcap, alibi):
+    """Softcap and ALiBi (per-row positions from 0) in the split kernel."""
+    B, S, Lq, Hq, Hkv, D, lens, split, window, n_sink = case
+    say(f"decode mods {case} cap={softcap} alibi={alibi}")
+    q, k, v = _cache(B, S, Lq, Hq, Hkv, D, seed=43)
+    scale = D ** -0.5
+    al = _slopes(Hq) if alibi else None
+    kw = dict(softmax_scale=scale, window=window, n_sink=n_sink, softcap=softcap, alibi_slopes=al)
+    Op_ref, Lp_ref = decode_split_ref(q, k, v, lens, split_keys=split, **kw)
+    op, lp = usp.decode_split_fwd(q.cuda(), k.cuda(), v.cuda(), kv_lens=lens, split_keys=split, window=window,
+                                  n_sink=n_sink, softcap=softcap, alibi_slopes=None if al is None else al.cuda())
+    torch.cuda.synchronize()
+    for i in range(op.shape[0]):
+        _check(op[i], lp[i], Op_ref[i], Lp_ref[i], f"piece {i}")
+    O_ref, L_ref = decode_ref(q, k, v, lens, **kw)
+    out, lse = usp.decode_merge(op.clone(), lp.clone())
+    _check(out, lse, O_ref, L_ref, "merged")
+    O0, _ = decode_ref(q, k, v, lens, softmax_scale=scale, window=window, n_sink=n_sink)
+    assert float((O0 - O_ref).abs().max()) > 10 * OUT_TOL   # the modifiers matter here

@@ -87,7 +87,7 @@ _SIGS = {
                             ctypes.c_float, _I32, ctypes.POINTER(PosMap), ctypes.POINTER(PosMap), _I32, _I32,
                             _I32, _P, _P, _I32, ctypes.c_float, _P, _P], _I32),
     "usp_decode_split_fwd": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64, ctypes.c_float,
-                              _I32, _I32, _P], _I32),
+                              _I32, _I32, ctypes.c_float, _P, _P], _I32),
     "usp_decode_merge": ([_P, _P, _I64, _I64, _I64, _I64, _I64, _P, _I32, _P, _P], _I32),
     "usp_timing_enable": ([_I32], _I32),
     "usp_timing_reset": ([], _I32),
@@ -285,10 +285,11 @@ def default_split_keys(B: int, S: int, Hkv: int) -> int:
 
 
 def decode_split_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, kv_lens=None, split_keys: Optional[int] = None,
-                     window: int = 0, n_sink: int = 0, softmax_scale: float = 0.0, out_part=None, lse_part=None,
+                     window: int = 0, n_sink: int = 0, softmax_scale: float = 0.0, softcap: float = 0.0,
+                     alibi_slopes: Optional[torch.Tensor] = None, out_part=None, lse_part=None,
                      stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Partials of the cache pieces (usp_decode_split_fwd): q [B,Lq,Hq,D], cache k / v [B,S,Hkv,D] bf16.
-    Returns (out_part [n,B,Lq,Hq,D], lse_part [n,B,Hq,Lq]) f32."""
+    """Partials of the cache pieces (usp_decode_split_fwd): q [B,Lq,Hq,D], cache k / v [B,S,Hkv,D] bf16;
+    alibi_slopes [Hq] f32 on the device.  Returns (out_part [n,B,Lq,Hq,D], lse_part [n,B,Hq,Lq]) f32."""
     B, Lq, Hq, D = q.shape
     S, Hkv = k.shape[1], k.shape[2]
     if split_keys is None:
@@ -307,7 +308,8 @@ def decode_split_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, kv_le
         ctypes.c_void_p(lens_dev.data_ptr()) if lens_dev is not None else None,
         ctypes.c_void_p(lens_host.data_ptr()) if lens_host is not None else None,
         _dev(out_part, torch.float32, "out_part"), _dev(lse_part, torch.float32, "lse_part"),
-        B, Lq, S, Hq, Hkv, D, split_keys, float(softmax_scale), int(window), int(n_sink), _stream(stream)))
+        B, Lq, S, Hq, Hkv, D, split_keys, float(softmax_scale), int(window), int(n_sink), float(softcap),
+        _slopes(alibi_slopes, Hq), _stream(stream)))
     if lens_dev is not None:
         torch.cuda.current_stream().synchronize()  # the kv_lens copy must outlive the launch
     return out_part, lse_part

@@ -563,7 +563,8 @@ usp_status usp_block_attn_bwd(const void* q, const void* k, const void* v, const
 usp_status usp_decode_split_fwd(const void* q, const void* k, const void* v, const int32_t* kv_lens_dev,
                                 const int32_t* kv_lens_host, float* out_part, float* lse_part, int64_t B, int64_t Lq,
                                 int64_t S, int64_t Hq, int64_t Hkv, int64_t D, int64_t split_keys,
-                                float softmax_scale, int window, int n_sink, void* stream) {
+                                float softmax_scale, int window, int n_sink, float softcap,
+                                const float* alibi_slopes, void* stream) {
   USP_CHECK(q && k && v && out_part && lse_part, USP_ERR_INVALID_ARG, "null tensor pointer");
   USP_CHECK(B >= 1 && Lq >= 1 && S >= 1 && Hq >= 1 && Hkv >= 1, USP_ERR_INVALID_ARG, "bad sizes");
   USP_CHECK(D == 64 || D == 128, USP_ERR_UNSUPPORTED, "head_dim must be 64 or 128, got %lld", (long long)D);
@@ -587,6 +588,9 @@ usp_status usp_decode_split_fwd(const void* q, const void* k, const void* v, con
                 "kv_lens[%lld] = %d outside [Lq, S] = [%lld, %lld]", (long long)b, kv_lens_host[b], (long long)Lq,
                 (long long)S);
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)D);
+  ScoreMods mods;
+  usp_status st = make_mods(softcap, alibi_slopes, USP_MASK_POSITIONAL, S, scale, &mods);
+  if (st != USP_OK) return st;
   DecodeParams p{};
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
@@ -604,6 +608,7 @@ usp_status usp_decode_split_fwd(const void* q, const void* k, const void* v, con
   p.window = window;
   p.n_sink = n_sink;
   p.scale_log2 = scale * 1.4426950408889634f;
+  p.mods = mods;
   return launch_decode_split(p, (int)D, as_stream(stream));
 }
 

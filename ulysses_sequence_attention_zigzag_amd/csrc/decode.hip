@@ -23,7 +23,7 @@ namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
 
-template <int D>
+template <int D, int MODS>
 __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p) {
   using T = SwzTile<D>;
   constexpr int KS = D / 16;
@@ -118,6 +118,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
   float lsum = 0.f;     // this lane's share of the running sum
   const float c = p.scale_log2;
   const int n_tiles = (k_hi - k_lo + TK - 1) / TK;
+  // score modifiers (MODS bit 0 softcap, bit 1 ALiBi; raw-score units as in
+  // the attention kernels): distance p_q - p_k of element e of the tile at
+  // k0 is (pq - k0 - 4*hi) - cc, formed in f32 (exact below 2^22 keys)
+  const float slope = ((MODS & 2) && valid) ? p.mods.alibi[h] * p.mods.inv_scale : 0.f;
 
   copy_tile(wbuf, k_lo);
   for (int n = 0; n < n_tiles; ++n) {
@@ -134,13 +138,18 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
     // element e is key k0 + 4*hi + cc, cc = 8*(e/4) + e%4
     const int sh = k0 + 4 * hi;
     const int lo = lo_k - sh, up = min(hi_k, k_hi - 1) - sh, sup = min(sink_hi, k_hi - 1) - sh;
+    const float ab = (float)(pq - sh);
     float x[16];
     float tmax = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int cc = 8 * (e >> 2) + (e & 3);
       const bool vis = ((cc >= lo) & (cc <= up)) | (cc <= sup);
-      x[e] = vis ? st[e] * c : -INFINITY;
+      float sv = st[e];
+      if constexpr ((MODS & 1) != 0)
+        sv = p.mods.a - 2.f * p.mods.a * __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(sv * p.mods.b2) + 1.f);
+      if constexpr ((MODS & 2) != 0) sv -= slope * __builtin_fabsf(ab - (float)cc);
+      x[e] = vis ? sv * c : -INFINITY;
       tmax = fmaxf(tmax, x[e]);
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
@@ -279,8 +288,18 @@ usp_status launch_decode_split(const DecodeParams& p, int D, hipStream_t stream)
   const dim3 grid((unsigned)((p.n_split + 3) / 4), (unsigned)p.Hkv, (unsigned)p.B);
   {
     TimingScope ts(K_DECODE, stream);
-    if (D == 128) hipLaunchKernelGGL((decode_split_kernel<128>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((decode_split_kernel<64>), grid, dim3(256), 0, stream, p);
+    const int mods = mods_variant(p.mods);
+#define USP_LAUNCH_DEC(DD, M) hipLaunchKernelGGL((decode_split_kernel<DD, M>), grid, dim3(256), 0, stream, p)
+#define USP_LAUNCH_DEC_M(DD)                \
+  switch (mods) {                           \
+    case 0: USP_LAUNCH_DEC(DD, 0); break;   \
+    case 1: USP_LAUNCH_DEC(DD, 1); break;   \
+    case 2: USP_LAUNCH_DEC(DD, 2); break;   \
+    default: USP_LAUNCH_DEC(DD, 3); break;  \
+  }
+    if (D == 128) { USP_LAUNCH_DEC_M(128) } else { USP_LAUNCH_DEC_M(64) }
+#undef USP_LAUNCH_DEC_M
+#undef USP_LAUNCH_DEC
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {

@@ -243,6 +243,7 @@ struct DecodeParams {
   int32_t n_split, split_keys;
   int32_t window, n_sink;
   float scale_log2;        // softmax_scale * log2(e)
+  ScoreMods mods;          // slopes indexed by query head
 };
 usp_status launch_decode_split(const DecodeParams& p, int D, hipStream_t stream);
 usp_status launch_decode_merge(float* out_part, float* lse_part, int32_t n_split, int32_t B, int32_t Lq,

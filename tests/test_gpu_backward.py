@@ -374,3 +374,84 @@ def test_ring_bwd_packed_qkv(w):
     torch.cuda.synchronize()
     for g, r, name in zip(got, ref, ("dq", "dk", "dv")):
         assert_grad(g, r, name)
+
+
+# ---------------------------------------------------------------- full size, sampled
+def _local_rows(w: si.Workload, seed: int, n: int):
+    L = w.S // w.ring_degree
+    rows = {0, 1, L // 2 - 1, L // 2, L - 1}
+    g = torch.Generator().manual_seed(seed)
+    rows |= set(torch.randint(0, L, (n,), generator=g).tolist())
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("name", ["usp_zigzag_gqa", "stripe_mqa"])
+def test_large_workloads_full_size_backward_sampled(name):
+    """usp_ring_bwd at the workload's full size, after usp_ring_fwd on the
+    device (the benchmark's launch configuration): dq on sampled query rows of
+    the rank, and dk / dv on the keys nearest the sequence end, whose few
+    visible queries the oracle can take one by one (keys no query of the rank
+    sees must come back exactly zero)."""
+    w = si.WORKLOADS[name]
+    say(f"full-size backward {name}: generating inputs")
+    q, k, v = w.make_inputs()
+    fwd = usp.RingCall(q.cuda(), k.cuda(), v.cuda(), impl=w.impl, ring_degree=w.ring_degree,
+                       ulysses_degree=w.ulysses_degree, stripe_block=w.stripe_block, causal=w.causal,
+                       window=w.window, n_sink=w.n_sink, softmax_scale=w.softmax_scale or 0.0, rank=w.rank,
+                       ulysses_rank=w.ulysses_rank)
+    fwd.run()
+    dout = si.randn_bf16(tuple(fwd.out.shape), w.seed, 3)
+    dq, dk, dv = usp.RingBwdCall(fwd, dout.cuda()).run()
+    torch.cuda.synchronize()
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
+    N, ud, u = w.ring_degree, w.ulysses_degree, w.ulysses_rank
+    Hl, Hkl = w.Hq // ud, w.Hkv // ud
+    heads, kvh = list(range(u * Hl, (u + 1) * Hl)), list(range(u * Hkl, (u + 1) * Hkl))
+    pos = ix.rank_positions(w.impl, w.S, N, w.rank, w.stripe_block)
+    kw = dict(softmax_scale=w.scale, causal=w.causal, window=w.window, n_sink=w.n_sink)
+    ks, vs = k[:, :, kvh].contiguous(), v[:, :, kvh].contiguous()
+
+    # the oracle's forward (O, LSE) and delta of every query row used below,
+    # in one pass over the keys
+    rows = _local_rows(w, seed=17, n=3)
+    keys = sorted({w.S - 1, w.S - 2, w.S - 3, w.S - 9, w.S - 16})
+    seers = [t for t in range(len(pos)) if pos[t] >= min(keys)]
+    need = sorted(set(rows) | set(seers))
+    say(f"full-size backward {name}: oracle forward on {len(need)} rows")
+    O_all, LSE_all = attention_ref(q, k, v, rows=[pos[r] for r in need], heads=heads, **kw)
+    at = {r: i for i, r in enumerate(need)}
+
+    def oracle_rows(local_rows):
+        idx = torch.tensor([at[r] for r in local_rows], dtype=torch.long)
+        O, LSE = O_all[:, idx], LSE_all[:, :, idx]
+        do = dout[:, local_rows]
+        delta = (do.double() * O).sum(-1).transpose(1, 2)
+        return [pos[r] for r in local_rows], LSE, do, delta
+
+    # dq of sampled query rows: every key
+    say(f"full-size backward {name}: oracle dq on {len(rows)} rows")
+    p_rows, LSE, do, delta = oracle_rows(rows)
+    qi = q[:, p_rows][:, :, heads].contiguous()
+    dq_ref, _, _ = block_attention_bwd_ref(qi, ks, vs, do, LSE, delta, p_rows, list(range(w.S)), scale=w.scale,
+                                           causal=w.causal, window=w.window, n_sink=w.n_sink)
+    assert_grad(dq[:, rows], dq_ref, "dq sampled")
+
+    # dk / dv of the last keys: only the rank's queries at or after them see them
+    allpos = [ix.rank_positions(w.impl, w.S, N, r, w.stripe_block) for r in range(N)]
+    out_row = {p: i for i, p in enumerate(p for r in range(N) for p in allpos[r])}   # rank-major rows
+    say(f"full-size backward {name}: oracle dk/dv on {len(keys)} keys from {len(seers)} query rows")
+    krow = torch.tensor([out_row[p] for p in keys])
+    got_k, got_v = dk[:, krow], dv[:, krow]
+    if not seers:
+        assert float(got_k.abs().max()) == 0.0 and float(got_v.abs().max()) == 0.0
+        return
+    p_s, LSE_s, do_s, delta_s = oracle_rows(seers)
+    qs = q[:, p_s][:, :, heads].contiguous()
+    _, dk_ref, dv_ref = block_attention_bwd_ref(qs, ks[:, keys], vs[:, keys], do_s, LSE_s, delta_s, p_s, keys,
+                                                scale=w.scale, causal=w.causal, window=w.window, n_sink=w.n_sink)
+    unseen = torch.tensor([all(pp < p for pp in p_s) for p in keys])
+    if unseen.any():
+        assert float(got_k[:, unseen].abs().max()) == 0.0 and float(got_v[:, unseen].abs().max()) == 0.0
+    seen = ~unseen
+    assert_grad(got_k[:, seen], dk_ref[:, seen], "dk last keys")
+    assert_grad(got_v[:, seen], dv_ref[:, seen], "dv last keys")

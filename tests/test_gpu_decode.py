@@ -97,6 +97,30 @@ def test_decode_large_cache_and_determinism():
         assert torch.equal(out, o2) and torch.equal(lse, l2)
 
 
+@pytest.mark.parametrize("name", ["decode_gqa_128k", "decode_mqa_1m"])
+def test_decode_workloads_full_size(name):
+    """The two decode workloads at full size, with the piece size and inputs
+    the benchmark uses: every piece's partial and the merged result against
+    the oracle."""
+    import bench
+    cfg = bench.DECODE_WORKLOADS[name]
+    B, S, Lq, Hq, Hkv, D = (cfg[x] for x in ("B", "S", "Lq", "Hq", "Hkv", "D"))
+    say(f"decode full size {name}: generating inputs")
+    q = si.randn_bf16((B, Lq, Hq, D), cfg["seed"], 0)
+    k = si.randn_bf16((B, S, Hkv, D), cfg["seed"], 1)
+    v = si.randn_bf16((B, S, Hkv, D), cfg["seed"], 2)
+    split = usp.default_split_keys(B, S, Hkv)
+    op, lp = usp.decode_split_fwd(q.cuda(), k.cuda(), v.cuda(), split_keys=split)
+    out, lse = usp.decode_merge(op.clone(), lp.clone())
+    torch.cuda.synchronize()
+    say(f"decode full size {name}: oracle ({op.shape[0]} pieces of {split} keys)")
+    Op_ref, Lp_ref = decode_split_ref(q, k, v, split_keys=split)
+    for i in (0, 1, op.shape[0] // 2, op.shape[0] - 1):
+        _check(op[i], lp[i], Op_ref[i], Lp_ref[i], f"piece {i}")
+    O_ref, L_ref = decode_ref(q, k, v)
+    _check(out, lse, O_ref, L_ref, "merged")
+
+
 def _slopes(H):
     return torch.tensor([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=torch.float32)
 

@@ -3,8 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one usp_ring_fwd call over the whole hot path of the workload:
-token permutation of q/k/v (natural -> ring layout), Ulysses seq->head
-relayout, every ring step's block attention with the LSE merge, and the
+token permutation of q/k/v (natural -> ring layout) with the Ulysses
+seq->head relayout (one strided gather per tensor when ulysses_degree > 1),
+every ring step's block attention with the LSE merge, and the
 output finalisation.  Inputs are seeded bf16 N(0,1), resident in HBM before
 the timed region.  Prints one JSON line.
 
@@ -92,19 +93,22 @@ def visible_pairs_per_head(w, rank_rows=None) -> int:
 
 
 def step_bytes(w):
-    """Algorithmic HBM bytes (read + write) of the copy kernels in one step."""
+    """Algorithmic HBM bytes (read + write) of the staging copies in one step,
+    as (row gather, Ulysses relayout).  With ulysses_degree > 1 the ring
+    library does both in one strided copy per tensor (ring-ordered rows of
+    Ulysses rank u's head group): its bytes are the first entry and the
+    second is 0."""
     N, ud, S, B, D = w.ring_degree, w.ulysses_degree, w.S, w.B, w.D
     L = S // N
+    q_rows = L if w.rank >= 0 else S                              # q: rank extract or full
+    if ud > 1:
+        return (2 * B * q_rows * (w.Hq // ud) * D * 2              # q rows of head group u
+                + 2 * 2 * B * S * (w.Hkv // ud) * D * 2), 0        # k and v, all pieces
     perm = 0
     if w.impl != "basic":
         perm += 2 * 2 * B * S * w.Hkv * D * 2                      # k and v, full permute
-        q_rows = L if w.rank >= 0 else S                          # q: rank extract or full
         perm += 2 * B * q_rows * w.Hq * D * 2
-    relay = 0
-    if ud > 1:
-        relay += 2 * B * L * (w.Hq // ud) * D * 2                  # q
-        relay += 2 * 2 * B * S * (w.Hkv // ud) * D * 2             # k and v
-    return perm, relay
+    return perm, 0
 
 
 def cpu_baseline(w, q, k, v, budget_s: float):
@@ -328,9 +332,8 @@ def main():
     attn_ms, attn_n = kt["attn"]
     attn_ms_step = attn_ms / args.steps
     attn_tflops = flops / (attn_ms_step * 1e-3) / 1e12 if attn_ms > 0 else None
-    perm_bytes, relay_bytes = step_bytes(w)
+    perm_bytes, _ = step_bytes(w)
     perm_ms = kt["permute"][0] / args.steps
-    relay_ms = kt["relayout"][0] / args.steps
 
     def gbs(b, ms):
         return round(b / (ms * 1e-3) / 1e9, 1) if ms > 0 and b > 0 else None
@@ -370,12 +373,11 @@ def main():
             "kernel_ms_per_step": round(attn_ms_step, 4),
         },
         "copy_kernels": {
-            "permute": {"bytes": perm_bytes, "ms": round(perm_ms, 4), "GB/s": gbs(perm_bytes, perm_ms),
-                        "pct_hbm": round(100 * perm_bytes / (perm_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 1)
-                        if perm_ms > 0 and perm_bytes > 0 else None},
-            "relayout": {"bytes": relay_bytes, "ms": round(relay_ms, 4), "GB/s": gbs(relay_bytes, relay_ms),
-                         "pct_hbm": round(100 * relay_bytes / (relay_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 1)
-                         if relay_ms > 0 and relay_bytes > 0 else None},
+            # the layout's row gather (with Ulysses: fused with the head split)
+            ("permute+relayout" if w.ulysses_degree > 1 else "permute"): {
+                "bytes": perm_bytes, "ms": round(perm_ms, 4), "GB/s": gbs(perm_bytes, perm_ms),
+                "pct_hbm": round(100 * perm_bytes / (perm_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 1)
+                if perm_ms > 0 and perm_bytes > 0 else None},
         },
         "cpu_baseline": None,
     }

@@ -709,7 +709,7 @@ RingLayout ring_layout(const usp_ring_args* a) {
     return o;
   };
   const size_t D = (size_t)a->D, B = (size_t)a->B, S = (size_t)a->S;
-  if (r.copy_in) {
+  if (r.copy_in && ud == 1) {
     r.off_qp = take(B * (size_t)r.q_rows * a->Hq * D * 2);
     r.off_kp = take(B * S * a->Hkv * D * 2);
     r.off_vp = take(B * S * a->Hkv * D * 2);
@@ -737,6 +737,12 @@ RingLayout ring_layout(const usp_ring_args* a) {
 // Steps 1-2 of the ring (shared by forward and backward): token order
 // (rank-major q, or ring rank r's rows; k, v), then the Ulysses seq -> head
 // relayout for Ulysses rank u.  Uses the workspace regions of `R`.
+//
+// With ulysses_degree > 1 the two steps are one strided copy per tensor.
+// Ulysses rank u gathers, for each ring rank, the ud sub-shards of that
+// rank's rows in order and keeps head group u, so its relayouted tensor is
+// the ring-ordered rows restricted to heads [u H/ud, (u+1) H/ud): a gather
+// of rows (the layout's permutation or rank extract) of a head slice.
 struct Staged {
   const uint16_t* q;
   const uint16_t* k;
@@ -752,6 +758,44 @@ usp_status stage_ring_inputs(const usp_ring_args* a, const RingLayout& R, char* 
   const int N = a->ring_degree, ud = a->ulysses_degree, u = a->ulysses_rank;
   const int64_t B = a->B, S = a->S, D = a->D, L = R.L;
   const int b = a->impl == USP_RING_STRIPE ? a->stripe_block : 1;
+  if (ud > 1) {
+    // rows in ring order (all pieces of k and v; ring rank r's rows of q),
+    // heads of group u, from natural or rank-major order, packed or not
+    const int64_t Hq_l = R.Hq_l, Hkv_l = R.Hkv_l;
+    const int64_t q_row = a->Hq * D * 2, kv_row = a->Hkv * D * 2;  // source row bytes (one tensor)
+    const int64_t src_stride_q = a->qkv_packed ? 3 * q_row : q_row;
+    const int64_t src_stride_kv = a->qkv_packed ? 3 * kv_row : kv_row;
+    const char* qb = static_cast<const char*>(a->q);
+    const char* kb = a->qkv_packed ? qb + q_row : static_cast<const char*>(a->k);
+    const char* vb = a->qkv_packed ? qb + 2 * q_row : static_cast<const char*>(a->v);
+    auto spec = [&](bool extract) {
+      GatherSpec gs{};
+      gs.impl = R.need_perm ? a->impl : USP_RING_BASIC;
+      gs.N = N;
+      gs.ud = 1;
+      gs.b = R.need_perm ? b : 1;
+      gs.g = extract ? a->rank : 0;
+      gs.L = (int32_t)L;
+      gs.S = (int32_t)S;
+      gs.kind = extract ? G_EXTRACT : G_PERMUTE;
+      return gs;
+    };
+    uint16_t* ql = reinterpret_cast<uint16_t*>(ws + R.off_ql);
+    uint16_t* kl = reinterpret_cast<uint16_t*>(ws + R.off_kl);
+    uint16_t* vl = reinterpret_cast<uint16_t*>(ws + R.off_vl);
+    st = launch_permute_strided(kb + u * Hkv_l * D * 2, kl, B, S, S, Hkv_l * D * 2, src_stride_kv,
+                                Hkv_l * D * 2, spec(false), stream);
+    if (st == USP_OK)
+      st = launch_permute_strided(vb + u * Hkv_l * D * 2, vl, B, S, S, Hkv_l * D * 2, src_stride_kv,
+                                  Hkv_l * D * 2, spec(false), stream);
+    if (st == USP_OK)
+      st = launch_permute_strided(qb + u * Hq_l * D * 2, ql, B, S, L, Hq_l * D * 2, src_stride_q,
+                                  Hq_l * D * 2, spec(true), stream);
+    if (st != USP_OK) return st;
+    *out = Staged{ql, kl, vl, L, 0, Hq_l, Hkv_l};
+    return USP_OK;
+  }
+
   // 1. token order: rank-major q (or ring rank r's rows), k, v
   const uint16_t* qsrc = static_cast<const uint16_t*>(a->q);
   const uint16_t* ksrc = static_cast<const uint16_t*>(a->k);
@@ -809,37 +853,7 @@ usp_status stage_ring_inputs(const usp_ring_args* a, const RingLayout& R, char* 
     q_row_off = (int64_t)a->rank * L;
   }
 
-  // 2. Ulysses seq -> head relayout for Ulysses rank u
-  int64_t Hq_l = a->Hq, Hkv_l = a->Hkv;
-  if (ud > 1) {
-    uint16_t* ql = reinterpret_cast<uint16_t*>(ws + R.off_ql);
-    uint16_t* kl = reinterpret_cast<uint16_t*>(ws + R.off_kl);
-    uint16_t* vl = reinterpret_cast<uint16_t*>(ws + R.off_vl);
-    void* sh[8];
-    for (int up = 0; up < ud; ++up)
-      sh[up] = const_cast<uint16_t*>(qsrc) + (q_row_off + up * R.Ls) * a->Hq * D;
-    st = launch_relayout_strided(sh, ql, B, R.Ls, a->Hq, D, 2, ud, u, 0, q_batch_rows, L, stream);
-    if (st != USP_OK) return st;
-    for (int j = 0; j < N; ++j) {
-      for (int up = 0; up < ud; ++up)
-        sh[up] = const_cast<uint16_t*>(ksrc) + ((int64_t)j * L + up * R.Ls) * a->Hkv * D;
-      st = launch_relayout_strided(sh, kl + (int64_t)j * L * R.Hkv_l * D, B, R.Ls, a->Hkv, D, 2, ud, u, 0, S, S, stream);
-      if (st != USP_OK) return st;
-      for (int up = 0; up < ud; ++up)
-        sh[up] = const_cast<uint16_t*>(vsrc) + ((int64_t)j * L + up * R.Ls) * a->Hkv * D;
-      st = launch_relayout_strided(sh, vl + (int64_t)j * L * R.Hkv_l * D, B, R.Ls, a->Hkv, D, 2, ud, u, 0, S, S, stream);
-      if (st != USP_OK) return st;
-    }
-    qsrc = ql;
-    ksrc = kl;
-    vsrc = vl;
-    q_batch_rows = L;
-    q_row_off = 0;
-    Hq_l = R.Hq_l;
-    Hkv_l = R.Hkv_l;
-  }
-
-  *out = Staged{qsrc, ksrc, vsrc, q_batch_rows, q_row_off, Hq_l, Hkv_l};
+  *out = Staged{qsrc, ksrc, vsrc, q_batch_rows, q_row_off, a->Hq, a->Hkv};
   return USP_OK;
 }
 
@@ -870,7 +884,7 @@ RingBwdLayout ring_bwd_layout(const usp_ring_args* a) {
   // the staging regions, as the forward lays them out; no forward accumulators
   R.off_qp = R.off_kp = R.off_vp = R.off_ql = R.off_kl = R.off_vl = NONE;
   R.off_oacc = R.off_lacc = R.off_opart = R.off_lpart = NONE;
-  if (R.copy_in) {
+  if (R.copy_in && a->ulysses_degree == 1) {
     R.off_qp = take(B * (size_t)R.q_rows * a->Hq * D * 2);
     R.off_kp = take(B * S * a->Hkv * D * 2);
     R.off_vp = take(B * S * a->Hkv * D * 2);

@@ -111,6 +111,50 @@ def step_bytes(w):
     return perm, 0
 
 
+def time_lse_merge(w, merge_mode: int, merge_timing) -> dict:
+    """GB/s of the LSE merge kernel (usp_lse_merge) over one step's
+    accumulator: f32 O [B, rows, Hq_local, D] and LSE [B, Hq_local, rows],
+    timed standalone on seeded accumulators of that shape, outside the timed
+    steps (the ring merges inside the attention epilogue unless merge_mode
+    is 1).  With merge_mode 1 the ring's own merge launches are reported
+    too; they read a partial the attention kernel has just written, much of
+    it still in the cache, so their rate is not an HBM rate."""
+    import torch
+
+    import ulysses_sequence_attention_zigzag_amd as usp
+
+    Hl = w.Hq // w.ulysses_degree
+    rows = w.S // w.ring_degree if w.rank >= 0 else w.S
+    B = 1 if w.cu_seqlens is not None else w.B
+    nbytes = 3 * B * rows * Hl * (w.D + 1) * 4       # read acc + part, write acc (O and LSE)
+    g = torch.Generator(device="cuda").manual_seed(77)
+    oa = torch.randn((B, rows, Hl, w.D), generator=g, device="cuda")
+    op = torch.randn((B, rows, Hl, w.D), generator=g, device="cuda")
+    la = torch.randn((B, Hl, rows), generator=g, device="cuda")
+    lp = torch.randn((B, Hl, rows), generator=g, device="cuda")
+    for _ in range(2):
+        usp.lse_merge(oa, la, op, lp)
+    torch.cuda.synchronize()
+    reps = 5
+    usp.timing_reset()
+    usp.timing_enable(True)
+    for _ in range(reps):
+        usp.lse_merge(oa, la, op, lp)
+    torch.cuda.synchronize()
+    usp.timing_enable(False)
+    ms, n = usp.timing_read("merge")
+    usp.timing_reset()
+    rec = {"bytes": nbytes, "ms": None, "GB/s": None, "pct_hbm": None,
+           "source": "standalone usp_lse_merge on seeded accumulators of one step's shape"}
+    if n > 0 and ms > 0:
+        per = ms / n
+        gbps = nbytes / (per * 1e-3) / 1e9
+        rec.update({"ms": round(per, 4), "GB/s": round(gbps, 1), "pct_hbm": round(100 * gbps / PEAK_HBM_GBS, 1)})
+    if merge_mode == 1 and merge_timing[1] > 0:
+        rec["in_ring_ms"] = round(merge_timing[0] / merge_timing[1], 4)
+    return rec
+
+
 def cpu_baseline(w, q, k, v, budget_s: float):
     """Times the float64 oracle on a seeded sample of the workload's output rows."""
     import torch
@@ -334,6 +378,7 @@ def main():
     attn_tflops = flops / (attn_ms_step * 1e-3) / 1e12 if attn_ms > 0 else None
     perm_bytes, _ = step_bytes(w)
     perm_ms = kt["permute"][0] / args.steps
+    merge_rec = time_lse_merge(w, args.merge_mode, kt["merge"])
 
     def gbs(b, ms):
         return round(b / (ms * 1e-3) / 1e9, 1) if ms > 0 and b > 0 else None
@@ -378,6 +423,7 @@ def main():
                 "bytes": perm_bytes, "ms": round(perm_ms, 4), "GB/s": gbs(perm_bytes, perm_ms),
                 "pct_hbm": round(100 * perm_bytes / (perm_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 1)
                 if perm_ms > 0 and perm_bytes > 0 else None},
+            "merge": merge_rec,
         },
         "cpu_baseline": None,
     }

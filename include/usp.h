@@ -258,7 +258,9 @@ usp_status usp_decode_merge(float* out_part, float* lse_part, int64_t n_split,
  * logsumexp are associative]:
  *   M = max(L_a, L_b); L = M + ln(e^(L_a - M) + e^(L_b - M));
  *   O = e^(L_a - L) O_a + e^(L_b - L) O_b;   (L_b = -inf leaves (O_a, L_a)).
- * out_acc/out_part are f32 [B,L,H,D]; lse_acc/lse_part f32 [B,H,L]. */
+ * out_acc/out_part are f32 [B,L,H,D]; lse_acc/lse_part f32 [B,H,L].
+ * D/4 must divide 64 (D = 4, 8, 16, ..., 256), else USP_ERR_UNSUPPORTED;
+ * a row range outside [0, L] is USP_ERR_INVALID_ARG. */
 usp_status usp_lse_merge(float* out_acc, float* lse_acc, const float* out_part, const float* lse_part,
                          int64_t B, int64_t L, int64_t H, int64_t D, int64_t row_begin,
                          int64_t row_end, void* stream);

@@ -145,6 +145,9 @@ def test_merge_validation():
     assert st == 1 and "row range" in msg
     st, msg = _status(L.usp_lse_merge, FAKE, FAKE, FAKE, FAKE, 1, 10, 2, 6, 0, 10, None)
     assert st == 2
+    # a (row, head) of D/4 threads must fit in one wave of 64
+    st, msg = _status(L.usp_lse_merge, FAKE, FAKE, FAKE, FAKE, 1, 10, 2, 512, 0, 10, None)
+    assert st == 2 and "dividing 64" in msg
 
 
 def _ring_args(**kw):

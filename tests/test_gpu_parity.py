@@ -204,10 +204,11 @@ def test_block_attn_accumulate_matches_merge():
     assert_parity(out, lse, O_ref, L_ref, "accumulate")
 
 
-def test_lse_merge_kernel():
-    say("lse_merge")
+@pytest.mark.parametrize("D", [8, 64, 128, 256])
+def test_lse_merge_kernel(D):
+    say(f"lse_merge D={D}")
     g = torch.Generator().manual_seed(3)
-    B, L, H, D = 2, 300, 3, 128
+    B, L, H = 2, 300, 3
     oa = torch.randn(B, L, H, D, generator=g, dtype=torch.float64)
     ob = torch.randn(B, L, H, D, generator=g, dtype=torch.float64)
     la = torch.randn(B, H, L, generator=g, dtype=torch.float64) * 4

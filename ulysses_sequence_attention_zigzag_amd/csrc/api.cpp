@@ -333,8 +333,8 @@ usp_status usp_lse_merge(float* out_acc, float* lse_acc, const float* out_part, 
                          int64_t row_end, void* stream) {
   USP_CHECK(out_acc && lse_acc && out_part && lse_part, USP_ERR_INVALID_ARG, "null pointer");
   USP_CHECK(B >= 0 && L >= 0 && H >= 1, USP_ERR_INVALID_ARG, "bad sizes");
-  USP_CHECK(D >= 4 && D % 4 == 0 && 256 % (D / 4) == 0, USP_ERR_UNSUPPORTED,
-            "merge supports D with D/4 dividing 256 (got %lld)", (long long)D);
+  USP_CHECK(D >= 4 && D % 4 == 0 && 64 % (D / 4) == 0, USP_ERR_UNSUPPORTED,
+            "merge supports D with D/4 dividing 64 (D = 4, 8, ..., 256; got %lld)", (long long)D);
   USP_CHECK(0 <= row_begin && row_begin <= row_end && row_end <= L, USP_ERR_INVALID_ARG,
             "row range [%lld, %lld) outside [0, %lld)", (long long)row_begin, (long long)row_end, (long long)L);
   USP_CHECK(B * L * H <= kMaxI32, USP_ERR_UNSUPPORTED, "tensor too large");

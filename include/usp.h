@@ -272,7 +272,9 @@ usp_status usp_lse_merge(float* out_acc, float* lse_acc, const float* out_part, 
  * mask its positions imply and merges its partial into the running result.
  * The KV "send" is a pointer offset; every step is enqueued in order on one
  * stream.  With ulysses_degree ud > 1 the Ulysses seq -> head relayout of
- * q, k, v runs first for Ulysses rank `ulysses_rank` [YC "2. Usage"].
+ * q, k, v runs first for Ulysses rank `ulysses_rank` [YC "2. Usage"]; its
+ * result is the ring-ordered rows restricted to head group u, so the token
+ * permutation and the relayout are one strided copy per tensor.
  *
  * Inputs q [B,S,Hq,D], k/v [B,S,Hkv,D] bf16 hold the whole sequence, in
  * natural order (input_order 0; permuted on the device first) or already

@@ -279,9 +279,9 @@ def block_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torc
 
 def default_split_keys(B: int, S: int, Hkv: int) -> int:
     """Keys per cache piece: up to 1024 (longer streams per wave, fewer partials), but small enough that
-    the split kernel runs at least ~1024 waves (one per SIMD of the 256 CUs), since one wave handles one
-    (piece, batch row, KV head)."""
-    return max(32, min(1024, (S * B * Hkv // 1024) // 32 * 32))
+    the split kernel runs at least ~2048 waves (8 per CU of the 256, two per SIMD), since one wave handles
+    one (piece, batch row, KV head) and the kernel's rate follows the waves per CU."""
+    return max(32, min(1024, (S * B * Hkv // 2048) // 32 * 32))
 
 
 def decode_split_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, kv_lens=None, split_keys: Optional[int] = None,

@@ -23,8 +23,42 @@ namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
 
+// Waves per workgroup, LDS stages (K + V tile buffers) per wave and the
+// minimum waves per SIMD the register budget must allow, for the split
+// kernel; a workgroup's LDS is waves x stages x 16 KB at D = 128.  With one
+// stage a wave copies a tile, waits for it and computes on it, and the other
+// waves of its SIMD cover the wait; with more, a wave keeps stages - 1 tiles
+// in flight (their copies must fit the 6-bit vmcnt).  Measured on MI355X
+// (kernel GB/s): the rate follows the waves per CU, not the tiles in flight
+// per wave -- 4 waves x 2 stages (one workgroup per CU) 4.7-5.0 TB/s; one
+// stage with 8-10 waves per CU (2 x 1, 4 x 1, 8 x 1, 1 x 1) 5.4-5.5 TB/s.
+#ifndef USP_DEC_WAVES
+#define USP_DEC_WAVES 2
+#endif
+#ifndef USP_DEC_STAGES
+#define USP_DEC_STAGES 1
+#endif
+#ifndef USP_DEC_MINW
+#define USP_DEC_MINW 2
+#endif
+constexpr int kDecWaves = USP_DEC_WAVES;
+constexpr int kDecStages = USP_DEC_STAGES;
+
+// s_waitcnt vmcnt(n) for the counts the split kernel uses (any other count
+// waits for everything, which is only slower).
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 16: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+    case 24: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
+    case 32: asm volatile("s_waitcnt vmcnt(32)" ::: "memory"); break;
+    case 48: asm volatile("s_waitcnt vmcnt(48)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
+
 template <int D, int MODS>
-__global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(64 * kDecWaves, USP_DEC_MINW) void decode_split_kernel(const DecodeParams p) {
   using T = SwzTile<D>;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
@@ -32,7 +66,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
   constexpr int TILEB = TK * D * 2;
   constexpr int NLD = TILEB / 1024;      // 1 KB copies per tile and tensor
   constexpr int RPI = 1024 / T::ROWB;
-  __shared__ __attribute__((aligned(1024))) char smem[4 * 2 * 2 * TILEB];
+  constexpr int NST = kDecStages;
+  static_assert(NST >= 1 && (NST - 2) * 2 * NLD <= 63, "tiles in flight must fit vmcnt");
+  __shared__ __attribute__((aligned(1024))) char smem[kDecWaves * NST * 2 * TILEB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -40,7 +76,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  const int split = blockIdx.x * 4 + wid;
+  const int split = blockIdx.x * kDecWaves + wid;
   if (split >= p.n_split) return;  // the whole wave leaves; the kernel has no barrier
   const int hk = blockIdx.y;
   const int b = blockIdx.z;
@@ -94,7 +130,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
   const uint32_t row_bytes = (uint32_t)row_elems * 2;
   const int lrow = lane / T::CPR;
   const int lslot = lane % T::CPR;
-  char* const wbuf = smem + wid * 2 * 2 * TILEB;  // this wave's two (K, V) buffers
+  char* const wbuf = smem + wid * NST * 2 * TILEB;  // this wave's NST (K, V) buffers
 
   // copy of the tile at key k0: lane i of copy j moves physical (row, slot) =
   // (j*RPI + i / CPR, i % CPR), i.e. logical chunk slot ^ swz(row); rows past
@@ -123,14 +159,21 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
   // k0 is (pq - k0 - 4*hi) - cc, formed in f32 (exact below 2^22 keys)
   const float slope = ((MODS & 2) && valid) ? p.mods.alibi[h] * p.mods.inv_scale : 0.f;
 
-  copy_tile(wbuf, k_lo);
+  // tile n lives in buffer n % NST.  With NST > 1, tiles n + 1 .. n + NST - 1
+  // are copied while tile n computes, into the buffers of tiles
+  // n + 1 - NST .. n - 1, whose reads the MFMAs of earlier iterations have
+  // consumed; with NST = 1 the next copy starts after tile n's last MFMA.
+  for (int i = 0; i < max(NST - 1, 1) && i < n_tiles; ++i) copy_tile(wbuf + i * 2 * TILEB, k_lo + i * TK);
   for (int n = 0; n < n_tiles; ++n) {
     const int k0 = k_lo + n * TK;
-    const char* tK = wbuf + (n & 1) * 2 * TILEB;
+    const char* tK = wbuf + (n % NST) * 2 * TILEB;
     const char* tV = tK + TILEB;
-    // this wave's copies of tile n are in LDS; no memory access moves across
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (n + 1 < n_tiles) copy_tile(wbuf + ((n + 1) & 1) * 2 * TILEB, k0 + TK);
+    // tile n's copies are in LDS once at most the copies of the tiles issued
+    // after it (n + 1 .. n + NST - 2) are outstanding (loads complete in
+    // order); no memory access moves across the wait
+    wait_vmcnt(NST >= 2 ? min(NST - 2, n_tiles - 1 - n) * 2 * NLD : 0);
+    if (NST >= 2 && n + NST - 1 < n_tiles)
+      copy_tile(wbuf + ((n + NST - 1) % NST) * 2 * TILEB, k0 + (NST - 1) * TK);
 
     f32x16 st = {};
 #pragma unroll
@@ -177,6 +220,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
     for (int half = 0; half < 2; ++half)
 #pragma unroll
       for (int d = 0; d < DB; ++d) ot[d] = mfma32(frag_tr<D>(tV, 0, half, d, lane), pb[half], ot[d]);
+    if (NST == 1 && n + 1 < n_tiles) {
+      // every fragment read of the buffer has returned (the MFMAs above
+      // consumed them) before the next tile's copy is issued into it
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      copy_tile(wbuf, k0 + TK);
+    }
   }
 
   const float ltot = lsum + __shfl_xor(lsum, 32);
@@ -285,11 +334,11 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(float* out_part, floa
 }  // namespace
 
 usp_status launch_decode_split(const DecodeParams& p, int D, hipStream_t stream) {
-  const dim3 grid((unsigned)((p.n_split + 3) / 4), (unsigned)p.Hkv, (unsigned)p.B);
+  const dim3 grid((unsigned)((p.n_split + kDecWaves - 1) / kDecWaves), (unsigned)p.Hkv, (unsigned)p.B);
   {
     TimingScope ts(K_DECODE, stream);
     const int mods = mods_variant(p.mods);
-#define USP_LAUNCH_DEC(DD, M) hipLaunchKernelGGL((decode_split_kernel<DD, M>), grid, dim3(256), 0, stream, p)
+#define USP_LAUNCH_DEC(DD, M) hipLaunchKernelGGL((decode_split_kernel<DD, M>), grid, dim3(64 * kDecWaves), 0, stream, p)
 #define USP_LAUNCH_DEC_M(DD)                \
   switch (mods) {                           \
     case 0: USP_LAUNCH_DEC(DD, 0); break;   \

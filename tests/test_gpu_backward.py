@@ -283,6 +283,9 @@ RING_BWD = [
                                             impl="zigzag"),
     si.WORKLOADS["varlen_streaming"].scaled(S=2048, Hq=4, Hkv=1, window=0, n_sink=0, causal=True,
                                             cu_seqlens=[0, 700, 701, 2048], impl="stripe", stripe_block=4),
+    si.WORKLOADS["usp_zigzag_gqa"].scaled(S=4096, Hq=8, Hkv=4, ulysses_degree=4, rank=1, ulysses_rank=2),
+    si.WORKLOADS["stripe_mqa"].scaled(S=4096, Hq=4, Hkv=2, ring_degree=4, ulysses_degree=2, rank=2,
+                                      ulysses_rank=1),
 ]
 
 

@@ -275,10 +275,18 @@ SMALL_RING = [
                                             impl="zigzag"),
     si.WORKLOADS["varlen_streaming"].scaled(S=2048, Hq=4, Hkv=1, window=0, n_sink=0, causal=True,
                                             cu_seqlens=[0, 700, 701, 2048], impl="stripe", stripe_block=4),
+    # Ulysses head groups with every layout: the staging gathers ring-ordered
+    # rows of head group u in one strided pass
+    si.WORKLOADS["usp_zigzag_gqa"].scaled(S=4096, Hq=8, Hkv=4, ulysses_degree=4, rank=1, ulysses_rank=2),
+    si.WORKLOADS["stripe_mqa"].scaled(S=4096, Hq=4, Hkv=2, ring_degree=4, ulysses_degree=2, rank=2,
+                                      ulysses_rank=1),
+    si.WORKLOADS["ring_swa"].scaled(S=2048, Hq=4, Hkv=4, window=300, ulysses_degree=2, rank=5, ulysses_rank=1),
+    si.WORKLOADS["varlen_streaming"].scaled(S=2048, Hq=4, Hkv=2, window=250, cu_seqlens=[0, 128, 1000, 2048],
+                                            impl="zigzag", ulysses_degree=2, rank=1, ulysses_rank=0),
 ]
 
 
-@pytest.mark.parametrize("w", SMALL_RING, ids=lambda w: f"{w.name}-S{w.S}-r{w.rank}")
+@pytest.mark.parametrize("w", SMALL_RING, ids=lambda w: f"{w.name}-S{w.S}-r{w.rank}-u{w.ulysses_degree}.{w.ulysses_rank}")
 @pytest.mark.parametrize("merge_mode", [0, 1])
 def test_ring_small_full_oracle(w, merge_mode):
     say(f"ring {w.name} S={w.S} rank={w.rank} merge_mode={merge_mode}")

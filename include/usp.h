@@ -105,7 +105,8 @@ const char* usp_version(void);
  *        (only that shard's rows are written).
  * Out-of-place only (in and out must not overlap).  S must be divisible by N
  * (BASIC), 2N (ZIGZAG) or N*b (STRIPE), and L by ulysses_degree.  Bit-exact
- * copy; HBM-bound. */
+ * copy; HBM-bound.  outer may be 0 (nothing is enqueued; in and out may then
+ * be NULL). */
 usp_status usp_permute(const void* in, void* out, int64_t outer, int64_t S, int64_t inner,
                        usp_dtype dt, usp_ring_impl impl, int ring_degree, int ulysses_degree,
                        int stripe_block, int rank, int inverse, void* stream);
@@ -150,6 +151,9 @@ usp_status usp_ulysses_relayout(void* const* shards, void* local, int64_t B, int
  * int32, host) plans the tiles; cu_seqlens_dev (same values, device) is read
  * by the kernel.  The first call with a new shape/mask builds and uploads a
  * tile plan (one synchronous copy); later calls reuse it.
+ * Lq or Lk may be 0.  With Lk = 0 no row has a visible key: out = 0 and
+ * lse = -inf (accumulate = 1 leaves them unchanged); k and v may then be
+ * NULL.  With Lq = 0 nothing is enqueued and q, out, lse may be NULL.
  *
  * Score modifiers, applied to s in this order before the mask and softmax
  * (both off with softcap = 0 and alibi_slopes = NULL):
@@ -260,7 +264,8 @@ usp_status usp_decode_merge(float* out_part, float* lse_part, int64_t n_split,
  *   O = e^(L_a - L) O_a + e^(L_b - L) O_b;   (L_b = -inf leaves (O_a, L_a)).
  * out_acc/out_part are f32 [B,L,H,D]; lse_acc/lse_part f32 [B,H,L].
  * D/4 must divide 64 (D = 4, 8, 16, ..., 256), else USP_ERR_UNSUPPORTED;
- * a row range outside [0, L] is USP_ERR_INVALID_ARG. */
+ * a row range outside [0, L] is USP_ERR_INVALID_ARG.  An empty row range
+ * changes nothing; with B or L = 0 the pointers may be NULL. */
 usp_status usp_lse_merge(float* out_acc, float* lse_acc, const float* out_part, const float* lse_part,
                          int64_t B, int64_t L, int64_t H, int64_t D, int64_t row_begin,
                          int64_t row_end, void* stream);

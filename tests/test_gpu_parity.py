@@ -236,6 +236,54 @@ def test_lse_merge_kernel(D):
     assert float((o - O_exp).abs().max()) < 1e-5
 
 
+# ---------------------------------------------------------------- zero-length inputs
+@pytest.mark.parametrize("D", [64, 128])
+def test_block_attn_zero_length(D):
+    """A step with no keys: every row has no visible key, so its partial is
+    (O = 0, LSE = -inf), the empty-row convention of the definition, and
+    merging it changes nothing; a step with no queries enqueues nothing."""
+    say(f"zero-length block D={D}")
+    g = torch.Generator().manual_seed(5)
+    q = torch.randn(2, 70, 4, D, generator=g).to(torch.bfloat16).cuda()
+    k0 = torch.empty(2, 0, 2, D, dtype=torch.bfloat16, device="cuda")
+    for mask in ("full", "causal", "empty"):
+        out = torch.full((2, 70, 4, D), 7.0, device="cuda")
+        lse = torch.full((2, 4, 70), 7.0, device="cuda")
+        usp.block_attn_fwd(q, k0, k0, mask=mask, out=out, lse=lse)
+        torch.cuda.synchronize()
+        assert torch.equal(out.cpu(), torch.zeros(2, 70, 4, D)), mask
+        assert bool(torch.all(torch.isneginf(lse.cpu()))), mask
+    # accumulate: the empty partial leaves the running result as it was
+    out = torch.randn(2, 70, 4, D, generator=g).cuda()
+    lse = torch.randn(2, 4, 70, generator=g).cuda()
+    o0, l0 = out.clone(), lse.clone()
+    usp.block_attn_fwd(q, k0, k0, mask="full", accumulate=True, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o0) and torch.equal(lse, l0)
+    # no queries
+    qe = torch.empty(2, 0, 4, D, dtype=torch.bfloat16, device="cuda")
+    k = torch.randn(2, 33, 2, D, generator=g).to(torch.bfloat16).cuda()
+    oe, le = usp.block_attn_fwd(qe, k, k, mask="full")
+    torch.cuda.synchronize()
+    assert oe.shape == (2, 0, 4, D) and le.shape == (2, 4, 0)
+
+
+def test_copy_and_merge_zero_length():
+    """Permute of zero batch rows and a merge over an empty row range change nothing."""
+    say("zero-length permute / merge")
+    x = torch.empty(0, 64, 3, 8, dtype=torch.bfloat16, device="cuda")
+    y = usp.permute(x, "zigzag", 4)
+    torch.cuda.synchronize()
+    assert y.shape == x.shape
+    g = torch.Generator().manual_seed(6)
+    oa = torch.randn(1, 40, 2, 64, generator=g).cuda()
+    la = torch.randn(1, 2, 40, generator=g).cuda()
+    o0, l0 = oa.clone(), la.clone()
+    usp.lse_merge(oa, la, torch.randn_like(oa), torch.randn_like(la), 17, 17)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, o0) and torch.equal(la, l0)
+
+
 # ---------------------------------------------------------------- virtual ring, end to end
 def _run_ring(w: si.Workload, q, k, v, **kw):
     call = usp.RingCall(q.cuda(), k.cuda(), v.cuda(), impl=w.impl, ring_degree=w.ring_degree,

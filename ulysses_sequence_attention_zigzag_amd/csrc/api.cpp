@@ -277,8 +277,8 @@ const char* usp_version(void) { return "usp-gfx950 0.1"; }
 usp_status usp_permute(const void* in, void* out, int64_t outer, int64_t S, int64_t inner,
                        usp_dtype dt, usp_ring_impl impl, int ring_degree, int ulysses_degree,
                        int stripe_block, int rank, int inverse, void* stream) {
-  USP_CHECK(in && out, USP_ERR_INVALID_ARG, "null tensor pointer");
   USP_CHECK(outer >= 0 && inner >= 1, USP_ERR_INVALID_ARG, "bad outer/inner sizes");
+  USP_CHECK((in && out) || outer == 0, USP_ERR_INVALID_ARG, "null tensor pointer");
   USP_CHECK(dt == USP_DT_BF16 || dt == USP_DT_F32, USP_ERR_INVALID_ARG, "bad dtype %d", (int)dt);
   usp_status st = check_layout(impl, S, ring_degree, stripe_block);
   if (st != USP_OK) return st;
@@ -331,8 +331,8 @@ usp_status usp_ulysses_relayout(void* const* shards, void* local, int64_t B, int
 usp_status usp_lse_merge(float* out_acc, float* lse_acc, const float* out_part, const float* lse_part,
                          int64_t B, int64_t L, int64_t H, int64_t D, int64_t row_begin,
                          int64_t row_end, void* stream) {
-  USP_CHECK(out_acc && lse_acc && out_part && lse_part, USP_ERR_INVALID_ARG, "null pointer");
   USP_CHECK(B >= 0 && L >= 0 && H >= 1, USP_ERR_INVALID_ARG, "bad sizes");
+  USP_CHECK((out_acc && lse_acc && out_part && lse_part) || B * L == 0, USP_ERR_INVALID_ARG, "null pointer");
   USP_CHECK(D >= 4 && D % 4 == 0 && 64 % (D / 4) == 0, USP_ERR_UNSUPPORTED,
             "merge supports D with D/4 dividing 64 (D = 4, 8, ..., 256; got %lld)", (long long)D);
   USP_CHECK(0 <= row_begin && row_begin <= row_end && row_end <= L, USP_ERR_INVALID_ARG,
@@ -413,8 +413,10 @@ usp_status usp_block_attn_fwd(const void* q, const void* k, const void* v, void*
                               const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int nseq,
                               usp_dtype out_dt, int accumulate, float softcap, const float* alibi_slopes,
                               void* stream) {
-  USP_CHECK(q && k && v && out && lse, USP_ERR_INVALID_ARG, "null tensor pointer");
   USP_CHECK(B >= 1 && Lq >= 0 && Lk >= 0 && Hq >= 1 && Hkv >= 1, USP_ERR_INVALID_ARG, "bad sizes");
+  // k / v are never read without keys, q / out / lse never touched without queries
+  USP_CHECK((q && out && lse) || Lq == 0, USP_ERR_INVALID_ARG, "null q / out / lse pointer");
+  USP_CHECK((k && v) || Lk == 0, USP_ERR_INVALID_ARG, "null k / v pointer");
   USP_CHECK(D == 64 || D == 128, USP_ERR_UNSUPPORTED, "head_dim must be 64 or 128, got %lld", (long long)D);
   USP_CHECK(Hq % Hkv == 0, USP_ERR_INVALID_ARG, "Hq (%lld) must be a multiple of Hkv (%lld)", (long long)Hq, (long long)Hkv);
   USP_CHECK(out_dt == USP_DT_BF16 || out_dt == USP_DT_F32, USP_ERR_INVALID_ARG, "bad out dtype");

@@ -89,6 +89,14 @@ def visible_pairs_per_head(w, rank_rows=None) -> int:
         return 2 * N * c * c + c
     if w.impl == "stripe" and w.stripe_block == 1:
         return N * L * (L - 1) // 2 + (w.rank + 1) * L
+    if w.impl == "stripe":
+        # striped blocks of b tokens: local row t = j*b + o of rank r sits at
+        # position p = (j*N + r)*b + o and sees the p + 1 keys 0..p; summed
+        # over j < L/b and o < b
+        b, r = w.stripe_block, w.rank
+        nb = L // b
+        sum_j = nb * (nb - 1) // 2
+        return b * b * N * sum_j + nb * b * r * b + nb * (b * (b - 1) // 2) + L
     raise ValueError("no closed form for this workload")
 
 
@@ -300,6 +308,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="usp_zigzag_gqa")
     ap.add_argument("--merge-mode", type=int, default=0)
+    ap.add_argument("--stripe-block", type=int, default=0,
+                    help="striped workload only: tokens per stripe block (0: the workload's own, 1); b > 1 runs "
+                         "the kernel form for stepped masks")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pass", dest="which", choices=["forward", "backward", "decode"], default="forward",
@@ -339,6 +350,11 @@ def main():
     if args.which == "decode":
         return bench_decode(args)
     w = si.WORKLOADS[args.workload]
+    if args.stripe_block:
+        if w.impl != "stripe":
+            print("--stripe-block applies to the striped workload only", file=sys.stderr)
+            sys.exit(2)
+        w = w.scaled(stripe_block=args.stripe_block)
     t0 = time.perf_counter()
     q, k, v = w.make_inputs()
     t_gen = time.perf_counter() - t0
@@ -400,6 +416,7 @@ def main():
             "workload": w.name,
             "B": w.B, "S_global": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
             "ring_impl": w.impl, "ring_degree": w.ring_degree, "ulysses_degree": w.ulysses_degree,
+            "stripe_block": w.stripe_block,
             "rank": w.rank, "ulysses_rank": w.ulysses_rank, "causal": w.causal, "window": w.window,
             "n_sink": w.n_sink, "cu_seqlens": w.cu_seqlens, "merge_mode": args.merge_mode,
             "mask_adjusted_tflop_per_step": round(flops / 1e12, 4),
@@ -411,9 +428,10 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4) if attn_tflops else None,
-            "traffic": measured_traffic(w.name),
+            # the counter record covers the workloads' own (linear-position) kernel form
+            "traffic": measured_traffic(w.name) if w.stripe_block == 1 else None,
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-            "kernel": "attn_fwd_kernel<%d>" % w.D,
+            "kernel": "attn_fwd_kernel<%d%s>" % (w.D, "" if w.stripe_block == 1 else ", stepped"),
             "launches_per_step": attn_n // max(1, args.steps),
             "kernel_ms_per_step": round(attn_ms_step, 4),
         },
@@ -498,6 +516,7 @@ def bench_backward(args, w, q, k, v, qd, kd, vd):
             "workload": w.name, "pass": "backward",
             "B": w.B, "S_global": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
             "ring_impl": w.impl, "ring_degree": w.ring_degree, "ulysses_degree": w.ulysses_degree,
+            "stripe_block": w.stripe_block,
             "rank": w.rank, "ulysses_rank": w.ulysses_rank, "causal": w.causal, "window": w.window,
             "n_sink": w.n_sink, "cu_seqlens": w.cu_seqlens,
             "algorithmic_tflop_per_step": round(flops / 1e12, 4),

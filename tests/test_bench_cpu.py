@@ -32,7 +32,10 @@ def _rank_pairs(w):
     si.WORKLOADS["usp_zigzag_gqa"].scaled(S=2048, rank=3),
     si.WORKLOADS["stripe_mqa"].scaled(S=2048),
     si.WORKLOADS["stripe_mqa"].scaled(S=2048, rank=7),
-], ids=lambda w: f"{w.name}-r{w.rank}")
+    si.WORKLOADS["stripe_mqa"].scaled(S=2048, stripe_block=4),
+    si.WORKLOADS["stripe_mqa"].scaled(S=4096, stripe_block=16, rank=5),
+    si.WORKLOADS["stripe_mqa"].scaled(S=2048, stripe_block=2, ring_degree=4, rank=3),
+], ids=lambda w: f"{w.name}-b{w.stripe_block}-r{w.rank}")
 def test_one_rank_pair_count_matches_oracle(w):
     assert bench.visible_pairs_per_head(w) == _rank_pairs(w)
 

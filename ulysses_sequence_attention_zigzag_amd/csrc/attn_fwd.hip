@@ -1,7 +1,7 @@
 // Block attention forward for one ring step on gfx950 (CDNA4).
 //
 // One workgroup = 8 waves = 256 query rows of one (batch, head); each wave
-// owns 32 rows.  Per key tile (128 keys, or 64 for striped blocks):
+// owns 32 rows.  Per key tile (128 keys):
 //   S^T = K Q^T      v_mfma_f32_32x32x16_bf16, K from LDS (A operand),
 //                    Q resident in VGPRs (B operand);
 //   mask             only in partial runs (the planner marks fully visible
@@ -54,14 +54,6 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Floor / ceiling of a / b for b >= 1 (a of either sign).
-__device__ __forceinline__ int32_t floor_div(int32_t a, int32_t b) {
-  if (b == 1) return a;
-  const int32_t q = a / b;
-  return (a % b != 0 && a < 0) ? q - 1 : q;
-}
-__device__ __forceinline__ int32_t ceil_div(int32_t a, int32_t b) { return -floor_div(-a, b); }
-
 // LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
 // lanes, lane i supplies the address of 4 consecutive bf16 (row i/4 of a
 // 4 x 16 block, columns 4*(i%4)..+3); lane j receives column j of the block,
@@ -95,9 +87,10 @@ struct TileLayout {
   __device__ static __forceinline__ int swz_v(int r) { return 4 * ((r / RPL) & (CPR / 4 - 1)); }
 };
 
-// LINEAR: key positions step linearly through every run (all layouts except
-// striped blocks of more than one token), which keeps the partial-tile mask
-// to interval compares.
+// Masks.  Key positions increase through every run of the plan for every
+// layout (striped blocks of any size included), so the keys a query sees in a
+// partial tile form at most two intervals (window band, sinks), found once
+// per tile through the inverse of the position map.
 //
 // Wave roles.  The workgroup is 8 waves in two groups of 4 (waves 0-3 and
 // 4-7); the hardware places wave w and wave w + 4 on the same SIMD.  Each
@@ -114,18 +107,11 @@ struct TileLayout {
 // reading, and waits for them at the end of its V(t), before the barrier
 // that hands the phase over.  Phase barriers carry no memory fence: every
 // LDS read of a matrix phase is consumed by its MFMAs before the phase ends.
-template <int D, bool LINEAR, int MODS>
+template <int D, int MODS>
 __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
   using TL = TileLayout<D>;
-  // Keys per tile.  The LINEAR kernel stages its tiles with buffer loads
-  // straight into LDS and runs 128-key tiles; the other kernel (striped
-  // blocks of more than one token) needs more registers for its mask, spills
-  // a little, and keeps the register-staged path with 64-key tiles (a spill
-  // reload tracked by the same counter as an in-flight LDS load is not a
-  // combination this kernel relies on).  The planner's full runs come in
-  // multiples of kTileN, which both divide.
-  constexpr int BN = LINEAR ? 128 : 64;
-  constexpr bool kDma = LINEAR;
+  // Keys per tile; the planner's full runs come in multiples of kTileN.
+  constexpr int BN = 128;
   static_assert(kTileN % BN == 0, "planner granularity");
   constexpr int KS = D / 16;        // k-steps of the QK^T contraction
   constexpr int DB = D / 32;        // 32-wide blocks of the output's head dim
@@ -213,7 +199,6 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
     vis_lo = p.mask.window > 0 ? max(s0, pq - p.mask.window + 1) : s0;
     sink_hi = p.mask.window > 0 ? min(s0 + p.mask.n_sink - 1, vis_hi) : s0 - 1;
   }
-  const int32_t kv_step = km.kind == MAP_STRIPE ? km.N : 1;
 
   const int64_t kv_row_stride = (int64_t)p.Hkv * D;
   const uint16_t* kbase = p.k + (int64_t)b * p.kv_batch_stride + (int64_t)it.k_row0 * kv_row_stride + hk * D;
@@ -234,20 +219,6 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(grp ? vbase : kbase), (short)0, 0x7fffffff, kBufferRsrcWord3);
   char* const stage_tiles = smem + grp * 2 * TILEB;
-  auto load_tile = [&](i32x4 (&r)[LPT], int k0, int kend) {
-#pragma unroll
-    for (int j = 0; j < LPT; ++j) {
-      const int row = (wg * LPT + j) * RPI + lrow;
-      const int sw = grp ? TL::swz_v(row) : TL::swz_k(row);
-      const uint32_t off = (uint32_t)min(k0 + row, kend - 1) * row_bytes + (uint32_t)((lslot ^ sw) * 16);
-      r[j] = __builtin_amdgcn_raw_buffer_load_b128(srs, off, 0, 0);
-    }
-  };
-  auto store_tile = [&](char* tile, const i32x4 (&r)[LPT]) {
-#pragma unroll
-    for (int j = 0; j < LPT; ++j)
-      *reinterpret_cast<i32x4*>(tile + (wg * LPT + j) * 1024 + lane * 16) = r[j];
-  };
   auto dma_tile = [&](char* tile, int k0, int kend) {
 #pragma unroll
     for (int j = 0; j < LPT; ++j) {
@@ -397,38 +368,24 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
 
   // Per-element mask of a partial tile starting at key k0.  Element (kb, r)
   // of this lane is key k0 + du with du = c + 4*hi, c = kb*32 + 8*(r/4) + r%4.
-  // For layouts whose key positions step linearly through a run, the visible
-  // du form at most two intervals (window band, sinks); their bounds are
-  // computed once, shifted by 4*hi, and compared with the compile-time c.
+  // Key positions increase with du, so the visible du form at most two
+  // intervals (window band, sinks); their bounds come from the inverse of
+  // the position map once per tile, shifted by 4*hi, and are compared with
+  // the compile-time c.
   auto apply_mask = [&](f32x16 (&sc)[NB], int k0, int kend) {
     const int32_t kend_du = kend - 1 - k0;
-    if constexpr (LINEAR) {
-      const int32_t pk0 = position(km, k0);
-      const int32_t sh = 4 * hi;
-      const int32_t lo = ceil_div(vis_lo - pk0, kv_step) - sh;
-      const int32_t up = min(floor_div(vis_hi - pk0, kv_step), kend_du) - sh;
-      const int32_t slo = ceil_div(sstart - pk0, kv_step) - sh;
-      const int32_t sup = min(floor_div(sink_hi - pk0, kv_step), kend_du) - sh;
+    const int32_t sh = k0 + 4 * hi;
+    const int32_t lo = first_row_at_least(km, k0, vis_lo) - sh;
+    const int32_t up = min(first_row_at_least(km, k0, vis_hi + 1) - 1 - k0, kend_du) - 4 * hi;
+    const int32_t slo = first_row_at_least(km, k0, sstart) - sh;
+    const int32_t sup = min(first_row_at_least(km, k0, sink_hi + 1) - 1 - k0, kend_du) - 4 * hi;
 #pragma unroll
-      for (int kb = 0; kb < NB; ++kb) {
+    for (int kb = 0; kb < NB; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
-          const bool vis = ((c >= lo) & (c <= up)) | ((c >= slo) & (c <= sup));
-          sc[kb][r] = vis ? sc[kb][r] : -INFINITY;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < NB; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int du = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const int32_t pk = position(km, k0 + du);
-          const bool vis = (du <= kend_du) & (pk <= vis_hi) &
-                           ((pk >= vis_lo) | ((pk >= sstart) & (pk <= sink_hi)));
-          sc[kb][r] = vis ? sc[kb][r] : -INFINITY;
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
+        const bool vis = ((c >= lo) & (c <= up)) | ((c >= slo) & (c <= sup));
+        sc[kb][r] = vis ? sc[kb][r] : -INFINITY;
       }
     }
   };
@@ -445,22 +402,15 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
     int ri = it.run_begin;
     Run run = p.runs[ri];
     int k0 = run.k_begin;
-    if constexpr (kDma) {
-      dma_tile(stage_tiles, k0, run.k_end);
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    } else {
-      i32x4 r0[LPT];
-      load_tile(r0, k0, run.k_end);
-      store_tile(stage_tiles, r0);
-    }
+    dma_tile(stage_tiles, k0, run.k_end);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
 
     f32x16 s[NB];
     bf16x8 pb[NB][2];
-    i32x4 stg[LPT];  // register-staged tile t+1 (kernel without LDS loads)
     int nri = ri, nk0 = k0;
     Run nrun = run;
-    // Cursor of tile t+1 (and, register-staged, its global loads).
+    // Cursor of tile t+1.
     auto prefetch_next = [&]() {
       nk0 = k0 + BN;
       nri = ri;
@@ -470,7 +420,6 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
         nrun = p.runs[nri];
         nk0 = nrun.k_begin;
       }
-      if constexpr (!kDma) load_tile(stg, nk0, nrun.k_end);
     };
     // V(t): mask, online softmax (log2 domain, lazy rescale); tile t+1 lands.
     auto v_phase = [&](int t) {
@@ -515,10 +464,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
           for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
       }
       if (t + 1 < n_tiles) {
-        if constexpr (kDma)
-          __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this group's tile t+1 is in LDS
-        else
-          store_tile(stage_tiles + ((t + 1) & 1) * TILEB, stg);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this group's tile t+1 is in LDS
         ri = nri;
         run = nrun;
         k0 = nk0;
@@ -530,29 +476,20 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
     // Phase barrier: no memory fence (the matrix phase's LDS reads are all
     // consumed by its MFMAs before it ends, and tile loads are waited for
     // explicitly), only a compiler ordering point.
-    auto phase_barrier = [&]() {
-      if constexpr (kDma)
-        asm volatile("s_barrier" ::: "memory");
-      else
-        __syncthreads();  // also completes this wave's LDS stores of the staged tile
-    };
+    auto phase_barrier = [&]() { asm volatile("s_barrier" ::: "memory"); };
     // Group 1 starts one phase late (group 0 runs M(0) meanwhile) and group
     // 0 ends one phase early, so both pass the same number of barriers.
     if (grp == 1) phase_barrier();
     if (n_tiles > 1) prefetch_next();
     m_phase(F_{}, T_{}, nullptr, smem, s, pb);
-    if constexpr (kDma) {
-      if (n_tiles > 1) dma_tile(stage_tiles + TILEB, nk0, nrun.k_end);
-    }
+    if (n_tiles > 1) dma_tile(stage_tiles + TILEB, nk0, nrun.k_end);
     phase_barrier();
     v_phase(0);
     phase_barrier();
     for (int t = 1; t < n_tiles; ++t) {
       if (t + 1 < n_tiles) prefetch_next();
       m_phase(T_{}, T_{}, smem + (2 + ((t - 1) & 1)) * TILEB, smem + (t & 1) * TILEB, s, pb);
-      if constexpr (kDma) {
-        if (t + 1 < n_tiles) dma_tile(stage_tiles + ((t + 1) & 1) * TILEB, nk0, nrun.k_end);
-      }
+      if (t + 1 < n_tiles) dma_tile(stage_tiles + ((t + 1) & 1) * TILEB, nk0, nrun.k_end);
       phase_barrier();
       v_phase(t);
       phase_barrier();
@@ -627,21 +564,20 @@ usp_status launch_attn_fwd(const AttnParams& p, int D, hipStream_t stream) {
     return USP_ERR_UNSUPPORTED;
   }
   const dim3 grid((unsigned)total), block(512);
-  const bool linear = !(p.kmap.kind == MAP_STRIPE && p.kmap.b > 1);
   TimingScope ts(K_ATTN, stream);
   const int mods = mods_variant(p.mods);
-#define USP_LAUNCH(DD, LIN, M) hipLaunchKernelGGL((attn_fwd_kernel<DD, LIN, M>), grid, block, 0, stream, p)
-#define USP_LAUNCH_M(DD, LIN)                     \
-  switch (mods) {                                  \
-    case 0: USP_LAUNCH(DD, LIN, 0); break;         \
-    case 1: USP_LAUNCH(DD, LIN, 1); break;         \
-    case 2: USP_LAUNCH(DD, LIN, 2); break;         \
-    default: USP_LAUNCH(DD, LIN, 3); break;        \
+#define USP_LAUNCH(DD, M) hipLaunchKernelGGL((attn_fwd_kernel<DD, M>), grid, block, 0, stream, p)
+#define USP_LAUNCH_M(DD)                     \
+  switch (mods) {                             \
+    case 0: USP_LAUNCH(DD, 0); break;         \
+    case 1: USP_LAUNCH(DD, 1); break;         \
+    case 2: USP_LAUNCH(DD, 2); break;         \
+    default: USP_LAUNCH(DD, 3); break;        \
   }
   if (D == 128) {
-    if (linear) { USP_LAUNCH_M(128, true) } else { USP_LAUNCH_M(128, false) }
+    USP_LAUNCH_M(128)
   } else {
-    if (linear) { USP_LAUNCH_M(64, true) } else { USP_LAUNCH_M(64, false) }
+    USP_LAUNCH_M(64)
   }
 #undef USP_LAUNCH_M
 #undef USP_LAUNCH

@@ -69,23 +69,6 @@ __device__ __forceinline__ int32_t floor_div(int32_t a, int32_t b) {
 }
 __device__ __forceinline__ int32_t ceil_div(int32_t a, int32_t b) { return -floor_div(-a, b); }
 
-// Smallest local row t with position(m, t) >= P, for a row t_ref of the
-// same monotone piece (positions increase with t across a whole basic,
-// stripe or affine rank, and within each chunk of a zigzag rank, where
-// they are consecutive).  Stripe: the rank holds blocks j*N + rank (block
-// j at rows j*b ..); P in one of them maps to its row, otherwise to the
-// first row of the rank's next block.  Exact for every t of the piece;
-// callers clamp to the rows they hold.
-__device__ __forceinline__ int32_t first_row_at_least(const PosMap& m, int32_t t_ref, int32_t P) {
-  if (m.kind == MAP_STRIPE) {
-    const int32_t beta = floor_div(P, m.b);
-    const int32_t o = P - beta * m.b;
-    const int32_t j = floor_div(beta - m.rank, m.N);
-    return (j * m.N + m.rank == beta) ? j * m.b + o : (j + 1) * m.b;
-  }
-  return t_ref + (P - position(m, t_ref));
-}
-
 // Raw buffer resource of `base` (no stride, 2^31 - 1 bytes, no swizzle),
 // wave-uniform so it lives in SGPRs.
 __device__ __forceinline__ i32x4 buffer_rsrc(const void* base) {

@@ -45,6 +45,28 @@ __host__ __device__ inline int32_t position(const PosMap& m, int32_t t) {
   }
 }
 
+// Smallest local row t with position(m, t) >= P, for a row t_ref of the
+// same monotone piece (positions increase with t across a whole basic,
+// stripe or affine rank, and within each chunk of a zigzag rank, where
+// they are consecutive).  Stripe: the rank holds blocks j*N + rank (block
+// j at rows j*b ..); P in one of them maps to its row, otherwise to the
+// first row of the rank's next block.  Exact for every t of the piece;
+// callers clamp to the rows they hold.
+__host__ __device__ inline int32_t first_row_at_least(const PosMap& m, int32_t t_ref, int32_t P) {
+  if (m.kind == MAP_STRIPE) {
+    // floor divisions of possibly negative numerators by b, N >= 1
+    auto fdiv = [](int32_t a, int32_t d) {
+      const int32_t q = a / d;
+      return (a % d != 0 && a < 0) ? q - 1 : q;
+    };
+    const int32_t beta = fdiv(P, m.b);
+    const int32_t o = P - beta * m.b;
+    const int32_t j = fdiv(beta - m.rank, m.N);
+    return (j * m.N + m.rank == beta) ? j * m.b + o : (j + 1) * m.b;
+  }
+  return t_ref + (P - position(m, t_ref));
+}
+
 // Monotone pieces of a rank's local rows: positions increase with t inside
 // each piece.  Zigzag has two (its two chunks); the others one.
 inline int monotone_segments(const PosMap& m, int32_t seg_lo[2], int32_t seg_hi[2]) {

@@ -159,6 +159,11 @@ POSITIONAL = [
     ("basic", 4096, 4, 1, False, 300, 4, [0, 512, 2000, 4096], 2, 2, 128),
     ("basic", 3000, 3, 1, True, 0, 0, [0, 1, 700, 701, 2900, 3000], 2, 1, 64),
     ("zigzag", 3072, 4, 1, False, 300, 2, None, 2, 2, 128),
+    # striped blocks (stepped positions) under window, sink and varlen masks:
+    # partial tiles whose visible keys are intervals of the inverse position map
+    ("stripe", 4096, 4, 8, False, 300, 3, None, 2, 1, 128),
+    ("stripe", 3072, 4, 3, False, 250, 2, [0, 700, 2000, 3072], 2, 2, 128),
+    ("stripe", 2048, 8, 16, True, 0, 0, None, 4, 1, 128),
 ]
 
 

@@ -372,6 +372,19 @@ size_t usp_ring_bwd_workspace_size(const usp_ring_bwd_args* a);
  * usp_ring_bwd_workspace_size(a) bytes, 256-byte aligned. */
 usp_status usp_ring_bwd(const usp_ring_bwd_args* a, void* workspace, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------ tile plan cache
+ * usp_block_attn_fwd, usp_block_attn_bwd, usp_ring_fwd and usp_ring_bwd
+ * upload the tile plan of each distinct shape / mask / cu_seqlens once per
+ * device and keep it for the life of the process (a few int32 per tile).
+ * Callers that see many distinct plans (varlen batches with new cu_seqlens
+ * every step) can bound that memory: usp_plan_cache_size returns the number
+ * of cached plans, and usp_plan_cache_clear frees them all.  Clearing is
+ * for a quiet point: no enqueued call may still run on a cached plan (hipFree
+ * waits for the device), and no other thread may be inside a library call.
+ * Later calls rebuild what they need. */
+int64_t usp_plan_cache_size(void);
+usp_status usp_plan_cache_clear(void);
+
 /* ------------------------------------------------------ tile scheduler
  * Host-only inspection of the tile plan usp_block_attn_fwd would run (no
  * device work).  Items are 8 int32 each: {q_row0, t0, q_rows, q_rank, k_row0,

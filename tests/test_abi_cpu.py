@@ -139,6 +139,19 @@ def test_block_attn_validation():
     assert st == 2 and "ALiBi" in msg
 
 
+def test_plan_cache_host_planning_caches_nothing():
+    # clearing needs no device when nothing is cached; host-only planning
+    # (usp_plan_block) adds nothing to the device cache
+    usp.plan_cache_clear()
+    assert usp.plan_cache_size() == 0
+    n = ctypes.c_int64()
+    st = usp.lib().usp_plan_block(256, 256, 128, usp.MASK["causal"], None, None, 0, 0, 0, None, 0, 0,
+                                  None, 0, None, 0, ctypes.byref(n), ctypes.byref(ctypes.c_int64()),
+                                  ctypes.byref(ctypes.c_int32()), ctypes.byref(ctypes.c_int32()))
+    assert st == 0 and n.value > 0
+    assert usp.plan_cache_size() == 0
+
+
 def test_merge_validation():
     L = usp.lib()
     st, msg = _status(L.usp_lse_merge, FAKE, FAKE, FAKE, FAKE, 1, 10, 2, 128, 5, 11, None)

@@ -89,6 +89,8 @@ _SIGS = {
     "usp_decode_split_fwd": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64, ctypes.c_float,
                               _I32, _I32, ctypes.c_float, _P, _P], _I32),
     "usp_decode_merge": ([_P, _P, _I64, _I64, _I64, _I64, _I64, _P, _I32, _P, _P], _I32),
+    "usp_plan_cache_size": ([], _I64),
+    "usp_plan_cache_clear": ([], _I32),
     "usp_timing_enable": ([_I32], _I32),
     "usp_timing_reset": ([], _I32),
     "usp_timing_read": ([_I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64)], _I32),
@@ -478,6 +480,16 @@ KERNEL_CLASSES = {"attn": 0, "permute": 1, "relayout": 2, "merge": 3, "bwd_dq": 
 
 def timing_enable(on: bool = True) -> None:
     _check(lib().usp_timing_enable(int(on)))
+
+
+def plan_cache_size() -> int:
+    """Number of tile plans the library keeps on the devices (usp_plan_cache_size)."""
+    return int(lib().usp_plan_cache_size())
+
+
+def plan_cache_clear() -> None:
+    """Frees every cached tile plan (usp_plan_cache_clear); call at a quiet point."""
+    _check(lib().usp_plan_cache_clear())
 
 
 def timing_reset() -> None:

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -340,6 +341,30 @@ usp_status usp_lse_merge(float* out_acc, float* lse_acc, const float* out_part, 
   USP_CHECK(B * L * H <= kMaxI32, USP_ERR_UNSUPPORTED, "tensor too large");
   return launch_lse_merge(out_acc, lse_acc, out_part, lse_part, B, L, H, D, row_begin, row_end,
                           as_stream(stream));
+}
+
+int64_t usp_plan_cache_size(void) {
+  std::lock_guard<std::mutex> lock(g_plan_mu);
+  return (int64_t)g_plans.size();
+}
+
+usp_status usp_plan_cache_clear(void) {
+  std::lock_guard<std::mutex> lock(g_plan_mu);
+  usp_status st = USP_OK;
+  int cur = 0;
+  const bool have_dev = hipGetDevice(&cur) == hipSuccess;
+  for (auto& kv : g_plans) {
+    // the key starts with the plan's device ordinal
+    const int dev = std::atoi(kv.first.c_str());
+    if (have_dev && dev != cur) (void)hipSetDevice(dev);
+    if (hipFree(kv.second.items) != hipSuccess || hipFree(kv.second.runs) != hipSuccess) {
+      set_error("hipFree of a cached tile plan failed");
+      st = USP_ERR_HIP;
+    }
+  }
+  if (have_dev) (void)hipSetDevice(cur);
+  g_plans.clear();
+  return st;
 }
 
 usp_status usp_plan_block(int64_t Lq, int64_t Lk, int64_t D, usp_mask_class mask,

@@ -428,7 +428,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4) if attn_tflops else None,
-            # the counter record covers the workloads' own (linear-position) kernel form
+            # the counter record was taken on the workloads as defined (stripe block 1)
             "traffic": measured_traffic(w.name) if w.stripe_block == 1 else None,
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "kernel": "attn_fwd_kernel<%d%s>" % (w.D, "" if w.stripe_block == 1 else ", stepped"),

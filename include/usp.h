@@ -189,8 +189,8 @@ usp_status usp_block_attn_fwd(const void* q, const void* k, const void* v, void*
  * ring steps add up to the gradients of the whole attention.
  *
  * usp_attn_bwd_preprocess: delta [B,H,L] f32 = rowsum(dout * out), with out
- *   [B,L,H,D] in out_dt (bf16 or f32) and dout [B,L,H,D] bf16; D a multiple
- *   of 8 up to 256.
+ *   [B,L,H,D] in out_dt (bf16 or f32) and dout [B,L,H,D] bf16; D one of
+ *   8, 16, 32, 64, 128, 256 (D/8 threads share a row inside one wave).
  * usp_block_attn_bwd: q, dout [B,Lq,Hq,D] and k, v [B,Lk,Hkv,D] bf16; lse
  *   and delta [B,Hq,Lq] f32 (a row with LSE = -inf contributes nothing);
  *   dq [B,Lq,Hq,D], dk, dv [B,Lk,Hkv,D] f32 are ACCUMULATED into (+=): the

@@ -76,6 +76,8 @@ def test_preprocess_validation():
     assert st == 1 and "null" in msg
     st, msg = _status(L.usp_attn_bwd_preprocess, FAKE, 0, FAKE, FAKE, 1, 16, 2, 60, None)
     assert st == 2 and "head_dim" in msg
+    st, msg = _status(L.usp_attn_bwd_preprocess, FAKE, 0, FAKE, FAKE, 1, 16, 2, 96, None)
+    assert st == 2 and "head_dim" in msg   # D/8 threads of a row must fit one wave in powers of two
     st, msg = _status(L.usp_attn_bwd_preprocess, FAKE, 7, FAKE, FAKE, 1, 16, 2, 64, None)
     assert st == 1 and "dtype" in msg
     st, msg = _status(L.usp_attn_bwd_preprocess, FAKE, 0, FAKE, FAKE, 1, 16, 0, 64, None)

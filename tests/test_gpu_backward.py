@@ -64,7 +64,8 @@ def _delta(do, O):
 
 
 # ---------------------------------------------------------------- delta
-@pytest.mark.parametrize("B,L,H,D", [(1, 1, 1, 64), (2, 333, 3, 128), (1, 1000, 4, 64)])
+@pytest.mark.parametrize("B,L,H,D", [(1, 1, 1, 64), (2, 333, 3, 128), (1, 1000, 4, 64), (1, 77, 5, 8),
+                                     (2, 65, 3, 256)])
 @pytest.mark.parametrize("odt", [torch.float32, torch.bfloat16])
 def test_preprocess_delta(B, L, H, D, odt):
     say(f"delta B={B} L={L} H={H} D={D} {odt}")

@@ -504,7 +504,8 @@ usp_status usp_attn_bwd_preprocess(const void* out, usp_dtype out_dt, const void
                                    int64_t B, int64_t L, int64_t H, int64_t D, void* stream) {
   USP_CHECK(out && dout && delta, USP_ERR_INVALID_ARG, "null tensor pointer");
   USP_CHECK(B >= 0 && L >= 0 && H >= 1, USP_ERR_INVALID_ARG, "bad sizes");
-  USP_CHECK(D >= 8 && D % 8 == 0 && D <= 256, USP_ERR_UNSUPPORTED, "head_dim must be a multiple of 8 in [8, 256]");
+  USP_CHECK(D == 8 || D == 16 || D == 32 || D == 64 || D == 128 || D == 256, USP_ERR_UNSUPPORTED,
+            "head_dim must be 8, 16, 32, 64, 128 or 256");
   USP_CHECK(out_dt == USP_DT_BF16 || out_dt == USP_DT_F32, USP_ERR_INVALID_ARG, "bad out dtype");
   USP_CHECK(B * L * H <= kMaxI32 * 8, USP_ERR_UNSUPPORTED, "tensor too large");
   USP_CHECK(L <= kMaxI32, USP_ERR_UNSUPPORTED, "sequence too long");

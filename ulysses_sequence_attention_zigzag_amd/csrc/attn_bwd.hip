@@ -36,31 +36,38 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float4* p, int64_t n4) {
 }
 
 // ------------------------------------------------------------------ delta
-// delta[b, h, t] = sum_d dO[b, t, h, d] * O[b, t, h, d]; one thread per row.
+// delta[b, h, t] = sum_d dO[b, t, h, d] * O[b, t, h, d].  A group of D/8
+// threads per (row, head) reads 8 consecutive elements each (16 bytes of
+// dO, 32 or 16 of O), so a wave's loads are contiguous; the group (inside
+// one wave: D/8 divides 64) sums with cross-lane adds in a fixed order.
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const void* out, int out_f32, const uint16_t* dout,
                                                         float* delta, int64_t n_rows, int32_t L, int32_t H,
                                                         int32_t D) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= n_rows) return;
-  const int64_t bt = idx / H;
-  const int32_t h = (int32_t)(idx - bt * H);
-  const int64_t b = bt / L;
-  const int32_t t = (int32_t)(bt - b * L);
-  const uint16_t* dp = dout + idx * D;
+  const int32_t tpr = D / 8;
+  const int64_t idx = ((int64_t)blockIdx.x * 256 + threadIdx.x) / tpr;
+  const int32_t j = threadIdx.x % tpr;
+  const bool live = idx < n_rows;
   float acc = 0.f;
-  for (int d = 0; d < D; d += 8) {
-    const bf16x8 g = *reinterpret_cast<const bf16x8*>(dp + d);
+  if (live) {
+    const int64_t e0 = idx * D + j * 8;
+    const bf16x8 g = *reinterpret_cast<const bf16x8*>(dout + e0);
     if (out_f32) {
-      const float4 o0 = *reinterpret_cast<const float4*>(static_cast<const float*>(out) + idx * D + d);
-      const float4 o1 = *reinterpret_cast<const float4*>(static_cast<const float*>(out) + idx * D + d + 4);
-      acc += (float)g[0] * o0.x + (float)g[1] * o0.y + (float)g[2] * o0.z + (float)g[3] * o0.w;
+      const float4 o0 = *reinterpret_cast<const float4*>(static_cast<const float*>(out) + e0);
+      const float4 o1 = *reinterpret_cast<const float4*>(static_cast<const float*>(out) + e0 + 4);
+      acc = (float)g[0] * o0.x + (float)g[1] * o0.y + (float)g[2] * o0.z + (float)g[3] * o0.w;
       acc += (float)g[4] * o1.x + (float)g[5] * o1.y + (float)g[6] * o1.z + (float)g[7] * o1.w;
     } else {
-      const bf16x8 o = *reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(out) + idx * D + d);
+      const bf16x8 o = *reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(out) + e0);
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc += (float)g[e] * (float)o[e];
     }
   }
+  for (int32_t off = tpr >> 1; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (!live || j != 0) return;
+  const int64_t bt = idx / H;
+  const int32_t h = (int32_t)(idx - bt * H);
+  const int64_t b = bt / L;
+  const int32_t t = (int32_t)(bt - b * L);
   delta[(b * H + h) * L + t] = acc;
 }
 
@@ -441,8 +448,9 @@ usp_status launch_bwd_delta(const void* out, int out_f32, const uint16_t* dout, 
   if (n == 0) return USP_OK;
   {
     TimingScope ts(K_BWD_DELTA, stream);
-    hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, out, out_f32,
-                       dout, delta, n, (int32_t)L, (int32_t)H, (int32_t)D);
+    const int64_t threads = n * (D / 8);
+    hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, out,
+                       out_f32, dout, delta, n, (int32_t)L, (int32_t)H, (int32_t)D);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {

@@ -107,7 +107,7 @@ struct TileLayout {
 // reading, and waits for them at the end of its V(t), before the barrier
 // that hands the phase over.  Phase barriers carry no memory fence: every
 // LDS read of a matrix phase is consumed by its MFMAs before the phase ends.
-template <int D, int MODS>
+template <int D, int MODS, bool WIN>
 __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
   using TL = TileLayout<D>;
   // Keys per tile; the planner's full runs come in multiples of kTileN.
@@ -379,8 +379,24 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
     const int32_t up = min(first_row_at_least(km, k0, vis_hi + 1) - 1 - k0, kend_du) - 4 * hi;
     const int32_t slo = first_row_at_least(km, k0, sstart) - sh;
     const int32_t sup = min(first_row_at_least(km, k0, sink_hi + 1) - 1 - k0, kend_du) - 4 * hi;
+    // With a window (WIN) most of a partial tile's 32-key blocks are
+    // visible or hidden as a whole for every lane of the wave: such a block
+    // takes no per-element mask (wave-uniform branches).  Without one the
+    // partial tiles are the few along a causal diagonal, and the plain mask
+    // keeps the kernel's code as it is.
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb) {
+      if constexpr (WIN) {
+        const int cmin = kb * 32, cmax = kb * 32 + 27;  // this lane's keys of the block
+        const bool all_vis = ((lo <= cmin) & (cmax <= up)) | ((slo <= cmin) & (cmax <= sup));
+        const bool none_vis = ((up < cmin) | (lo > cmax)) & ((sup < cmin) | (slo > cmax));
+        if (__builtin_amdgcn_readfirstlane((int)(__ballot(!all_vis) == 0ull))) continue;
+        if (__builtin_amdgcn_readfirstlane((int)(__ballot(!none_vis) == 0ull))) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sc[kb][r] = -INFINITY;
+          continue;
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
@@ -566,18 +582,19 @@ usp_status launch_attn_fwd(const AttnParams& p, int D, hipStream_t stream) {
   const dim3 grid((unsigned)total), block(512);
   TimingScope ts(K_ATTN, stream);
   const int mods = mods_variant(p.mods);
-#define USP_LAUNCH(DD, M) hipLaunchKernelGGL((attn_fwd_kernel<DD, M>), grid, block, 0, stream, p)
-#define USP_LAUNCH_M(DD)                     \
-  switch (mods) {                             \
-    case 0: USP_LAUNCH(DD, 0); break;         \
-    case 1: USP_LAUNCH(DD, 1); break;         \
-    case 2: USP_LAUNCH(DD, 2); break;         \
-    default: USP_LAUNCH(DD, 3); break;        \
+  const bool win = p.mask.window > 0;
+#define USP_LAUNCH(DD, M, W) hipLaunchKernelGGL((attn_fwd_kernel<DD, M, W>), grid, block, 0, stream, p)
+#define USP_LAUNCH_M(DD, W)                     \
+  switch (mods) {                                \
+    case 0: USP_LAUNCH(DD, 0, W); break;         \
+    case 1: USP_LAUNCH(DD, 1, W); break;         \
+    case 2: USP_LAUNCH(DD, 2, W); break;         \
+    default: USP_LAUNCH(DD, 3, W); break;        \
   }
   if (D == 128) {
-    USP_LAUNCH_M(128)
+    if (win) { USP_LAUNCH_M(128, true) } else { USP_LAUNCH_M(128, false) }
   } else {
-    USP_LAUNCH_M(64)
+    if (win) { USP_LAUNCH_M(64, true) } else { USP_LAUNCH_M(64, false) }
   }
 #undef USP_LAUNCH_M
 #undef USP_LAUNCH

@@ -164,6 +164,9 @@ POSITIONAL = [
     ("stripe", 4096, 4, 8, False, 300, 3, None, 2, 1, 128),
     ("stripe", 3072, 4, 3, False, 250, 2, [0, 700, 2000, 3072], 2, 2, 128),
     ("stripe", 2048, 8, 16, True, 0, 0, None, 4, 1, 128),
+    # window masks at D = 64 (the kernel's windowed instantiation)
+    ("basic", 4096, 4, 1, False, 200, 2, [0, 300, 2500, 4096], 4, 2, 64),
+    ("zigzag", 2048, 2, 1, False, 700, 0, None, 2, 1, 64),
 ]
 
 

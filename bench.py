@@ -308,6 +308,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="usp_zigzag_gqa")
     ap.add_argument("--merge-mode", type=int, default=0)
+    ap.add_argument("--graph", action="store_true",
+                    help="forward: also time the ring call replayed from a HIP graph (graph_replay in the JSON; "
+                         "value stays the eager rate)")
     ap.add_argument("--stripe-block", type=int, default=0,
                     help="striped workload only: tokens per stripe block (0: the workload's own, 1); b > 1 runs "
                          "the kernel form for stepped masks")
@@ -395,6 +398,18 @@ def main():
     perm_bytes, _ = step_bytes(w)
     perm_ms = kt["permute"][0] / args.steps
     merge_rec = time_lse_merge(w, args.merge_mode, kt["merge"])
+    graph_rec = None
+    if args.graph:
+        graph = call.capture()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        g_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        graph_rec = {"ms_per_step": round(g_ms, 4), "TFLOP/s": None}
 
     def gbs(b, ms):
         return round(b / (ms * 1e-3) / 1e9, 1) if ms > 0 and b > 0 else None
@@ -445,6 +460,9 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if graph_rec is not None:
+        graph_rec["TFLOP/s"] = round(flops / (graph_rec["ms_per_step"] * 1e-3) / 1e12, 2)
+        rec["graph_replay"] = graph_rec
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
     print(json.dumps(rec), flush=True)

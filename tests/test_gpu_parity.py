@@ -244,6 +244,35 @@ def test_lse_merge_kernel(D):
     assert float((o - O_exp).abs().max()) < 1e-5
 
 
+# ---------------------------------------------------------------- HIP graph
+@pytest.mark.parametrize("w", [si.WORKLOADS["zigzag_causal_small"],
+                               si.WORKLOADS["usp_zigzag_gqa"].scaled(S=4096, Hq=8, Hkv=4)],
+                         ids=lambda w: w.name)
+def test_ring_graph_replay(w):
+    """usp_ring_fwd recorded into a HIP graph: every replay, with eager calls
+    and synchronisations between them, gives the eager result bit for bit."""
+    say(f"graph replay {w.name}")
+    q, k, v = w.make_inputs()
+    call = usp.RingCall(q.cuda(), k.cuda(), v.cuda(), impl=w.impl, ring_degree=w.ring_degree,
+                        ulysses_degree=w.ulysses_degree, causal=w.causal, softmax_scale=w.softmax_scale or 0.0,
+                        rank=w.rank, ulysses_rank=w.ulysses_rank)
+    out, lse = call.run()
+    torch.cuda.synchronize()
+    ref_o, ref_l = out.cpu().clone(), lse.cpu().clone()
+    O_ref, L_ref = _oracle_share(w, q, k, v)
+    assert_parity(ref_o, ref_l, O_ref, L_ref, "eager")
+    graph = call.capture()
+    for i in range(3):
+        call.out.zero_()
+        call.lse.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(call.out.cpu(), ref_o) and torch.equal(call.lse.cpu(), ref_l), f"replay {i}"
+        call.run()                      # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(call.out.cpu(), ref_o) and torch.equal(call.lse.cpu(), ref_l), f"eager {i}"
+
+
 # ---------------------------------------------------------------- plan cache
 def test_plan_cache_clear_and_rebuild():
     """Cached tile plans can be freed at a quiet point; the next call rebuilds

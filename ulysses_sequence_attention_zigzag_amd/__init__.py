@@ -425,6 +425,18 @@ class RingCall:
         _check(lib().usp_ring_fwd(ctypes.byref(self.args), ws, self.ws_bytes, _stream(stream)))
         return self.out, self.lse
 
+    def capture(self) -> "torch.cuda.CUDAGraph":
+        """Records one usp_ring_fwd call into a HIP graph (torch.cuda.CUDAGraph) over this call's
+        buffers.  A warm call first builds and uploads the tile plans (the only synchronous work);
+        the recorded call then enqueues kernels only.  ``graph.replay()`` reruns it on the same
+        inputs / outputs."""
+        self.run()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.run(stream=torch.cuda.current_stream())
+        return graph
+
 
 class RingBwdCall:
     """A prepared usp_ring_bwd call for the forward described by ``fwd`` (a

@@ -352,10 +352,24 @@ def test_ring_fwd_then_bwd_end_to_end(w):
                        softmax_scale=w.softmax_scale or 0.0, rank=w.rank, ulysses_rank=w.ulysses_rank,
                        out_dtype=torch.bfloat16)
     fwd.run()
-    got = usp.RingBwdCall(fwd, dout.cuda()).run()
+    bwd = usp.RingBwdCall(fwd, dout.cuda())
+    got = bwd.run()
     torch.cuda.synchronize()
     for g, r, name in zip(got, ref, ("dq", "dk", "dv")):
         assert_grad(g, r, name)
+    # the same backward replayed from a HIP graph, with eager calls between
+    # replays: the eager bits every time
+    eager = [g.cpu().clone() for g in got]
+    graph = bwd.capture()
+    for i in range(2):
+        for g in (bwd.dq, bwd.dk, bwd.dv):
+            g.fill_(3.0)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(g.cpu(), e) for g, e in zip((bwd.dq, bwd.dk, bwd.dv), eager)), f"replay {i}"
+        bwd.run()
+        torch.cuda.synchronize()
+        assert all(torch.equal(g.cpu(), e) for g, e in zip((bwd.dq, bwd.dk, bwd.dv), eager)), f"eager {i}"
 
 
 @pytest.mark.parametrize("w", [RING_BWD[0], RING_BWD[2], si.WORKLOADS["usp_zigzag_gqa"].scaled(S=4096, Hq=4, Hkv=4,

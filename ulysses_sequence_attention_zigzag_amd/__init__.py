@@ -476,6 +476,17 @@ class RingBwdCall:
                                   self.ws_bytes, _stream(stream)))
         return self.dq, self.dk, self.dv
 
+    def capture(self) -> "torch.cuda.CUDAGraph":
+        """Records one usp_ring_bwd call into a HIP graph, after a warm call that builds the plans
+        (see RingCall.capture); the gradients are zeroed by a kernel inside the call, so replays
+        recompute them."""
+        self.run()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.run(stream=torch.cuda.current_stream())
+        return graph
+
 
 def ring_fwd(q, k, v, **kw) -> Tuple[torch.Tensor, torch.Tensor]:
     """All ring steps on one device (usp_ring_fwd); see RingCall for arguments."""

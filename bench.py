@@ -309,8 +309,8 @@ def main():
     ap.add_argument("--workload", default="usp_zigzag_gqa")
     ap.add_argument("--merge-mode", type=int, default=0)
     ap.add_argument("--graph", action="store_true",
-                    help="forward: also time the ring call replayed from a HIP graph (graph_replay in the JSON; "
-                         "value stays the eager rate)")
+                    help="forward / decode: also time the step replayed from a HIP graph (graph_replay in the "
+                         "JSON; value stays the eager rate)")
     ap.add_argument("--stripe-block", type=int, default=0,
                     help="striped workload only: tokens per stripe block (0: the workload's own, 1); b > 1 runs "
                          "the kernel form for stepped masks")
@@ -638,6 +638,19 @@ def bench_decode(args):
     usp.timing_reset()
     split_ms /= args.steps
     merge_ms /= args.steps
+    graph_ms = None
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     kv_bytes = 2 * B * S * Hkv * D * 2
     part_bytes = n * B * Lq * Hq * (D + 1) * 4
     split_bytes = kv_bytes + B * Lq * Hq * D * 2 + part_bytes          # read K, V, q; write partials
@@ -672,6 +685,9 @@ def bench_decode(args):
         "merge_ms_per_step": round(merge_ms, 4),
         "cpu_baseline": None,
     }
+    if graph_ms is not None:
+        rec["graph_replay"] = {"ms_per_step": round(graph_ms, 4),
+                               "GB/s": round(step_bytes / (graph_ms * 1e-3) / 1e9, 1)}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline_decode(cfg, q, k, v, args.cpu_budget)
     print(json.dumps(rec), flush=True)

@@ -146,3 +146,40 @@ def test_decode_score_mods(case, softcap, alibi):
     _check(out, lse, O_ref, L_ref, "merged")
     O0, _ = decode_ref(q, k, v, lens, softmax_scale=scale, window=window, n_sink=n_sink)
     assert float((O0 - O_ref).abs().max()) > 10 * OUT_TOL   # the modifiers matter here
+
+
+def test_decode_graph_replay():
+    """A decode step (split kernel + merge) recorded into a HIP graph: every
+    replay, with eager steps between, gives the eager bits."""
+    say("decode graph replay")
+    B, S, Lq, Hq, Hkv, D = 2, 8192, 1, 8, 2, 128
+    q, k, v = _cache(B, S, Lq, Hq, Hkv, D, seed=47)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    split = 512
+    n = S // split
+    op = torch.empty((n, B, Lq, Hq, D), dtype=torch.float32, device="cuda")
+    lp = torch.empty((n, B, Hq, Lq), dtype=torch.float32, device="cuda")
+    out = torch.empty((B, Lq, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device="cuda")
+
+    def step():
+        usp.decode_split_fwd(qd, kd, vd, split_keys=split, out_part=op, lse_part=lp)
+        usp.decode_merge(op, lp, out=out, lse=lse)
+
+    step()
+    torch.cuda.synchronize()
+    O_ref, L_ref = decode_ref(q, k, v)
+    _check(out, lse, O_ref, L_ref, "eager")
+    eo, el = out.cpu().clone(), lse.cpu().clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for i in range(3):
+        out.fill_(5.0)
+        lse.fill_(5.0)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.cpu(), eo) and torch.equal(lse.cpu(), el), f"replay {i}"
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(out.cpu(), eo) and torch.equal(lse.cpu(), el), f"eager {i}"

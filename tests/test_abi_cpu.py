@@ -152,6 +152,35 @@ def test_plan_cache_host_planning_caches_nothing():
     assert usp.plan_cache_size() == 0
 
 
+def test_size_limits_are_rejected_before_device_work():
+    """Shapes past the 32-bit offset limits fail validation (USP_ERR_UNSUPPORTED)
+    instead of launching; the pointers are never touched."""
+    L = usp.lib()
+    # block attention: one batch row of k/v over 2 GiB (2^24 keys x 1 head x 128 x 2 B)
+    st, msg = _attn(Lk=1 << 24, Hkv=1, Hq=1, mask=usp.MASK["full"])
+    assert st == 2 and "2 GiB" in msg
+    st, msg = _attn(B=1 << 16, Lq=1 << 16)
+    assert st == 2 and "too large" in msg
+    # permute: outer * S beyond the index range
+    st, msg = _status(L.usp_permute, FAKE, FAKE2, 1 << 20, 1 << 14, 8, 0, 0, 4, 1, 1, -1, 0, None)
+    assert st == 2 and "too large" in msg
+    # merge: more (batch, row, head) groups than 32-bit indices
+    st, msg = _status(L.usp_lse_merge, FAKE, FAKE, FAKE2, FAKE2, 1 << 12, 1 << 12, 1 << 8, 64, 0, 1 << 12, None)
+    assert st == 2 and "too large" in msg
+    # ring: one ring rank's k/v rows over 2 GiB
+    a = _ring_args(S=1 << 26, Hq=8, Hkv=8, impl=0, ring_degree=2, causal=1)
+    assert L.usp_ring_fwd_workspace_size(ctypes.byref(a)) == 0
+    st, msg = _status(L.usp_ring_fwd, ctypes.byref(a), None, 0, None)
+    assert st == 2 and "2 GiB" in msg, msg
+    # decode: one batch row of the cache over 2 GiB; more than 65535 batch rows
+    dec = lambda B, S: _status(L.usp_decode_split_fwd, FAKE, FAKE, FAKE, None, None, FAKE2, FAKE2,
+                               B, 1, S, 8, 1, 128, 1024, 0.0, 0, 0, 0.0, None, None)
+    st, msg = dec(1, 1 << 24)
+    assert st == 2 and "2 GiB" in msg, msg
+    st, msg = dec(1 << 16, 1024)
+    assert st == 2 and "rows or heads" in msg, msg
+
+
 def test_merge_validation():
     L = usp.lib()
     st, msg = _status(L.usp_lse_merge, FAKE, FAKE, FAKE, FAKE, 1, 10, 2, 128, 5, 11, None)

@@ -397,6 +397,34 @@ def test_ring_small_full_oracle(w, merge_mode):
     assert_parity(out, lse, O_ref, L_ref, w.name)
 
 
+DEGENERATE = [
+    # one rank: the ring is plain attention (ragged length, D 64)
+    si.WORKLOADS["zigzag_causal_small"].scaled(impl="basic", ring_degree=1, S=777, Hq=2, Hkv=1, rank=-1),
+    # zigzag chunks of one token and stripes of one token per rank
+    si.WORKLOADS["zigzag_causal_small"].scaled(S=8, ring_degree=4, Hq=2, Hkv=2, D=128, rank=-1),
+    si.WORKLOADS["stripe_mqa"].scaled(S=8, ring_degree=8, Hq=2, Hkv=1, rank=-1),
+    # a window of one key: every query sees only itself
+    si.WORKLOADS["ring_swa"].scaled(B=1, S=512, Hq=2, Hkv=2, ring_degree=2, window=1),
+]
+
+
+@pytest.mark.parametrize("w", DEGENERATE, ids=lambda w: f"{w.name}-{w.impl}-N{w.ring_degree}-S{w.S}-W{w.window}")
+def test_ring_degenerate_cases(w):
+    say(f"degenerate ring {w.impl} N={w.ring_degree} S={w.S} W={w.window}")
+    q, k, v = w.make_inputs()
+    O_ref, L_ref = _oracle_share(w, q, k, v)
+    out, lse = _run_ring(w, q, k, v)
+    assert_parity(out, lse, O_ref, L_ref, "degenerate")
+    if w.window == 1:
+        # closed form: O = v of the query's own position, LSE = scale * q . k_self
+        rep = w.Hq // w.Hkv
+        vs = v.float().repeat_interleave(rep, dim=2)
+        ks = k.float().repeat_interleave(rep, dim=2)
+        assert float((out.cpu() - vs).abs().max()) <= 1e-6
+        l_self = (q.float() * ks).sum(-1).transpose(1, 2) * w.scale
+        assert float((lse.cpu() - l_self).abs().max()) <= 1e-4
+
+
 @pytest.mark.parametrize("w", [si.WORKLOADS["zigzag_causal_small"], SMALL_RING[3]], ids=lambda w: w.name)
 def test_ring_permuted_input_and_bf16_output(w):
     q, k, v = w.make_inputs()

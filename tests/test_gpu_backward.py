@@ -287,6 +287,8 @@ RING_BWD = [
     si.WORKLOADS["usp_zigzag_gqa"].scaled(S=4096, Hq=8, Hkv=4, ulysses_degree=4, rank=1, ulysses_rank=2),
     si.WORKLOADS["stripe_mqa"].scaled(S=4096, Hq=4, Hkv=2, ring_degree=4, ulysses_degree=2, rank=2,
                                       ulysses_rank=1),
+    # degenerate: one rank, the ring is plain attention
+    si.WORKLOADS["zigzag_causal_small"].scaled(impl="basic", ring_degree=1, S=777, Hq=2, Hkv=1, rank=-1),
 ]
 
 
@@ -337,6 +339,33 @@ def test_ring_bwd_oracle_forward(w):
     torch.cuda.synchronize()
     for a_, b_ in zip(got, again):
         assert torch.equal(a_, b_)
+
+
+def test_ring_bwd_window_one():
+    """A window of one key: each query sees only itself, so P = 1, delta = dO . v
+    = dP and the exact dQ and dK are 0 (dV = dO).  dP and delta are two f32
+    sums of the same products in different orders, so the kernel's dS is their
+    rounding difference: |dq_t| <= scale |dP_t - delta_t| max|k_t| with
+    |dP - delta| <= 2 D 2^-24 sum_d |dO_d v_d| (f32 summation), and dk the same
+    with q.  dV is compared with the usual relative bar."""
+    w = si.WORKLOADS["ring_swa"].scaled(B=1, S=512, Hq=2, Hkv=2, ring_degree=2, window=1)
+    say("ring_bwd window 1")
+    q, k, v = w.make_inputs()
+    O, LSE, dout, ref = _ring_bwd_expected(w, q, k, v)
+    fwd = usp.RingCall(q.cuda(), k.cuda(), v.cuda(), impl=w.impl, ring_degree=w.ring_degree, window=w.window,
+                       softmax_scale=w.softmax_scale or 0.0)
+    fwd.out.copy_(O.float())
+    fwd.lse.copy_(LSE.float())
+    dq, dk, dv = usp.RingBwdCall(fwd, dout.cuda()).run()
+    torch.cuda.synchronize()
+    assert_grad(dv, ref[2], "dv")
+    dsum = (dout.double() * v.double()).abs().sum(-1, keepdim=True)          # [B,S,H,1]
+    ds_bound = 2 * w.D * 2.0 ** -24 * dsum
+    for g, other, name in ((dq, k, "dq"), (dk, q, "dk")):
+        bound = w.scale * ds_bound * other.double().abs().amax(-1, keepdim=True)
+        err = (g.cpu().double() - 0.0).abs()
+        say(f"  {name}: max|g|={float(err.max()):.3e}, max bound={float(bound.max()):.3e}")
+        assert bool((err <= bound).all()), name
 
 
 @pytest.mark.parametrize("w", [RING_BWD[0], RING_BWD[3], RING_BWD[6]],

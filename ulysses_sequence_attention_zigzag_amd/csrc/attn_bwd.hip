@@ -50,14 +50,15 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const void* out, int out
   float acc = 0.f;
   if (live) {
     const int64_t e0 = idx * D + j * 8;
-    const bf16x8 g = *reinterpret_cast<const bf16x8*>(dout + e0);
+    const bf16x8 g = ld_nt(reinterpret_cast<const bf16x8*>(dout + e0));
     if (out_f32) {
-      const float4 o0 = *reinterpret_cast<const float4*>(static_cast<const float*>(out) + e0);
-      const float4 o1 = *reinterpret_cast<const float4*>(static_cast<const float*>(out) + e0 + 4);
+      typedef float f32x4 __attribute__((ext_vector_type(4)));
+      const f32x4 o0 = ld_nt(reinterpret_cast<const f32x4*>(static_cast<const float*>(out) + e0));
+      const f32x4 o1 = ld_nt(reinterpret_cast<const f32x4*>(static_cast<const float*>(out) + e0 + 4));
       acc = (float)g[0] * o0.x + (float)g[1] * o0.y + (float)g[2] * o0.z + (float)g[3] * o0.w;
       acc += (float)g[4] * o1.x + (float)g[5] * o1.y + (float)g[6] * o1.z + (float)g[7] * o1.w;
     } else {
-      const bf16x8 o = *reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(out) + e0);
+      const bf16x8 o = ld_nt(reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(out) + e0));
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc += (float)g[e] * (float)o[e];
     }

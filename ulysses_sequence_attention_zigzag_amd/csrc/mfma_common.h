@@ -101,6 +101,15 @@ __device__ __forceinline__ void copy16_to_lds(const i32x4& rsrc, uint32_t lds, u
       : "=&s"(saved)
       : "s"(__builtin_amdgcn_readfirstlane((int)lds)), "v"(voff), "s"(rsrc));
 }
+// the same copy with the non-temporal hint (data read once)
+__device__ __forceinline__ void copy16_to_lds_nt(const i32x4& rsrc, uint32_t lds, uint32_t voff) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen nt lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane((int)lds)), "v"(voff), "s"(rsrc));
+}
 __device__ __forceinline__ void copy4_to_lds(const i32x4& rsrc, uint32_t lds, uint32_t voff) {
   int saved;
   asm volatile(

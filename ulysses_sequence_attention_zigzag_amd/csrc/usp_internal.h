@@ -45,6 +45,14 @@ __host__ __device__ inline int32_t position(const PosMap& m, int32_t t) {
   }
 }
 
+// Load with the non-temporal cache hint, for data a kernel reads exactly once
+// and nothing reads again soon (the row sums of O and dO: 0.068 against 0.094
+// ms on a 402 MB input; the copy and merge kernels gained nothing from it).
+template <class T>
+__device__ __forceinline__ T ld_nt(const T* p) {
+  return __builtin_nontemporal_load(p);
+}
+
 // Smallest local row t with position(m, t) >= P, for a row t_ref of the
 // same monotone piece (positions increase with t across a whole basic,
 // stripe or affine rank, and within each chunk of a zigzag rank, where

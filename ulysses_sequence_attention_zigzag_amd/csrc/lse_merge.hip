@@ -38,8 +38,11 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(float* __restrict__ out_
   const int64_t o_idx = (((int64_t)b * L + r) * H + h) * quads + q;
   const float la = lse_acc[lse_idx];
   const float lb = lse_part[lse_idx];
-  const float4 a = reinterpret_cast<const float4*>(out_acc)[o_idx];
-  const float4 p = reinterpret_cast<const float4*>(out_part)[o_idx];
+  // non-temporal loads, plain stores: 0.124 against 0.143 ms on an 811 MB
+  // step (the hint on the stores as well was slower than none)
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const f32x4 a = ld_nt(reinterpret_cast<const f32x4*>(out_acc) + o_idx);
+  const f32x4 p = ld_nt(reinterpret_cast<const f32x4*>(out_part) + o_idx);
   const float M = fmaxf(la, lb);
   if (lb == -INFINITY || M == -INFINITY) return;  // nothing to merge
   const float Lm = M + logf(expf(la - M) + expf(lb - M));

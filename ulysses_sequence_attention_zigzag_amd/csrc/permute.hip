@@ -15,8 +15,10 @@ namespace usp {
 namespace {
 
 template <int BYTES> struct UnitT;
-template <> struct UnitT<16> { using type = uint4; };
-template <> struct UnitT<8> { using type = uint2; };
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <> struct UnitT<16> { using type = u32x4; };
+template <> struct UnitT<8> { using type = u32x2; };
 template <> struct UnitT<4> { using type = uint32_t; };
 template <> struct UnitT<2> { using type = uint16_t; };
 
@@ -67,7 +69,9 @@ __global__ __launch_bounds__(256) void permute_rows_kernel(const char* __restric
   const int64_t dst_row = o * S_out + (scatter ? m : i);
   const U* src = reinterpret_cast<const U*>(in) + src_row * in_stride;
   U* dst = reinterpret_cast<U*>(out) + dst_row * out_stride;
-  for (int32_t c = lane; c < units_per_row; c += tpr) dst[c] = src[c];
+    // loads with the non-temporal hint, plain stores (the hint on the stores
+  // too made the copies slower)
+  for (int32_t c = lane; c < units_per_row; c += tpr) dst[c] = ld_nt(src + c);
 }
 
 // fp32 rows in, bf16 rows out (round to nearest even), same row mapping.
@@ -122,7 +126,9 @@ __global__ __launch_bounds__(256) void relayout_kernel(ShardPtrs shards, char* _
   char* local_row = local + row * local_row_bytes;
   const U* src = reinterpret_cast<const U*>(direction == 0 ? shard_row : local_row);
   U* dst = reinterpret_cast<U*>(direction == 0 ? local_row : shard_row);
-  for (int32_t c = lane; c < units_per_row; c += tpr) dst[c] = src[c];
+    // loads with the non-temporal hint, plain stores (the hint on the stores
+  // too made the copies slower)
+  for (int32_t c = lane; c < units_per_row; c += tpr) dst[c] = ld_nt(src + c);
 }
 
 int unit_bytes_for(int64_t row_bytes, uintptr_t a, uintptr_t b) {

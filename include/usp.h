@@ -26,11 +26,16 @@
  *     visible keys, f32, laid out [B,Hq,S]; a row with no visible key has
  *     LSE = -inf and output 0.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
- *     enqueued; nothing synchronises except where a call says so.
+ *     enqueued; no call synchronises, allocates device memory or copies from
+ *     the host, so every call can be recorded into a HIP graph.  Scratch
+ *     (tile lists, staged copies, accumulators) lives in caller-owned
+ *     workspace sized by the matching *_workspace_size call; the tile lists
+ *     are built on the device at the start of each call.
  *   - Every argument is validated on the host before anything is enqueued.
- *     On a non-OK status nothing was enqueued and outputs are untouched;
- *     usp_last_error() returns a message for the calling thread.
- *     USP_ERR_HIP reports a HIP runtime failure (launch or memory call).
+ *     On a status other than USP_OK and USP_ERR_HIP nothing was enqueued
+ *     and outputs are untouched; usp_last_error() returns a message for the
+ *     calling thread.  USP_ERR_HIP reports a failed kernel launch, after
+ *     which the launches before it stay enqueued.
  *   - Results are deterministic: no atomics in any reduction.
  */
 #ifndef USP_H_
@@ -148,9 +153,11 @@ usp_status usp_ulysses_relayout(void* const* shards, void* local, int64_t B, int
  * overwrites them with this call's partial; accumulate = 1 (out_dt must be
  * F32) merges this partial into the running (out, lse) with the associative
  * rescale of usp_lse_merge.  D must be 64 or 128.  cu_seqlens_host (nseq+1
- * int32, host) plans the tiles; cu_seqlens_dev (same values, device) is read
- * by the kernel.  The first call with a new shape/mask builds and uploads a
- * tile plan (one synchronous copy); later calls reuse it.
+ * int32, host) sizes the tile plan; cu_seqlens_dev (same values, device) is
+ * read by the device planner and the kernel.  workspace: caller-owned device
+ * memory, 256-byte aligned, of at least usp_block_attn_fwd_workspace_size
+ * bytes for the same mask arguments (USP_ERR_WORKSPACE otherwise); it holds
+ * the call's tile plan, built on the device.
  * Lq or Lk may be 0.  With Lk = 0 no row has a visible key: out = 0 and
  * lse = -inf (accumulate = 1 leaves them unchanged); k and v may then be
  * NULL.  With Lq = 0 nothing is enqueued and q, out, lse may be NULL.
@@ -166,6 +173,10 @@ usp_status usp_ulysses_relayout(void* const* shards, void* local, int64_t B, int
  * The returned LSE is that of the modified scores.  A negative or non-finite
  * softcap is USP_ERR_INVALID_ARG; ALiBi over more than 2^22 positions
  * (S, or the varlen token count) is USP_ERR_UNSUPPORTED. */
+size_t usp_block_attn_fwd_workspace_size(int64_t Lq, int64_t Lk, usp_mask_class mask, const usp_posmap* qmap,
+                                         const usp_posmap* kmap, int causal, int window, int n_sink,
+                                         const int32_t* cu_seqlens_host, int nseq);
+
 usp_status usp_block_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                               int64_t B, int64_t Lq, int64_t Lk, int64_t Hq, int64_t Hkv, int64_t D,
                               float softmax_scale, usp_mask_class mask,
@@ -173,7 +184,7 @@ usp_status usp_block_attn_fwd(const void* q, const void* k, const void* v, void*
                               int causal, int window, int n_sink,
                               const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int nseq,
                               usp_dtype out_dt, int accumulate, float softcap, const float* alibi_slopes,
-                              void* stream);
+                              void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------- backward
  * The backward of block attention, as the ring runs it [LCA "Ring
@@ -199,13 +210,18 @@ usp_status usp_block_attn_fwd(const void* q, const void* k, const void* v, void*
  *   softmax_scale, cu_seqlens and D are as in usp_block_attn_fwd; EMPTY
  *   leaves the gradients unchanged.  dq must not alias dk or dv.  Each
  *   gradient element is written by one workgroup (deterministic, no
- *   atomics).  The first call with a new shape/mask builds and uploads its
- *   tile plans (synchronous copies); later calls reuse them.  softcap and
+ *   atomics).  workspace (caller-owned, 256-byte aligned, at least
+ *   usp_block_attn_bwd_workspace_size bytes; may be NULL when that is 0)
+ *   holds the call's two tile plans, built on the device.  softcap and
  *   alibi_slopes are those of the forward (s above is the modified score,
  *   and with softcap dS is multiplied by the derivative 1 - tanh^2 of the
  *   cap before it reaches dQ and dK). */
 usp_status usp_attn_bwd_preprocess(const void* out, usp_dtype out_dt, const void* dout, float* delta,
                                    int64_t B, int64_t L, int64_t H, int64_t D, void* stream);
+
+size_t usp_block_attn_bwd_workspace_size(int64_t Lq, int64_t Lk, usp_mask_class mask, const usp_posmap* qmap,
+                                         const usp_posmap* kmap, int causal, int window, int n_sink,
+                                         const int32_t* cu_seqlens_host, int nseq);
 
 usp_status usp_block_attn_bwd(const void* q, const void* k, const void* v, const void* dout,
                               const float* lse, const float* delta, float* dq, float* dk, float* dv,
@@ -214,7 +230,8 @@ usp_status usp_block_attn_bwd(const void* q, const void* k, const void* v, const
                               const usp_posmap* qmap, const usp_posmap* kmap,
                               int causal, int window, int n_sink,
                               const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int nseq,
-                              float softcap, const float* alibi_slopes, void* stream);
+                              float softcap, const float* alibi_slopes, void* workspace, size_t ws_bytes,
+                              void* stream);
 
 /* --------------------------------------------------------------- decode
  * Decode-time attention over a KV cache, as flash decoding: the cache is cut
@@ -291,8 +308,19 @@ usp_status usp_lse_merge(float* out_acc, float* lse_acc, const float* out_part, 
  *   rank == -1: every rank; out [B,S,Hq,D] (out_dtype) and lse [B,Hq,S] in
  *     the input's order (ud must be 1: the head split does not change the
  *     result of all ranks together);
- *   rank >= 0 : ring rank `rank`'s share for Ulysses rank `ulysses_rank`:
- *     out [B,L,Hq/ud,D] and lse [B,Hq/ud,L] in that rank's local row order.
+ *   rank >= 0, out_layout 0: ring rank `rank`'s share for Ulysses rank
+ *     `ulysses_rank` as attention leaves it, heads split: out [B,L,Hq/ud,D]
+ *     and lse [B,Hq/ud,L] in that rank's local row order;
+ *   rank >= 0, out_layout 1: the same share after the Ulysses head -> seq
+ *     relayout that follows attention [YC "Why not apply Ulysses and Ring
+ *     Attention Individually?": the all-to-all before and after attention]:
+ *     out [B,L,Hq,D] and lse [B,Hq,L] hold ring rank r's rows in local order
+ *     with every head, i.e. the ud Ulysses sequence shards one after another
+ *     (shard u' = rows [u' L/ud, (u'+1) L/ud) of each batch row, the rows
+ *     usp_permute extracts for global rank r*ud + u'); this call writes head
+ *     group u = ulysses_rank of every row and nothing else, so the ud
+ *     Ulysses ranks' calls together fill the tensors.  The relayout is part
+ *     of the attention epilogue (f32 output) or of the final copy.
  * merge_mode 0 merges in the attention kernel's epilogue; 1 writes each
  * step's partial to the workspace and runs usp_lse_merge.
  * qkv_packed = 1 takes q, k, v from one packed [B,S,3,H,D] tensor (varlen
@@ -328,15 +356,31 @@ typedef struct usp_ring_args {
   const float* alibi_slopes;         /* device, Hq f32 over ALL heads (the
                                         Ulysses rank reads its own group),
                                         or NULL                            */
+  int32_t out_layout;                /* rank >= 0: 0 heads split, 1 Ulysses
+                                        sequence shards (see Outputs)      */
 } usp_ring_args;
 
 /* Bytes of device workspace usp_ring_fwd needs for these arguments. */
 size_t usp_ring_fwd_workspace_size(const usp_ring_args* a);
 
 /* Runs the virtual ring.  workspace: device memory of at least
- * usp_ring_fwd_workspace_size(a) bytes (may be NULL when that is 0), owned
- * by the caller, 256-byte aligned. */
+ * usp_ring_fwd_workspace_size(a) bytes, owned by the caller, 256-byte
+ * aligned; it holds the tile plans of every step (built on the device by the
+ * call), the staged q / k / v and the accumulators. */
 usp_status usp_ring_fwd(const usp_ring_args* a, void* workspace, size_t ws_bytes, void* stream);
+
+/* The ring's input staging on its own: writes q, k, v exactly as the
+ * attention kernels of usp_ring_fwd / usp_ring_bwd read them for arguments
+ * `a`, i.e. the layout's token order [YC "2. Usage": the extract function;
+ * LCA "Solution", "Zig-Zag Attention"] restricted to Ulysses head group u:
+ *   q_staged [B, Lq_rows, Hq/ud, D]: every rank's rows rank-major (rank -1,
+ *     Lq_rows = S) or ring rank r's rows in local order (Lq_rows = L);
+ *   k_staged, v_staged [B, S, Hkv/ud, D]: all ranks' rows, rank-major.
+ * From natural or rank-major input, packed or not; bf16, bit-exact copies.
+ * Where the ring reads the caller's tensors in place (rank-major or basic
+ * input, ud = 1, not packed) the same rows are copied with the same gather
+ * kernel.  Buffers are caller-owned and must not overlap the inputs. */
+usp_status usp_ring_stage(const usp_ring_args* a, void* q_staged, void* k_staged, void* v_staged, void* stream);
 
 /* ------------------------------------------------ virtual ring backward
  * The backward of usp_ring_fwd on one device [LCA "Ring Attention": the
@@ -353,10 +397,13 @@ usp_status usp_ring_fwd(const usp_ring_args* a, void* workspace, size_t ws_bytes
  *     [B,S,Hkv/ud,D] in rank-major order (piece j at rows j*L): the
  *     contributions of this rank's queries to every piece, which a real ring
  *     would sum over the hosts.
+ * With fwd.out_layout 1, out, lse and dout are in the sequence-shard layout
+ * and their head group u is read; dq stays [B,L,Hq/ud,D].
  * Steps: staging of q, k, v as in usp_ring_fwd; delta =
  * usp_attn_bwd_preprocess(out, dout); N steps of usp_block_attn_bwd (every
  * host of a step in one launch per kernel); natural-order outputs are
- * un-permuted at the end. */
+ * un-permuted at the end.  The workspace holds the dQ and dK / dV tile plans
+ * of every step (built on the device by the call) and the staged tensors. */
 typedef struct usp_ring_bwd_args {
   usp_ring_args fwd;
   const void* dout;
@@ -372,19 +419,6 @@ size_t usp_ring_bwd_workspace_size(const usp_ring_bwd_args* a);
  * usp_ring_bwd_workspace_size(a) bytes, 256-byte aligned. */
 usp_status usp_ring_bwd(const usp_ring_bwd_args* a, void* workspace, size_t ws_bytes, void* stream);
 
-/* ------------------------------------------------------ tile plan cache
- * usp_block_attn_fwd, usp_block_attn_bwd, usp_ring_fwd and usp_ring_bwd
- * upload the tile plan of each distinct shape / mask / cu_seqlens once per
- * device and keep it for the life of the process (a few int32 per tile).
- * Callers that see many distinct plans (varlen batches with new cu_seqlens
- * every step) can bound that memory: usp_plan_cache_size returns the number
- * of cached plans, and usp_plan_cache_clear frees them all.  Clearing is
- * for a quiet point: no enqueued call may still run on a cached plan (hipFree
- * waits for the device), and no other thread may be inside a library call.
- * Later calls rebuild what they need. */
-int64_t usp_plan_cache_size(void);
-usp_status usp_plan_cache_clear(void);
-
 /* ------------------------------------------------------ tile scheduler
  * Host-only inspection of the tile plan usp_block_attn_fwd would run (no
  * device work).  Items are 8 int32 each: {q_row0, t0, q_rows, q_rank, k_row0,
@@ -392,8 +426,9 @@ usp_status usp_plan_cache_clear(void);
  * 0}: keys [k_begin, k_end) of the item's KV rows, `full` = 1 when every key
  * of the run is visible to every query row of the item (no per-element
  * mask; length a multiple of *tile_n).  Keys outside every run are visible
- * to no row of the item.  Items come ordered by decreasing work.
- * Pass NULL buffers to query the counts only. */
+ * to no row of the item.  Items come ordered by decreasing work (ties in
+ * tile order) when the plan has at most 16384 candidate tiles, in tile
+ * order otherwise.  Pass NULL buffers to query the counts only. */
 usp_status usp_plan_block(int64_t Lq, int64_t Lk, int64_t D, usp_mask_class mask,
                           const usp_posmap* qmap, const usp_posmap* kmap,
                           int causal, int window, int n_sink,
@@ -408,13 +443,29 @@ usp_status usp_plan_block(int64_t Lq, int64_t Lk, int64_t D, usp_mask_class mask
  * t_end, full, 0} of local query rows, `full` = 1 when every key of the item
  * is visible to every query row of the run (length a multiple of *tile_q).
  * Query rows outside every run see no key of the item; tiles no query sees
- * get no item.  Items come ordered by decreasing work. */
+ * get no item.  Items come ordered as in usp_plan_block. */
 usp_status usp_plan_block_kv(int64_t Lq, int64_t Lk, int64_t D, usp_mask_class mask,
                              const usp_posmap* qmap, const usp_posmap* kmap,
                              int causal, int window, int n_sink,
                              const int32_t* cu_seqlens_host, int nseq,
                              int32_t* items, int64_t items_cap, int32_t* runs, int64_t runs_cap,
                              int64_t* n_items, int64_t* n_runs, int32_t* tile_k, int32_t* tile_q);
+
+/* The device planner on one block, for inspection: the plan the calls above
+ * run, built by the GPU into `workspace` exactly as the attention calls
+ * build theirs (kv_tiles 0: usp_block_attn_fwd's plan, kv_tiles 1: the dK /
+ * dV plan).  Outputs: *n_candidates tiles, *run_slots runs per tile, and
+ * *ws_needed bytes; with workspace NULL only these are returned.  Layout:
+ * items (8 int32 each, as in usp_plan_block) at byte 0, ordered as there,
+ * with the tiles that have nothing to do last (or in place, above 16384
+ * candidates) and marked by q_rows = 0; runs (4 int32 each) at byte
+ * ((n_candidates * 32 + 255) / 256) * 256, tile g's in slots [g * run_slots,
+ * ...), addressed by run_begin / run_end as the kernels read them. */
+usp_status usp_plan_block_device(int64_t Lq, int64_t Lk, usp_mask_class mask, const usp_posmap* qmap,
+                                 const usp_posmap* kmap, int causal, int window, int n_sink,
+                                 const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int nseq,
+                                 int accumulate, int kv_tiles, void* workspace, size_t ws_bytes,
+                                 int64_t* n_candidates, int32_t* run_slots, size_t* ws_needed, void* stream);
 
 /* ---------------------------------------------------- kernel timing
  * Instrumentation for benchmarks.  While enabled, every kernel launch of the
@@ -431,7 +482,8 @@ typedef enum {
   USP_KERNEL_BWD_DKDV = 5,  /* backward: dK / dV kernel of usp_block_attn_bwd       */
   USP_KERNEL_BWD_DELTA = 6, /* backward: usp_attn_bwd_preprocess                    */
   USP_KERNEL_DECODE = 7,    /* decode: usp_decode_split_fwd                         */
-  USP_KERNEL_DECODE_MERGE = 8 /* decode: usp_decode_merge                           */
+  USP_KERNEL_DECODE_MERGE = 8, /* decode: usp_decode_merge                          */
+  USP_KERNEL_PLAN = 9       /* device tile planner (both of its kernels)            */
 } usp_kernel_class;
 
 usp_status usp_timing_enable(int enable);

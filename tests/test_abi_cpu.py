@@ -1,9 +1,13 @@
 """CPU tests of the C ABI: exported symbols, host-side validation and the
-tile planner (usp_plan_block), which is host code and is checked here
-bit-exactly against the oracle's visibility predicate.
+tile planner (usp_plan_block: the per-item planner the device planner kernels
+run, built on the host), checked here bit-exactly against the oracle's
+visibility predicate.
 
 No test here launches device work: every call either fails validation on the
-host before anything is enqueued, or is the host-only planner.
+host before anything is enqueued, or is the host-only planner.  This
+container has no GPU, so a call that got as far as enqueueing would return
+USP_ERR_HIP (test_reaching_the_device_reports_hip shows it): a validation
+status therefore also shows that nothing was enqueued.
 """
 import ctypes
 import os
@@ -91,7 +95,7 @@ def _attn(**kw):
     return _status(L.usp_block_attn_fwd, a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Lq"], a["Lk"],
                    a["Hq"], a["Hkv"], a["D"], a["scale"], a["mask"], a["qmap"], a["kmap"], a["causal"],
                    a["window"], a["n_sink"], a["cud"], a["cuh"], a["nseq"], a["dt"], a["acc"], a["softcap"],
-                   a["alibi"], None)
+                   a["alibi"], a.get("ws"), a.get("ws_bytes", 0), None)
 
 
 def test_block_attn_validation():
@@ -139,17 +143,56 @@ def test_block_attn_validation():
     assert st == 2 and "ALiBi" in msg
 
 
-def test_plan_cache_host_planning_caches_nothing():
-    # clearing needs no device when nothing is cached; host-only planning
-    # (usp_plan_block) adds nothing to the device cache
-    usp.plan_cache_clear()
-    assert usp.plan_cache_size() == 0
+def test_block_workspace_sizes_and_checks():
+    """Block calls take their tile plan's workspace from the caller: the size
+    calls report it, and a missing or short workspace is USP_ERR_WORKSPACE
+    before anything is enqueued."""
+    L = usp.lib()
+    need = L.usp_block_attn_fwd_workspace_size(300, 300, usp.MASK["causal"], None, None, 0, 0, 0, None, 0)
+    # 2 query tiles of 256 rows: items, run slots (3 per tile), candidate items and costs, 256-byte aligned
+    assert need == 4 * 256
+    st, msg = _attn(Lq=300, Lk=300)
+    assert st == 3 and "workspace" in msg
+    st, msg = _attn(Lq=300, Lk=300, ws=FAKE, ws_bytes=need - 1)
+    assert st == 3 and "workspace" in msg
+    st, msg = _attn(Lq=300, Lk=300, ws=ctypes.c_void_p(0x10010), ws_bytes=need)
+    assert st == 3 and "aligned" in msg
+    # invalid arguments: size 0, and the call reports the reason
+    assert L.usp_block_attn_fwd_workspace_size(300, 300, usp.MASK["causal"], None, None, 1, 0, 0, None, 0) == 0
+    qm, km = usp.posmap("zigzag", 4, 1, 4096), usp.posmap("zigzag", 4, 2, 4096)
+    nb = L.usp_block_attn_bwd_workspace_size(1024, 1024, usp.MASK["positional"], ctypes.byref(qm), ctypes.byref(km),
+                                             1, 0, 0, None, 0)
+    assert nb > 0
+    args = [FAKE] * 9 + [1, 1024, 1024, 4, 4, 128, 0.0, usp.MASK["positional"], ctypes.byref(qm),
+                         ctypes.byref(km), 1, 0, 0, None, None, 0, 0.0, None]
+    st, msg = _status(L.usp_block_attn_bwd, *args, None, 0, None)
+    assert st == 3 and "workspace" in msg
+    # EMPTY has no work: no workspace needed
+    assert L.usp_block_attn_bwd_workspace_size(64, 64, usp.MASK["empty"], None, None, 0, 0, 0, None, 0) == 0
+
+
+def test_reaching_the_device_reports_hip():
+    """Positive control for the 'nothing enqueued' tests: a valid call whose
+    workspace is large enough goes on to enqueue, which this GPU-less
+    container refuses, so the status is USP_ERR_HIP."""
+    L = usp.lib()
+    need = L.usp_block_attn_fwd_workspace_size(300, 300, usp.MASK["causal"], None, None, 0, 0, 0, None, 0)
+    st, msg = _attn(Lq=300, Lk=300, ws=ctypes.c_void_p(0x100000), ws_bytes=need)
+    assert st == 4, (st, msg)
+
+
+def test_host_planning_allocates_nothing_on_device():
+    # usp_plan_block is host-only: it works without a device
     n = ctypes.c_int64()
     st = usp.lib().usp_plan_block(256, 256, 128, usp.MASK["causal"], None, None, 0, 0, 0, None, 0, 0,
                                   None, 0, None, 0, ctypes.byref(n), ctypes.byref(ctypes.c_int64()),
                                   ctypes.byref(ctypes.c_int32()), ctypes.byref(ctypes.c_int32()))
     assert st == 0 and n.value > 0
-    assert usp.plan_cache_size() == 0
+    nc, slots, need = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_size_t()
+    # the device planner's sizes without a workspace (no device work)
+    st = usp.lib().usp_plan_block_device(256, 256, usp.MASK["causal"], None, None, 0, 0, 0, None, None, 0, 0, 0,
+                                         None, 0, ctypes.byref(nc), ctypes.byref(slots), ctypes.byref(need), None)
+    assert st == 0 and nc.value == 1 and slots.value == 3 and need.value > 0
 
 
 def test_size_limits_are_rejected_before_device_work():
@@ -236,9 +279,32 @@ def test_ring_validation_and_workspace():
     assert st == 3 and "workspace" in msg
     st, msg = _status(L.usp_ring_fwd, ctypes.byref(a), ctypes.c_void_p(0x10010), need, None)
     assert st == 3 and "aligned" in msg
-    # pre-permuted f32 output of basic layout accumulates in place: no workspace
+    # pre-permuted f32 output of basic layout accumulates in place: the
+    # workspace holds only the tile plans (4 steps x 4 ranks x 1 tile)
     a = _ring_args(impl=0, input_order=1, out_dtype=1)
-    assert L.usp_ring_fwd_workspace_size(ctypes.byref(a)) == 0
+    need = L.usp_ring_fwd_workspace_size(ctypes.byref(a))
+    assert 0 < need <= 4 * 1024
+    st, msg = _status(L.usp_ring_fwd, ctypes.byref(a), None, 0, None)
+    assert st == 3 and "workspace" in msg
+    # out_layout: 0 or 1, and the sequence-shard layout is one rank's share
+    for kw, word in ((dict(out_layout=2), "out_layout"), (dict(out_layout=1), "rank >= 0")):
+        a = _ring_args(**kw)
+        assert L.usp_ring_fwd_workspace_size(ctypes.byref(a)) == 0
+        st, msg = _status(L.usp_ring_fwd, ctypes.byref(a), None, 0, None)
+        assert st == 1 and word in msg, (kw, msg)
+    # staging entry point: the ring's argument checks, then its buffers
+    st, msg = _status(L.usp_ring_stage, ctypes.byref(_ring_args(S=1020)), FAKE, FAKE, FAKE, None)
+    assert st == 1 and "zigzag" in msg
+    st, msg = _status(L.usp_ring_stage, ctypes.byref(_ring_args()), None, FAKE, FAKE, None)
+    assert st == 1 and "staging" in msg
+    # backward: same checks, its own workspace
+    b = usp.RingBwdArgs()
+    b.fwd = _ring_args()
+    b.dout, b.dq, b.dk, b.dv = 0x10000, 0x20000, 0x30000, 0x40000
+    need = L.usp_ring_bwd_workspace_size(ctypes.byref(b))
+    assert need > 0
+    st, msg = _status(L.usp_ring_bwd, ctypes.byref(b), ctypes.c_void_p(0x100000), need - 256, None)
+    assert st == 3 and "workspace" in msg
     # packed qkv: multi-head only; the copies of q, k, v always take workspace
     a = _ring_args(qkv_packed=1)
     st, msg = _status(L.usp_ring_fwd, ctypes.byref(a), None, 0, None)

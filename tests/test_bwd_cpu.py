@@ -35,7 +35,7 @@ def _bwd(**kw):
     return _status(usp.lib().usp_block_attn_bwd, a["q"], a["k"], a["v"], a["do"], a["lse"], a["delta"], a["dq"],
                    a["dk"], a["dv"], a["B"], a["Lq"], a["Lk"], a["Hq"], a["Hkv"], a["D"], a["scale"], a["mask"],
                    a["qmap"], a["kmap"], a["causal"], a["window"], a["n_sink"], a["cud"], a["cuh"], a["nseq"],
-                   a["softcap"], a["alibi"], None)
+                   a["softcap"], a["alibi"], a.get("ws"), a.get("ws_bytes", 0), None)
 
 
 def test_block_attn_bwd_validation():
@@ -200,11 +200,18 @@ def test_ring_bwd_validation_and_workspace():
     need = L.usp_ring_bwd_workspace_size(ctypes.byref(b))
     S, Hq, Hkv, D = 1024, 8, 2, 128
     expect = S * (Hq + 2 * Hkv) * D * 2 + 2 * Hq * S * 4 + S * Hq * D * 2 + Hq * S * 4 + S * (Hq + 2 * Hkv) * D * 4
-    assert expect <= need <= expect + 16 * 256
+
+    def plan_bytes(cands, slots):   # items, run slots, candidate items, costs; each 256-byte aligned
+        a = lambda x: (x + 255) // 256 * 256
+        return a(cands * 32) + a(cands * slots * 16) + a(cands * 32) + a(cands * 8)
+
+    # dQ and dK / dV plans: 4 steps x 4 ranks x 2 tiles of 128 (one per zigzag chunk), 2 chunks x 3 run slots
+    plans = 2 * plan_bytes(32, 6)
+    assert expect + plans <= need <= expect + plans + 16 * 256
     st, msg = _status(L.usp_ring_bwd, ctypes.byref(b), None, 0, None)
     assert st == 3 and "workspace" in msg
     st, msg = _status(L.usp_ring_bwd, ctypes.byref(b), ctypes.c_void_p(0x10010), need, None)
     assert st == 3 and "aligned" in msg
-    # basic layout, rank-major input: only delta
+    # basic layout, rank-major input: only delta and the plans (one piece per rank: 3 run slots)
     b = bargs(impl=0, input_order=1)
-    assert L.usp_ring_bwd_workspace_size(ctypes.byref(b)) == ((Hq * S * 4 + 255) // 256) * 256
+    assert L.usp_ring_bwd_workspace_size(ctypes.byref(b)) == ((Hq * S * 4 + 255) // 256) * 256 + 2 * plan_bytes(32, 3)

@@ -1,0 +1,306 @@
+"""GPU tests of the boundary's data movement and scheduling, bit-exact:
+
+* the ring's input staging (usp_ring_stage: the layout's token order fused
+  with the Ulysses head-group split) against the oracle's index formulas --
+  extract_rows / permute_rows composed with ulysses_seq_to_head -- for every
+  layout, Ulysses degree 1 / 2 / 4, packed and separate q, k, v, natural and
+  rank-major input;
+* the output's Ulysses head -> seq relayout (out_layout 1) against the
+  head-split output scattered by the oracle's ulysses_head_to_seq, and the
+  backward of that layout against the head-split backward;
+* the device tile planner (usp_plan_block_device) against the host planner
+  (usp_plan_block / usp_plan_block_kv), whose plans the CPU suite checks
+  against the oracle's visibility predicate;
+* calls on a side stream, and a first call recorded straight into a HIP
+  graph (no call allocates, copies from the host or synchronises).
+"""
+import sys
+
+import pytest
+import torch
+
+import seeded_inputs as si
+import ulysses_sequence_attention_zigzag_amd as usp
+from oracle import index_ref as ix
+from oracle.attention_ref import attention_ref
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 1e-2
+LSE_TOL = 5e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a device"
+    usp.lib()
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def bits(t):
+    t = t.contiguous()
+    return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)
+
+
+def same_bits(a, b):
+    return a.shape == b.shape and torch.equal(bits(a.cpu()), bits(b.cpu()))
+
+
+# ---------------------------------------------------------------- staging
+def _expected_staging(x, impl, N, ud, b, rank, u):
+    """Rows of the natural-order tensor x [B,S,H,D] as the ring reads them:
+    rank -1 -> every rank's rows rank-major (ud must be 1); rank r -> Ulysses
+    rank u's relayout of ring rank r's shard (seq -> head over the ud USP
+    ranks r*ud + u')."""
+    if rank < 0:
+        return ix.permute_rows(x, impl, N, b)
+    shards = [ix.extract_rows(x, impl, N, ud, rank * ud + up, b) for up in range(ud)]
+    return ix.ulysses_seq_to_head(shards, u)
+
+
+def _expected_kv_staging(x, impl, N, ud, b, u):
+    """Every ring rank's K / V pieces, rank-major, each relayouted for Ulysses rank u."""
+    return torch.cat([_expected_staging(x, impl, N, ud, b, r, u) for r in range(N)], dim=1)
+
+
+STAGE_LAYOUTS = [("basic", 1), ("zigzag", 1), ("stripe", 1), ("stripe", 3)]
+
+
+@pytest.mark.parametrize("impl,b", STAGE_LAYOUTS)
+@pytest.mark.parametrize("ud", [1, 2, 4])
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("order", ["natural", "permuted"])
+def test_ring_staging_bit_exact(impl, b, ud, packed, order):
+    """The strided gathers the ring calls run before attention, bit for bit."""
+    N, S, B, D = 4, 384, 2, 64
+    Hq, Hkv = (8, 8) if packed else (8, 4)
+    say(f"staging {impl} b={b} ud={ud} packed={packed} {order}")
+    q = si.randn_bf16((B, S, Hq, D), 31, 0)
+    k = si.randn_bf16((B, S, Hkv, D), 31, 1)
+    v = si.randn_bf16((B, S, Hkv, D), 31, 2)
+    if order == "permuted":
+        qi, ki, vi = (ix.permute_rows(t, impl, N, b) for t in (q, k, v))
+    else:
+        qi, ki, vi = q, k, v
+    ranks = [(-1, 0), (2, 0)] if ud == 1 else [(1, 0), (3, ud - 1), (0, ud // 2)]
+    for rank, u in ranks:
+        kw = dict(impl=impl, ring_degree=N, ulysses_degree=ud, stripe_block=b, causal=True, rank=rank,
+                  ulysses_rank=u, input_order=order)
+        if packed:
+            qkv = torch.stack([qi, ki, vi], dim=-3).contiguous().cuda()
+            call = usp.RingCall(qkv, None, None, qkv_packed=True, **kw)
+        else:
+            call = usp.RingCall(qi.cuda(), ki.cuda(), vi.cuda(), **kw)
+        qs, ks, vs = call.stage()
+        torch.cuda.synchronize()
+        assert same_bits(qs, _expected_staging(q, impl, N, ud, b, rank, u)), (rank, u, "q")
+        assert same_bits(ks, _expected_kv_staging(k, impl, N, ud, b, u)), (rank, u, "k")
+        assert same_bits(vs, _expected_kv_staging(v, impl, N, ud, b, u)), (rank, u, "v")
+
+
+@pytest.mark.parametrize("impl,b", [("zigzag", 1), ("stripe", 2)])
+def test_ring_staging_varlen_bit_exact(impl, b):
+    """Varlen input [T,H,D]: the layout applies to the packed token axis."""
+    N, S, D = 4, 512, 128
+    say(f"staging varlen {impl}")
+    q = si.randn_bf16((S, 4, D), 32, 0)
+    k = si.randn_bf16((S, 2, D), 32, 1)
+    v = si.randn_bf16((S, 2, D), 32, 2)
+    for rank, ud, u in ((-1, 1, 0), (1, 2, 1)):
+        call = usp.RingCall(q.cuda(), k.cuda(), v.cuda(), impl=impl, ring_degree=N, ulysses_degree=ud,
+                            stripe_block=b, cu_seqlens=[0, 100, 333, S], rank=rank, ulysses_rank=u, window=64)
+        qs, ks, vs = call.stage()
+        torch.cuda.synchronize()
+        one = lambda t: t.unsqueeze(0)
+        assert same_bits(qs, _expected_staging(one(q), impl, N, ud, b, rank, u)[0])
+        assert same_bits(ks, _expected_kv_staging(one(k), impl, N, ud, b, u)[0])
+        assert same_bits(vs, _expected_kv_staging(one(v), impl, N, ud, b, u)[0])
+
+
+# ---------------------------------------------------------------- output relayout
+SEQ_OUT = [
+    si.WORKLOADS["usp_zigzag_gqa"].scaled(S=4096, Hq=8, Hkv=4),
+    si.WORKLOADS["usp_zigzag_gqa"].scaled(S=4096, Hq=8, Hkv=4, ulysses_degree=4, rank=2),
+    si.WORKLOADS["stripe_mqa"].scaled(S=4096, Hq=4, Hkv=2, ring_degree=4, ulysses_degree=2, rank=3),
+]
+
+
+@pytest.mark.parametrize("w", SEQ_OUT, ids=lambda w: f"{w.impl}-ud{w.ulysses_degree}-r{w.rank}")
+@pytest.mark.parametrize("out_dtype,merge_mode", [(torch.float32, 0), (torch.float32, 1), (torch.bfloat16, 0)])
+def test_ring_output_head_to_seq(w, out_dtype, merge_mode):
+    """out_layout 1: the ud Ulysses ranks' calls fill [B,L,Hq,D] / [B,Hq,L];
+    equal bit for bit to the head-split outputs scattered by the oracle's
+    head -> seq relayout, and within the bars of the float64 oracle."""
+    say(f"head->seq {w.impl} ud={w.ulysses_degree} rank={w.rank} {out_dtype} merge={merge_mode}")
+    q, k, v = w.make_inputs()
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    ud, L = w.ulysses_degree, w.S // w.ring_degree
+    Ls, Hl = L // ud, w.Hq // ud
+    kw = dict(impl=w.impl, ring_degree=w.ring_degree, ulysses_degree=ud, stripe_block=w.stripe_block,
+              causal=True, rank=w.rank, out_dtype=out_dtype, merge_mode=merge_mode)
+    out_seq = torch.full((w.B, L, w.Hq, w.D), float("nan"), device="cuda").to(out_dtype)
+    lse_seq = torch.full((w.B, w.Hq, L), float("nan"), device="cuda")
+    shards = [torch.full((w.B, Ls, w.Hq, w.D), float("nan")).to(out_dtype) for _ in range(ud)]
+    for u in range(ud):
+        oh, lh = usp.RingCall(qd, kd, vd, ulysses_rank=u, **kw).run()
+        usp.RingCall(qd, kd, vd, ulysses_rank=u, out_layout="seq", out=out_seq, lse=lse_seq, **kw).run()
+        torch.cuda.synchronize()
+        ix.ulysses_head_to_seq(oh.cpu(), u, shards)
+        assert same_bits(lse_seq[:, u * Hl:(u + 1) * Hl], lh), f"lse head group {u}"
+    assert same_bits(out_seq, torch.cat(shards, dim=1)), "output rows"
+    # and against the definition, every head of the ring rank's rows
+    pos = ix.rank_positions(w.impl, w.S, w.ring_degree, w.rank, w.stripe_block)
+    O_ref, L_ref = attention_ref(q, k, v, softmax_scale=w.scale, causal=True, rows=pos)
+    err_o = float((out_seq.float().cpu().double() - O_ref).abs().max())
+    err_l = float((lse_seq.cpu().double() - L_ref).abs().max())
+    say(f"  max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}")
+    assert err_l <= LSE_TOL
+    # bf16 output: plus its rounding, at most 2^-8 of |o|
+    assert err_o <= (OUT_TOL if out_dtype == torch.float32 else 2 ** -8 * float(O_ref.abs().max()) + OUT_TOL)
+
+
+def test_ring_backward_of_seq_layout():
+    """usp_ring_bwd of an out_layout 1 forward reads head group u of out, LSE
+    and dout: the gradients equal those of the head-split forward bit for bit."""
+    w = SEQ_OUT[0]
+    say("backward of the sequence-shard layout")
+    q, k, v = w.make_inputs()
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    kw = dict(impl=w.impl, ring_degree=w.ring_degree, ulysses_degree=w.ulysses_degree, causal=True, rank=w.rank)
+    Hl = w.Hq // w.ulysses_degree
+    for u in range(w.ulysses_degree):
+        fh = usp.RingCall(qd, kd, vd, ulysses_rank=u, **kw)
+        fh.run()
+        fs = usp.RingCall(qd, kd, vd, ulysses_rank=u, out_layout="seq", **kw)
+        fs.run()
+        dout_seq = si.randn_bf16(tuple(fs.out.shape), 77, u).cuda()
+        dout_h = dout_seq[:, :, u * Hl:(u + 1) * Hl].contiguous()
+        gh = usp.RingBwdCall(fh, dout_h).run()
+        gs = usp.RingBwdCall(fs, dout_seq).run()
+        torch.cuda.synchronize()
+        for a, b_, name in zip(gh, gs, ("dq", "dk", "dv")):
+            assert same_bits(a, b_), (u, name)
+
+
+# ---------------------------------------------------------------- device planner
+PLAN_CASES = [
+    # impl, S, N, b, causal, window, n_sink, cu
+    ("zigzag", 2 * 4 * 200, 4, 1, True, 0, 0, None),
+    ("stripe", 2048, 8, 1, True, 0, 0, None),
+    ("stripe", 1536, 4, 3, True, 0, 0, None),
+    ("basic", 8192, 4, 1, False, 1000, 4, [0, 512, 4000, 8192]),
+    ("basic", 4096, 4, 1, True, 0, 0, [0, 1, 700, 701, 2900, 4096]),
+    ("zigzag", 3072, 4, 1, False, 300, 2, None),
+    ("stripe", 3072, 4, 3, False, 200, 3, [0, 1000, 1100, 3072]),
+    # many short sequences with sinks: several sink intervals per tile
+    ("basic", 4096, 2, 1, False, 40, 3, list(range(0, 4096, 37)) + [4096]),
+]
+
+
+def _runs_of(items, runs):
+    """Items (q_rows > 0) with their run lists, in plan order."""
+    out = []
+    for it in items.tolist():
+        if it[2] == 0:
+            continue
+        rb, re_ = it[6], it[7]
+        out.append((tuple(it[:6]), [tuple(r[:3]) for r in runs[rb:re_].tolist()]))
+    return out
+
+
+@pytest.mark.parametrize("case", PLAN_CASES)
+def test_device_planner_matches_host_planner(case):
+    impl, S, N, b, causal, window, n_sink, cu = case
+    say(f"device planner {case[:7]}")
+    L = S // N
+    for i in range(N):
+        for j in sorted({0, i, (i + 1) % N, N - 1}):
+            qm, km = usp.posmap(impl, N, i, S, b), usp.posmap(impl, N, j, S, b)
+            kw = dict(mask="positional", qmap=qm, kmap=km, causal=causal, window=window, n_sink=n_sink,
+                      cu_seqlens=cu)
+            for acc in (False, True):
+                hi, hr, _, _ = usp.plan_block(L, L, 128, accumulate=acc, **kw)
+                di, dr, slots = usp.plan_block_device(L, L, accumulate=acc, **kw)
+                assert _runs_of(di, dr) == _runs_of(hi, hr), (i, j, acc)
+                # dropped tiles come last, with no runs
+                live = (di[:, 2] > 0).tolist()
+                assert live == sorted(live, reverse=True)
+            hi, hr, _, _ = usp.plan_block_kv(L, L, 128, **kw)
+            di, dr, slots = usp.plan_block_device(L, L, kv_tiles=True, **kw)
+            assert _runs_of(di, dr) == _runs_of(hi, hr), (i, j, "kv")
+
+
+@pytest.mark.parametrize("mask", ["full", "causal", "causal_strict", "empty"])
+def test_device_planner_explicit_classes(mask):
+    for Lq, Lk in ((300, 300), (200, 77), (64, 1000)):
+        for acc in (False, True):
+            hi, hr, _, _ = usp.plan_block(Lq, Lk, 128, mask=mask, accumulate=acc)
+            di, dr, _ = usp.plan_block_device(Lq, Lk, mask=mask, accumulate=acc)
+            assert _runs_of(di, dr) == _runs_of(hi, hr), (mask, Lq, Lk, acc)
+
+
+# ---------------------------------------------------------------- streams and graphs
+def test_varlen_calls_on_a_side_stream():
+    """cu_seqlens copies and workspaces follow the stream a call is enqueued
+    on: block and ring calls on a non-current stream give the oracle's result."""
+    say("side stream")
+    w = si.WORKLOADS["varlen_streaming"].scaled(S=2048, Hq=4, Hkv=2, window=250, cu_seqlens=[0, 128, 1000, 2048])
+    q, k, v = w.make_inputs()
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    O_ref, L_ref = attention_ref(q, k, v, softmax_scale=w.scale, window=w.window, n_sink=w.n_sink,
+                                 cu_seqlens=w.cu_seqlens)
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    call = usp.RingCall(qd, kd, vd, impl="basic", ring_degree=w.ring_degree, window=w.window, n_sink=w.n_sink,
+                        cu_seqlens=w.cu_seqlens)
+    out, lse = call.run(stream=side)
+    side.synchronize()
+    assert float((out.cpu().double() - O_ref).abs().max()) <= OUT_TOL
+    assert float((lse.cpu().double() - L_ref).abs().max()) <= LSE_TOL
+    # one block call (rank 1 against rank 0's keys, basic layout) on the side stream, the
+    # current stream left idle
+    N, S = w.ring_degree, w.S
+    Ls = S // N
+    qb = qd[Ls:2 * Ls].unsqueeze(0)
+    kb, vb = kd[:Ls].unsqueeze(0), vd[:Ls].unsqueeze(0)
+    o1, l1 = usp.block_attn_fwd(qb, kb, vb, qmap=usp.posmap("basic", N, 1, S), kmap=usp.posmap("basic", N, 0, S),
+                                window=w.window, n_sink=w.n_sink, cu_seqlens=w.cu_seqlens, stream=side)
+    side.synchronize()
+    torch.cuda.synchronize()
+    o2, l2 = usp.block_attn_fwd(qb, kb, vb, qmap=usp.posmap("basic", N, 1, S), kmap=usp.posmap("basic", N, 0, S),
+                                window=w.window, n_sink=w.n_sink, cu_seqlens=w.cu_seqlens)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.cpu(), o2.cpu()) and torch.equal(l1.cpu(), l2.cpu())
+
+
+def test_first_varlen_ring_call_recorded_into_a_graph():
+    """A ring call with never-seen cu_seqlens, recorded into a HIP graph before
+    any eager call: each replay (with eager work and synchronisations between)
+    gives the eager result bit for bit."""
+    say("first call captured")
+    w = si.WORKLOADS["varlen_streaming"].scaled(S=2048, Hq=4, Hkv=4, window=200, n_sink=3,
+                                                cu_seqlens=[0, 77, 1500, 1501, 2048], impl="zigzag")
+    q, k, v = w.make_inputs()
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    kw = dict(impl=w.impl, ring_degree=w.ring_degree, window=w.window, n_sink=w.n_sink, cu_seqlens=w.cu_seqlens)
+    call = usp.RingCall(qd, kd, vd, **kw)
+    graph = call.capture()
+    ref = usp.RingCall(qd, kd, vd, **kw)
+    ro, rl = ref.run()
+    torch.cuda.synchronize()
+    ro, rl = ro.cpu().clone(), rl.cpu().clone()
+    O_ref, L_ref = attention_ref(q, k, v, softmax_scale=w.scale, window=w.window, n_sink=w.n_sink,
+                                 cu_seqlens=w.cu_seqlens)
+    assert float((ro.double() - O_ref).abs().max()) <= OUT_TOL
+    for i in range(3):
+        call.out.fill_(7.0)
+        call.lse.fill_(7.0)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(call.out.cpu(), ro) and torch.equal(call.lse.cpu(), rl), f"replay {i}"
+        ref.run()
+        torch.cuda.synchronize()

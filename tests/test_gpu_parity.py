@@ -273,22 +273,6 @@ def test_ring_graph_replay(w):
         assert torch.equal(call.out.cpu(), ref_o) and torch.equal(call.lse.cpu(), ref_l), f"eager {i}"
 
 
-# ---------------------------------------------------------------- plan cache
-def test_plan_cache_clear_and_rebuild():
-    """Cached tile plans can be freed at a quiet point; the next call rebuilds
-    its plan and returns the same bits."""
-    say("plan cache clear")
-    w = si.WORKLOADS["varlen_streaming"].scaled(S=2048, Hq=4, Hkv=4, window=250, cu_seqlens=[0, 128, 1000, 2048])
-    q, k, v = w.make_inputs()
-    out1, lse1 = _run_ring(w, q, k, v)
-    assert usp.plan_cache_size() >= 1
-    usp.plan_cache_clear()
-    assert usp.plan_cache_size() == 0
-    out2, lse2 = _run_ring(w, q, k, v)
-    assert usp.plan_cache_size() >= 1
-    assert torch.equal(out1.cpu(), out2.cpu()) and torch.equal(lse1.cpu(), lse2.cpu())
-
-
 # ---------------------------------------------------------------- zero-length inputs
 @pytest.mark.parametrize("D", [64, 128])
 def test_block_attn_zero_length(D):

@@ -49,7 +49,8 @@ class RingArgs(ctypes.Structure):
                 ("rank", ctypes.c_int32), ("ulysses_rank", ctypes.c_int32),
                 ("input_order", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("merge_mode", ctypes.c_int32), ("qkv_packed", ctypes.c_int32),
-                ("softcap", ctypes.c_float), ("alibi_slopes", ctypes.c_void_p)]
+                ("softcap", ctypes.c_float), ("alibi_slopes", ctypes.c_void_p),
+                ("out_layout", ctypes.c_int32)]
 
 
 class RingBwdArgs(ctypes.Structure):
@@ -62,17 +63,21 @@ _lib = None
 _I64 = ctypes.c_int64
 _I32 = ctypes.c_int
 _P = ctypes.c_void_p
+_SZ = ctypes.c_size_t
+_PM = ctypes.POINTER(PosMap)
 _SIGS = {
     "usp_last_error": ([], ctypes.c_char_p),
     "usp_version": ([], ctypes.c_char_p),
     "usp_permute": ([_P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P], _I32),
     "usp_ulysses_relayout": ([_P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P], _I32),
+    "usp_block_attn_fwd_workspace_size": ([_I64, _I64, _I32, _PM, _PM, _I32, _I32, _I32, _P, _I32], _SZ),
     "usp_block_attn_fwd": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, ctypes.c_float, _I32,
-                            ctypes.POINTER(PosMap), ctypes.POINTER(PosMap), _I32, _I32, _I32, _P, _P, _I32,
-                            _I32, _I32, ctypes.c_float, _P, _P], _I32),
+                            _PM, _PM, _I32, _I32, _I32, _P, _P, _I32,
+                            _I32, _I32, ctypes.c_float, _P, _P, _SZ, _P], _I32),
     "usp_lse_merge": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P], _I32),
     "usp_ring_fwd_workspace_size": ([ctypes.POINTER(RingArgs)], ctypes.c_size_t),
     "usp_ring_fwd": ([ctypes.POINTER(RingArgs), _P, ctypes.c_size_t, _P], _I32),
+    "usp_ring_stage": ([ctypes.POINTER(RingArgs), _P, _P, _P, _P], _I32),
     "usp_ring_bwd_workspace_size": ([ctypes.POINTER(RingBwdArgs)], ctypes.c_size_t),
     "usp_ring_bwd": ([ctypes.POINTER(RingBwdArgs), _P, ctypes.c_size_t, _P], _I32),
     "usp_plan_block": ([_I64, _I64, _I64, _I32, ctypes.POINTER(PosMap), ctypes.POINTER(PosMap), _I32, _I32,
@@ -83,14 +88,16 @@ _SIGS = {
                            _I32, _P, _I32, _P, _I64, _P, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64),
                            ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)], _I32),
     "usp_attn_bwd_preprocess": ([_P, _I32, _P, _P, _I64, _I64, _I64, _I64, _P], _I32),
+    "usp_block_attn_bwd_workspace_size": ([_I64, _I64, _I32, _PM, _PM, _I32, _I32, _I32, _P, _I32], _SZ),
     "usp_block_attn_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64,
-                            ctypes.c_float, _I32, ctypes.POINTER(PosMap), ctypes.POINTER(PosMap), _I32, _I32,
-                            _I32, _P, _P, _I32, ctypes.c_float, _P, _P], _I32),
+                            ctypes.c_float, _I32, _PM, _PM, _I32, _I32,
+                            _I32, _P, _P, _I32, ctypes.c_float, _P, _P, _SZ, _P], _I32),
+    "usp_plan_block_device": ([_I64, _I64, _I32, _PM, _PM, _I32, _I32, _I32, _P, _P, _I32, _I32, _I32, _P, _SZ,
+                               ctypes.POINTER(_I64), ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(_SZ), _P],
+                              _I32),
     "usp_decode_split_fwd": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64, ctypes.c_float,
                               _I32, _I32, ctypes.c_float, _P, _P], _I32),
     "usp_decode_merge": ([_P, _P, _I64, _I64, _I64, _I64, _I64, _P, _I32, _P, _P], _I32),
-    "usp_plan_cache_size": ([], _I64),
-    "usp_plan_cache_clear": ([], _I32),
     "usp_timing_enable": ([_I32], _I32),
     "usp_timing_reset": ([], _I32),
     "usp_timing_read": ([_I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64)], _I32),
@@ -121,6 +128,39 @@ def _check(status: int) -> None:
 def _stream(stream=None):
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _resolve(stream=None):
+    """The torch stream a call is enqueued on (the current one by default)."""
+    return stream if stream is not None else torch.cuda.current_stream()
+
+
+def _on_stream(t: torch.Tensor, s) -> None:
+    """Keeps a temporary device tensor from being reused before the work
+    enqueued on stream ``s`` has run (no host synchronisation)."""
+    if t is not None and t.is_cuda:
+        t.record_stream(s)
+
+
+def _host_to_device_on(values, dtype, device, s) -> torch.Tensor:
+    """A small host list copied to the device in stream order on ``s``."""
+    host = torch.tensor(list(values), dtype=dtype)
+    with torch.cuda.stream(s):
+        dev = host.to(device)
+    _on_stream(dev, s)
+    return dev
+
+
+def _workspace(nbytes: int, device, s) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    _on_stream(ws, s)
+    return ws
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
 def _dev(t: torch.Tensor, dtype=None, name="tensor"):
@@ -178,13 +218,15 @@ def ulysses_relayout(shards: Sequence[torch.Tensor], local: torch.Tensor, ulysse
 
 
 # ---------------------------------------------------------------- attention
-def _cu(cu_seqlens, device):
+def _cu(cu_seqlens, device, s=None):
+    """(device copy, host copy, nseq) of cu_seqlens; the device copy is made in
+    stream order on ``s`` and kept alive for the work enqueued there."""
     if cu_seqlens is None:
-        return None, None, 0, None
-    host = torch.tensor(list(cu_seqlens) if not torch.is_tensor(cu_seqlens) else cu_seqlens.tolist(),
-                        dtype=torch.int32)
-    dev = host.to(device)
-    return dev, host, host.numel() - 1, (dev, host)
+        return None, None, 0
+    vals = list(cu_seqlens) if not torch.is_tensor(cu_seqlens) else cu_seqlens.tolist()
+    host = torch.tensor(vals, dtype=torch.int32)
+    dev = _host_to_device_on(vals, torch.int32, device, s if s is not None else torch.cuda.current_stream())
+    return dev, host, host.numel() - 1
 
 
 def _slopes(alibi_slopes: Optional[torch.Tensor], H: int):
@@ -210,17 +252,20 @@ def block_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, mask: s
         out = torch.empty((B, Lq, Hq, D), dtype=out_dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
-    cu_dev, cu_host, nseq, keep = _cu(cu_seqlens, q.device)
+    s = _resolve(stream)
+    cu_dev, cu_host, nseq = _cu(cu_seqlens, q.device, s)
+    qm = ctypes.byref(qmap) if qmap else None
+    km = ctypes.byref(kmap) if kmap else None
+    nbytes = lib().usp_block_attn_fwd_workspace_size(Lq, Lk, MASK[mask], qm, km, int(causal), int(window),
+                                                     int(n_sink), _ptr(cu_host), nseq)
+    ws = _workspace(nbytes, q.device, s)
     _check(lib().usp_block_attn_fwd(
         _dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"),
         _dev(out, out_dtype, "out"), _dev(lse, torch.float32, "lse"), B, Lq, Lk, Hq, Hkv, D,
-        float(softmax_scale), MASK[mask], ctypes.byref(qmap) if qmap else None,
-        ctypes.byref(kmap) if kmap else None, int(causal), int(window), int(n_sink),
-        ctypes.c_void_p(cu_dev.data_ptr()) if cu_dev is not None else None,
-        ctypes.c_void_p(cu_host.data_ptr()) if cu_host is not None else None, nseq,
-        DT[out.dtype], int(accumulate), float(softcap), _slopes(alibi_slopes, Hq), _stream(stream)))
-    if keep is not None:
-        torch.cuda.current_stream().synchronize()  # cu_seqlens copies must outlive the launch
+        float(softmax_scale), MASK[mask], qm, km, int(causal), int(window), int(n_sink),
+        _ptr(cu_dev), _ptr(cu_host), nseq,
+        DT[out.dtype], int(accumulate), float(softcap), _slopes(alibi_slopes, Hq), _ptr(ws), nbytes,
+        ctypes.c_void_p(s.cuda_stream)))
     return out, lse
 
 
@@ -264,18 +309,20 @@ def block_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torc
     for name, t, shp in (("dq", dq, (B, Lq, Hq, D)), ("dk", dk, (B, Lk, Hkv, D)), ("dv", dv, (B, Lk, Hkv, D))):
         if tuple(t.shape) != shp:
             raise ValueError(f"{name} must be {list(shp)}")
-    cu_dev, cu_host, nseq, keep = _cu(cu_seqlens, q.device)
+    s = _resolve(stream)
+    cu_dev, cu_host, nseq = _cu(cu_seqlens, q.device, s)
+    qm = ctypes.byref(qmap) if qmap else None
+    km = ctypes.byref(kmap) if kmap else None
+    nbytes = lib().usp_block_attn_bwd_workspace_size(Lq, Lk, MASK[mask], qm, km, int(causal), int(window),
+                                                     int(n_sink), _ptr(cu_host), nseq)
+    ws = _workspace(nbytes, q.device, s)
     _check(lib().usp_block_attn_bwd(
         _dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"),
         _dev(dout, torch.bfloat16, "dout"), _dev(lse, torch.float32, "lse"), _dev(delta, torch.float32, "delta"),
         _dev(dq, torch.float32, "dq"), _dev(dk, torch.float32, "dk"), _dev(dv, torch.float32, "dv"),
-        B, Lq, Lk, Hq, Hkv, D, float(softmax_scale), MASK[mask], ctypes.byref(qmap) if qmap else None,
-        ctypes.byref(kmap) if kmap else None, int(causal), int(window), int(n_sink),
-        ctypes.c_void_p(cu_dev.data_ptr()) if cu_dev is not None else None,
-        ctypes.c_void_p(cu_host.data_ptr()) if cu_host is not None else None, nseq, float(softcap),
-        _slopes(alibi_slopes, Hq), _stream(stream)))
-    if keep is not None:
-        torch.cuda.current_stream().synchronize()  # cu_seqlens copies must outlive the launch
+        B, Lq, Lk, Hq, Hkv, D, float(softmax_scale), MASK[mask], qm, km, int(causal), int(window), int(n_sink),
+        _ptr(cu_dev), _ptr(cu_host), nseq, float(softcap),
+        _slopes(alibi_slopes, Hq), _ptr(ws), nbytes, ctypes.c_void_p(s.cuda_stream)))
     return dq, dk, dv
 
 
@@ -301,19 +348,19 @@ def decode_split_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, kv_le
         out_part = torch.empty((n, B, Lq, Hq, D), dtype=torch.float32, device=q.device)
     if lse_part is None:
         lse_part = torch.empty((n, B, Hq, Lq), dtype=torch.float32, device=q.device)
+    s = _resolve(stream)
     lens_host = lens_dev = None
     if kv_lens is not None:
-        lens_host = torch.tensor([int(x) for x in kv_lens], dtype=torch.int32)
-        lens_dev = lens_host.to(q.device)
+        vals = [int(x) for x in kv_lens]
+        lens_host = torch.tensor(vals, dtype=torch.int32)
+        lens_dev = _host_to_device_on(vals, torch.int32, q.device, s)
     _check(lib().usp_decode_split_fwd(
         _dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"),
         ctypes.c_void_p(lens_dev.data_ptr()) if lens_dev is not None else None,
         ctypes.c_void_p(lens_host.data_ptr()) if lens_host is not None else None,
         _dev(out_part, torch.float32, "out_part"), _dev(lse_part, torch.float32, "lse_part"),
         B, Lq, S, Hq, Hkv, D, split_keys, float(softmax_scale), int(window), int(n_sink), float(softcap),
-        _slopes(alibi_slopes, Hq), _stream(stream)))
-    if lens_dev is not None:
-        torch.cuda.current_stream().synchronize()  # the kv_lens copy must outlive the launch
+        _slopes(alibi_slopes, Hq), ctypes.c_void_p(s.cuda_stream)))
     return out_part, lse_part
 
 
@@ -358,9 +405,13 @@ class RingCall:
                  window: int = 0, n_sink: int = 0, cu_seqlens=None, softmax_scale: float = 0.0, rank: int = -1,
                  ulysses_rank: int = 0, input_order: str = "natural", out_dtype=torch.float32,
                  merge_mode: int = 0, qkv_packed: bool = False, softcap: float = 0.0,
-                 alibi_slopes: Optional[torch.Tensor] = None):
+                 alibi_slopes: Optional[torch.Tensor] = None, out_layout: str = "heads",
+                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
         """q, k, v as [B,S,H,D] (varlen [T,H,D]); with qkv_packed, q is the packed [B,S,3,H,D] (varlen
-        [T,3,H,D]) tensor and k, v are None.  alibi_slopes: [Hq] f32 on the device, over all heads."""
+        [T,3,H,D]) tensor and k, v are None.  alibi_slopes: [Hq] f32 on the device, over all heads.
+        out_layout (one rank's share): "heads" -> out [B,L,Hq/ud,D], lse [B,Hq/ud,L] (head group u);
+        "seq" -> out [B,L,Hq,D], lse [B,Hq,L] after the Ulysses head -> seq relayout, of which this
+        call writes head group u (``out`` / ``lse`` may be given to let the ud calls share them)."""
         varlen = cu_seqlens is not None
         if qkv_packed:
             if varlen:
@@ -379,16 +430,25 @@ class RingCall:
         N, ud = ring_degree, ulysses_degree
         L = S // N
         Hl = Hq // ud
+        layout = {"heads": 0, "seq": 1}[out_layout]
         if rank < 0:
             out_shape = (S, Hq, D) if varlen else (B, S, Hq, D)
             lse_shape = (Hq, S) if varlen else (B, Hq, S)
         else:
-            out_shape = (L, Hl, D) if varlen else (B, L, Hl, D)
-            lse_shape = (Hl, L) if varlen else (B, Hl, L)
+            Ho = Hq if layout == 1 else Hl
+            out_shape = (L, Ho, D) if varlen else (B, L, Ho, D)
+            lse_shape = (Ho, L) if varlen else (B, Ho, L)
         self.q, self.k, self.v = q, k, v
-        self.out = torch.empty(out_shape, dtype=out_dtype, device=q.device)
-        self.lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
-        cu_dev, cu_host, nseq, _ = _cu(cu_seqlens, q.device)
+        self.out = out if out is not None else torch.empty(out_shape, dtype=out_dtype, device=q.device)
+        self.lse = lse if lse is not None else torch.empty(lse_shape, dtype=torch.float32, device=q.device)
+        if tuple(self.out.shape) != out_shape or self.out.dtype != out_dtype:
+            raise ValueError(f"out must be {list(out_shape)} {out_dtype}")
+        if tuple(self.lse.shape) != lse_shape:
+            raise ValueError(f"lse must be {list(lse_shape)}")
+        cu_dev, cu_host, nseq = _cu(cu_seqlens, q.device)
+        if cu_dev is not None:
+            # construction only: the device copy is complete before any stream a run() uses
+            torch.cuda.current_stream().synchronize()
         self._cu = (cu_dev, cu_host)
         a = RingArgs()
         a.q = _dev(q, torch.bfloat16, "q").value
@@ -410,8 +470,12 @@ class RingCall:
         a.softcap = float(softcap)
         sp = _slopes(alibi_slopes, Hq)
         a.alibi_slopes = sp.value if sp is not None else None
+        a.out_layout = layout
         self.alibi_slopes = alibi_slopes
         self.args = a
+        self.q_rows = L if rank >= 0 else S
+        self.Hl, self.Hkl = Hl, Hkv // ud
+        self.B_, self.S_, self.D_ = B, S, D
         nbytes = lib().usp_ring_fwd_workspace_size(ctypes.byref(a))
         if nbytes == 0:
             # either nothing is needed or the arguments are invalid: let the call report which
@@ -425,13 +489,23 @@ class RingCall:
         _check(lib().usp_ring_fwd(ctypes.byref(self.args), ws, self.ws_bytes, _stream(stream)))
         return self.out, self.lse
 
+    def stage(self, stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+        """The q, k, v rows exactly as this call's attention kernels read them (usp_ring_stage):
+        q [B, rows, Hq/ud, D] (rows = L for one rank, S for all), k / v [B, S, Hkv/ud, D] rank-major;
+        varlen drops B."""
+        dev = self.q.device
+        qs = torch.empty((self.B_, self.q_rows, self.Hl, self.D_), dtype=torch.bfloat16, device=dev)
+        ks = torch.empty((self.B_, self.S_, self.Hkl, self.D_), dtype=torch.bfloat16, device=dev)
+        vs = torch.empty_like(ks)
+        _check(lib().usp_ring_stage(ctypes.byref(self.args), _ptr(qs), _ptr(ks), _ptr(vs), _stream(stream)))
+        if self._cu[0] is not None:
+            qs, ks, vs = qs[0], ks[0], vs[0]
+        return qs, ks, vs
+
     def capture(self) -> "torch.cuda.CUDAGraph":
         """Records one usp_ring_fwd call into a HIP graph (torch.cuda.CUDAGraph) over this call's
-        buffers.  A warm call first builds and uploads the tile plans (the only synchronous work);
-        the recorded call then enqueues kernels only.  ``graph.replay()`` reruns it on the same
-        inputs / outputs."""
-        self.run()
-        torch.cuda.synchronize()
+        buffers.  The call only enqueues kernels (its tile plans are built on the device), so it is
+        recorded as it stands; ``graph.replay()`` reruns it on the same inputs / outputs."""
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             self.run(stream=torch.cuda.current_stream())
@@ -477,11 +551,8 @@ class RingBwdCall:
         return self.dq, self.dk, self.dv
 
     def capture(self) -> "torch.cuda.CUDAGraph":
-        """Records one usp_ring_bwd call into a HIP graph, after a warm call that builds the plans
-        (see RingCall.capture); the gradients are zeroed by a kernel inside the call, so replays
-        recompute them."""
-        self.run()
-        torch.cuda.synchronize()
+        """Records one usp_ring_bwd call into a HIP graph (see RingCall.capture); the gradients are
+        zeroed by a kernel inside the call, so replays recompute them."""
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             self.run(stream=torch.cuda.current_stream())
@@ -492,7 +563,9 @@ def ring_fwd(q, k, v, **kw) -> Tuple[torch.Tensor, torch.Tensor]:
     """All ring steps on one device (usp_ring_fwd); see RingCall for arguments."""
     call = RingCall(q, k, v, **kw)
     out = call.run()
-    torch.cuda.current_stream().synchronize()  # the workspace is released on return
+    # the workspace goes back to torch's stream-ordered cache, so later work on this stream is
+    # ordered after the call; other streams may not reuse it before the call has run
+    _on_stream(call.workspace, torch.cuda.current_stream())
     return out
 
 
@@ -503,16 +576,6 @@ KERNEL_CLASSES = {"attn": 0, "permute": 1, "relayout": 2, "merge": 3, "bwd_dq": 
 
 def timing_enable(on: bool = True) -> None:
     _check(lib().usp_timing_enable(int(on)))
-
-
-def plan_cache_size() -> int:
-    """Number of tile plans the library keeps on the devices (usp_plan_cache_size)."""
-    return int(lib().usp_plan_cache_size())
-
-
-def plan_cache_clear() -> None:
-    """Frees every cached tile plan (usp_plan_cache_clear); call at a quiet point."""
-    _check(lib().usp_plan_cache_clear())
 
 
 def timing_reset() -> None:
@@ -574,3 +637,29 @@ def plan_block_kv(Lq: int, Lk: int, D: int = 128, *, mask: str = "positional", q
                                ctypes.c_void_p(items.data_ptr()), ni.value, ctypes.c_void_p(runs.data_ptr()),
                                nr.value, ctypes.byref(ni), ctypes.byref(nr), ctypes.byref(tk), ctypes.byref(tq)))
     return items[:ni.value], runs[:nr.value], tk.value, tq.value
+
+
+def plan_block_device(Lq: int, Lk: int, *, mask: str = "positional", qmap: Optional[PosMap] = None,
+                      kmap: Optional[PosMap] = None, causal: bool = False, window: int = 0, n_sink: int = 0,
+                      cu_seqlens=None, accumulate: bool = False, kv_tiles: bool = False, device="cuda"):
+    """The device planner's plan of one block (usp_plan_block_device), read back:
+    (items [n,8] int32 in the kernels' order, runs [n*slots,4] int32, run_slots)."""
+    L = lib()
+    s = torch.cuda.current_stream()
+    cu_dev, cu_host, nseq = _cu(cu_seqlens, device, s)
+    qm = ctypes.byref(qmap) if qmap else None
+    km = ctypes.byref(kmap) if kmap else None
+    n, slots, need = _I64(0), ctypes.c_int32(0), _SZ(0)
+    args = (Lq, Lk, MASK[mask], qm, km, int(causal), int(window), int(n_sink), _ptr(cu_dev), _ptr(cu_host), nseq,
+            int(accumulate), int(kv_tiles))
+    _check(L.usp_plan_block_device(*args, None, 0, ctypes.byref(n), ctypes.byref(slots), ctypes.byref(need),
+                                   ctypes.c_void_p(s.cuda_stream)))
+    ws = torch.zeros(max(1, need.value), dtype=torch.uint8, device=device)
+    _check(L.usp_plan_block_device(*args, _ptr(ws), need.value, ctypes.byref(n), ctypes.byref(slots),
+                                   ctypes.byref(need), ctypes.c_void_p(s.cuda_stream)))
+    torch.cuda.synchronize()
+    nc = n.value
+    roff = (nc * 32 + 255) // 256 * 256
+    items = ws[:nc * 32].view(torch.int32).view(nc, 8).cpu()
+    runs = ws[roff:roff + nc * slots.value * 16].view(torch.int32).view(-1, 4).cpu()
+    return items, runs, slots.value

@@ -1,20 +1,21 @@
-// C ABI of libusp: argument validation, tile-plan cache, and the virtual
+// C ABI of libusp: argument validation, workspace layout and the virtual
 // ring driver.  Every entry point validates everything on the host before
-// enqueueing anything; see include/usp.h for the contract of each call.
+// enqueueing anything; the tile plans are built on the device into the
+// caller's workspace, so no call allocates, copies from the host or waits for
+// the device.  See include/usp.h for the contract of each call.
 
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
-#include <mutex>
 #include <string>
-#include <unordered_map>
 #include <vector>
 
-#include "usp_internal.h"
+#include "plan_core.h"
 
 namespace usp {
 
@@ -42,65 +43,6 @@ namespace {
   } while (0)
 
 constexpr int64_t kMaxI32 = 0x7fffffff;
-
-// ------------------------------------------------------------ plan cache
-std::mutex g_plan_mu;
-std::unordered_map<std::string, DevicePlan> g_plans;
-
-// Returns the device copy of the plan cached under `key`; builds it with
-// `build` and uploads it on a miss (one synchronous copy).
-template <typename F>
-usp_status device_plan(const std::string& key_in, F&& build, DevicePlan* out) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) {
-    set_error("hipGetDevice failed");
-    return USP_ERR_HIP;
-  }
-  const std::string key = std::to_string(dev) + "|" + key_in;
-  std::lock_guard<std::mutex> lock(g_plan_mu);
-  auto f = g_plans.find(key);
-  if (f != g_plans.end()) {
-    *out = f->second;
-    return USP_OK;
-  }
-  Plan plan;
-  build(plan);
-  finalize_plan(plan);
-  USP_CHECK(plan.items.size() <= (size_t)kMaxI32 && plan.runs.size() <= (size_t)kMaxI32,
-            USP_ERR_UNSUPPORTED, "tile plan too large");
-  DevicePlan dp;
-  dp.n_items = (int32_t)plan.items.size();
-  dp.n_runs = (int32_t)plan.runs.size();
-  const size_t ib = std::max<size_t>(1, plan.items.size()) * sizeof(WorkItem);
-  const size_t rb = std::max<size_t>(1, plan.runs.size()) * sizeof(Run);
-  if (hipMalloc(reinterpret_cast<void**>(&dp.items), ib) != hipSuccess ||
-      hipMalloc(reinterpret_cast<void**>(&dp.runs), rb) != hipSuccess) {
-    if (dp.items) (void)hipFree(dp.items);
-    set_error("hipMalloc of tile plan failed");
-    return USP_ERR_HIP;
-  }
-  hipError_t e = hipSuccess;
-  if (!plan.items.empty())
-    e = hipMemcpy(dp.items, plan.items.data(), plan.items.size() * sizeof(WorkItem), hipMemcpyHostToDevice);
-  if (e == hipSuccess && !plan.runs.empty())
-    e = hipMemcpy(dp.runs, plan.runs.data(), plan.runs.size() * sizeof(Run), hipMemcpyHostToDevice);
-  if (e != hipSuccess) {
-    (void)hipFree(dp.items);
-    (void)hipFree(dp.runs);
-    set_error("upload of tile plan failed: %s", hipGetErrorString(e));
-    return USP_ERR_HIP;
-  }
-  g_plans.emplace(key, dp);
-  *out = dp;
-  return USP_OK;
-}
-
-std::string cu_key(const int32_t* cu, int nseq) {
-  std::string s;
-  if (!cu) return "-";
-  for (int i = 0; i <= nseq; ++i) s += std::to_string(cu[i]) + ",";
-  return s;
-}
 
 // ------------------------------------------------------------ validation
 usp_status check_layout(int impl, int64_t S, int N, int b) {
@@ -215,17 +157,73 @@ usp_status setup_block_mask(int64_t Lq, int64_t Lk, usp_mask_class mask, const u
   return USP_OK;
 }
 
-// Items / runs of one block call (explicit class or positional).
-void build_block_plan(const BlockMaskSetup& su, int32_t Lq, int32_t Lk, const int32_t* cu_host,
-                      int accumulate, int32_t tile_m, Plan& plan) {
-  if (!su.empty) {
-    BlockSpec blk{su.qmap, su.kmap, Lq, Lk, 0, 0, tile_m};
-    plan_block(blk, su.ms, cu_host, accumulate, plan);
-  } else if (!accumulate) {
-    // EMPTY without accumulate: items with no runs write O = 0, LSE = -inf
-    for (int32_t t0 = 0; t0 < Lq; t0 += tile_m)
-      plan.items.push_back({t0, t0, std::min<int32_t>(tile_m, Lq - t0), 0, 0, 0, 0, 0});
-  }
+// ------------------------------------------------------------ tile plans
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Offsets (bytes, within a workspace) of one job's device buffers.
+struct JobSlots {
+  size_t items = 0, runs = 0, tmp = 0, cost = 0;
+};
+
+// Reserves J's buffers at `off` (advanced past them).
+JobSlots reserve_job(const PlanJob& J, size_t& off) {
+  const size_t C = (size_t)J.candidates();
+  JobSlots s;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + std::max<size_t>(bytes, 1));
+    return o;
+  };
+  s.items = take(C * sizeof(WorkItem));
+  s.runs = take(C * (size_t)J.cap * sizeof(Run));
+  s.tmp = take(C * sizeof(WorkItem));
+  s.cost = take(C * sizeof(int64_t));
+  return s;
+}
+
+void bind_job(PlanJob& J, const JobSlots& s, char* ws, const int32_t* cu_dev) {
+  J.items = reinterpret_cast<WorkItem*>(ws + s.items);
+  J.runs = reinterpret_cast<Run*>(ws + s.runs);
+  J.tmp = reinterpret_cast<WorkItem*>(ws + s.tmp);
+  J.cost = reinterpret_cast<int64_t*>(ws + s.cost);
+  J.cu = J.mask.nseq > 0 ? cu_dev : nullptr;
+}
+
+// Sets J.cap (run slots per item) and checks that run indices fit in int32.
+usp_status finish_job(PlanJob& J, const int32_t* cu_host) {
+  J.cap = job_cap(J, cu_host);
+  USP_CHECK(J.candidates() * J.cap <= kMaxI32, USP_ERR_UNSUPPORTED,
+            "tile plan too large (%lld items x %d run slots)", (long long)J.candidates(), J.cap);
+  return USP_OK;
+}
+
+// The job of one block call: query tiles (kind 0, forward and dQ) or key
+// tiles (kind 1, dK / dV) of the one block.
+PlanJob block_job(const BlockMaskSetup& su, int kind, int32_t tile, int32_t gran, int32_t acc_from_step) {
+  PlanJob J{};
+  J.qmap = su.qmap;
+  J.kmap = su.kmap;
+  J.mask = su.ms;
+  J.kind = kind;
+  J.tile = tile;
+  J.gran = gran;
+  J.acc_from_step = acc_from_step;
+  J.empty = su.empty ? 1 : 0;
+  J.ring = 0;
+  J.N = 1;
+  J.rank_lo = 0;
+  J.n_ranks = 1;
+  J.n_steps = 1;
+  J.one_rank = 1;
+  J.L = 0;
+  J.cpb = tile_count(kind == 0 ? su.qmap : su.kmap, tile);
+  return J;
+}
+
+// The two jobs of a backward block: dQ (query tiles) and dK / dV (key tiles).
+void bwd_block_jobs(const BlockMaskSetup& su, PlanJob* jq, PlanJob* jk) {
+  *jq = block_job(su, 0, kBwdTileM, kTileN, 0);
+  *jk = block_job(su, 1, kBwdTileK, kBwdTileQ, 0);
 }
 
 // Score modifiers in the kernels' raw-score units (ScoreMods).
@@ -248,21 +246,7 @@ usp_status make_mods(float softcap, const float* alibi, usp_mask_class mask, int
   return USP_OK;
 }
 
-std::string map_key(const PosMap& m) {
-  char buf[96];
-  snprintf(buf, sizeof(buf), "%d.%d.%d.%d.%d.%d", m.kind, m.N, m.rank, m.b, m.L, m.offset);
-  return buf;
-}
-
-std::string mask_key(const MaskSpec& ms) {
-  char buf[96];
-  snprintf(buf, sizeof(buf), "c%d.w%d.s%d.n%d.S%d", ms.causal, ms.window, ms.n_sink, ms.nseq, ms.S);
-  return buf;
-}
-
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
-
-inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
 }  // namespace usp
@@ -273,7 +257,7 @@ extern "C" {
 
 const char* usp_last_error(void) { return g_err.c_str(); }
 
-const char* usp_version(void) { return "usp-gfx950 0.1"; }
+const char* usp_version(void) { return "usp-gfx950 0.2"; }
 
 usp_status usp_permute(const void* in, void* out, int64_t outer, int64_t S, int64_t inner,
                        usp_dtype dt, usp_ring_impl impl, int ring_degree, int ulysses_degree,
@@ -343,30 +327,7 @@ usp_status usp_lse_merge(float* out_acc, float* lse_acc, const float* out_part, 
                           as_stream(stream));
 }
 
-int64_t usp_plan_cache_size(void) {
-  std::lock_guard<std::mutex> lock(g_plan_mu);
-  return (int64_t)g_plans.size();
-}
-
-usp_status usp_plan_cache_clear(void) {
-  std::lock_guard<std::mutex> lock(g_plan_mu);
-  usp_status st = USP_OK;
-  int cur = 0;
-  const bool have_dev = hipGetDevice(&cur) == hipSuccess;
-  for (auto& kv : g_plans) {
-    // the key starts with the plan's device ordinal
-    const int dev = std::atoi(kv.first.c_str());
-    if (have_dev && dev != cur) (void)hipSetDevice(dev);
-    if (hipFree(kv.second.items) != hipSuccess || hipFree(kv.second.runs) != hipSuccess) {
-      set_error("hipFree of a cached tile plan failed");
-      st = USP_ERR_HIP;
-    }
-  }
-  if (have_dev) (void)hipSetDevice(cur);
-  g_plans.clear();
-  return st;
-}
-
+// ------------------------------------------------------------ plan inspection
 usp_status usp_plan_block(int64_t Lq, int64_t Lk, int64_t D, usp_mask_class mask,
                           const usp_posmap* qmap, const usp_posmap* kmap, int causal, int window,
                           int n_sink, const int32_t* cu_seqlens_host, int nseq, int accumulate,
@@ -379,10 +340,15 @@ usp_status usp_plan_block(int64_t Lq, int64_t Lk, int64_t D, usp_mask_class mask
   usp_status st = setup_block_mask(Lq, Lk, mask, qmap, kmap, causal, window, n_sink, cu_seqlens_host,
                                    nseq, 1, &su);
   if (st != USP_OK) return st;
-  Plan plan;
   const int32_t tm = choose_tile_m(su.qmap);
-  build_block_plan(su, (int32_t)Lq, (int32_t)Lk, cu_seqlens_host, accumulate, tm, plan);
-  finalize_plan(plan);
+  Plan plan;
+  if (Lq > 0) {
+    PlanJob J = block_job(su, 0, tm, kTileN, accumulate ? 0 : INT_MAX);
+    st = finish_job(J, cu_seqlens_host);
+    if (st != USP_OK) return st;
+    USP_CHECK(plan_job_host(J, cu_seqlens_host, 0, plan), USP_ERR_UNSUPPORTED,
+              "internal: an item needs more than %d run slots", J.cap);
+  }
   *n_items = (int64_t)plan.items.size();
   *n_runs = (int64_t)plan.runs.size();
   if (tile_m) *tile_m = tm;
@@ -411,11 +377,13 @@ usp_status usp_plan_block_kv(int64_t Lq, int64_t Lk, int64_t D, usp_mask_class m
                                    nseq, 1, &su);
   if (st != USP_OK) return st;
   Plan plan;
-  if (!su.empty) {
-    BlockSpec blk{su.qmap, su.kmap, (int32_t)Lq, (int32_t)Lk, 0, 0, kBwdTileM};
-    plan_block_kv(blk, su.ms, cu_seqlens_host, kBwdTileK, kBwdTileQ, plan);
+  if (Lk > 0 && Lq > 0 && !su.empty) {
+    PlanJob J = block_job(su, 1, kBwdTileK, kBwdTileQ, 0);
+    st = finish_job(J, cu_seqlens_host);
+    if (st != USP_OK) return st;
+    USP_CHECK(plan_job_host(J, cu_seqlens_host, 0, plan), USP_ERR_UNSUPPORTED,
+              "internal: an item needs more than %d run slots", J.cap);
   }
-  finalize_plan(plan);
   *n_items = (int64_t)plan.items.size();
   *n_runs = (int64_t)plan.runs.size();
   if (tile_k) *tile_k = kBwdTileK;
@@ -431,13 +399,61 @@ usp_status usp_plan_block_kv(int64_t Lq, int64_t Lk, int64_t D, usp_mask_class m
   return USP_OK;
 }
 
+usp_status usp_plan_block_device(int64_t Lq, int64_t Lk, usp_mask_class mask, const usp_posmap* qmap,
+                                 const usp_posmap* kmap, int causal, int window, int n_sink,
+                                 const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int nseq,
+                                 int accumulate, int kv_tiles, void* workspace, size_t ws_bytes,
+                                 int64_t* n_candidates, int32_t* run_slots, size_t* ws_needed, void* stream) {
+  USP_CHECK(n_candidates && run_slots && ws_needed, USP_ERR_INVALID_ARG, "null count pointer");
+  USP_CHECK(Lq >= 1 && Lk >= 0 && Lq <= kMaxI32 / 2 && Lk <= kMaxI32 / 2, USP_ERR_INVALID_ARG, "bad Lq/Lk");
+  USP_CHECK(kv_tiles == 0 || kv_tiles == 1, USP_ERR_INVALID_ARG, "kv_tiles must be 0 or 1");
+  USP_CHECK((cu_seqlens_host == nullptr) == (cu_seqlens_dev == nullptr), USP_ERR_INVALID_ARG,
+            "cu_seqlens must be given on both host and device, or neither");
+  BlockMaskSetup su;
+  usp_status st = setup_block_mask(Lq, Lk, mask, qmap, kmap, causal, window, n_sink, cu_seqlens_host,
+                                   nseq, 1, &su);
+  if (st != USP_OK) return st;
+  PlanJob J = kv_tiles ? block_job(su, 1, kBwdTileK, kBwdTileQ, 0)
+                       : block_job(su, 0, choose_tile_m(su.qmap), kTileN, accumulate ? 0 : INT_MAX);
+  st = finish_job(J, cu_seqlens_host);
+  if (st != USP_OK) return st;
+  size_t need = 0;
+  const JobSlots js = reserve_job(J, need);
+  *n_candidates = J.candidates();
+  *run_slots = J.cap;
+  *ws_needed = need;
+  if (!workspace) return USP_OK;
+  USP_CHECK(ws_bytes >= need, USP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  USP_CHECK(((uintptr_t)workspace & 255) == 0, USP_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  bind_job(J, js, static_cast<char*>(workspace), cu_seqlens_dev);
+  PlanJobs jobs{};
+  jobs.j[0] = J;
+  jobs.n = 1;
+  return launch_plan(jobs, as_stream(stream));
+}
+
+// ------------------------------------------------------------ block attention
+size_t usp_block_attn_fwd_workspace_size(int64_t Lq, int64_t Lk, usp_mask_class mask, const usp_posmap* qmap,
+                                         const usp_posmap* kmap, int causal, int window, int n_sink,
+                                         const int32_t* cu_seqlens_host, int nseq) {
+  if (Lq <= 0 || Lk < 0 || Lq > kMaxI32 / 2 || Lk > kMaxI32 / 2) return 0;
+  BlockMaskSetup su;
+  if (setup_block_mask(Lq, Lk, mask, qmap, kmap, causal, window, n_sink, cu_seqlens_host, nseq, 1, &su) != USP_OK)
+    return 0;
+  PlanJob J = block_job(su, 0, choose_tile_m(su.qmap), kTileN, 0);
+  if (finish_job(J, cu_seqlens_host) != USP_OK) return 0;
+  size_t off = 0;
+  reserve_job(J, off);
+  return off;
+}
+
 usp_status usp_block_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                               int64_t B, int64_t Lq, int64_t Lk, int64_t Hq, int64_t Hkv, int64_t D,
                               float softmax_scale, usp_mask_class mask, const usp_posmap* qmap,
                               const usp_posmap* kmap, int causal, int window, int n_sink,
                               const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int nseq,
                               usp_dtype out_dt, int accumulate, float softcap, const float* alibi_slopes,
-                              void* stream) {
+                              void* workspace, size_t ws_bytes, void* stream) {
   USP_CHECK(B >= 1 && Lq >= 0 && Lk >= 0 && Hq >= 1 && Hkv >= 1, USP_ERR_INVALID_ARG, "bad sizes");
   // k / v are never read without keys, q / out / lse never touched without queries
   USP_CHECK((q && out && lse) || Lq == 0, USP_ERR_INVALID_ARG, "null q / out / lse pointer");
@@ -463,13 +479,22 @@ usp_status usp_block_attn_fwd(const void* q, const void* k, const void* v, void*
   if (Lq == 0) return USP_OK;
 
   const int32_t tm = choose_tile_m(su.qmap);
-  std::string key = "blk|" + std::to_string(Lq) + "|" + std::to_string(Lk) + "|" + map_key(su.qmap) + "|" +
-                    map_key(su.kmap) + "|" + mask_key(su.ms) + "|" + cu_key(su.ms.nseq ? cu_seqlens_host : nullptr, nseq) +
-                    "|a" + std::to_string(accumulate) + "|e" + std::to_string(su.empty) + "|m" + std::to_string(tm);
-  DevicePlan dp;
-  st = device_plan(key, [&](Plan& plan) {
-    build_block_plan(su, (int32_t)Lq, (int32_t)Lk, cu_seqlens_host, accumulate, tm, plan);
-  }, &dp);
+  PlanJob J = block_job(su, 0, tm, kTileN, accumulate ? 0 : INT_MAX);
+  st = finish_job(J, cu_seqlens_host);
+  if (st != USP_OK) return st;
+  size_t need = 0;
+  const JobSlots js = reserve_job(J, need);
+  USP_CHECK(workspace && ws_bytes >= need, USP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+            workspace ? ws_bytes : (size_t)0);
+  USP_CHECK(((uintptr_t)workspace & 255) == 0, USP_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  // a partial with no visible pair changes nothing when merged
+  if (accumulate && (su.empty || !block_has_work(su.qmap, su.kmap, su.ms, cu_seqlens_host))) return USP_OK;
+  bind_job(J, js, static_cast<char*>(workspace), cu_seqlens_dev);
+  PlanJobs jobs{};
+  jobs.j[0] = J;
+  jobs.n = 1;
+  const hipStream_t stream_h = as_stream(stream);
+  st = launch_plan(jobs, stream_h);
   if (st != USP_OK) return st;
 
   AttnParams p{};
@@ -478,14 +503,16 @@ usp_status usp_block_attn_fwd(const void* q, const void* k, const void* v, void*
   p.v = static_cast<const uint16_t*>(v);
   p.out = out;
   p.lse = lse;
-  p.items = dp.items;
-  p.runs = dp.runs;
+  p.items = J.items;
+  p.runs = J.runs;
   p.cu_seqlens = su.ms.nseq ? cu_seqlens_dev : nullptr;
   p.q_batch_stride = Lq * Hq * D;
   p.o_batch_stride = Lq * Hq * D;
   p.kv_batch_stride = Lk * Hkv * D;
   p.Lq_buf = (int32_t)Lq;
-  p.n_items = dp.n_items;
+  p.o_heads = (int32_t)Hq;
+  p.o_head0 = 0;
+  p.n_items = (int32_t)J.cpp();
   p.B = (int32_t)B;
   p.Hq = (int32_t)Hq;
   p.Hkv = (int32_t)Hkv;
@@ -497,7 +524,7 @@ usp_status usp_block_attn_fwd(const void* q, const void* k, const void* v, void*
   p.kmap = su.kmap;
   p.mask = su.ms;
   p.mods = mods;
-  return launch_attn_fwd(p, (int)D, as_stream(stream));
+  return launch_attn_fwd(p, (int)D, stream_h);
 }
 
 usp_status usp_attn_bwd_preprocess(const void* out, usp_dtype out_dt, const void* dout, float* delta,
@@ -513,13 +540,30 @@ usp_status usp_attn_bwd_preprocess(const void* out, usp_dtype out_dt, const void
                           as_stream(stream));
 }
 
+size_t usp_block_attn_bwd_workspace_size(int64_t Lq, int64_t Lk, usp_mask_class mask, const usp_posmap* qmap,
+                                         const usp_posmap* kmap, int causal, int window, int n_sink,
+                                         const int32_t* cu_seqlens_host, int nseq) {
+  if (Lq <= 0 || Lk <= 0 || Lq > kMaxI32 / 2 || Lk > kMaxI32 / 2) return 0;
+  BlockMaskSetup su;
+  if (setup_block_mask(Lq, Lk, mask, qmap, kmap, causal, window, n_sink, cu_seqlens_host, nseq, 1, &su) != USP_OK)
+    return 0;
+  if (su.empty) return 0;
+  PlanJob jq, jk;
+  bwd_block_jobs(su, &jq, &jk);
+  if (finish_job(jq, cu_seqlens_host) != USP_OK || finish_job(jk, cu_seqlens_host) != USP_OK) return 0;
+  size_t off = 0;
+  reserve_job(jq, off);
+  reserve_job(jk, off);
+  return off;
+}
+
 usp_status usp_block_attn_bwd(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                               const float* delta, float* dq, float* dk, float* dv, int64_t B, int64_t Lq,
                               int64_t Lk, int64_t Hq, int64_t Hkv, int64_t D, float softmax_scale,
                               usp_mask_class mask, const usp_posmap* qmap, const usp_posmap* kmap, int causal,
                               int window, int n_sink, const int32_t* cu_seqlens_dev,
                               const int32_t* cu_seqlens_host, int nseq, float softcap,
-                              const float* alibi_slopes, void* stream) {
+                              const float* alibi_slopes, void* workspace, size_t ws_bytes, void* stream) {
   USP_CHECK(q && k && v && dout && lse && delta && dq && dk && dv, USP_ERR_INVALID_ARG, "null tensor pointer");
   USP_CHECK(B >= 1 && Lq >= 0 && Lk >= 0 && Hq >= 1 && Hkv >= 1, USP_ERR_INVALID_ARG, "bad sizes");
   USP_CHECK(D == 64 || D == 128, USP_ERR_UNSUPPORTED, "head_dim must be 64 or 128, got %lld", (long long)D);
@@ -540,18 +584,26 @@ usp_status usp_block_attn_bwd(const void* q, const void* k, const void* v, const
   if (st != USP_OK) return st;
   if (Lq == 0 || Lk == 0 || su.empty) return USP_OK;
 
-  const std::string base = std::to_string(Lq) + "|" + std::to_string(Lk) + "|" + map_key(su.qmap) + "|" +
-                           map_key(su.kmap) + "|" + mask_key(su.ms) + "|" +
-                           cu_key(su.ms.nseq ? cu_seqlens_host : nullptr, nseq);
-  DevicePlan dpq, dpk;
-  st = device_plan("bwdq|" + base, [&](Plan& plan) {
-    build_block_plan(su, (int32_t)Lq, (int32_t)Lk, cu_seqlens_host, 1, kBwdTileM, plan);
-  }, &dpq);
+  PlanJob jq, jk;
+  bwd_block_jobs(su, &jq, &jk);
+  st = finish_job(jq, cu_seqlens_host);
+  if (st == USP_OK) st = finish_job(jk, cu_seqlens_host);
   if (st != USP_OK) return st;
-  st = device_plan("bwdkv|" + base, [&](Plan& plan) {
-    BlockSpec blk{su.qmap, su.kmap, (int32_t)Lq, (int32_t)Lk, 0, 0, kBwdTileM};
-    plan_block_kv(blk, su.ms, cu_seqlens_host, kBwdTileK, kBwdTileQ, plan);
-  }, &dpk);
+  size_t need = 0;
+  const JobSlots sq = reserve_job(jq, need);
+  const JobSlots sk = reserve_job(jk, need);
+  USP_CHECK(workspace && ws_bytes >= need, USP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+            workspace ? ws_bytes : (size_t)0);
+  USP_CHECK(((uintptr_t)workspace & 255) == 0, USP_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (!block_has_work(su.qmap, su.kmap, su.ms, cu_seqlens_host)) return USP_OK;
+  bind_job(jq, sq, static_cast<char*>(workspace), cu_seqlens_dev);
+  bind_job(jk, sk, static_cast<char*>(workspace), cu_seqlens_dev);
+  PlanJobs jobs{};
+  jobs.j[0] = jq;
+  jobs.j[1] = jk;
+  jobs.n = 2;
+  const hipStream_t stream_h = as_stream(stream);
+  st = launch_plan(jobs, stream_h);
   if (st != USP_OK) return st;
 
   BwdParams p{};
@@ -579,13 +631,13 @@ usp_status usp_block_attn_bwd(const void* q, const void* k, const void* v, const
   p.mask = su.ms;
   p.mods = mods;
   BwdParams pq = p, pk = p;
-  pq.items = dpq.items;
-  pq.runs = dpq.runs;
-  pq.n_items = dpq.n_items;
-  pk.items = dpk.items;
-  pk.runs = dpk.runs;
-  pk.n_items = dpk.n_items;
-  return launch_bwd(pq, pk, (int)D, as_stream(stream));
+  pq.items = jq.items;
+  pq.runs = jq.runs;
+  pq.n_items = (int32_t)jq.cpp();
+  pk.items = jk.items;
+  pk.runs = jk.runs;
+  pk.n_items = (int32_t)jk.cpp();
+  return launch_bwd(pq, pk, (int)D, stream_h);
 }
 
 usp_status usp_decode_split_fwd(const void* q, const void* k, const void* v, const int32_t* kv_lens_dev,
@@ -654,15 +706,20 @@ usp_status usp_decode_merge(float* out_part, float* lse_part, int64_t n_split, i
 // ------------------------------------------------------------ virtual ring
 namespace {
 
+constexpr size_t NONE = SIZE_MAX;
+
 struct RingLayout {
   bool one;          // one rank's share
   bool need_perm;    // natural-order input with a non-basic layout
-  bool copy_in;      // q, k, v copied into the workspace (permutation or packed input)
+  bool copy_in;      // q, k, v copied into the workspace (permutation, packed input, head group)
+  bool seq_out;      // out_layout 1 with ud > 1: output rows hold every head, this call writes group u
   int64_t L, Ls;     // rows per ring rank, per Ulysses piece
   int64_t Hq_l, Hkv_l;
   int64_t q_rows;    // rows of the q buffer the kernel reads (per batch)
-  // workspace offsets (bytes), SIZE_MAX if unused
-  size_t off_qp, off_kp, off_vp, off_ql, off_kl, off_vl, off_oacc, off_lacc, off_opart, off_lpart;
+  // workspace offsets (bytes), NONE if unused
+  size_t off_q, off_k, off_v, off_oacc, off_lacc, off_opart, off_lpart;
+  PlanJob job;       // the ring's tile plans (one per step)
+  JobSlots slots;
   size_t total;
   bool out_is_acc;   // accumulate straight into out / lse
 };
@@ -679,6 +736,7 @@ usp_status check_ring_args(const usp_ring_args* a) {
   USP_CHECK(a->Hq % a->Hkv == 0, USP_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
   usp_status st = check_layout(a->impl, a->S, a->ring_degree, a->stripe_block);
   if (st != USP_OK) return st;
+  USP_CHECK(a->ring_degree <= 65535, USP_ERR_UNSUPPORTED, "ring_degree must be at most 65535");
   USP_CHECK(a->ulysses_degree >= 1 && a->ulysses_degree <= 8, USP_ERR_UNSUPPORTED, "ulysses_degree must be in [1, 8]");
   USP_CHECK(a->Hq % a->ulysses_degree == 0 && a->Hkv % a->ulysses_degree == 0, USP_ERR_INVALID_ARG,
             "ulysses_degree %d must divide Hq (%lld) and Hkv (%lld)", a->ulysses_degree, (long long)a->Hq,
@@ -692,6 +750,9 @@ usp_status check_ring_args(const usp_ring_args* a) {
   USP_CHECK(a->input_order == 0 || a->input_order == 1, USP_ERR_INVALID_ARG, "input_order must be 0 or 1");
   USP_CHECK(a->out_dtype == USP_DT_BF16 || a->out_dtype == USP_DT_F32, USP_ERR_INVALID_ARG, "bad out dtype");
   USP_CHECK(a->merge_mode == 0 || a->merge_mode == 1, USP_ERR_INVALID_ARG, "merge_mode must be 0 or 1");
+  USP_CHECK(a->out_layout == 0 || a->out_layout == 1, USP_ERR_INVALID_ARG, "out_layout must be 0 or 1");
+  USP_CHECK(a->out_layout == 0 || a->rank >= 0, USP_ERR_INVALID_ARG,
+            "out_layout 1 (Ulysses sequence shards) needs one rank's share (rank >= 0)");
   USP_CHECK(std::isfinite(a->softmax_scale), USP_ERR_INVALID_ARG, "softmax_scale must be finite");
   USP_CHECK(std::isfinite(a->softcap) && a->softcap >= 0.f, USP_ERR_INVALID_ARG, "softcap must be finite and >= 0");
   USP_CHECK(!a->alibi_slopes || a->S <= kMaxAlibiPositions, USP_ERR_UNSUPPORTED,
@@ -716,19 +777,77 @@ usp_status ring_mods(const usp_ring_args* a, int64_t Hq_l, float scale, ScoreMod
   return make_mods(a->softcap, slopes, USP_MASK_POSITIONAL, a->S, scale, out);
 }
 
-RingLayout ring_layout(const usp_ring_args* a) {
-  RingLayout r;
-  const size_t NONE = SIZE_MAX;
+MaskSpec ring_mask(const usp_ring_args* a) {
+  MaskSpec ms;
+  ms.causal = a->causal ? 1 : 0;
+  ms.window = a->window;
+  ms.n_sink = a->n_sink;
+  ms.nseq = a->cu_seqlens_host ? a->nseq : 0;
+  ms.S = (int32_t)a->S;
+  return ms;
+}
+
+PosMap ring_base_map(const usp_ring_args* a) {
+  usp_posmap pm{a->impl, a->ring_degree, 0, a->impl == USP_RING_STRIPE ? a->stripe_block : 1, a->S};
+  return make_map(pm);
+}
+
+// The ring's plan job: plan s is ring step s, its blocks the hosts i (all,
+// or the one rank) against KV piece (i - s) mod N.
+PlanJob ring_job(const usp_ring_args* a, int kind, int32_t tile, int32_t gran, int32_t acc_from_step) {
+  const int N = a->ring_degree;
+  const bool one = a->rank >= 0;
+  PlanJob J{};
+  J.qmap = J.kmap = ring_base_map(a);
+  J.mask = ring_mask(a);
+  J.kind = kind;
+  J.tile = tile;
+  J.gran = gran;
+  J.acc_from_step = acc_from_step;
+  J.empty = 0;
+  J.ring = 1;
+  J.N = N;
+  J.rank_lo = one ? a->rank : 0;
+  J.n_ranks = one ? 1 : N;
+  J.n_steps = N;
+  J.one_rank = one ? 1 : 0;
+  J.L = (int32_t)(a->S / N);
+  J.cpb = tile_count(J.qmap, tile);
+  return J;
+}
+
+// Staging regions of q, k, v (shared by the forward and backward layouts).
+void reserve_staging(const usp_ring_args* a, RingLayout& r, size_t& off) {
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  const size_t D = (size_t)a->D, B = (size_t)a->B, S = (size_t)a->S;
+  r.off_q = r.off_k = r.off_v = NONE;
+  if (r.copy_in) {
+    r.off_q = take(B * (size_t)r.q_rows * r.Hq_l * D * 2);
+    r.off_k = take(B * S * r.Hkv_l * D * 2);
+    r.off_v = take(B * S * r.Hkv_l * D * 2);
+  }
+}
+
+void ring_shape(const usp_ring_args* a, RingLayout& r) {
   r.one = a->rank >= 0;
   r.need_perm = a->input_order == 0 && a->impl != USP_RING_BASIC;
-  r.copy_in = r.need_perm || a->qkv_packed;
-  r.L = a->S / a->ring_degree;
   const int ud = a->ulysses_degree;
+  r.copy_in = r.need_perm || a->qkv_packed || ud > 1;
+  r.seq_out = a->out_layout == 1 && ud > 1;
+  r.L = a->S / a->ring_degree;
   r.Ls = r.L / ud;
   r.Hq_l = a->Hq / ud;
   r.Hkv_l = a->Hkv / ud;
   r.q_rows = r.one ? r.L : a->S;
-  r.off_qp = r.off_kp = r.off_vp = r.off_ql = r.off_kl = r.off_vl = NONE;
+}
+
+usp_status ring_layout(const usp_ring_args* a, RingLayout* out) {
+  RingLayout r;
+  ring_shape(a, r);
   r.off_oacc = r.off_lacc = r.off_opart = r.off_lpart = NONE;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -736,20 +855,12 @@ RingLayout ring_layout(const usp_ring_args* a) {
     off = align256(off + bytes);
     return o;
   };
-  const size_t D = (size_t)a->D, B = (size_t)a->B, S = (size_t)a->S;
-  if (r.copy_in && ud == 1) {
-    r.off_qp = take(B * (size_t)r.q_rows * a->Hq * D * 2);
-    r.off_kp = take(B * S * a->Hkv * D * 2);
-    r.off_vp = take(B * S * a->Hkv * D * 2);
-  }
-  if (ud > 1) {
-    r.off_ql = take(B * (size_t)r.L * r.Hq_l * D * 2);
-    r.off_kl = take(B * S * r.Hkv_l * D * 2);
-    r.off_vl = take(B * S * r.Hkv_l * D * 2);
-  }
+  reserve_staging(a, r, off);
+  const size_t D = (size_t)a->D, B = (size_t)a->B;
   // accumulate directly into out/lse when they are f32 and already in the
-  // order the kernel computes in
-  r.out_is_acc = a->out_dtype == USP_DT_F32 && (r.one || !r.need_perm);
+  // order the kernel computes in (the merge kernel works on dense rows, so a
+  // sequence-shard output with merge_mode 1 goes through the accumulator)
+  r.out_is_acc = a->out_dtype == USP_DT_F32 && (r.one || !r.need_perm) && !(r.seq_out && a->merge_mode == 1);
   if (!r.out_is_acc) {
     r.off_oacc = take(B * (size_t)r.q_rows * r.Hq_l * D * 4);
     r.off_lacc = take(B * (size_t)r.Hq_l * r.q_rows * 4);
@@ -758,13 +869,33 @@ RingLayout ring_layout(const usp_ring_args* a) {
     r.off_opart = take(B * (size_t)r.q_rows * r.Hq_l * D * 4);
     r.off_lpart = take(B * (size_t)r.Hq_l * r.q_rows * 4);
   }
+  r.job = ring_job(a, 0, choose_tile_m(ring_base_map(a)), kTileN, a->merge_mode == 0 ? 1 : INT_MAX);
+  usp_status st = finish_job(r.job, a->cu_seqlens_host);
+  if (st != USP_OK) return st;
+  r.slots = reserve_job(r.job, off);
   r.total = off;
-  return r;
+  *out = r;
+  return USP_OK;
+}
+
+// Identity row map (row i -> row i) over rows of `rows` per outer slice.
+GatherSpec identity_rows(int64_t rows, int kind) {
+  GatherSpec gs{};
+  gs.impl = USP_RING_BASIC;
+  gs.N = 1;
+  gs.ud = 1;
+  gs.b = 1;
+  gs.g = 0;
+  gs.L = (int32_t)rows;
+  gs.S = (int32_t)rows;
+  gs.kind = kind;
+  return gs;
 }
 
 // Steps 1-2 of the ring (shared by forward and backward): token order
 // (rank-major q, or ring rank r's rows; k, v), then the Ulysses seq -> head
-// relayout for Ulysses rank u.  Uses the workspace regions of `R`.
+// relayout for Ulysses rank u, written to qd, kd, vd when the ring reads
+// copies (R.copy_in).
 //
 // With ulysses_degree > 1 the two steps are one strided copy per tensor.
 // Ulysses rank u gathers, for each ring rank, the ud sub-shards of that
@@ -780,128 +911,76 @@ struct Staged {
   int64_t Hq_l, Hkv_l;   // heads after the Ulysses split
 };
 
-usp_status stage_ring_inputs(const usp_ring_args* a, const RingLayout& R, char* ws, hipStream_t stream,
-                             Staged* out) {
-  usp_status st = USP_OK;
+usp_status stage_ring_inputs(const usp_ring_args* a, const RingLayout& R, uint16_t* qd, uint16_t* kd,
+                             uint16_t* vd, hipStream_t stream, Staged* out) {
   const int N = a->ring_degree, ud = a->ulysses_degree, u = a->ulysses_rank;
   const int64_t B = a->B, S = a->S, D = a->D, L = R.L;
   const int b = a->impl == USP_RING_STRIPE ? a->stripe_block : 1;
-  if (ud > 1) {
-    // rows in ring order (all pieces of k and v; ring rank r's rows of q),
-    // heads of group u, from natural or rank-major order, packed or not
-    const int64_t Hq_l = R.Hq_l, Hkv_l = R.Hkv_l;
-    const int64_t q_row = a->Hq * D * 2, kv_row = a->Hkv * D * 2;  // source row bytes (one tensor)
-    const int64_t src_stride_q = a->qkv_packed ? 3 * q_row : q_row;
-    const int64_t src_stride_kv = a->qkv_packed ? 3 * kv_row : kv_row;
-    const char* qb = static_cast<const char*>(a->q);
-    const char* kb = a->qkv_packed ? qb + q_row : static_cast<const char*>(a->k);
-    const char* vb = a->qkv_packed ? qb + 2 * q_row : static_cast<const char*>(a->v);
-    auto spec = [&](bool extract) {
-      GatherSpec gs{};
-      gs.impl = R.need_perm ? a->impl : USP_RING_BASIC;
-      gs.N = N;
-      gs.ud = 1;
-      gs.b = R.need_perm ? b : 1;
-      gs.g = extract ? a->rank : 0;
-      gs.L = (int32_t)L;
-      gs.S = (int32_t)S;
-      gs.kind = extract ? G_EXTRACT : G_PERMUTE;
-      return gs;
-    };
-    uint16_t* ql = reinterpret_cast<uint16_t*>(ws + R.off_ql);
-    uint16_t* kl = reinterpret_cast<uint16_t*>(ws + R.off_kl);
-    uint16_t* vl = reinterpret_cast<uint16_t*>(ws + R.off_vl);
-    st = launch_permute_strided(kb + u * Hkv_l * D * 2, kl, B, S, S, Hkv_l * D * 2, src_stride_kv,
-                                Hkv_l * D * 2, spec(false), stream);
-    if (st == USP_OK)
-      st = launch_permute_strided(vb + u * Hkv_l * D * 2, vl, B, S, S, Hkv_l * D * 2, src_stride_kv,
-                                  Hkv_l * D * 2, spec(false), stream);
-    if (st == USP_OK)
-      st = launch_permute_strided(qb + u * Hq_l * D * 2, ql, B, S, L, Hq_l * D * 2, src_stride_q,
-                                  Hq_l * D * 2, spec(true), stream);
-    if (st != USP_OK) return st;
-    *out = Staged{ql, kl, vl, L, 0, Hq_l, Hkv_l};
+  if (!R.copy_in) {
+    // the caller's rank-major (or basic-layout) tensors are read in place
+    *out = Staged{static_cast<const uint16_t*>(a->q), static_cast<const uint16_t*>(a->k),
+                  static_cast<const uint16_t*>(a->v), S, R.one ? (int64_t)a->rank * L : 0, a->Hq, a->Hkv};
     return USP_OK;
   }
-
-  // 1. token order: rank-major q (or ring rank r's rows), k, v
-  const uint16_t* qsrc = static_cast<const uint16_t*>(a->q);
-  const uint16_t* ksrc = static_cast<const uint16_t*>(a->k);
-  const uint16_t* vsrc = static_cast<const uint16_t*>(a->v);
-  int64_t q_batch_rows = S;   // rows between batches in the q buffer
-  int64_t q_row_off = 0;      // first row of the rank's q rows
-  if (a->qkv_packed) {
-    // rows of the packed [B,S,3,H,D] tensor hold q, k, v one after the other:
-    // copy each slice out (and into rank-major order when the input is
-    // natural-order with a non-basic layout; the rank's rows only for q in
-    // one-rank mode)
-    const int64_t H = a->Hq, slice = H * D * 2;
-    const char* base = static_cast<const char*>(a->q);
-    auto spec = [&](bool extract) {
-      GatherSpec gs{};
-      gs.impl = R.need_perm ? a->impl : USP_RING_BASIC;
-      gs.N = N;
-      gs.ud = 1;
-      gs.b = R.need_perm ? b : 1;
-      gs.g = extract ? a->rank : 0;
-      gs.L = (int32_t)L;
-      gs.S = (int32_t)S;
-      gs.kind = extract ? G_EXTRACT : G_PERMUTE;
-      return gs;
-    };
-    uint16_t* qp = reinterpret_cast<uint16_t*>(ws + R.off_qp);
-    uint16_t* kp = reinterpret_cast<uint16_t*>(ws + R.off_kp);
-    uint16_t* vp = reinterpret_cast<uint16_t*>(ws + R.off_vp);
-    st = launch_permute_strided(base + slice, kp, B, S, S, slice, 3 * slice, slice, spec(false), stream);
-    if (st == USP_OK)
-      st = launch_permute_strided(base + 2 * slice, vp, B, S, S, slice, 3 * slice, slice, spec(false), stream);
-    if (st == USP_OK)
-      st = launch_permute_strided(base, qp, B, S, R.q_rows, slice, 3 * slice, slice, spec(R.one), stream);
-    if (st != USP_OK) return st;
-    qsrc = qp;
-    ksrc = kp;
-    vsrc = vp;
-    q_batch_rows = R.q_rows;
-  } else if (R.need_perm) {
-    uint16_t* qp = reinterpret_cast<uint16_t*>(ws + R.off_qp);
-    uint16_t* kp = reinterpret_cast<uint16_t*>(ws + R.off_kp);
-    uint16_t* vp = reinterpret_cast<uint16_t*>(ws + R.off_vp);
-    st = usp_permute(a->k, kp, B, S, a->Hkv * D, USP_DT_BF16, (usp_ring_impl)a->impl, N, 1, b, -1, 0, stream);
-    if (st == USP_OK)
-      st = usp_permute(a->v, vp, B, S, a->Hkv * D, USP_DT_BF16, (usp_ring_impl)a->impl, N, 1, b, -1, 0, stream);
-    if (st == USP_OK)
-      st = usp_permute(a->q, qp, B, S, a->Hq * D, USP_DT_BF16, (usp_ring_impl)a->impl, N, 1, b,
-                       R.one ? a->rank : -1, 0, stream);
-    if (st != USP_OK) return st;
-    qsrc = qp;
-    ksrc = kp;
-    vsrc = vp;
-    q_batch_rows = R.q_rows;
-  } else if (R.one) {
-    q_row_off = (int64_t)a->rank * L;
-  }
-
-  *out = Staged{qsrc, ksrc, vsrc, q_batch_rows, q_row_off, a->Hq, a->Hkv};
+  // rows in ring order (all pieces of k and v; every rank's rows of q, or
+  // ring rank r's), heads of group u, from natural or rank-major order,
+  // packed or not: one strided row gather per tensor
+  const int64_t Hq_l = R.Hq_l, Hkv_l = R.Hkv_l;
+  const int64_t q_row = a->Hq * D * 2, kv_row = a->Hkv * D * 2;  // source row bytes (one tensor)
+  const int64_t src_stride_q = a->qkv_packed ? 3 * q_row : q_row;
+  const int64_t src_stride_kv = a->qkv_packed ? 3 * kv_row : kv_row;
+  const char* qb = static_cast<const char*>(a->q);
+  const char* kb = a->qkv_packed ? qb + q_row : static_cast<const char*>(a->k);
+  const char* vb = a->qkv_packed ? qb + 2 * q_row : static_cast<const char*>(a->v);
+  auto spec = [&](bool extract) {
+    GatherSpec gs{};
+    gs.impl = R.need_perm ? a->impl : USP_RING_BASIC;
+    gs.N = N;
+    gs.ud = 1;
+    gs.b = R.need_perm ? b : 1;
+    gs.g = extract ? a->rank : 0;
+    gs.L = (int32_t)L;
+    gs.S = (int32_t)S;
+    gs.kind = extract ? G_EXTRACT : G_PERMUTE;
+    return gs;
+  };
+  usp_status st = launch_permute_strided(kb + u * Hkv_l * D * 2, kd, B, S, S, Hkv_l * D * 2, src_stride_kv,
+                                         Hkv_l * D * 2, spec(false), stream);
+  if (st == USP_OK)
+    st = launch_permute_strided(vb + u * Hkv_l * D * 2, vd, B, S, S, Hkv_l * D * 2, src_stride_kv, Hkv_l * D * 2,
+                                spec(false), stream);
+  if (st == USP_OK)
+    st = launch_permute_strided(qb + u * Hq_l * D * 2, qd, B, S, R.q_rows, Hq_l * D * 2, src_stride_q,
+                                Hq_l * D * 2, spec(R.one), stream);
+  if (st != USP_OK) return st;
+  *out = Staged{qd, kd, vd, R.q_rows, 0, Hq_l, Hkv_l};
   return USP_OK;
 }
 
-// Workspace of the backward ring: the forward's staging regions (permuted /
-// relayouted q, k, v), delta, and -- when the caller's tensors are in
-// natural order but the ring runs rank-major (all ranks, non-basic layout)
-// -- rank-major copies of dout and LSE and rank-major f32 gradient
-// accumulators that are un-permuted into the outputs at the end.
+uint16_t* ws_ptr(char* ws, size_t off) { return off == NONE ? nullptr : reinterpret_cast<uint16_t*>(ws + off); }
+
+// Workspace of the backward ring: the forward's staging regions, delta, and
+// -- when the caller's tensors are in natural order but the ring runs
+// rank-major (all ranks, non-basic layout) -- rank-major copies of dout and
+// LSE and rank-major f32 gradient accumulators that are un-permuted into the
+// outputs at the end; with a sequence-shard forward output (out_layout 1),
+// head group u of out, dout and LSE gathered into the head-split layout.
 struct RingBwdLayout {
-  RingLayout base;        // only the staging offsets of the forward layout are used
+  RingLayout base;        // only the staging regions of the forward layout are used
   bool reorder;           // all ranks, natural-order tensors, non-basic layout
   size_t off_delta, off_delta_nat, off_dop, off_lsep, off_dq, off_dk, off_dv;
+  size_t off_og, off_dog, off_lg;  // head group u of out / dout / LSE (sequence-shard output)
+  PlanJob jq, jk;         // dQ and dK / dV plans, one per step
+  JobSlots sq, sk;
   size_t total;
 };
 
-RingBwdLayout ring_bwd_layout(const usp_ring_args* a) {
+usp_status ring_bwd_layout(const usp_ring_args* a, RingBwdLayout* out) {
   RingBwdLayout r;
-  const size_t NONE = SIZE_MAX;
-  r.base = ring_layout(a);
   RingLayout& R = r.base;
+  ring_shape(a, R);
+  R.off_oacc = R.off_lacc = R.off_opart = R.off_lpart = NONE;
+  R.out_is_acc = false;
   const size_t D = (size_t)a->D, B = (size_t)a->B, S = (size_t)a->S;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -909,22 +988,11 @@ RingBwdLayout ring_bwd_layout(const usp_ring_args* a) {
     off = align256(off + bytes);
     return o;
   };
-  // the staging regions, as the forward lays them out; no forward accumulators
-  R.off_qp = R.off_kp = R.off_vp = R.off_ql = R.off_kl = R.off_vl = NONE;
-  R.off_oacc = R.off_lacc = R.off_opart = R.off_lpart = NONE;
-  if (R.copy_in && a->ulysses_degree == 1) {
-    R.off_qp = take(B * (size_t)R.q_rows * a->Hq * D * 2);
-    R.off_kp = take(B * S * a->Hkv * D * 2);
-    R.off_vp = take(B * S * a->Hkv * D * 2);
-  }
-  if (a->ulysses_degree > 1) {
-    R.off_ql = take(B * (size_t)R.L * R.Hq_l * D * 2);
-    R.off_kl = take(B * S * R.Hkv_l * D * 2);
-    R.off_vl = take(B * S * R.Hkv_l * D * 2);
-  }
+  reserve_staging(a, R, off);
   r.reorder = R.need_perm && !R.one;
   r.off_delta = take(B * (size_t)R.Hq_l * R.q_rows * 4);
   r.off_delta_nat = r.off_dop = r.off_lsep = r.off_dq = r.off_dk = r.off_dv = NONE;
+  r.off_og = r.off_dog = r.off_lg = NONE;
   if (r.reorder) {
     r.off_delta_nat = take(B * (size_t)a->Hq * S * 4);
     r.off_dop = take(B * S * a->Hq * D * 2);
@@ -933,111 +1001,131 @@ RingBwdLayout ring_bwd_layout(const usp_ring_args* a) {
     r.off_dk = take(B * S * a->Hkv * D * 4);
     r.off_dv = take(B * S * a->Hkv * D * 4);
   }
+  if (R.seq_out) {
+    const size_t eb = a->out_dtype == USP_DT_F32 ? 4 : 2;
+    r.off_og = take(B * (size_t)R.L * R.Hq_l * D * eb);
+    r.off_dog = take(B * (size_t)R.L * R.Hq_l * D * 2);
+    r.off_lg = take(B * (size_t)R.Hq_l * R.L * 4);
+  }
+  r.jq = ring_job(a, 0, kBwdTileM, kTileN, 0);
+  r.jk = ring_job(a, 1, kBwdTileK, kBwdTileQ, 0);
+  usp_status st = finish_job(r.jq, a->cu_seqlens_host);
+  if (st == USP_OK) st = finish_job(r.jk, a->cu_seqlens_host);
+  if (st != USP_OK) return st;
+  r.sq = reserve_job(r.jq, off);
+  r.sk = reserve_job(r.jk, off);
   R.total = off;
   r.total = off;
-  return r;
+  *out = r;
+  return USP_OK;
 }
 
 }  // namespace
 
 size_t usp_ring_fwd_workspace_size(const usp_ring_args* a) {
   if (check_ring_args(a) != USP_OK) return 0;
-  return ring_layout(a).total;
+  RingLayout R;
+  if (ring_layout(a, &R) != USP_OK) return 0;
+  return R.total;
+}
+
+usp_status usp_ring_stage(const usp_ring_args* a, void* q_staged, void* k_staged, void* v_staged, void* stream_) {
+  usp_status st = check_ring_args(a);
+  if (st != USP_OK) return st;
+  USP_CHECK(q_staged && k_staged && v_staged, USP_ERR_INVALID_ARG, "null staging buffer");
+  RingLayout R;
+  ring_shape(a, R);
+  hipStream_t stream = as_stream(stream_);
+  uint16_t* qd = static_cast<uint16_t*>(q_staged);
+  uint16_t* kd = static_cast<uint16_t*>(k_staged);
+  uint16_t* vd = static_cast<uint16_t*>(v_staged);
+  Staged stg;
+  st = stage_ring_inputs(a, R, qd, kd, vd, stream, &stg);
+  if (st != USP_OK || R.copy_in) return st;
+  // the ring reads the caller's tensors in place: copy the rows it reads
+  const int64_t B = a->B, S = a->S, D = a->D;
+  st = launch_permute_strided(stg.q + stg.q_row_off * a->Hq * D, qd, B, stg.q_batch_rows, R.q_rows, a->Hq * D * 2,
+                              a->Hq * D * 2, a->Hq * D * 2, identity_rows(R.q_rows, G_PERMUTE), stream);
+  if (st == USP_OK)
+    st = launch_permute(stg.k, kd, B, S, S, a->Hkv * D * 2, identity_rows(S, G_PERMUTE), stream);
+  if (st == USP_OK)
+    st = launch_permute(stg.v, vd, B, S, S, a->Hkv * D * 2, identity_rows(S, G_PERMUTE), stream);
+  return st;
 }
 
 usp_status usp_ring_fwd(const usp_ring_args* a, void* workspace, size_t ws_bytes, void* stream_) {
   usp_status st = check_ring_args(a);
   if (st != USP_OK) return st;
-  const RingLayout R = ring_layout(a);
-  USP_CHECK(R.total == 0 || (workspace && ws_bytes >= R.total), USP_ERR_WORKSPACE,
-            "workspace of %zu bytes needed, %zu given", R.total, workspace ? ws_bytes : (size_t)0);
+  RingLayout R;
+  st = ring_layout(a, &R);
+  if (st != USP_OK) return st;
+  USP_CHECK(workspace && ws_bytes >= R.total, USP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", R.total,
+            workspace ? ws_bytes : (size_t)0);
   USP_CHECK(((uintptr_t)workspace & 255) == 0, USP_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const int N = a->ring_degree;
+  const int64_t B = a->B, D = a->D;
+  const int64_t Hq_l = R.Hq_l;
+  const float scale = a->softmax_scale > 0.f ? a->softmax_scale : 1.0f / std::sqrt((float)D);
+  ScoreMods mods;
+  st = ring_mods(a, Hq_l, scale, &mods);
+  if (st != USP_OK) return st;
+  // steps without a visible pair are skipped (step 0 always runs: it
+  // initialises every row)
+  std::vector<char> live(N, 1);
+  for (int s = 1; s < N; ++s) live[s] = step_has_work(R.job, s, a->cu_seqlens_host) ? 1 : 0;
+
+  // everything is validated: enqueue
   hipStream_t stream = as_stream(stream_);
   char* ws = static_cast<char*>(workspace);
-  const int N = a->ring_degree;
-  const int64_t B = a->B, S = a->S, D = a->D, L = R.L;
-  const int b = a->impl == USP_RING_STRIPE ? a->stripe_block : 1;
-
-  Staged stg;
-  st = stage_ring_inputs(a, R, ws, stream, &stg);
+  PlanJob J = R.job;
+  bind_job(J, R.slots, ws, a->cu_seqlens_dev);
+  PlanJobs jobs{};
+  jobs.j[0] = J;
+  jobs.n = 1;
+  st = launch_plan(jobs, stream);
   if (st != USP_OK) return st;
-  const uint16_t* qsrc = stg.q;
-  const uint16_t* ksrc = stg.k;
-  const uint16_t* vsrc = stg.v;
-  const int64_t q_batch_rows = stg.q_batch_rows, q_row_off = stg.q_row_off;
-  const int64_t Hq_l = stg.Hq_l, Hkv_l = stg.Hkv_l;
+  Staged stg;
+  st = stage_ring_inputs(a, R, ws_ptr(ws, R.off_q), ws_ptr(ws, R.off_k), ws_ptr(ws, R.off_v), stream, &stg);
+  if (st != USP_OK) return st;
 
   // 3. ring steps
   float* oacc = R.out_is_acc ? static_cast<float*>(a->out) : reinterpret_cast<float*>(ws + R.off_oacc);
   float* lacc = R.out_is_acc ? a->lse : reinterpret_cast<float*>(ws + R.off_lacc);
   float* opart = a->merge_mode ? reinterpret_cast<float*>(ws + R.off_opart) : nullptr;
   float* lpart = a->merge_mode ? reinterpret_cast<float*>(ws + R.off_lpart) : nullptr;
-  const float scale = a->softmax_scale > 0.f ? a->softmax_scale : 1.0f / std::sqrt((float)D);
-  ScoreMods mods;
-  st = ring_mods(a, Hq_l, scale, &mods);
-  if (st != USP_OK) return st;
-
-  MaskSpec ms;
-  ms.causal = a->causal ? 1 : 0;
-  ms.window = a->window;
-  ms.n_sink = a->n_sink;
-  ms.nseq = a->cu_seqlens_host ? a->nseq : 0;
-  ms.S = (int32_t)S;
-  usp_posmap pm{a->impl, N, 0, b, S};
-  const PosMap base_map = make_map(pm);
-
-  const int32_t tm = choose_tile_m(base_map);
+  const int64_t cpp = J.cpp();
+  const int32_t o_heads_acc = R.out_is_acc && R.seq_out ? (int32_t)a->Hq : (int32_t)Hq_l;
+  const int32_t o_head0_acc = R.out_is_acc && R.seq_out ? (int32_t)(a->ulysses_rank * Hq_l) : 0;
   for (int s = 0; s < N; ++s) {
+    if (!live[s]) continue;
     const int acc_flag = (s > 0 && a->merge_mode == 0) ? 1 : 0;
-    const std::string key = "ring|" + map_key(base_map) + "|" + mask_key(ms) + "|" +
-                            cu_key(ms.nseq ? a->cu_seqlens_host : nullptr, a->nseq) + "|r" +
-                            std::to_string(a->rank) + "|s" + std::to_string(s) + "|a" + std::to_string(acc_flag) +
-                            "|m" + std::to_string(tm);
-    DevicePlan dp;
-    st = device_plan(key, [&](Plan& plan) {
-      const int i0 = R.one ? a->rank : 0, i1 = R.one ? a->rank + 1 : N;
-      for (int i = i0; i < i1; ++i) {
-        const int j = ((i - s) % N + N) % N;
-        BlockSpec blk;
-        blk.qmap = base_map;
-        blk.qmap.rank = i;
-        blk.kmap = base_map;
-        blk.kmap.rank = j;
-        blk.Lq = (int32_t)L;
-        blk.Lk = (int32_t)L;
-        blk.q_row_base = R.one ? 0 : (int32_t)(i * L);
-        blk.k_row_base = (int32_t)(j * L);
-        blk.tile_m = tm;
-        plan_block(blk, ms, a->cu_seqlens_host, acc_flag, plan);
-      }
-    }, &dp);
-    if (st != USP_OK) return st;
-
     AttnParams p{};
-    p.q = qsrc + q_row_off * Hq_l * D;
-    p.k = ksrc;
-    p.v = vsrc;
+    p.q = stg.q + stg.q_row_off * Hq_l * D;
+    p.k = stg.k;
+    p.v = stg.v;
     const bool to_part = a->merge_mode == 1 && s > 0;
     p.out = to_part ? static_cast<void*>(opart) : static_cast<void*>(oacc);
     p.lse = to_part ? lpart : lacc;
-    p.items = dp.items;
-    p.runs = dp.runs;
-    p.cu_seqlens = ms.nseq ? a->cu_seqlens_dev : nullptr;
-    p.q_batch_stride = q_batch_rows * Hq_l * D;
-    p.o_batch_stride = R.q_rows * Hq_l * D;
-    p.kv_batch_stride = S * Hkv_l * D;
+    p.items = J.items + (int64_t)s * cpp;
+    p.runs = J.runs;
+    p.cu_seqlens = J.mask.nseq ? a->cu_seqlens_dev : nullptr;
+    p.q_batch_stride = stg.q_batch_rows * Hq_l * D;
+    p.o_heads = to_part ? (int32_t)Hq_l : o_heads_acc;
+    p.o_head0 = to_part ? 0 : o_head0_acc;
+    p.o_batch_stride = R.q_rows * p.o_heads * D;
+    p.kv_batch_stride = a->S * stg.Hkv_l * D;
     p.Lq_buf = (int32_t)R.q_rows;
-    p.n_items = dp.n_items;
+    p.n_items = (int32_t)cpp;
     p.B = (int32_t)B;
     p.Hq = (int32_t)Hq_l;
-    p.Hkv = (int32_t)Hkv_l;
+    p.Hkv = (int32_t)stg.Hkv_l;
     p.out_f32 = 1;
     p.accumulate = acc_flag;
-    p.tile_m = tm;
+    p.tile_m = J.tile;
     p.scale_log2 = scale * 1.4426950408889634f;
-    p.qmap = base_map;
-    p.kmap = base_map;
-    p.mask = ms;
+    p.qmap = J.qmap;
+    p.kmap = J.kmap;
+    p.mask = J.mask;
     p.mods = mods;
     st = launch_attn_fwd(p, (int)D, stream);
     if (st != USP_OK) return st;
@@ -1047,25 +1135,35 @@ usp_status usp_ring_fwd(const usp_ring_args* a, void* workspace, size_t ws_bytes
     }
   }
 
-  // 4. finalize: dtype and order of the outputs
+  // 4. finalize: dtype, order and head layout of the outputs
   if (!R.out_is_acc) {
-    GatherSpec gs{};
-    gs.impl = R.need_perm && !R.one ? a->impl : USP_RING_BASIC;
-    gs.N = R.need_perm && !R.one ? N : 1;
-    gs.ud = 1;
-    gs.b = R.need_perm && !R.one ? b : 1;
-    gs.g = 0;
-    gs.L = (int32_t)(R.need_perm && !R.one ? L : R.q_rows);
-    gs.S = (int32_t)R.q_rows;
-    gs.kind = G_UNPERMUTE;
+    const bool perm = R.need_perm && !R.one;
+    GatherSpec gs = identity_rows(R.q_rows, G_UNPERMUTE);
+    if (perm) {
+      gs.impl = a->impl;
+      gs.N = N;
+      gs.b = a->impl == USP_RING_STRIPE ? a->stripe_block : 1;
+      gs.L = (int32_t)R.L;
+    }
+    const int64_t row = Hq_l * D;                         // elements of one accumulator row
+    const int64_t orow = R.seq_out ? a->Hq * D : row;     // elements between output rows
+    const int64_t ohead = R.seq_out ? a->ulysses_rank * row : 0;
     if (a->out_dtype == USP_DT_F32) {
-      st = launch_permute(oacc, a->out, B, R.q_rows, R.q_rows, Hq_l * D * 4, gs, stream);
+      st = launch_permute_strided(oacc, static_cast<float*>(a->out) + ohead, B, R.q_rows, R.q_rows, row * 4, row * 4,
+                                  orow * 4, gs, stream);
     } else {
-      st = launch_permute_f32_to_bf16(oacc, static_cast<uint16_t*>(a->out), B, R.q_rows, R.q_rows,
-                                      Hq_l * D, gs, stream);
+      st = launch_permute_f32_to_bf16(oacc, static_cast<uint16_t*>(a->out) + ohead, B, R.q_rows, R.q_rows, row, orow,
+                                      gs, stream);
     }
     if (st != USP_OK) return st;
-    st = launch_permute(lacc, a->lse, B * Hq_l, R.q_rows, R.q_rows, 4, gs, stream);
+    if (R.seq_out) {
+      // one rank's rows in order: batch row b's [Hq/ud, L] block goes to heads of group u
+      const int64_t blk = Hq_l * R.q_rows;
+      st = launch_permute_strided(lacc, a->lse + a->ulysses_rank * blk, 1, B, B, blk * 4, blk * 4,
+                                  a->Hq * R.q_rows * 4, identity_rows(B, G_PERMUTE), stream);
+    } else {
+      st = launch_permute(lacc, a->lse, B * Hq_l, R.q_rows, R.q_rows, 4, gs, stream);
+    }
     if (st != USP_OK) return st;
   }
   return USP_OK;
@@ -1073,7 +1171,9 @@ usp_status usp_ring_fwd(const usp_ring_args* a, void* workspace, size_t ws_bytes
 
 size_t usp_ring_bwd_workspace_size(const usp_ring_bwd_args* a) {
   if (!a || check_ring_args(&a->fwd) != USP_OK) return 0;
-  return ring_bwd_layout(&a->fwd).total;
+  RingBwdLayout RB;
+  if (ring_bwd_layout(&a->fwd, &RB) != USP_OK) return 0;
+  return RB.total;
 }
 
 usp_status usp_ring_bwd(const usp_ring_bwd_args* ba, void* workspace, size_t ws_bytes, void* stream_) {
@@ -1082,49 +1182,90 @@ usp_status usp_ring_bwd(const usp_ring_bwd_args* ba, void* workspace, size_t ws_
   usp_status st = check_ring_args(a);
   if (st != USP_OK) return st;
   USP_CHECK(ba->dout && ba->dq && ba->dk && ba->dv, USP_ERR_INVALID_ARG, "null gradient pointer");
-  const RingBwdLayout RB = ring_bwd_layout(a);
-  USP_CHECK(RB.base.L * RB.base.Hq_l * a->D * 2 < ((int64_t)1 << 31) &&
-                RB.base.q_rows * RB.base.Hq_l * 4 < ((int64_t)1 << 31),
+  RingBwdLayout RB;
+  st = ring_bwd_layout(a, &RB);
+  if (st != USP_OK) return st;
+  const RingLayout& R = RB.base;
+  USP_CHECK(R.L * R.Hq_l * a->D * 2 < ((int64_t)1 << 31) && R.q_rows * R.Hq_l * 4 < ((int64_t)1 << 31),
             USP_ERR_UNSUPPORTED, "one ring rank's q rows and one batch row of LSE must be under 2 GiB "
             "(32-bit tile offsets)");
-  const RingLayout& R = RB.base;
   USP_CHECK(workspace && ws_bytes >= RB.total, USP_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
             RB.total, workspace ? ws_bytes : (size_t)0);
   USP_CHECK(((uintptr_t)workspace & 255) == 0, USP_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  hipStream_t stream = as_stream(stream_);
-  char* ws = static_cast<char*>(workspace);
   const int N = a->ring_degree;
   const int64_t B = a->B, S = a->S, D = a->D, L = R.L;
   const int b = a->impl == USP_RING_STRIPE ? a->stripe_block : 1;
+  const int64_t Hq_l = R.Hq_l;
+  const float scale = a->softmax_scale > 0.f ? a->softmax_scale : 1.0f / std::sqrt((float)D);
+  ScoreMods mods;
+  st = ring_mods(a, Hq_l, scale, &mods);
+  if (st != USP_OK) return st;
+  std::vector<char> live(N, 1);
+  for (int s = 0; s < N; ++s) live[s] = step_has_work(RB.jq, s, a->cu_seqlens_host) ? 1 : 0;
+
+  // everything is validated: enqueue
+  hipStream_t stream = as_stream(stream_);
+  char* ws = static_cast<char*>(workspace);
+  PlanJob jq = RB.jq, jk = RB.jk;
+  bind_job(jq, RB.sq, ws, a->cu_seqlens_dev);
+  bind_job(jk, RB.sk, ws, a->cu_seqlens_dev);
+  PlanJobs jobs{};
+  jobs.j[0] = jq;
+  jobs.j[1] = jk;
+  jobs.n = 2;
+  st = launch_plan(jobs, stream);
+  if (st != USP_OK) return st;
 
   // 1-2. the forward's staging of q, k, v
   Staged stg;
-  st = stage_ring_inputs(a, R, ws, stream, &stg);
+  st = stage_ring_inputs(a, R, ws_ptr(ws, R.off_q), ws_ptr(ws, R.off_k), ws_ptr(ws, R.off_v), stream, &stg);
   if (st != USP_OK) return st;
-  const int64_t Hq_l = stg.Hq_l, Hkv_l = stg.Hkv_l;
+
+  // the forward's out / LSE and dout in the head-split layout the kernels read
+  const usp_dtype odt = (usp_dtype)a->out_dtype;
+  const void* fout = a->out;
+  const float* lse = a->lse;
+  const uint16_t* dout = static_cast<const uint16_t*>(ba->dout);
+  if (R.seq_out) {
+    const int64_t eb = odt == USP_DT_F32 ? 4 : 2;
+    const int64_t u = a->ulysses_rank;
+    char* og = ws + RB.off_og;
+    char* dog = ws + RB.off_dog;
+    float* lg = reinterpret_cast<float*>(ws + RB.off_lg);
+    const GatherSpec id = identity_rows(L, G_PERMUTE);
+    st = launch_permute_strided(static_cast<const char*>(a->out) + u * Hq_l * D * eb, og, B, L, L, Hq_l * D * eb,
+                                a->Hq * D * eb, Hq_l * D * eb, id, stream);
+    if (st == USP_OK)
+      st = launch_permute_strided(static_cast<const char*>(ba->dout) + u * Hq_l * D * 2, dog, B, L, L, Hq_l * D * 2,
+                                  a->Hq * D * 2, Hq_l * D * 2, id, stream);
+    if (st == USP_OK)
+      st = launch_permute_strided(a->lse + u * Hq_l * L, lg, 1, B, B, Hq_l * L * 4, a->Hq * L * 4, Hq_l * L * 4,
+                                  identity_rows(B, G_PERMUTE), stream);
+    if (st != USP_OK) return st;
+    fout = og;
+    dout = reinterpret_cast<const uint16_t*>(dog);
+    lse = lg;
+  }
 
   // delta = rowsum(dO * O) over the rows the ring visits, in their order;
   // dout and LSE in that order too
   float* delta = reinterpret_cast<float*>(ws + RB.off_delta);
-  const uint16_t* dout = static_cast<const uint16_t*>(ba->dout);
-  const float* lse = a->lse;
-  const usp_dtype odt = (usp_dtype)a->out_dtype;
   if (RB.reorder) {
     float* dn = reinterpret_cast<float*>(ws + RB.off_delta_nat);
     uint16_t* dop = reinterpret_cast<uint16_t*>(ws + RB.off_dop);
     float* lsep = reinterpret_cast<float*>(ws + RB.off_lsep);
-    st = launch_bwd_delta(a->out, odt == USP_DT_F32, dout, dn, B, S, a->Hq, D, stream);
+    st = launch_bwd_delta(fout, odt == USP_DT_F32, dout, dn, B, S, a->Hq, D, stream);
     if (st == USP_OK)
       st = usp_permute(dn, delta, B * a->Hq, S, 1, USP_DT_F32, (usp_ring_impl)a->impl, N, 1, b, -1, 0, stream);
     if (st == USP_OK)
-      st = usp_permute(a->lse, lsep, B * a->Hq, S, 1, USP_DT_F32, (usp_ring_impl)a->impl, N, 1, b, -1, 0, stream);
+      st = usp_permute(lse, lsep, B * a->Hq, S, 1, USP_DT_F32, (usp_ring_impl)a->impl, N, 1, b, -1, 0, stream);
     if (st == USP_OK)
-      st = usp_permute(ba->dout, dop, B, S, a->Hq * D, USP_DT_BF16, (usp_ring_impl)a->impl, N, 1, b, -1, 0, stream);
+      st = usp_permute(dout, dop, B, S, a->Hq * D, USP_DT_BF16, (usp_ring_impl)a->impl, N, 1, b, -1, 0, stream);
     if (st != USP_OK) return st;
     dout = dop;
     lse = lsep;
   } else {
-    st = launch_bwd_delta(a->out, odt == USP_DT_F32, dout, delta, B, R.q_rows, Hq_l, D, stream);
+    st = launch_bwd_delta(fout, odt == USP_DT_F32, dout, delta, B, R.q_rows, Hq_l, D, stream);
     if (st != USP_OK) return st;
   }
 
@@ -1133,58 +1274,16 @@ usp_status usp_ring_bwd(const usp_ring_bwd_args* ba, void* workspace, size_t ws_
   float* dk = RB.reorder ? reinterpret_cast<float*>(ws + RB.off_dk) : ba->dk;
   float* dv = RB.reorder ? reinterpret_cast<float*>(ws + RB.off_dv) : ba->dv;
   st = launch_fill_zero(dq, B * R.q_rows * Hq_l * D, stream);
-  if (st == USP_OK) st = launch_fill_zero(dk, B * S * Hkv_l * D, stream);
-  if (st == USP_OK) st = launch_fill_zero(dv, B * S * Hkv_l * D, stream);
+  if (st == USP_OK) st = launch_fill_zero(dk, B * S * stg.Hkv_l * D, stream);
+  if (st == USP_OK) st = launch_fill_zero(dv, B * S * stg.Hkv_l * D, stream);
   if (st != USP_OK) return st;
 
   // 3. ring steps: host i meets KV piece j = (i - s) mod N; one launch per
   // kernel per step covers every host of the step (their dq rows and dk / dv
   // pieces are disjoint)
-  const float scale = a->softmax_scale > 0.f ? a->softmax_scale : 1.0f / std::sqrt((float)D);
-  ScoreMods mods;
-  st = ring_mods(a, Hq_l, scale, &mods);
-  if (st != USP_OK) return st;
-  MaskSpec ms;
-  ms.causal = a->causal ? 1 : 0;
-  ms.window = a->window;
-  ms.n_sink = a->n_sink;
-  ms.nseq = a->cu_seqlens_host ? a->nseq : 0;
-  ms.S = (int32_t)S;
-  usp_posmap pm{a->impl, N, 0, b, S};
-  const PosMap base_map = make_map(pm);
+  const int64_t cq = jq.cpp(), ck = jk.cpp();
   for (int s = 0; s < N; ++s) {
-    const std::string key = map_key(base_map) + "|" + mask_key(ms) + "|" +
-                            cu_key(ms.nseq ? a->cu_seqlens_host : nullptr, a->nseq) + "|r" +
-                            std::to_string(a->rank) + "|s" + std::to_string(s);
-    auto blocks = [&](auto&& add) {
-      const int i0 = R.one ? a->rank : 0, i1 = R.one ? a->rank + 1 : N;
-      for (int i = i0; i < i1; ++i) {
-        const int j = ((i - s) % N + N) % N;
-        BlockSpec blk;
-        blk.qmap = base_map;
-        blk.qmap.rank = i;
-        blk.kmap = base_map;
-        blk.kmap.rank = j;
-        blk.Lq = (int32_t)L;
-        blk.Lk = (int32_t)L;
-        blk.q_row_base = R.one ? 0 : (int32_t)(i * L);
-        blk.k_row_base = (int32_t)(j * L);
-        blk.tile_m = kBwdTileM;
-        add(blk);
-      }
-    };
-    DevicePlan dpq, dpk;
-    st = device_plan("rbq|" + key, [&](Plan& plan) {
-      blocks([&](const BlockSpec& blk) { plan_block(blk, ms, a->cu_seqlens_host, 1, plan); });
-    }, &dpq);
-    if (st != USP_OK) return st;
-    st = device_plan("rbk|" + key, [&](Plan& plan) {
-      blocks([&](const BlockSpec& blk) {
-        plan_block_kv(blk, ms, a->cu_seqlens_host, kBwdTileK, kBwdTileQ, plan);
-      });
-    }, &dpk);
-    if (st != USP_OK) return st;
-
+    if (!live[s]) continue;
     BwdParams p{};
     p.q = stg.q + stg.q_row_off * Hq_l * D;
     p.k = stg.k;
@@ -1195,27 +1294,27 @@ usp_status usp_ring_bwd(const usp_ring_bwd_args* ba, void* workspace, size_t ws_
     p.dq = dq;
     p.dk = dk;
     p.dv = dv;
-    p.cu_seqlens = ms.nseq ? a->cu_seqlens_dev : nullptr;
+    p.cu_seqlens = jq.mask.nseq ? a->cu_seqlens_dev : nullptr;
     p.q_batch_stride = stg.q_batch_rows * Hq_l * D;
     p.g_batch_stride = R.q_rows * Hq_l * D;
-    p.kv_batch_stride = S * Hkv_l * D;
+    p.kv_batch_stride = S * stg.Hkv_l * D;
     p.Lq_buf = (int32_t)R.q_rows;
     p.B = (int32_t)B;
     p.Hq = (int32_t)Hq_l;
-    p.Hkv = (int32_t)Hkv_l;
+    p.Hkv = (int32_t)stg.Hkv_l;
     p.scale = scale;
     p.scale_log2 = scale * 1.4426950408889634f;
-    p.qmap = base_map;
-    p.kmap = base_map;
-    p.mask = ms;
+    p.qmap = jq.qmap;
+    p.kmap = jq.kmap;
+    p.mask = jq.mask;
     p.mods = mods;
     BwdParams pq = p, pk = p;
-    pq.items = dpq.items;
-    pq.runs = dpq.runs;
-    pq.n_items = dpq.n_items;
-    pk.items = dpk.items;
-    pk.runs = dpk.runs;
-    pk.n_items = dpk.n_items;
+    pq.items = jq.items + (int64_t)s * cq;
+    pq.runs = jq.runs;
+    pq.n_items = (int32_t)cq;
+    pk.items = jk.items + (int64_t)s * ck;
+    pk.runs = jk.runs;
+    pk.n_items = (int32_t)ck;
     st = launch_bwd(pq, pk, (int)D, stream);
     if (st != USP_OK) return st;
   }

@@ -117,6 +117,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   const int hk = hb % p.Hkv;
   const int b = hb / p.Hkv;
   const WorkItem it = p.items[item_idx];
+  if (it.q_rows == 0) return;  // key tile no query sees (whole workgroup)
   const int group = p.Hq / p.Hkv;
 
   const int kr_ = wid * 32 + l32;

@@ -44,6 +44,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const BwdParams p) {
   const int h = hb % p.Hq;
   const int b = hb / p.Hq;
   const WorkItem it = p.items[item_idx];
+  if (it.q_rows == 0) return;  // planner slot with nothing to do (whole workgroup)
   const int hk = h / (p.Hq / p.Hkv);
 
   const int qr = wid * 32 + l32;

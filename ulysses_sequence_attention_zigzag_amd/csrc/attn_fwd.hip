@@ -141,6 +141,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
   const int h = hb % p.Hq;
   const int b = hb / p.Hq;
   const WorkItem it = p.items[item_idx];
+  if (it.q_rows == 0) return;  // planner slot with nothing to do (whole workgroup)
   const int hk = h / (p.Hq / p.Hkv);
 
   // This lane's query row: wid*32 + l32.
@@ -518,8 +519,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
   const float ltot = lsum + __shfl_xor(lsum, 32);
   if (!qvalid) return;
   const float lse_new = ltot > 0.f ? m * kLn2 + logf(ltot) : -INFINITY;
-  float* lse_ptr = p.lse + ((int64_t)b * p.Hq + h) * p.Lq_buf + qrow;
-  const int64_t obase = (int64_t)b * p.o_batch_stride + (qrow * p.Hq + h) * D;
+  // out rows and lse batch rows hold o_heads heads; this call's are o_head0 ..
+  float* lse_ptr = p.lse + ((int64_t)b * p.o_heads + p.o_head0 + h) * p.Lq_buf + qrow;
+  const int64_t obase = (int64_t)b * p.o_batch_stride + (qrow * p.o_heads + p.o_head0 + h) * D;
   float wa = 0.f, wb = ltot > 0.f ? 1.f / ltot : 0.f;
   float lse_out = lse_new;
   if (p.accumulate) {

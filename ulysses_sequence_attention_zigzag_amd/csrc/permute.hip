@@ -75,9 +75,12 @@ __global__ __launch_bounds__(256) void permute_rows_kernel(const char* __restric
 }
 
 // fp32 rows in, bf16 rows out (round to nearest even), same row mapping.
+// Consecutive output rows sit out_stride_elems bf16 apart (the row length
+// for a dense output; larger to write one head group of wider rows).
 __global__ __launch_bounds__(256) void permute_rows_f32_bf16_kernel(
     const float* __restrict__ in, uint16_t* __restrict__ out, int64_t n_task_rows, int32_t S_task,
-    int64_t S_in, int64_t S_out, int32_t quads_per_row, int32_t log_tpr, GatherSpec gs) {
+    int64_t S_in, int64_t S_out, int32_t quads_per_row, int64_t out_stride_elems, int32_t log_tpr,
+    GatherSpec gs) {
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const int32_t tpr = 1 << log_tpr;
@@ -91,7 +94,7 @@ __global__ __launch_bounds__(256) void permute_rows_f32_bf16_kernel(
   const int64_t src_row = o * S_in + (scatter ? i : m);
   const int64_t dst_row = o * S_out + (scatter ? m : i);
   const float4* src = reinterpret_cast<const float4*>(in + src_row * quads_per_row * 4);
-  uint2* dst = reinterpret_cast<uint2*>(out + dst_row * quads_per_row * 4);
+  uint2* dst = reinterpret_cast<uint2*>(out + dst_row * out_stride_elems);
   for (int32_t c = lane; c < quads_per_row; c += tpr) {
     const float4 x = src[c];
     const bf16x2 lo = __builtin_convertvector((f32x2){x.x, x.y}, bf16x2);
@@ -187,19 +190,19 @@ usp_status launch_permute_strided(const void* in, void* out, int64_t outer, int6
 }
 
 usp_status launch_permute_f32_to_bf16(const float* in, uint16_t* out, int64_t outer, int64_t S_in,
-                                      int64_t S_out, int64_t row_elems, const GatherSpec& gs,
-                                      hipStream_t stream) {
+                                      int64_t S_out, int64_t row_elems, int64_t out_row_stride,
+                                      const GatherSpec& gs, hipStream_t stream) {
   const bool extract_like = gs.kind == G_EXTRACT || gs.kind == G_INSERT;
   const int64_t S_task = extract_like ? (int64_t)gs.L / gs.ud : (gs.kind == G_PERMUTE ? S_out : S_in);
   const int64_t n_rows = outer * S_task;
   if (n_rows == 0 || row_elems == 0) return USP_OK;
-  const int64_t quads = row_elems / 4;  // callers guarantee row_elems % 4 == 0
+  const int64_t quads = row_elems / 4;  // callers guarantee row_elems % 4 == 0 and out_row_stride % 4 == 0
   const int ltpr = log_tpr_for(quads);
   const int64_t rows_per_block = 256 >> ltpr;
   const int64_t blocks = (n_rows + rows_per_block - 1) / rows_per_block;
   TimingScope ts(K_PERMUTE, stream);
   hipLaunchKernelGGL(permute_rows_f32_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, in,
-                     out, n_rows, (int32_t)S_task, S_in, S_out, (int32_t)quads, ltpr, gs);
+                     out, n_rows, (int32_t)S_task, S_in, S_out, (int32_t)quads, out_row_stride, ltpr, gs);
   return check_launch("permute_f32_bf16");
 }
 

@@ -77,7 +77,7 @@ __host__ __device__ inline int32_t first_row_at_least(const PosMap& m, int32_t t
 
 // Monotone pieces of a rank's local rows: positions increase with t inside
 // each piece.  Zigzag has two (its two chunks); the others one.
-inline int monotone_segments(const PosMap& m, int32_t seg_lo[2], int32_t seg_hi[2]) {
+__host__ __device__ inline int monotone_segments(const PosMap& m, int32_t seg_lo[2], int32_t seg_hi[2]) {
   if (m.kind == MAP_ZIGZAG) {
     seg_lo[0] = 0;
     seg_hi[0] = m.L / 2;
@@ -131,44 +131,10 @@ inline int32_t choose_tile_m(const PosMap& qmap) {
   return 256;
 }
 
-// Host-side plan for one launch (all ranks of one step, or one block call).
+// Host-built plan of one launch (the inspection calls return it).
 struct Plan {
   std::vector<WorkItem> items;
   std::vector<Run> runs;
-};
-
-// One (q rank, kv rank) block to plan.
-struct BlockSpec {
-  PosMap qmap;
-  PosMap kmap;
-  int32_t Lq;        // rows of the q rank
-  int32_t Lk;        // rows of the kv rank
-  int32_t q_row_base;
-  int32_t k_row_base;
-  int32_t tile_m;    // query rows per item
-};
-
-// Appends the items / runs of one block (not yet sorted).
-void plan_block(const BlockSpec& blk, const MaskSpec& ms, const int32_t* cu_host, int accumulate,
-                Plan& plan);
-// Transposed plan for the dK / dV kernel: one item per tile of `tile_k` keys
-// of the KV rank (inside one of its monotone pieces), with runs of local
-// query rows; item fields: q_row0 = first key row in the k/v buffers, t0 =
-// its local key index, q_rows = keys in the tile, q_rank = KV rank, k_row0 =
-// row of local query 0 of the query rank in the q buffers, k_rank = query
-// rank.  Full runs are multiples of `q_gran` rows.  Tiles no query sees get
-// no item.
-void plan_block_kv(const BlockSpec& blk, const MaskSpec& ms, const int32_t* cu_host, int32_t tile_k,
-                   int32_t q_gran, Plan& plan);
-// Orders items by decreasing work (stable).
-void finalize_plan(Plan& plan);
-
-// Device-resident plan, cached by key.
-struct DevicePlan {
-  WorkItem* items = nullptr;
-  Run* runs = nullptr;
-  int32_t n_items = 0;
-  int32_t n_runs = 0;
 };
 
 // Score modifiers of the attention call, in the kernels' raw-score units
@@ -205,6 +171,9 @@ struct AttnParams {
   int64_t o_batch_stride;   // elements between batch rows of out
   int64_t kv_batch_stride;  // elements between batch rows of k / v
   int32_t Lq_buf;           // rows per batch of q / out / lse
+  int32_t o_heads;          // heads per row of out and per batch row of lse (Hq, or
+                            // all heads when this call writes one head group)
+  int32_t o_head0;          // first head of this call's group in out / lse
   int32_t n_items;
   int32_t B;
   int32_t Hq;
@@ -302,10 +271,11 @@ usp_status launch_permute(const void* in, void* out, int64_t outer, int64_t S_in
 usp_status launch_permute_strided(const void* in, void* out, int64_t outer, int64_t S_in, int64_t S_out,
                                   int64_t row_bytes, int64_t in_row_stride, int64_t out_row_stride,
                                   const GatherSpec& gs, hipStream_t stream);
-// Same as launch_permute with fp32 -> bf16 conversion (row_elems fp32 in, bf16 out).
+// Same as launch_permute with fp32 -> bf16 conversion (row_elems fp32 in, bf16
+// out); output rows are out_row_stride bf16 apart (row_elems when dense).
 usp_status launch_permute_f32_to_bf16(const float* in, uint16_t* out, int64_t outer, int64_t S_in,
-                                      int64_t S_out, int64_t row_elems, const GatherSpec& gs,
-                                      hipStream_t stream);
+                                      int64_t S_out, int64_t row_elems, int64_t out_row_stride,
+                                      const GatherSpec& gs, hipStream_t stream);
 usp_status launch_relayout(void* const* shards, void* local, int64_t B, int64_t Ls, int64_t H,
                            int64_t D, int64_t elem_bytes, int ud, int u, int direction,
                            hipStream_t stream);
@@ -330,7 +300,8 @@ enum KernelClass : int {
   K_BWD_DKDV = 5,
   K_BWD_DELTA = 6,
   K_DECODE = 7,
-  K_DECODE_MERGE = 8
+  K_DECODE_MERGE = 8,
+  K_PLAN = 9
 };
 
 // Brackets one launch with hipEvents on `stream` while timing is enabled.

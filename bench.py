@@ -3,11 +3,17 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one usp_ring_fwd call over the whole hot path of the workload:
-token permutation of q/k/v (natural -> ring layout) with the Ulysses
-seq->head relayout (one strided gather per tensor when ulysses_degree > 1),
-every ring step's block attention with the LSE merge, and the
-output finalisation.  Inputs are seeded bf16 N(0,1), resident in HBM before
-the timed region.  Prints one JSON line.
+the device tile planner, token permutation of q/k/v (natural -> ring layout)
+with the Ulysses seq->head relayout (one strided gather per tensor when
+ulysses_degree > 1), every ring step's block attention with the LSE merge,
+and the output finalisation, including the Ulysses head->seq relayout of
+the output for a Ulysses rank.  Inputs are seeded bf16 N(0,1), resident in
+HBM before the timed region.  Prints one JSON line.
+
+With no --workload the line's headline is the striped MQA share (one rank
+of S = 2^20, the largest one-GPU workload), and "extra" carries the same
+share's last rank and the USP zigzag GQA share, each with its own
+roofline; --workload NAME times that workload alone.
 
 value  = mask-adjusted attention TFLOP/s of the whole step
          (4 * D * Hq_local * B * visible pairs / step time);
@@ -15,7 +21,8 @@ roofline = the block-attention kernel alone: the same FLOPs over the summed
          duration of its launches, measured with HIP events on the launch
          stream, against the dense bf16 MFMA peak;
 cpu_baseline = the float64 oracle on a bounded sample of the same
-         workload's output rows, on this host's cores, in the same unit.
+         workload's output rows, on this host's cores, in the same unit,
+         with the full-output time extrapolated from the sampled rate.
 """
 from __future__ import annotations
 
@@ -163,6 +170,40 @@ def time_lse_merge(w, merge_mode: int, merge_timing) -> dict:
     return rec
 
 
+def host_info() -> dict:
+    """The host the oracle runs on: the threads torch uses (the process's CPU
+    share, set through OMP_NUM_THREADS), the machine's logical CPU count, the
+    CPUs this process may run on, and the CPU model."""
+    import subprocess
+
+    import torch
+
+    info = {"threads": torch.get_num_threads(), "cpu_count": os.cpu_count()}
+    try:
+        info["affinity_cpus"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        pass
+    model = None
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except (OSError, subprocess.SubprocessError):
+        pass
+    if model is None:
+        try:
+            for line in open("/proc/cpuinfo"):
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            pass
+    info["model"] = model
+    return info
+
+
 def cpu_baseline(w, q, k, v, budget_s: float):
     """Times the float64 oracle on a seeded sample of the workload's output rows."""
     import torch
@@ -206,15 +247,26 @@ def cpu_baseline(w, q, k, v, budget_s: float):
         # grow the batch so the remaining budget is used in a few calls
         per_row = dt / max(1, len(rows))
         n = max(1, min(4096, int(0.3 * max(0.0, budget_s - t_used) / max(per_row, 1e-6))))
-    return {
-        "value": flops / t_used / 1e12,
+    rate = flops / t_used
+    bmul = 1 if w.cu_seqlens is not None else w.B
+    full_flops = 4.0 * w.D * len(heads) * bmul * visible_pairs_per_head(w)
+    rec = {
+        "value": rate / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
         "sample": f"{done} of {len(pos)} output rows x {len(heads)} heads"
                   f"{' x ' + str(w.B) + ' batch rows' if w.B > 1 and w.cu_seqlens is None else ''}, "
                   f"float64 torch CPU, {t_used:.1f} s",
+        "host": host_info(),
     }
+    if done < len(pos):
+        # the whole output at the sampled rate (FLOP-weighted, so causal rows count by their keys)
+        rec["extrapolated_full_s"] = round(full_flops / rate, 1)
+        rec["extrapolated_note"] = "extrapolated: full-output oracle time = the workload's FLOPs / the sampled rate"
+    else:
+        rec["full_s"] = round(t_used, 2)
+    return rec
 
 
 def cpu_baseline_bwd(w, q, k, v, dout, budget_s: float):
@@ -304,10 +356,15 @@ def visible_pairs_for_rows(w, rows) -> int:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="usp_zigzag_gqa")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None,
+                    help="one workload (default: the striped MQA share as the headline, with the USP zigzag "
+                         "GQA share and the striped share's last rank as extra records)")
+    ap.add_argument("--rank", type=int, default=None, help="one-rank workloads: the ring rank to time")
     ap.add_argument("--merge-mode", type=int, default=0)
+    ap.add_argument("--out-layout", choices=["seq", "heads"], default="seq",
+                    help="Ulysses ranks: seq (head -> seq relayout of the output, the default) or heads")
     ap.add_argument("--graph", action="store_true",
                     help="forward / decode: also time the step replayed from a HIP graph (graph_replay in the "
                          "JSON; value stays the eager rate)")
@@ -335,7 +392,6 @@ def main():
     import torch
 
     import seeded_inputs as si
-    import ulysses_sequence_attention_zigzag_amd as usp
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -352,27 +408,82 @@ def main():
         return
     if args.which == "decode":
         return bench_decode(args)
-    w = si.WORKLOADS[args.workload]
+    if args.workload is None and args.which == "backward":
+        args.workload = "usp_zigzag_gqa"
+    if args.workload is not None:
+        w = workload_of(si, args, args.workload)
+        q, k, v = gen_inputs(w)
+        qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+        if args.which == "backward":
+            return bench_backward(args, w, q, k, v, qd, kd, vd)
+        rec = forward_record(args, w, q, k, v, qd, kd, vd, with_cpu=not args.no_cpu_baseline,
+                             cpu_budget=args.cpu_budget)
+        print(json.dumps(rec), flush=True)
+        return
+
+    # default: the striped MQA share (the largest one-GPU workload) is the
+    # headline; its last rank (the most work) and the USP zigzag GQA share
+    # (with the Ulysses output relayout) are extra records
+    w4 = workload_of(si, args, "stripe_mqa")
+    q, k, v = gen_inputs(w4)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    rec = forward_record(args, w4, q, k, v, qd, kd, vd, with_cpu=not args.no_cpu_baseline,
+                         cpu_budget=args.cpu_budget)
+    w4r = w4.scaled(rank=w4.ring_degree - 1)
+    extra = {"stripe_mqa_rank%d" % w4r.rank: forward_record(args, w4r, q, k, v, qd, kd, vd, with_cpu=False)}
+    del q, k, v, qd, kd, vd
+    torch.cuda.empty_cache()
+    w3 = workload_of(si, args, "usp_zigzag_gqa")
+    q, k, v = gen_inputs(w3)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    extra["usp_zigzag_gqa"] = forward_record(args, w3, q, k, v, qd, kd, vd, with_cpu=not args.no_cpu_baseline,
+                                             cpu_budget=min(args.cpu_budget, 10.0))
+    for r in extra.values():
+        for key in ("n_gpus", "steps", "warmup", "higher_is_better", "scaling", "vs_baseline", "dtype", "data",
+                    "metric"):
+            r.pop(key, None)
+    rec["extra"] = extra
+    print(json.dumps(rec), flush=True)
+
+
+def workload_of(si, args, name):
+    w = si.WORKLOADS[name]
     if args.stripe_block:
         if w.impl != "stripe":
             print("--stripe-block applies to the striped workload only", file=sys.stderr)
             sys.exit(2)
         w = w.scaled(stripe_block=args.stripe_block)
+    if args.rank is not None:
+        if w.rank < 0:
+            print("--rank applies to the one-rank workloads only", file=sys.stderr)
+            sys.exit(2)
+        w = w.scaled(rank=args.rank)
+    return w
+
+
+def gen_inputs(w):
     t0 = time.perf_counter()
     q, k, v = w.make_inputs()
-    t_gen = time.perf_counter() - t0
-    print(f"# inputs generated in {t_gen:.1f}s", file=sys.stderr, flush=True)
-    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
-    if args.which == "backward":
-        return bench_backward(args, w, q, k, v, qd, kd, vd)
+    print(f"# {w.name}: inputs generated in {time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
+    return q, k, v
+
+
+def forward_record(args, w, q, k, v, qd, kd, vd, with_cpu: bool, cpu_budget: float = 15.0) -> dict:
+    """Times usp_ring_fwd over the workload: K steps after W warm-ups, the
+    attention kernel's own launches bracketed by HIP events on its stream."""
+    import torch
+
+    import ulysses_sequence_attention_zigzag_amd as usp
+
+    out_layout = args.out_layout if (w.rank >= 0 and w.ulysses_degree > 1) else "heads"
     call = usp.RingCall(qd, kd, vd, impl=w.impl, ring_degree=w.ring_degree, ulysses_degree=w.ulysses_degree,
                         stripe_block=w.stripe_block, causal=w.causal, window=w.window, n_sink=w.n_sink,
                         cu_seqlens=w.cu_seqlens, softmax_scale=w.softmax_scale or 0.0, rank=w.rank,
-                        ulysses_rank=w.ulysses_rank, merge_mode=args.merge_mode)
+                        ulysses_rank=w.ulysses_rank, merge_mode=args.merge_mode, out_layout=out_layout)
     for _ in range(args.warmup):
         call.run()
     torch.cuda.synchronize()
-    print("# warmup done", file=sys.stderr, flush=True)
+    print(f"# {w.name} rank {w.rank}: warmup done", file=sys.stderr, flush=True)
 
     usp.timing_reset()
     usp.timing_enable(True)
@@ -384,7 +495,7 @@ def main():
     elapsed = time.perf_counter() - t0
     usp.timing_enable(False)
     ms_step = elapsed * 1e3 / args.steps
-    kt = {c: usp.timing_read(c) for c in ("attn", "permute", "relayout", "merge")}
+    kt = {c: usp.timing_read(c) for c in ("attn", "permute", "relayout", "merge", "plan")}
     usp.timing_reset()
 
     Hl = w.Hq // w.ulysses_degree
@@ -409,11 +520,12 @@ def main():
             graph.replay()
         torch.cuda.synchronize()
         g_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-        graph_rec = {"ms_per_step": round(g_ms, 4), "TFLOP/s": None}
+        graph_rec = {"ms_per_step": round(g_ms, 4), "TFLOP/s": round(flops / (g_ms * 1e-3) / 1e12, 2)}
 
     def gbs(b, ms):
         return round(b / (ms * 1e-3) / 1e9, 1) if ms > 0 and b > 0 else None
 
+    copy_name = "permute+relayout" if w.ulysses_degree > 1 else "permute"
     rec = {
         "metric": "masked-attention TFLOPS (mask-adjusted, % of dense bf16 MFMA peak); permute/merge GB/s",
         "value": round(tflops, 2),
@@ -434,6 +546,7 @@ def main():
             "stripe_block": w.stripe_block,
             "rank": w.rank, "ulysses_rank": w.ulysses_rank, "causal": w.causal, "window": w.window,
             "n_sink": w.n_sink, "cu_seqlens": w.cu_seqlens, "merge_mode": args.merge_mode,
+            "out_layout": out_layout,
             "mask_adjusted_tflop_per_step": round(flops / 1e12, 4),
         },
         "pct_peak_end_to_end": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
@@ -443,8 +556,8 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4) if attn_tflops else None,
-            # the counter record was taken on the workloads as defined (stripe block 1)
-            "traffic": measured_traffic(w.name) if w.stripe_block == 1 else None,
+            # the counter record was taken on the workloads as defined (stripe block 1, rank 0)
+            "traffic": measured_traffic(w.name) if (w.stripe_block == 1 and w.rank <= 0) else None,
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "kernel": "attn_fwd_kernel<%d%s>" % (w.D, "" if w.stripe_block == 1 else ", stepped"),
             "launches_per_step": attn_n // max(1, args.steps),
@@ -452,20 +565,21 @@ def main():
         },
         "copy_kernels": {
             # the layout's row gather (with Ulysses: fused with the head split)
-            ("permute+relayout" if w.ulysses_degree > 1 else "permute"): {
+            copy_name: {
                 "bytes": perm_bytes, "ms": round(perm_ms, 4), "GB/s": gbs(perm_bytes, perm_ms),
                 "pct_hbm": round(100 * perm_bytes / (perm_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 1)
                 if perm_ms > 0 and perm_bytes > 0 else None},
             "merge": merge_rec,
         },
+        "planner_ms_per_step": round(kt["plan"][0] / args.steps, 4),
         "cpu_baseline": None,
     }
     if graph_rec is not None:
-        graph_rec["TFLOP/s"] = round(flops / (graph_rec["ms_per_step"] * 1e-3) / 1e12, 2)
         rec["graph_replay"] = graph_rec
-    if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
-    print(json.dumps(rec), flush=True)
+    if with_cpu:
+        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, cpu_budget)
+    del call
+    return rec
 
 
 def bench_backward(args, w, q, k, v, qd, kd, vd):

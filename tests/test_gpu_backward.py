@@ -432,20 +432,34 @@ def _local_rows(w: si.Workload, seed: int, n: int):
     return sorted(rows)
 
 
+# keys checked at full size: positions near the sequence end, so that the
+# oracle can take every query that sees them, yet each is seen by hundreds
+# (striped MQA: 8 heads over up to 2^20 keys per query) or about two
+# thousand (USP share) of the rank's queries; with GQA the check covers two
+# KV heads of the Ulysses rank (all query heads of those groups)
+FULL_BWD = {
+    "usp_zigzag_gqa": dict(keys=lambda S: [S - 1972, S - 1500, S - 1001, S - 640, S - 129, S - 2], kv_groups=[0, 3]),
+    "stripe_mqa": dict(keys=lambda S: [S - 2048, S - 1601, S - 1024, S - 777, S - 256, S - 9], kv_groups=[0]),
+}
+
+
 @pytest.mark.parametrize("name", ["usp_zigzag_gqa", "stripe_mqa"])
 def test_large_workloads_full_size_backward_sampled(name):
     """usp_ring_bwd at the workload's full size, after usp_ring_fwd on the
-    device (the benchmark's launch configuration): dq on sampled query rows of
-    the rank, and dk / dv on the keys nearest the sequence end, whose few
-    visible queries the oracle can take one by one (keys no query of the rank
-    sees must come back exactly zero)."""
+    device in the configuration bench.py times (the USP share with the Ulysses
+    head -> seq output layout): dq on sampled query rows of the rank, and dk /
+    dv of keys that hundreds to thousands of the rank's queries see, each
+    accumulated over all of them (keys no query of the rank sees come back
+    exactly zero)."""
     w = si.WORKLOADS[name]
+    cfg = FULL_BWD[name]
     say(f"full-size backward {name}: generating inputs")
     q, k, v = w.make_inputs()
+    seq = w.ulysses_degree > 1
     fwd = usp.RingCall(q.cuda(), k.cuda(), v.cuda(), impl=w.impl, ring_degree=w.ring_degree,
                        ulysses_degree=w.ulysses_degree, stripe_block=w.stripe_block, causal=w.causal,
                        window=w.window, n_sink=w.n_sink, softmax_scale=w.softmax_scale or 0.0, rank=w.rank,
-                       ulysses_rank=w.ulysses_rank)
+                       ulysses_rank=w.ulysses_rank, out_layout="seq" if seq else "heads")
     fwd.run()
     dout = si.randn_bf16(tuple(fwd.out.shape), w.seed, 3)
     dq, dk, dv = usp.RingBwdCall(fwd, dout.cuda()).run()
@@ -453,52 +467,53 @@ def test_large_workloads_full_size_backward_sampled(name):
     dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
     N, ud, u = w.ring_degree, w.ulysses_degree, w.ulysses_rank
     Hl, Hkl = w.Hq // ud, w.Hkv // ud
+    group = w.Hq // w.Hkv
     heads, kvh = list(range(u * Hl, (u + 1) * Hl)), list(range(u * Hkl, (u + 1) * Hkl))
+    if seq:
+        dout = dout[:, :, heads[0]:heads[-1] + 1]          # this Ulysses rank's head group
     pos = ix.rank_positions(w.impl, w.S, N, w.rank, w.stripe_block)
-    kw = dict(softmax_scale=w.scale, causal=w.causal, window=w.window, n_sink=w.n_sink)
+    kw = dict(scale=w.scale, causal=w.causal, window=w.window, n_sink=w.n_sink)
     ks, vs = k[:, :, kvh].contiguous(), v[:, :, kvh].contiguous()
 
-    # the oracle's forward (O, LSE) and delta of every query row used below,
-    # in one pass over the keys
-    rows = _local_rows(w, seed=17, n=3)
-    keys = sorted({w.S - 1, w.S - 2, w.S - 3, w.S - 9, w.S - 16})
-    seers = [t for t in range(len(pos)) if pos[t] >= min(keys)]
-    need = sorted(set(rows) | set(seers))
-    say(f"full-size backward {name}: oracle forward on {len(need)} rows")
-    O_all, LSE_all = attention_ref(q, k, v, rows=[pos[r] for r in need], heads=heads, **kw)
-    at = {r: i for i, r in enumerate(need)}
-
-    def oracle_rows(local_rows):
-        idx = torch.tensor([at[r] for r in local_rows], dtype=torch.long)
-        O, LSE = O_all[:, idx], LSE_all[:, :, idx]
-        do = dout[:, local_rows]
+    def oracle_fwd(local_rows, hs):
+        """float64 (O, LSE) and delta of the rank's local rows for query heads hs (positions in
+        increasing order, every key)."""
+        order = sorted(local_rows, key=lambda r: pos[r])
+        O, LSE = attention_ref(q, k, v, softmax_scale=w.scale, causal=w.causal, window=w.window,
+                               n_sink=w.n_sink, rows=[pos[r] for r in order], heads=hs, block_bytes=1 << 32)
+        hl = [h - heads[0] for h in hs]
+        do = dout[:, order][:, :, hl]
         delta = (do.double() * O).sum(-1).transpose(1, 2)
-        return [pos[r] for r in local_rows], LSE, do, delta
+        return order, [pos[r] for r in order], LSE, do, delta
 
-    # dq of sampled query rows: every key
+    # dq of sampled query rows: every key, every head of the Ulysses rank
+    rows = _local_rows(w, seed=17, n=3)
     say(f"full-size backward {name}: oracle dq on {len(rows)} rows")
-    p_rows, LSE, do, delta = oracle_rows(rows)
+    order, p_rows, LSE, do, delta = oracle_fwd(rows, heads)
     qi = q[:, p_rows][:, :, heads].contiguous()
-    dq_ref, _, _ = block_attention_bwd_ref(qi, ks, vs, do, LSE, delta, p_rows, list(range(w.S)), scale=w.scale,
-                                           causal=w.causal, window=w.window, n_sink=w.n_sink)
-    assert_grad(dq[:, rows], dq_ref, "dq sampled")
+    dq_ref, _, _ = block_attention_bwd_ref(qi, ks, vs, do, LSE, delta, p_rows, list(range(w.S)), **kw)
+    assert_grad(dq[:, order], dq_ref, "dq sampled")
 
-    # dk / dv of the last keys: only the rank's queries at or after them see them
+    # dk / dv of the chosen keys, per checked KV head (its group of query heads)
+    keys = sorted(cfg["keys"](w.S))
     allpos = [ix.rank_positions(w.impl, w.S, N, r, w.stripe_block) for r in range(N)]
     out_row = {p: i for i, p in enumerate(p for r in range(N) for p in allpos[r])}   # rank-major rows
-    say(f"full-size backward {name}: oracle dk/dv on {len(keys)} keys from {len(seers)} query rows")
     krow = torch.tensor([out_row[p] for p in keys])
-    got_k, got_v = dk[:, krow], dv[:, krow]
-    if not seers:
-        assert float(got_k.abs().max()) == 0.0 and float(got_v.abs().max()) == 0.0
-        return
-    p_s, LSE_s, do_s, delta_s = oracle_rows(seers)
-    qs = q[:, p_s][:, :, heads].contiguous()
-    _, dk_ref, dv_ref = block_attention_bwd_ref(qs, ks[:, keys], vs[:, keys], do_s, LSE_s, delta_s, p_s, keys,
-                                                scale=w.scale, causal=w.causal, window=w.window, n_sink=w.n_sink)
-    unseen = torch.tensor([all(pp < p for pp in p_s) for p in keys])
-    if unseen.any():
-        assert float(got_k[:, unseen].abs().max()) == 0.0 and float(got_v[:, unseen].abs().max()) == 0.0
-    seen = ~unseen
-    assert_grad(got_k[:, seen], dk_ref[:, seen], "dk last keys")
-    assert_grad(got_v[:, seen], dv_ref[:, seen], "dv last keys")
+    seers = [t for t in range(len(pos)) if pos[t] >= keys[0]]
+    say(f"full-size backward {name}: oracle dk/dv on {len(keys)} keys seen by up to {len(seers)} query rows")
+    for g in cfg["kv_groups"]:
+        hs = [heads[g * group + i] for i in range(group)]
+        order, p_s, LSE_s, do_s, delta_s = oracle_fwd(seers, hs)
+        qs = q[:, p_s][:, :, hs].contiguous()
+        kg, vg = ks[:, keys][:, :, g:g + 1].contiguous(), vs[:, keys][:, :, g:g + 1].contiguous()
+        _, dk_ref, dv_ref = block_attention_bwd_ref(qs, kg, vg, do_s, LSE_s, delta_s, p_s, keys, **kw)
+        n_seen = [sum(1 for pp in p_s if pp >= p) for p in keys]
+        say(f"  kv head {g}: queries per key {n_seen}")
+        assert_grad(dk[:, krow][:, :, g:g + 1], dk_ref, f"dk kv head {g}")
+        assert_grad(dv[:, krow][:, :, g:g + 1], dv_ref, f"dv kv head {g}")
+    # keys after the rank's last query: no query of the rank sees them
+    last = max(pos)
+    unseen = [p for p in range(last + 1, w.S)]
+    if unseen:
+        urow = torch.tensor([out_row[p] for p in unseen])
+        assert float(dk[:, urow].abs().max()) == 0.0 and float(dv[:, urow].abs().max()) == 0.0

@@ -451,15 +451,6 @@ def test_workload_full_size_full_oracle(name):
     assert_parity(out, lse, O_ref, L_ref, name)
 
 
-def _sample_rows(w: si.Workload, n: int, seed: int):
-    """Local rows of the rank: chunk / stripe boundaries, the first rows and a seeded spread."""
-    L = w.S // w.ring_degree
-    rows = set(range(0, 8)) | {L - 1, L // 2 - 1, L // 2, L // 2 + 1}
-    g = torch.Generator().manual_seed(seed)
-    rows |= set(torch.randint(0, L, (n,), generator=g).tolist())
-    return sorted(r for r in rows if 0 <= r < L)
-
-
 @pytest.mark.parametrize("name,scaled", [("usp_zigzag_gqa", dict(S=16384)), ("stripe_mqa", dict(S=32768))])
 def test_large_workloads_scaled_full_oracle(name, scaled):
     w = si.WORKLOADS[name].scaled(**scaled)
@@ -470,17 +461,64 @@ def test_large_workloads_scaled_full_oracle(name, scaled):
     assert_parity(out, lse, O_ref, L_ref, f"{name} scaled")
 
 
-@pytest.mark.parametrize("name,n_rows", [("usp_zigzag_gqa", 48), ("stripe_mqa", 24)])
+def full_size_rows(w: si.Workload, total: int, seed: int):
+    """Local rows of the rank for the full-size checks: the first eight rows,
+    the rows around the zigzag chunk boundary and the last rows, two whole
+    256-row work items of the attention kernel (zigzag: one in each chunk,
+    i.e. a tile that meets only the diagonal step and one that meets every
+    step; striped: the first tile and one in the middle), and seeded random
+    rows up to `total`."""
+    L = w.S // w.ring_degree
+    rows = set(range(8)) | {L - 2, L - 1}
+    if w.impl == "zigzag":
+        c = L // 2
+        rows |= {c - 2, c - 1, c, c + 1}
+        items = [(c // 2) // 256 * 256, c + (c // 4) // 256 * 256]
+    else:
+        items = [0, (L // 2) // 256 * 256]
+    for t0 in items:
+        rows |= set(range(t0, t0 + 256))
+    g = torch.Generator().manual_seed(seed)
+    while len(rows) < total:
+        rows |= set(torch.randint(0, L, (total - len(rows),), generator=g).tolist())
+    return sorted(rows), items
+
+
+def oracle_rows_sorted(w: si.Workload, q, k, v, heads, rows):
+    """Oracle (O, LSE) of the rank's local rows, computed over the rows' global
+    positions in increasing order (so each block of rows spans few keys), and
+    returned in the order of `rows`."""
+    pos = ix.rank_positions(w.impl, w.S, w.ring_degree, w.rank, w.stripe_block)
+    order = sorted(range(len(rows)), key=lambda i: pos[rows[i]])
+    sel = [pos[rows[i]] for i in order]
+    O, LSE = attention_ref(q, k, v, softmax_scale=w.scale, causal=w.causal, window=w.window, n_sink=w.n_sink,
+                           cu_seqlens=w.cu_seqlens, rows=sel, heads=heads, block_bytes=1 << 32)
+    back = torch.empty(len(rows), dtype=torch.long)
+    back[torch.tensor(order)] = torch.arange(len(rows))
+    return O[:, back], LSE[:, :, back]
+
+
+@pytest.mark.parametrize("name,n_rows", [("usp_zigzag_gqa", 2048), ("stripe_mqa", 1024)])
 def test_large_workloads_full_size_sampled_rows(name, n_rows):
+    """The two large one-rank workloads at full size, in the configuration
+    bench.py times (the USP share with the Ulysses head -> seq output layout):
+    every head of n_rows local rows against the float64 oracle."""
     w = si.WORKLOADS[name]
     say(f"full-size {name}: generating inputs")
     q, k, v = w.make_inputs()
-    out, lse = _run_ring(w, q, k, v)
-    rows = _sample_rows(w, n_rows, seed=99)
-    say(f"full-size {name}: oracle on {len(rows)} rows")
-    O_ref, L_ref = _oracle_share(w, q, k, v, rows=rows)
+    seq = w.ulysses_degree > 1
+    out, lse = _run_ring(w, q, k, v, out_layout="seq" if seq else "heads")
+    Hl = w.Hq // w.ulysses_degree
+    heads = list(range(w.ulysses_rank * Hl, (w.ulysses_rank + 1) * Hl))
+    if seq:
+        out = out[:, :, heads[0]:heads[-1] + 1]
+        lse = lse[:, heads[0]:heads[-1] + 1]
+    out, lse = out.cpu(), lse.cpu()
+    rows, items = full_size_rows(w, n_rows, seed=99)
+    say(f"full-size {name}: oracle on {len(rows)} rows (whole items at {items})")
+    O_ref, L_ref = oracle_rows_sorted(w, q, k, v, heads, rows)
     idx = torch.tensor(rows)
-    assert_parity(out.cpu()[:, idx], lse.cpu()[:, :, idx], O_ref, L_ref, f"{name} sampled")
+    assert_parity(out[:, idx], lse[:, :, idx], O_ref, L_ref, f"{name} {len(rows)} rows")
 
 
 # ---------------------------------------------------------------- packed qkv input

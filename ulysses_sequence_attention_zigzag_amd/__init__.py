@@ -571,7 +571,7 @@ def ring_fwd(q, k, v, **kw) -> Tuple[torch.Tensor, torch.Tensor]:
 
 # ---------------------------------------------------------------- timing
 KERNEL_CLASSES = {"attn": 0, "permute": 1, "relayout": 2, "merge": 3, "bwd_dq": 4, "bwd_dkdv": 5,
-                  "bwd_delta": 6, "decode": 7, "decode_merge": 8}
+                  "bwd_delta": 6, "decode": 7, "decode_merge": 8, "plan": 9}
 
 
 def timing_enable(on: bool = True) -> None:

@@ -369,6 +369,19 @@ size_t usp_ring_fwd_workspace_size(const usp_ring_args* a);
  * call), the staged q / k / v and the accumulators. */
 usp_status usp_ring_fwd(const usp_ring_args* a, void* workspace, size_t ws_bytes, void* stream);
 
+/* usp_ring_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same call with its workspace in a 64 MiB array the library holds on
+ * each GPU it runs on, from the first call on that GPU until the process
+ * ends.  No allocation of any kind happens in the call.  Arguments whose
+ * usp_ring_fwd_workspace_size exceeds 64 MiB are rejected with
+ * USP_ERR_WORKSPACE before anything is enqueued.  Every call on one GPU uses
+ * that GPU's one array: calls that overlap on a GPU (other streams or
+ * threads, or a recorded graph replayed while another call runs) race on it
+ * and must be ordered by the caller.  Nothing in it needs to start at zero:
+ * each call rewrites what it reads. */
+usp_status usp_ring_fwd_noalloc(const usp_ring_args* a, void* stream);
+
 /* The ring's input staging on its own: writes q, k, v exactly as the
  * attention kernels of usp_ring_fwd / usp_ring_bwd read them for arguments
  * `a`, i.e. the layout's token order [YC "2. Usage": the extract function;

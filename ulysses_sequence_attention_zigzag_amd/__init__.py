@@ -78,6 +78,7 @@ _SIGS = {
     "usp_ring_fwd_workspace_size": ([ctypes.POINTER(RingArgs)], ctypes.c_size_t),
     "usp_ring_fwd": ([ctypes.POINTER(RingArgs), _P, ctypes.c_size_t, _P], _I32),
     "usp_ring_stage": ([ctypes.POINTER(RingArgs), _P, _P, _P, _P], _I32),
+    "usp_ring_fwd_noalloc": ([ctypes.POINTER(RingArgs), _P], _I32),
     "usp_ring_bwd_workspace_size": ([ctypes.POINTER(RingBwdArgs)], ctypes.c_size_t),
     "usp_ring_bwd": ([ctypes.POINTER(RingBwdArgs), _P, ctypes.c_size_t, _P], _I32),
     "usp_plan_block": ([_I64, _I64, _I64, _I32, ctypes.POINTER(PosMap), ctypes.POINTER(PosMap), _I32, _I32,

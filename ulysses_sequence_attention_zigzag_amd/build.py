@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libusp.so")
 SOURCES = ["api.cpp", "plan.cpp", "plan_dev.hip", "timing.cpp", "permute.hip", "lse_merge.hip", "attn_fwd.hip", "attn_bwd.hip",
-           "attn_bwd_dq.hip", "decode.hip"]
+           "attn_bwd_dq.hip", "decode.hip", "noalloc.hip"]
 # per-source flags: the dQ kernel is built with VGPR-form MFMAs
 SOURCE_FLAGS = {"attn_bwd_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"

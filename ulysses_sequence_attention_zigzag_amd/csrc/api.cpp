@@ -1069,11 +1069,6 @@ usp_status usp_ring_fwd(const usp_ring_args* a, void* workspace, size_t ws_bytes
   ScoreMods mods;
   st = ring_mods(a, Hq_l, scale, &mods);
   if (st != USP_OK) return st;
-  // steps without a visible pair are skipped (step 0 always runs: it
-  // initialises every row)
-  std::vector<char> live(N, 1);
-  for (int s = 1; s < N; ++s) live[s] = step_has_work(R.job, s, a->cu_seqlens_host) ? 1 : 0;
-
   // everything is validated: enqueue
   hipStream_t stream = as_stream(stream_);
   char* ws = static_cast<char*>(workspace);
@@ -1097,7 +1092,9 @@ usp_status usp_ring_fwd(const usp_ring_args* a, void* workspace, size_t ws_bytes
   const int32_t o_heads_acc = R.out_is_acc && R.seq_out ? (int32_t)a->Hq : (int32_t)Hq_l;
   const int32_t o_head0_acc = R.out_is_acc && R.seq_out ? (int32_t)(a->ulysses_rank * Hq_l) : 0;
   for (int s = 0; s < N; ++s) {
-    if (!live[s]) continue;
+    // steps without a visible pair are skipped (step 0 always runs: it
+    // initialises every row); a host-only test on the step's position ranges
+    if (s > 0 && !step_has_work(R.job, s, a->cu_seqlens_host)) continue;
     const int acc_flag = (s > 0 && a->merge_mode == 0) ? 1 : 0;
     AttnParams p{};
     p.q = stg.q + stg.q_row_off * Hq_l * D;
@@ -1200,9 +1197,6 @@ usp_status usp_ring_bwd(const usp_ring_bwd_args* ba, void* workspace, size_t ws_
   ScoreMods mods;
   st = ring_mods(a, Hq_l, scale, &mods);
   if (st != USP_OK) return st;
-  std::vector<char> live(N, 1);
-  for (int s = 0; s < N; ++s) live[s] = step_has_work(RB.jq, s, a->cu_seqlens_host) ? 1 : 0;
-
   // everything is validated: enqueue
   hipStream_t stream = as_stream(stream_);
   char* ws = static_cast<char*>(workspace);
@@ -1283,7 +1277,7 @@ usp_status usp_ring_bwd(const usp_ring_bwd_args* ba, void* workspace, size_t ws_
   // pieces are disjoint)
   const int64_t cq = jq.cpp(), ck = jk.cpp();
   for (int s = 0; s < N; ++s) {
-    if (!live[s]) continue;
+    if (!step_has_work(RB.jq, s, a->cu_seqlens_host)) continue;
     BwdParams p{};
     p.q = stg.q + stg.q_row_off * Hq_l * D;
     p.k = stg.k;

@@ -57,6 +57,13 @@ def build(extra=(), verbose: bool = False, csrc: str = CSRC, out: str = LIB) -> 
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    # every symbol of the library's own namespace must be defined in it (a
+    # kernel whose host stub the compiler failed to emit shows up here
+    # instead of at load time)
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in nm.stdout.splitlines() if "_ZN3usp" in l]
+    if nm.returncode != 0 or missing:
+        raise RuntimeError(f"link of {out} left undefined library symbols: {missing[:5]} {nm.stderr}")
     shutil.move(tmp, out)
     if verbose:
         print(f"built {out}")

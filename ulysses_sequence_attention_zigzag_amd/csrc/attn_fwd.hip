@@ -173,7 +173,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
   // running sum.  m is raised lazily: only when a tile's max exceeds it by
   // more than kRescale, so the exponentials stay <= 2^kRescale.
   constexpr float kRescale = 8.f;
-  float m = -INFINITY, lsum = 0.f;
+  // The row sum is accumulated from the bf16-rounded probabilities with
+  // v_dot2 (one instruction per pair instead of two adds; numerator and
+  // denominator then use the same rounded P), in two partial sums that
+  // halve the dependency chain.  1.2-1.5 % faster on both large shares.
+  float m = -INFINITY, lsum = 0.f, lsum2 = 0.f;
+  const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
 
   // Visible key positions of this query: [vis_lo, vis_hi], plus the sinks
   // [sstart, sink_hi] when a window is set (same sequence, causal band,
@@ -457,6 +462,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
       const float alpha = (m_new == m || m_new == -INFINITY) ? 1.f : fast_exp2(m - m_new);
       m = m_new;
       lsum *= alpha;
+      lsum2 *= alpha;
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb) {
@@ -466,8 +472,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
           for (int e = 0; e < 8; e += 2) {
             const float p0 = fast_exp2(s[kb][half * 8 + e] * p.scale_log2 - m_use);
             const float p1 = fast_exp2(s[kb][half * 8 + e + 1] * p.scale_log2 - m_use);
-            lsum += p0 + p1;
             const bf16x2 pk2 = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
+            if (half == 0)
+              lsum = __builtin_amdgcn_fdot2_f32_bf16(pk2, ones2, lsum, false);
+            else
+              lsum2 = __builtin_amdgcn_fdot2_f32_bf16(pk2, ones2, lsum2, false);
             pb[kb][half][e] = pk2[0];
             pb[kb][half][e + 1] = pk2[1];
           }
@@ -494,28 +503,40 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
     // consumed by its MFMAs before it ends, and tile loads are waited for
     // explicitly), only a compiler ordering point.
     auto phase_barrier = [&]() { asm volatile("s_barrier" ::: "memory"); };
+    // A wave runs its matrix phase at raised priority, so the SIMD's other
+    // wave (in its softmax) does not delay its MFMA and LDS issue: 0.6-1.5 %
+    // faster on both large shares.
+    auto prio_hi = []() { __builtin_amdgcn_s_setprio(1); };
+    auto prio_lo = []() { __builtin_amdgcn_s_setprio(0); };
     // Group 1 starts one phase late (group 0 runs M(0) meanwhile) and group
     // 0 ends one phase early, so both pass the same number of barriers.
     if (grp == 1) phase_barrier();
     if (n_tiles > 1) prefetch_next();
+    prio_hi();
     m_phase(F_{}, T_{}, nullptr, smem, s, pb);
+    prio_lo();
     if (n_tiles > 1) dma_tile(stage_tiles + TILEB, nk0, nrun.k_end);
     phase_barrier();
     v_phase(0);
     phase_barrier();
     for (int t = 1; t < n_tiles; ++t) {
       if (t + 1 < n_tiles) prefetch_next();
+      prio_hi();
       m_phase(T_{}, T_{}, smem + (2 + ((t - 1) & 1)) * TILEB, smem + (t & 1) * TILEB, s, pb);
+      prio_lo();
       if (t + 1 < n_tiles) dma_tile(stage_tiles + ((t + 1) & 1) * TILEB, nk0, nrun.k_end);
       phase_barrier();
       v_phase(t);
       phase_barrier();
     }
+    prio_hi();
     m_phase(T_{}, F_{}, smem + (2 + ((n_tiles - 1) & 1)) * TILEB, nullptr, s, pb);
+    prio_lo();
     if (grp == 0) phase_barrier();
   }
 
   // epilogue: O = O_acc / l, LSE = m ln 2 + ln l; or merge into (out, lse)
+  lsum += lsum2;
   const float ltot = lsum + __shfl_xor(lsum, 32);
   if (!qvalid) return;
   const float lse_new = ltot > 0.f ? m * kLn2 + logf(ltot) : -INFINITY;

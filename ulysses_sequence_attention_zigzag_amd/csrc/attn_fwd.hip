@@ -336,6 +336,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
   // layout and at t + (p(k0) - k0) inside a run of the others (inv_b = 0
   // there), so p_k - p_q = floor((t + 0.5) inv_b) nb1 + t + rb.
   const float slope_raw = (MODS & 2) ? p.mods.alibi[h] * p.mods.inv_scale : 0.f;
+  // softcap constants held in VGPRs (the window kernels use every SGPR)
+  float cap_a = p.mods.a, cap_2a = 2.f * p.mods.a, cap_b2 = p.mods.b2;
+  if constexpr ((MODS & 1) != 0) asm("" : "+v"(cap_a), "+v"(cap_2a), "+v"(cap_b2));
   // rb of a tile: rb0, or rb1 for a tile in the second zigzag chunk.
   const bool kstripe = km.kind == MAP_STRIPE;
   const float inv_b = kstripe ? 1.f / (float)km.b : 0.f;
@@ -349,8 +352,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
       for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(sc[kb][r] * p.mods.b2);
-          sc[kb][r] = p.mods.a - 2.f * p.mods.a * __builtin_amdgcn_rcpf(e + 1.f);
+          const float e = __builtin_amdgcn_exp2f(sc[kb][r] * cap_b2);
+          sc[kb][r] = cap_a - cap_2a * __builtin_amdgcn_rcpf(e + 1.f);
         }
     }
     if constexpr ((MODS & 2) != 0) {
@@ -378,13 +381,27 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
   // intervals (window band, sinks); their bounds come from the inverse of
   // the position map once per tile, shifted by 4*hi, and are compared with
   // the compile-time c.
+  // Under the stripe layout the first key row at or past a position does
+  // not depend on the tile: the four bounds are found once (per-lane
+  // divisions kept out of the tile loop).  Under the others key rows and
+  // positions differ by a constant per monotone piece (per zigzag chunk).
+  const int32_t dpos0 = kstripe ? 0 : -position(km, 0);
+  const int32_t dpos1 = km.kind == MAP_ZIGZAG ? khalf - position(km, khalf) : dpos0;
+  int32_t fs_lo = 0, fs_hi = 0, fs_slo = 0, fs_shi = 0;
+  if (kstripe) {
+    fs_lo = first_row_at_least(km, 0, vis_lo);
+    fs_hi = first_row_at_least(km, 0, vis_hi + 1);
+    fs_slo = first_row_at_least(km, 0, sstart);
+    fs_shi = first_row_at_least(km, 0, sink_hi + 1);
+  }
   auto apply_mask = [&](f32x16 (&sc)[NB], int k0, int kend) {
     const int32_t kend_du = kend - 1 - k0;
     const int32_t sh = k0 + 4 * hi;
-    const int32_t lo = first_row_at_least(km, k0, vis_lo) - sh;
-    const int32_t up = min(first_row_at_least(km, k0, vis_hi + 1) - 1 - k0, kend_du) - 4 * hi;
-    const int32_t slo = first_row_at_least(km, k0, sstart) - sh;
-    const int32_t sup = min(first_row_at_least(km, k0, sink_hi + 1) - 1 - k0, kend_du) - 4 * hi;
+    const int32_t dpos = k0 >= khalf ? dpos1 : dpos0;
+    const int32_t lo = (kstripe ? fs_lo : vis_lo + dpos) - sh;
+    const int32_t up = min((kstripe ? fs_hi : vis_hi + 1 + dpos) - 1 - k0, kend_du) - 4 * hi;
+    const int32_t slo = (kstripe ? fs_slo : sstart + dpos) - sh;
+    const int32_t sup = min((kstripe ? fs_shi : sink_hi + 1 + dpos) - 1 - k0, kend_du) - 4 * hi;
     // With a window (WIN) most of a partial tile's 32-key blocks are
     // visible or hidden as a whole for every lane of the wave: such a block
     // takes no per-element mask (wave-uniform branches).  Without one the
@@ -403,11 +420,30 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
           continue;
         }
       }
+      if constexpr (WIN) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
-        const bool vis = ((c >= lo) & (c <= up)) | ((c >= slo) & (c <= sup));
-        sc[kb][r] = vis ? sc[kb][r] : -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
+          const bool vis = ((c >= lo) & (c <= up)) | ((c >= slo) & (c <= sup));
+          sc[kb][r] = vis ? sc[kb][r] : -INFINITY;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        // no window: no sinks either, one interval [lo, up], tested with
+        // one unsigned compare per element (an empty interval becomes one
+        // that starts past every key of the tile).  The scheduling barrier
+        // per 32-key block keeps the compiler from computing all the blocks'
+        // lane masks ahead of their selects (which spilled hundreds of SGPRs).
+        const bool empty = up < lo;
+        const int32_t lo1 = empty ? (1 << 30) : lo;
+        const uint32_t w1 = empty ? 0u : (uint32_t)(up - lo);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
+          const bool vis = (uint32_t)(c - lo1) <= w1;
+          sc[kb][r] = vis ? sc[kb][r] : -INFINITY;
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };

@@ -12,10 +12,13 @@
 //                    resident in registers (each lane holds one query, as in
 //                    the forward kernel), then dQ^T += K^T dS^T with dS^T
 //                    taken straight from the accumulator layout;
-//   bwd_dkdv_kernel: 4 waves x 32 keys; K and V of the tile resident in
-//                    registers; Q, dO, LSE and delta of 64-row query tiles in
-//                    LDS; S = Q K^T and dP = dO V^T (each lane holds one
-//                    key), then dV^T += dO^T P and dK^T += Q^T dS.
+//   bwd_dkdv_kernel: 8 waves in pairs over 32 keys each (one key per
+//                    lane); Q, dO, LSE and delta of 64-row query tiles in
+//                    LDS; in each pair one wave holds K, forms S = Q K^T and
+//                    P and accumulates dV^T += dO^T P, the other holds V,
+//                    forms dP = dO V^T and dS (P through LDS) and
+//                    accumulates dK^T += Q^T dS, the two alternating
+//                    between the matrix core and the vector ALU.
 // Both walk the visible pairs from host plans: the forward's (query tile ->
 // key runs) for dQ, and its transpose (key tile -> query runs) for dK / dV,
 // with per-element masks only in partial runs.
@@ -79,31 +82,50 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const void* out, int out
 // q/dout buffers, k_rank = query rank; runs: local query rows
 // [k_begin, k_end) and whether every pair of the run is visible.
 //
-// The workgroup walks one flat sequence of query tiles ((run, 64-row tile)
-// backwards, query head of the KV group innermost) with two LDS buffers: tile n + 1 (Q, dO, LSE,
-// delta) is copied global -> LDS directly (buffer loads to LDS) while tile
-// n is computed.  Per tile and wave (32 keys, one per lane):
-//   A(qb): S and dP of query block qb (32 rows) = Q K^T, dO V^T;
-//   B(qb): P = exp2(S c - LSE log2 e), dS = P (dP - delta) -> bf16;
-//   C(qb): dV^T += dO^T P, dK^T += Q^T dS.
-// Issue order A0 A1 B0 B1 C0 C1, with B0's VALU work placed between A1's
-// MFMAs and B1's between C0's, and LDS fragment reads kPF MFMAs ahead.
+// Wave roles.  8 waves: wave wg (0-3) and wave wg + 4 share the 32 keys
+// wg*32 .. +31 of the tile (one key per lane) and, by the hardware's
+// placement, one SIMD.  Wave wg (the P wave) holds K and accumulates dV^T;
+// wave wg + 4 (the dS wave) holds V and accumulates dK^T.  Per 64-row query
+// tile n (Q, dO, LSE, delta), with S = Q K^T and dP = dO V^T in the C layout
+// of the forward kernel (lane = key, 16 query rows per 32-row block):
+//   P wave:  S(n)                  [matrix]
+//            P = exp2(S c - LSE log2 e) -> LDS exchange (f32, times the
+//            softcap derivative), bf16 P for dV   [vector]
+//            dV^T += dO^T P         [matrix]
+//   dS wave: dP(n)                 [matrix]
+//            dS = P (dP - delta) from the exchange   [vector]
+//            dK^T += Q^T dS         [matrix]
+// The two waves of a SIMD alternate: in phase 2n the P wave runs its
+// softmax of tile n while the dS wave runs dK(n-1) and dP(n) on the matrix
+// core; in phase 2n+1 the P wave runs dV(n) and S(n+1) while the dS wave
+// forms dS(n).  Every phase ends with a workgroup barrier (no memory fence;
+// each wave waits for its own LDS writes and tile loads explicitly first).
+// Tile staging straight into LDS: the P waves load Q (3 buffers: Q(n) is
+// read in phases 2n-1 .. 2n+2), issued two phases ahead of use; the dS
+// waves load dO, LSE and delta (2 buffers, read in phases 2n, 2n+1).
 template <int D, int MODS>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
   using T = SwzTile<D>;
-  constexpr int BQ = 64;            // query rows per tile
+  constexpr int BQ = 64;                    // query rows per tile
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int TILEB = BQ * D * 2;
-  constexpr int LPW = TILEB / 4096;
+  constexpr int TILEB = BQ * D * 2;         // one Q or dO tile
+  constexpr int LPT = TILEB / 4096;         // 16-byte copies per thread of a 4-wave group
   constexpr int RPI = 1024 / T::ROWB;
-  constexpr int BUFB = 2 * TILEB + 2 * BQ * 4;  // Q, dO, LSE, delta
+  constexpr int OBUFB = TILEB + 2 * BQ * 4; // dO, LSE, delta
+  constexpr int XB = BQ * 32 * 4;           // P exchange of one wave pair (f32)
   constexpr int PF = kPF;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * BUFB];
+  static_assert(TILEB % 4096 == 0 && OBUFB % 512 == 0, "tile layout");
+  __shared__ __attribute__((aligned(1024))) char smem[3 * TILEB + 2 * OBUFB + 4 * XB];
+  char* const qbuf = smem;
+  char* const obuf = smem + 3 * TILEB;
+  char* const xbuf = obuf + 2 * OBUFB;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wid = tid >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wid >> 2;   // 0: P wave, 1: dS wave
+  const int wg = wid & 3;     // key slice
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
@@ -117,10 +139,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   const int hk = hb % p.Hkv;
   const int b = hb / p.Hkv;
   const WorkItem it = p.items[item_idx];
-  if (it.q_rows == 0) return;  // key tile no query sees (whole workgroup)
+  if (it.q_rows == 0 || it.run_begin == it.run_end) return;  // no query sees these keys (whole workgroup)
   const int group = p.Hq / p.Hkv;
 
-  const int kr_ = wid * 32 + l32;
+  const int kr_ = wg * 32 + l32;
   const bool kvalid = kr_ < it.q_rows;
   const int64_t krow = (int64_t)it.q_row0 + kr_;
   const int64_t kv_row_stride = (int64_t)p.Hkv * D;
@@ -140,52 +162,80 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   const float* lbase = p.lse + ((int64_t)b * p.Hq + h0) * p.Lq_buf + it.k_row0;
   const float* dbase = p.delta + ((int64_t)b * p.Hq + h0) * p.Lq_buf + it.k_row0;
   const uint32_t qrow_bytes = (uint32_t)p.Hq * D * 2;
-  const i32x4 qrs = buffer_rsrc(qbase);
-  const i32x4 ors = buffer_rsrc(obase);
-  const i32x4 lrs = buffer_rsrc(wid == 1 ? (const void*)dbase : (const void*)lbase);
+  const i32x4 trs = buffer_rsrc(grp ? (const void*)obase : (const void*)qbase);
+  const i32x4 lrs = buffer_rsrc(wg == 1 ? (const void*)dbase : (const void*)lbase);
   const int lrow = lane / T::CPR;
   const int lslot = lane % T::CPR;
 
-  // Thread (wave wid, lane i) copies slices wid*LPW + j of Q and dO: physical
-  // (row, chunk slot) = (slice*RPI + i / CPR, i % CPR), i.e. logical chunk
-  // slot ^ swz(row) of that row; waves 0 and 1 copy the 64 LSE / delta
-  // values.  Rows past the run's end are clamped to its last row (they are
-  // masked in the partial runs that have them; full runs are multiples of
-  // BQ rows).
-  auto dma = [&](char* buf, int gi, int t0, int tend) {
-#pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-      const int row = (wid * LPW + j) * RPI + lrow;
-      const uint32_t off = (uint32_t)min(t0 + row, tend - 1) * qrow_bytes + (uint32_t)(gi * D * 2) +
-                           (uint32_t)((lslot ^ T::swz(row)) * 16);
-      copy16_to_lds(qrs, lds_addr(buf + (wid * LPW + j) * 1024), off);
-      copy16_to_lds(ors, lds_addr(buf + TILEB + (wid * LPW + j) * 1024), off);
-    }
-    if (wid < 2) {
-      const uint32_t off = (uint32_t)(gi * p.Lq_buf + min(t0 + lane, tend - 1)) * 4u;
-      copy4_to_lds(lrs, lds_addr(buf + 2 * TILEB + wid * BQ * 4), off);
+  // Tile cursor: query tiles from the last run's last tile backwards, the
+  // group's query heads innermost.  Under a causal mask every key tile's
+  // query range ends at the rank's last row, so the workgroups resident at
+  // one time start at the same rows and stream the same Q / dO tiles at
+  // about the same time (shared through L2 instead of refetched).
+  struct Cursor {
+    int gi, ri, t0;
+    Run run;
+  };
+  auto last_tile = [](const Run& r) { return r.k_begin + ((r.k_end - r.k_begin - 1) / BQ) * BQ; };
+  Cursor c0;
+  c0.gi = 0;
+  c0.ri = it.run_end - 1;
+  c0.run = p.runs[c0.ri];
+  c0.t0 = last_tile(c0.run);
+  auto advance = [&](Cursor& c) {  // only while another tile follows
+    if (++c.gi == group) {
+      c.gi = 0;
+      c.t0 -= BQ;
+      if (c.t0 < c.run.k_begin) {
+        c.run = p.runs[--c.ri];
+        c.t0 = last_tile(c.run);
+      }
     }
   };
 
-  bf16x8 kf[KS], vf[KS];
+  // Tile copy by this wave's group (Q for the P waves; dO, LSE and delta for
+  // the dS waves): thread (wave wg, lane i) copies slices wg*LPT + j, i.e.
+  // physical (row, chunk slot) = (slice*RPI + i / CPR, i % CPR) = logical
+  // chunk slot ^ swz(row) of that row; dS waves 0 and 1 copy the 64 LSE /
+  // delta values.  Rows past the run's end are clamped to its last row
+  // (masked in the partial runs that have them; full runs are multiples of
+  // BQ rows).
+  auto dma = [&](char* buf, const Cursor& c) {
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      const int row = (wg * LPT + j) * RPI + lrow;
+      const uint32_t off = (uint32_t)min(c.t0 + row, c.run.k_end - 1) * qrow_bytes + (uint32_t)(c.gi * D * 2) +
+                           (uint32_t)((lslot ^ T::swz(row)) * 16);
+      copy16_to_lds(trs, lds_addr(buf + (wg * LPT + j) * 1024), off);
+    }
+    if (grp == 1 && wg < 2) {
+      const uint32_t off = (uint32_t)(c.gi * p.Lq_buf + min(c.t0 + lane, c.run.k_end - 1)) * 4u;
+      copy4_to_lds(lrs, lds_addr(buf + TILEB + wg * BQ * 4), off);
+    }
+  };
+
+  // K (P waves) or V (dS waves) fragments of this lane's key: B operand
+  bf16x8 kv[KS];
   {
-    const int64_t off = (int64_t)b * p.kv_batch_stride + krow * kv_row_stride + hk * D + hi * 8;
+    const uint16_t* src = (grp ? p.v : p.k) + (int64_t)b * p.kv_batch_stride + krow * kv_row_stride + hk * D + hi * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (kvalid) {
-        kf[ks] = *reinterpret_cast<const bf16x8*>(p.k + off + ks * 16);
-        vf[ks] = *reinterpret_cast<const bf16x8*>(p.v + off + ks * 16);
+        kv[ks] = *reinterpret_cast<const bf16x8*>(src + ks * 16);
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) kf[ks][e] = vf[ks][e] = (__bf16)0.f;
+        for (int e = 0; e < 8; ++e) kv[ks][e] = (__bf16)0.f;
       }
     }
   }
-  f32x16 dkt[DB], dvt[DB];
+  // acc: dV^T (P waves) or dK^T (dS waves); sc: S or dP of the two 32-row
+  // blocks; bb: bf16 P or dS (B operand of the accumulating products)
+  f32x16 acc[DB], sc[2];
+  bf16x8 bb[2][2];
 #pragma unroll
   for (int d = 0; d < DB; ++d)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dkt[d][r] = dvt[d][r] = 0.f;
+    for (int r = 0; r < 16; ++r) acc[d][r] = 0.f;
 
   // This lane's key position pk; the query positions that see it form one
   // interval [lo_p, hi_p]: same sequence, p_q >= p_k under causal / window,
@@ -219,212 +269,310 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   const int32_t qhalf = qm.kind == MAP_ZIGZAG ? qm.L >> 1 : 0x7fffffff;
   const float rb0 = (float)((qstripe ? qm.rank * qm.b : position(qm, 0)) - pk);
   const float rb1 = qm.kind == MAP_ZIGZAG ? (float)(position(qm, qhalf) - qhalf - pk) : rb0;
+  float cap_a = p.mods.a, cap_2a = 2.f * p.mods.a, cap_b2 = p.mods.b2;
+  if constexpr ((MODS & 1) != 0) asm("" : "+v"(cap_a), "+v"(cap_2a), "+v"(cap_b2));
 
-  // One tile.  FULL: every pair visible.  Otherwise element r of query
-  // block qb is local row t0 + qb*32 + 8*(r/4) + 4*hi + r%4; query
-  // positions increase through the run, so the rows that see this lane's
-  // key are one interval, found once per tile.
-  auto tile = [&](auto full_c, const char* buf, int t0, int tend, int gi) {
-    constexpr bool FULL = decltype(full_c)::value;
-    const char* tQ = buf;
-    const char* tO = buf + TILEB;
-    const float* sl = reinterpret_cast<const float*>(buf + 2 * TILEB);
-    const float* sd = sl + BQ;
-    int32_t lo = 0, up = 0;
-    if constexpr (!FULL) {
-      lo = first_row_at_least(qm, t0, lo_p) - t0 - 4 * hi;
-      up = min(first_row_at_least(qm, t0, hi_p + 1) - 1, tend - 1) - t0 - 4 * hi;
-    }
-    auto visible = [&](int qb, int r) -> bool {
-      if constexpr (FULL) {
-        return true;
-      } else {
-        const int cc = qb * 32 + 8 * (r >> 2) + (r & 3);
-        return (cc >= lo) & (cc <= up);
-      }
-    };
-    auto read_a = [&](int i) {
-      const int qb = i / (2 * KS), w = i % (2 * KS);
-      return T::frag((w & 1) ? tO : tQ, qb * 32 + l32, 2 * (w >> 1) + hi);
-    };
-    // C stream j: (qb, half, d, which): which 0 -> dO^T for dV, 1 -> Q^T for dK
-    auto read_c = [&](int j) {
-      const int qb = j / (4 * DB), r = j % (4 * DB), half = r / (2 * DB), d = (r / 2) % DB;
-      return frag_tr<D>((r & 1) ? tQ : tO, qb, half, d, lane);
-    };
-    constexpr int NA = 2 * 2 * KS;
-    constexpr int NC = 2 * 4 * DB;
-    f32x16 s[2], dp[2];
-    bf16x8 fa[NA], fc[NC];
-    bf16x8 pb[2][2], dsb[2][2];
-    const f32x16 zero = {};
-    // LSE and delta of this lane's 16 query rows per block (rows
-    // qb*32 + 8*g + 4*hi + 0..3 for g = 0..3)
-    float4 l4[2][4], d4[2][4];
+  // Matrix phase: the transposed-operand products acc += X^T bb (X = dO for
+  // dV, Q for dK; 2 blocks x 2 halves x DB MFMAs), then the row-operand
+  // products sc = Y kv (Y = Q for S, dO for dP; 2 blocks x KS MFMAs, the two
+  // blocks alternating).  Fragments are read PF MFMAs ahead, across the
+  // boundary, in an order pinned with scheduling groups.
+  constexpr int NT = 2 * 2 * DB;
+  constexpr int NR = 2 * KS;
+  static_assert(PF <= NT && PF <= NR, "prefetch depth");
+  // Per-lane LDS byte offsets of the fragments.  The swizzle of a row
+  // depends on its low 4 bits only, which the 16-row steps of the blocks
+  // leave alone, so one offset per (row, chunk) of block 0 serves all
+  // blocks (their distance is an immediate).  Transposed reads (the rows
+  // of the contraction index, as frag_tr): rows trow and trow + 8 of each
+  // 16-row half, chunk 4d + tchunk, 8-byte half th8.  Row reads: row l32,
+  // chunk 2ks + hi.
+  int tro[2][DB], rro[KS];
+  {
+    const int trow = 4 * hi + ((lane & 15) >> 2);
+    const int tchunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int x = 0; x < 2; ++x)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        l4[qb][g] = *reinterpret_cast<const float4*>(sl + qb * 32 + 8 * g + 4 * hi);
-        d4[qb][g] = *reinterpret_cast<const float4*>(sd + qb * 32 + 8 * g + 4 * hi);
+      for (int d = 0; d < DB; ++d) {
+        const int r = trow + 8 * x;
+        tro[x][d] = r * T::ROWB + (((4 * d + tchunk) ^ T::swz(r)) * 16) + (lane & 1) * 8;
       }
 #pragma unroll
-    for (int i = 0; i < PF; ++i) fa[i] = read_a(i);
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      if (i + PF < NA) fa[i + PF] = read_a(i + PF);
-      else fc[i + PF - NA] = read_c(i + PF - NA);
-      const int qb = i / (2 * KS), w = i % (2 * KS), ks = w >> 1;
-      if (w & 1) dp[qb] = mfma32(fa[i], vf[ks], ks == 0 ? zero : dp[qb]);
-      else s[qb] = mfma32(fa[i], kf[ks], ks == 0 ? zero : s[qb]);
-    }
-    // Score modifiers of element r of block qb (raw units, as the
-    // forward): softcap a - 2a rc with rc = 1 / (exp2(s b2) + 1), whose
-    // derivative factor 1 - tanh^2 = 4 rc (1 - rc) scales dS; then ALiBi.
-    float slope = 0.f, abase = 0.f, rb = 0.f;
-    if constexpr ((MODS & 2) != 0) {
-      slope = p.mods.alibi[h0 + gi] * p.mods.inv_scale;
-      abase = (float)(t0 + 4 * hi);
-      rb = t0 >= qhalf ? rb1 : rb0;
-    }
-    auto mods = [&](int qb, int r, float& sv, float& f, float ab) {
-      if constexpr ((MODS & 1) != 0) {
-        const float rc = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(sv * p.mods.b2) + 1.f);
-        sv = p.mods.a - 2.f * p.mods.a * rc;
-        f = 4.f * rc * (1.f - rc);
-      }
-      if constexpr ((MODS & 2) != 0) {
-        // row index t (the constant is added first so that it folds into one
-        // instruction)
-        const float t = ab + (float)(qb * 32 + 8 * (r >> 2) + (r & 3));
-        const float dd = __builtin_floorf((t + 0.5f) * inv_b) * nb1 + (t + rb);
-        sv -= slope * __builtin_fabsf(dd);
-      }
+    for (int ks = 0; ks < KS; ++ks) rro[ks] = l32 * T::ROWB + (((2 * ks + hi) ^ T::swz(l32)) * 16);
+  }
+  auto m_phase = [&](auto do_t_c, auto do_r_c, const char* tT, const char* tR) {
+    constexpr bool DT = decltype(do_t_c)::value;
+    constexpr bool DR = decltype(do_r_c)::value;
+    auto rd_t = [&](int j) {
+      const int qb = j / (2 * DB), half = (j / DB) & 1, d = j % DB;
+      const char* blk = tT + (qb * 32 + half * 16) * T::ROWB;
+      const bf16x4 a0 = lds_read_tr(blk + tro[0][d]);
+      const bf16x4 a1 = lds_read_tr(blk + tro[1][d]);
+      return bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
     };
-    auto softmax = [&](int qb) {
-      // The bias terms depend on nothing the MFMAs produce; the empty asm
-      // keeps the compiler from hoisting all of them into live registers
-      // ahead of the matrix products.
-      float ab = abase;
-      if constexpr ((MODS & 2) != 0) asm volatile("" : "+v"(ab));
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float lq[4] = {l4[qb][g].x, l4[qb][g].y, l4[qb][g].z, l4[qb][g].w};
-        const float dq4[4] = {d4[qb][g].x, d4[qb][g].y, d4[qb][g].z, d4[qb][g].w};
-#pragma unroll
-        for (int e = 0; e < 4; e += 2) {
-          const int r0 = 4 * g + e, r1 = r0 + 1;
-          float s0 = s[qb][r0], s1 = s[qb][r1], f0 = 1.f, f1 = 1.f;
-          if constexpr (MODS != 0) {
-            mods(qb, r0, s0, f0, ab);
-            mods(qb, r1, s1, f1, ab);
-          }
-          float p0 = __builtin_amdgcn_exp2f(s0 * c - lq[e] * kLog2e);
-          float p1 = __builtin_amdgcn_exp2f(s1 * c - lq[e + 1] * kLog2e);
-          if constexpr (!FULL) {
-            p0 = visible(qb, r0) ? p0 : 0.f;
-            p1 = visible(qb, r1) ? p1 : 0.f;
-          }
-          float d0 = p0 * (dp[qb][r0] - dq4[e]);
-          float d1 = p1 * (dp[qb][r1] - dq4[e + 1]);
-          if constexpr ((MODS & 1) != 0) {
-            d0 *= f0;
-            d1 *= f1;
-          }
-          const bf16x2 pp = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
-          const bf16x2 dd = __builtin_convertvector((f32x2){d0, d1}, bf16x2);
-          pb[qb][r0 >> 3][r0 & 7] = pp[0];
-          pb[qb][r0 >> 3][r1 & 7] = pp[1];
-          dsb[qb][r0 >> 3][r0 & 7] = dd[0];
-          dsb[qb][r0 >> 3][r1 & 7] = dd[1];
-        }
-      }
+    auto rd_r = [&](int i) {
+      const int ks = i >> 1, qb = i & 1;
+      return *reinterpret_cast<const bf16x8*>(tR + qb * 32 * T::ROWB + rro[ks]);
     };
-    softmax(0);
-    softmax(1);
+    bf16x8 ft[NT], fr[NR];
+    if constexpr (DT) {
 #pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      if (j + PF < NC) fc[j + PF] = read_c(j + PF);
-      const int qb = j / (4 * DB), r = j % (4 * DB), half = r / (2 * DB), d = (r / 2) % DB;
-      if (r & 1) dkt[d] = mfma32(fc[j], dsb[qb][half], dkt[d]);
-      else dvt[d] = mfma32(fc[j], pb[qb][half], dvt[d]);
+      for (int j = 0; j < PF; ++j) ft[j] = rd_t(j);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        if (j + PF < NT) ft[j + PF] = rd_t(j + PF);
+        else if (DR) fr[j + PF - NT] = rd_r(j + PF - NT);
+        const int qb = j / (2 * DB), half = (j / DB) & 1, d = j % DB;
+        acc[d] = mfma32(ft[j], bb[qb][half], acc[d]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PF; ++i) fr[i] = rd_r(i);
     }
-    // scheduling groups, in issue order: the LSE / delta reads, A0 (MFMA,
-    // read), A1 (MFMA, read, B0's VALU), C0 (MFMA, reads, B1's VALU), C1
-    // (MFMA, reads)
-    constexpr int NA0 = 2 * KS;
-    constexpr int NC0 = 4 * DB;
-    __builtin_amdgcn_sched_group_barrier(0x100, 16 + PF, 0);
+    if constexpr (DR) {
+      const f32x16 zero = {};
 #pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      sched_ds_read((i + PF < NA) ? 1 : 2);
-      if (i >= NA0) __builtin_amdgcn_sched_group_barrier(0x002, kKvValuA, 0);
+      for (int i = 0; i < NR; ++i) {
+        if (i + PF < NR) fr[i + PF] = rd_r(i + PF);
+        const int ks = i >> 1, qb = i & 1;
+        sc[qb] = mfma32(fr[i], kv[ks], ks == 0 ? zero : sc[qb]);
+      }
     }
+    // scheduling groups, in issue order (a transposed fragment is 2 reads)
+    if constexpr (DT) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
 #pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (j + PF < NC) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      if (j < NC0) __builtin_amdgcn_sched_group_barrier(0x002, kKvValuC, 0);
+      for (int j = 0; j < NT - PF; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < PF; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if constexpr (DR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    } else {
+      __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+    }
+    if constexpr (DR) {
+#pragma unroll
+      for (int i = 0; i < NR - PF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < PF; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
   };
 
-  // Tile order: query tiles from the last run's last tile backwards, the
-  // group's query heads innermost.  Under a causal mask every key tile's
-  // query range ends at the rank's last row, so the workgroups resident at
-  // one time start at the same rows and stream the same Q / dO tiles at
-  // about the same time (shared through L2 instead of refetched).
-  auto last_tile = [](const Run& r) { return r.k_begin + ((r.k_end - r.k_begin - 1) / BQ) * BQ; };
-  int c_gi = 0, c_ri = it.run_end - 1;
-  Run c_run = p.runs[c_ri];
-  int c_t0 = last_tile(c_run);
-  dma(smem, c_gi, c_t0, c_run.k_end);
+  // P exchange slot of this wave pair: float4 j (block qb, row group g) of
+  // lane l at (j * 64 + l) * 16
+  float* const xw = reinterpret_cast<float*>(xbuf + wg * XB);
 
-  for (int n = 0; n < n_tiles; ++n) {
-    const int gi = c_gi;
-    const int t0 = c_t0;
-    const int t_end = c_run.k_end;
-    const bool full = c_run.full != 0;
-    const char* buf = smem + (n & 1) * BUFB;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile n are in LDS
-    __syncthreads();                     // every wave's copies landed; tile n - 1's buffer is free
-    if (n + 1 < n_tiles) {
-      if (++c_gi == group) {
-        c_gi = 0;
-        c_t0 -= BQ;
-        if (c_t0 < c_run.k_begin) {
-          c_run = p.runs[--c_ri];
-          c_t0 = last_tile(c_run);
+  // Vector phase of the P wave: P of tile `cur` (S in sc), element r of
+  // block qb is local row t0 + qb*32 + 8*(r/4) + 4*hi + r%4 of head gi.
+  // FULL: every pair visible; otherwise the rows that see this lane's key
+  // are one interval (query positions increase through a run), found once.
+  auto softmax = [&](auto full_c, const Cursor& cur, const char* ob) {
+    constexpr bool FULL = decltype(full_c)::value;
+    const float* sl = reinterpret_cast<const float*>(ob + TILEB);
+    const int t0 = cur.t0;
+    int32_t lo = 0, up = 0;
+    if constexpr (!FULL) {
+      lo = first_row_at_least(qm, t0, lo_p) - t0 - 4 * hi;
+      up = min(first_row_at_least(qm, t0, hi_p + 1) - 1, cur.run.k_end - 1) - t0 - 4 * hi;
+    }
+    // Score modifiers (raw units, as the forward): softcap a - 2a rc with
+    // rc = 1 / (exp2(s b2) + 1), whose derivative factor 1 - tanh^2 =
+    // 4 rc (1 - rc) scales dS (the exchange carries P times it); then ALiBi.
+    float slope = 0.f, ab = 0.f, rb = 0.f;
+    if constexpr ((MODS & 2) != 0) {
+      slope = p.mods.alibi[h0 + cur.gi] * p.mods.inv_scale;
+      ab = (float)(t0 + 4 * hi);
+      rb = t0 >= qhalf ? rb1 : rb0;
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 l4 = *reinterpret_cast<const float4*>(sl + qb * 32 + 8 * g + 4 * hi);
+        const float lq[4] = {l4.x, l4.y, l4.z, l4.w};
+        float px[4], pf[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          float sv = sc[qb][r], f = 1.f;
+          if constexpr ((MODS & 1) != 0) {
+            const float rc = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(sv * cap_b2) + 1.f);
+            sv = cap_a - cap_2a * rc;
+            f = 4.f * rc * (1.f - rc);
+          }
+          if constexpr ((MODS & 2) != 0) {
+            const float t = ab + (float)(qb * 32 + 8 * g + e);
+            const float dd = __builtin_floorf((t + 0.5f) * inv_b) * nb1 + (t + rb);
+            sv -= slope * __builtin_fabsf(dd);
+          }
+          float pe = __builtin_amdgcn_exp2f(sv * c - lq[e] * kLog2e);
+          if constexpr (!FULL) {
+            const int cc = qb * 32 + 8 * g + e;
+            pe = ((cc >= lo) & (cc <= up)) ? pe : 0.f;
+          }
+          px[e] = pe;
+          pf[e] = ((MODS & 1) != 0) ? pe * f : pe;
         }
+        *reinterpret_cast<float4*>(xw + ((qb * 4 + g) * 64 + lane) * 4) = make_float4(pf[0], pf[1], pf[2], pf[3]);
+        const bf16x2 p01 = __builtin_convertvector((f32x2){px[0], px[1]}, bf16x2);
+        const bf16x2 p23 = __builtin_convertvector((f32x2){px[2], px[3]}, bf16x2);
+        const int half = g >> 1, e0 = (g & 1) * 4;
+        bb[qb][half][e0] = p01[0];
+        bb[qb][half][e0 + 1] = p01[1];
+        bb[qb][half][e0 + 2] = p23[0];
+        bb[qb][half][e0 + 3] = p23[1];
       }
-      dma(smem + ((n + 1) & 1) * BUFB, c_gi, c_t0, c_run.k_end);
+      if constexpr (!FULL) __builtin_amdgcn_sched_barrier(0);
     }
-    if (full) tile(std::true_type{}, buf, t0, t_end, gi);
-    else tile(std::false_type{}, buf, t0, t_end, gi);
-  }
+  };
+  // Vector phase of the dS wave: dS = P (dP - delta), dP in sc.
+  auto form_ds = [&](const char* ob) {
+    const float* sd = reinterpret_cast<const float*>(ob + TILEB + BQ * 4);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 px = *reinterpret_cast<const float4*>(xw + ((qb * 4 + g) * 64 + lane) * 4);
+        const float4 d4 = *reinterpret_cast<const float4*>(sd + qb * 32 + 8 * g + 4 * hi);
+        const float d0 = px.x * (sc[qb][4 * g] - d4.x);
+        const float d1 = px.y * (sc[qb][4 * g + 1] - d4.y);
+        const float d2 = px.z * (sc[qb][4 * g + 2] - d4.z);
+        const float d3 = px.w * (sc[qb][4 * g + 3] - d4.w);
+        const bf16x2 a01 = __builtin_convertvector((f32x2){d0, d1}, bf16x2);
+        const bf16x2 a23 = __builtin_convertvector((f32x2){d2, d3}, bf16x2);
+        const int half = g >> 1, e0 = (g & 1) * 4;
+        bb[qb][half][e0] = a01[0];
+        bb[qb][half][e0 + 1] = a01[1];
+        bb[qb][half][e0 + 2] = a23[0];
+        bb[qb][half][e0 + 3] = a23[1];
+      }
+    }
+  };
 
-  if (!kvalid || it.run_begin == it.run_end) return;
-  float* kp = p.dk + (int64_t)b * p.kv_batch_stride + krow * kv_row_stride + hk * D;
-  float* vp = p.dv + (int64_t)b * p.kv_batch_stride + krow * kv_row_stride + hk * D;
-  const float sc = p.scale;
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  auto barrier = []() { asm volatile("s_barrier" ::: "memory"); };
+  auto prio_hi = []() { __builtin_amdgcn_s_setprio(1); };
+  auto prio_lo = []() { __builtin_amdgcn_s_setprio(0); };
+  auto qb_at = [&](int n) { return qbuf + (n % 3) * TILEB; };
+  auto ob_at = [&](int n) { return obuf + (n & 1) * OBUFB; };
+
+  // Epilogue: dV (P waves) or scale * dK (dS waves) added into the f32
+  // gradients of this lane's key.
+  auto store = [&](float* base, float w) {
+    if (!kvalid) return;
+    float* dst = base + (int64_t)b * p.kv_batch_stride + krow * kv_row_stride + hk * D;
 #pragma unroll
-  for (int d = 0; d < DB; ++d) {
+    for (int d = 0; d < DB; ++d) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int dd = d * 32 + 8 * g + 4 * hi;
-      float4 a = *reinterpret_cast<const float4*>(kp + dd);
-      a.x += sc * dkt[d][4 * g];
-      a.y += sc * dkt[d][4 * g + 1];
-      a.z += sc * dkt[d][4 * g + 2];
-      a.w += sc * dkt[d][4 * g + 3];
-      *reinterpret_cast<float4*>(kp + dd) = a;
-      float4 v4 = *reinterpret_cast<const float4*>(vp + dd);
-      v4.x += dvt[d][4 * g];
-      v4.y += dvt[d][4 * g + 1];
-      v4.z += dvt[d][4 * g + 2];
-      v4.w += dvt[d][4 * g + 3];
-      *reinterpret_cast<float4*>(vp + dd) = v4;
+      for (int g = 0; g < 4; ++g) {
+        const int dd = d * 32 + 8 * g + 4 * hi;
+        float4 a = *reinterpret_cast<const float4*>(dst + dd);
+        a.x += w * acc[d][4 * g];
+        a.y += w * acc[d][4 * g + 1];
+        a.z += w * acc[d][4 * g + 2];
+        a.w += w * acc[d][4 * g + 3];
+        *reinterpret_cast<float4*>(dst + dd) = a;
+      }
     }
+  };
+
+  // The two roles run separate programs that pass the same barriers:
+  // prologue (tile 0 lands; the P waves compute S(0)), two phases per tile,
+  // and the dS waves' last dK after the final barrier.  Each loop body holds
+  // one copy of its matrix phase (the first and last tiles' phases are
+  // peeled), so the accumulators keep their registers across iterations.
+  if (grp == 0) {
+    Cursor cs = c0;  // tile of S / softmax
+    Cursor cq = c0;  // tile of the last Q copy
+    dma(qb_at(0), cq);
+    if (n_tiles > 1) {
+      advance(cq);
+      dma(qb_at(1), cq);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    barrier();
+    prio_hi();
+    m_phase(F_{}, T_{}, nullptr, qb_at(0));
+    prio_lo();
+    barrier();
+    // phase 0: softmax of tile 0
+    if (cs.run.full) softmax(T_{}, cs, ob_at(0));
+    else softmax(F_{}, cs, ob_at(0));
+    // the exchange writes, and Q(1) complete
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    barrier();
+    for (int n = 0; n + 1 < n_tiles; ++n) {
+      // phase 2n+1: dV(n), S(n+1)
+      prio_hi();
+      m_phase(T_{}, T_{}, ob_at(n), qb_at(n + 1));
+      prio_lo();
+      if (n + 2 < n_tiles) {
+        advance(cq);
+        dma(qb_at(n + 2), cq);
+      }
+      advance(cs);
+      barrier();
+      // phase 2n+2: softmax of tile n+1
+      if (cs.run.full) softmax(T_{}, cs, ob_at(n + 1));
+      else softmax(F_{}, cs, ob_at(n + 1));
+      // the exchange writes, and Q(n+2) (copied since phase 2n+1), complete
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+      barrier();
+    }
+    // phase 2N-1: dV(N-1)
+    prio_hi();
+    m_phase(T_{}, F_{}, ob_at(n_tiles - 1), nullptr);
+    prio_lo();
+    barrier();
+    store(p.dv, 1.f);
+  } else {
+    Cursor co = c0;  // tile of the last dO copy
+    dma(ob_at(0), co);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    barrier();
+    barrier();
+    // phase 0: dP(0)
+    prio_hi();
+    m_phase(F_{}, T_{}, nullptr, ob_at(0));
+    prio_lo();
+    if (n_tiles > 1) {
+      advance(co);
+      dma(ob_at(1), co);
+    }
+    barrier();
+    // phase 1: dS(0)
+    form_ds(ob_at(0));
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): dO(1) landed
+    barrier();
+    for (int n = 0; n + 1 < n_tiles; ++n) {
+      // phase 2n+2: dK(n), dP(n+1)
+      prio_hi();
+      m_phase(T_{}, T_{}, qb_at(n), ob_at(n + 1));
+      prio_lo();
+      if (n + 2 < n_tiles) {
+        advance(co);
+        dma(ob_at(n + 2), co);
+      }
+      barrier();
+      // phase 2n+3: dS(n+1)
+      form_ds(ob_at(n + 1));
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): dO(n+2) landed
+      barrier();
+    }
+    // phase 2N: dK(N-1)
+    prio_hi();
+    m_phase(T_{}, F_{}, qb_at(n_tiles - 1), nullptr);
+    prio_lo();
+    store(p.dk, p.scale);
   }
 }
 
@@ -474,7 +622,7 @@ usp_status launch_bwd(const BwdParams& pq, const BwdParams& pkv, int D, hipStrea
   if (e == hipSuccess && nk > 0) {
     TimingScope ts(K_BWD_DKDV, stream);
     const int mods = mods_variant(pkv.mods);
-#define USP_LAUNCH_KV(DD, M) hipLaunchKernelGGL((bwd_dkdv_kernel<DD, M>), dim3((unsigned)nk), dim3(256), 0, stream, pkv)
+#define USP_LAUNCH_KV(DD, M) hipLaunchKernelGGL((bwd_dkdv_kernel<DD, M>), dim3((unsigned)nk), dim3(512), 0, stream, pkv)
 #define USP_LAUNCH_KV_M(DD)                  \
   switch (mods) {                            \
     case 0: USP_LAUNCH_KV(DD, 0); break;     \

@@ -114,7 +114,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
   constexpr int RPI = 1024 / T::ROWB;
   constexpr int OBUFB = TILEB + 2 * BQ * 4; // dO, LSE, delta
   constexpr int XB = BQ * 32 * 4;           // P exchange of one wave pair (f32)
-  constexpr int PF = kPF;
   static_assert(TILEB % 4096 == 0 && OBUFB % 512 == 0, "tile layout");
   __shared__ __attribute__((aligned(1024))) char smem[3 * TILEB + 2 * OBUFB + 4 * XB];
   char* const qbuf = smem;
@@ -272,98 +271,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
   float cap_a = p.mods.a, cap_2a = 2.f * p.mods.a, cap_b2 = p.mods.b2;
   if constexpr ((MODS & 1) != 0) asm("" : "+v"(cap_a), "+v"(cap_2a), "+v"(cap_b2));
 
-  // Matrix phase: the transposed-operand products acc += X^T bb (X = dO for
-  // dV, Q for dK; 2 blocks x 2 halves x DB MFMAs), then the row-operand
-  // products sc = Y kv (Y = Q for S, dO for dP; 2 blocks x KS MFMAs, the two
-  // blocks alternating).  Fragments are read PF MFMAs ahead, across the
-  // boundary, in an order pinned with scheduling groups.
-  constexpr int NT = 2 * 2 * DB;
-  constexpr int NR = 2 * KS;
-  static_assert(PF <= NT && PF <= NR, "prefetch depth");
-  // Per-lane LDS byte offsets of the fragments.  The swizzle of a row
-  // depends on its low 4 bits only, which the 16-row steps of the blocks
-  // leave alone, so one offset per (row, chunk) of block 0 serves all
-  // blocks (their distance is an immediate).  Transposed reads (the rows
-  // of the contraction index, as frag_tr): rows trow and trow + 8 of each
-  // 16-row half, chunk 4d + tchunk, 8-byte half th8.  Row reads: row l32,
-  // chunk 2ks + hi.
+  // Matrix phases: acc += X^T bb (X = dO for dV, Q for dK), then sc = Y kv
+  // (Y = Q for S, dO for dP).
   int tro[2][DB], rro[KS];
-  {
-    const int trow = 4 * hi + ((lane & 15) >> 2);
-    const int tchunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-      for (int d = 0; d < DB; ++d) {
-        const int r = trow + 8 * x;
-        tro[x][d] = r * T::ROWB + (((4 * d + tchunk) ^ T::swz(r)) * 16) + (lane & 1) * 8;
-      }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) rro[ks] = l32 * T::ROWB + (((2 * ks + hi) ^ T::swz(l32)) * 16);
-  }
+  pp_offsets<D>(lane, tro, rro);
   auto m_phase = [&](auto do_t_c, auto do_r_c, const char* tT, const char* tR) {
-    constexpr bool DT = decltype(do_t_c)::value;
-    constexpr bool DR = decltype(do_r_c)::value;
-    auto rd_t = [&](int j) {
-      const int qb = j / (2 * DB), half = (j / DB) & 1, d = j % DB;
-      const char* blk = tT + (qb * 32 + half * 16) * T::ROWB;
-      const bf16x4 a0 = lds_read_tr(blk + tro[0][d]);
-      const bf16x4 a1 = lds_read_tr(blk + tro[1][d]);
-      return bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-    };
-    auto rd_r = [&](int i) {
-      const int ks = i >> 1, qb = i & 1;
-      return *reinterpret_cast<const bf16x8*>(tR + qb * 32 * T::ROWB + rro[ks]);
-    };
-    bf16x8 ft[NT], fr[NR];
-    if constexpr (DT) {
-#pragma unroll
-      for (int j = 0; j < PF; ++j) ft[j] = rd_t(j);
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        if (j + PF < NT) ft[j + PF] = rd_t(j + PF);
-        else if (DR) fr[j + PF - NT] = rd_r(j + PF - NT);
-        const int qb = j / (2 * DB), half = (j / DB) & 1, d = j % DB;
-        acc[d] = mfma32(ft[j], bb[qb][half], acc[d]);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < PF; ++i) fr[i] = rd_r(i);
-    }
-    if constexpr (DR) {
-      const f32x16 zero = {};
-#pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        if (i + PF < NR) fr[i + PF] = rd_r(i + PF);
-        const int ks = i >> 1, qb = i & 1;
-        sc[qb] = mfma32(fr[i], kv[ks], ks == 0 ? zero : sc[qb]);
-      }
-    }
-    // scheduling groups, in issue order (a transposed fragment is 2 reads)
-    if constexpr (DT) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
-#pragma unroll
-      for (int j = 0; j < NT - PF; ++j) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-#pragma unroll
-      for (int j = 0; j < PF; ++j) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if constexpr (DR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-    } else {
-      __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
-    }
-    if constexpr (DR) {
-#pragma unroll
-      for (int i = 0; i < NR - PF; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < PF; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
+    pp_matrix_phase<D, decltype(do_t_c)::value, decltype(do_r_c)::value>(acc, sc, bb, kv, tro, rro, tT, tR);
   };
 
   // P exchange slot of this wave pair: float4 j (block qb, row group g) of
@@ -459,7 +372,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
 
   using T_ = std::true_type;
   using F_ = std::false_type;
-  auto barrier = []() { asm volatile("s_barrier" ::: "memory"); };
+  auto barrier = []() { pp_barrier(); };
   auto prio_hi = []() { __builtin_amdgcn_s_setprio(1); };
   auto prio_lo = []() { __builtin_amdgcn_s_setprio(0); };
   auto qb_at = [&](int n) { return qbuf + (n % 3) * TILEB; };

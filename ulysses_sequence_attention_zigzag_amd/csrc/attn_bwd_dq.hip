@@ -1,8 +1,6 @@
 // dQ kernel of the block-attention backward (see attn_bwd.hip for the
-// terms and the plan it walks).  Built in a translation unit of its own so
-// that its MFMAs take the VGPR accumulator form: the S^T / dP^T results
-// feed VALU softmax work directly and the dQ accumulators stay put, where the
-// AGPR form would copy them between register files every tile.
+// terms and the plan it walks).  Built with VGPR-form MFMAs: the S^T / dP^T
+// results feed the vector phases directly.
 
 #include "mfma_common.h"
 
@@ -10,29 +8,45 @@ namespace usp {
 namespace {
 
 // -------------------------------------------------------------------- dQ
-// Per 64-key tile and wave (32 query rows, one per lane):
-//   A(kb): S^T and dP^T of key block kb (32 keys) = K Q^T, V dO^T;
-//   B(kb): dS^T = exp2(S^T c - lse2) (dP^T - delta) -> bf16 (B-operand order);
-//   C(kb): dQ^T += K^T dS^T.
-// Issue order A0 A1 B0 C0 B1 C1, with B0's VALU work placed between A1's
-// MFMAs and B1's between C0's, and every LDS fragment read issued kPF
-// MFMAs ahead of its use.
+// Wave roles.  8 waves: wave wg (0-3) and wave wg + 4 share the 32 query
+// rows wg*32 .. +31 of the item (one row per lane) and, by the hardware's
+// placement, one SIMD.  Wave wg (the P wave) holds Q; wave wg + 4 (the dS
+// wave) holds dO and accumulates dQ^T.  Per 64-key tile n (K, V), with
+// S^T = K Q^T and dP^T = V dO^T in the C layout (lane = query, 16 keys per
+// 32-key block):
+//   P wave:  S^T(n)                 [matrix]
+//            P^T = exp2(S^T c - LSE log2 e) -> LDS exchange (f32, times the
+//            softcap derivative)    [vector]
+//   dS wave: dP^T(n)                [matrix]
+//            dS^T = P^T (dP^T - delta) from the exchange   [vector]
+//            dQ^T += K^T dS^T       [matrix]
+// Phases: in phase 2n the P wave forms P(n) while the dS wave runs dQ(n-1)
+// and dP(n); in phase 2n+1 the P wave runs S(n+1) while the dS wave forms
+// dS(n).  Every phase ends with a workgroup barrier.  Tile staging straight
+// into LDS: the P waves load K (3 buffers: K(n) is read in phases
+// 2n-1 .. 2n+2), the dS waves V (2 buffers), each two phases ahead of use.
 template <int D, int MODS>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const BwdParams p) {
+__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
   using T = SwzTile<D>;
-  constexpr int BN = 64;
+  constexpr int BN = 64;                   // keys per tile
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int TILEB = BN * D * 2;
-  constexpr int LPW = TILEB / 4096;
+  constexpr int LPT = TILEB / 4096;        // 16-byte copies per thread of a 4-wave group
   constexpr int RPI = 1024 / T::ROWB;
-  constexpr int PF = kPF;
+  constexpr int XB = BN * 32 * 4;          // P exchange of one wave pair (f32)
   static_assert(kTileN % BN == 0, "planner granularity");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILEB];  // two buffers of (K, V)
+  static_assert(TILEB % 4096 == 0, "tile layout");
+  __shared__ __attribute__((aligned(1024))) char smem[3 * TILEB + 2 * TILEB + 4 * XB];
+  char* const kbuf = smem;
+  char* const vbuf = smem + 3 * TILEB;
+  char* const xbuf = vbuf + 2 * TILEB;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wid = tid >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wid >> 2;   // 0: P wave, 1: dS wave
+  const int wg = wid & 3;     // query slice
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
@@ -44,25 +58,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const BwdParams p) {
   const int h = hb % p.Hq;
   const int b = hb / p.Hq;
   const WorkItem it = p.items[item_idx];
-  if (it.q_rows == 0) return;  // planner slot with nothing to do (whole workgroup)
+  if (it.q_rows == 0 || it.run_begin == it.run_end) return;  // nothing to do (whole workgroup)
   const int hk = h / (p.Hq / p.Hkv);
 
-  const int qr = wid * 32 + l32;
+  const int qr = wg * 32 + l32;
   const bool qvalid = qr < it.q_rows;
   const int64_t qrow = (int64_t)it.q_row0 + qr;
 
-  bf16x8 qf[KS], dof[KS];
+  // Q (P waves) or dO (dS waves) fragments of this lane's row: B operand
+  bf16x8 kv[KS];
   {
-    const int64_t off = (int64_t)b * p.q_batch_stride + (qrow * p.Hq + h) * D + hi * 8;
-    const int64_t goff = (int64_t)b * p.g_batch_stride + (qrow * p.Hq + h) * D + hi * 8;
+    const uint16_t* src = grp ? p.dout + (int64_t)b * p.g_batch_stride : p.q + (int64_t)b * p.q_batch_stride;
+    src += (qrow * p.Hq + h) * D + hi * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (qvalid) {
-        qf[ks] = *reinterpret_cast<const bf16x8*>(p.q + off + ks * 16);
-        dof[ks] = *reinterpret_cast<const bf16x8*>(p.dout + goff + ks * 16);
+        kv[ks] = *reinterpret_cast<const bf16x8*>(src + ks * 16);
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qf[ks][e] = dof[ks][e] = (__bf16)0.f;
+        for (int e = 0; e < 8; ++e) kv[ks][e] = (__bf16)0.f;
       }
     }
   }
@@ -74,12 +88,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const BwdParams p) {
     lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
     dl = p.delta[li];
   }
-
-  f32x16 dqt[DB];
+  // acc: dQ^T (dS waves); sc: S^T or dP^T of the two 32-key blocks; bb: dS^T
+  f32x16 acc[DB], sc[2];
+  bf16x8 bb[2][2];
 #pragma unroll
   for (int d = 0; d < DB; ++d)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dqt[d][r] = 0.f;
+    for (int r = 0; r < 16; ++r) acc[d][r] = 0.f;
 
   PosMap qm = p.qmap;
   qm.rank = it.q_rank;
@@ -105,11 +120,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const BwdParams p) {
   }
 
   const int64_t kv_row_stride = (int64_t)p.Hkv * D;
-  const uint16_t* kbase = p.k + (int64_t)b * p.kv_batch_stride + (int64_t)it.k_row0 * kv_row_stride + hk * D;
-  const uint16_t* vbase = p.v + (int64_t)b * p.kv_batch_stride + (int64_t)it.k_row0 * kv_row_stride + hk * D;
+  const uint16_t* tbase = (grp ? p.v : p.k) + (int64_t)b * p.kv_batch_stride + (int64_t)it.k_row0 * kv_row_stride + hk * D;
   const uint32_t row_bytes = (uint32_t)kv_row_stride * 2;
-  const i32x4 krs = buffer_rsrc(kbase);
-  const i32x4 vrs = buffer_rsrc(vbase);
+  const i32x4 trs = buffer_rsrc(tbase);
   const int lrow = lane / T::CPR;
   const int lslot = lane % T::CPR;
   const float c = p.scale_log2;
@@ -125,201 +138,251 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const BwdParams p) {
   const float rb0 = (float)((kstripe ? km.rank * km.b : position(km, 0)) - pq_row);
   const float rb1 = km.kind == MAP_ZIGZAG ? (float)(position(km, khalf) - khalf - pq_row) : rb0;
   const float slope = (MODS & 2) ? p.mods.alibi[h] * p.mods.inv_scale : 0.f;
+  float cap_a = p.mods.a, cap_2a = 2.f * p.mods.a, cap_b2 = p.mods.b2;
+  if constexpr ((MODS & 1) != 0) asm("" : "+v"(cap_a), "+v"(cap_2a), "+v"(cap_b2));
+  // Key rows and positions differ by a constant per monotone piece (per
+  // zigzag chunk) except under the stripe layout, whose first key row at or
+  // past a position does not depend on the tile: those bounds are found once.
+  const int32_t dpos0 = kstripe ? 0 : -position(km, 0);
+  const int32_t dpos1 = km.kind == MAP_ZIGZAG ? khalf - position(km, khalf) : dpos0;
+  int32_t fs_lo = 0, fs_hi = 0, fs_slo = 0, fs_shi = 0;
+  if (kstripe) {
+    fs_lo = first_row_at_least(km, 0, vis_lo);
+    fs_hi = first_row_at_least(km, 0, vis_hi + 1);
+    fs_slo = first_row_at_least(km, 0, sstart);
+    fs_shi = first_row_at_least(km, 0, sink_hi + 1);
+  }
 
-  // The workgroup walks the key tiles of its runs with two LDS buffers: tile
-  // n + 1 is copied global -> LDS directly (buffer loads to LDS) while tile
-  // n is computed.  Thread (wave wid, lane i) copies slices wid*LPW + j of K
-  // and V: physical (row, chunk slot) = (slice*RPI + i / CPR, i % CPR), i.e.
-  // logical chunk slot ^ swz(row); rows past the run's end are clamped to its
-  // last row (masked in partial runs; full runs are multiples of BN keys).
-  auto dma = [&](char* buf, int k0, int kend) {
-#pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-      const int row = (wid * LPW + j) * RPI + lrow;
-      const uint32_t off = (uint32_t)min(k0 + row, kend - 1) * row_bytes + (uint32_t)((lslot ^ T::swz(row)) * 16);
-      copy16_to_lds(krs, lds_addr(buf + (wid * LPW + j) * 1024), off);
-      copy16_to_lds(vrs, lds_addr(buf + TILEB + (wid * LPW + j) * 1024), off);
+  // Tile cursor: the key tiles of the item's runs in order.
+  struct Cursor {
+    int ri, k0;
+    Run run;
+  };
+  Cursor c0;
+  c0.ri = it.run_begin;
+  c0.run = p.runs[c0.ri];
+  c0.k0 = c0.run.k_begin;
+  auto advance = [&](Cursor& cu) {  // only while another tile follows
+    cu.k0 += BN;
+    if (cu.k0 >= cu.run.k_end) {
+      cu.run = p.runs[++cu.ri];
+      cu.k0 = cu.run.k_begin;
     }
   };
-
-  // One tile.  FULL: every pair visible (no mask).  Otherwise element r of
-  // key block kb is key k0 + du, du = kb*32 + 8*(r/4) + 4*hi + r%4; key
-  // positions increase through the run, so this lane's visible keys (window
-  // band, sinks) are at most two intervals of du, found once per tile.
-  auto tile = [&](auto full_c, const char* tK, int k0, int kend) {
-    constexpr bool FULL = decltype(full_c)::value;
-    const char* tV = tK + TILEB;
-    int32_t lo = 0, up = 0, slo = 0, sup = -1;
-    if constexpr (!FULL) {
-      const int32_t last = kend - 1 - k0;
-      const int32_t sh = k0 + 4 * hi;
-      lo = first_row_at_least(km, k0, vis_lo) - sh;
-      up = min(first_row_at_least(km, k0, vis_hi + 1) - 1 - k0, last) - 4 * hi;
-      slo = first_row_at_least(km, k0, sstart) - sh;
-      sup = min(first_row_at_least(km, k0, sink_hi + 1) - 1 - k0, last) - 4 * hi;
-    }
-    auto visible = [&](int kb, int r) -> bool {
-      if constexpr (FULL) {
-        return true;
-      } else {
-        const int cc = kb * 32 + 8 * (r >> 2) + (r & 3);
-        return ((cc >= lo) & (cc <= up)) | ((cc >= slo) & (cc <= sup));
-      }
-    };
-    // fragment streams: A phase i -> (K or V row kb*32 + l32, chunk 2*(i/2)+hi);
-    // C phase j -> K^T block (kb, half, d)
-    auto read_a = [&](int i) {
-      const int kb = i / (2 * KS), w = i % (2 * KS);
-      return T::frag((w & 1) ? tV : tK, kb * 32 + l32, 2 * (w >> 1) + hi);
-    };
-    auto read_c = [&](int j) {
-      const int kb = j / (2 * DB), half = (j / DB) & 1, d = j % DB;
-      return frag_tr<D>(tK, kb, half, d, lane);
-    };
-    constexpr int NA = 2 * 2 * KS;   // A0 + A1 MFMAs
-    constexpr int NC = 2 * 2 * DB;   // C0 + C1 MFMAs
-    f32x16 st[2], dpt[2];
-    bf16x8 fa[NA], fc[NC];
-    bf16x8 dsb[2][2];
-    const f32x16 zero = {};
-#pragma unroll
-    for (int i = 0; i < PF; ++i) fa[i] = read_a(i);
-    // A0, A1 (B0 follows in program order; the groups below interleave it)
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      if (i + PF < NA) fa[i + PF] = read_a(i + PF);
-      else fc[i + PF - NA] = read_c(i + PF - NA);
-      const int kb = i / (2 * KS), w = i % (2 * KS), ks = w >> 1;
-      if (w & 1) dpt[kb] = mfma32(fa[i], dof[ks], ks == 0 ? zero : dpt[kb]);
-      else st[kb] = mfma32(fa[i], qf[ks], ks == 0 ? zero : st[kb]);
-    }
-    // Score modifiers of element r of key block kb (raw units, as the
-    // forward): softcap a - 2a rc with rc = 1 / (exp2(s b2) + 1), whose
-    // derivative factor 1 - tanh^2 = 4 rc (1 - rc) scales dS; then ALiBi.
-    float abase = 0.f, rb = 0.f;
-    if constexpr ((MODS & 2) != 0) {
-      abase = (float)(k0 + 4 * hi);
-      rb = k0 >= khalf ? rb1 : rb0;
-    }
-    auto mods = [&](int kb, int r, float& sv, float& f, float ab) {
-      if constexpr ((MODS & 1) != 0) {
-        const float rc = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(sv * p.mods.b2) + 1.f);
-        sv = p.mods.a - 2.f * p.mods.a * rc;
-        f = 4.f * rc * (1.f - rc);
-      }
-      if constexpr ((MODS & 2) != 0) {
-        // key index t (the constant is added first so that it folds into one
-        // instruction)
-        const float t = ab + (float)(kb * 32 + 8 * (r >> 2) + (r & 3));
-        const float dd = __builtin_floorf((t + 0.5f) * inv_b) * nb1 + (t + rb);
-        sv -= slope * __builtin_fabsf(dd);
-      }
-    };
-    auto softmax = [&](int kb) {
-      // The bias terms depend on nothing the MFMAs produce; the empty asm
-      // keeps the compiler from hoisting all of them into live registers
-      // ahead of the matrix products.
-      float ab = abase;
-      if constexpr ((MODS & 2) != 0) asm volatile("" : "+v"(ab));
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const int r0 = half * 8 + e, r1 = r0 + 1;
-          float s0 = st[kb][r0], s1 = st[kb][r1], f0 = 1.f, f1 = 1.f;
-          if constexpr (MODS != 0) {
-            mods(kb, r0, s0, f0, ab);
-            mods(kb, r1, s1, f1, ab);
-          }
-          float p0 = __builtin_amdgcn_exp2f(s0 * c - lse2);
-          float p1 = __builtin_amdgcn_exp2f(s1 * c - lse2);
-          if constexpr (!FULL) {
-            p0 = visible(kb, r0) ? p0 : 0.f;
-            p1 = visible(kb, r1) ? p1 : 0.f;
-          }
-          float d0 = p0 * (dpt[kb][r0] - dl);
-          float d1 = p1 * (dpt[kb][r1] - dl);
-          if constexpr ((MODS & 1) != 0) {
-            d0 *= f0;
-            d1 *= f1;
-          }
-          const bf16x2 pk2 = __builtin_convertvector((f32x2){d0, d1}, bf16x2);
-          dsb[kb][half][e] = pk2[0];
-          dsb[kb][half][e + 1] = pk2[1];
-        }
-      }
-    };
-    softmax(0);
-    softmax(1);
-    // C0, C1
-#pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      if (j + PF < NC) fc[j + PF] = read_c(j + PF);
-      const int kb = j / (2 * DB), half = (j / DB) & 1, d = j % DB;
-      dqt[d] = mfma32(fc[j], dsb[kb][half], dqt[d]);
-    }
-    // scheduling groups, in issue order: A0 (MFMA, read), A1 (MFMA, read,
-    // B0's VALU), C0 (MFMA, reads, B1's VALU), C1 (MFMA, reads); a frag_tr
-    // is two DS reads
-    constexpr int NA0 = 2 * KS;
-    constexpr int NC0 = 2 * DB;
-    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      sched_ds_read((i + PF < NA) ? 1 : 2);
-      if (i >= NA0) __builtin_amdgcn_sched_group_barrier(0x002, kDqValuA, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (j + PF < NC) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      if (j < NC0) __builtin_amdgcn_sched_group_barrier(0x002, kDqValuC, 0);
-    }
-  };
-
   int n_tiles = 0;
   for (int ri = it.run_begin; ri < it.run_end; ++ri) {
     const Run r = p.runs[ri];
     n_tiles += (r.k_end - r.k_begin + BN - 1) / BN;
   }
-  int c_ri = it.run_begin;
-  Run c_run = n_tiles > 0 ? p.runs[c_ri] : Run{0, 0, 0, 0};
-  int c_k0 = c_run.k_begin;
-  if (n_tiles > 0) dma(smem, c_k0, c_run.k_end);
-  for (int n = 0; n < n_tiles; ++n) {
-    const int k0 = c_k0;
-    const Run run = c_run;
-    const char* tK = smem + (n & 1) * 2 * TILEB;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile n are in LDS
-    __syncthreads();                     // every wave's copies landed; tile n - 1's buffer is free
-    if (n + 1 < n_tiles) {
-      c_k0 += BN;
-      if (c_k0 >= c_run.k_end) {
-        c_run = p.runs[++c_ri];
-        c_k0 = c_run.k_begin;
-      }
-      dma(smem + ((n + 1) & 1) * 2 * TILEB, c_k0, c_run.k_end);
-    }
-    if (run.full) tile(std::true_type{}, tK, k0, run.k_end);
-    else tile(std::false_type{}, tK, k0, run.k_end);
-  }
 
-  // dq[b, row, h, :] += scale * dQ (this lane: query qrow, head-dim rows of dQ^T)
-  if (!qvalid || it.run_begin == it.run_end) return;
-  float* op = p.dq + (int64_t)b * p.g_batch_stride + (qrow * p.Hq + h) * D;
-  const float sc = p.scale;
+  // Tile copy by this wave's group (K for the P waves, V for the dS waves):
+  // thread (wave wg, lane i) copies slices wg*LPT + j, physical (row, chunk
+  // slot) = (slice*RPI + i / CPR, i % CPR) = logical chunk slot ^ swz(row);
+  // rows past the run's end are clamped to its last row (masked in partial
+  // runs; full runs are multiples of BN keys).
+  auto dma = [&](char* buf, const Cursor& cu) {
 #pragma unroll
-  for (int d = 0; d < DB; ++d) {
+    for (int j = 0; j < LPT; ++j) {
+      const int row = (wg * LPT + j) * RPI + lrow;
+      const uint32_t off = (uint32_t)min(cu.k0 + row, cu.run.k_end - 1) * row_bytes + (uint32_t)((lslot ^ T::swz(row)) * 16);
+      copy16_to_lds(trs, lds_addr(buf + (wg * LPT + j) * 1024), off);
+    }
+  };
+
+  int tro[2][DB], rro[KS];
+  pp_offsets<D>(lane, tro, rro);
+  auto m_phase = [&](auto do_t_c, auto do_r_c, const char* tT, const char* tR) {
+    pp_matrix_phase<D, decltype(do_t_c)::value, decltype(do_r_c)::value>(acc, sc, bb, kv, tro, rro, tT, tR);
+  };
+
+  // P exchange slot of this wave pair: float4 j (block kb, key group g) of
+  // lane l at (j * 64 + l) * 16
+  float* const xw = reinterpret_cast<float*>(xbuf + wg * XB);
+
+  // Vector phase of the P wave: P^T of the tile at cu (S^T in sc); element
+  // r of key block kb is key k0 + du, du = kb*32 + 8*(r/4) + 4*hi + r%4.
+  // FULL: every pair visible; otherwise key positions increase through the
+  // run, so this lane's visible keys (window band, sinks) are at most two
+  // intervals of du, found once per tile.
+  auto softmax = [&](auto full_c, const Cursor& cu) {
+    constexpr bool FULL = decltype(full_c)::value;
+    const int k0 = cu.k0;
+    int32_t lo = 0, up = 0, slo = 0, sup = -1;
+    if constexpr (!FULL) {
+      const int32_t last = cu.run.k_end - 1 - k0;
+      const int32_t sh = k0 + 4 * hi;
+      const int32_t dpos = k0 >= khalf ? dpos1 : dpos0;
+      lo = (kstripe ? fs_lo : vis_lo + dpos) - sh;
+      up = min((kstripe ? fs_hi : vis_hi + 1 + dpos) - 1 - k0, last) - 4 * hi;
+      slo = (kstripe ? fs_slo : sstart + dpos) - sh;
+      sup = min((kstripe ? fs_shi : sink_hi + 1 + dpos) - 1 - k0, last) - 4 * hi;
+    }
+    // Score modifiers (raw units, as the forward): softcap a - 2a rc with
+    // rc = 1 / (exp2(s b2) + 1), whose derivative factor 1 - tanh^2 =
+    // 4 rc (1 - rc) scales dS (the exchange carries P times it); then ALiBi.
+    float ab = 0.f, rb = 0.f;
+    if constexpr ((MODS & 2) != 0) {
+      ab = (float)(k0 + 4 * hi);
+      rb = k0 >= khalf ? rb1 : rb0;
+    }
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int dd = d * 32 + 8 * g + 4 * hi;
-      float4 a = *reinterpret_cast<const float4*>(op + dd);
-      a.x += sc * dqt[d][4 * g];
-      a.y += sc * dqt[d][4 * g + 1];
-      a.z += sc * dqt[d][4 * g + 2];
-      a.w += sc * dqt[d][4 * g + 3];
-      *reinterpret_cast<float4*>(op + dd) = a;
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float pf[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          float sv = sc[kb][r], f = 1.f;
+          if constexpr ((MODS & 1) != 0) {
+            const float rc = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(sv * cap_b2) + 1.f);
+            sv = cap_a - cap_2a * rc;
+            f = 4.f * rc * (1.f - rc);
+          }
+          if constexpr ((MODS & 2) != 0) {
+            const float t = ab + (float)(kb * 32 + 8 * g + e);
+            const float dd = __builtin_floorf((t + 0.5f) * inv_b) * nb1 + (t + rb);
+            sv -= slope * __builtin_fabsf(dd);
+          }
+          float pe = __builtin_amdgcn_exp2f(sv * c - lse2);
+          if constexpr (!FULL) {
+            const int cc = kb * 32 + 8 * g + e;
+            pe = (((cc >= lo) & (cc <= up)) | ((cc >= slo) & (cc <= sup))) ? pe : 0.f;
+          }
+          pf[e] = ((MODS & 1) != 0) ? pe * f : pe;
+        }
+        *reinterpret_cast<float4*>(xw + ((kb * 4 + g) * 64 + lane) * 4) = make_float4(pf[0], pf[1], pf[2], pf[3]);
+      }
+      if constexpr (!FULL) __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Vector phase of the dS wave: dS^T = P^T (dP^T - delta), dP^T in sc.
+  auto form_ds = [&]() {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 px = *reinterpret_cast<const float4*>(xw + ((kb * 4 + g) * 64 + lane) * 4);
+        const float d0 = px.x * (sc[kb][4 * g] - dl);
+        const float d1 = px.y * (sc[kb][4 * g + 1] - dl);
+        const float d2 = px.z * (sc[kb][4 * g + 2] - dl);
+        const float d3 = px.w * (sc[kb][4 * g + 3] - dl);
+        const bf16x2 a01 = __builtin_convertvector((f32x2){d0, d1}, bf16x2);
+        const bf16x2 a23 = __builtin_convertvector((f32x2){d2, d3}, bf16x2);
+        const int half = g >> 1, e0 = (g & 1) * 4;
+        bb[kb][half][e0] = a01[0];
+        bb[kb][half][e0 + 1] = a01[1];
+        bb[kb][half][e0 + 2] = a23[0];
+        bb[kb][half][e0 + 3] = a23[1];
+      }
+    }
+  };
+
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  auto prio_hi = []() { __builtin_amdgcn_s_setprio(1); };
+  auto prio_lo = []() { __builtin_amdgcn_s_setprio(0); };
+  auto kb_at = [&](int n) { return kbuf + (n % 3) * TILEB; };
+  auto vb_at = [&](int n) { return vbuf + (n & 1) * TILEB; };
+
+  // The two roles run separate programs that pass the same barriers:
+  // prologue (tile 0 lands; the P waves compute S(0)), two phases per tile,
+  // and the dS waves' last dQ after the final barrier.  Each loop body holds
+  // one copy of its matrix phase and exits at the bottom, so the
+  // accumulators keep their registers across iterations.
+  if (grp == 0) {
+    Cursor cs = c0;  // tile of S / softmax
+    Cursor ck = c0;  // tile of the last K copy
+    dma(kb_at(0), ck);
+    if (n_tiles > 1) {
+      advance(ck);
+      dma(kb_at(1), ck);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    pp_barrier();
+    prio_hi();
+    m_phase(F_{}, T_{}, nullptr, kb_at(0));
+    prio_lo();
+    pp_barrier();
+    // phase 0: P of tile 0
+    if (cs.run.full) softmax(T_{}, cs);
+    else softmax(F_{}, cs);
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): the exchange writes, K(1)
+    pp_barrier();
+    for (int n = 0; n + 1 < n_tiles; ++n) {
+      // phase 2n+1: S(n+1)
+      prio_hi();
+      m_phase(F_{}, T_{}, nullptr, kb_at(n + 1));
+      prio_lo();
+      if (n + 2 < n_tiles) {
+        advance(ck);
+        dma(kb_at(n + 2), ck);
+      }
+      advance(cs);
+      pp_barrier();
+      // phase 2n+2: P of tile n+1
+      if (cs.run.full) softmax(T_{}, cs);
+      else softmax(F_{}, cs);
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): the exchange writes, K(n+2)
+      pp_barrier();
+    }
+    // phase 2N-1: the dS waves form dS(N-1)
+    pp_barrier();
+  } else {
+    Cursor cv = c0;  // tile of the last V copy
+    dma(vb_at(0), cv);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    pp_barrier();
+    pp_barrier();
+    // phase 0: dP(0)
+    prio_hi();
+    m_phase(F_{}, T_{}, nullptr, vb_at(0));
+    prio_lo();
+    if (n_tiles > 1) {
+      advance(cv);
+      dma(vb_at(1), cv);
+    }
+    pp_barrier();
+    // phase 1: dS(0)
+    form_ds();
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): V(1) landed
+    pp_barrier();
+    for (int n = 0; n + 1 < n_tiles; ++n) {
+      // phase 2n+2: dQ(n), dP(n+1)
+      prio_hi();
+      m_phase(T_{}, T_{}, kb_at(n), vb_at(n + 1));
+      prio_lo();
+      if (n + 2 < n_tiles) {
+        advance(cv);
+        dma(vb_at(n + 2), cv);
+      }
+      pp_barrier();
+      // phase 2n+3: dS(n+1)
+      form_ds();
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): V(n+2) landed
+      pp_barrier();
+    }
+    // phase 2N: dQ(N-1)
+    prio_hi();
+    m_phase(T_{}, F_{}, kb_at(n_tiles - 1), nullptr);
+    prio_lo();
+
+    // dq[b, row, h, :] += scale * dQ (this lane: query qrow, head-dim rows of dQ^T)
+    if (!qvalid) return;
+    float* op = p.dq + (int64_t)b * p.g_batch_stride + (qrow * p.Hq + h) * D;
+    const float w = p.scale;
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dd = d * 32 + 8 * g + 4 * hi;
+        float4 a = *reinterpret_cast<const float4*>(op + dd);
+        a.x += w * acc[d][4 * g];
+        a.y += w * acc[d][4 * g + 1];
+        a.z += w * acc[d][4 * g + 2];
+        a.w += w * acc[d][4 * g + 3];
+        *reinterpret_cast<float4*>(op + dd) = a;
+      }
     }
   }
 }
@@ -329,7 +392,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const BwdParams p) {
 void launch_bwd_dq(const BwdParams& p, int D, unsigned grid, hipStream_t stream) {
   TimingScope ts(K_BWD_DQ, stream);
   const int mods = mods_variant(p.mods);
-#define USP_LAUNCH_Q(DD, M) hipLaunchKernelGGL((bwd_dq_kernel<DD, M>), dim3(grid), dim3(256), 0, stream, p)
+#define USP_LAUNCH_Q(DD, M) hipLaunchKernelGGL((bwd_dq_kernel<DD, M>), dim3(grid), dim3(512), 0, stream, p)
 #define USP_LAUNCH_Q_M(DD)                  \
   switch (mods) {                           \
     case 0: USP_LAUNCH_Q(DD, 0); break;     \

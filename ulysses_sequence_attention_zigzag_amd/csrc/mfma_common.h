@@ -170,5 +170,116 @@ __device__ __forceinline__ bf16x8 frag_tr(const char* t, int kb, int half, int d
   return bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
 }
 
+
+// ---------------------------------------------------------------- ping-pong
+// Helpers of the 8-wave backward kernels, whose waves work on 64-row tiles
+// (two 32-row blocks) of a staged operand with one lane per row of their
+// own 32-row slice.
+
+// Per-lane LDS byte offsets of the fragments of a 64-row SwzTile.  The
+// swizzle of a row depends on its low 4 bits only, which the 16-row steps of
+// the blocks leave alone, so one offset per (row, chunk) of block 0 serves
+// all blocks (their distance is an immediate).  Transposed reads (as
+// frag_tr): rows trow and trow + 8 of each 16-row half, chunk 4d + tchunk,
+// 8-byte half (lane & 1).  Row reads: row lane % 32, chunk 2ks + lane / 32.
+template <int D>
+__device__ __forceinline__ void pp_offsets(int lane, int (&tro)[2][D / 32], int (&rro)[D / 16]) {
+  using T = SwzTile<D>;
+  const int hi = lane >> 5, l32 = lane & 31;
+  const int trow = 4 * hi + ((lane & 15) >> 2);
+  const int tchunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int d = 0; d < D / 32; ++d) {
+      const int r = trow + 8 * x;
+      tro[x][d] = r * T::ROWB + (((4 * d + tchunk) ^ T::swz(r)) * 16) + (lane & 1) * 8;
+    }
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) rro[ks] = l32 * T::ROWB + (((2 * ks + hi) ^ T::swz(l32)) * 16);
+}
+
+// Matrix phase: the transposed-operand products acc[d] += X^T bb (X the
+// 64-row tile at tT; 2 blocks x 2 halves x D/32 MFMAs) if DT, then the
+// row-operand products sc[blk] = Y kv (Y the tile at tR; 2 blocks x D/16
+// MFMAs, the two blocks alternating) if DR.  Fragments are read kPF MFMAs
+// ahead, across the boundary, in an order pinned with scheduling groups.
+template <int D, bool DT, bool DR>
+__device__ __forceinline__ void pp_matrix_phase(f32x16 (&acc)[D / 32], f32x16 (&sc)[2], const bf16x8 (&bb)[2][2],
+                                                const bf16x8 (&kv)[D / 16], const int (&tro)[2][D / 32],
+                                                const int (&rro)[D / 16], const char* tT, const char* tR) {
+  using T = SwzTile<D>;
+  constexpr int KS = D / 16, DB = D / 32;
+  constexpr int NT = 2 * 2 * DB;
+  constexpr int NR = 2 * KS;
+  constexpr int PF = kPF;
+  static_assert(PF <= NT && PF <= NR, "prefetch depth");
+  auto rd_t = [&](int j) {
+    const int blk = j / (2 * DB), half = (j / DB) & 1, d = j % DB;
+    const char* base = tT + (blk * 32 + half * 16) * T::ROWB;
+    const bf16x4 a0 = lds_read_tr(base + tro[0][d]);
+    const bf16x4 a1 = lds_read_tr(base + tro[1][d]);
+    return bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+  };
+  auto rd_r = [&](int i) {
+    const int ks = i >> 1, blk = i & 1;
+    return *reinterpret_cast<const bf16x8*>(tR + blk * 32 * T::ROWB + rro[ks]);
+  };
+  bf16x8 ft[NT], fr[NR];
+  if constexpr (DT) {
+#pragma unroll
+    for (int j = 0; j < PF; ++j) ft[j] = rd_t(j);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      if (j + PF < NT) ft[j + PF] = rd_t(j + PF);
+      else if (DR) fr[j + PF - NT] = rd_r(j + PF - NT);
+      const int blk = j / (2 * DB), half = (j / DB) & 1, d = j % DB;
+      acc[d] = mfma32(ft[j], bb[blk][half], acc[d]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) fr[i] = rd_r(i);
+  }
+  if constexpr (DR) {
+    const f32x16 zero = {};
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      if (i + PF < NR) fr[i + PF] = rd_r(i + PF);
+      const int ks = i >> 1, blk = i & 1;
+      sc[blk] = mfma32(fr[i], kv[ks], ks == 0 ? zero : sc[blk]);
+    }
+  }
+  // scheduling groups, in issue order (a transposed fragment is 2 reads)
+  if constexpr (DT) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
+#pragma unroll
+    for (int j = 0; j < NT - PF; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if constexpr (DR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  } else {
+    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+  }
+  if constexpr (DR) {
+#pragma unroll
+    for (int i = 0; i < NR - PF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < PF; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  }
+}
+
+// Workgroup barrier of the phase programs: no memory fence (each wave waits
+// for its own LDS writes and tile copies explicitly before it), only a
+// compiler ordering point.
+__device__ __forceinline__ void pp_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 }  // namespace
 }  // namespace usp

@@ -89,8 +89,8 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const void* out, int out
 // tile n (Q, dO, LSE, delta), with S = Q K^T and dP = dO V^T in the C layout
 // of the forward kernel (lane = key, 16 query rows per 32-row block):
 //   P wave:  S(n)                  [matrix]
-//            P = exp2(S c - LSE log2 e) -> LDS exchange (f32, times the
-//            softcap derivative), bf16 P for dV   [vector]
+//            P = exp2(S c - LSE log2 e) -> bf16 P for dV, and to the LDS
+//            exchange (times the softcap derivative)   [vector]
 //            dV^T += dO^T P         [matrix]
 //   dS wave: dP(n)                 [matrix]
 //            dS = P (dP - delta) from the exchange   [vector]
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
   constexpr int LPT = TILEB / 4096;         // 16-byte copies per thread of a 4-wave group
   constexpr int RPI = 1024 / T::ROWB;
   constexpr int OBUFB = TILEB + 2 * BQ * 4; // dO, LSE, delta
-  constexpr int XB = BQ * 32 * 4;           // P exchange of one wave pair (f32)
+  constexpr int XB = BQ * 32 * 2;           // P exchange of one wave pair (bf16)
   static_assert(TILEB % 4096 == 0 && OBUFB % 512 == 0, "tile layout");
   __shared__ __attribute__((aligned(1024))) char smem[3 * TILEB + 2 * OBUFB + 4 * XB];
   char* const qbuf = smem;
@@ -279,9 +279,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
     pp_matrix_phase<D, decltype(do_t_c)::value, decltype(do_r_c)::value>(acc, sc, bb, kv, tro, rro, tT, tR);
   };
 
-  // P exchange slot of this wave pair: float4 j (block qb, row group g) of
-  // lane l at (j * 64 + l) * 16
-  float* const xw = reinterpret_cast<float*>(xbuf + wg * XB);
+  // P exchange slot of this wave pair: the 8 bf16 of (block qb, half) of
+  // lane l at ((qb * 2 + half) * 64 + l) * 16, in the B-operand order
+  char* const xw = xbuf + wg * XB;
 
   // Vector phase of the P wave: P of tile `cur` (S in sc), element r of
   // block qb is local row t0 + qb*32 + 8*(r/4) + 4*hi + r%4 of head gi.
@@ -305,6 +305,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
       ab = (float)(t0 + 4 * hi);
       rb = t0 >= qhalf ? rb1 : rb0;
     }
+    bf16x8 xf[2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
@@ -334,7 +335,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
           px[e] = pe;
           pf[e] = ((MODS & 1) != 0) ? pe * f : pe;
         }
-        *reinterpret_cast<float4*>(xw + ((qb * 4 + g) * 64 + lane) * 4) = make_float4(pf[0], pf[1], pf[2], pf[3]);
         const bf16x2 p01 = __builtin_convertvector((f32x2){px[0], px[1]}, bf16x2);
         const bf16x2 p23 = __builtin_convertvector((f32x2){px[2], px[3]}, bf16x2);
         const int half = g >> 1, e0 = (g & 1) * 4;
@@ -342,7 +342,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
         bb[qb][half][e0 + 1] = p01[1];
         bb[qb][half][e0 + 2] = p23[0];
         bb[qb][half][e0 + 3] = p23[1];
+        if constexpr ((MODS & 1) != 0) {
+          const bf16x2 f01 = __builtin_convertvector((f32x2){pf[0], pf[1]}, bf16x2);
+          const bf16x2 f23 = __builtin_convertvector((f32x2){pf[2], pf[3]}, bf16x2);
+          xf[qb][half][e0] = f01[0];
+          xf[qb][half][e0 + 1] = f01[1];
+          xf[qb][half][e0 + 2] = f23[0];
+          xf[qb][half][e0 + 3] = f23[1];
+        }
       }
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+        *reinterpret_cast<bf16x8*>(xw + ((qb * 2 + half) * 64 + lane) * 16) =
+            ((MODS & 1) != 0) ? xf[qb][half] : bb[qb][half];
       if constexpr (!FULL) __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -351,9 +363,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
     const float* sd = reinterpret_cast<const float*>(ob + TILEB + BQ * 4);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
+      const bf16x8 xh[2] = {*reinterpret_cast<const bf16x8*>(xw + (qb * 2 * 64 + lane) * 16),
+                            *reinterpret_cast<const bf16x8*>(xw + ((qb * 2 + 1) * 64 + lane) * 16)};
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const float4 px = *reinterpret_cast<const float4*>(xw + ((qb * 4 + g) * 64 + lane) * 4);
+        const int hh = g >> 1, o = (g & 1) * 4;
+        const float4 px = make_float4((float)xh[hh][o], (float)xh[hh][o + 1], (float)xh[hh][o + 2], (float)xh[hh][o + 3]);
         const float4 d4 = *reinterpret_cast<const float4*>(sd + qb * 32 + 8 * g + 4 * hi);
         const float d0 = px.x * (sc[qb][4 * g] - d4.x);
         const float d1 = px.y * (sc[qb][4 * g + 1] - d4.y);

@@ -15,8 +15,8 @@ namespace {
 // S^T = K Q^T and dP^T = V dO^T in the C layout (lane = query, 16 keys per
 // 32-key block):
 //   P wave:  S^T(n)                 [matrix]
-//            P^T = exp2(S^T c - LSE log2 e) -> LDS exchange (f32, times the
-//            softcap derivative)    [vector]
+//            P^T = exp2(S^T c - LSE log2 e) -> LDS exchange (bf16, times
+//            the softcap derivative)    [vector]
 //   dS wave: dP^T(n)                [matrix]
 //            dS^T = P^T (dP^T - delta) from the exchange   [vector]
 //            dQ^T += K^T dS^T       [matrix]
@@ -34,7 +34,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
   constexpr int TILEB = BN * D * 2;
   constexpr int LPT = TILEB / 4096;        // 16-byte copies per thread of a 4-wave group
   constexpr int RPI = 1024 / T::ROWB;
-  constexpr int XB = BN * 32 * 4;          // P exchange of one wave pair (f32)
+  constexpr int XB = BN * 32 * 2;          // P exchange of one wave pair (bf16)
   static_assert(kTileN % BN == 0, "planner granularity");
   static_assert(TILEB % 4096 == 0, "tile layout");
   __shared__ __attribute__((aligned(1024))) char smem[3 * TILEB + 2 * TILEB + 4 * XB];
@@ -195,9 +195,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
     pp_matrix_phase<D, decltype(do_t_c)::value, decltype(do_r_c)::value>(acc, sc, bb, kv, tro, rro, tT, tR);
   };
 
-  // P exchange slot of this wave pair: float4 j (block kb, key group g) of
-  // lane l at (j * 64 + l) * 16
-  float* const xw = reinterpret_cast<float*>(xbuf + wg * XB);
+  // P exchange slot of this wave pair: the 8 bf16 of (block kb, half) of
+  // lane l at ((kb * 2 + half) * 64 + l) * 16, in the B-operand order
+  char* const xw = xbuf + wg * XB;
 
   // Vector phase of the P wave: P^T of the tile at cu (S^T in sc); element
   // r of key block kb is key k0 + du, du = kb*32 + 8*(r/4) + 4*hi + r%4.
@@ -225,6 +225,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
       ab = (float)(k0 + 4 * hi);
       rb = k0 >= khalf ? rb1 : rb0;
     }
+    bf16x8 xq[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -251,8 +252,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
           }
           pf[e] = ((MODS & 1) != 0) ? pe * f : pe;
         }
-        *reinterpret_cast<float4*>(xw + ((kb * 4 + g) * 64 + lane) * 4) = make_float4(pf[0], pf[1], pf[2], pf[3]);
+        const bf16x2 p01 = __builtin_convertvector((f32x2){pf[0], pf[1]}, bf16x2);
+        const bf16x2 p23 = __builtin_convertvector((f32x2){pf[2], pf[3]}, bf16x2);
+        const int half = g >> 1, e0 = (g & 1) * 4;
+        xq[kb][half][e0] = p01[0];
+        xq[kb][half][e0 + 1] = p01[1];
+        xq[kb][half][e0 + 2] = p23[0];
+        xq[kb][half][e0 + 3] = p23[1];
       }
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+        *reinterpret_cast<bf16x8*>(xw + ((kb * 2 + half) * 64 + lane) * 16) = xq[kb][half];
       if constexpr (!FULL) __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -260,9 +270,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
   auto form_ds = [&]() {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 xh[2] = {*reinterpret_cast<const bf16x8*>(xw + (kb * 2 * 64 + lane) * 16),
+                            *reinterpret_cast<const bf16x8*>(xw + ((kb * 2 + 1) * 64 + lane) * 16)};
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const float4 px = *reinterpret_cast<const float4*>(xw + ((kb * 4 + g) * 64 + lane) * 4);
+        const int hh = g >> 1, o = (g & 1) * 4;
+        const float4 px = make_float4((float)xh[hh][o], (float)xh[hh][o + 1], (float)xh[hh][o + 2], (float)xh[hh][o + 3]);
         const float d0 = px.x * (sc[kb][4 * g] - dl);
         const float d1 = px.y * (sc[kb][4 * g + 1] - dl);
         const float d2 = px.z * (sc[kb][4 * g + 2] - dl);

@@ -38,18 +38,21 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0       # HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_traffic.txt")
+TRAFFIC_FILES = {
+    "fwd": os.path.join(ROOT, "profiles", "attn_fwd_traffic.txt"),   # attn_fwd_kernel
+    "bwd": os.path.join(ROOT, "profiles", "attn_bwd_traffic.txt"),   # bwd_dkdv_kernel
+}
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per attention launch from the committed counter record
-    (FETCH_SIZE / WRITE_SIZE scaled by the copy-kernel calibration), or None
-    when there is no record for the workload or the kernel source changed
+def measured_traffic(workload: str, kind: str = "fwd"):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    record (FETCH_SIZE / WRITE_SIZE scaled by the copy-kernel calibration), or
+    None when there is no record for the workload or the kernel source changed
     since the counters were taken."""
     import hashlib
     try:
         kv = {}
-        for line in open(TRAFFIC_FILE):
+        for line in open(TRAFFIC_FILES[kind]):
             line = line.strip()
             if line and not line.startswith("#") and "=" in line:
                 key, val = line.split("=", 1)
@@ -660,7 +663,8 @@ def bench_backward(args, w, q, k, v, qd, kd, vd):
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(ach / PEAK_BF16_TFLOPS, 4) if ach else None,
-            "traffic": None,
+            "traffic": measured_traffic(w.name, "bwd") if dom.startswith("bwd_dkdv") else None,
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "kernel": dom,
             "launches_per_step": kernels[dom]["launches_per_step"],
             "kernel_ms_per_step": kernels[dom]["ms_per_step"],

@@ -173,6 +173,20 @@ def time_lse_merge(w, merge_mode: int, merge_timing) -> dict:
     return rec
 
 
+def oracle_threads() -> int:
+    """Gives the oracle every CPU this process may run on (the machine's
+    logical CPUs unless an affinity mask narrows them) and returns that
+    count."""
+    import torch
+
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    torch.set_num_threads(max(1, n))
+    return torch.get_num_threads()
+
+
 def host_info() -> dict:
     """The host the oracle runs on: the threads torch uses (the process's CPU
     share, set through OMP_NUM_THREADS), the machine's logical CPU count, the
@@ -213,7 +227,7 @@ def cpu_baseline(w, q, k, v, budget_s: float):
     from oracle import index_ref as ix
     from oracle.attention_ref import attention_ref
 
-    threads = torch.get_num_threads()
+    threads = oracle_threads()
     if w.rank >= 0:
         pos = ix.rank_positions(w.impl, w.S, w.ring_degree, w.rank, w.stripe_block)
         Hl = w.Hq // w.ulysses_degree
@@ -282,7 +296,7 @@ def cpu_baseline_bwd(w, q, k, v, dout, budget_s: float):
     from oracle.attention_ref import attention_ref
     from oracle.backward_ref import block_attention_bwd_ref
 
-    threads = torch.get_num_threads()
+    threads = oracle_threads()
     varlen = w.cu_seqlens is not None
     qb, kb, vb = (t.unsqueeze(0) if varlen else t for t in (q, k, v))
     db = dout.unsqueeze(0) if varlen else dout
@@ -693,7 +707,7 @@ def cpu_baseline_decode(cfg, q, k, v, budget_s: float):
     import torch
     from oracle.decode_ref import decode_ref
 
-    threads = torch.get_num_threads()
+    threads = oracle_threads()
     B, Hkv, group = cfg["B"], cfg["Hkv"], cfg["Hq"] // cfg["Hkv"]
     done, t_used, nbytes = 0, 0.0, 0
     units = [(b, g) for b in range(B) for g in range(Hkv)]

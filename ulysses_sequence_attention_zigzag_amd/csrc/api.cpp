@@ -340,7 +340,7 @@ usp_status usp_plan_block(int64_t Lq, int64_t Lk, int64_t D, usp_mask_class mask
   usp_status st = setup_block_mask(Lq, Lk, mask, qmap, kmap, causal, window, n_sink, cu_seqlens_host,
                                    nseq, 1, &su);
   if (st != USP_OK) return st;
-  const int32_t tm = choose_tile_m(su.qmap);
+  const int32_t tm = choose_tile_m(su.ms.window);
   Plan plan;
   if (Lq > 0) {
     PlanJob J = block_job(su, 0, tm, kTileN, accumulate ? 0 : INT_MAX);
@@ -414,7 +414,7 @@ usp_status usp_plan_block_device(int64_t Lq, int64_t Lk, usp_mask_class mask, co
                                    nseq, 1, &su);
   if (st != USP_OK) return st;
   PlanJob J = kv_tiles ? block_job(su, 1, kBwdTileK, kBwdTileQ, 0)
-                       : block_job(su, 0, choose_tile_m(su.qmap), kTileN, accumulate ? 0 : INT_MAX);
+                       : block_job(su, 0, choose_tile_m(su.ms.window), kTileN, accumulate ? 0 : INT_MAX);
   st = finish_job(J, cu_seqlens_host);
   if (st != USP_OK) return st;
   size_t need = 0;
@@ -440,7 +440,7 @@ size_t usp_block_attn_fwd_workspace_size(int64_t Lq, int64_t Lk, usp_mask_class 
   BlockMaskSetup su;
   if (setup_block_mask(Lq, Lk, mask, qmap, kmap, causal, window, n_sink, cu_seqlens_host, nseq, 1, &su) != USP_OK)
     return 0;
-  PlanJob J = block_job(su, 0, choose_tile_m(su.qmap), kTileN, 0);
+  PlanJob J = block_job(su, 0, choose_tile_m(su.ms.window), kTileN, 0);
   if (finish_job(J, cu_seqlens_host) != USP_OK) return 0;
   size_t off = 0;
   reserve_job(J, off);
@@ -478,7 +478,7 @@ usp_status usp_block_attn_fwd(const void* q, const void* k, const void* v, void*
   if (st != USP_OK) return st;
   if (Lq == 0) return USP_OK;
 
-  const int32_t tm = choose_tile_m(su.qmap);
+  const int32_t tm = choose_tile_m(su.ms.window);
   PlanJob J = block_job(su, 0, tm, kTileN, accumulate ? 0 : INT_MAX);
   st = finish_job(J, cu_seqlens_host);
   if (st != USP_OK) return st;
@@ -869,7 +869,7 @@ usp_status ring_layout(const usp_ring_args* a, RingLayout* out) {
     r.off_opart = take(B * (size_t)r.q_rows * r.Hq_l * D * 4);
     r.off_lpart = take(B * (size_t)r.Hq_l * r.q_rows * 4);
   }
-  r.job = ring_job(a, 0, choose_tile_m(ring_base_map(a)), kTileN, a->merge_mode == 0 ? 1 : INT_MAX);
+  r.job = ring_job(a, 0, choose_tile_m(a->window), kTileN, a->merge_mode == 0 ? 1 : INT_MAX);
   usp_status st = finish_job(r.job, a->cu_seqlens_host);
   if (st != USP_OK) return st;
   r.slots = reserve_job(r.job, off);

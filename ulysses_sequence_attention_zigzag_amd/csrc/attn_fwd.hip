@@ -107,11 +107,20 @@ struct TileLayout {
 // reading, and waits for them at the end of its V(t), before the barrier
 // that hands the phase over.  Phase barriers carry no memory fence: every
 // LDS read of a matrix phase is consumed by its MFMAs before the phase ends.
-template <int D, int MODS, bool WIN>
-__global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
+//
+// Window masks (WIN) make short work items: a query tile sees a band of a few
+// key tiles, and the item's fixed costs (loading q, the first tile, reading
+// and writing the f32 accumulator) take half of its time.  Those launches run
+// the 4-wave form (W4): 128-row items, 64-key tiles at D = 128 (64 KB of
+// LDS), so that two workgroups share a CU and one's prologue and epilogue
+// overlap the other's tiles.  Its waves stage K and V together and run
+// M(t), V(t) in turn, with a barrier before each tile copy (all waves are
+// done with the buffer) and after each V(t) (the copy landed).
+template <int D, int MODS, bool WIN, bool W4>
+__global__ __launch_bounds__(W4 ? 256 : 512, 2) void attn_fwd_kernel(const AttnParams p) {
   using TL = TileLayout<D>;
   // Keys per tile; the planner's full runs come in multiples of kTileN.
-  constexpr int BN = 128;
+  constexpr int BN = (W4 && D == 128) ? 64 : 128;
   static_assert(kTileN % BN == 0, "planner granularity");
   constexpr int KS = D / 16;        // k-steps of the QK^T contraction
   constexpr int DB = D / 32;        // 32-wide blocks of the output's head dim
@@ -125,7 +134,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wid >> 2;
+  const int grp = W4 ? 0 : wid >> 2;
   const int wg = wid & 3;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
@@ -225,13 +234,26 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(grp ? vbase : kbase), (short)0, 0x7fffffff, kBufferRsrcWord3);
   char* const stage_tiles = smem + grp * 2 * TILEB;
-  auto dma_tile = [&](char* tile, int k0, int kend) {
+  // one tile (V when is_v) into `tile`
+  auto dma_one = [&](const __amdgpu_buffer_rsrc_t& rs, bool is_v, char* tile, int k0, int kend) {
 #pragma unroll
     for (int j = 0; j < LPT; ++j) {
       const int row = (wg * LPT + j) * RPI + lrow;
-      const int sw = grp ? TL::swz_v(row) : TL::swz_k(row);
+      const int sw = is_v ? TL::swz_v(row) : TL::swz_k(row);
       const uint32_t off = (uint32_t)min(k0 + row, kend - 1) * row_bytes + (uint32_t)((lslot ^ sw) * 16);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (__attribute__((address_space(3))) void*)(tile + (wg * LPT + j) * 1024), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(tile + (wg * LPT + j) * 1024), 16, off, 0, 0, 0);
+    }
+  };
+  // this group's tile (8 waves: K for group 0, V for group 1), or both (W4:
+  // K into `tile`, V two tiles further)
+  auto dma_tile = [&](char* tile, int k0, int kend) {
+    if constexpr (W4) {
+      const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, 0x7fffffff,
+                                                                           kBufferRsrcWord3);
+      dma_one(srs, false, tile, k0, kend);
+      dma_one(vrs, true, tile + 2 * TILEB, k0, kend);
+    } else {
+      dma_one(srs, grp != 0, tile, k0, kend);
     }
   };
 
@@ -455,6 +477,27 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
     n_tiles += (rr.k_end - rr.k_begin + BN - 1) / BN;
   }
 
+  // W4, accumulating into an f32 result: the previous partial of this lane's
+  // row is loaded before the last matrix phase, which then covers part of
+  // the load's latency (the epilogue is a third of a window item's time).
+  float4 oprev[W4 ? DB : 1][4];
+  float la_pre = 0.f;
+  bool have_pre = false;
+  auto load_prev = [&]() {
+    if constexpr (W4) {
+      if (p.accumulate && p.out_f32 && qvalid) {
+        la_pre = p.lse[((int64_t)b * p.o_heads + p.o_head0 + h) * p.Lq_buf + qrow];
+        const float* op = static_cast<const float*>(p.out) + (int64_t)b * p.o_batch_stride +
+                          (qrow * p.o_heads + p.o_head0 + h) * D;
+#pragma unroll
+        for (int d = 0; d < DB; ++d)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) oprev[d][g] = *reinterpret_cast<const float4*>(op + d * 32 + 8 * g + 4 * hi);
+        have_pre = true;
+      }
+    }
+  };
+
   if (n_tiles > 0) {
     // This wave's tile cursor (tile t of its current step).
     int ri = it.run_begin;
@@ -544,31 +587,57 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
     // faster on both large shares.
     auto prio_hi = []() { __builtin_amdgcn_s_setprio(1); };
     auto prio_lo = []() { __builtin_amdgcn_s_setprio(0); };
-    // Group 1 starts one phase late (group 0 runs M(0) meanwhile) and group
-    // 0 ends one phase early, so both pass the same number of barriers.
-    if (grp == 1) phase_barrier();
-    if (n_tiles > 1) prefetch_next();
-    prio_hi();
-    m_phase(F_{}, T_{}, nullptr, smem, s, pb);
-    prio_lo();
-    if (n_tiles > 1) dma_tile(stage_tiles + TILEB, nk0, nrun.k_end);
-    phase_barrier();
-    v_phase(0);
-    phase_barrier();
-    for (int t = 1; t < n_tiles; ++t) {
-      if (t + 1 < n_tiles) prefetch_next();
+    if constexpr (W4) {
+      // M(t) then V(t) in every wave; tile t+1 is copied into the buffers of
+      // tile t-1 once every wave has finished M(t) (its last reads of them).
+      if (n_tiles > 1) prefetch_next();
       prio_hi();
-      m_phase(T_{}, T_{}, smem + (2 + ((t - 1) & 1)) * TILEB, smem + (t & 1) * TILEB, s, pb);
+      m_phase(F_{}, T_{}, nullptr, smem, s, pb);
       prio_lo();
-      if (t + 1 < n_tiles) dma_tile(stage_tiles + ((t + 1) & 1) * TILEB, nk0, nrun.k_end);
+      if (n_tiles > 1) dma_tile(smem + TILEB, nk0, nrun.k_end);
+      v_phase(0);
       phase_barrier();
-      v_phase(t);
+      for (int t = 1; t < n_tiles; ++t) {
+        if (t + 1 < n_tiles) prefetch_next();
+        prio_hi();
+        m_phase(T_{}, T_{}, smem + (2 + ((t - 1) & 1)) * TILEB, smem + (t & 1) * TILEB, s, pb);
+        prio_lo();
+        phase_barrier();
+        if (t + 1 < n_tiles) dma_tile(smem + ((t + 1) & 1) * TILEB, nk0, nrun.k_end);
+        v_phase(t);
+        phase_barrier();
+      }
+      load_prev();
+      prio_hi();
+      m_phase(T_{}, F_{}, smem + (2 + ((n_tiles - 1) & 1)) * TILEB, nullptr, s, pb);
+      prio_lo();
+    } else {
+      // Group 1 starts one phase late (group 0 runs M(0) meanwhile) and group
+      // 0 ends one phase early, so both pass the same number of barriers.
+      if (grp == 1) phase_barrier();
+      if (n_tiles > 1) prefetch_next();
+      prio_hi();
+      m_phase(F_{}, T_{}, nullptr, smem, s, pb);
+      prio_lo();
+      if (n_tiles > 1) dma_tile(stage_tiles + TILEB, nk0, nrun.k_end);
       phase_barrier();
+      v_phase(0);
+      phase_barrier();
+      for (int t = 1; t < n_tiles; ++t) {
+        if (t + 1 < n_tiles) prefetch_next();
+        prio_hi();
+        m_phase(T_{}, T_{}, smem + (2 + ((t - 1) & 1)) * TILEB, smem + (t & 1) * TILEB, s, pb);
+        prio_lo();
+        if (t + 1 < n_tiles) dma_tile(stage_tiles + ((t + 1) & 1) * TILEB, nk0, nrun.k_end);
+        phase_barrier();
+        v_phase(t);
+        phase_barrier();
+      }
+      prio_hi();
+      m_phase(T_{}, F_{}, smem + (2 + ((n_tiles - 1) & 1)) * TILEB, nullptr, s, pb);
+      prio_lo();
+      if (grp == 0) phase_barrier();
     }
-    prio_hi();
-    m_phase(T_{}, F_{}, smem + (2 + ((n_tiles - 1) & 1)) * TILEB, nullptr, s, pb);
-    prio_lo();
-    if (grp == 0) phase_barrier();
   }
 
   // epilogue: O = O_acc / l, LSE = m ln 2 + ln l; or merge into (out, lse)
@@ -582,7 +651,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
   float wa = 0.f, wb = ltot > 0.f ? 1.f / ltot : 0.f;
   float lse_out = lse_new;
   if (p.accumulate) {
-    const float la = *lse_ptr;
+    const float la = have_pre ? la_pre : *lse_ptr;
     const float M = fmaxf(la, lse_new);
     if (lse_new == -INFINITY || M == -INFINITY) return;  // nothing to merge
     const float Lm = M + logf(expf(la - M) + expf(lse_new - M));
@@ -599,7 +668,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(const AttnParams p) {
         const int dd = d * 32 + 8 * g + 4 * hi;
         float4 v = make_float4(o[d][4 * g] * wb, o[d][4 * g + 1] * wb, o[d][4 * g + 2] * wb, o[d][4 * g + 3] * wb);
         if (wa != 0.f) {
-          const float4 a = *reinterpret_cast<const float4*>(op + dd);
+          const float4 a = have_pre ? oprev[d][g] : *reinterpret_cast<const float4*>(op + dd);
           v.x += wa * a.x;
           v.y += wa * a.y;
           v.z += wa * a.z;
@@ -634,15 +703,15 @@ usp_status launch_attn_fwd(const AttnParams& p, int D, hipStream_t stream) {
     set_error("attention grid too large (%lld workgroups)", (long long)total);
     return USP_ERR_UNSUPPORTED;
   }
-  if (p.tile_m != 256) {
+  const bool win = p.mask.window > 0;
+  if (p.tile_m != (win ? 128 : 256)) {
     set_error("internal: unsupported query tile %d", p.tile_m);
     return USP_ERR_UNSUPPORTED;
   }
-  const dim3 grid((unsigned)total), block(512);
+  const dim3 grid((unsigned)total), block(win ? 256 : 512);
   TimingScope ts(K_ATTN, stream);
   const int mods = mods_variant(p.mods);
-  const bool win = p.mask.window > 0;
-#define USP_LAUNCH(DD, M, W) hipLaunchKernelGGL((attn_fwd_kernel<DD, M, W>), grid, block, 0, stream, p)
+#define USP_LAUNCH(DD, M, W) hipLaunchKernelGGL((attn_fwd_kernel<DD, M, W, W>), grid, block, 0, stream, p)
 #define USP_LAUNCH_M(DD, W)                     \
   switch (mods) {                                \
     case 0: USP_LAUNCH(DD, 0, W); break;         \

@@ -125,11 +125,10 @@ static_assert(sizeof(Run) == 16, "Run layout");
 // query rows per workgroup, 8 waves of 32 rows).
 constexpr int kTileN = 128;
 
-// Query rows per workgroup for a rank whose rows are `qmap`.
-inline int32_t choose_tile_m(const PosMap& qmap) {
-  (void)qmap;
-  return 256;
-}
+// Query rows per forward workgroup: 256 (8 waves), or 128 (4 waves, two
+// workgroups per CU) under a window mask, whose short items are dominated by
+// per-item fixed costs that a second resident workgroup overlaps.
+inline int32_t choose_tile_m(int32_t window) { return window > 0 ? 128 : 256; }
 
 // Host-built plan of one launch (the inspection calls return it).
 struct Plan {

@@ -69,6 +69,7 @@ W = si.WORKLOADS
 CASES = [
     W["zigzag_causal_small"],                                                       # D=64, every rank
     W["zigzag_causal_small"].scaled(causal=False, impl="basic"),                    # both distance signs
+    W["zigzag_causal_small"].scaled(window=200, n_sink=2),                           # D=64 window kernel form
     W["ring_swa"].scaled(B=1, S=2048, Hq=4, Hkv=4, window=300),
     W["varlen_streaming"].scaled(S=2048, Hq=4, Hkv=2, window=250, cu_seqlens=[0, 128, 1000, 2048],
                                  impl="zigzag"),
@@ -98,7 +99,7 @@ def _ring(w, q, k, v, softcap, al):
 
 
 @pytest.mark.parametrize("softcap,alibi", MODS, ids=lambda m: str(m))
-@pytest.mark.parametrize("w", CASES, ids=lambda w: f"{w.name}-{w.impl}-b{w.stripe_block}-r{w.rank}-c{int(w.causal)}")
+@pytest.mark.parametrize("w", CASES, ids=lambda w: f"{w.name}-{w.impl}-b{w.stripe_block}-r{w.rank}-c{int(w.causal)}-w{w.window}")
 def test_ring_forward_score_mods(w, softcap, alibi):
     say(f"mods fwd {w.name} {w.impl} r={w.rank} cap={softcap} alibi={alibi}")
     q, k, v = w.make_inputs()
@@ -155,7 +156,7 @@ BWD_CASES = [CASES[0], CASES[1], CASES[3], CASES[4], CASES[5], CASES[6]]
 
 @pytest.mark.parametrize("softcap,alibi", MODS, ids=lambda m: str(m))
 @pytest.mark.parametrize("w", BWD_CASES,
-                         ids=lambda w: f"{w.name}-{w.impl}-b{w.stripe_block}-r{w.rank}-c{int(w.causal)}")
+                         ids=lambda w: f"{w.name}-{w.impl}-b{w.stripe_block}-r{w.rank}-c{int(w.causal)}-w{w.window}")
 def test_ring_backward_score_mods(w, softcap, alibi):
     """usp_ring_bwd with the oracle's forward output and LSE."""
     say(f"mods bwd {w.name} {w.impl} r={w.rank} cap={softcap} alibi={alibi}")

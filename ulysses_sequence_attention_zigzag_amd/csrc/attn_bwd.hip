@@ -395,6 +395,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
 
   // Epilogue: dV (P waves) or scale * dK (dS waves) added into the f32
   // gradients of this lane's key.
+  // The gradient this call adds to is loaded before the role's last matrix
+  // phase (K or V and the S / dP results are dead by then), which covers
+  // part of the load's latency: the store is a fifth to a quarter of a
+  // short (window) item's time.
+  float4 prev[DB][4];
+  auto load_prev = [&](const float* base) {
+    if (!kvalid) return;
+    const float* src = base + (int64_t)b * p.kv_batch_stride + krow * kv_row_stride + hk * D;
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) prev[d][g] = *reinterpret_cast<const float4*>(src + d * 32 + 8 * g + 4 * hi);
+  };
   auto store = [&](float* base, float w) {
     if (!kvalid) return;
     float* dst = base + (int64_t)b * p.kv_batch_stride + krow * kv_row_stride + hk * D;
@@ -403,7 +416,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int dd = d * 32 + 8 * g + 4 * hi;
-        float4 a = *reinterpret_cast<const float4*>(dst + dd);
+        float4 a = prev[d][g];
         a.x += w * acc[d][4 * g];
         a.y += w * acc[d][4 * g + 1];
         a.z += w * acc[d][4 * g + 2];
@@ -458,6 +471,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
     }
     // phase 2N-1: dV(N-1)
     prio_hi();
+    load_prev(p.dv);
     m_phase(T_{}, F_{}, ob_at(n_tiles - 1), nullptr);
     prio_lo();
     barrier();
@@ -498,6 +512,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
     }
     // phase 2N: dK(N-1)
     prio_hi();
+    load_prev(p.dk);
     m_phase(T_{}, F_{}, qb_at(n_tiles - 1), nullptr);
     prio_lo();
     store(p.dk, p.scale);

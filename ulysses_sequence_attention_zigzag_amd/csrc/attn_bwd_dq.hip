@@ -375,21 +375,30 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): V(n+2) landed
       pp_barrier();
     }
-    // phase 2N: dQ(N-1)
+    // phase 2N: dQ(N-1).  The dq rows this call adds to are loaded before
+    // it (V and the dP results are dead by then), which covers part of the
+    // load's latency.
+    float4 prev[DB][4];
+    float* op = p.dq + (int64_t)b * p.g_batch_stride + (qrow * p.Hq + h) * D;
+    if (qvalid) {
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) prev[d][g] = *reinterpret_cast<const float4*>(op + d * 32 + 8 * g + 4 * hi);
+    }
     prio_hi();
     m_phase(T_{}, F_{}, kb_at(n_tiles - 1), nullptr);
     prio_lo();
 
     // dq[b, row, h, :] += scale * dQ (this lane: query qrow, head-dim rows of dQ^T)
     if (!qvalid) return;
-    float* op = p.dq + (int64_t)b * p.g_batch_stride + (qrow * p.Hq + h) * D;
     const float w = p.scale;
 #pragma unroll
     for (int d = 0; d < DB; ++d) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int dd = d * 32 + 8 * g + 4 * hi;
-        float4 a = *reinterpret_cast<const float4*>(op + dd);
+        float4 a = prev[d][g];
         a.x += w * acc[d][4 * g];
         a.y += w * acc[d][4 * g + 1];
         a.z += w * acc[d][4 * g + 2];

@@ -1,7 +1,9 @@
 // Block attention forward for one ring step on gfx950 (CDNA4).
 //
 // One workgroup = 8 waves = 256 query rows of one (batch, head); each wave
-// owns 32 rows.  Per key tile (128 keys):
+// owns 32 rows (under a window mask: 4 waves, 128 rows, two workgroups per
+// CU; see the kernel).  Per key tile (128 keys; 64 in the window form at
+// D = 128):
 //   S^T = K Q^T      v_mfma_f32_32x32x16_bf16, K from LDS (A operand),
 //                    Q resident in VGPRs (B operand);
 //   mask             only in partial runs (the planner marks fully visible

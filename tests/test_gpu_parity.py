@@ -246,7 +246,10 @@ def test_lse_merge_kernel(D):
 
 # ---------------------------------------------------------------- HIP graph
 @pytest.mark.parametrize("w", [si.WORKLOADS["zigzag_causal_small"],
-                               si.WORKLOADS["usp_zigzag_gqa"].scaled(S=4096, Hq=8, Hkv=4)],
+                               si.WORKLOADS["usp_zigzag_gqa"].scaled(S=4096, Hq=8, Hkv=4),
+                               # window masks: the 4-wave kernel form
+                               si.WORKLOADS["varlen_streaming"].scaled(S=2048, Hq=4, Hkv=2, window=300,
+                                                                       cu_seqlens=[0, 300, 1200, 2048])],
                          ids=lambda w: w.name)
 def test_ring_graph_replay(w):
     """usp_ring_fwd recorded into a HIP graph: every replay, with eager calls
@@ -254,7 +257,8 @@ def test_ring_graph_replay(w):
     say(f"graph replay {w.name}")
     q, k, v = w.make_inputs()
     call = usp.RingCall(q.cuda(), k.cuda(), v.cuda(), impl=w.impl, ring_degree=w.ring_degree,
-                        ulysses_degree=w.ulysses_degree, causal=w.causal, softmax_scale=w.softmax_scale or 0.0,
+                        ulysses_degree=w.ulysses_degree, causal=w.causal, window=w.window, n_sink=w.n_sink,
+                        cu_seqlens=w.cu_seqlens, softmax_scale=w.softmax_scale or 0.0,
                         rank=w.rank, ulysses_rank=w.ulysses_rank)
     out, lse = call.run()
     torch.cuda.synchronize()

@@ -199,18 +199,33 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
   // delta values.  Rows past the run's end are clamped to its last row
   // (masked in the partial runs that have them; full runs are multiples of
   // BQ rows).
-  auto dma = [&](char* buf, const Cursor& c) {
-#pragma unroll
-    for (int j = 0; j < LPT; ++j) {
-      const int row = (wg * LPT + j) * RPI + lrow;
-      const uint32_t off = (uint32_t)min(c.t0 + row, c.run.k_end - 1) * qrow_bytes + (uint32_t)(c.gi * D * 2) +
-                           (uint32_t)((lslot ^ T::swz(row)) * 16);
-      copy16_to_lds(trs, lds_addr(buf + (wg * LPT + j) * 1024), off);
-    }
+  auto dma_slice = [&](char* buf, const Cursor& c, int j) {
+    const int row = (wg * LPT + j) * RPI + lrow;
+    const uint32_t off = (uint32_t)min(c.t0 + row, c.run.k_end - 1) * qrow_bytes + (uint32_t)(c.gi * D * 2) +
+                         (uint32_t)((lslot ^ T::swz(row)) * 16);
+    copy16_to_lds(trs, lds_addr(buf + (wg * LPT + j) * 1024), off);
+  };
+  auto dma_side = [&](char* buf, const Cursor& c) {
     if (grp == 1 && wg < 2) {
       const uint32_t off = (uint32_t)(c.gi * p.Lq_buf + min(c.t0 + lane, c.run.k_end - 1)) * 4u;
       copy4_to_lds(lrs, lds_addr(buf + TILEB + wg * BQ * 4), off);
     }
+  };
+  auto dma = [&](char* buf, const Cursor& c) {
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) dma_slice(buf, c, j);
+    dma_side(buf, c);
+  };
+  // Inside a matrix phase of NM MFMAs: slice m / (NM / LPT) after MFMA m,
+  // spread over the phase (the copies then overlap the matrix work instead
+  // of delaying the barrier).  Past the last tile the copy repeats the last
+  // one into the free buffer, which nothing reads again: the phase keeps a
+  // single straight-line body.
+  auto copy_in = [&](char* buf, const Cursor* c, auto nm_c) {
+    constexpr int STRIDE = decltype(nm_c)::value / LPT;
+    return [&dma_slice, buf, c](int m) {
+      if (m % STRIDE == STRIDE - 1 && m / STRIDE < LPT) dma_slice(buf, *c, m / STRIDE);
+    };
   };
 
   // K (P waves) or V (dS waves) fragments of this lane's key: B operand
@@ -275,9 +290,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
   // (Y = Q for S, dO for dP).
   int tro[2][DB], rro[KS];
   pp_offsets<D>(lane, tro, rro);
-  auto m_phase = [&](auto do_t_c, auto do_r_c, const char* tT, const char* tR) {
-    pp_matrix_phase<D, decltype(do_t_c)::value, decltype(do_r_c)::value>(acc, sc, bb, kv, tro, rro, tT, tR);
+  auto m_phase = [&](auto do_t_c, auto do_r_c, const char* tT, const char* tR, auto&& hook) {
+    pp_matrix_phase<D, decltype(do_t_c)::value, decltype(do_r_c)::value>(acc, sc, bb, kv, tro, rro, tT, tR, hook);
   };
+  const auto no_copy = [](int) {};
 
   // P exchange slot of this wave pair: the 8 bf16 of (block qb, half) of
   // lane l at ((qb * 2 + half) * 64 + l) * 16, in the B-operand order
@@ -442,7 +458,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     barrier();
     prio_hi();
-    m_phase(F_{}, T_{}, nullptr, qb_at(0));
+    m_phase(F_{}, T_{}, nullptr, qb_at(0), no_copy);
     prio_lo();
     barrier();
     // phase 0: softmax of tile 0
@@ -452,14 +468,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     barrier();
     for (int n = 0; n + 1 < n_tiles; ++n) {
-      // phase 2n+1: dV(n), S(n+1)
+      // phase 2n+1: dV(n), S(n+1); Q(n+2) copied meanwhile
+      if (n + 2 < n_tiles) advance(cq);
       prio_hi();
-      m_phase(T_{}, T_{}, ob_at(n), qb_at(n + 1));
+      m_phase(T_{}, T_{}, ob_at(n), qb_at(n + 1), copy_in(qb_at(n + 2), &cq, std::integral_constant<int, 4 * KS>{}));
       prio_lo();
-      if (n + 2 < n_tiles) {
-        advance(cq);
-        dma(qb_at(n + 2), cq);
-      }
       advance(cs);
       barrier();
       // phase 2n+2: softmax of tile n+1
@@ -472,7 +485,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
     // phase 2N-1: dV(N-1)
     prio_hi();
     load_prev(p.dv);
-    m_phase(T_{}, F_{}, ob_at(n_tiles - 1), nullptr);
+    m_phase(T_{}, F_{}, ob_at(n_tiles - 1), nullptr, no_copy);
     prio_lo();
     barrier();
     store(p.dv, 1.f);
@@ -484,7 +497,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
     barrier();
     // phase 0: dP(0)
     prio_hi();
-    m_phase(F_{}, T_{}, nullptr, ob_at(0));
+    m_phase(F_{}, T_{}, nullptr, ob_at(0), no_copy);
     prio_lo();
     if (n_tiles > 1) {
       advance(co);
@@ -496,14 +509,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): dO(1) landed
     barrier();
     for (int n = 0; n + 1 < n_tiles; ++n) {
-      // phase 2n+2: dK(n), dP(n+1)
+      // phase 2n+2: dK(n), dP(n+1); dO(n+2) copied meanwhile
+      if (n + 2 < n_tiles) advance(co);
       prio_hi();
-      m_phase(T_{}, T_{}, qb_at(n), ob_at(n + 1));
+      m_phase(T_{}, T_{}, qb_at(n), ob_at(n + 1), copy_in(ob_at(n + 2), &co, std::integral_constant<int, 4 * KS>{}));
       prio_lo();
-      if (n + 2 < n_tiles) {
-        advance(co);
-        dma(ob_at(n + 2), co);
-      }
+      if (n + 2 < n_tiles) dma_side(ob_at(n + 2), co);
       barrier();
       // phase 2n+3: dS(n+1)
       form_ds(ob_at(n + 1));
@@ -513,7 +524,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
     // phase 2N: dK(N-1)
     prio_hi();
     load_prev(p.dk);
-    m_phase(T_{}, F_{}, qb_at(n_tiles - 1), nullptr);
+    m_phase(T_{}, F_{}, qb_at(n_tiles - 1), nullptr, no_copy);
     prio_lo();
     store(p.dk, p.scale);
   }

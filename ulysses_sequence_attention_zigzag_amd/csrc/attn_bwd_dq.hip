@@ -180,20 +180,33 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
   // slot) = (slice*RPI + i / CPR, i % CPR) = logical chunk slot ^ swz(row);
   // rows past the run's end are clamped to its last row (masked in partial
   // runs; full runs are multiples of BN keys).
+  auto dma_slice = [&](char* buf, const Cursor& cu, int j) {
+    const int row = (wg * LPT + j) * RPI + lrow;
+    const uint32_t off = (uint32_t)min(cu.k0 + row, cu.run.k_end - 1) * row_bytes + (uint32_t)((lslot ^ T::swz(row)) * 16);
+    copy16_to_lds(trs, lds_addr(buf + (wg * LPT + j) * 1024), off);
+  };
   auto dma = [&](char* buf, const Cursor& cu) {
 #pragma unroll
-    for (int j = 0; j < LPT; ++j) {
-      const int row = (wg * LPT + j) * RPI + lrow;
-      const uint32_t off = (uint32_t)min(cu.k0 + row, cu.run.k_end - 1) * row_bytes + (uint32_t)((lslot ^ T::swz(row)) * 16);
-      copy16_to_lds(trs, lds_addr(buf + (wg * LPT + j) * 1024), off);
-    }
+    for (int j = 0; j < LPT; ++j) dma_slice(buf, cu, j);
+  };
+  // Inside a matrix phase of NM MFMAs: slice m / (NM / LPT) after MFMA m,
+  // spread over the phase (the copies then overlap the matrix work instead
+  // of delaying the barrier).  Past the last tile the copy repeats the last
+  // one into the free buffer, which nothing reads again: the phase keeps a
+  // single straight-line body.
+  auto copy_in = [&](char* buf, const Cursor* cu, auto nm_c) {
+    constexpr int STRIDE = decltype(nm_c)::value / LPT;
+    return [&dma_slice, buf, cu](int m) {
+      if (m % STRIDE == STRIDE - 1 && m / STRIDE < LPT) dma_slice(buf, *cu, m / STRIDE);
+    };
   };
 
   int tro[2][DB], rro[KS];
   pp_offsets<D>(lane, tro, rro);
-  auto m_phase = [&](auto do_t_c, auto do_r_c, const char* tT, const char* tR) {
-    pp_matrix_phase<D, decltype(do_t_c)::value, decltype(do_r_c)::value>(acc, sc, bb, kv, tro, rro, tT, tR);
+  auto m_phase = [&](auto do_t_c, auto do_r_c, const char* tT, const char* tR, auto&& hook) {
+    pp_matrix_phase<D, decltype(do_t_c)::value, decltype(do_r_c)::value>(acc, sc, bb, kv, tro, rro, tT, tR, hook);
   };
+  const auto no_copy = [](int) {};
 
   // P exchange slot of this wave pair: the 8 bf16 of (block kb, half) of
   // lane l at ((kb * 2 + half) * 64 + l) * 16, in the B-operand order
@@ -314,7 +327,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     pp_barrier();
     prio_hi();
-    m_phase(F_{}, T_{}, nullptr, kb_at(0));
+    m_phase(F_{}, T_{}, nullptr, kb_at(0), no_copy);
     prio_lo();
     pp_barrier();
     // phase 0: P of tile 0
@@ -323,14 +336,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): the exchange writes, K(1)
     pp_barrier();
     for (int n = 0; n + 1 < n_tiles; ++n) {
-      // phase 2n+1: S(n+1)
+      // phase 2n+1: S(n+1); K(n+2) copied meanwhile
+      if (n + 2 < n_tiles) advance(ck);
       prio_hi();
-      m_phase(F_{}, T_{}, nullptr, kb_at(n + 1));
+      m_phase(F_{}, T_{}, nullptr, kb_at(n + 1), copy_in(kb_at(n + 2), &ck, std::integral_constant<int, 2 * KS>{}));
       prio_lo();
-      if (n + 2 < n_tiles) {
-        advance(ck);
-        dma(kb_at(n + 2), ck);
-      }
       advance(cs);
       pp_barrier();
       // phase 2n+2: P of tile n+1
@@ -349,7 +359,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
     pp_barrier();
     // phase 0: dP(0)
     prio_hi();
-    m_phase(F_{}, T_{}, nullptr, vb_at(0));
+    m_phase(F_{}, T_{}, nullptr, vb_at(0), no_copy);
     prio_lo();
     if (n_tiles > 1) {
       advance(cv);
@@ -361,14 +371,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): V(1) landed
     pp_barrier();
     for (int n = 0; n + 1 < n_tiles; ++n) {
-      // phase 2n+2: dQ(n), dP(n+1)
+      // phase 2n+2: dQ(n), dP(n+1); V(n+2) copied meanwhile
+      if (n + 2 < n_tiles) advance(cv);
       prio_hi();
-      m_phase(T_{}, T_{}, kb_at(n), vb_at(n + 1));
+      m_phase(T_{}, T_{}, kb_at(n), vb_at(n + 1), copy_in(vb_at(n + 2), &cv, std::integral_constant<int, 4 * KS>{}));
       prio_lo();
-      if (n + 2 < n_tiles) {
-        advance(cv);
-        dma(vb_at(n + 2), cv);
-      }
       pp_barrier();
       // phase 2n+3: dS(n+1)
       form_ds();
@@ -387,7 +394,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
         for (int g = 0; g < 4; ++g) prev[d][g] = *reinterpret_cast<const float4*>(op + d * 32 + 8 * g + 4 * hi);
     }
     prio_hi();
-    m_phase(T_{}, F_{}, kb_at(n_tiles - 1), nullptr);
+    m_phase(T_{}, F_{}, kb_at(n_tiles - 1), nullptr, no_copy);
     prio_lo();
 
     // dq[b, row, h, :] += scale * dQ (this lane: query qrow, head-dim rows of dQ^T)

@@ -103,12 +103,14 @@ struct TileLayout {
 // every SIMD one wave feeds the matrix core while the other does its softmax:
 //   phase 2t  : group 0 in M(t), group 1 in V(t-1)
 //   phase 2t+1: group 0 in V(t), group 1 in M(t)
-// Group 0 stages the K tiles and group 1 the V tiles: right after the last
-// LDS read of its M(t) a group issues the loads of tile t+1 straight into
-// LDS, into the buffer whose previous tile both groups have finished
-// reading, and waits for them at the end of its V(t), before the barrier
-// that hands the phase over.  Phase barriers carry no memory fence: every
-// LDS read of a matrix phase is consumed by its MFMAs before the phase ends.
+// Group 0 stages the K tiles and group 1 the V tiles: at the start of its
+// V(t), past the barrier that ends its M(t), a group issues the loads of
+// tile t+1 straight into LDS, into the buffer whose previous tile both
+// groups have finished reading, and waits for them at the end of its V(t),
+// before the barrier that hands the phase over.  (Issued at the end of M(t)
+// instead, the copies lengthened the matrix phases, the longer side of
+// each phase.)  Phase barriers carry no memory fence: every LDS read of a
+// matrix phase is consumed by its MFMAs before the phase ends.
 //
 // Window masks (WIN) make short work items: a query tile sees a band of a few
 // key tiles, and the item's fixed costs (loading q, the first tile, reading
@@ -236,14 +238,43 @@ __global__ __launch_bounds__(W4 ? 256 : 512, 2) void attn_fwd_kernel(const AttnP
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(grp ? vbase : kbase), (short)0, 0x7fffffff, kBufferRsrcWord3);
   char* const stage_tiles = smem + grp * 2 * TILEB;
-  // one tile (V when is_v) into `tile`
+  // A tile that lies inside its run needs no clamp, and the lane's part of
+  // each offset is loop-invariant: slice s = wg*LPT + j starts at row s*RPI,
+  // which the swizzles see only through s % NSW (s*RPI/RPL = 4s), and
+  // wg*LPT is a multiple of NSW.  So NSW per-lane offsets (one for V, whose
+  // swizzle ignores the slice) serve every slice, and the tile's first key
+  // plus the slice's row go into the scalar offset of the load.  (Named
+  // scalars rather than an array: an array indexed inside the copy lambda
+  // made the host pass drop the kernels' launch stubs.)
+  constexpr int NSW = TL::CPR / 4;
+  static_assert(LPT % NSW == 0 && RPI == 4 * TL::RPL && NSW <= 4, "slice / swizzle period");
+  const uint32_t lrb = (uint32_t)lrow * row_bytes;
+  const uint32_t lofs_k0 = lrb + (uint32_t)((lslot ^ TL::swz_k(lrow)) * 16);
+  const uint32_t lofs_k1 = lrb + (uint32_t)((lslot ^ TL::swz_k(RPI + lrow)) * 16);
+  const uint32_t lofs_k2 = lrb + (uint32_t)((lslot ^ TL::swz_k(2 * RPI + lrow)) * 16);
+  const uint32_t lofs_k3 = lrb + (uint32_t)((lslot ^ TL::swz_k(3 * RPI + lrow)) * 16);
+  const uint32_t lofs_v = lrb + (uint32_t)((lslot ^ TL::swz_v(lrow)) * 16);
+  // one tile (V when is_v) into `tile` (the D = 64 window kernels keep the
+  // clamped form: the scalar offsets would take them past the SGPR budget)
+  constexpr bool kFastCopy = !(W4 && D == 64);
   auto dma_one = [&](const __amdgpu_buffer_rsrc_t& rs, bool is_v, char* tile, int k0, int kend) {
+    if (kFastCopy && k0 + BN <= kend) {
 #pragma unroll
-    for (int j = 0; j < LPT; ++j) {
-      const int row = (wg * LPT + j) * RPI + lrow;
-      const int sw = is_v ? TL::swz_v(row) : TL::swz_k(row);
-      const uint32_t off = (uint32_t)min(k0 + row, kend - 1) * row_bytes + (uint32_t)((lslot ^ sw) * 16);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(tile + (wg * LPT + j) * 1024), 16, off, 0, 0, 0);
+      for (int j = 0; j < LPT; ++j) {
+        const uint32_t soff = (uint32_t)(k0 + (wg * LPT + j) * RPI) * row_bytes;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(tile + (wg * LPT + j) * 1024), 16,
+                                                 is_v ? lofs_v
+                                                      : (j % NSW == 0 ? lofs_k0 : j % NSW == 1 ? lofs_k1 : j % NSW == 2 ? lofs_k2 : lofs_k3),
+                                                 soff, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < LPT; ++j) {
+        const int row = (wg * LPT + j) * RPI + lrow;
+        const int sw = is_v ? TL::swz_v(row) : TL::swz_k(row);
+        const uint32_t off = (uint32_t)min(k0 + row, kend - 1) * row_bytes + (uint32_t)((lslot ^ sw) * 16);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(tile + (wg * LPT + j) * 1024), 16, off, 0, 0, 0);
+      }
     }
   };
   // this group's tile (8 waves: K for group 0, V for group 1), or both (W4:
@@ -621,8 +652,8 @@ __global__ __launch_bounds__(W4 ? 256 : 512, 2) void attn_fwd_kernel(const AttnP
       prio_hi();
       m_phase(F_{}, T_{}, nullptr, smem, s, pb);
       prio_lo();
-      if (n_tiles > 1) dma_tile(stage_tiles + TILEB, nk0, nrun.k_end);
       phase_barrier();
+      if (n_tiles > 1) dma_tile(stage_tiles + TILEB, nk0, nrun.k_end);
       v_phase(0);
       phase_barrier();
       for (int t = 1; t < n_tiles; ++t) {
@@ -630,8 +661,8 @@ __global__ __launch_bounds__(W4 ? 256 : 512, 2) void attn_fwd_kernel(const AttnP
         prio_hi();
         m_phase(T_{}, T_{}, smem + (2 + ((t - 1) & 1)) * TILEB, smem + (t & 1) * TILEB, s, pb);
         prio_lo();
-        if (t + 1 < n_tiles) dma_tile(stage_tiles + ((t + 1) & 1) * TILEB, nk0, nrun.k_end);
         phase_barrier();
+        if (t + 1 < n_tiles) dma_tile(stage_tiles + ((t + 1) & 1) * TILEB, nk0, nrun.k_end);
         v_phase(t);
         phase_barrier();
       }

@@ -204,10 +204,13 @@ __device__ __forceinline__ void pp_offsets(int lane, int (&tro)[2][D / 32], int 
 // row-operand products sc[blk] = Y kv (Y the tile at tR; 2 blocks x D/16
 // MFMAs, the two blocks alternating) if DR.  Fragments are read kPF MFMAs
 // ahead, across the boundary, in an order pinned with scheduling groups.
-template <int D, bool DT, bool DR>
+// hook(m) runs after the phase's m-th MFMA (m a constant once unrolled): the
+// kernels issue their tile copies from it, spread over the phase.
+template <int D, bool DT, bool DR, typename Hook>
 __device__ __forceinline__ void pp_matrix_phase(f32x16 (&acc)[D / 32], f32x16 (&sc)[2], const bf16x8 (&bb)[2][2],
                                                 const bf16x8 (&kv)[D / 16], const int (&tro)[2][D / 32],
-                                                const int (&rro)[D / 16], const char* tT, const char* tR) {
+                                                const int (&rro)[D / 16], const char* tT, const char* tR,
+                                                Hook&& hook) {
   using T = SwzTile<D>;
   constexpr int KS = D / 16, DB = D / 32;
   constexpr int NT = 2 * 2 * DB;
@@ -235,6 +238,7 @@ __device__ __forceinline__ void pp_matrix_phase(f32x16 (&acc)[D / 32], f32x16 (&
       else if (DR) fr[j + PF - NT] = rd_r(j + PF - NT);
       const int blk = j / (2 * DB), half = (j / DB) & 1, d = j % DB;
       acc[d] = mfma32(ft[j], bb[blk][half], acc[d]);
+      hook(j);
     }
   } else {
 #pragma unroll
@@ -247,6 +251,7 @@ __device__ __forceinline__ void pp_matrix_phase(f32x16 (&acc)[D / 32], f32x16 (&
       if (i + PF < NR) fr[i + PF] = rd_r(i + PF);
       const int ks = i >> 1, blk = i & 1;
       sc[blk] = mfma32(fr[i], kv[ks], ks == 0 ? zero : sc[blk]);
+      hook((DT ? NT : 0) + i);
     }
   }
   // scheduling groups, in issue order (a transposed fragment is 2 reads)

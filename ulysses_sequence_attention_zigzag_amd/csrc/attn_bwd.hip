@@ -199,10 +199,22 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
   // delta values.  Rows past the run's end are clamped to its last row
   // (masked in the partial runs that have them; full runs are multiples of
   // BQ rows).
+  // The offsets' lane parts are loop-invariant: row s*RPI + lrow of slice
+  // s = wg*LPT + j has a swizzle that depends on s only through j (s*RPI/RPL
+  // = 4s, and wg*LPT is a multiple of the swizzle's period in s), and the
+  // clamp distributes over the row stride, so a slice costs an add and a
+  // min besides the copy.  (Named scalars, not an array: the copy lambdas
+  // run inside the matrix phase's unrolled loop.)
+  const uint32_t lrb = (uint32_t)lrow * qrow_bytes;
+  const uint32_t lsw0 = (uint32_t)((lslot ^ T::swz(lrow)) * 16);
+  const uint32_t lsw1 = (uint32_t)((lslot ^ T::swz(RPI + lrow)) * 16);
+  const uint32_t lsw2 = (uint32_t)((lslot ^ T::swz(2 * RPI + lrow)) * 16);
+  const uint32_t lsw3 = (uint32_t)((lslot ^ T::swz(3 * RPI + lrow)) * 16);
+  static_assert(LPT <= 4, "four lane swizzles");
   auto dma_slice = [&](char* buf, const Cursor& c, int j) {
-    const int row = (wg * LPT + j) * RPI + lrow;
-    const uint32_t off = (uint32_t)min(c.t0 + row, c.run.k_end - 1) * qrow_bytes + (uint32_t)(c.gi * D * 2) +
-                         (uint32_t)((lslot ^ T::swz(row)) * 16);
+    const uint32_t rows = min(lrb + (uint32_t)(c.t0 + (wg * LPT + j) * RPI) * qrow_bytes,
+                              (uint32_t)(c.run.k_end - 1) * qrow_bytes);
+    const uint32_t off = rows + (uint32_t)(c.gi * D * 2) + (j == 0 ? lsw0 : j == 1 ? lsw1 : j == 2 ? lsw2 : lsw3);
     copy16_to_lds(trs, lds_addr(buf + (wg * LPT + j) * 1024), off);
   };
   auto dma_side = [&](char* buf, const Cursor& c) {
@@ -216,15 +228,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
     for (int j = 0; j < LPT; ++j) dma_slice(buf, c, j);
     dma_side(buf, c);
   };
-  // Inside a matrix phase of NM MFMAs: slice m / (NM / LPT) after MFMA m,
-  // spread over the phase (the copies then overlap the matrix work instead
-  // of delaying the barrier).  Past the last tile the copy repeats the last
-  // one into the free buffer, which nothing reads again: the phase keeps a
-  // single straight-line body.
+  // Inside a matrix phase of NM MFMAs: slice j after MFMA FIRST + j*STRIDE
+  // (mfma_common.h's placement; the copies then overlap the matrix work
+  // instead of delaying the barrier).  Past the last tile the copy repeats
+  // the last one into the free buffer, which nothing reads again: the phase
+  // keeps a single straight-line body.
   auto copy_in = [&](char* buf, const Cursor* c, auto nm_c) {
-    constexpr int STRIDE = decltype(nm_c)::value / LPT;
+    constexpr int STRIDE = kCopyStride > 0 ? kCopyStride : decltype(nm_c)::value / LPT;
+    constexpr int FIRST = kCopyFirst >= 0 ? kCopyFirst : STRIDE - 1;
+    static_assert(FIRST + (LPT - 1) * STRIDE < decltype(nm_c)::value, "copy positions");
     return [&dma_slice, buf, c](int m) {
-      if (m % STRIDE == STRIDE - 1 && m / STRIDE < LPT) dma_slice(buf, *c, m / STRIDE);
+      if (m >= FIRST && (m - FIRST) % STRIDE == 0 && (m - FIRST) / STRIDE < LPT) dma_slice(buf, *c, (m - FIRST) / STRIDE);
     };
   };
 

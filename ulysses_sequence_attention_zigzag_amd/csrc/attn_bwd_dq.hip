@@ -180,24 +180,36 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
   // slot) = (slice*RPI + i / CPR, i % CPR) = logical chunk slot ^ swz(row);
   // rows past the run's end are clamped to its last row (masked in partial
   // runs; full runs are multiples of BN keys).
+  // Loop-invariant lane parts of the offsets (as in the dK/dV kernel: the
+  // swizzle of row s*RPI + lrow depends on s only through j, and the clamp
+  // distributes over the row stride).
+  const uint32_t lrb = (uint32_t)lrow * row_bytes;
+  const uint32_t lsw0 = (uint32_t)((lslot ^ T::swz(lrow)) * 16);
+  const uint32_t lsw1 = (uint32_t)((lslot ^ T::swz(RPI + lrow)) * 16);
+  const uint32_t lsw2 = (uint32_t)((lslot ^ T::swz(2 * RPI + lrow)) * 16);
+  const uint32_t lsw3 = (uint32_t)((lslot ^ T::swz(3 * RPI + lrow)) * 16);
+  static_assert(LPT <= 4, "four lane swizzles");
   auto dma_slice = [&](char* buf, const Cursor& cu, int j) {
-    const int row = (wg * LPT + j) * RPI + lrow;
-    const uint32_t off = (uint32_t)min(cu.k0 + row, cu.run.k_end - 1) * row_bytes + (uint32_t)((lslot ^ T::swz(row)) * 16);
+    const uint32_t rows = min(lrb + (uint32_t)(cu.k0 + (wg * LPT + j) * RPI) * row_bytes,
+                              (uint32_t)(cu.run.k_end - 1) * row_bytes);
+    const uint32_t off = rows + (j == 0 ? lsw0 : j == 1 ? lsw1 : j == 2 ? lsw2 : lsw3);
     copy16_to_lds(trs, lds_addr(buf + (wg * LPT + j) * 1024), off);
   };
   auto dma = [&](char* buf, const Cursor& cu) {
 #pragma unroll
     for (int j = 0; j < LPT; ++j) dma_slice(buf, cu, j);
   };
-  // Inside a matrix phase of NM MFMAs: slice m / (NM / LPT) after MFMA m,
-  // spread over the phase (the copies then overlap the matrix work instead
-  // of delaying the barrier).  Past the last tile the copy repeats the last
-  // one into the free buffer, which nothing reads again: the phase keeps a
-  // single straight-line body.
+  // Inside a matrix phase of NM MFMAs: slice j after MFMA FIRST + j*STRIDE
+  // (mfma_common.h's placement; the copies then overlap the matrix work
+  // instead of delaying the barrier).  Past the last tile the copy repeats
+  // the last one into the free buffer, which nothing reads again: the phase
+  // keeps a single straight-line body.
   auto copy_in = [&](char* buf, const Cursor* cu, auto nm_c) {
-    constexpr int STRIDE = decltype(nm_c)::value / LPT;
+    constexpr int STRIDE = kCopyStride > 0 ? kCopyStride : decltype(nm_c)::value / LPT;
+    constexpr int FIRST = kCopyFirst >= 0 ? kCopyFirst : STRIDE - 1;
+    static_assert(FIRST + (LPT - 1) * STRIDE < decltype(nm_c)::value, "copy positions");
     return [&dma_slice, buf, cu](int m) {
-      if (m % STRIDE == STRIDE - 1 && m / STRIDE < LPT) dma_slice(buf, *cu, m / STRIDE);
+      if (m >= FIRST && (m - FIRST) % STRIDE == 0 && (m - FIRST) / STRIDE < LPT) dma_slice(buf, *cu, (m - FIRST) / STRIDE);
     };
   };
 

@@ -40,6 +40,19 @@ constexpr float kLog2e = 1.44269504088896340736f;
 #define USP_BWD_KV_VALU_C 6
 #endif
 constexpr int kPF = USP_BWD_PF;
+// Positions of the tile-copy slices inside a matrix phase: slice j after MFMA
+// kCopyFirst + j * kCopyStride (0 / -1: spread evenly over the phase).  Early
+// in the phase, every other MFMA, measured best (0.5-0.9 % over spread
+// evenly; every fourth from the second MFMA lost 2-3 %): the copies then have
+// the rest of the phase and the next one to land.
+#ifndef USP_BWD_COPY_STRIDE
+#define USP_BWD_COPY_STRIDE 2
+#endif
+#ifndef USP_BWD_COPY_FIRST
+#define USP_BWD_COPY_FIRST 0
+#endif
+constexpr int kCopyStride = USP_BWD_COPY_STRIDE;
+constexpr int kCopyFirst = USP_BWD_COPY_FIRST;
 constexpr int kDqValuA = USP_BWD_DQ_VALU_A;
 constexpr int kDqValuC = USP_BWD_DQ_VALU_C;
 constexpr int kKvValuA = USP_BWD_KV_VALU_A;

@@ -21,23 +21,10 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.44269504088896340736f;
-// LDS fragment reads in flight ahead of the MFMAs that use them, and VALU
-// instructions placed after each MFMA of the phases that overlap a softmax
+// LDS fragment reads in flight ahead of the MFMAs that use them
 // (build-time overridable for tuning sweeps)
 #ifndef USP_BWD_PF
 #define USP_BWD_PF 4
-#endif
-#ifndef USP_BWD_DQ_VALU_A
-#define USP_BWD_DQ_VALU_A 5
-#endif
-#ifndef USP_BWD_DQ_VALU_C
-#define USP_BWD_DQ_VALU_C 10
-#endif
-#ifndef USP_BWD_KV_VALU_A
-#define USP_BWD_KV_VALU_A 6
-#endif
-#ifndef USP_BWD_KV_VALU_C
-#define USP_BWD_KV_VALU_C 6
 #endif
 constexpr int kPF = USP_BWD_PF;
 // Positions of the tile-copy slices inside a matrix phase: slice j after MFMA
@@ -53,23 +40,7 @@ constexpr int kPF = USP_BWD_PF;
 #endif
 constexpr int kCopyStride = USP_BWD_COPY_STRIDE;
 constexpr int kCopyFirst = USP_BWD_COPY_FIRST;
-constexpr int kDqValuA = USP_BWD_DQ_VALU_A;
-constexpr int kDqValuC = USP_BWD_DQ_VALU_C;
-constexpr int kKvValuA = USP_BWD_KV_VALU_A;
-constexpr int kKvValuC = USP_BWD_KV_VALU_C;
 constexpr int kBufferRsrcWord3 = 0x00020000;  // raw buffer resource word 3 (gfx9 family)
-
-// Scheduling group of n DS reads / n VALU instructions; n is a constant
-// after unrolling, so the switch folds away.
-__device__ __forceinline__ void sched_ds_read(int n) {
-  switch (n) {
-    case 1: __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); break;
-    case 2: __builtin_amdgcn_sched_group_barrier(0x100, 2, 0); break;
-    case 3: __builtin_amdgcn_sched_group_barrier(0x100, 3, 0); break;
-    case 4: __builtin_amdgcn_sched_group_barrier(0x100, 4, 0); break;
-    default: break;
-  }
-}
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);

@@ -574,7 +574,8 @@ def forward_record(args, w, q, k, v, qd, kd, vd, with_cpu: bool, cpu_budget: flo
             "unit": "TFLOP/s",
             "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4) if attn_tflops else None,
             # the counter record was taken on the workloads as defined (stripe block 1, rank 0)
-            "traffic": measured_traffic(w.name) if (w.stripe_block == 1 and w.rank <= 0) else None,
+            "traffic": (measured_traffic(w.name if w.rank <= 0 else "%s_rank%d" % (w.name, w.rank))
+                        if w.stripe_block == 1 else None),
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "kernel": "attn_fwd_kernel<%d%s>" % (w.D, "" if w.stripe_block == 1 else ", stepped"),
             "launches_per_step": attn_n // max(1, args.steps),

@@ -92,8 +92,8 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const void* out, int out
 //            P = exp2(S c - LSE log2 e) -> bf16 P for dV, and to the LDS
 //            exchange (times the softcap derivative)   [vector]
 //            dV^T += dO^T P         [matrix]
-//   dS wave: dP(n)                 [matrix]
-//            dS = P (dP - delta) from the exchange   [vector]
+//   dS wave: delta - dP(n)         [matrix: -V fragments, C = delta]
+//            dS = -P (delta - dP) from the exchange   [vector]
 //            dK^T += Q^T dS         [matrix]
 // The two waves of a SIMD alternate: in phase 2n the P wave runs its
 // softmax of tile n while the dS wave runs dK(n-1) and dP(n) on the matrix
@@ -102,7 +102,9 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const void* out, int out
 // each wave waits for its own LDS writes and tile loads explicitly first).
 // Tile staging straight into LDS: the P waves load Q (3 buffers: Q(n) is
 // read in phases 2n-1 .. 2n+2), issued two phases ahead of use; the dS
-// waves load dO, LSE and delta (2 buffers, read in phases 2n, 2n+1).
+// waves load dO, LSE and delta (2 buffers, read in phases 2n, 2n+1); once
+// a tile's LSE has landed, dS wave 0 rewrites it in place as -LSE log2 e,
+// the exp2 argument's second term.
 template <int D, int MODS>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
   using T = SwzTile<D>;
@@ -217,6 +219,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
     const uint32_t off = rows + (uint32_t)(c.gi * D * 2) + (j == 0 ? lsw0 : j == 1 ? lsw1 : j == 2 ? lsw2 : lsw3);
     copy16_to_lds(trs, lds_addr(buf + (wg * LPT + j) * 1024), off);
   };
+
   auto dma_side = [&](char* buf, const Cursor& c) {
     if (grp == 1 && wg < 2) {
       const uint32_t off = (uint32_t)(c.gi * p.Lq_buf + min(c.t0 + lane, c.run.k_end - 1)) * 4u;
@@ -242,22 +245,29 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
     };
   };
 
-  // K (P waves) or V (dS waves) fragments of this lane's key: B operand
+  // K (P waves) or -V (dS waves, sign bits flipped: exact) fragments of this
+  // lane's key: B operand
   bf16x8 kv[KS];
   {
     const uint16_t* src = (grp ? p.v : p.k) + (int64_t)b * p.kv_batch_stride + krow * kv_row_stride + hk * D + hi * 8;
+    const uint32_t flip = grp ? 0x80008000u : 0u;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (kvalid) {
-        kv[ks] = *reinterpret_cast<const bf16x8*>(src + ks * 16);
+        uint4 u = *reinterpret_cast<const uint4*>(src + ks * 16);
+        u.x ^= flip;
+        u.y ^= flip;
+        u.z ^= flip;
+        u.w ^= flip;
+        kv[ks] = __builtin_bit_cast(bf16x8, u);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) kv[ks][e] = (__bf16)0.f;
       }
     }
   }
-  // acc: dV^T (P waves) or dK^T (dS waves); sc: S or dP of the two 32-row
-  // blocks; bb: bf16 P or dS (B operand of the accumulating products)
+  // acc: dV^T (P waves) or dK^T (dS waves); sc: S or delta - dP of the two
+  // 32-row blocks; bb: bf16 P or dS (B operand of the accumulating products)
   f32x16 acc[DB], sc[2];
   bf16x8 bb[2][2];
 #pragma unroll
@@ -304,10 +314,40 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
   // (Y = Q for S, dO for dP).
   int tro[2][DB], rro[KS];
   pp_offsets<D>(lane, tro, rro);
-  auto m_phase = [&](auto do_t_c, auto do_r_c, const char* tT, const char* tR, auto&& hook) {
-    pp_matrix_phase<D, decltype(do_t_c)::value, decltype(do_r_c)::value>(acc, sc, bb, kv, tro, rro, tT, tR, hook);
+  auto m_phase = [&](auto do_t_c, auto do_r_c, uint32_t tT, uint32_t tR, const f32x16(&c0)[2], auto&& hook) {
+    pp_matrix_phase<D, decltype(do_t_c)::value, decltype(do_r_c)::value>(acc, sc, bb, kv, tro, rro, tT, tR, c0, hook);
   };
   const auto no_copy = [](int) {};
+  // C operands of the first S MFMA (0) and of the first dP MFMA (delta of
+  // the tile's rows, element r of block qb for row qb*32 + 8*(r/4) + 4*hi +
+  // r%4, read from the tile's side buffer)
+  f32x16 c_zero[2];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) c_zero[0][r] = c_zero[1][r] = 0.f;
+  auto delta_c = [&](f32x16 (&cd)[2], const char* ob) {
+    const float* sd = reinterpret_cast<const float*>(ob + TILEB + BQ * 4);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 d4 = *reinterpret_cast<const float4*>(sd + qb * 32 + 8 * g + 4 * hi);
+        cd[qb][4 * g] = d4.x;
+        cd[qb][4 * g + 1] = d4.y;
+        cd[qb][4 * g + 2] = d4.z;
+        cd[qb][4 * g + 3] = d4.w;
+      }
+  };
+  // dS wave 0, once its tile's LSE has landed: LSE -> -LSE log2 e in place
+  // (its own copy, so the wait on its own loads covers it); the write is
+  // complete before the barrier that follows.
+  auto fix_lse = [&](char* ob) {
+    if (wg == 0) {
+      asm volatile("" ::: "memory");
+      float* sl = reinterpret_cast<float*>(ob + TILEB);
+      sl[lane] = -sl[lane] * kLog2e;
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    }
+  };
 
   // P exchange slot of this wave pair: the 8 bf16 of (block qb, half) of
   // lane l at ((qb * 2 + half) * 64 + l) * 16, in the B-operand order
@@ -357,7 +397,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
             const float dd = __builtin_floorf((t + 0.5f) * inv_b) * nb1 + (t + rb);
             sv -= slope * __builtin_fabsf(dd);
           }
-          float pe = __builtin_amdgcn_exp2f(sv * c - lq[e] * kLog2e);
+          float pe = __builtin_amdgcn_exp2f(fmaf(sv, c, lq[e]));
           if constexpr (!FULL) {
             const int cc = qb * 32 + 8 * g + e;
             pe = ((cc >= lo) & (cc <= up)) ? pe : 0.f;
@@ -388,9 +428,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
       if constexpr (!FULL) __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // Vector phase of the dS wave: dS = P (dP - delta), dP in sc.
-  auto form_ds = [&](const char* ob) {
-    const float* sd = reinterpret_cast<const float*>(ob + TILEB + BQ * 4);
+  // Vector phase of the dS wave: dS = -P (delta - dP), the latter in sc.
+  auto form_ds = [&]() {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const bf16x8 xh[2] = {*reinterpret_cast<const bf16x8*>(xw + (qb * 2 * 64 + lane) * 16),
@@ -399,11 +438,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
       for (int g = 0; g < 4; ++g) {
         const int hh = g >> 1, o = (g & 1) * 4;
         const float4 px = make_float4((float)xh[hh][o], (float)xh[hh][o + 1], (float)xh[hh][o + 2], (float)xh[hh][o + 3]);
-        const float4 d4 = *reinterpret_cast<const float4*>(sd + qb * 32 + 8 * g + 4 * hi);
-        const float d0 = px.x * (sc[qb][4 * g] - d4.x);
-        const float d1 = px.y * (sc[qb][4 * g + 1] - d4.y);
-        const float d2 = px.z * (sc[qb][4 * g + 2] - d4.z);
-        const float d3 = px.w * (sc[qb][4 * g + 3] - d4.w);
+        const float d0 = -(px.x * sc[qb][4 * g]);
+        const float d1 = -(px.y * sc[qb][4 * g + 1]);
+        const float d2 = -(px.z * sc[qb][4 * g + 2]);
+        const float d3 = -(px.w * sc[qb][4 * g + 3]);
         const bf16x2 a01 = __builtin_convertvector((f32x2){d0, d1}, bf16x2);
         const bf16x2 a23 = __builtin_convertvector((f32x2){d2, d3}, bf16x2);
         const int half = g >> 1, e0 = (g & 1) * 4;
@@ -422,6 +460,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
   auto prio_lo = []() { __builtin_amdgcn_s_setprio(0); };
   auto qb_at = [&](int n) { return qbuf + (n % 3) * TILEB; };
   auto ob_at = [&](int n) { return obuf + (n & 1) * OBUFB; };
+  auto ql_at = [&](int n) { return lds_addr(qb_at(n)); };
+  auto ol_at = [&](int n) { return lds_addr(ob_at(n)); };
 
   // Epilogue: dV (P waves) or scale * dK (dS waves) added into the f32
   // gradients of this lane's key.
@@ -472,7 +512,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     barrier();
     prio_hi();
-    m_phase(F_{}, T_{}, nullptr, qb_at(0), no_copy);
+    m_phase(F_{}, T_{}, 0u, ql_at(0), c_zero, no_copy);
     prio_lo();
     barrier();
     // phase 0: softmax of tile 0
@@ -485,7 +525,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
       // phase 2n+1: dV(n), S(n+1); Q(n+2) copied meanwhile
       if (n + 2 < n_tiles) advance(cq);
       prio_hi();
-      m_phase(T_{}, T_{}, ob_at(n), qb_at(n + 1), copy_in(qb_at(n + 2), &cq, std::integral_constant<int, 4 * KS>{}));
+      m_phase(T_{}, T_{}, ol_at(n), ql_at(n + 1), c_zero, copy_in(qb_at(n + 2), &cq, std::integral_constant<int, 4 * KS>{}));
       prio_lo();
       advance(cs);
       barrier();
@@ -499,19 +539,22 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
     // phase 2N-1: dV(N-1)
     prio_hi();
     load_prev(p.dv);
-    m_phase(T_{}, F_{}, ob_at(n_tiles - 1), nullptr, no_copy);
+    m_phase(T_{}, F_{}, ol_at(n_tiles - 1), 0u, c_zero, no_copy);
     prio_lo();
     barrier();
     store(p.dv, 1.f);
   } else {
     Cursor co = c0;  // tile of the last dO copy
+    f32x16 cd[2];    // delta of the next dP's rows
     dma(ob_at(0), co);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    fix_lse(ob_at(0));
     barrier();
     barrier();
     // phase 0: dP(0)
+    delta_c(cd, ob_at(0));
     prio_hi();
-    m_phase(F_{}, T_{}, nullptr, ob_at(0), no_copy);
+    m_phase(F_{}, T_{}, 0u, ol_at(0), cd, no_copy);
     prio_lo();
     if (n_tiles > 1) {
       advance(co);
@@ -519,26 +562,29 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
     }
     barrier();
     // phase 1: dS(0)
-    form_ds(ob_at(0));
+    form_ds();
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): dO(1) landed
+    if (n_tiles > 1) fix_lse(ob_at(1));
     barrier();
     for (int n = 0; n + 1 < n_tiles; ++n) {
       // phase 2n+2: dK(n), dP(n+1); dO(n+2) copied meanwhile
       if (n + 2 < n_tiles) advance(co);
+      delta_c(cd, ob_at(n + 1));
       prio_hi();
-      m_phase(T_{}, T_{}, qb_at(n), ob_at(n + 1), copy_in(ob_at(n + 2), &co, std::integral_constant<int, 4 * KS>{}));
+      m_phase(T_{}, T_{}, ql_at(n), ol_at(n + 1), cd, copy_in(ob_at(n + 2), &co, std::integral_constant<int, 4 * KS>{}));
       prio_lo();
       if (n + 2 < n_tiles) dma_side(ob_at(n + 2), co);
       barrier();
       // phase 2n+3: dS(n+1)
-      form_ds(ob_at(n + 1));
+      form_ds();
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): dO(n+2) landed
+      if (n + 2 < n_tiles) fix_lse(ob_at(n + 2));
       barrier();
     }
     // phase 2N: dK(N-1)
     prio_hi();
     load_prev(p.dk);
-    m_phase(T_{}, F_{}, qb_at(n_tiles - 1), nullptr, no_copy);
+    m_phase(T_{}, F_{}, ql_at(n_tiles - 1), 0u, c_zero, no_copy);
     prio_lo();
     store(p.dk, p.scale);
   }

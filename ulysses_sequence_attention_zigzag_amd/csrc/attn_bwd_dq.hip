@@ -17,8 +17,8 @@ namespace {
 //   P wave:  S^T(n)                 [matrix]
 //            P^T = exp2(S^T c - LSE log2 e) -> LDS exchange (bf16, times
 //            the softcap derivative)    [vector]
-//   dS wave: dP^T(n)                [matrix]
-//            dS^T = P^T (dP^T - delta) from the exchange   [vector]
+//   dS wave: delta - dP^T(n)        [matrix: -dO fragments, C = delta]
+//            dS^T = -P^T (delta - dP^T) from the exchange   [vector]
 //            dQ^T += K^T dS^T       [matrix]
 // Phases: in phase 2n the P wave forms P(n) while the dS wave runs dQ(n-1)
 // and dP(n); in phase 2n+1 the P wave runs S(n+1) while the dS wave forms
@@ -65,15 +65,22 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
   const bool qvalid = qr < it.q_rows;
   const int64_t qrow = (int64_t)it.q_row0 + qr;
 
-  // Q (P waves) or dO (dS waves) fragments of this lane's row: B operand
+  // Q (P waves) or -dO (dS waves, sign bits flipped: exact) fragments of
+  // this lane's row: B operand
   bf16x8 kv[KS];
   {
     const uint16_t* src = grp ? p.dout + (int64_t)b * p.g_batch_stride : p.q + (int64_t)b * p.q_batch_stride;
     src += (qrow * p.Hq + h) * D + hi * 8;
+    const uint32_t flip = grp ? 0x80008000u : 0u;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (qvalid) {
-        kv[ks] = *reinterpret_cast<const bf16x8*>(src + ks * 16);
+        uint4 u = *reinterpret_cast<const uint4*>(src + ks * 16);
+        u.x ^= flip;
+        u.y ^= flip;
+        u.z ^= flip;
+        u.w ^= flip;
+        kv[ks] = __builtin_bit_cast(bf16x8, u);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) kv[ks][e] = (__bf16)0.f;
@@ -88,13 +95,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
     lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
     dl = p.delta[li];
   }
-  // acc: dQ^T (dS waves); sc: S^T or dP^T of the two 32-key blocks; bb: dS^T
+  // acc: dQ^T (dS waves); sc: S^T or delta - dP^T of the two 32-key blocks;
+  // bb: dS^T; c_s / c_dp: C operands of the first S / dP MFMA (0 / delta)
   f32x16 acc[DB], sc[2];
   bf16x8 bb[2][2];
 #pragma unroll
   for (int d = 0; d < DB; ++d)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[d][r] = 0.f;
+  f32x16 c_s[2], c_dp[2];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    c_s[0][r] = c_s[1][r] = 0.f;
+    c_dp[0][r] = c_dp[1][r] = dl;
+  }
 
   PosMap qm = p.qmap;
   qm.rank = it.q_rank;
@@ -195,6 +209,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
     const uint32_t off = rows + (j == 0 ? lsw0 : j == 1 ? lsw1 : j == 2 ? lsw2 : lsw3);
     copy16_to_lds(trs, lds_addr(buf + (wg * LPT + j) * 1024), off);
   };
+
   auto dma = [&](char* buf, const Cursor& cu) {
 #pragma unroll
     for (int j = 0; j < LPT; ++j) dma_slice(buf, cu, j);
@@ -215,8 +230,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
 
   int tro[2][DB], rro[KS];
   pp_offsets<D>(lane, tro, rro);
-  auto m_phase = [&](auto do_t_c, auto do_r_c, const char* tT, const char* tR, auto&& hook) {
-    pp_matrix_phase<D, decltype(do_t_c)::value, decltype(do_r_c)::value>(acc, sc, bb, kv, tro, rro, tT, tR, hook);
+  auto m_phase = [&](auto do_t_c, auto do_r_c, uint32_t tT, uint32_t tR, const f32x16(&c0)[2], auto&& hook) {
+    pp_matrix_phase<D, decltype(do_t_c)::value, decltype(do_r_c)::value>(acc, sc, bb, kv, tro, rro, tT, tR, c0, hook);
   };
   const auto no_copy = [](int) {};
 
@@ -291,7 +306,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
       if constexpr (!FULL) __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // Vector phase of the dS wave: dS^T = P^T (dP^T - delta), dP^T in sc.
+  // Vector phase of the dS wave: dS^T = -P^T (delta - dP^T), the latter in sc.
   auto form_ds = [&]() {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -301,10 +316,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
       for (int g = 0; g < 4; ++g) {
         const int hh = g >> 1, o = (g & 1) * 4;
         const float4 px = make_float4((float)xh[hh][o], (float)xh[hh][o + 1], (float)xh[hh][o + 2], (float)xh[hh][o + 3]);
-        const float d0 = px.x * (sc[kb][4 * g] - dl);
-        const float d1 = px.y * (sc[kb][4 * g + 1] - dl);
-        const float d2 = px.z * (sc[kb][4 * g + 2] - dl);
-        const float d3 = px.w * (sc[kb][4 * g + 3] - dl);
+        const float d0 = -(px.x * sc[kb][4 * g]);
+        const float d1 = -(px.y * sc[kb][4 * g + 1]);
+        const float d2 = -(px.z * sc[kb][4 * g + 2]);
+        const float d3 = -(px.w * sc[kb][4 * g + 3]);
         const bf16x2 a01 = __builtin_convertvector((f32x2){d0, d1}, bf16x2);
         const bf16x2 a23 = __builtin_convertvector((f32x2){d2, d3}, bf16x2);
         const int half = g >> 1, e0 = (g & 1) * 4;
@@ -322,6 +337,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
   auto prio_lo = []() { __builtin_amdgcn_s_setprio(0); };
   auto kb_at = [&](int n) { return kbuf + (n % 3) * TILEB; };
   auto vb_at = [&](int n) { return vbuf + (n & 1) * TILEB; };
+  auto kl_at = [&](int n) { return lds_addr(kb_at(n)); };
+  auto vl_at = [&](int n) { return lds_addr(vb_at(n)); };
 
   // The two roles run separate programs that pass the same barriers:
   // prologue (tile 0 lands; the P waves compute S(0)), two phases per tile,
@@ -339,7 +356,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     pp_barrier();
     prio_hi();
-    m_phase(F_{}, T_{}, nullptr, kb_at(0), no_copy);
+    m_phase(F_{}, T_{}, 0u, kl_at(0), c_s, no_copy);
     prio_lo();
     pp_barrier();
     // phase 0: P of tile 0
@@ -351,7 +368,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
       // phase 2n+1: S(n+1); K(n+2) copied meanwhile
       if (n + 2 < n_tiles) advance(ck);
       prio_hi();
-      m_phase(F_{}, T_{}, nullptr, kb_at(n + 1), copy_in(kb_at(n + 2), &ck, std::integral_constant<int, 2 * KS>{}));
+      m_phase(F_{}, T_{}, 0u, kl_at(n + 1), c_s, copy_in(kb_at(n + 2), &ck, std::integral_constant<int, 2 * KS>{}));
       prio_lo();
       advance(cs);
       pp_barrier();
@@ -371,7 +388,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
     pp_barrier();
     // phase 0: dP(0)
     prio_hi();
-    m_phase(F_{}, T_{}, nullptr, vb_at(0), no_copy);
+    m_phase(F_{}, T_{}, 0u, vl_at(0), c_dp, no_copy);
     prio_lo();
     if (n_tiles > 1) {
       advance(cv);
@@ -386,7 +403,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
       // phase 2n+2: dQ(n), dP(n+1); V(n+2) copied meanwhile
       if (n + 2 < n_tiles) advance(cv);
       prio_hi();
-      m_phase(T_{}, T_{}, kb_at(n), vb_at(n + 1), copy_in(vb_at(n + 2), &cv, std::integral_constant<int, 4 * KS>{}));
+      m_phase(T_{}, T_{}, kl_at(n), vl_at(n + 1), c_dp, copy_in(vb_at(n + 2), &cv, std::integral_constant<int, 4 * KS>{}));
       prio_lo();
       pp_barrier();
       // phase 2n+3: dS(n+1)
@@ -406,7 +423,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
         for (int g = 0; g < 4; ++g) prev[d][g] = *reinterpret_cast<const float4*>(op + d * 32 + 8 * g + 4 * hi);
     }
     prio_hi();
-    m_phase(T_{}, F_{}, kb_at(n_tiles - 1), nullptr, no_copy);
+    m_phase(T_{}, F_{}, kl_at(n_tiles - 1), 0u, c_dp, no_copy);
     prio_lo();
 
     // dq[b, row, h, :] += scale * dQ (this lane: query qrow, head-dim rows of dQ^T)

@@ -112,6 +112,16 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((__attribute__((address_space(3))) char*)(p)));
   return __builtin_bit_cast(bf16x4, v);
 }
+// The two reads at LDS byte addresses.
+__device__ __forceinline__ bf16x4 lds_read_tr_at(uint32_t a) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4*>(a));
+  return __builtin_bit_cast(bf16x4, v);
+}
+__device__ __forceinline__ bf16x8 lds_read_b128_at(uint32_t a) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(a);
+}
 
 // LDS tile of R rows x D bf16 (CPR 16-byte chunks per row, RPL rows per
 // 256-byte bank line) with chunk c of row r at slot c ^ swz(r),
@@ -184,33 +194,53 @@ __device__ __forceinline__ void pp_offsets(int lane, int (&tro)[2][D / 32], int 
 }
 
 // Matrix phase: the transposed-operand products acc[d] += X^T bb (X the
-// 64-row tile at tT; 2 blocks x 2 halves x D/32 MFMAs) if DT, then the
-// row-operand products sc[blk] = Y kv (Y the tile at tR; 2 blocks x D/16
-// MFMAs, the two blocks alternating) if DR.  Fragments are read kPF MFMAs
+// 64-row tile at LDS address tT; 2 blocks x 2 halves x D/32 MFMAs) if DT,
+// then the row-operand products sc[blk] = Y kv + c0[blk] (Y the tile at
+// tR; 2 blocks x D/16 MFMAs, the two blocks alternating) if DR.  Fragments are read kPF MFMAs
 // ahead, across the boundary, in an order pinned with scheduling groups.
 // hook(m) runs after the phase's m-th MFMA (m a constant once unrolled): the
 // kernels issue their tile copies from it, spread over the phase.
 template <int D, bool DT, bool DR, typename Hook>
 __device__ __forceinline__ void pp_matrix_phase(f32x16 (&acc)[D / 32], f32x16 (&sc)[2], const bf16x8 (&bb)[2][2],
                                                 const bf16x8 (&kv)[D / 16], const int (&tro)[2][D / 32],
-                                                const int (&rro)[D / 16], const char* tT, const char* tR,
-                                                Hook&& hook) {
+                                                const int (&rro)[D / 16], uint32_t tT, uint32_t tR,
+                                                const f32x16 (&c0)[2], Hook&& hook) {
   using T = SwzTile<D>;
   constexpr int KS = D / 16, DB = D / 32;
   constexpr int NT = 2 * 2 * DB;
   constexpr int NR = 2 * KS;
   constexpr int PF = kPF;
   static_assert(PF <= NT && PF <= NR, "prefetch depth");
+  // Per-phase lane bases (tile + lane offset), made opaque: otherwise the
+  // loop-invariant sums lane offset + fragment constant are hoisted out of
+  // the tile loop (one register each) and every read pays an add; from an
+  // opaque base each fragment's constant goes in the read's offset field.
+  uint32_t bt0[D / 32], bt1[D / 32], br[D / 16];
+  if constexpr (DT) {
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+      bt0[d] = tT + (uint32_t)tro[0][d];
+      bt1[d] = tT + (uint32_t)tro[1][d];
+      asm volatile("" : "+v"(bt0[d]), "+v"(bt1[d]));
+    }
+  }
+  if constexpr (DR) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      br[ks] = tR + (uint32_t)rro[ks];
+      asm volatile("" : "+v"(br[ks]));
+    }
+  }
   auto rd_t = [&](int j) {
     const int blk = j / (2 * DB), half = (j / DB) & 1, d = j % DB;
-    const char* base = tT + (blk * 32 + half * 16) * T::ROWB;
-    const bf16x4 a0 = lds_read_tr(base + tro[0][d]);
-    const bf16x4 a1 = lds_read_tr(base + tro[1][d]);
+    const uint32_t cst = (uint32_t)((blk * 32 + half * 16) * T::ROWB);
+    const bf16x4 a0 = lds_read_tr_at(bt0[d] + cst);
+    const bf16x4 a1 = lds_read_tr_at(bt1[d] + cst);
     return bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
   };
   auto rd_r = [&](int i) {
     const int ks = i >> 1, blk = i & 1;
-    return *reinterpret_cast<const bf16x8*>(tR + blk * 32 * T::ROWB + rro[ks]);
+    return lds_read_b128_at(br[ks] + (uint32_t)(blk * 32 * T::ROWB));
   };
   bf16x8 ft[NT], fr[NR];
   if constexpr (DT) {
@@ -229,12 +259,11 @@ __device__ __forceinline__ void pp_matrix_phase(f32x16 (&acc)[D / 32], f32x16 (&
     for (int i = 0; i < PF; ++i) fr[i] = rd_r(i);
   }
   if constexpr (DR) {
-    const f32x16 zero = {};
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       if (i + PF < NR) fr[i + PF] = rd_r(i + PF);
       const int ks = i >> 1, blk = i & 1;
-      sc[blk] = mfma32(fr[i], kv[ks], ks == 0 ? zero : sc[blk]);
+      sc[blk] = mfma32(fr[i], kv[ks], ks == 0 ? c0[blk] : sc[blk]);
       hook((DT ? NT : 0) + i);
     }
   }

@@ -46,13 +46,6 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ int32_t floor_div(int32_t a, int32_t b) {
-  if (b == 1) return a;
-  const int32_t q = a / b;
-  return (a % b != 0 && a < 0) ? q - 1 : q;
-}
-__device__ __forceinline__ int32_t ceil_div(int32_t a, int32_t b) { return -floor_div(-a, b); }
-
 // Raw buffer resource of `base` (no stride, 2^31 - 1 bytes, no swizzle),
 // wave-uniform so it lives in SGPRs.
 __device__ __forceinline__ i32x4 buffer_rsrc(const void* base) {

@@ -131,12 +131,18 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
   const int hi = lane >> 5;
 
   // Items come sorted by decreasing work and the hardware deals consecutive
-  // workgroups round-robin to the 8 XCDs, so the plain order gives every XCD
-  // an even share of large and small items (with one KV head, a contiguous
-  // block per XCD would hand one XCD all the largest).
+  // workgroups round-robin to the 8 XCDs (and, inside one, to its shader
+  // engines), so the plain order gives every XCD an even share of large and
+  // small items (with one KV head, a contiguous block per XCD would hand one
+  // XCD all the largest).  The heads of one item are adjacent: ordered
+  // head-major, each head's largest item sat n_items workgroups from the
+  // next one's, which with n_items a multiple of 32 put all of them on one
+  // shader engine of one XCD (varlen steps whose work is a few long items
+  // ran them 8 at a time).
   const int bid = blockIdx.x;
-  const int hb = bid / p.n_items;
-  const int item_idx = bid - hb * p.n_items;
+  const int n_hb = p.Hkv * p.B;
+  const int item_idx = bid / n_hb;
+  const int hb = bid - item_idx * n_hb;
   const int hk = hb % p.Hkv;
   const int b = hb / p.Hkv;
   const WorkItem it = p.items[item_idx];

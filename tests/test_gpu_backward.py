@@ -289,6 +289,12 @@ RING_BWD = [
                                       ulysses_rank=1),
     # degenerate: one rank, the ring is plain attention
     si.WORKLOADS["zigzag_causal_small"].scaled(impl="basic", ring_degree=1, S=777, Hq=2, Hkv=1, rank=-1),
+    # one rank with ring steps that see nothing: the dk / dv pieces of those
+    # steps are zeros (window; causal pieces after the rank's own; varlen)
+    si.WORKLOADS["ring_swa"].scaled(B=1, S=2048, Hq=2, Hkv=2, window=300, rank=5),
+    si.WORKLOADS["zigzag_causal_small"].scaled(impl="basic", rank=1),
+    si.WORKLOADS["varlen_streaming"].scaled(S=2048, Hq=2, Hkv=1, window=250, cu_seqlens=[0, 128, 1000, 2048],
+                                            rank=2),
 ]
 
 
@@ -307,13 +313,19 @@ def _ring_bwd_expected(w: si.Workload, q, k, v):
     pos = [ix.rank_positions(w.impl, w.S, N, r, w.stripe_block) for r in range(N)]
     O, LSE = attention_ref(q, k, v, rows=pos[w.rank], heads=heads, **kw)
     dout = si.randn_bf16(tuple(O.shape), w.seed, 3)
-    qi = q[:, pos[w.rank]][:, :, heads].contiguous()
-    ks, vs = k[:, :, kvh].contiguous(), v[:, :, kvh].contiguous()
-    dq, dk, dv = block_attention_bwd_ref(qi, ks, vs, dout, LSE, _delta(dout, O), pos[w.rank], list(range(w.S)),
+    # the block oracle takes a batch dimension, which varlen tensors lack
+    bat = (lambda t: t.unsqueeze(0)) if w.cu_seqlens is not None else (lambda t: t)
+    qb, kb, vb, Ob, LSEb, dob = (bat(t) for t in (q, k, v, O, LSE, dout))
+    qi = qb[:, pos[w.rank]][:, :, heads].contiguous()
+    ks, vs = kb[:, :, kvh].contiguous(), vb[:, :, kvh].contiguous()
+    dq, dk, dv = block_attention_bwd_ref(qi, ks, vs, dob, LSEb, _delta(dob, Ob), pos[w.rank], list(range(w.S)),
                                          scale=w.scale, causal=w.causal, window=w.window, n_sink=w.n_sink,
                                          cu_seqlens=w.cu_seqlens)
     perm = [p for r in range(N) for p in pos[r]]          # rank-major row order
-    return O, LSE, dout, (dq, dk[:, perm], dv[:, perm])
+    grads = (dq, dk[:, perm], dv[:, perm])
+    if w.cu_seqlens is not None:
+        grads = tuple(g[0] for g in grads)
+    return O, LSE, dout, grads
 
 
 @pytest.mark.parametrize("w", RING_BWD, ids=lambda w: f"{w.name}-S{w.S}-r{w.rank}-u{w.ulysses_rank}")
@@ -329,6 +341,11 @@ def test_ring_bwd_oracle_forward(w):
     fwd.out.copy_(O.float())
     fwd.lse.copy_(LSE.float())
     bwd = usp.RingBwdCall(fwd, dout.cuda())
+    # outputs and workspace start as NaN: a gradient row the call leaves
+    # unwritten, or a workspace byte it reads before writing, shows
+    for t in (bwd.dq, bwd.dk, bwd.dv):
+        t.fill_(float("nan"))
+    bwd.workspace.fill_(0xFF)
     got = bwd.run()
     torch.cuda.synchronize()
     for g, r, name in zip(got, ref, ("dq", "dk", "dv")):

@@ -1007,8 +1007,12 @@ usp_status ring_bwd_layout(const usp_ring_args* a, RingBwdLayout* out) {
     r.off_dog = take(B * (size_t)R.L * R.Hq_l * D * 2);
     r.off_lg = take(B * (size_t)R.Hq_l * R.L * 4);
   }
-  r.jq = ring_job(a, 0, kBwdTileM, kTileN, 0);
-  r.jk = ring_job(a, 1, kBwdTileK, kBwdTileQ, 0);
+  // Step 0 stores dq (and, with every host in the call, dk / dv) instead of
+  // adding to zeros, so its plans keep the tiles no query reaches; for one
+  // rank each step owns the dk / dv piece it meets, and every step stores.
+  const int N = a->ring_degree;
+  r.jq = ring_job(a, 0, kBwdTileM, kTileN, 1);
+  r.jk = ring_job(a, 1, kBwdTileK, kBwdTileQ, a->rank >= 0 ? N : 1);
   usp_status st = finish_job(r.jq, a->cu_seqlens_host);
   if (st == USP_OK) st = finish_job(r.jk, a->cu_seqlens_host);
   if (st != USP_OK) return st;
@@ -1267,17 +1271,19 @@ usp_status usp_ring_bwd(const usp_ring_bwd_args* ba, void* workspace, size_t ws_
   float* dq = RB.reorder ? reinterpret_cast<float*>(ws + RB.off_dq) : ba->dq;
   float* dk = RB.reorder ? reinterpret_cast<float*>(ws + RB.off_dk) : ba->dk;
   float* dv = RB.reorder ? reinterpret_cast<float*>(ws + RB.off_dv) : ba->dv;
-  st = launch_fill_zero(dq, B * R.q_rows * Hq_l * D, stream);
-  if (st == USP_OK) st = launch_fill_zero(dk, B * S * stg.Hkv_l * D, stream);
-  if (st == USP_OK) st = launch_fill_zero(dv, B * S * stg.Hkv_l * D, stream);
-  if (st != USP_OK) return st;
 
   // 3. ring steps: host i meets KV piece j = (i - s) mod N; one launch per
   // kernel per step covers every host of the step (their dq rows and dk / dv
-  // pieces are disjoint)
+  // pieces are disjoint).  Step 0 always runs and stores dq; dk / dv are
+  // stored by step 0 when every host is in the call (each piece meets its
+  // own host there), and by every step for one rank (each step meets a
+  // different piece), so a step without work still runs its dK / dV launch
+  // then, with tiles that only store zeros.
+  const bool one = a->rank >= 0;
   const int64_t cq = jq.cpp(), ck = jk.cpp();
   for (int s = 0; s < N; ++s) {
-    if (!step_has_work(RB.jq, s, a->cu_seqlens_host)) continue;
+    const bool work = s == 0 || step_has_work(RB.jq, s, a->cu_seqlens_host);
+    if (!work && !one) continue;
     BwdParams p{};
     p.q = stg.q + stg.q_row_off * Hq_l * D;
     p.k = stg.k;
@@ -1305,10 +1311,12 @@ usp_status usp_ring_bwd(const usp_ring_bwd_args* ba, void* workspace, size_t ws_
     BwdParams pq = p, pk = p;
     pq.items = jq.items + (int64_t)s * cq;
     pq.runs = jq.runs;
-    pq.n_items = (int32_t)cq;
+    pq.n_items = work ? (int32_t)cq : 0;
+    pq.overwrite = s == 0;
     pk.items = jk.items + (int64_t)s * ck;
     pk.runs = jk.runs;
     pk.n_items = (int32_t)ck;
+    pk.overwrite = s == 0 || one;
     st = launch_bwd(pq, pk, (int)D, stream);
     if (st != USP_OK) return st;
   }

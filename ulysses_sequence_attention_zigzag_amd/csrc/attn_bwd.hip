@@ -33,11 +33,6 @@
 namespace usp {
 namespace {
 
-__global__ __launch_bounds__(256) void fill_zero_kernel(float4* p, int64_t n4) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256)
-    p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-}
-
 // ------------------------------------------------------------------ delta
 // delta[b, h, t] = sum_d dO[b, t, h, d] * O[b, t, h, d].  A group of D/8
 // threads per (row, head) reads 8 consecutive elements each (16 bytes of
@@ -146,13 +141,24 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
   const int hk = hb % p.Hkv;
   const int b = hb / p.Hkv;
   const WorkItem it = p.items[item_idx];
-  if (it.q_rows == 0 || it.run_begin == it.run_end) return;  // no query sees these keys (whole workgroup)
+  if (it.q_rows == 0) return;  // planner slot with nothing to do (whole workgroup)
   const int group = p.Hq / p.Hkv;
 
   const int kr_ = wg * 32 + l32;
   const bool kvalid = kr_ < it.q_rows;
   const int64_t krow = (int64_t)it.q_row0 + kr_;
   const int64_t kv_row_stride = (int64_t)p.Hkv * D;
+  if (it.run_begin == it.run_end) {  // no query sees these keys (whole workgroup)
+    // a storing launch still writes their gradient rows: dV (P waves), dK
+    if (p.overwrite && kvalid) {
+      float* dst = (grp ? p.dk : p.dv) + (int64_t)b * p.kv_batch_stride + krow * kv_row_stride + hk * D;
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) *reinterpret_cast<float4*>(dst + d * 32 + 8 * g + 4 * hi) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    return;
+  }
 
   // query tiles of this item: group heads x runs x ceil(run / BQ)
   int tiles_per_head = 0;
@@ -470,7 +476,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
   auto ol_at = [&](int n) { return lds_addr(ob_at(n)); };
 
   // Epilogue: dV (P waves) or scale * dK (dS waves) added into the f32
-  // gradients of this lane's key.
+  // gradients of this lane's key (stored alone by a storing launch).
   // The gradient this call adds to is loaded before the role's last matrix
   // phase (K or V and the S / dP results are dead by then), which covers
   // part of the load's latency: the store is a fifth to a quarter of a
@@ -478,6 +484,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
   float4 prev[DB][4];
   auto load_prev = [&](const float* base) {
     if (!kvalid) return;
+    if (p.overwrite) {  // storing launch: nothing to add to
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) prev[d][g] = make_float4(0.f, 0.f, 0.f, 0.f);
+      return;
+    }
     const float* src = base + (int64_t)b * p.kv_batch_stride + krow * kv_row_stride + hk * D;
 #pragma unroll
     for (int d = 0; d < DB; ++d)
@@ -597,20 +610,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdParams p) {
 }
 
 }  // namespace
-
-usp_status launch_fill_zero(float* p, int64_t n, hipStream_t stream) {
-  // n is a multiple of 4 and p 16-byte aligned (the callers' f32 tensors of D >= 64 columns)
-  if (n <= 0) return USP_OK;
-  const int64_t n4 = n / 4;
-  const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, 8192);
-  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, reinterpret_cast<float4*>(p), n4);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) {
-    set_error("fill launch failed: %s", hipGetErrorString(e));
-    return USP_ERR_HIP;
-  }
-  return USP_OK;
-}
 
 usp_status launch_bwd_delta(const void* out, int out_f32, const uint16_t* dout, float* delta, int64_t B,
                             int64_t L, int64_t H, int64_t D, hipStream_t stream) {

@@ -25,7 +25,9 @@ namespace {
 // dS(n).  Every phase ends with a workgroup barrier.  Tile staging straight
 // into LDS: the P waves load K (3 buffers: K(n) is read in phases
 // 2n-1 .. 2n+2), the dS waves V (2 buffers), each two phases ahead of use.
-template <int D, int MODS>
+// OW: a storing launch (p.overwrite), built apart so that the adding form
+// keeps its own code.
+template <int D, int MODS, bool OW>
 __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
   using T = SwzTile<D>;
   constexpr int BN = 64;                   // keys per tile
@@ -58,12 +60,27 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
   const int h = hb % p.Hq;
   const int b = hb / p.Hq;
   const WorkItem it = p.items[item_idx];
-  if (it.q_rows == 0 || it.run_begin == it.run_end) return;  // nothing to do (whole workgroup)
+  // nothing to do (whole workgroup); a storing launch still writes the dq
+  // rows of a tile that sees no key
+  if (it.q_rows == 0 || (!OW && it.run_begin == it.run_end)) return;
   const int hk = h / (p.Hq / p.Hkv);
 
   const int qr = wg * 32 + l32;
   const bool qvalid = qr < it.q_rows;
   const int64_t qrow = (int64_t)it.q_row0 + qr;
+  if constexpr (OW) {
+    if (it.run_begin == it.run_end) {  // the dS waves own dq
+      if (grp == 1 && qvalid) {
+        float* op = p.dq + (int64_t)b * p.g_batch_stride + (qrow * p.Hq + h) * D;
+#pragma unroll
+        for (int d = 0; d < DB; ++d)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<float4*>(op + d * 32 + 8 * g + 4 * hi) = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      return;
+    }
+  }
 
   // Q (P waves) or -dO (dS waves, sign bits flipped: exact) fragments of
   // this lane's row: B operand
@@ -413,10 +430,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
     }
     // phase 2N: dQ(N-1).  The dq rows this call adds to are loaded before
     // it (V and the dP results are dead by then), which covers part of the
-    // load's latency.
+    // load's latency; a storing launch adds to nothing.
     float4 prev[DB][4];
     float* op = p.dq + (int64_t)b * p.g_batch_stride + (qrow * p.Hq + h) * D;
-    if (qvalid) {
+    if constexpr (OW) {
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) prev[d][g] = make_float4(0.f, 0.f, 0.f, 0.f);
+    } else if (qvalid) {
 #pragma unroll
       for (int d = 0; d < DB; ++d)
 #pragma unroll
@@ -426,7 +448,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
     m_phase(T_{}, F_{}, kl_at(n_tiles - 1), 0u, c_dp, no_copy);
     prio_lo();
 
-    // dq[b, row, h, :] += scale * dQ (this lane: query qrow, head-dim rows of dQ^T)
+    // dq[b, row, h, :] += scale * dQ (this lane: query qrow, head-dim rows of
+    // dQ^T), or = for a storing launch
     if (!qvalid) return;
     const float w = p.scale;
 #pragma unroll
@@ -450,7 +473,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdParams p) {
 void launch_bwd_dq(const BwdParams& p, int D, unsigned grid, hipStream_t stream) {
   TimingScope ts(K_BWD_DQ, stream);
   const int mods = mods_variant(p.mods);
-#define USP_LAUNCH_Q(DD, M) hipLaunchKernelGGL((bwd_dq_kernel<DD, M>), dim3(grid), dim3(512), 0, stream, p)
+#define USP_LAUNCH_Q(DD, M)                                                                                 \
+  do {                                                                                                      \
+    if (p.overwrite)                                                                                        \
+      hipLaunchKernelGGL((bwd_dq_kernel<DD, M, true>), dim3(grid), dim3(512), 0, stream, p);                \
+    else                                                                                                    \
+      hipLaunchKernelGGL((bwd_dq_kernel<DD, M, false>), dim3(grid), dim3(512), 0, stream, p);               \
+  } while (0)
 #define USP_LAUNCH_Q_M(DD)                  \
   switch (mods) {                           \
     case 0: USP_LAUNCH_Q(DD, 0); break;     \

@@ -264,7 +264,7 @@ struct PlanJob {
   int32_t kind;            // 0: query tiles (forward, dQ); 1: key tiles (dK / dV)
   int32_t tile;            // rows (kind 0) or keys (kind 1) per item
   int32_t gran;            // granularity of full runs
-  int32_t acc_from_step;   // kind 0: items without runs are dropped at steps >= this
+  int32_t acc_from_step;   // items without runs are dropped at steps >= this
   int32_t empty;           // explicit EMPTY class: no keys at all
   int32_t ring;            // 1: ring blocks; 0: one block
   int32_t N, rank_lo, n_ranks, n_steps, one_rank;
@@ -339,7 +339,7 @@ __host__ __device__ WorkItem plan_candidate(const PlanJob& J, const SeqView& seq
     it = WorkItem{qbase + t0, t0, rows, qm.rank, kbase, km.rank, rb, rb + imin32(n, J.cap)};
   else
     it = WorkItem{kbase + t0, t0, rows, km.rank, qbase, qm.rank, rb, rb + imin32(n, J.cap)};
-  const bool drop = n == 0 && (J.kind == 1 || s >= J.acc_from_step);
+  const bool drop = n == 0 && s >= J.acc_from_step;
   if (drop) {
     it.q_rows = 0;
     it.run_end = it.run_begin;

@@ -215,6 +215,8 @@ struct BwdParams {
   int32_t Hkv;
   float scale;               // softmax_scale
   float scale_log2;          // softmax_scale * log2(e)
+  int32_t overwrite;         // 1: the launch stores its gradient rows instead of adding to
+                             // them (a planned item without runs stores zeros)
   PosMap qmap;
   PosMap kmap;
   MaskSpec mask;
@@ -226,7 +228,6 @@ constexpr int kBwdTileQ = 64;   // query rows per dK / dV iteration
 usp_status launch_bwd(const BwdParams& pq, const BwdParams& pkv, int D, hipStream_t stream);
 // Enqueues the dQ kernel alone (no error check; launch_bwd checks).
 void launch_bwd_dq(const BwdParams& p, int D, unsigned grid, hipStream_t stream);
-usp_status launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 
 // Decode over a KV cache, split into pieces of split_keys keys (a multiple
 // of 32); one wave per (piece, batch row, KV head).

@@ -913,7 +913,7 @@ struct Staged {
 
 usp_status stage_ring_inputs(const usp_ring_args* a, const RingLayout& R, uint16_t* qd, uint16_t* kd,
                              uint16_t* vd, hipStream_t stream, Staged* out) {
-  const int N = a->ring_degree, ud = a->ulysses_degree, u = a->ulysses_rank;
+  const int N = a->ring_degree, u = a->ulysses_rank;
   const int64_t B = a->B, S = a->S, D = a->D, L = R.L;
   const int b = a->impl == USP_RING_STRIPE ? a->stripe_block : 1;
   if (!R.copy_in) {

@@ -295,6 +295,8 @@ RING_BWD = [
     si.WORKLOADS["zigzag_causal_small"].scaled(impl="basic", rank=1),
     si.WORKLOADS["varlen_streaming"].scaled(S=2048, Hq=2, Hkv=1, window=250, cu_seqlens=[0, 128, 1000, 2048],
                                             rank=2),
+    si.WORKLOADS["ring_swa"].scaled(B=1, S=2048, Hq=4, Hkv=2, window=300, rank=6, ulysses_degree=2,
+                                    ulysses_rank=1),
 ]
 
 

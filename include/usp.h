@@ -415,7 +415,10 @@ usp_status usp_ring_stage(const usp_ring_args* a, void* q_staged, void* k_staged
  * Steps: staging of q, k, v as in usp_ring_fwd; delta =
  * usp_attn_bwd_preprocess(out, dout); N steps of usp_block_attn_bwd (every
  * host of a step in one launch per kernel); natural-order outputs are
- * un-permuted at the end.  The workspace holds the dQ and dK / dV tile plans
+ * un-permuted at the end.  The outputs need no initial value: the first
+ * launch that reaches a gradient row stores it (step 0 for dq, and for
+ * dk / dv with every host; each step for one rank's dk / dv pieces), and
+ * rows that no query or key reaches are stored as zeros.  The workspace holds the dQ and dK / dV tile plans
  * of every step (built on the device by the call) and the staged tensors. */
 typedef struct usp_ring_bwd_args {
   usp_ring_args fwd;

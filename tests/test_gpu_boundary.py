@@ -243,6 +243,30 @@ def test_device_planner_explicit_classes(mask):
             assert _runs_of(di, dr) == _runs_of(hi, hr), (mask, Lq, Lk, acc)
 
 
+@pytest.mark.parametrize("S,cu", [
+    (280000, None),                                    # more candidates than one workgroup plans
+    (280000, [0, 1000, 150000, 280000]),               # the same, cu_seqlens staged in LDS
+    (280000, list(range(0, 280000, 100)) + [280000]),  # 2800 sequences: cu_seqlens read from memory
+    (4096, list(range(0, 4097, 2))),                   # one workgroup, cu_seqlens read from memory
+], ids=["large", "large-cu", "large-many-seqs", "small-many-seqs"])
+def test_device_planner_sizes(S, cu):
+    """Both forms of the device planner (one workgroup per plan up to 1024
+    candidates, else a planning and an ordering launch) and both places it
+    reads cu_seqlens from give the host planner's plan."""
+    N = 2
+    L = S // N
+    say(f"device planner S={S} nseq={0 if cu is None else len(cu) - 1}")
+    for i, j in ((1, 1), (1, 0), (0, 1)):
+        qm, km = usp.posmap("zigzag", N, i, S, 1), usp.posmap("zigzag", N, j, S, 1)
+        kw = dict(mask="positional", qmap=qm, kmap=km, causal=True, cu_seqlens=cu)
+        hi, hr, _, _ = usp.plan_block(L, L, 128, accumulate=True, **kw)
+        di, dr, _ = usp.plan_block_device(L, L, accumulate=True, **kw)
+        assert _runs_of(di, dr) == _runs_of(hi, hr), (i, j)
+        hi, hr, _, _ = usp.plan_block_kv(L, L, 128, **kw)
+        di, dr, _ = usp.plan_block_device(L, L, kv_tiles=True, **kw)
+        assert _runs_of(di, dr) == _runs_of(hi, hr), (i, j, "kv")
+
+
 # ---------------------------------------------------------------- streams and graphs
 def test_varlen_calls_on_a_side_stream():
     """cu_seqlens copies and workspaces follow the stream a call is enqueued

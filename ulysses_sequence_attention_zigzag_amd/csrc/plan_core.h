@@ -55,22 +55,19 @@ struct SeqView {
   __host__ __device__ int64_t end(int32_t i) const { return cu ? cu[i + 1] : S; }
 };
 
-// First u in [lo, hi) with position(u) >= P (hi if none); positions increase on [lo, hi).
+// First u in [lo, hi) with position(u) >= P (hi if none); positions increase
+// on [lo, hi), a monotone piece.  Closed form (first_row_at_least) between
+// the two end checks, which also keep P inside int32.
 __host__ __device__ inline int32_t bsearch_at_least(const PosMap& m, int32_t lo, int32_t hi, int64_t P) {
-  while (lo < hi) {
-    const int32_t mid = lo + (hi - lo) / 2;
-    if (position(m, mid) >= P) hi = mid; else lo = mid + 1;
-  }
-  return lo;
+  if (lo >= hi || P <= position(m, lo)) return lo;
+  if (P > position(m, hi - 1)) return hi;
+  const int32_t u = first_row_at_least(m, lo, (int32_t)P);
+  return u < lo ? lo : (u > hi ? hi : u);
 }
 
 // First u in [lo, hi) with position(u) > P (hi if none).
 __host__ __device__ inline int32_t bsearch_above(const PosMap& m, int32_t lo, int32_t hi, int64_t P) {
-  while (lo < hi) {
-    const int32_t mid = lo + (hi - lo) / 2;
-    if (position(m, mid) > P) hi = mid; else lo = mid + 1;
-  }
-  return lo;
+  return bsearch_at_least(m, lo, hi, P + 1);
 }
 
 // Items (tiles of `tile` rows inside the monotone pieces) of one rank's rows.
